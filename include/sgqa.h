@@ -1,0 +1,179 @@
+/*
+ * sgqa.h -- C ABI of the blockwise Sparse GQA hot path for AMD MI355X (gfx950).
+ *
+ * Source of the method: "Inside Step 5 Preview" (StepFun blog), section "Sparse GQA":
+ *   - paragraph "Reducing indexer's cost": the index keys of B adjacent historical positions are
+ *     compressed into one block representation (B = 8), which cuts indexer + top-k cost by B;
+ *   - paragraph "Efficient implementation of sparse attention": during prefill the top-k results
+ *     of adjacent tokens are unioned so that overlapping work is grouped;
+ *   - paragraph "Trade-off between top-k and block size": k = 4096 tokens = k/B = 512 blocks;
+ *   - Figure 3 caption: the index keys are shared, every KV group selects its own history, and the
+ *     main path reads the original K/V of the selected blocks plus the causally visible positions
+ *     of the query's own (current) block.
+ * The pages leave the indexer's form open. This library fixes it as:
+ *   block key      kbar[b] = bf16_rne( mean_{j<B} ki[b*B + j] )            (complete blocks only)
+ *   block score    s(i,g,b) = sum_h w[g,h] * max(0, <qi[i,g,h,:], kbar[b]>)  for b < c(i) = floor(i/B)
+ *   selection      Sel(i,g) = first min(k/B, c(i)) blocks in the order (s descending, b ascending)
+ *   attended set   Sel(i,g) plus the own block c(i), causally masked at token level (j <= i)
+ *   prefill union  U(t,g) = union over the queries i of tile t = floor(i/Tq) of Sel(i,g) + {c(i)};
+ *                  every query of the tile attends over U(t,g), causally masked.
+ *
+ * Conventions for every call
+ *   - bf16 tensors are raw IEEE bfloat16 bit patterns (uint16_t).
+ *   - Every tensor pointer is DEVICE memory owned by the caller; it must be 16-byte aligned and
+ *     the tensor dense (row-major, innermost dimension last, no padding).
+ *   - The library never allocates, frees or keeps a pointer after a call returns. Scratch memory
+ *     comes only from the caller's workspace `ws` of `ws_bytes`, sized by sgqa_workspace_size.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; 0 = the null stream). Nothing is copied
+ *     between host and device and nothing synchronizes the device.
+ *   - Arguments are validated on the host BEFORE anything is enqueued: a nonzero status means no
+ *     work was launched. A fault inside a kernel surfaces at the caller's next synchronization.
+ *   - Results are deterministic: the same inputs give the same bits (no floating-point atomics).
+ *   - Calls keep no state; calls on different streams may run concurrently if their outputs and
+ *     workspaces do not overlap.
+ *   - v1 limits: head_dim == 128, idx_heads == 4, idx_dim == 64, block a power of two <= 64,
+ *     topk_tokens a positive multiple of block with topk_tokens/block <= 2048, n_q_heads a multiple
+ *     of n_kv_heads, n_q_heads/n_kv_heads <= 16, n_tokens >= 1, union_tile >= 1.
+ *     Any other value returns SGQA_ERR_SHAPE.
+ */
+#ifndef SGQA_H
+#define SGQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SGQA_ABI_VERSION 1
+
+typedef uint16_t sgqa_bf16;   /* raw bfloat16 bits */
+typedef void* sgqa_stream;    /* a hipStream_t */
+
+/* Status codes returned by every call. */
+enum {
+  SGQA_OK = 0,
+  SGQA_ERR_NULL = 1,       /* a required pointer is NULL */
+  SGQA_ERR_SHAPE = 2,      /* unsupported or inconsistent sizes (see v1 limits) */
+  SGQA_ERR_ALIGN = 3,      /* a tensor pointer is not 16-byte aligned */
+  SGQA_ERR_WORKSPACE = 4,  /* workspace missing or smaller than sgqa_workspace_size */
+  SGQA_ERR_DEVICE = 5,     /* the current device is not a gfx950 GPU, or no device */
+  SGQA_ERR_HIP = 6         /* the HIP runtime reported an error while launching */
+};
+
+/* Operation selectors for sgqa_workspace_size. */
+enum {
+  SGQA_OP_COMPRESS = 0,
+  SGQA_OP_INDEX_TOPK = 1,
+  SGQA_OP_UNION = 2,
+  SGQA_OP_ATTEND = 3,
+  SGQA_OP_PREFILL = 4,
+  SGQA_OP_DECODE = 5
+};
+
+/* Sizes of one call. Symbols: N tokens, S sequences, Hq query heads, G KV groups (KV heads),
+ * r = Hq/G query heads per group, D head dim, H_I indexer heads, d_I indexer dim, B block,
+ * k selected tokens, K_B = k/B selected blocks, Tq union tile, NB = floor(N/B) complete blocks,
+ * NBc = ceil(N/B) blocks, T = ceil(N/Tq) tiles, W = ceil(NBc/32) mask words. */
+typedef struct sgqa_params {
+  int32_t n_tokens;      /* prefill: N. decode: L, the cached context length INCLUDING the query token */
+  int32_t n_seqs;        /* prefill: must be 1 (compress accepts S >= 1). decode: S */
+  int32_t n_q_heads;     /* Hq */
+  int32_t n_kv_heads;    /* G */
+  int32_t head_dim;      /* D (v1: 128) */
+  int32_t idx_heads;     /* H_I (v1: 4) */
+  int32_t idx_dim;       /* d_I (v1: 64) */
+  int32_t block;         /* B (power of two, 1..64) */
+  int32_t topk_tokens;   /* k (multiple of B) */
+  int32_t union_tile;    /* Tq (>= 1; 1 = no union, every query keeps its own selection) */
+  float softmax_scale;   /* sigma; <= 0 selects 1/sqrt(D) */
+} sgqa_params;
+
+/* ABI version of the loaded library (SGQA_ABI_VERSION). Host only. */
+int sgqa_abi_version(void);
+
+/* Static text for a status code. Host only; never NULL. */
+const char* sgqa_status_string(int status);
+
+/* Bytes of workspace that operation `op` (SGQA_OP_*) needs for `p`, written to *bytes.
+ * Host only: touches no device. Returns SGQA_ERR_NULL / SGQA_ERR_SHAPE like the operation would. */
+int sgqa_workspace_size(const sgqa_params* p, int op, size_t* bytes);
+
+/* Block compression ("Inside Step 5 Preview", Sparse GQA, paragraph "Reducing indexer's cost",
+ * and Figure 3: one shared set of index keys is merged block by block into block keys).
+ *   idx_k  [S][N][d_I]        bf16   shared index keys of every token
+ *   blk_k  [S][floor(N/B)][d_I] bf16 out: blk_k[s][b][d] = bf16_rne(sum_{j<B} idx_k[s][b*B+j][d] / B),
+ *                                    summed in fp32 in ascending j. A trailing partial block is not
+ *                                    compressed (it can only ever be a query's own block).
+ * Uses p->n_seqs, n_tokens, idx_dim, block. No workspace. */
+int sgqa_compress(const sgqa_params* p, const sgqa_bf16* idx_k, sgqa_bf16* blk_k, sgqa_stream stream);
+
+/* Indexer scores and per-query top-k ("Reducing indexer's cost"; Figure 3: the selection is
+ * made separately for every KV group; "Trade-off between top-k and block size" for k/B).
+ *   idx_q  [N][G][H_I][d_I]  bf16   per-group indexer queries
+ *   idx_w  [G][H_I]          fp32   per-group indexer head weights
+ *   blk_k  [floor(N/B)][d_I] bf16   block keys from sgqa_compress
+ *   topk   [G][N][K_B]       int32  out: Sel(i,g), ascending block ids, padded with -1 after
+ *                                   min(K_B, c(i)) entries. The own block c(i) is NOT stored.
+ * Scores are fp32 (products of bf16 accumulated in fp32 on the matrix cores); -0 counts as +0;
+ * ties go to the lower block id. No workspace (pass NULL/0). */
+int sgqa_index_topk(const sgqa_params* p, const sgqa_bf16* idx_q, const float* idx_w,
+                    const sgqa_bf16* blk_k, int32_t* topk, void* ws, size_t ws_bytes,
+                    sgqa_stream stream);
+
+/* Tile union of adjacent queries' selections (Sparse GQA, paragraph "Efficient implementation
+ * of sparse attention": prefill groups the overlapping selections of neighbouring tokens).
+ *   topk   [G][N][K_B]  int32   from sgqa_index_topk
+ *   umask  [G][T][W]    uint32  out: bit (b % 32) of word b/32 is set iff block b is in U(t,g)
+ *   ucount [G][T]       int32   out: |U(t,g)| (popcount of the row)
+ * Tiles are aligned at token 0; the last tile may be partial. No workspace. */
+int sgqa_union(const sgqa_params* p, const int32_t* topk, uint32_t* umask, int32_t* ucount,
+               sgqa_stream stream);
+
+/* Gathered-block causal GQA attention over the tile unions (Figure 3: the attention main path
+ * loads the uncompressed K/V of the chosen history blocks and, for the query's own block, only
+ * the positions the causal mask lets it see).
+ *   q      [N][Hq][D]  bf16
+ *   k, v   [G][N][D]   bf16  (head-major: one block of one group is B*D contiguous elements)
+ *   umask, ucount          from sgqa_union
+ *   out    [N][Hq][D]  bf16  out: for head h, group g = h / r, tile t = floor(i/Tq):
+ *          out[i][h] = sum_{j in J} softmax_j(sigma * <q[i][h], k[g][j]>) v[g][j],
+ *          J = { j <= i : floor(j/B) in U(t,g) }; fp32 softmax and accumulation, bf16 RNE output.
+ * No workspace (pass NULL/0). */
+int sgqa_attend(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k, const sgqa_bf16* v,
+                const uint32_t* umask, const int32_t* ucount, sgqa_bf16* out, void* ws,
+                size_t ws_bytes, sgqa_stream stream);
+
+/* Whole prefill layer path on one stream: compress -> index_topk -> union -> attend, with
+ * blk_k, topk, umask and ucount kept in the workspace (layouts as above). Arguments as in the
+ * single calls; out [N][Hq][D] bf16. Workspace: sgqa_workspace_size(p, SGQA_OP_PREFILL). */
+int sgqa_prefill(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k, const sgqa_bf16* v,
+                 const sgqa_bf16* idx_q, const float* idx_w, const sgqa_bf16* idx_k,
+                 sgqa_bf16* out, void* ws, size_t ws_bytes, sgqa_stream stream);
+
+/* Single-token decode over a cache: the same selection for the last position and no union,
+ * since the pages introduce the union only for prefill ("Efficient implementation of sparse
+ * attention").
+ * For every sequence s the query sits at position i = L-1 of its cache; candidates are the
+ * blocks b < c = floor((L-1)/B); the attended tokens are those of Sel(s,g) plus the own-block
+ * tokens c*B .. L-1.
+ *   q          [S][Hq][D]          bf16
+ *   k_cache,
+ *   v_cache    [S][G][L][D]        bf16
+ *   blk_k      [S][floor(L/B)][d_I] bf16  block keys of the cached index keys (sgqa_compress)
+ *   idx_q      [S][G][H_I][d_I]    bf16
+ *   idx_w      [G][H_I]            fp32
+ *   topk_out   [S][G][K_B]         int32  optional (NULL = not written): Sel, ascending, -1 pad
+ *   out        [S][Hq][D]          bf16
+ * Workspace: sgqa_workspace_size(p, SGQA_OP_DECODE). */
+int sgqa_decode(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k_cache,
+                const sgqa_bf16* v_cache, const sgqa_bf16* blk_k, const sgqa_bf16* idx_q,
+                const float* idx_w, int32_t* topk_out, sgqa_bf16* out, void* ws, size_t ws_bytes,
+                sgqa_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGQA_H */

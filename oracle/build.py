@@ -1,0 +1,26 @@
+"""Build liboracle.so from sgqa_oracle.c with the host C compiler (test infrastructure only)."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def build(verbose: bool = False) -> str:
+    src = os.path.join(_HERE, "sgqa_oracle.c")
+    out = os.path.join(_HERE, "liboracle.so")
+    tmp = out + ".tmp"
+    # -ffp-contract=off: every product and sum is rounded as written (no fused multiply-add).
+    cmd = ["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared",
+           "-Wall", "-Wextra", "-o", tmp, src, "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))
