@@ -1,0 +1,89 @@
+// compress.hip -- block compression of the shared index keys.
+//
+// "Inside Step 5 Preview", section Sparse GQA, paragraph "Reducing indexer's cost" and Figure 3:
+// the index keys of B adjacent positions are merged into one block key. Here the merge is the
+// mean, rounded once to bf16: kbar[s][b][d] = bf16_rne((sum_{j<B} ki[s][b*B+j][d]) * (1/B)),
+// summed in fp32 in ascending j (1/B is a power of two, so the scaling is exact).
+//
+// HBM-bound: every thread owns 8 consecutive dims (16 B) of one block and streams the B rows of
+// that block; 8 lanes cover one 128-byte row, so each wave reads 8 blocks' rows with full 128-byte
+// segments and writes 8 whole 128-byte block keys.
+#include "sgqa_device.hpp"
+#include "sgqa_internal.hpp"
+
+namespace sgqa {
+
+template <int BLOCK>
+__global__ __launch_bounds__(256) void k_compress(const uint16_t* __restrict__ ki, uint16_t* __restrict__ kbar,
+                                                  int n_tokens, int n_blocks, int idx_dim, int dyn_block,
+                                                  long long n_items) {
+  const int block = BLOCK > 0 ? BLOCK : dyn_block;
+  const int chunks = idx_dim >> 3;  // 16-byte pieces per row
+  const float inv = 1.0f / (float)block;
+  for (long long item = (long long)blockIdx.x * blockDim.x + threadIdx.x; item < n_items;
+       item += (long long)gridDim.x * blockDim.x) {
+    const int c = (int)(item % chunks);
+    const long long sb = item / chunks;  // s * n_blocks + b
+    const long long s = sb / n_blocks;
+    const long long b = sb - s * n_blocks;
+    const uint16_t* src = ki + ((s * n_tokens + b * block) * idx_dim + c * 8);
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+    if (BLOCK > 0) {
+      u32x4 rows[BLOCK > 0 ? BLOCK : 1];
+#pragma unroll
+      for (int j = 0; j < BLOCK; ++j) rows[j] = *reinterpret_cast<const u32x4*>(src + (long long)j * idx_dim);
+#pragma unroll
+      for (int j = 0; j < BLOCK; ++j) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += bf16_bits_to_f32(rows[j][e] & 0xFFFFu);
+          acc[2 * e + 1] += bf16_bits_to_f32(rows[j][e] >> 16);
+        }
+      }
+    } else {
+      for (int j = 0; j < block; ++j) {
+        u32x4 r = *reinterpret_cast<const u32x4*>(src + (long long)j * idx_dim);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += bf16_bits_to_f32(r[e] & 0xFFFFu);
+          acc[2 * e + 1] += bf16_bits_to_f32(r[e] >> 16);
+        }
+      }
+    }
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+    *reinterpret_cast<u32x4*>(kbar + (sb * idx_dim + c * 8)) = o;
+  }
+}
+
+hipError_t launch_compress(const uint16_t* ki, uint16_t* kbar, int n_seqs, int n_tokens, int idx_dim, int block,
+                           hipStream_t stream) {
+  const int n_blocks = n_tokens / block;
+  const long long n_items = (long long)n_seqs * n_blocks * (idx_dim / 8);
+  if (n_items == 0) return hipSuccess;
+  const int threads = 256;
+  long long grid = (n_items + threads - 1) / threads;
+  if (grid > 1 << 20) grid = 1 << 20;
+#define SGQA_COMPRESS_CASE(BV)                                                                             \
+  case BV:                                                                                                 \
+    hipLaunchKernelGGL(k_compress<BV>, dim3((unsigned)grid), dim3(threads), 0, stream, ki, kbar, n_tokens, \
+                       n_blocks, idx_dim, block, n_items);                                                 \
+    break;
+  switch (block) {
+    SGQA_COMPRESS_CASE(1)
+    SGQA_COMPRESS_CASE(2)
+    SGQA_COMPRESS_CASE(4)
+    SGQA_COMPRESS_CASE(8)
+    SGQA_COMPRESS_CASE(16)
+    default:
+      hipLaunchKernelGGL(k_compress<0>, dim3((unsigned)grid), dim3(threads), 0, stream, ki, kbar, n_tokens, n_blocks,
+                         idx_dim, block, n_items);
+  }
+#undef SGQA_COMPRESS_CASE
+  return hipGetLastError();
+}
+
+}  // namespace sgqa

@@ -1,0 +1,311 @@
+// sgqa_api.hip -- the C ABI of libsgqa (declared in include/sgqa.h): host-side validation,
+// workspace carving and kernel launches. Nothing here allocates, copies or synchronizes.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <string.h>
+
+#include "../../include/sgqa.h"
+#include "sgqa_internal.hpp"
+
+namespace sgqa {
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+int g_lds_max[kMaxDevices];  // 0 = not queried yet
+int g_is_gfx950[kMaxDevices];  // 0 = unknown, 1 = yes, -1 = no
+
+int current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  return (dev >= 0 && dev < kMaxDevices) ? dev : -1;
+}
+
+}  // namespace
+
+int max_lds_per_block() {
+  const int dev = current_device();
+  if (dev < 0) return 65536;
+  if (g_lds_max[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0) v = 65536;
+    g_lds_max[dev] = v;
+  }
+  return g_lds_max[dev];
+}
+
+namespace {
+
+bool device_ok() {
+  const int dev = current_device();
+  if (dev < 0) return false;
+  if (g_is_gfx950[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return false;
+    g_is_gfx950[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+  }
+  return g_is_gfx950[dev] == 1;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0u; }
+
+size_t round_up(size_t x) { return (x + 255) / 256 * 256; }
+
+bool is_pow2_le64(int b) { return b >= 1 && b <= 64 && (b & (b - 1)) == 0; }
+
+int kb_of(const sgqa_params* p) { return p->topk_tokens / p->block; }
+
+float scale_of(const sgqa_params* p) {
+  return p->softmax_scale > 0.0f ? p->softmax_scale : (float)(1.0 / sqrt((double)p->head_dim));
+}
+
+// Checks shared by the calls; `need` selects which groups of fields matter.
+enum { NEED_INDEX = 1, NEED_ATTN = 2, NEED_SELECT = 4, NEED_UNION = 8, NEED_LIST = 16, NEED_DSELECT = 32 };
+
+int check_params(const sgqa_params* p, int need, bool prefill) {
+  if (!p) return SGQA_ERR_NULL;
+  if (p->n_tokens < 1 || p->n_seqs < 1) return SGQA_ERR_SHAPE;
+  if (prefill && p->n_seqs != 1) return SGQA_ERR_SHAPE;
+  if (!is_pow2_le64(p->block)) return SGQA_ERR_SHAPE;
+  if (need & NEED_INDEX) {
+    if (p->idx_dim != 64) return SGQA_ERR_SHAPE;
+  }
+  if (need & (NEED_SELECT | NEED_ATTN | NEED_UNION)) {
+    if (p->n_kv_heads < 1) return SGQA_ERR_SHAPE;
+    if (p->topk_tokens < p->block || p->topk_tokens % p->block != 0) return SGQA_ERR_SHAPE;
+    if (kb_of(p) > 2048) return SGQA_ERR_SHAPE;
+  }
+  if (need & NEED_SELECT) {
+    if (p->idx_heads != 4 || p->idx_dim != 64) return SGQA_ERR_SHAPE;
+    if (p->n_kv_heads > 16) return SGQA_ERR_SHAPE;
+    if (index_topk_lds_min(kb_of(p)) > kGfx950LdsBytes) return SGQA_ERR_SHAPE;
+  }
+  if (need & NEED_DSELECT) {
+    if (decode_select_lds(p->n_kv_heads, kb_of(p)) > kGfx950LdsBytes) return SGQA_ERR_SHAPE;
+  }
+  if (need & NEED_UNION) {
+    if (p->union_tile < 1) return SGQA_ERR_SHAPE;
+  }
+  if (need & NEED_ATTN) {
+    if (p->head_dim != 128) return SGQA_ERR_SHAPE;
+    if (p->n_q_heads < 1 || p->n_q_heads % p->n_kv_heads != 0) return SGQA_ERR_SHAPE;
+    if (p->n_q_heads / p->n_kv_heads > 16) return SGQA_ERR_SHAPE;
+  }
+  if (need & NEED_LIST) {
+    // Prefill attention keeps the tile's ascending block list as 16-bit ids in LDS.
+    if ((long long)(p->n_tokens + p->block - 1) / p->block > 32768) return SGQA_ERR_SHAPE;
+    if (attend_lds_bytes_for(p->n_tokens, p->block) > kGfx950LdsBytes) return SGQA_ERR_SHAPE;
+  }
+  return SGQA_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? SGQA_OK : SGQA_ERR_HIP; }
+
+struct PrefillWs {
+  uint16_t* kbar;
+  int32_t* topk;
+  uint32_t* umask;
+  int32_t* ucount;
+  size_t bytes;
+};
+
+PrefillWs prefill_layout(const sgqa_params* p, void* ws) {
+  const long long N = p->n_tokens, G = p->n_kv_heads;
+  const long long NB = N / p->block, T = (N + p->union_tile - 1) / p->union_tile;
+  const long long nbc = (N + p->block - 1) / p->block, W = (nbc + 31) / 32;
+  size_t off = 0;
+  PrefillWs l;
+  uint8_t* b = reinterpret_cast<uint8_t*>(ws);
+  l.kbar = reinterpret_cast<uint16_t*>(b ? b + off : nullptr);
+  off += round_up((size_t)NB * p->idx_dim * 2);
+  l.topk = reinterpret_cast<int32_t*>(b ? b + off : nullptr);
+  off += round_up((size_t)G * N * kb_of(p) * 4);
+  l.umask = reinterpret_cast<uint32_t*>(b ? b + off : nullptr);
+  off += round_up((size_t)G * T * W * 4);
+  l.ucount = reinterpret_cast<int32_t*>(b ? b + off : nullptr);
+  off += round_up((size_t)G * T * 4);
+  l.bytes = off;
+  return l;
+}
+
+struct DecodeWs {
+  int32_t* sel;
+  void* select_ws;
+  void* part;
+  size_t bytes;
+};
+
+DecodeWs decode_layout(const sgqa_params* p, void* ws) {
+  const int kb = kb_of(p);
+  size_t off = 0;
+  DecodeWs l;
+  uint8_t* b = reinterpret_cast<uint8_t*>(ws);
+  l.sel = reinterpret_cast<int32_t*>(b ? b + off : nullptr);
+  off += round_up((size_t)p->n_seqs * p->n_kv_heads * kb * 4);
+  l.select_ws = b ? b + off : nullptr;
+  off += round_up(decode_select_ws_bytes(p->n_seqs, p->n_tokens, p->n_kv_heads, p->block, kb));
+  l.part = b ? b + off : nullptr;
+  off += round_up(decode_attend_part_bytes(p->n_seqs, p->n_q_heads, decode_split_count(kb)));
+  l.bytes = off;
+  return l;
+}
+
+}  // namespace
+
+}  // namespace sgqa
+
+using namespace sgqa;
+
+extern "C" {
+
+int sgqa_abi_version(void) { return SGQA_ABI_VERSION; }
+
+const char* sgqa_status_string(int status) {
+  switch (status) {
+    case SGQA_OK:
+      return "ok";
+    case SGQA_ERR_NULL:
+      return "a required pointer is NULL";
+    case SGQA_ERR_SHAPE:
+      return "unsupported or inconsistent sizes";
+    case SGQA_ERR_ALIGN:
+      return "a tensor pointer is not 16-byte aligned";
+    case SGQA_ERR_WORKSPACE:
+      return "workspace missing or too small";
+    case SGQA_ERR_DEVICE:
+      return "the current device is not a gfx950 GPU";
+    case SGQA_ERR_HIP:
+      return "the HIP runtime reported an error while launching";
+    default:
+      return "unknown status";
+  }
+}
+
+int sgqa_workspace_size(const sgqa_params* p, int op, size_t* bytes) {
+  if (!bytes || !p) return SGQA_ERR_NULL;
+  int st = SGQA_OK;
+  switch (op) {
+    case SGQA_OP_COMPRESS:
+      st = check_params(p, NEED_INDEX, false);
+      if (st == SGQA_OK) *bytes = 0;
+      return st;
+    case SGQA_OP_INDEX_TOPK:
+      st = check_params(p, NEED_SELECT, true);
+      if (st == SGQA_OK) *bytes = 0;
+      return st;
+    case SGQA_OP_UNION:
+      st = check_params(p, NEED_UNION, true);
+      if (st == SGQA_OK) *bytes = 0;
+      return st;
+    case SGQA_OP_ATTEND:
+      st = check_params(p, NEED_ATTN | NEED_UNION | NEED_LIST, true);
+      if (st == SGQA_OK) *bytes = 0;
+      return st;
+    case SGQA_OP_PREFILL:
+      st = check_params(p, NEED_INDEX | NEED_SELECT | NEED_UNION | NEED_ATTN | NEED_LIST, true);
+      if (st == SGQA_OK) *bytes = prefill_layout(p, nullptr).bytes;
+      return st;
+    case SGQA_OP_DECODE:
+      st = check_params(p, NEED_INDEX | NEED_SELECT | NEED_DSELECT | NEED_ATTN, false);
+      if (st == SGQA_OK) *bytes = decode_layout(p, nullptr).bytes;
+      return st;
+    default:
+      return SGQA_ERR_SHAPE;
+  }
+}
+
+int sgqa_compress(const sgqa_params* p, const sgqa_bf16* idx_k, sgqa_bf16* blk_k, sgqa_stream stream) {
+  int st = check_params(p, NEED_INDEX, false);
+  if (st) return st;
+  if (!idx_k || !blk_k) return SGQA_ERR_NULL;
+  if (!aligned16(idx_k) || !aligned16(blk_k)) return SGQA_ERR_ALIGN;
+  if (!device_ok()) return SGQA_ERR_DEVICE;
+  return status_of(launch_compress(idx_k, blk_k, p->n_seqs, p->n_tokens, p->idx_dim, p->block, (hipStream_t)stream));
+}
+
+int sgqa_index_topk(const sgqa_params* p, const sgqa_bf16* idx_q, const float* idx_w, const sgqa_bf16* blk_k,
+                    int32_t* topk, void* ws, size_t ws_bytes, sgqa_stream stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int st = check_params(p, NEED_SELECT, true);
+  if (st) return st;
+  if (!idx_q || !idx_w || !topk || (!blk_k && p->n_tokens >= p->block)) return SGQA_ERR_NULL;
+  if (!aligned16(idx_q) || !aligned16(idx_w) || !aligned16(blk_k) || !aligned16(topk)) return SGQA_ERR_ALIGN;
+  if (!device_ok()) return SGQA_ERR_DEVICE;
+  return status_of(launch_index_topk(idx_q, idx_w, blk_k, topk, p->n_tokens, p->n_kv_heads, p->block, kb_of(p),
+                                     (hipStream_t)stream));
+}
+
+int sgqa_union(const sgqa_params* p, const int32_t* topk, uint32_t* umask, int32_t* ucount, sgqa_stream stream) {
+  int st = check_params(p, NEED_UNION, true);
+  if (st) return st;
+  if (!topk || !umask || !ucount) return SGQA_ERR_NULL;
+  if (!aligned16(topk) || !aligned16(umask) || !aligned16(ucount)) return SGQA_ERR_ALIGN;
+  if (!device_ok()) return SGQA_ERR_DEVICE;
+  return status_of(launch_union(topk, umask, ucount, p->n_tokens, p->n_kv_heads, p->block, kb_of(p), p->union_tile,
+                                (hipStream_t)stream));
+}
+
+int sgqa_attend(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k, const sgqa_bf16* v,
+                const uint32_t* umask, const int32_t* ucount, sgqa_bf16* out, void* ws, size_t ws_bytes,
+                sgqa_stream stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int st = check_params(p, NEED_ATTN | NEED_UNION | NEED_LIST, true);
+  if (st) return st;
+  if (!q || !k || !v || !umask || !ucount || !out) return SGQA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(umask) || !aligned16(ucount) || !aligned16(out))
+    return SGQA_ERR_ALIGN;
+  if (!device_ok()) return SGQA_ERR_DEVICE;
+  return status_of(launch_attend(q, k, v, umask, ucount, out, p->n_tokens, p->n_q_heads, p->n_kv_heads, p->block,
+                                 p->union_tile, scale_of(p), (hipStream_t)stream));
+}
+
+int sgqa_prefill(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k, const sgqa_bf16* v,
+                 const sgqa_bf16* idx_q, const float* idx_w, const sgqa_bf16* idx_k, sgqa_bf16* out, void* ws,
+                 size_t ws_bytes, sgqa_stream stream) {
+  int st = check_params(p, NEED_INDEX | NEED_SELECT | NEED_UNION | NEED_ATTN | NEED_LIST, true);
+  if (st) return st;
+  if (!q || !k || !v || !idx_q || !idx_w || !idx_k || !out) return SGQA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(idx_q) || !aligned16(idx_w) ||
+      !aligned16(idx_k) || !aligned16(out) || !aligned16(ws))
+    return SGQA_ERR_ALIGN;
+  const PrefillWs l = prefill_layout(p, ws);
+  if (!ws || ws_bytes < l.bytes) return SGQA_ERR_WORKSPACE;
+  if (!device_ok()) return SGQA_ERR_DEVICE;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_compress(idx_k, l.kbar, 1, p->n_tokens, p->idx_dim, p->block, s);
+  if (e == hipSuccess)
+    e = launch_index_topk(idx_q, idx_w, l.kbar, l.topk, p->n_tokens, p->n_kv_heads, p->block, kb_of(p), s);
+  if (e == hipSuccess)
+    e = launch_union(l.topk, l.umask, l.ucount, p->n_tokens, p->n_kv_heads, p->block, kb_of(p), p->union_tile, s);
+  if (e == hipSuccess)
+    e = launch_attend(q, k, v, l.umask, l.ucount, out, p->n_tokens, p->n_q_heads, p->n_kv_heads, p->block,
+                      p->union_tile, scale_of(p), s);
+  return status_of(e);
+}
+
+int sgqa_decode(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k_cache, const sgqa_bf16* v_cache,
+                const sgqa_bf16* blk_k, const sgqa_bf16* idx_q, const float* idx_w, int32_t* topk_out,
+                sgqa_bf16* out, void* ws, size_t ws_bytes, sgqa_stream stream) {
+  int st = check_params(p, NEED_INDEX | NEED_SELECT | NEED_DSELECT | NEED_ATTN, false);
+  if (st) return st;
+  if (!q || !k_cache || !v_cache || !idx_q || !idx_w || !out || (!blk_k && p->n_tokens > p->block))
+    return SGQA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(blk_k) || !aligned16(idx_q) ||
+      !aligned16(idx_w) || !aligned16(topk_out) || !aligned16(out) || !aligned16(ws))
+    return SGQA_ERR_ALIGN;
+  const DecodeWs l = decode_layout(p, ws);
+  if (!ws || ws_bytes < l.bytes) return SGQA_ERR_WORKSPACE;
+  if (!device_ok()) return SGQA_ERR_DEVICE;
+  hipStream_t s = (hipStream_t)stream;
+  const int kb = kb_of(p);
+  hipError_t e = launch_decode_select(idx_q, idx_w, blk_k, l.sel, topk_out, l.select_ws, p->n_seqs, p->n_tokens,
+                                      p->n_kv_heads, p->block, kb, s);
+  if (e == hipSuccess)
+    e = launch_decode_attend(q, k_cache, v_cache, l.sel, l.part, out, p->n_seqs, p->n_tokens, p->n_q_heads,
+                             p->n_kv_heads, p->block, kb, scale_of(p), s);
+  return status_of(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+// sgqa_device.hpp -- device-side building blocks shared by the gfx950 kernels of libsgqa.
+//
+// Only the HIP library includes this file. It fixes the register layouts of the two bf16 matrix
+// instructions used here (CDNA4 v_mfma_f32_16x16x32_bf16 and v_mfma_f32_32x32x16_bf16, wave64):
+//
+//   16x16x32: A operand lane l holds row (l % 16), 8 consecutive k starting at 8 * (l / 16);
+//             B operand lane l holds column (l % 16), the same 8 k;
+//             result lane l holds column (l % 16), rows 4 * (l / 16) + 0..3.
+//   32x32x16: A operand lane l holds row (l % 32), 8 consecutive k starting at 8 * (l / 32);
+//             B operand lane l holds column (l % 32), the same 8 k;
+//             result register j of lane l holds column (l % 32), row 8 * (j / 4) + 4 * (l / 32) + j % 4.
+//
+// Only the row/column placement matters for correctness: A and B always use the same k order, so
+// any consistent permutation of k inside a step gives the same contraction.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sgqa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (lowered to v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+  __bf16 b = (__bf16)x;
+  return (uint32_t)__builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// Order-preserving unsigned key of an fp32 score: a larger score gives a larger key; -0 and +0 map
+// to the same key. (Non-negative floats get the top bit set; negative floats are bit-inverted.)
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if ((u << 1) == 0u) u = 0u;  // -0 -> +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int l = lane_id();
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+__device__ __forceinline__ int popc64(uint64_t x) { return __popcll(x); }
+
+template <typename T>
+__device__ __forceinline__ T readlane(T v, int l) {
+  return __shfl(v, l, 64);
+}
+
+// Inclusive suffix sum across the 64 lanes: lane l gets sum_{l' >= l} v[l'].
+__device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    uint32_t o = __shfl_down(v, off, 64);
+    if (l + off < 64) v += o;
+  }
+  return v;
+}
+
+// Inclusive prefix sum across the 64 lanes.
+__device__ __forceinline__ uint32_t wave_prefix_sum(uint32_t v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    uint32_t o = __shfl_up(v, off, 64);
+    if (l >= off) v += o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+}  // namespace sgqa

@@ -1,0 +1,53 @@
+// sgqa_internal.hpp -- launch functions shared between the kernel files and the C-ABI layer of
+// libsgqa. Every launcher only enqueues work on `stream` and returns hipGetLastError(); argument
+// validation happens in sgqa_api.hip before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sgqa {
+
+// Block compression: ki [S][N][dI] -> kbar [S][N/B][dI].
+hipError_t launch_compress(const uint16_t* ki, uint16_t* kbar, int n_seqs, int n_tokens, int idx_dim, int block,
+                           hipStream_t stream);
+
+// Per-query block top-k for a prefill: qi [N][G][4][64], w [G][4], kbar [N/B][64] -> topk [G][N][kb].
+hipError_t launch_index_topk(const uint16_t* qi, const float* w, const uint16_t* kbar, int32_t* topk, int n_tokens,
+                             int n_groups, int block, int kb, hipStream_t stream);
+
+// Tile union: topk [G][N][kb] -> umask [G][T][W], ucount [G][T].
+hipError_t launch_union(const int32_t* topk, uint32_t* umask, int32_t* ucount, int n_tokens, int n_groups, int block,
+                        int kb, int tile, hipStream_t stream);
+
+// Gathered-block prefill attention over the tile unions.
+hipError_t launch_attend(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint32_t* umask,
+                         const int32_t* ucount, uint16_t* out, int n_tokens, int n_q_heads, int n_groups, int block,
+                         int tile, float scale, hipStream_t stream);
+
+// Decode selection: K-bar cache [S][L/B][64], qi [S][G][4][64] -> sel [S][G][kb] (and topk_out if not
+// null). Uses decode_select_ws_bytes() of workspace.
+size_t decode_select_ws_bytes(int n_seqs, int n_tokens, int n_groups, int block, int kb);
+hipError_t launch_decode_select(const uint16_t* qi, const float* w, const uint16_t* kbar, int32_t* sel,
+                                int32_t* topk_out, void* ws, int n_seqs, int n_tokens, int n_groups, int block, int kb,
+                                hipStream_t stream);
+
+// Decode attention over Sel + own block: split-K partials (decode_attend_part_bytes of workspace)
+// and a fixed-order combine into out [S][Hq][D].
+size_t decode_attend_part_bytes(int n_seqs, int n_q_heads, int n_split);
+int decode_split_count(int kb);
+hipError_t launch_decode_attend(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, const int32_t* sel,
+                                void* part_ws, uint16_t* out, int n_seqs, int ctx, int n_q_heads, int n_groups,
+                                int block, int kb, float scale, hipStream_t stream);
+
+// LDS a launch needs (validation rejects shapes that do not fit before anything is enqueued).
+size_t index_topk_lds_min(int kb);
+size_t decode_select_lds(int n_groups, int kb);
+size_t attend_lds_bytes_for(int n_tokens, int block);
+constexpr size_t kGfx950LdsBytes = 160 * 1024;
+
+// Largest dynamic LDS allocation one workgroup may use on the current device (bytes).
+int max_lds_per_block();
+
+}  // namespace sgqa

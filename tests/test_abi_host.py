@@ -1,0 +1,121 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+The library must load, export every function that include/sgqa.h declares, report its version and
+status texts, size workspaces on the host, and reject bad arguments with the documented status
+before touching the device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sgqa.h")
+
+
+@pytest.fixture(scope="module")
+def sg():
+    import block_sparse_long_sgqa_amd as sg
+
+    if not os.path.exists(sg.LIB_PATH):
+        from block_sparse_long_sgqa_amd import build
+
+        build.build()
+    sg.lib()
+    return sg
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(sgqa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_calls():
+    names = declared_functions()
+    for n in ("sgqa_compress", "sgqa_index_topk", "sgqa_union", "sgqa_attend", "sgqa_prefill", "sgqa_decode",
+              "sgqa_workspace_size", "sgqa_status_string", "sgqa_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(sg):
+    lib = ctypes.CDLL(sg.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(sg.EXPORTED)
+
+
+def test_abi_version_and_status_strings(sg):
+    assert sg.lib().sgqa_abi_version() == 1
+    for code in range(7):
+        assert len(sg.status_string(code)) > 0
+    assert sg.status_string(0) == "ok"
+    assert sg.status_string(99) == "unknown status"
+
+
+def _p(**kw):
+    import block_sparse_long_sgqa_amd as sg
+
+    base = dict(n_tokens=32768, n_q_heads=64, n_kv_heads=8, block=8, topk_tokens=4096, union_tile=64)
+    base.update(kw)
+    return sg.Params(**base)
+
+
+def test_workspace_sizes_match_layout(sg):
+    p = _p()
+    assert sg.workspace_size(p, sg.SGQA_OP_COMPRESS) == 0
+    assert sg.workspace_size(p, sg.SGQA_OP_INDEX_TOPK) == 0
+    assert sg.workspace_size(p, sg.SGQA_OP_ATTEND) == 0
+    r = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    N, G, kb, T, W = 32768, 8, 512, 512, 128
+    want = r(N // 8 * 64 * 2) + r(G * N * kb * 4) + r(G * T * W * 4) + r(G * T * 4)
+    assert sg.workspace_size(p, sg.SGQA_OP_PREFILL) == want
+    d = _p(n_tokens=262144, n_seqs=32, union_tile=1)
+    assert sg.workspace_size(d, sg.SGQA_OP_DECODE) > 32 * 8 * 512 * 4
+
+
+@pytest.mark.parametrize("kw", [
+    dict(head_dim=64), dict(idx_heads=3), dict(idx_dim=32), dict(block=3), dict(block=128),
+    dict(topk_tokens=100), dict(topk_tokens=0), dict(topk_tokens=8 * 4096), dict(n_q_heads=60),
+    dict(union_tile=0), dict(n_tokens=0), dict(n_seqs=2), dict(n_kv_heads=0),
+    dict(n_q_heads=8 * 32, n_kv_heads=8), dict(n_tokens=32768 * 8 + 8),
+])
+def test_bad_shapes_are_rejected_before_any_launch(sg, kw):
+    p = _p(**kw)
+    out = ctypes.c_size_t(0)
+    st = sg.lib().sgqa_workspace_size(ctypes.byref(p.c()), sg.SGQA_OP_PREFILL, ctypes.byref(out))
+    assert st == sg.SGQA_ERR_SHAPE
+    nul = ctypes.c_void_p(0)
+    buf = (ctypes.c_uint8 * 64)()
+    a = ctypes.c_void_p((ctypes.addressof(buf) + 15) // 16 * 16)
+    st = sg.lib().sgqa_prefill(ctypes.byref(p.c()), a, a, a, a, a, a, a, a, 1 << 40, nul)
+    assert st == sg.SGQA_ERR_SHAPE
+
+
+def test_null_and_alignment_errors(sg):
+    lib = sg.lib()
+    p = _p()
+    nul = ctypes.c_void_p(0)
+    assert lib.sgqa_workspace_size(None, 0, ctypes.byref(ctypes.c_size_t())) == sg.SGQA_ERR_NULL
+    assert lib.sgqa_compress(None, nul, nul, nul) == sg.SGQA_ERR_NULL
+    assert lib.sgqa_compress(ctypes.byref(p.c()), nul, nul, nul) == sg.SGQA_ERR_NULL
+    buf = (ctypes.c_uint8 * 64)()
+    a = ctypes.c_void_p((ctypes.addressof(buf) + 15) // 16 * 16)
+    mis = ctypes.c_void_p(a.value + 4)
+    assert lib.sgqa_compress(ctypes.byref(p.c()), mis, a, nul) == sg.SGQA_ERR_ALIGN
+    assert lib.sgqa_union(ctypes.byref(p.c()), a, mis, a, nul) == sg.SGQA_ERR_ALIGN
+    assert lib.sgqa_attend(ctypes.byref(p.c()), a, a, a, a, a, nul, nul, 0, nul) == sg.SGQA_ERR_NULL
+    # workspace too small is reported before the device is queried
+    assert lib.sgqa_prefill(ctypes.byref(p.c()), a, a, a, a, a, a, a, a, 16, nul) == sg.SGQA_ERR_WORKSPACE
+    d = _p(n_tokens=4096, n_seqs=4, union_tile=1)
+    assert lib.sgqa_decode(ctypes.byref(d.c()), a, a, a, a, a, a, nul, a, a, 16, nul) == sg.SGQA_ERR_WORKSPACE
+
+
+def test_binding_refuses_host_tensors(sg):
+    import torch
+
+    p = _p(n_tokens=64, n_q_heads=8, n_kv_heads=1, topk_tokens=64, union_tile=16)
+    ki = torch.zeros((64, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        sg.sgqa_compress(p, ki, torch.zeros((8, 64), dtype=torch.bfloat16))

@@ -1,0 +1,219 @@
+"""GPU parity of every C-ABI call against the CPU oracle, at sizes the oracle finishes in seconds.
+
+Bar: block keys, selections and unions bit-exact (integer-valued indexer inputs make fp32 scores
+exact); attention within max-abs 1e-2 and mean-abs 1e-3 of the fp64 oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+from tests.gpu_common import (OracleChain, assert_close_attention, bits, params_of, say, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sg():
+    import block_sparse_long_sgqa_amd as sg
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    sg.lib()
+    return sg
+
+
+# Small workloads: several tiles, ragged tails, every block size of interest.
+SMALL = {
+    "tiny": datagen.TINY,
+    "gqa_ragged": datagen.PREFILL.replace(name="gqa_ragged", n_tokens=3000 + 5, topk_tokens=512, union_tile=64),
+    "b4_tile24": datagen.PREFILL.replace(name="b4_tile24", n_tokens=1531, n_q_heads=16, n_kv_heads=2, block=4,
+                                         topk_tokens=256, union_tile=24),
+    "b1_token": datagen.PREFILL.replace(name="b1_token", n_tokens=1100, n_q_heads=8, n_kv_heads=1, block=1,
+                                        topk_tokens=200, union_tile=16),
+    "b16_iid": datagen.PREFILL.replace(name="b16_iid", n_tokens=2048 + 17, n_q_heads=32, n_kv_heads=4, block=16,
+                                       topk_tokens=512, union_tile=32, qi_mode="iid"),
+    "tile1": datagen.PREFILL.replace(name="tile1", n_tokens=700, n_q_heads=8, n_kv_heads=1, topk_tokens=128,
+                                     union_tile=1),
+    "b64_r4": datagen.PREFILL.replace(name="b64_r4", n_tokens=4096 + 64 + 3, n_q_heads=16, n_kv_heads=4, block=64,
+                                      topk_tokens=1024, union_tile=128),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_compress_bit_exact(sg, name):
+    wl = SMALL[name]
+    p = params_of(wl)
+    say(f"compress {name} N={p.n_tokens} B={p.block}")
+    x = datagen.prefill_inputs(wl)
+    want = oracle.compress(bits(x["ki"]), p.block)
+    ki = x["ki"].cuda()
+    out = torch.empty((max(p.n_tokens // p.block, 1), p.idx_dim), dtype=torch.bfloat16, device="cuda")
+    sg.sgqa_compress(p, ki, out)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(out)[: p.n_tokens // p.block], want)
+
+
+def test_compress_multi_sequence_and_normal_data(sg):
+    # S sequences at once (the decode cache build); N(0,1) keys: the fp32 sum may round once more than
+    # the fp64 oracle, so at most one bf16 ulp apart, and identical on almost every element.
+    S, N, B = 3, 4096 + 24, 8
+    g = torch.Generator().manual_seed(5)
+    ki = torch.randn((S, N, 64), generator=g).to(torch.bfloat16)
+    want = oracle.compress(bits(ki), B)
+    p = sg.Params(n_tokens=N, n_q_heads=8, n_kv_heads=1, block=B, n_seqs=S)
+    out = torch.empty((S, N // B, 64), dtype=torch.bfloat16, device="cuda")
+    say("compress S=3 normal data")
+    sg.sgqa_compress(p, ki.cuda(), out)
+    torch.cuda.synchronize()
+    got = bits(out).astype(np.int32)
+    diff = np.abs(got - want.astype(np.int32))
+    assert diff.max() <= 1
+    assert (diff == 0).mean() > 0.99
+
+
+def run_topk(sg, p, xd, kbar_dev):
+    topk = torch.empty((p.n_kv_heads, p.n_tokens, p.kb), dtype=torch.int32, device="cuda")
+    sg.sgqa_index_topk(p, xd["qi"], xd["w"], kbar_dev, topk)
+    return topk
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_index_topk_bit_exact(sg, name):
+    wl = SMALL[name]
+    p = params_of(wl)
+    x = datagen.prefill_inputs(wl)
+    ch = OracleChain(x, p)
+    say(f"index_topk {name} N={p.n_tokens} G={p.n_kv_heads} B={p.block} kb={p.kb}")
+    xd = to_dev(x)
+    kbar = torch.from_numpy(ch.kbar.view(np.int16)).view(torch.bfloat16).cuda()
+    topk = run_topk(sg, p, xd, kbar)
+    torch.cuda.synchronize()
+    want = ch.topk()
+    np.testing.assert_array_equal(topk.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("case", ["zero_queries", "dense_k", "negative_weights", "all_equal_keys"])
+def test_index_topk_degenerate_cases(sg, case):
+    wl = datagen.PREFILL.replace(name=f"deg_{case}", n_tokens=2500, n_q_heads=16, n_kv_heads=2, topk_tokens=400,
+                                 union_tile=32)
+    if case == "dense_k":
+        wl = wl.replace(topk_tokens=4096)
+    x = datagen.prefill_inputs(wl)
+    if case == "zero_queries":
+        x["qi"] = torch.zeros_like(x["qi"])
+    if case == "negative_weights":
+        x["w"] = -x["w"]          # every score <= 0; -0 and +0 must tie
+    if case == "all_equal_keys":
+        x["ki"] = torch.ones_like(x["ki"])
+    p = params_of(wl)
+    ch = OracleChain(x, p)
+    say(f"index_topk degenerate {case}")
+    xd = to_dev(x)
+    kbar = torch.from_numpy(ch.kbar.view(np.int16)).view(torch.bfloat16).cuda()
+    topk = run_topk(sg, p, xd, kbar)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(topk.cpu().numpy(), ch.topk())
+
+
+@pytest.mark.parametrize("name", ["tiny", "gqa_ragged", "b4_tile24", "b1_token", "tile1"])
+def test_union_bit_exact(sg, name):
+    wl = SMALL[name]
+    p = params_of(wl)
+    x = datagen.prefill_inputs(wl)
+    ch = OracleChain(x, p)
+    sel = ch.topk()
+    want_mask, want_cnt = oracle.union(sel, p.n_tokens, p.block, p.union_tile)
+    say(f"union {name} T={p.n_tiles} W={p.n_words}")
+    umask = torch.empty((p.n_kv_heads, p.n_tiles, p.n_words), dtype=torch.int32, device="cuda")
+    ucount = torch.empty((p.n_kv_heads, p.n_tiles), dtype=torch.int32, device="cuda")
+    sg.sgqa_union(p, torch.from_numpy(sel).cuda(), umask, ucount)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(umask.cpu().numpy().view(np.uint32), want_mask)
+    np.testing.assert_array_equal(ucount.cpu().numpy(), want_cnt)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_attend_within_tolerance(sg, name):
+    wl = SMALL[name]
+    p = params_of(wl)
+    x = datagen.prefill_inputs(wl)
+    ch = OracleChain(x, p)
+    umask, ucount = oracle.union(ch.topk(), p.n_tokens, p.block, p.union_tile)
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([np.arange(0, 40), np.arange(p.n_tokens - 40, p.n_tokens),
+                                     rng.integers(0, p.n_tokens, 300)])).astype(np.int32)
+    want = oracle.attend(bits(x["q"]), bits(x["k"]), bits(x["v"]), umask, p.block, p.union_tile, rows=rows)
+    say(f"attend {name} N={p.n_tokens} Hq={p.n_q_heads} G={p.n_kv_heads} B={p.block} Tq={p.union_tile}")
+    xd = to_dev(x)
+    out = torch.empty((p.n_tokens, p.n_q_heads, p.head_dim), dtype=torch.bfloat16, device="cuda")
+    sg.sgqa_attend(p, xd["q"], xd["k"], xd["v"], torch.from_numpy(umask.view(np.int32)).cuda(),
+                   torch.from_numpy(ucount).cuda(), out)
+    torch.cuda.synchronize()
+    assert_close_attention(out[torch.from_numpy(rows).long().cuda()], want, f"attend {name}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "gqa_ragged", "b4_tile24", "b1_token"])
+def test_prefill_end_to_end(sg, name):
+    wl = SMALL[name]
+    p = params_of(wl)
+    x = datagen.prefill_inputs(wl)
+    ch = OracleChain(x, p)
+    umask, _ = oracle.union(ch.topk(), p.n_tokens, p.block, p.union_tile)
+    want = oracle.attend(bits(x["q"]), bits(x["k"]), bits(x["v"]), umask, p.block, p.union_tile)
+    say(f"prefill {name}")
+    xd = to_dev(x)
+    out = torch.empty((p.n_tokens, p.n_q_heads, p.head_dim), dtype=torch.bfloat16, device="cuda")
+    ws = sg.workspace(p, sg.SGQA_OP_PREFILL)
+    sg.sgqa_prefill(p, xd["q"], xd["k"], xd["v"], xd["qi"], xd["w"], xd["ki"], out, ws)
+    torch.cuda.synchronize()
+    assert_close_attention(out, want, f"prefill {name}")
+    # Determinism: a second run gives the same bits.
+    out2 = torch.empty_like(out)
+    sg.sgqa_prefill(p, xd["q"], xd["k"], xd["v"], xd["qi"], xd["w"], xd["ki"], out2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+def test_prefill_dense_when_k_covers_context(sg):
+    # k >= N: selection is everything, the path is dense causal GQA attention (oracle pinned to SDPA).
+    wl = datagen.PREFILL.replace(name="dense_e2e", n_tokens=1024 + 8, n_q_heads=16, n_kv_heads=2,
+                                 topk_tokens=2048, union_tile=64)
+    p = params_of(wl)
+    x = datagen.prefill_inputs(wl)
+    full = np.full((2, p.n_tokens, p.kb), -1, np.int32)
+    for i in range(p.n_tokens):
+        c = i // p.block
+        full[:, i, :c] = np.arange(c)
+    umask, _ = oracle.union(full, p.n_tokens, p.block, p.union_tile)
+    want = oracle.attend(bits(x["q"]), bits(x["k"]), bits(x["v"]), umask, p.block, p.union_tile)
+    say("prefill dense")
+    xd = to_dev(x)
+    out = torch.empty((p.n_tokens, p.n_q_heads, p.head_dim), dtype=torch.bfloat16, device="cuda")
+    ws = sg.workspace(p, sg.SGQA_OP_PREFILL)
+    sg.sgqa_prefill(p, xd["q"], xd["k"], xd["v"], xd["qi"], xd["w"], xd["ki"], out, ws)
+    torch.cuda.synchronize()
+    assert_close_attention(out, want, "prefill dense")
+
+
+@pytest.mark.parametrize("L,S,G,kb_tokens,B", [(203, 3, 2, 48, 8), (4096 + 5, 4, 8, 4096, 8), (9000, 2, 8, 2048, 8),
+                                               (3000, 2, 1, 256, 4)])
+def test_decode_matches_oracle(sg, L, S, G, kb_tokens, B):
+    wl = datagen.DECODE.replace(name=f"dec_{L}_{S}_{G}", n_tokens=L, n_seqs=S, n_q_heads=8 * G, n_kv_heads=G,
+                                topk_tokens=kb_tokens, block=B)
+    p = params_of(wl)
+    x = datagen.decode_inputs(wl)
+    kbar = oracle.compress(bits(x["ki_cache"]), B)
+    want_sel, want_out = oracle.decode(x["q"], x["k_cache"], x["v_cache"], kbar, x["qi"], x["w"], B, p.kb)
+    say(f"decode L={L} S={S} G={G} kb={p.kb} B={B}")
+    xd = to_dev(x)
+    blk = torch.empty((S, L // B, 64), dtype=torch.bfloat16, device="cuda")
+    sg.sgqa_compress(p, xd["ki_cache"], blk)
+    out = torch.empty((S, p.n_q_heads, 128), dtype=torch.bfloat16, device="cuda")
+    topk = torch.empty((S, G, p.kb), dtype=torch.int32, device="cuda")
+    ws = sg.workspace(p, sg.SGQA_OP_DECODE)
+    sg.sgqa_decode(p, xd["q"], xd["k_cache"], xd["v_cache"], blk, xd["qi"], xd["w"], out, ws, topk_out=topk)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(blk), kbar)
+    np.testing.assert_array_equal(topk.cpu().numpy(), want_sel)
+    assert_close_attention(out, want_out, f"decode L={L}")
