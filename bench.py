@@ -1,0 +1,326 @@
+"""Throughput of the blockwise Sparse GQA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long_prefill_128k|prefill_32k]
+                    [--no-decode] [--no-cpu-baseline] [--copy-calibration]
+
+One step = one full-attention layer's prefill over the whole workload: compress -> index + top-k
+-> tile union -> gathered-block attention (the four kernels behind sgqa_prefill), on synthetic
+inputs already resident in HBM. `value` = prefill tokens per second. The same JSON line carries the
+per-stage times (HIP events on the launch stream), the roofline of the dominant kernel (attention
+on the matrix cores), the single-token decode step over the 262144-token cache (tokens/s and the
+HBM roofline of its gather) and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak (published)
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long_prefill_128k")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+def attended_pairs(umask, n_tokens: int, block: int, tile: int) -> int:
+    """sum over (i, g) of |J(i,g)|: causally visible tokens of the tile union (exact count)."""
+    import torch
+
+    G, T, W = umask.shape
+    shifts = torch.arange(32, device=umask.device, dtype=torch.int32)
+    total = 0
+    for g in range(G):
+        bitsel = ((umask[g].unsqueeze(-1) >> shifts) & 1).reshape(T, W * 32).to(torch.int32)
+        cum = torch.cumsum(bitsel, dim=1)  # blocks <= b in U
+        i = torch.arange(n_tokens, device=umask.device)
+        c = i // block
+        t = i // tile
+        below = torch.where(c > 0, cum[t, (c - 1).clamp(min=0)], torch.zeros_like(c, dtype=torch.int32))
+        total += int((below.to(torch.int64) * block + (i - c * block + 1)).sum())
+    return total
+
+
+class Timer:
+    """HIP events on the stream the library launches on (torch's current stream)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.marks = []
+
+    def mark(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.marks.append(e)
+
+    def spans(self):
+        return [a.elapsed_time(b) for a, b in zip(self.marks[:-1], self.marks[1:])]
+
+
+def bench_prefill(sg, datagen, torch, wl, steps, warmup):
+    p = sg.Params(n_tokens=wl.n_tokens, n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads, block=wl.block,
+                  topk_tokens=wl.topk_tokens, union_tile=wl.union_tile)
+    t0 = time.time()
+    x = datagen.prefill_inputs(wl, device="cuda")
+    torch.cuda.synchronize()
+    log(f"{wl.name}: inputs drawn on the GPU in {time.time() - t0:.1f}s")
+    o = sg.alloc_prefill_outputs(p)
+    ws = sg.workspace(p, sg.SGQA_OP_PREFILL)
+    out_full = torch.empty_like(o["out"])
+
+    def staged(timer=None):
+        if timer:
+            timer.mark()
+        sg.sgqa_compress(p, x["ki"], o["blk_k"])
+        if timer:
+            timer.mark()
+        sg.sgqa_index_topk(p, x["qi"], x["w"], o["blk_k"], o["topk"])
+        if timer:
+            timer.mark()
+        sg.sgqa_union(p, o["topk"], o["umask"], o["ucount"])
+        if timer:
+            timer.mark()
+        sg.sgqa_attend(p, x["q"], x["k"], x["v"], o["umask"], o["ucount"], o["out"])
+        if timer:
+            timer.mark()
+
+    def whole():
+        sg.sgqa_prefill(p, x["q"], x["k"], x["v"], x["qi"], x["w"], x["ki"], out_full, ws)
+
+    for _ in range(warmup):
+        whole()
+        staged()
+    torch.cuda.synchronize()
+    # Timed region 1: the whole layer through sgqa_prefill.
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
+        whole()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_step = ev0.elapsed_time(ev1) / steps
+    # Timed region 2: the same kernels through the single calls, with events between the stages.
+    stage_ms = [0.0, 0.0, 0.0, 0.0]
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        tm = Timer(torch)
+        staged(tm)
+        torch.cuda.synchronize()
+        for k, v in enumerate(tm.spans()):
+            stage_ms[k] += v / steps
+    same = bool(torch.equal(out_full.view(torch.int16), o["out"].view(torch.int16)))
+    pairs = attended_pairs(o["umask"], p.n_tokens, p.block, p.union_tile)
+    r = p.n_q_heads // p.n_kv_heads
+    attn_flops = 4.0 * p.head_dim * pairs * r
+    n_blocks = p.n_tokens // p.block
+    q_, r_ = divmod(p.n_tokens, p.block)   # sum_i floor(i/B) in closed form
+    scored = p.n_kv_heads * (p.block * q_ * (q_ - 1) // 2 + r_ * q_)
+    index_flops = 2.0 * p.idx_heads * p.idx_dim * scored
+    ucount = o["ucount"].double()
+    inflation = float((ucount.mean() * p.block / (p.topk_tokens + p.union_tile)).item())
+    compress_bytes = p.n_tokens * p.idx_dim * 2 * (1 + 1 / p.block)
+    union_bytes = p.n_kv_heads * p.n_tokens * p.kb * 4 + o["umask"].numel() * 4
+    res = {
+        "p": p,
+        "ms_per_step": ms_step,
+        "wall_s": wall,
+        "stage_ms": dict(zip(["compress", "index_topk", "union", "attend"], stage_ms)),
+        "prefill_matches_single_calls": same,
+        "attended_pairs": pairs,
+        "attn_flops": attn_flops,
+        "index_flops": index_flops,
+        "union_inflation": inflation,
+        "compress_bytes": compress_bytes,
+        "union_bytes": union_bytes,
+        "n_blocks": n_blocks,
+        "x": x,
+    }
+    return res
+
+
+def bench_decode(sg, datagen, torch, steps, warmup):
+    wl = datagen.DECODE
+    p = sg.Params(n_tokens=wl.n_tokens, n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads, block=wl.block,
+                  topk_tokens=wl.topk_tokens, union_tile=1, n_seqs=wl.n_seqs)
+    t0 = time.time()
+    y = datagen.decode_inputs(wl, device="cuda")
+    torch.cuda.synchronize()
+    log(f"{wl.name}: caches drawn on the GPU in {time.time() - t0:.1f}s")
+    blk = torch.empty((p.n_seqs, p.n_tokens // p.block, p.idx_dim), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((p.n_seqs, p.n_q_heads, p.head_dim), dtype=torch.bfloat16, device="cuda")
+    ws = sg.workspace(p, sg.SGQA_OP_DECODE)
+    for _ in range(warmup):
+        sg.sgqa_compress(p, y["ki_cache"], blk)
+        sg.sgqa_decode(p, y["q"], y["k_cache"], y["v_cache"], blk, y["qi"], y["w"], out, ws)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record()
+    for _ in range(steps):
+        sg.sgqa_compress(p, y["ki_cache"], blk)
+    ev[1].record()
+    for _ in range(steps):
+        sg.sgqa_decode(p, y["q"], y["k_cache"], y["v_cache"], blk, y["qi"], y["w"], out, ws)
+    ev[2].record()
+    torch.cuda.synchronize()
+    compress_ms = ev[0].elapsed_time(ev[1]) / steps
+    step_ms = ev[1].elapsed_time(ev[2]) / steps
+    c = (p.n_tokens - 1) // p.block
+    gather_bytes = p.n_seqs * p.n_kv_heads * (p.kb + 1) * p.block * p.head_dim * 2 * 2
+    index_bytes = p.n_seqs * c * p.idx_dim * 2
+    qo_bytes = 2 * p.n_seqs * p.n_q_heads * p.head_dim * 2
+    step_bytes = gather_bytes + index_bytes + qo_bytes
+    cache_build_bytes = p.n_seqs * p.n_tokens * p.idx_dim * 2 * (1 + 1 / p.block)
+    del y
+    return {
+        "metric": "decode tok/s",
+        "value": p.n_seqs / (step_ms / 1e3),
+        "unit": "tokens/s",
+        "ms_per_step": step_ms,
+        "config": {"workload": wl.name, "n_seqs": p.n_seqs, "ctx": p.n_tokens, "n_q_heads": p.n_q_heads,
+                   "n_kv_heads": p.n_kv_heads, "block": p.block, "topk_tokens": p.topk_tokens},
+        "roofline": {"bound": "hbm", "achieved": step_bytes / (step_ms / 1e3) / 1e9, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": step_bytes / (step_ms / 1e3) / 1e9 / PEAK_HBM_GBS,
+                     "traffic": None, "algorithmic_bytes_per_step": step_bytes},
+        "cache_compress": {"ms": compress_ms, "bytes": cache_build_bytes,
+                           "GB_per_s": cache_build_bytes / (compress_ms / 1e3) / 1e9},
+    }
+
+
+def cpu_baseline(oracle, datagen, torch, np, res, wl):
+    """The oracle as it is, on a bounded sample of the same prefill: whole union tiles spread over
+    the sequence (mean position ~ N/2), every group; index + top-k, union and attention of every
+    query of the sampled tiles (plus the block compression of the whole sequence)."""
+    import numpy as np  # noqa: F811
+
+    p = res["p"]
+    x = res["x"]
+
+    def bits(t):
+        return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    host = {k: bits(x[k]) for k in ("q", "k", "v", "qi", "ki")}
+    w = x["w"].cpu().numpy()
+    T = p.n_tiles
+    n_sample_tiles = 4 if p.n_tokens >= 65536 else 8
+    tiles = [int((2 * s + 1) * T // (2 * n_sample_tiles)) for s in range(n_sample_tiles)]
+    rows = np.concatenate([np.arange(t * p.union_tile, min(p.n_tokens, (t + 1) * p.union_tile)) for t in tiles])
+    rows = rows.astype(np.int32)
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
+    t0 = time.perf_counter()
+    kbar = oracle.compress(host["ki"], p.block)
+    sel = oracle.index_topk(host["qi"], w, kbar, p.block, p.kb, rows=rows)
+    full = np.full((p.n_kv_heads, p.n_tokens, p.kb), -1, dtype=np.int32)
+    full[:, rows] = sel
+    umask, _ = oracle.union(full, p.n_tokens, p.block, p.union_tile)
+    oracle.attend(host["q"], host["k"], host["v"], umask, p.block, p.union_tile, rows=rows)
+    dt = time.perf_counter() - t0
+    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} queries = {n_sample_tiles} whole union tiles of {p.union_tile} spread over "
+                      f"the {p.n_tokens}-token sequence (tiles {tiles}), all {p.n_kv_heads} groups and "
+                      f"{p.n_q_heads} heads; compress of all keys + index/top-k + union + attention; "
+                      f"{dt:.1f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import block_sparse_long_sgqa_amd as sg
+    import datagen
+
+    if not os.path.exists(sg.LIB_PATH):
+        from block_sparse_long_sgqa_amd import build as hip_build
+
+        hip_build.build()
+    sg.lib()
+    wl = datagen.WORKLOADS[args.workload]
+    log(f"workload {wl.name}: N={wl.n_tokens} Hq={wl.n_q_heads} G={wl.n_kv_heads} B={wl.block} "
+        f"k={wl.topk_tokens} Tq={wl.union_tile}")
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 29, dtype=torch.int16, device="cuda")  # 1 GiB
+        b = torch.empty_like(a)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    res = bench_prefill(sg, datagen, torch, wl, args.steps, args.warmup)
+    p = res["p"]
+    st = res["stage_ms"]
+    attn_tflops = res["attn_flops"] / (st["attend"] / 1e3) / 1e12
+    line = {
+        "metric": "prefill tokens/s (one full-attention layer, B=8 k=4096)",
+        "value": p.n_tokens / (res["ms_per_step"] / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; shapes and value structure of the pages' setting)",
+        "config": {"workload": wl.name, "n_tokens": p.n_tokens, "n_q_heads": p.n_q_heads,
+                   "n_kv_heads": p.n_kv_heads, "head_dim": p.head_dim, "block": p.block,
+                   "topk_tokens": p.topk_tokens, "union_tile": p.union_tile, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "attend", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                     "algorithmic_flops_per_launch": res["attn_flops"]},
+        "stages_ms": st,
+        "stage_rooflines": {
+            "compress": {"bound": "hbm", "GB_per_s": res["compress_bytes"] / (st["compress"] / 1e3) / 1e9},
+            "index_topk": {"bound": "mfma", "TFLOP_per_s": res["index_flops"] / (st["index_topk"] / 1e3) / 1e12},
+            "union": {"bound": "hbm", "GB_per_s": res["union_bytes"] / (st["union"] / 1e3) / 1e9},
+            "attend": {"bound": "mfma", "TFLOP_per_s": attn_tflops},
+        },
+        "union_inflation": res["union_inflation"],
+        "attended_pairs": res["attended_pairs"],
+        "prefill_matches_single_calls": res["prefill_matches_single_calls"],
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        log("timing the CPU oracle on a bounded sample")
+        line["cpu_baseline"] = cpu_baseline(oracle, datagen, torch, np, res, wl)
+    del res
+    torch.cuda.empty_cache()
+    if not args.no_decode:
+        line["decode"] = bench_decode(sg, datagen, torch, args.steps, args.warmup)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
