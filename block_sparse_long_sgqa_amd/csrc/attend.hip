@@ -29,29 +29,40 @@
 #include "sgqa_device.hpp"
 #include "sgqa_internal.hpp"
 
+#ifndef SGQA_ATTN_WAVES
+#define SGQA_ATTN_WAVES 8
+#endif
+#ifndef SGQA_ATTN_QT
+#define SGQA_ATTN_QT 1
+#endif
+
 namespace sgqa {
 
 namespace {
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kD = 128;
-constexpr int kKeys = 64;            // keys per chunk
-constexpr int kTileBytes = kKeys * kD * 2;  // 16 KiB per tensor per chunk
+constexpr int kKeys = 64;                        // keys per chunk
+constexpr int kRowBytes = 272;                   // 256 B of a K/V row + 16 B pad (bank spread)
+constexpr int kSlotsPerRow = kRowBytes / 16;     // 17 slots of 16 B, the last one is padding
+constexpr int kTileSlots = kKeys * kSlotsPerRow; // 1088
+constexpr int kTileBytes = kTileSlots * 16;      // 17408 B per tensor per chunk
+constexpr int kTileInsts = kTileSlots / 64;      // 17 wave-wide 16-byte loads fill a tile
 constexpr int kStageBytes = 2 * kTileBytes + kKeys * 4;  // K, V, token table
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kMinit = -1.0e30f;
 
-__device__ __forceinline__ int swz(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
-// Byte offset of the 16-byte piece `c` (0..15) of key row `row` in a K or V tile.
-__device__ __forceinline__ int kv_off(int row, int c) { return row * 256 + ((c ^ swz(row)) << 4); }
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <int QT>
 struct AttnState {
   f32x16 o[QT][4];  // O^T tiles: [d-tile][32 d x 32 rows], column = this lane's row
-  float m[QT];      // running max (log2 domain)
-  float l[QT];      // running denominator
+  float m[QT];      // running max (log2 domain), identical in lanes l and l^32
+  float l[QT];      // this lane's part of the running denominator (lanes l and l^32 hold halves)
 };
 
 template <int QT>
@@ -67,13 +78,28 @@ __device__ __forceinline__ void state_init(AttnState<QT>& st) {
   }
 }
 
+// Per-lane LDS byte offsets inside a stage (constant over the chunks).
+struct LaneOffsets {
+  int k;  // K A-operand: key row (l % 32), 16-byte piece (l / 32); + kt * 32 rows + ks * 32 B
+  int v;  // V transposing read: row 4 * khalf + (s16 / 4), byte 32 * dgrp + 8 * (s16 % 4)
+};
+
+__device__ __forceinline__ LaneOffsets lane_offsets() {
+  const int l = lane_id();
+  LaneOffsets o;
+  o.k = (l & 31) * kRowBytes + (l >> 5) * 16;
+  const int grp = l >> 4, s16 = l & 15;
+  o.v = kTileBytes + (4 * (grp >> 1) + (s16 >> 2)) * kRowBytes + 32 * (grp & 1) + 8 * (s16 & 3);
+  return o;
+}
+
 // One 64-key chunk for the QT Q tiles of this wave.
-//   kt/vt: K and V tiles (row-major, swizzled); tok: token ids of the 64 keys (INT_MAX = invalid)
+//   stage: K tile, V tile (row-major, 272-byte rows), token table (INT_MAX = invalid key)
 //   row_pos[qt]: query position of this lane's Q row in tile qt (for the causal mask)
 template <int QT>
-__device__ __forceinline__ void attn_chunk(const uint8_t* kt_lds, const uint8_t* vt_lds, const int* tok,
-                                           const bf16x8 (&qreg)[QT][8], AttnState<QT>& st, float scale_log2,
-                                           bool masked, const int (&row_pos)[QT]) {
+__device__ __forceinline__ void attn_chunk(const uint8_t* stage, const LaneOffsets& lo, const bf16x8 (&qreg)[QT][8],
+                                           AttnState<QT>& st, float scale_log2, bool masked,
+                                           const int (&row_pos)[QT]) {
   const int l = lane_id();
   const int hi = l >> 5;
   f32x16 s[QT][2];
@@ -83,14 +109,32 @@ __device__ __forceinline__ void attn_chunk(const uint8_t* kt_lds, const uint8_t*
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int j = 0; j < 16; ++j) s[qt][kt][j] = 0.0f;
+  // S^T = K Q^T: the K operands of step ks+1 are read while the MFMAs of step ks run.
+  const uint8_t* kp = stage + lo.k;
+  bf16x8 ka[2][2];
+  ka[0][0] = *reinterpret_cast<const bf16x8*>(kp);
+  ka[0][1] = *reinterpret_cast<const bf16x8*>(kp + 32 * kRowBytes);
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt_lds + kv_off(kt * 32 + (l & 31), 2 * ks + hi));
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) s[qt][kt] = mfma32(a, qreg[qt][ks], s[qt][kt]);
+    if (ks < 7) {
+      ka[(ks + 1) & 1][0] = *reinterpret_cast<const bf16x8*>(kp + (ks + 1) * 32);
+      ka[(ks + 1) & 1][1] = *reinterpret_cast<const bf16x8*>(kp + 32 * kRowBytes + (ks + 1) * 32);
     }
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) s[qt][kt] = mfma32(ka[ks & 1][kt], qreg[qt][ks], s[qt][kt]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // Tokens of this lane's keys: key kt*32 + 8*a + 4*hi + (0..3), four consecutive ints.
+  int4 tk[2][4];
+  if (masked) {
+    const int* tok = reinterpret_cast<const int*>(stage + 2 * kTileBytes);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) tk[kt][a] = *reinterpret_cast<const int4*>(tok + kt * 32 + 8 * a + 4 * hi);
   }
 
   bf16x8 pb[QT][4];
@@ -101,114 +145,103 @@ __device__ __forceinline__ void attn_chunk(const uint8_t* kt_lds, const uint8_t*
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        float x = s[qt][kt][j] * scale_log2;
+        float x = s[qt][kt][j];
         if (masked) {
-          const int key = kt * 32 + 8 * (j >> 2) + 4 * hi + (j & 3);
-          if (tok[key] > row_pos[qt]) x = kNegInf;
+          const int4 t4 = tk[kt][j >> 2];
+          const int t = (j & 3) == 0 ? t4.x : (j & 3) == 1 ? t4.y : (j & 3) == 2 ? t4.z : t4.w;
+          if (t > row_pos[qt]) x = kNegInf;
         }
         s[qt][kt][j] = x;
         mx = fmaxf(mx, x);
       }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(st.m[qt], mx);
-    const float alpha = exp2f(st.m[qt] - m_new);
+    const float m_new = fmaxf(st.m[qt], mx * scale_log2);
+    if (ballot(m_new > st.m[qt])) {  // rescale only when some row's max moved
+      const float alpha = fast_exp2(st.m[qt] - m_new);
+      st.l[qt] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) st.o[qt][dt][j] *= alpha;
+      st.m[qt] = m_new;
+    }
     float sum = 0.0f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float p = exp2f(s[qt][kt][j] - m_new);
+        const float p = fast_exp2(__builtin_fmaf(s[qt][kt][j], scale_log2, -m_new));
         s[qt][kt][j] = p;
         sum += p;
       }
-    sum += __shfl_xor(sum, 32, 64);
-    st.l[qt] = st.l[qt] * alpha + sum;
-    st.m[qt] = m_new;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) st.o[qt][dt][j] *= alpha;
+    st.l[qt] += sum;
 #pragma unroll
     for (int ss = 0; ss < 4; ++ss)
 #pragma unroll
       for (int e = 0; e < 8; ++e) pb[qt][ss][e] = (__bf16)s[qt][ss >> 1][8 * (ss & 1) + e];
   }
 
-  // V^T operand: lane group (l / 16) -> d half (dgrp) and key half (khalf); two transposing
-  // reads each give 4 keys of this lane's d.
-  const int grp = l >> 4;
-  const int dgrp = grp & 1, khalf = grp >> 1, s16 = l & 15;
+  // O^T += V^T P^T. The V^T operand of lane l (row d, 8 keys) comes from two transposing reads,
+  // each returning 4 keys of this lane's d, in the key order the score registers already have.
+  const uint8_t* vp = stage + lo.v;
+  auto vread = [&](int step) -> bf16x8 {
+    const int dt = step >> 2, ss = step & 3;
+    const uint8_t* a0 = vp + (16 * ss) * kRowBytes + 64 * dt;
+    const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
+    const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0 + 8 * kRowBytes));
+    const i16x8 cat = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, cat);
+  };
+  bf16x8 va[2];
+  va[0] = vread(0);
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
-    const int d0 = dt * 32 + 16 * dgrp + 4 * (s16 & 3);
+  for (int step = 0; step < 16; ++step) {
+    if (step < 15) va[(step + 1) & 1] = vread(step + 1);
+    const int dt = step >> 2, ss = step & 3;
 #pragma unroll
-    for (int ss = 0; ss < 4; ++ss) {
-      i16x4 r2[2];
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int row = 16 * ss + 8 * r + 4 * khalf + (s16 >> 2);
-        const int off = row * 256 + (((d0 >> 3) ^ swz(row)) << 4) + ((d0 & 7) << 1);
-        r2[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt_lds + off));
-      }
-      typedef short i16x8 __attribute__((ext_vector_type(8)));
-      const i16x8 cat = __builtin_shufflevector(r2[0], r2[1], 0, 1, 2, 3, 4, 5, 6, 7);
-      const bf16x8 a = __builtin_bit_cast(bf16x8, cat);
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) st.o[qt][dt] = mfma32(a, pb[qt][ss], st.o[qt][dt]);
-    }
+    for (int qt = 0; qt < QT; ++qt) st.o[qt][dt] = mfma32(va[step & 1], pb[qt][ss], st.o[qt][dt]);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Register staging of one chunk: NT threads copy 64 K rows and 64 V rows (16-byte pieces).
-template <int NT>
-struct ChunkRegs {
-  static constexpr int kPer = (kKeys * 16 + NT - 1) / NT;
-  u32x4 k[kPer];
-  u32x4 v[kPer];
-  int tok_mine;
-};
-
-// tok_of(key) -> token id or -1 (invalid). kbase/vbase: rows of this (sequence, group).
+// Gather one chunk of 64 keys straight from global memory into the K and V tiles of `stage`
+// (global_load_lds: every wave-wide instruction fills 64 consecutive 16-byte slots; slot s of a
+// tile is row s / 17, piece s % 17, and piece 16 is padding). Invalid keys read row 0 of the
+// group (finite data, always masked out through the token table). Waves of the workgroup split
+// the 17 + 17 instructions. The token table is written by the first wave.
 template <int NT, typename TokFn>
-__device__ __forceinline__ void chunk_load(ChunkRegs<NT>& cr, const uint16_t* kbase, const uint16_t* vbase,
-                                           TokFn tok_of) {
+__device__ __forceinline__ void chunk_issue(uint8_t* stage, const uint16_t* kbase, const uint16_t* vbase,
+                                            TokFn tok_of) {
+  constexpr int kWaves = NT / 64;
+  const int l = lane_id(), wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int x = 0; x < ChunkRegs<NT>::kPer; ++x) {
-    const int p = threadIdx.x + x * NT;
-    const int row = p >> 4, c = p & 15;
-    int tk = -1;
-    if (p < kKeys * 16) tk = tok_of(row);
-    if (tk >= 0) {
-      cr.k[x] = *reinterpret_cast<const u32x4*>(kbase + (long long)tk * kD + c * 8);
-      cr.v[x] = *reinterpret_cast<const u32x4*>(vbase + (long long)tk * kD + c * 8);
-    } else {
-      cr.k[x] = u32x4{0u, 0u, 0u, 0u};
-      cr.v[x] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  cr.tok_mine = (threadIdx.x < kKeys) ? tok_of((int)threadIdx.x) : -1;
-}
-
-template <int NT>
-__device__ __forceinline__ void chunk_store(const ChunkRegs<NT>& cr, uint8_t* stage) {
-#pragma unroll
-  for (int x = 0; x < ChunkRegs<NT>::kPer; ++x) {
-    const int p = threadIdx.x + x * NT;
-    if (p < kKeys * 16) {
-      const int row = p >> 4, c = p & 15;
-      *reinterpret_cast<u32x4*>(stage + kv_off(row, c)) = cr.k[x];
-      *reinterpret_cast<u32x4*>(stage + kTileBytes + kv_off(row, c)) = cr.v[x];
+  for (int x = 0; x < (2 * kTileInsts + kWaves - 1) / kWaves; ++x) {
+    const int inst = wave + x * kWaves;
+    if (inst < 2 * kTileInsts) {
+      const bool is_v = inst >= kTileInsts;
+      const int ti = is_v ? inst - kTileInsts : inst;
+      const int slot = ti * 64 + l;
+      const int row = slot / kSlotsPerRow;
+      int piece = slot - row * kSlotsPerRow;
+      if (piece == 16) piece = 0;  // padding slot: any in-bounds data
+      int tkn = tok_of(row);
+      if (tkn < 0) tkn = 0;
+      const uint16_t* src = (is_v ? vbase : kbase) + (long long)tkn * kD + piece * 8;
+      uint8_t* dst = stage + (is_v ? kTileBytes : 0) + ti * 1024;
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)dst, 16, 0, 0);
     }
   }
   if (threadIdx.x < kKeys) {
-    int* tok = reinterpret_cast<int*>(stage + 2 * kTileBytes);
-    tok[threadIdx.x] = cr.tok_mine >= 0 ? cr.tok_mine : 0x7FFFFFFF;
+    const int t = tok_of((int)threadIdx.x);
+    reinterpret_cast<int*>(stage + 2 * kTileBytes)[threadIdx.x] = t >= 0 ? t : 0x7FFFFFFF;
   }
 }
 
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Block-wide exclusive scan of one value per thread (NT threads); returns the exclusive prefix and
-// writes the total to *total. `scratch` holds NT/64 + 1 ints of LDS.
+// writes the total to *total. `scratch` holds NT/64 ints of LDS.
 template <int NT>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
   const int l = lane_id(), wave = threadIdx.x >> 6;
@@ -236,8 +269,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
                                                        const uint16_t* __restrict__ v,
                                                        const uint32_t* __restrict__ umask,
                                                        uint16_t* __restrict__ out, int n_tokens, int n_q_heads,
-                                                       int n_groups, int block, int tile, float scale_log2,
-                                                       int n_words, int parts, int n_pairs) {
+                                                       int n_groups, int block, int block_shift, int tile,
+                                                       float scale_log2, int n_words, int parts, int n_pairs) {
   constexpr int NT = WAVES * 64;
   constexpr int kRowsWg = WAVES * 32 * QT;
   extern __shared__ __align__(16) uint8_t smem[];
@@ -340,39 +373,37 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
   auto tok_at = [&](int chunk, int key) -> int {
     const int kp = chunk * kKeys + key;
     if (kp >= n_keys) return -1;
-    const int tk = (int)list[kp / block] * block + (kp % block);
+    const int tk = ((int)list[kp >> block_shift] << block_shift) + (kp & (block - 1));
     return tk < n_tokens ? tk : -1;
   };
 
-  ChunkRegs<NT> cr;
-  if (n_chunks > 0) {
-    chunk_load<NT>(cr, kbase, vbase, [&](int key) { return tok_at(0, key); });
-    chunk_store<NT>(cr, stage);
-  }
+  const LaneOffsets lo = lane_offsets();
+  if (n_chunks > 0) chunk_issue<NT>(stage, kbase, vbase, [&](int key) { return tok_at(0, key); });
+  wait_vm();
   __syncthreads();
   for (int n = 0; n < n_chunks; ++n) {
     const int buf = n & 1;
     const bool has_next = n + 1 < n_chunks;
-    if (has_next) chunk_load<NT>(cr, kbase, vbase, [&](int key) { return tok_at(n + 1, key); });
+    if (has_next)
+      chunk_issue<NT>(stage + (buf ^ 1) * kStageBytes, kbase, vbase, [&](int key) { return tok_at(n + 1, key); });
     const uint8_t* sb = stage + buf * kStageBytes;
-    const int* tok = reinterpret_cast<const int*>(sb + 2 * kTileBytes);
     // The chunk's last valid key has the largest token; mask only if it can exceed a query.
     const int last_kp = min((n + 1) * kKeys, n_keys) - 1;
-    const int last_tok = (int)list[last_kp / block] * block + (last_kp % block);
+    const int last_tok = ((int)list[last_kp >> block_shift] << block_shift) + (last_kp & (block - 1));
     const bool masked = ((n + 1) * kKeys > n_keys) || (last_tok > wave_i_min);
-    if (wave_i_min != 0x7FFFFFFF)
-      attn_chunk<QT>(sb, sb + kTileBytes, tok, qreg, st, scale_log2, masked, row_pos);
-    if (has_next) chunk_store<NT>(cr, stage + (buf ^ 1) * kStageBytes);
+    if (wave_i_min != 0x7FFFFFFF) attn_chunk<QT>(sb, lo, qreg, st, scale_log2, masked, row_pos);
+    wait_vm();
     __syncthreads();
   }
 
   // out[i][h][d] = O^T[d][row] / l
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
+    const float l_all = st.l[qt] + __shfl_xor(st.l[qt], 32, 64);
     const int row = row0 + (wave * QT + qt) * 32 + (l & 31);
     if (row >= tile_rows) continue;
     const int i = i0 + row / r, h = g * r + row % r;
-    const float inv = 1.0f / st.l[qt];
+    const float inv = 1.0f / l_all;
     uint16_t* dst = out + ((long long)i * n_q_heads + h) * kD;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -388,8 +419,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
 }
 
 namespace {
-constexpr int kPrefillWaves = 4;
-constexpr int kPrefillQT = 2;
+constexpr int kPrefillWaves = SGQA_ATTN_WAVES;
+constexpr int kPrefillQT = SGQA_ATTN_QT;
 
 size_t attend_lds_bytes(int waves, int list_cap) {
   return (size_t)2 * kStageBytes + 16 * ((waves + 4) / 4) + (size_t)list_cap * 2;
@@ -423,7 +454,7 @@ hipError_t launch_attend(const uint16_t* q, const uint16_t* k, const uint16_t* v
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kPrefillWaves * 64), lds, stream, q, k, v, umask, out, n_tokens,
-                     n_q_heads, n_groups, block, tile, scale_log2, n_words, parts, n_pairs);
+                     n_q_heads, n_groups, block, __builtin_ctz(block), tile, scale_log2, n_words, parts, n_pairs);
   return hipGetLastError();
 }
 
@@ -436,8 +467,8 @@ __global__ __launch_bounds__(64) void k_decode_attend(const uint16_t* __restrict
                                                       const uint16_t* __restrict__ vc,
                                                       const int32_t* __restrict__ sel, float* __restrict__ part_o,
                                                       float* __restrict__ part_ml, int n_seqs, int ctx, int n_q_heads,
-                                                      int n_groups, int block, int kb, int n_split, int per_split,
-                                                      float scale_log2) {
+                                                      int n_groups, int block, int block_shift, int kb, int n_split,
+                                                      int per_split, float scale_log2) {
   constexpr int NT = 64;
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* stage = smem;
@@ -490,27 +521,25 @@ __global__ __launch_bounds__(64) void k_decode_attend(const uint16_t* __restrict
   auto tok_at = [&](int chunk, int key) -> int {
     const int kp = chunk * kKeys + key;
     if (kp >= n_keys) return -1;
-    const int tk = blocks[kp / block] * block + (kp % block);
+    const int tk = (blocks[kp >> block_shift] << block_shift) + (kp & (block - 1));
     return tk < ctx ? tk : -1;
   };
-  ChunkRegs<NT> cr;
-  if (n_chunks > 0) {
-    chunk_load<NT>(cr, kbase, vbase, [&](int key) { return tok_at(0, key); });
-    chunk_store<NT>(cr, stage);
-  }
+  const LaneOffsets lo = lane_offsets();
+  if (n_chunks > 0) chunk_issue<NT>(stage, kbase, vbase, [&](int key) { return tok_at(0, key); });
+  wait_vm();
   __syncthreads();
   for (int n = 0; n < n_chunks; ++n) {
     const int buf = n & 1;
     const bool has_next = n + 1 < n_chunks;
-    if (has_next) chunk_load<NT>(cr, kbase, vbase, [&](int key) { return tok_at(n + 1, key); });
-    const uint8_t* sb = stage + buf * kStageBytes;
-    const int* tok = reinterpret_cast<const int*>(sb + 2 * kTileBytes);
-    attn_chunk<1>(sb, sb + kTileBytes, tok, qreg, st, scale_log2, true, row_pos);
-    if (has_next) chunk_store<NT>(cr, stage + (buf ^ 1) * kStageBytes);
+    if (has_next)
+      chunk_issue<NT>(stage + (buf ^ 1) * kStageBytes, kbase, vbase, [&](int key) { return tok_at(n + 1, key); });
+    attn_chunk<1>(stage + buf * kStageBytes, lo, qreg, st, scale_log2, true, row_pos);
+    wait_vm();
     __syncthreads();
   }
   // Partials: part_o [S][G][n_split][r][D], part_ml [S][G][n_split][r][2]
   const int hh = l & 31;
+  const float l_all = st.l[0] + __shfl_xor(st.l[0], 32, 64);
   if (hh < r) {
     const long long pr = (((long long)s * n_groups + g) * n_split + p) * r + hh;
     float* dst = part_o + pr * kD;
@@ -524,7 +553,7 @@ __global__ __launch_bounds__(64) void k_decode_attend(const uint16_t* __restrict
       }
     if (l < 32) {
       part_ml[pr * 2 + 0] = st.m[0];
-      part_ml[pr * 2 + 1] = st.l[0];
+      part_ml[pr * 2 + 1] = l_all;
     }
   }
 }
@@ -580,7 +609,8 @@ hipError_t launch_decode_attend(const uint16_t* q, const uint16_t* kc, const uin
   const float scale_log2 = scale * 1.4426950408889634f;
   const long long grid = (long long)n_seqs * n_groups * n_split;
   hipLaunchKernelGGL(k_decode_attend, dim3((unsigned)grid), dim3(64), lds, stream, q, kc, vc, sel, part_o, part_ml,
-                     n_seqs, ctx, n_q_heads, n_groups, block, kb, n_split, per_split, scale_log2);
+                     n_seqs, ctx, n_q_heads, n_groups, block, __builtin_ctz(block), kb, n_split, per_split,
+                     scale_log2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_decode_combine, dim3((unsigned)(n_seqs * n_q_heads)), dim3(kD), 0, stream, part_o, part_ml, out,
