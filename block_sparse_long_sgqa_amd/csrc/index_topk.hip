@@ -8,20 +8,24 @@
 //   s(i,g,b) = sum_h w[g][h] * max(0, <qi[i][g][h], kbar[b]>)          (fp32)
 // Sel(i,g) = the first min(K_B, c(i)) candidates in the order (s descending, b ascending).
 //
-// Design (gfx950):
-//  * A workgroup owns WAVES*4 consecutive rows; every wave owns 4 rows. One 16x16x32 bf16 MFMA
-//    takes A = (4 rows x 4 indexer heads) x 32 dims and B = 32 dims x 16 blocks, so after the two
-//    K-steps of d_I = 64 each lane holds the 4 head dots of one (row, block) pair and forms the
-//    score locally (ReLU, weights, head sum) -- no cross-lane traffic.
-//  * Block keys stream through LDS in chunks of 64 blocks (8 KiB, double buffered, XOR-swizzled
-//    16-byte pieces); each chunk is shared by all rows of the workgroup.
-//  * Selection never materialises the score matrix. Every row keeps, in LDS, a list of (key, id)
-//    candidates in ascending id order plus an acceptance threshold. New scores above the threshold
-//    are appended in id order (ballot + popcount compaction). When the list could overflow, the
-//    wave trims it to exactly the top K_B by an exact radix select on the order-preserving 32-bit
-//    key (4 passes of 8-bit digits, LDS histogram) and keeps ties at the threshold by lowest id; the
-//    trim raises the threshold to the new K_B-th key. A rejected candidate is already beaten by K_B
-//    others (higher key, or equal key and lower id), so the final list is the exact selection.
+// Design (gfx950)
+//  * A workgroup owns 4*WAVES consecutive rows (4 per wave). One 16x16x32 bf16 MFMA takes
+//    A = (4 rows x 4 indexer heads) x 32 dims and B = 32 dims x 16 blocks; after the two K-steps
+//    of d_I = 64 every lane holds the 4 head dots of one (row, block) pair and forms the score
+//    locally (ReLU, weights, head sum): no cross-lane traffic, no score matrix in memory.
+//  * Block keys stream through LDS in chunks of 128 blocks, gathered with global_load_lds into
+//    double-buffered 144-byte rows (16 B of padding spread the MFMA operand reads over all banks);
+//    each chunk feeds every row of the workgroup.
+//  * Pass 1 finds, per row, the exact K_B-th largest score tau and how many candidates equal to
+//    tau belong to the selection. Each row keeps in LDS only the keys of candidates scoring above
+//    an acceptance threshold; when the list could overflow it is trimmed to the multiset of its
+//    K_B largest keys and the threshold rises to the new K_B-th key (a rejected candidate is
+//    already beaten by K_B others). The K-th largest key is found by binary search over the
+//    order-preserving 32-bit key, counting with wave ballots (no atomics).
+//  * Pass 2 recomputes the scores and emits, in ascending block order, every candidate with
+//    s > tau plus the lowest-id candidates with s == tau (ballot + popcount compaction).
+//  * The decode form runs the same two passes on slices of one sequence's candidates and emits
+//    (key, id) lists; k_select_merge merges the slices of a (sequence, group) with the same logic.
 #include "sgqa_device.hpp"
 #include "sgqa_internal.hpp"
 
@@ -29,81 +33,105 @@ namespace sgqa {
 
 namespace {
 
+typedef __attribute__((address_space(3))) void lds_void;
+
 constexpr int kIdxHeads = 4;
 constexpr int kIdxDim = 64;
-constexpr int kChunk = 64;                       // candidate blocks per stage
-constexpr int kStageBytes = kChunk * kIdxDim * 2;  // 8 KiB
+constexpr int kChunk = 128;                        // candidate blocks per stage
+constexpr int kKRowBytes = 144;                    // 128 B block key + 16 B pad
+constexpr int kKSlots = kKRowBytes / 16;           // 9 slots of 16 B per row, the last is padding
+constexpr int kStageBytes = kChunk * kKRowBytes;   // 18432 B
+constexpr int kStageInsts = kChunk * kKSlots / 64;  // 18 wave-wide 16-byte loads per stage
+constexpr float kNegInf = -__builtin_huge_valf();
 
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Byte offset of 16-byte piece `c` (0..7) of block-key row `row` inside one stage buffer.
-__device__ __forceinline__ int stage_off(int row, int c) { return row * 128 + ((c ^ (row & 7)) << 4); }
+// Inverse of score_key (canonical +0).
+__device__ __forceinline__ float key_to_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
 
-// Exact top-K of a row list (n > K entries, ascending ids) kept in LDS; the whole wave cooperates.
-// Returns the threshold key tau: afterwards the list holds exactly K entries in ascending id order,
-// all keys > tau plus the lowest-id entries with key == tau.
-__device__ __forceinline__ uint32_t wave_trim(uint32_t* keys, uint32_t* ids, int n, int K, uint32_t* hist) {
+// A key list in registers: lane l holds entries l, l + 64, ... (P per lane; absent entries are 0,
+// which no finite score maps to).
+template <int P>
+struct KeyRegs {
+  uint32_t k[P];
+};
+
+template <int P>
+__device__ __forceinline__ void keys_load(KeyRegs<P>& r, const uint32_t* keys, int n) {
   const int l = lane_id();
-  uint32_t prefix = 0;
-  uint32_t kk = (uint32_t)K;
-#pragma unroll 1
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int x = l; x < 256; x += 64) hist[x] = 0u;
-    lds_wait();
-    const uint32_t hi_mask = (shift == 24) ? 0u : (0xFFFFFFFFu << (shift + 8));
-    for (int e = l; e < n; e += 64) {
-      const uint32_t k = keys[e];
-      if (((k ^ prefix) & hi_mask) == 0u) atomicAdd(&hist[(k >> shift) & 255u], 1u);
-    }
-    lds_wait();
-    const u32x4 h = *reinterpret_cast<const u32x4*>(hist + 4 * l);
-    const uint32_t local = h[0] + h[1] + h[2] + h[3];
-    const uint32_t suf = wave_suffix_sum(local);  // keys in bins >= 4l
-    const uint64_t ge = ballot(suf >= kk);
-    const int ls = 63 - __clzll((long long)ge);
-    uint32_t above = suf - local;  // keys in bins > 4l+3
-    int digit = 4 * l;
-    if (above + h[3] >= kk) {
-      digit = 4 * l + 3;
-    } else if (above + h[3] + h[2] >= kk) {
-      digit = 4 * l + 2;
-      above += h[3];
-    } else if (above + h[3] + h[2] + h[1] >= kk) {
-      digit = 4 * l + 1;
-      above += h[3] + h[2];
-    } else {
-      above += h[3] + h[2] + h[1];
-    }
-    digit = readlane(digit, ls);
-    above = readlane(above, ls);
-    kk -= above;
-    prefix |= ((uint32_t)digit) << shift;
-    lds_wait();
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    const int e = j * 64 + l;
+    r.k[j] = e < n ? keys[e] : 0u;
   }
-  const uint32_t tau = prefix;
-  const int r = (int)kk;  // entries equal to tau that stay
-  int wr = 0, ties = 0;
+}
+
+template <int P>
+__device__ __forceinline__ int keys_count_ge(const KeyRegs<P>& r, uint32_t t) {  // t >= 1
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < P; ++j) cnt += popc64(ballot(r.k[j] >= t));
+  return cnt;
+}
+
+// The K-th largest of the n listed keys (1 <= K <= n <= 64 P) and the number of keys above it,
+// by binary search over the 32-bit key between the list's minimum and maximum.
+template <int P>
+__device__ __forceinline__ uint32_t keys_kth_largest(const KeyRegs<P>& r, int K, int* n_above) {
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    if (r.k[j]) mn = min(mn, r.k[j]);
+    mx = max(mx, r.k[j]);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, off, 64));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
+  }
+  // Largest t in [mn, mx] with count(>= t) >= K; count(>= mn) = n >= K holds throughout.
+  uint32_t lo = mn, hi = mx;
+  while (lo < hi) {
+    const uint32_t mid = lo + (uint32_t)(((uint64_t)hi - lo + 1) >> 1);
+    if (keys_count_ge(r, mid) >= K)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  *n_above = (lo == 0xFFFFFFFFu) ? 0 : keys_count_ge(r, lo + 1);
+  return lo;
+}
+
+template <int P>
+__device__ __forceinline__ uint32_t wave_kth_largest(const uint32_t* keys, int n, int K, int* n_above) {
+  KeyRegs<P> r;
+  keys_load(r, keys, n);
+  return keys_kth_largest(r, K, n_above);
+}
+
+// Trim a key list to the multiset of its K largest keys (K < n); returns the K-th largest key.
+template <int P>
+__device__ __forceinline__ uint32_t wave_trim_keys(uint32_t* keys, int n, int K) {
+  KeyRegs<P> r;
+  keys_load(r, keys, n);
+  int above;
+  const uint32_t tau = keys_kth_largest(r, K, &above);
+  const int l = lane_id();
   const uint64_t lt = lanemask_lt();
-  for (int base = 0; base < n; base += 64) {
-    const int e = base + l;
-    const bool v = e < n;
-    const uint32_t k = v ? keys[e] : 0u;
-    const uint32_t id = v ? ids[e] : 0u;
-    const bool gt = v && k > tau;
-    const bool eq = v && k == tau;
-    const uint64_t em = ballot(eq);
-    const int trank = ties + popc64(em & lt);
-    const bool keep = gt || (eq && trank < r);
-    const uint64_t km = ballot(keep);
-    const int pos = wr + popc64(km & lt);
-    if (keep) {
-      keys[pos] = k;
-      ids[pos] = id;
-    }
-    wr += popc64(km);
-    ties += popc64(em);
+  int wr = 0;
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    const bool keep = r.k[j] > tau;
+    const uint64_t m = ballot(keep);
+    if (keep) keys[wr + popc64(m & lt)] = r.k[j];
+    wr += popc64(m);
   }
+  for (int e = wr + l; e < K; e += 64) keys[e] = tau;  // the tied keys that stay
   lds_wait();
+  (void)above;
   return tau;
 }
 
@@ -111,13 +139,13 @@ __device__ __forceinline__ uint32_t wave_trim(uint32_t* keys, uint32_t* ids, int
 
 // Row parameters of the two uses of the selection kernel.
 //  PREFILL: row = (i, g) flattened as i*G + g (largest rows first); candidates [0, c(i)); output
-//           the final ascending ids into topk [G][N][K_B].
-//  DECODE:  workgroup = (sequence s, candidate slice ch); row = group g; candidates
-//           [ch*slice, min(c, (ch+1)*slice)) with c = floor((L-1)/B); output the slice's exact local
-//           top-K_B as (key, id) lists plus counts. The global selection is the top-K_B of the
-//           concatenated slice lists (k_select_merge): a candidate in the global top-K_B is beaten
-//           by fewer than K_B others overall, hence inside its slice too.
-template <int WAVES, bool DECODE>
+//           the ascending ids into topk [G][N][K_B] (-1 padded).
+//  DECODE:  workgroup = (sequence s, candidate slice sl); row = group g; candidates
+//           [sl*slice, min(c, (sl+1)*slice)), c = floor((L-1)/B); output the slice's local top-K_B
+//           as (key, id) lists in ascending id order plus counts. A candidate of the global
+//           top-K_B is beaten by fewer than K_B others overall, hence inside its slice too, so the
+//           merge of the slice lists (k_select_merge) is exact.
+template <int WAVES, bool DECODE, int P>
 __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restrict__ qi, const float* __restrict__ w,
                                                        const uint16_t* __restrict__ kbar_all,
                                                        int32_t* __restrict__ topk, uint32_t* __restrict__ part_keys,
@@ -125,18 +153,16 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
                                                        int32_t* __restrict__ part_cnt, int n_tokens, int n_groups,
                                                        int block, int kb, int cap, int n_slices, int slice_len) {
   extern __shared__ __align__(16) uint8_t smem[];
-  uint8_t* stage = smem;                                                       // 2 x 8 KiB
-  uint32_t* hist_all = reinterpret_cast<uint32_t*>(smem + 2 * kStageBytes);    // WAVES x 256
-  uint32_t* keys_all = hist_all + WAVES * 256;                                 // WAVES*4 x cap
-  uint32_t* ids_all = keys_all + (size_t)WAVES * 4 * cap;                      // WAVES*4 x cap
+  uint8_t* stage = smem;                                                        // 2 x kStageBytes
+  uint32_t* keys_all = reinterpret_cast<uint32_t*>(smem + 2 * kStageBytes);     // 4*WAVES x cap
 
   constexpr int kRowsPerWg = WAVES * 4;
   const int wave = threadIdx.x >> 6;
   const int l = lane_id();
   const int quarter = l >> 4;
   const int l16 = l & 15;
+  const uint32_t lt16 = (1u << l16) - 1u;
 
-  // Rows of this workgroup.
   long long r0, n_rows;
   int seq = 0, slice = 0, lo = 0, hi_all = 0;
   const uint16_t* kbar = kbar_all;
@@ -157,21 +183,17 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
     hi_all = (int)(r_last / n_groups) / block;  // the last row has the most candidates
   }
   const int n_blocks = n_tokens / block;
-  uint32_t* hist = hist_all + wave * 256;
 
   auto row_group = [&](long long row) -> int { return DECODE ? (int)row : (int)(row % n_groups); };
-  auto row_qi = [&](long long row) -> long long {  // row index into qi [..][G][H_I][d_I]
-    return DECODE ? (long long)seq * n_groups + row : row;
-  };
-  auto row_hi = [&](long long row) -> int {  // exclusive candidate bound of a row
-    return DECODE ? hi_all : (int)(row / n_groups) / block;
-  };
+  auto row_qi = [&](long long row) -> long long { return DECODE ? (long long)seq * n_groups + row : row; };
+  auto row_hi = [&](long long row) -> int { return DECODE ? hi_all : (int)(row / n_groups) / block; };
 
-  // The row whose scores this lane produces (result rows 4*quarter .. +3 = row `quarter`, 4 heads).
+  // The row whose scores this lane produces: row `quarter` of the wave.
   const long long row_o = r0 + wave * 4 + quarter;
   const bool valid_o = row_o < n_rows;
   const int g_o = valid_o ? row_group(row_o) : 0;
   const int hi_lane = valid_o ? row_hi(row_o) : 0;
+  const int n_cand = max(0, hi_lane - lo);  // candidates of this lane's row
 
   if (!DECODE && hi_all <= kb) {
     // Every row has at most K_B candidates: all of them are selected.
@@ -205,134 +227,240 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
   float w4[4];
   for (int j = 0; j < 4; ++j) w4[j] = w[g_o * kIdxHeads + j];
 
-  uint32_t* my_keys = keys_all + (size_t)(wave * 4 + quarter) * cap;
-  uint32_t* my_ids = ids_all + (size_t)(wave * 4 + quarter) * cap;
-  int n_cnt = 0;           // entries in this lane's row list (uniform over the quarter)
-  uint32_t accept = 0u;    // keys >= accept are appended
-
-  // Stage loader: the workgroup copies 64 block keys (512 pieces of 16 B) into a stage buffer.
-  constexpr int kPieces = kChunk * 8;
-  constexpr int kPerThread = (kPieces + WAVES * 64 - 1) / (WAVES * 64);
-  u32x4 pre[kPerThread];
-  auto load_chunk = [&](int b0) {
-#pragma unroll
-    for (int x = 0; x < kPerThread; ++x) {
-      const int p = threadIdx.x + x * WAVES * 64;
-      const int row = p >> 3, c = p & 7;
-      const int b = b0 + row;
-      if (p < kPieces && b < n_blocks)
-        pre[x] = *reinterpret_cast<const u32x4*>(kbar + (long long)b * kIdxDim + c * 8);
-      else
-        pre[x] = u32x4{0u, 0u, 0u, 0u};
+  // Stage issue: 18 wave-wide loads of 64 slots; slot s = row s / 9, piece s % 9 (piece 8 = pad).
+  // Row r of the stage holds candidate block lo + (v0 + r) * stride + off.
+  auto issue = [&](int v0, int buf, int stride, int off, int n_virt) {
+    for (int ii = wave; ii < kStageInsts; ii += WAVES) {
+      const int slot = ii * 64 + l;
+      const int row = slot / kKSlots;
+      int piece = slot - row * kKSlots;
+      if (piece == kKSlots - 1) piece = 0;
+      const int v = v0 + row;
+      int b = lo + v * stride + off;
+      if (v >= n_virt || b >= n_blocks) b = 0;  // beyond the candidates: any valid key (never used)
+      __builtin_amdgcn_global_load_lds((const void*)(kbar + (long long)b * kIdxDim + piece * 8),
+                                       (lds_void*)(stage + buf * kStageBytes + ii * 1024), 16, 0, 0);
     }
   };
-  auto store_chunk = [&](int buf) {
+  const int boff = l16 * kKRowBytes + quarter * 16;  // B operand: row l16 of a 16-block tile
+  auto score_of = [&](const uint8_t* sb, int ct) -> float {
+    const uint8_t* p = sb + ct * 16 * kKRowBytes + boff;
+    const bf16x8 b_lo = *reinterpret_cast<const bf16x8*>(p);
+    const bf16x8 b_hi = *reinterpret_cast<const bf16x8*>(p + 64);
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    acc = mfma16(a_op[0], b_lo, acc);
+    acc = mfma16(a_op[1], b_hi, acc);
+    float s = 0.0f;
 #pragma unroll
-    for (int x = 0; x < kPerThread; ++x) {
-      const int p = threadIdx.x + x * WAVES * 64;
-      if (p < kPieces) *reinterpret_cast<u32x4*>(stage + buf * kStageBytes + stage_off(p >> 3, p & 7)) = pre[x];
-    }
+    for (int j = 0; j < 4; ++j) s += w4[j] * __builtin_amdgcn_fmed3f(acc[j], 0.0f, 3.402823466e38f);  // ReLU
+    return s;
   };
-
-  if (lo < hi_all) {
-    load_chunk(lo);
-    store_chunk(0);
-  }
-  __syncthreads();
-
-  int buf = 0;
-  for (int b0 = lo; b0 < hi_all; b0 += kChunk) {
-    const bool has_next = b0 + kChunk < hi_all;
-    if (has_next) load_chunk(b0 + kChunk);
-    const uint8_t* sb = stage + buf * kStageBytes;
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      const int row = ct * 16 + l16;
-      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      const bf16x8 b_lo = *reinterpret_cast<const bf16x8*>(sb + stage_off(row, quarter));
-      const bf16x8 b_hi = *reinterpret_cast<const bf16x8*>(sb + stage_off(row, 4 + quarter));
-      acc = mfma16(a_op[0], b_lo, acc);
-      acc = mfma16(a_op[1], b_hi, acc);
-      float s = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) s += w4[j] * fmaxf(acc[j], 0.0f);
-      const uint32_t key = score_key(s);
-      const int b = b0 + row;
-      const bool pass = (b < hi_lane) && (key >= accept);
-      const uint64_t m = ballot(pass);
-      const uint32_t m16 = (uint32_t)(m >> (16 * quarter)) & 0xFFFFu;
-      const int pos = n_cnt + __popc(m16 & ((1u << l16) - 1u));
-      if (pass) {
-        my_keys[pos] = key;
-        my_ids[pos] = (uint32_t)b;
+  // Streams candidates v in [0, n_virt) (block lo + v * stride + off) through the double-buffered
+  // stage; body(score, block, valid) runs for every (row, candidate) pair of this lane, after(..)
+  // once per chunk.
+  auto stream = [&](int n_virt, int stride, int off, auto&& body, auto&& after) {
+    const int n_ch = (n_virt + kChunk - 1) / kChunk;
+    if (n_ch > 0) issue(0, 0, stride, off, n_virt);
+    for (int n = 0; n < n_ch; ++n) {
+      wait_vm();
+      __syncthreads();
+      if (n + 1 < n_ch) issue((n + 1) * kChunk, (n + 1) & 1, stride, off, n_virt);
+      const uint8_t* sb = stage + (n & 1) * kStageBytes;
+#pragma unroll 2
+      for (int ct = 0; ct < kChunk / 16; ++ct) {
+        const float sc = score_of(sb, ct);
+        const int v = n * kChunk + ct * 16 + l16;
+        const int b = lo + v * stride + off;
+        body(sc, b, v < n_virt && b < hi_lane);
       }
+      after();
+    }
+    __syncthreads();  // the stage buffers are free again
+  };
+  const int n_all = hi_all - lo;
+
+  uint32_t* my_keys = keys_all + (size_t)(wave * 4 + quarter) * cap;
+  int n_cnt = 0;            // keys in this lane's row list (uniform over the quarter)
+  float accept = kNegInf;   // scores >= accept are kept
+  auto append = [&](float sc, int b, bool valid) {
+    const bool pass = valid && sc >= accept;
+    const uint64_t m = ballot(pass);
+    if (m) {
+      const uint32_t m16 = (uint32_t)(m >> (16 * quarter)) & 0xFFFFu;
+      if (pass) my_keys[n_cnt + __popc(m16 & lt16)] = score_key(sc);
       n_cnt += __popc(m16);
     }
-    // Trim rows whose list could overflow on the next chunk.
-    const bool need = n_cnt + kChunk > cap;
-    const uint64_t need_m = ballot(need);
+  };
+  auto trim_full = [&]() {  // trim the rows whose list could overflow on the next chunk
+    const uint64_t need_m = ballot(n_cnt + kChunk > cap);
     if (need_m) {
       lds_wait();
       for (int q = 0; q < 4; ++q) {
         if ((need_m >> (16 * q)) & 1ull) {
           const int nq = readlane(n_cnt, 16 * q);
-          const uint32_t tau = wave_trim(keys_all + (size_t)(wave * 4 + q) * cap,
-                                         ids_all + (size_t)(wave * 4 + q) * cap, nq, kb, hist);
+          const uint32_t tau = wave_trim_keys<P>(keys_all + (size_t)(wave * 4 + q) * cap, nq, kb);
           if (quarter == q) {
             n_cnt = kb;
-            accept = tau + 1u;
+            accept = key_to_score(tau);
           }
         }
       }
     }
-    if (has_next) store_chunk(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
+  };
+  auto nothing = [&]() {};
+
+  // ------------------------------------------------------------------ pass 0: starting threshold
+  // A strided sample of every row's candidates gives a conservative estimate of the K_B-th score:
+  // the sample quantile at which about 2*K_B candidates are expected above. It only sets where
+  // pass 1 starts keeping keys; a row whose estimate turns out too high is rescanned from -inf.
+  const int sample_max = min(512, cap - kChunk);
+  const int stride = n_all > 2 * kb ? (n_all + sample_max - 1) / sample_max : 0;
+  if (stride > 1) {
+    const int n_virt = (n_all - stride / 2 + stride - 1) / stride;
+    stream(n_virt, stride, stride / 2, append, nothing);
+    lds_wait();
+    float est = kNegInf;
+    for (int q = 0; q < 4; ++q) {
+      const int nq = readlane(n_cnt, 16 * q);     // samples of row q
+      const int cq = readlane(n_cand, 16 * q);    // candidates of row q
+      const int ks = cq > 0 ? (int)(((long long)2 * kb * nq + cq - 1) / cq) : 0;
+      if (cq > 2 * kb && ks >= 1 && ks < nq) {
+        int above;
+        const uint32_t t = wave_kth_largest<P>(keys_all + (size_t)(wave * 4 + q) * cap, nq, ks, &above);
+        if (quarter == q) est = key_to_score(t);
+      }
+    }
+    accept = est;
+    n_cnt = 0;
   }
 
-  // Final: exactly min(K_B, candidates) entries per row, ascending ids.
+  // ------------------------------------------------------------------ pass 1: tau and ties
+  stream(n_all, 1, 0, append, trim_full);
   lds_wait();
-  for (int q = 0; q < 4; ++q) {
-    const long long row = r0 + wave * 4 + q;
-    if (row >= n_rows) break;
-    int nq = readlane(n_cnt, 16 * q);
-    uint32_t* kq = keys_all + (size_t)(wave * 4 + q) * cap;
-    uint32_t* iq = ids_all + (size_t)(wave * 4 + q) * cap;
-    if (nq > kb) {
-      wave_trim(kq, iq, nq, kb, hist);
-      nq = kb;
-    }
-    if (DECODE) {
-      const long long base = (((long long)seq * n_slices + slice) * n_groups + row) * kb;
-      for (int e = l; e < nq; e += 64) {
-        part_keys[base + e] = kq[e];
-        part_ids[base + e] = iq[e];
+  // A row whose starting threshold was above its K_B-th score kept fewer than K_B keys: rescan
+  // those rows from -inf (the other rows keep their lists and take nothing new).
+  {
+    __shared__ int redo;
+    if (threadIdx.x == 0) redo = 0;
+    __syncthreads();
+    const bool failed = n_cand > kb && n_cnt < kb;
+    if (ballot(failed) && l == 0) redo = 1;
+    __syncthreads();
+    if (redo) {
+      if (failed) {
+        n_cnt = 0;
+        accept = kNegInf;
+      } else {
+        accept = __builtin_huge_valf();
       }
-      if (l == 0) part_cnt[((long long)seq * n_slices + slice) * n_groups + row] = nq;
+      stream(n_all, 1, 0, append, trim_full);
+      lds_wait();
+    }
+  }
+  // Exact threshold per row: select everything when the row has at most K_B candidates.
+  float tau_f = kNegInf;
+  int ties = 0;
+  for (int q = 0; q < 4; ++q) {
+    const int nq = readlane(n_cnt, 16 * q);
+    const int cq = readlane(n_cand, 16 * q);
+    if (cq > kb) {
+      int above;
+      const uint32_t tau = wave_kth_largest<P>(keys_all + (size_t)(wave * 4 + q) * cap, nq, kb, &above);
+      if (quarter == q) {
+        tau_f = key_to_score(tau);
+        ties = kb - above;
+      }
+    }
+  }
+
+  // ------------------------------------------------------------------ pass 2: emit in order
+  int n_out = 0, t_seen = 0;  // uniform over the quarter
+  int32_t* out_row = nullptr;
+  uint32_t* pk_row = nullptr;
+  uint32_t* pi_row = nullptr;
+  if (valid_o) {
+    if (DECODE) {
+      const long long base = (((long long)seq * n_slices + slice) * n_groups + row_o) * kb;
+      pk_row = part_keys + base;
+      pi_row = part_ids + base;
     } else {
-      const int i = (int)(row / n_groups), g = (int)(row % n_groups);
-      int32_t* out = topk + ((long long)g * n_tokens + i) * kb;
-      for (int e = l; e < kb; e += 64) out[e] = e < nq ? (int32_t)iq[e] : -1;
+      out_row = topk + ((long long)g_o * n_tokens + row_o / n_groups) * kb;
+    }
+  }
+  auto emit = [&](float sc, int b, bool valid) {
+    const bool gt = valid && sc > tau_f;
+    const bool eq = valid && sc == tau_f;
+    const uint32_t em16 = (uint32_t)(ballot(eq) >> (16 * quarter)) & 0xFFFFu;
+    const bool keep = gt || (eq && t_seen + __popc(em16 & lt16) < ties);
+    const uint32_t km16 = (uint32_t)(ballot(keep) >> (16 * quarter)) & 0xFFFFu;
+    if (keep) {
+      const int pos = n_out + __popc(km16 & lt16);
+      if (DECODE) {
+        pk_row[pos] = score_key(sc);
+        pi_row[pos] = (uint32_t)b;
+      } else {
+        out_row[pos] = b;
+      }
+    }
+    n_out += __popc(km16);
+    t_seen += __popc(em16);
+  };
+  stream(n_all, 1, 0, emit, nothing);
+  // Padding / counts.
+  if (valid_o) {
+    if (DECODE) {
+      if (l16 == 0) part_cnt[((long long)seq * n_slices + slice) * n_groups + row_o] = n_out;
+    } else {
+      for (int e = n_out + l16; e < kb; e += 16) out_row[e] = -1;
     }
   }
 }
 
-// Decode merge: one wave per (sequence, group) streams the slice lists (ascending ids) through the
-// same accept / trim list and writes Sel ascending, -1 padded, to sel (and to topk_out if given).
+// Decode merge: one wave per (sequence, group). The slice lists, concatenated in slice order, are
+// in ascending id order; pass 1 finds tau and the tie count from their keys, pass 2 emits.
+template <int P>
 __global__ __launch_bounds__(64) void k_select_merge(const uint32_t* __restrict__ part_keys,
                                                      const uint32_t* __restrict__ part_ids,
                                                      const int32_t* __restrict__ part_cnt, int32_t* __restrict__ sel,
                                                      int32_t* __restrict__ topk_out, int n_groups, int kb, int cap,
                                                      int n_slices) {
   extern __shared__ __align__(16) uint8_t smem[];
-  uint32_t* hist = reinterpret_cast<uint32_t*>(smem);
-  uint32_t* keys = hist + 256;
-  uint32_t* ids = keys + cap;
+  uint32_t* keys = reinterpret_cast<uint32_t*>(smem);
   const int s = blockIdx.x / n_groups, g = blockIdx.x % n_groups;
   const int l = lane_id();
   const uint64_t lt = lanemask_lt();
-  int n = 0;
-  uint32_t accept = 0u;
+  int n = 0, total = 0;
+  uint32_t accept = 0u;  // keys >= accept are kept
+  for (int ch = 0; ch < n_slices; ++ch) {
+    const long long pr = ((long long)s * n_slices + ch) * n_groups + g;
+    const int cnt = part_cnt[pr];
+    total += cnt;
+    for (int base = 0; base < cnt; base += 64) {
+      const int e = base + l;
+      const uint32_t key = e < cnt ? part_keys[pr * kb + e] : 0u;
+      const bool pass = e < cnt && key >= accept;
+      const uint64_t m = ballot(pass);
+      if (pass) keys[n + popc64(m & lt)] = key;
+      n += popc64(m);
+      if (n + 64 > cap) {
+        lds_wait();
+        accept = wave_trim_keys<P>(keys, n, kb) + 1u;
+        n = kb;
+      }
+    }
+  }
+  lds_wait();
+  uint32_t tau = 0u;
+  int ties = 0;
+  const bool all = total <= kb;  // fewer candidates than K_B: keep every one
+  if (!all) {
+    int above;
+    tau = wave_kth_largest<P>(keys, n, kb, &above);
+    ties = kb - above;
+  }
+  int32_t* dst = sel + ((long long)s * n_groups + g) * kb;
+  int32_t* dst2 = topk_out ? topk_out + ((long long)s * n_groups + g) * kb : nullptr;
+  int n_out = 0, t_seen = 0;
   for (int ch = 0; ch < n_slices; ++ch) {
     const long long pr = ((long long)s * n_slices + ch) * n_groups + g;
     const int cnt = part_cnt[pr];
@@ -340,84 +468,102 @@ __global__ __launch_bounds__(64) void k_select_merge(const uint32_t* __restrict_
       const int e = base + l;
       const bool v = e < cnt;
       const uint32_t key = v ? part_keys[pr * kb + e] : 0u;
-      const uint32_t id = v ? part_ids[pr * kb + e] : 0u;
-      const bool pass = v && key >= accept;
-      const uint64_t m = ballot(pass);
-      if (pass) {
-        const int pos = n + popc64(m & lt);
-        keys[pos] = key;
-        ids[pos] = id;
+      const int32_t id = v ? (int32_t)part_ids[pr * kb + e] : 0;
+      const bool gt = v && (all || key > tau);
+      const bool eq = v && !all && key == tau;
+      const uint64_t em = ballot(eq);
+      const bool keep = gt || (eq && t_seen + popc64(em & lt) < ties);
+      const uint64_t km = ballot(keep);
+      if (keep) {
+        const int pos = n_out + popc64(km & lt);
+        dst[pos] = id;
+        if (dst2) dst2[pos] = id;
       }
-      n += popc64(m);
-      if (n + 64 > cap) {
-        lds_wait();
-        accept = wave_trim(keys, ids, n, kb, hist) + 1u;
-        n = kb;
-      }
+      n_out += popc64(km);
+      t_seen += popc64(em);
     }
   }
-  lds_wait();
-  if (n > kb) {
-    wave_trim(keys, ids, n, kb, hist);
-    n = kb;
-  }
-  int32_t* dst = sel + ((long long)s * n_groups + g) * kb;
-  int32_t* dst2 = topk_out ? topk_out + ((long long)s * n_groups + g) * kb : nullptr;
-  for (int e = l; e < kb; e += 64) {
-    const int32_t val = e < n ? (int32_t)ids[e] : -1;
-    dst[e] = val;
-    if (dst2) dst2[e] = val;
+  for (int e = n_out + l; e < kb; e += 64) {
+    dst[e] = -1;
+    if (dst2) dst2[e] = -1;
   }
 }
 
 namespace {
 
-int topk_cap(int kb) {
-  int extra = kb > 128 ? kb : 128;
-  int cap = kb + extra;
-  return (cap + 63) / 64 * 64;
+size_t select_lds_bytes(int waves, int cap) { return (size_t)2 * kStageBytes + (size_t)waves * 4 * cap * 4; }
+
+// Largest list capacity (multiple of 64) that fits `waves` in the LDS budget, capped at a size
+// where trims are rare; 0 below the minimum (K_B plus one chunk of appends plus slack).
+int select_cap(int waves, int kb, size_t lds_budget) {
+  const long long avail = (long long)lds_budget - 2LL * kStageBytes - 256;  // 256 B: static LDS
+  if (avail <= 0) return 0;
+  int cap = (int)(avail / ((long long)waves * 4 * 4)) / 64 * 64;
+  const int need = kb + kChunk + 64;
+  const int enough = ((4 * kb + kChunk > need ? 4 * kb + kChunk : need) + 63) / 64 * 64;
+  if (cap > enough) cap = enough;
+  if (cap > 4096) cap = 4096;  // trims hold at most 64 keys per lane in registers
+  // Prefer the smaller register footprint when it still leaves room for K_B + a chunk or more.
+  if (cap > 1024 && 1024 >= 2 * kb + kChunk) cap = 1024;
+  if (cap > 2048 && 2048 >= 2 * kb + kChunk) cap = 2048;
+  return cap >= need ? cap : 0;
 }
 
-size_t topk_lds_bytes(int waves, int cap) {
-  return (size_t)2 * kStageBytes + (size_t)waves * 256 * 4 + (size_t)waves * 4 * cap * 8;
+// Keys per lane a trim holds in registers for a list capacity.
+int keys_per_lane(int cap) { return cap <= 1024 ? 16 : (cap <= 2048 ? 32 : 64); }
+
+int prefill_waves(int kb, size_t lds_budget) {
+  for (int wv = 8; wv >= 1; wv >>= 1)
+    if (select_cap(wv, kb, lds_budget) > 0) return wv;
+  return 0;
 }
 
 }  // namespace
+
+size_t index_topk_lds_min(int kb) {
+  const int cap = select_cap(1, kb, kGfx950LdsBytes);
+  return cap > 0 ? select_lds_bytes(1, cap) : kGfx950LdsBytes + 1;
+}
+
+size_t decode_select_lds(int n_groups, int kb) {
+  const int waves = (n_groups + 3) / 4;
+  const int cap = select_cap(waves, kb, kGfx950LdsBytes);
+  return cap > 0 ? select_lds_bytes(waves, cap) : kGfx950LdsBytes + 1;
+}
 
 hipError_t launch_index_topk(const uint16_t* qi, const float* w, const uint16_t* kbar, int32_t* topk, int n_tokens,
                              int n_groups, int block, int kb, hipStream_t stream) {
   const long long n_rows = (long long)n_tokens * n_groups;
   if (n_rows == 0) return hipSuccess;
-  const int cap = topk_cap(kb);
-  const int lds_max = max_lds_per_block();
-  int waves = 4;
-  while (waves > 1 && topk_lds_bytes(waves, cap) > (size_t)lds_max) waves >>= 1;
-  const size_t lds = topk_lds_bytes(waves, cap);
-  if (lds > (size_t)lds_max) return hipErrorInvalidValue;
+  const size_t budget = (size_t)max_lds_per_block();
+  const int waves = prefill_waves(kb, budget);
+  if (waves == 0) return hipErrorInvalidValue;
+  const int cap = select_cap(waves, kb, budget);
+  const size_t lds = select_lds_bytes(waves, cap);
   const long long grid = (n_rows + waves * 4 - 1) / (waves * 4);
-#define SGQA_TOPK_CASE(WV)                                                                                       \
-  case WV: {                                                                                                     \
-    hipError_t e = hipFuncSetAttribute((const void*)k_select<WV, false>,                                         \
+  const int pk = keys_per_lane(cap);
+#define SGQA_TOPK_CASE(WV, PK)                                                                                   \
+  if (waves == WV && pk == PK) {                                                                                 \
+    hipError_t e = hipFuncSetAttribute((const void*)k_select<WV, false, PK>,                                     \
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                    \
     if (e != hipSuccess) return e;                                                                               \
-    hipLaunchKernelGGL((k_select<WV, false>), dim3((unsigned)grid), dim3(WV * 64), lds, stream, qi, w, kbar,     \
+    hipLaunchKernelGGL((k_select<WV, false, PK>), dim3((unsigned)grid), dim3(WV * 64), lds, stream, qi, w, kbar, \
                        topk, nullptr, nullptr, nullptr, n_tokens, n_groups, block, kb, cap, 0, 0);               \
-    break;                                                                                                       \
+    return hipGetLastError();                                                                                    \
   }
-  switch (waves) {
-    SGQA_TOPK_CASE(4)
-    SGQA_TOPK_CASE(2)
-    SGQA_TOPK_CASE(1)
-    default:
-      return hipErrorInvalidValue;
-  }
+  SGQA_TOPK_CASE(8, 16)
+  SGQA_TOPK_CASE(4, 16)
+  SGQA_TOPK_CASE(4, 32)
+  SGQA_TOPK_CASE(2, 16)
+  SGQA_TOPK_CASE(2, 32)
+  SGQA_TOPK_CASE(2, 64)
+  SGQA_TOPK_CASE(1, 16)
+  SGQA_TOPK_CASE(1, 32)
+  SGQA_TOPK_CASE(1, 64)
 #undef SGQA_TOPK_CASE
+  return hipErrorInvalidValue;
   return hipGetLastError();
 }
-
-size_t index_topk_lds_min(int kb) { return topk_lds_bytes(1, topk_cap(kb)); }
-
-size_t decode_select_lds(int n_groups, int kb) { return topk_lds_bytes((n_groups + 3) / 4, topk_cap(kb)); }
 
 int decode_slice_len() { return 1024; }
 
@@ -440,41 +586,56 @@ hipError_t launch_decode_select(const uint16_t* qi, const float* w, const uint16
   uint32_t* part_keys = reinterpret_cast<uint32_t*>(ws);
   uint32_t* part_ids = part_keys + n_lists * kb;
   int32_t* part_cnt = reinterpret_cast<int32_t*>(part_ids + n_lists * kb);
-  const int cap = topk_cap(kb);
+  const size_t budget = (size_t)max_lds_per_block();
   const int waves = (n_groups + 3) / 4;
-  const size_t lds = topk_lds_bytes(waves, cap);
-  const int lds_max = max_lds_per_block();
-  if (lds > (size_t)lds_max) return hipErrorInvalidValue;
+  const int cap = select_cap(waves, kb, budget);
+  if (cap == 0) return hipErrorInvalidValue;
+  const size_t lds = select_lds_bytes(waves, cap);
   const long long grid = (long long)n_seqs * n_slices;
-#define SGQA_DSEL_CASE(WV)                                                                                       \
-  case WV: {                                                                                                     \
-    hipError_t e = hipFuncSetAttribute((const void*)k_select<WV, true>,                                          \
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                    \
+  const int pk = keys_per_lane(cap);
+  hipError_t e = hipErrorInvalidValue;
+#define SGQA_DSEL_CASE(WV, PK)                                                                                   \
+  if (waves == WV && pk == PK) {                                                                                 \
+    e = hipFuncSetAttribute((const void*)k_select<WV, true, PK>, hipFuncAttributeMaxDynamicSharedMemorySize,     \
+                            (int)lds);                                                                           \
     if (e != hipSuccess) return e;                                                                               \
-    hipLaunchKernelGGL((k_select<WV, true>), dim3((unsigned)grid), dim3(WV * 64), lds, stream, qi, w, kbar,      \
+    hipLaunchKernelGGL((k_select<WV, true, PK>), dim3((unsigned)grid), dim3(WV * 64), lds, stream, qi, w, kbar,  \
                        nullptr, part_keys, part_ids, part_cnt, n_tokens, n_groups, block, kb, cap, n_slices,     \
                        decode_slice_len());                                                                      \
-    break;                                                                                                       \
+    e = hipGetLastError();                                                                                       \
   }
-  switch (waves) {
-    SGQA_DSEL_CASE(1)
-    SGQA_DSEL_CASE(2)
-    SGQA_DSEL_CASE(3)
-    SGQA_DSEL_CASE(4)
-    default:
-      return hipErrorInvalidValue;
-  }
+  SGQA_DSEL_CASE(1, 16)
+  SGQA_DSEL_CASE(1, 32)
+  SGQA_DSEL_CASE(1, 64)
+  SGQA_DSEL_CASE(2, 16)
+  SGQA_DSEL_CASE(2, 32)
+  SGQA_DSEL_CASE(2, 64)
+  SGQA_DSEL_CASE(3, 16)
+  SGQA_DSEL_CASE(3, 32)
+  SGQA_DSEL_CASE(4, 16)
+  SGQA_DSEL_CASE(4, 32)
 #undef SGQA_DSEL_CASE
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t mlds = (size_t)(256 + 2 * cap) * 4;
-  if (mlds > 65536) {
-    e = hipFuncSetAttribute((const void*)k_select_merge, hipFuncAttributeMaxDynamicSharedMemorySize, (int)mlds);
-    if (e != hipSuccess) return e;
+  int mcap = 2 * kb + 64;
+  if (mcap > 4096) mcap = 4096;
+  const int mpk = keys_per_lane(mcap);
+  const size_t mlds = (size_t)mcap * 4;
+#define SGQA_MERGE_CASE(PK)                                                                                       \
+  if (mpk == PK) {                                                                                                \
+    if (mlds > 65536) {                                                                                           \
+      e = hipFuncSetAttribute((const void*)k_select_merge<PK>, hipFuncAttributeMaxDynamicSharedMemorySize,        \
+                              (int)mlds);                                                                         \
+      if (e != hipSuccess) return e;                                                                              \
+    }                                                                                                             \
+    hipLaunchKernelGGL(k_select_merge<PK>, dim3((unsigned)(n_seqs * n_groups)), dim3(64), mlds, stream,          \
+                       part_keys, part_ids, part_cnt, sel, topk_out, n_groups, kb, mcap, n_slices);               \
+    return hipGetLastError();                                                                                     \
   }
-  hipLaunchKernelGGL(k_select_merge, dim3((unsigned)(n_seqs * n_groups)), dim3(64), mlds, stream, part_keys, part_ids,
-                     part_cnt, sel, topk_out, n_groups, kb, cap, n_slices);
-  return hipGetLastError();
+  SGQA_MERGE_CASE(16)
+  SGQA_MERGE_CASE(32)
+  SGQA_MERGE_CASE(64)
+#undef SGQA_MERGE_CASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace sgqa

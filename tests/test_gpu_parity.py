@@ -93,12 +93,17 @@ def test_index_topk_bit_exact(sg, name):
     np.testing.assert_array_equal(topk.cpu().numpy(), want)
 
 
-@pytest.mark.parametrize("case", ["zero_queries", "dense_k", "negative_weights", "all_equal_keys"])
+@pytest.mark.parametrize("case", ["zero_queries", "dense_k", "negative_weights", "all_equal_keys",
+                                  "strided_outliers"])
 def test_index_topk_degenerate_cases(sg, case):
     wl = datagen.PREFILL.replace(name=f"deg_{case}", n_tokens=2500, n_q_heads=16, n_kv_heads=2, topk_tokens=400,
                                  union_tile=32)
     if case == "dense_k":
         wl = wl.replace(topk_tokens=4096)
+    if case == "strided_outliers":
+        # Every 4th block scores far above the rest and the others tie in small groups: a strided
+        # sample of the candidates is unrepresentative (the kernel must still be exact).
+        wl = wl.replace(n_tokens=4096, topk_tokens=128)
     x = datagen.prefill_inputs(wl)
     if case == "zero_queries":
         x["qi"] = torch.zeros_like(x["qi"])
@@ -106,6 +111,14 @@ def test_index_topk_degenerate_cases(sg, case):
         x["w"] = -x["w"]          # every score <= 0; -0 and +0 must tie
     if case == "all_equal_keys":
         x["ki"] = torch.ones_like(x["ki"])
+    if case == "strided_outliers":
+        ki = torch.randint(-1, 2, x["ki"].shape, generator=torch.Generator().manual_seed(11)).float()
+        blocks = torch.arange(wl.n_tokens) // wl.block
+        for res in (1, 2):
+            sel = (blocks % 4 == res)
+            ki[sel] = 4.0 if res == 2 else 3.0
+        x["ki"] = ki.to(torch.bfloat16)
+        x["qi"] = x["qi"].abs()
     p = params_of(wl)
     ch = OracleChain(x, p)
     say(f"index_topk degenerate {case}")
