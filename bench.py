@@ -44,6 +44,22 @@ def parse():
     return ap.parse_args()
 
 
+def profiled_traffic(kernel: str, workload: str, source: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 summary (FETCH_SIZE + WRITE_SIZE,
+    calibrated), or None when there is none or the kernel source changed since it was taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    cur = hashlib.sha256(open(os.path.join(ROOT, source), "rb").read()).hexdigest()[:16]
+    for line in open(path):
+        if line.startswith(f"traffic {kernel} "):
+            kv = dict(t.split("=", 1) for t in line.split()[2:])
+            return float(kv["bytes"]) if kv.get("source") == cur else None
+    return None
+
+
 def attended_pairs(umask, n_tokens: int, block: int, tile: int) -> int:
     """sum over (i, g) of |J(i,g)|: causally visible tokens of the tile union (exact count)."""
     import torch
@@ -268,13 +284,14 @@ def main():
         f"k={wl.topk_tokens} Tq={wl.union_tile}")
 
     if args.copy_calibration:
-        a = torch.empty(1 << 29, dtype=torch.int16, device="cuda")  # 1 GiB
-        b = torch.empty_like(a)
-        a.fill_(1)
+        # A plain streaming kernel of known size for the HBM byte counters: read 1 GiB, write 1 GiB
+        # (in-place multiply), after a 2 GiB write that evicts the source from the caches.
+        a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        evict = torch.zeros(1 << 29, dtype=torch.float32, device="cuda")
         torch.cuda.synchronize()
-        b.copy_(a)
+        a.mul_(2.0)
         torch.cuda.synchronize()
-        del a, b
+        del a, evict
 
     res = bench_prefill(sg, datagen, torch, wl, args.steps, args.warmup)
     p = res["p"]
@@ -297,7 +314,9 @@ def main():
                    "n_kv_heads": p.n_kv_heads, "head_dim": p.head_dim, "block": p.block,
                    "topk_tokens": p.topk_tokens, "union_tile": p.union_tile, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": "attend", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": profiled_traffic("attend", "long_prefill_128k", "block_sparse_long_sgqa_amd/csrc/attend.hip")
+                     if wl.name == "long_prefill_128k" else None,
                      "algorithmic_flops_per_launch": res["attn_flops"]},
         "stages_ms": st,
         "stage_rooflines": {
