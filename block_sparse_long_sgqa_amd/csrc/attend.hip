@@ -1,4 +1,4 @@
-// attend.hip -- gathered-block causal GQA flash attention (prefill over tile unions, decode split-K).
+// attend.hip -- gathered-block causal GQA flash attention (prefill over tile unions, decode over Sel + own block).
 //
 // "Inside Step 5 Preview", section Sparse GQA, Figure 3: the attention main path loads the original
 // (uncompressed) K/V of the selected history blocks and, in the query's own block, only the
@@ -46,13 +46,14 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kD = 128;
-constexpr int kKeys = 64;                        // keys per chunk
-constexpr int kRowBytes = 272;                   // 256 B of a K/V row + 16 B pad (bank spread)
-constexpr int kSlotsPerRow = kRowBytes / 16;     // 17 slots of 16 B, the last one is padding
-constexpr int kTileSlots = kKeys * kSlotsPerRow; // 1088
-constexpr int kTileBytes = kTileSlots * 16;      // 17408 B per tensor per chunk
-constexpr int kTileInsts = kTileSlots / 64;      // 17 wave-wide 16-byte loads fill a tile
-constexpr int kStageBytes = 2 * kTileBytes + kKeys * 4;  // K, V, token table
+constexpr int kKeys = 64;                          // keys per chunk
+constexpr int kKRowBytes = 272;                    // K row: 256 B + 16 B pad (bank spread for 16-B reads)
+constexpr int kKSlotsPerRow = kKRowBytes / 16;     // 17 slots of 16 B, the last one is padding
+constexpr int kKTileBytes = kKeys * kKRowBytes;    // 17408 B
+constexpr int kKTileInsts = kKeys * kKSlotsPerRow / 64;  // 17 wave-wide 16-byte loads fill the K tile
+constexpr int kVTileBytes = kKeys * 256;           // V rows unpadded; 16-B pieces XOR-swizzled by row
+constexpr int kVTileInsts = kVTileBytes / 1024;    // 16
+constexpr int kStageBytes = kKTileBytes + kVTileBytes + kKeys * 4;  // K, V, token table
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kMinit = -1.0e30f;
 
@@ -78,18 +79,28 @@ __device__ __forceinline__ void state_init(AttnState<QT>& st) {
   }
 }
 
+// Physical 16-byte piece of logical piece p in V row `row`: XOR with 4 * (row % 4). A transposing
+// read phase (32 lanes) touches 4 consecutive rows x 4 consecutive pieces; the swizzle spreads them
+// over all 16 piece positions, i.e. all 64 banks once.
+__device__ __forceinline__ int v_phys(int row, int p) { return p ^ ((row & 3) << 2); }
+
 // Per-lane LDS byte offsets inside a stage (constant over the chunks).
 struct LaneOffsets {
-  int k;  // K A-operand: key row (l % 32), 16-byte piece (l / 32); + kt * 32 rows + ks * 32 B
-  int v;  // V transposing read: row 4 * khalf + (s16 / 4), byte 32 * dgrp + 8 * (s16 % 4)
+  int k;     // K A-operand: key row (l % 32), 16-byte piece (l / 32); + kt * 32 rows + ks * 32 B
+  int v[4];  // V transposing read for d-tile dt: row 4 * khalf + (s16 / 4), d 32 dt + 16 dgrp + 4 (s16 % 4)
 };
 
 __device__ __forceinline__ LaneOffsets lane_offsets() {
   const int l = lane_id();
   LaneOffsets o;
-  o.k = (l & 31) * kRowBytes + (l >> 5) * 16;
+  o.k = (l & 31) * kKRowBytes + (l >> 5) * 16;
   const int grp = l >> 4, s16 = l & 15;
-  o.v = kTileBytes + (4 * (grp >> 1) + (s16 >> 2)) * kRowBytes + 32 * (grp & 1) + 8 * (s16 & 3);
+  const int row = 4 * (grp >> 1) + (s16 >> 2);  // + 16 ss + 8 r (multiples of 4: same swizzle)
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    const int piece = 4 * dt + 2 * (grp & 1) + ((s16 & 3) >> 1);
+    o.v[dt] = kKTileBytes + row * 256 + 16 * v_phys(row, piece) + 8 * (s16 & 1);
+  }
   return o;
 }
 
@@ -113,12 +124,12 @@ __device__ __forceinline__ void attn_chunk(const uint8_t* stage, const LaneOffse
   const uint8_t* kp = stage + lo.k;
   bf16x8 ka[2][2];
   ka[0][0] = *reinterpret_cast<const bf16x8*>(kp);
-  ka[0][1] = *reinterpret_cast<const bf16x8*>(kp + 32 * kRowBytes);
+  ka[0][1] = *reinterpret_cast<const bf16x8*>(kp + 32 * kKRowBytes);
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
     if (ks < 7) {
       ka[(ks + 1) & 1][0] = *reinterpret_cast<const bf16x8*>(kp + (ks + 1) * 32);
-      ka[(ks + 1) & 1][1] = *reinterpret_cast<const bf16x8*>(kp + 32 * kRowBytes + (ks + 1) * 32);
+      ka[(ks + 1) & 1][1] = *reinterpret_cast<const bf16x8*>(kp + 32 * kKRowBytes + (ks + 1) * 32);
     }
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -130,7 +141,7 @@ __device__ __forceinline__ void attn_chunk(const uint8_t* stage, const LaneOffse
   // Tokens of this lane's keys: key kt*32 + 8*a + 4*hi + (0..3), four consecutive ints.
   int4 tk[2][4];
   if (masked) {
-    const int* tok = reinterpret_cast<const int*>(stage + 2 * kTileBytes);
+    const int* tok = reinterpret_cast<const int*>(stage + kKTileBytes + kVTileBytes);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -184,12 +195,11 @@ __device__ __forceinline__ void attn_chunk(const uint8_t* stage, const LaneOffse
 
   // O^T += V^T P^T. The V^T operand of lane l (row d, 8 keys) comes from two transposing reads,
   // each returning 4 keys of this lane's d, in the key order the score registers already have.
-  const uint8_t* vp = stage + lo.v;
   auto vread = [&](int step) -> bf16x8 {
     const int dt = step >> 2, ss = step & 3;
-    const uint8_t* a0 = vp + (16 * ss) * kRowBytes + 64 * dt;
+    const uint8_t* a0 = stage + lo.v[dt] + (16 * ss) * 256;
     const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
-    const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0 + 8 * kRowBytes));
+    const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0 + 8 * 256));
     const i16x8 cat = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(bf16x8, cat);
   };
@@ -206,35 +216,46 @@ __device__ __forceinline__ void attn_chunk(const uint8_t* stage, const LaneOffse
 }
 
 // Gather one chunk of 64 keys straight from global memory into the K and V tiles of `stage`
-// (global_load_lds: every wave-wide instruction fills 64 consecutive 16-byte slots; slot s of a
-// tile is row s / 17, piece s % 17, and piece 16 is padding). Invalid keys read row 0 of the
-// group (finite data, always masked out through the token table). Waves of the workgroup split
-// the 17 + 17 instructions. The token table is written by the first wave.
+// (global_load_lds: every wave-wide instruction fills 64 consecutive 16-byte slots). K: slot s of
+// the tile is row s / 17, piece s % 17 (piece 16 is padding). V: slot s is row s / 16, physical
+// piece s % 16, holding logical piece v_phys(row, s % 16). Invalid keys read row 0 of the group
+// (finite data, always masked out through the token table). The waves of the workgroup split the
+// 17 + 16 instructions; the first wave writes the token table.
 template <int NT, typename TokFn>
 __device__ __forceinline__ void chunk_issue(uint8_t* stage, const uint16_t* kbase, const uint16_t* vbase,
                                             TokFn tok_of) {
   constexpr int kWaves = NT / 64;
-  const int l = lane_id(), wave = threadIdx.x >> 6;
+  constexpr int kInsts = kKTileInsts + kVTileInsts;
+  const int l = lane_id();
+  // NT == 64: one wave fills the stage alone (it may be any wave of a larger workgroup).
+  const int tid = kWaves == 1 ? l : (int)threadIdx.x;
+  const int wave = kWaves == 1 ? 0 : (int)threadIdx.x >> 6;
 #pragma unroll
-  for (int x = 0; x < (2 * kTileInsts + kWaves - 1) / kWaves; ++x) {
+  for (int x = 0; x < (kInsts + kWaves - 1) / kWaves; ++x) {
     const int inst = wave + x * kWaves;
-    if (inst < 2 * kTileInsts) {
-      const bool is_v = inst >= kTileInsts;
-      const int ti = is_v ? inst - kTileInsts : inst;
+    if (inst < kInsts) {
+      const bool is_v = inst >= kKTileInsts;
+      const int ti = is_v ? inst - kKTileInsts : inst;
       const int slot = ti * 64 + l;
-      const int row = slot / kSlotsPerRow;
-      int piece = slot - row * kSlotsPerRow;
-      if (piece == 16) piece = 0;  // padding slot: any in-bounds data
+      int row, piece;
+      if (is_v) {
+        row = slot >> 4;
+        piece = v_phys(row, slot & 15);
+      } else {
+        row = slot / kKSlotsPerRow;
+        piece = slot - row * kKSlotsPerRow;
+        if (piece == 16) piece = 0;  // padding slot: any in-bounds data
+      }
       int tkn = tok_of(row);
       if (tkn < 0) tkn = 0;
       const uint16_t* src = (is_v ? vbase : kbase) + (long long)tkn * kD + piece * 8;
-      uint8_t* dst = stage + (is_v ? kTileBytes : 0) + ti * 1024;
+      uint8_t* dst = stage + (is_v ? kKTileBytes : 0) + ti * 1024;
       __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)dst, 16, 0, 0);
     }
   }
-  if (threadIdx.x < kKeys) {
-    const int t = tok_of((int)threadIdx.x);
-    reinterpret_cast<int*>(stage + 2 * kTileBytes)[threadIdx.x] = t >= 0 ? t : 0x7FFFFFFF;
+  if (tid < kKeys) {
+    const int t = tok_of(tid);
+    reinterpret_cast<int*>(stage + kKTileBytes + kVTileBytes)[tid] = t >= 0 ? t : 0x7FFFFFFF;
   }
 }
 
@@ -460,38 +481,39 @@ hipError_t launch_attend(const uint16_t* q, const uint16_t* k, const uint16_t* v
 
 // ------------------------------------------------------------------------------------ decode
 
-// Split-K decode attention. Workgroup (one wave) = (sequence s, group g, split p): the Q rows are
-// the r heads of group g (one 32-row tile, r <= 32 valid); its keys are list entries
-// [p*per, (p+1)*per) of Sel(s,g) + {own block}. Writes unnormalised partial O, max and sum.
-__global__ __launch_bounds__(64) void k_decode_attend(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
-                                                      const uint16_t* __restrict__ vc,
-                                                      const int32_t* __restrict__ sel, float* __restrict__ part_o,
-                                                      float* __restrict__ part_ml, int n_seqs, int ctx, int n_q_heads,
-                                                      int n_groups, int block, int block_shift, int kb, int n_split,
-                                                      int per_split, float scale_log2) {
-  constexpr int NT = 64;
+// Decode attention: one workgroup of 4 waves per (sequence s, group g). The attended blocks are
+// Sel(s,g) (ascending) plus the own block; wave w streams chunks w, w+4, ... through its own LDS
+// buffer (HBM-bound: four independent chunk streams per CU keep enough bytes in flight), keeps its
+// own online-softmax state for the r heads (one 32-row tile, r <= 32 rows used), and the four
+// states are merged in LDS into the bf16 output.
+__global__ __launch_bounds__(256) void k_decode_attend(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+                                                       const uint16_t* __restrict__ vc,
+                                                       const int32_t* __restrict__ sel, uint16_t* __restrict__ out,
+                                                       int ctx, int n_q_heads, int n_groups, int block,
+                                                       int block_shift, int kb, float scale_log2) {
+  constexpr int kWavesD = 4;
   extern __shared__ __align__(16) uint8_t smem[];
-  uint8_t* stage = smem;
-  int* blocks = reinterpret_cast<int*>(smem + 2 * kStageBytes);  // per_split entries
+  const int wave = threadIdx.x >> 6;
+  uint8_t* stage = smem + wave * kStageBytes;  // this wave's K tile, V tile, token table
+  int* blocks = reinterpret_cast<int*>(smem + kWavesD * kStageBytes);  // kb + 1 entries
+  __shared__ int n_sel_shared;
 
-  const int p = blockIdx.x % n_split;
-  const int sg = blockIdx.x / n_split;
-  const int s = sg / n_groups, g = sg % n_groups;
+  const int s = blockIdx.x / n_groups, g = blockIdx.x % n_groups;
   const int r = n_q_heads / n_groups;
   const int l = lane_id();
   const int i_q = ctx - 1;
   const int own = i_q / block;
 
-  // Entries of this split: Sel entries (ascending, -1 padded) then the own block.
+  // Entries: Sel (ascending, -1 padded at the end) then the own block.
   const int32_t* srow = sel + ((long long)s * n_groups + g) * kb;
-  int n_sel = 0;
-  for (int e = l; e < kb; e += 64) n_sel += srow[e] >= 0 ? 1 : 0;
-  for (int off = 32; off >= 1; off >>= 1) n_sel += __shfl_xor(n_sel, off, 64);
-  const int n_ent = n_sel + 1;
-  const int e0 = p * per_split;
-  const int e1 = min(n_ent, e0 + per_split);
-  const int n_here = max(0, e1 - e0);
-  for (int e = l; e < n_here; e += 64) blocks[e] = (e0 + e < n_sel) ? srow[e0 + e] : own;
+  if (wave == 0) {
+    int cnt = 0;
+    for (int base = 0; base < kb; base += 64) cnt += popc64(ballot(base + l < kb && srow[base + l] >= 0));
+    if (l == 0) n_sel_shared = cnt;
+  }
+  __syncthreads();
+  const int n_sel = n_sel_shared;
+  for (int e = threadIdx.x; e <= n_sel; e += blockDim.x) blocks[e] = e < n_sel ? srow[e] : own;
   __syncthreads();
 
   bf16x8 qreg[1][8];
@@ -516,105 +538,69 @@ __global__ __launch_bounds__(64) void k_decode_attend(const uint16_t* __restrict
   const long long seq_off = ((long long)s * n_groups + g) * ctx * kD;
   const uint16_t* kbase = kc + seq_off;
   const uint16_t* vbase = vc + seq_off;
-  const int n_keys = n_here * block;
+  const int n_keys = (n_sel + 1) * block;
   const int n_chunks = (n_keys + kKeys - 1) / kKeys;
-  auto tok_at = [&](int chunk, int key) -> int {
-    const int kp = chunk * kKeys + key;
-    if (kp >= n_keys) return -1;
-    const int tk = (blocks[kp >> block_shift] << block_shift) + (kp & (block - 1));
-    return tk < ctx ? tk : -1;
-  };
   const LaneOffsets lo = lane_offsets();
-  if (n_chunks > 0) chunk_issue<NT>(stage, kbase, vbase, [&](int key) { return tok_at(0, key); });
-  wait_vm();
-  __syncthreads();
-  for (int n = 0; n < n_chunks; ++n) {
-    const int buf = n & 1;
-    const bool has_next = n + 1 < n_chunks;
-    if (has_next)
-      chunk_issue<NT>(stage + (buf ^ 1) * kStageBytes, kbase, vbase, [&](int key) { return tok_at(n + 1, key); });
-    attn_chunk<1>(stage + buf * kStageBytes, lo, qreg, st, scale_log2, true, row_pos);
+  for (int c = wave; c < n_chunks; c += kWavesD) {
+    auto tok_at = [&](int key) -> int {
+      const int kp = c * kKeys + key;
+      if (kp >= n_keys) return -1;
+      const int tk = (blocks[kp >> block_shift] << block_shift) + (kp & (block - 1));
+      return tk < ctx ? tk : -1;
+    };
+    chunk_issue<64>(stage, kbase, vbase, tok_at);
     wait_vm();
-    __syncthreads();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    attn_chunk<1>(stage, lo, qreg, st, scale_log2, true, row_pos);
   }
-  // Partials: part_o [S][G][n_split][r][D], part_ml [S][G][n_split][r][2]
-  const int hh = l & 31;
+
+  // Merge the four wave states: O^T tiles to LDS (reusing the wave's stage), then 256 threads
+  // combine r x 128 outputs.
   const float l_all = st.l[0] + __shfl_xor(st.l[0], 32, 64);
-  if (hh < r) {
-    const long long pr = (((long long)s * n_groups + g) * n_split + p) * r + hh;
-    float* dst = part_o + pr * kD;
+  float* o_lds = reinterpret_cast<float*>(stage);  // [32 rows][128]
+  float* ml_lds = reinterpret_cast<float*>(smem + kWavesD * kStageBytes) + (kb + 1);  // [4][32][2]
+  __syncthreads();  // every wave is done with its stage
+  {
+    const int row = l & 31;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int d = dt * 32 + 8 * a + 4 * (l >> 5);
-        *reinterpret_cast<float4*>(dst + d) =
-            make_float4(st.o[0][dt][4 * a], st.o[0][dt][4 * a + 1], st.o[0][dt][4 * a + 2], st.o[0][dt][4 * a + 3]);
+      for (int j = 0; j < 16; ++j) {
+        const int d = dt * 32 + 8 * (j >> 2) + 4 * (l >> 5) + (j & 3);
+        o_lds[row * kD + d] = st.o[0][dt][j];
       }
     if (l < 32) {
-      part_ml[pr * 2 + 0] = st.m[0];
-      part_ml[pr * 2 + 1] = l_all;
+      ml_lds[(wave * 32 + row) * 2 + 0] = st.m[0];
+      ml_lds[(wave * 32 + row) * 2 + 1] = l_all;
     }
   }
-}
-
-// Fixed-order combine of the split partials: one workgroup (128 threads = D) per (s, head).
-__global__ __launch_bounds__(128) void k_decode_combine(const float* __restrict__ part_o,
-                                                        const float* __restrict__ part_ml, uint16_t* __restrict__ out,
-                                                        int n_q_heads, int n_groups, int n_split) {
-  const int sh = blockIdx.x;
-  const int s = sh / n_q_heads, h = sh % n_q_heads;
-  const int r = n_q_heads / n_groups;
-  const int g = h / r, hh = h % r;
-  const int d = threadIdx.x;
-  float m = kMinit;
-  for (int p = 0; p < n_split; ++p) {
-    const long long pr = (((long long)s * n_groups + g) * n_split + p) * r + hh;
-    m = fmaxf(m, part_ml[pr * 2]);
+  __syncthreads();
+  for (int x = threadIdx.x; x < r * kD; x += blockDim.x) {
+    const int row = x / kD, d = x % kD;
+    float m = -1.0e30f;
+    for (int w = 0; w < kWavesD; ++w) m = fmaxf(m, ml_lds[(w * 32 + row) * 2]);
+    float num = 0.0f, den = 0.0f;
+    for (int w = 0; w < kWavesD; ++w) {
+      const float f = fast_exp2(ml_lds[(w * 32 + row) * 2] - m);
+      den += ml_lds[(w * 32 + row) * 2 + 1] * f;
+      num += reinterpret_cast<const float*>(smem + w * kStageBytes)[row * kD + d] * f;
+    }
+    out[((long long)s * n_q_heads + g * r + row) * kD + d] = (uint16_t)f32_to_bf16_bits(num / den);
   }
-  float acc = 0.0f, den = 0.0f;
-  for (int p = 0; p < n_split; ++p) {
-    const long long pr = (((long long)s * n_groups + g) * n_split + p) * r + hh;
-    const float wgt = exp2f(part_ml[pr * 2] - m);
-    den += part_ml[pr * 2 + 1] * wgt;
-    acc += part_o[pr * kD + d] * wgt;
-  }
-  out[((long long)s * n_q_heads + h) * kD + d] = (uint16_t)f32_to_bf16_bits(acc / den);
 }
 
-size_t decode_attend_part_bytes(int n_seqs, int n_q_heads, int n_split) {
-  return (size_t)n_seqs * n_q_heads * n_split * (kD + 2) * sizeof(float);
-}
-
-int decode_split_count(int kb) {
-  // Entries (<= kb + 1) per split: about 32 blocks each.
-  const int n = (kb + 1 + 31) / 32;
-  return n < 1 ? 1 : n;
-}
+size_t decode_attend_lds(int kb) { return (size_t)4 * kStageBytes + (size_t)(kb + 1) * 4 + 4 * 32 * 2 * 4; }
 
 hipError_t launch_decode_attend(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, const int32_t* sel,
-                                void* part_ws, uint16_t* out, int n_seqs, int ctx, int n_q_heads, int n_groups,
-                                int block, int kb, float scale, hipStream_t stream) {
-  const int n_split = decode_split_count(kb);
-  const int per_split = (kb + 1 + n_split - 1) / n_split;
-  float* part_o = reinterpret_cast<float*>(part_ws);
-  float* part_ml = part_o + (size_t)n_seqs * n_q_heads * n_split * kD;
-  const size_t lds = (size_t)2 * kStageBytes + (size_t)per_split * 4;
+                                uint16_t* out, int n_seqs, int ctx, int n_q_heads, int n_groups, int block, int kb,
+                                float scale, hipStream_t stream) {
+  const size_t lds = decode_attend_lds(kb);
   if (lds > (size_t)max_lds_per_block()) return hipErrorInvalidValue;
-  if (lds > 65536) {
-    hipError_t e =
-        hipFuncSetAttribute((const void*)k_decode_attend, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  const float scale_log2 = scale * 1.4426950408889634f;
-  const long long grid = (long long)n_seqs * n_groups * n_split;
-  hipLaunchKernelGGL(k_decode_attend, dim3((unsigned)grid), dim3(64), lds, stream, q, kc, vc, sel, part_o, part_ml,
-                     n_seqs, ctx, n_q_heads, n_groups, block, __builtin_ctz(block), kb, n_split, per_split,
-                     scale_log2);
-  hipError_t e = hipGetLastError();
+  hipError_t e = hipFuncSetAttribute((const void*)k_decode_attend, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_decode_combine, dim3((unsigned)(n_seqs * n_q_heads)), dim3(kD), 0, stream, part_o, part_ml, out,
-                     n_q_heads, n_groups, n_split);
+  const float scale_log2 = scale * 1.4426950408889634f;
+  hipLaunchKernelGGL(k_decode_attend, dim3((unsigned)(n_seqs * n_groups)), dim3(256), lds, stream, q, kc, vc, sel, out,
+                     ctx, n_q_heads, n_groups, block, __builtin_ctz(block), kb, scale_log2);
   return hipGetLastError();
 }
 

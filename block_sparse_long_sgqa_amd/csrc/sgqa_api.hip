@@ -82,6 +82,7 @@ int check_params(const sgqa_params* p, int need, bool prefill) {
   }
   if (need & NEED_DSELECT) {
     if (decode_select_lds(p->n_kv_heads, kb_of(p)) > kGfx950LdsBytes) return SGQA_ERR_SHAPE;
+    if (decode_attend_lds(kb_of(p)) > kGfx950LdsBytes) return SGQA_ERR_SHAPE;
   }
   if (need & NEED_UNION) {
     if (p->union_tile < 1) return SGQA_ERR_SHAPE;
@@ -131,7 +132,6 @@ PrefillWs prefill_layout(const sgqa_params* p, void* ws) {
 struct DecodeWs {
   int32_t* sel;
   void* select_ws;
-  void* part;
   size_t bytes;
 };
 
@@ -144,8 +144,6 @@ DecodeWs decode_layout(const sgqa_params* p, void* ws) {
   off += round_up((size_t)p->n_seqs * p->n_kv_heads * kb * 4);
   l.select_ws = b ? b + off : nullptr;
   off += round_up(decode_select_ws_bytes(p->n_seqs, p->n_tokens, p->n_kv_heads, p->block, kb));
-  l.part = b ? b + off : nullptr;
-  off += round_up(decode_attend_part_bytes(p->n_seqs, p->n_q_heads, decode_split_count(kb)));
   l.bytes = off;
   return l;
 }
@@ -303,7 +301,7 @@ int sgqa_decode(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k_cac
   hipError_t e = launch_decode_select(idx_q, idx_w, blk_k, l.sel, topk_out, l.select_ws, p->n_seqs, p->n_tokens,
                                       p->n_kv_heads, p->block, kb, s);
   if (e == hipSuccess)
-    e = launch_decode_attend(q, k_cache, v_cache, l.sel, l.part, out, p->n_seqs, p->n_tokens, p->n_q_heads,
+    e = launch_decode_attend(q, k_cache, v_cache, l.sel, out, p->n_seqs, p->n_tokens, p->n_q_heads,
                              p->n_kv_heads, p->block, kb, scale_of(p), s);
   return status_of(e);
 }

@@ -33,17 +33,16 @@ hipError_t launch_decode_select(const uint16_t* qi, const float* w, const uint16
                                 int32_t* topk_out, void* ws, int n_seqs, int n_tokens, int n_groups, int block, int kb,
                                 hipStream_t stream);
 
-// Decode attention over Sel + own block: split-K partials (decode_attend_part_bytes of workspace)
-// and a fixed-order combine into out [S][Hq][D].
-size_t decode_attend_part_bytes(int n_seqs, int n_q_heads, int n_split);
-int decode_split_count(int kb);
+// Decode attention over Sel + own block, one workgroup per (sequence, group), straight into
+// out [S][Hq][D] (no workspace).
 hipError_t launch_decode_attend(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, const int32_t* sel,
-                                void* part_ws, uint16_t* out, int n_seqs, int ctx, int n_q_heads, int n_groups,
+                                uint16_t* out, int n_seqs, int ctx, int n_q_heads, int n_groups,
                                 int block, int kb, float scale, hipStream_t stream);
 
 // LDS a launch needs (validation rejects shapes that do not fit before anything is enqueued).
 size_t index_topk_lds_min(int kb);
 size_t decode_select_lds(int n_groups, int kb);
+size_t decode_attend_lds(int kb);
 size_t attend_lds_bytes_for(int n_tokens, int block);
 constexpr size_t kGfx950LdsBytes = 160 * 1024;
 
