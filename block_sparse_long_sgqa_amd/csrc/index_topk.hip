@@ -24,8 +24,7 @@
 //    order-preserving 32-bit key, counting with wave ballots (no atomics).
 //  * Pass 2 recomputes the scores and emits, in ascending block order, every candidate with
 //    s > tau plus the lowest-id candidates with s == tau (ballot + popcount compaction).
-//  * The decode form runs the same two passes on slices of one sequence's candidates and emits
-//    (key, id) lists; k_select_merge merges the slices of a (sequence, group) with the same logic.
+//  * Decode selection (one query, many candidates) is shaped differently and lives on its own.
 #include "sgqa_device.hpp"
 #include "sgqa_internal.hpp"
 
@@ -137,21 +136,13 @@ __device__ __forceinline__ uint32_t wave_trim_keys(uint32_t* keys, int n, int K)
 
 }  // namespace
 
-// Row parameters of the two uses of the selection kernel.
-//  PREFILL: row = (i, g) flattened as i*G + g (largest rows first); candidates [0, c(i)); output
-//           the ascending ids into topk [G][N][K_B] (-1 padded).
-//  DECODE:  workgroup = (sequence s, candidate slice sl); row = group g; candidates
-//           [sl*slice, min(c, (sl+1)*slice)), c = floor((L-1)/B); output the slice's local top-K_B
-//           as (key, id) lists in ascending id order plus counts. A candidate of the global
-//           top-K_B is beaten by fewer than K_B others overall, hence inside its slice too, so the
-//           merge of the slice lists (k_select_merge) is exact.
-template <int WAVES, bool DECODE, int P>
+// Row = (i, g) flattened as i*G + g (largest rows first); candidates [0, c(i)); output the
+// ascending ids into topk [G][N][K_B] (-1 padded).
+template <int WAVES, int P>
 __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restrict__ qi, const float* __restrict__ w,
-                                                       const uint16_t* __restrict__ kbar_all,
-                                                       int32_t* __restrict__ topk, uint32_t* __restrict__ part_keys,
-                                                       uint32_t* __restrict__ part_ids,
-                                                       int32_t* __restrict__ part_cnt, int n_tokens, int n_groups,
-                                                       int block, int kb, int cap, int n_slices, int slice_len) {
+                                                       const uint16_t* __restrict__ kbar,
+                                                       int32_t* __restrict__ topk, int n_tokens, int n_groups,
+                                                       int block, int kb, int cap) {
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* stage = smem;                                                        // 2 x kStageBytes
   uint32_t* keys_all = reinterpret_cast<uint32_t*>(smem + 2 * kStageBytes);     // 4*WAVES x cap
@@ -163,30 +154,17 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
   const int l16 = l & 15;
   const uint32_t lt16 = (1u << l16) - 1u;
 
-  long long r0, n_rows;
-  int seq = 0, slice = 0, lo = 0, hi_all = 0;
-  const uint16_t* kbar = kbar_all;
-  if (DECODE) {
-    seq = blockIdx.x / n_slices;
-    slice = blockIdx.x % n_slices;
-    r0 = 0;
-    n_rows = n_groups;
-    const int c = (n_tokens - 1) / block;
-    lo = slice * slice_len;
-    hi_all = min(c, lo + slice_len);
-    kbar = kbar_all + (long long)seq * (n_tokens / block) * kIdxDim;
-  } else {
-    const long long wg = (long long)gridDim.x - 1 - blockIdx.x;  // largest rows first
-    r0 = wg * kRowsPerWg;
-    n_rows = (long long)n_tokens * n_groups;
-    const long long r_last = (r0 + kRowsPerWg - 1 < n_rows) ? r0 + kRowsPerWg - 1 : n_rows - 1;
-    hi_all = (int)(r_last / n_groups) / block;  // the last row has the most candidates
-  }
+  const long long wg = (long long)gridDim.x - 1 - blockIdx.x;  // largest rows first
+  const long long r0 = wg * kRowsPerWg;
+  const long long n_rows = (long long)n_tokens * n_groups;
+  const long long r_last = (r0 + kRowsPerWg - 1 < n_rows) ? r0 + kRowsPerWg - 1 : n_rows - 1;
+  const int lo = 0;
+  const int hi_all = (int)(r_last / n_groups) / block;  // the last row has the most candidates
   const int n_blocks = n_tokens / block;
 
-  auto row_group = [&](long long row) -> int { return DECODE ? (int)row : (int)(row % n_groups); };
-  auto row_qi = [&](long long row) -> long long { return DECODE ? (long long)seq * n_groups + row : row; };
-  auto row_hi = [&](long long row) -> int { return DECODE ? hi_all : (int)(row / n_groups) / block; };
+  auto row_group = [&](long long row) -> int { return (int)(row % n_groups); };
+  auto row_qi = [&](long long row) -> long long { return row; };
+  auto row_hi = [&](long long row) -> int { return (int)(row / n_groups) / block; };
 
   // The row whose scores this lane produces: row `quarter` of the wave.
   const long long row_o = r0 + wave * 4 + quarter;
@@ -195,7 +173,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
   const int hi_lane = valid_o ? row_hi(row_o) : 0;
   const int n_cand = max(0, hi_lane - lo);  // candidates of this lane's row
 
-  if (!DECODE && hi_all <= kb) {
+  if (hi_all <= kb) {
     // Every row has at most K_B candidates: all of them are selected.
     for (int q = 0; q < 4; ++q) {
       const long long row = r0 + wave * 4 + q;
@@ -375,18 +353,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
 
   // ------------------------------------------------------------------ pass 2: emit in order
   int n_out = 0, t_seen = 0;  // uniform over the quarter
-  int32_t* out_row = nullptr;
-  uint32_t* pk_row = nullptr;
-  uint32_t* pi_row = nullptr;
-  if (valid_o) {
-    if (DECODE) {
-      const long long base = (((long long)seq * n_slices + slice) * n_groups + row_o) * kb;
-      pk_row = part_keys + base;
-      pi_row = part_ids + base;
-    } else {
-      out_row = topk + ((long long)g_o * n_tokens + row_o / n_groups) * kb;
-    }
-  }
+  int32_t* out_row = valid_o ? topk + ((long long)g_o * n_tokens + row_o / n_groups) * kb : nullptr;
   auto emit = [&](float sc, int b, bool valid) {
     const bool gt = valid && sc > tau_f;
     const bool eq = valid && sc == tau_f;
@@ -395,98 +362,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
     const uint32_t km16 = (uint32_t)(ballot(keep) >> (16 * quarter)) & 0xFFFFu;
     if (keep) {
       const int pos = n_out + __popc(km16 & lt16);
-      if (DECODE) {
-        pk_row[pos] = score_key(sc);
-        pi_row[pos] = (uint32_t)b;
-      } else {
-        out_row[pos] = b;
-      }
+      out_row[pos] = b;
     }
     n_out += __popc(km16);
     t_seen += __popc(em16);
   };
   stream(n_all, 1, 0, emit, nothing);
   // Padding / counts.
-  if (valid_o) {
-    if (DECODE) {
-      if (l16 == 0) part_cnt[((long long)seq * n_slices + slice) * n_groups + row_o] = n_out;
-    } else {
-      for (int e = n_out + l16; e < kb; e += 16) out_row[e] = -1;
-    }
-  }
-}
-
-// Decode merge: one wave per (sequence, group). The slice lists, concatenated in slice order, are
-// in ascending id order; pass 1 finds tau and the tie count from their keys, pass 2 emits.
-template <int P>
-__global__ __launch_bounds__(64) void k_select_merge(const uint32_t* __restrict__ part_keys,
-                                                     const uint32_t* __restrict__ part_ids,
-                                                     const int32_t* __restrict__ part_cnt, int32_t* __restrict__ sel,
-                                                     int32_t* __restrict__ topk_out, int n_groups, int kb, int cap,
-                                                     int n_slices) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  uint32_t* keys = reinterpret_cast<uint32_t*>(smem);
-  const int s = blockIdx.x / n_groups, g = blockIdx.x % n_groups;
-  const int l = lane_id();
-  const uint64_t lt = lanemask_lt();
-  int n = 0, total = 0;
-  uint32_t accept = 0u;  // keys >= accept are kept
-  for (int ch = 0; ch < n_slices; ++ch) {
-    const long long pr = ((long long)s * n_slices + ch) * n_groups + g;
-    const int cnt = part_cnt[pr];
-    total += cnt;
-    for (int base = 0; base < cnt; base += 64) {
-      const int e = base + l;
-      const uint32_t key = e < cnt ? part_keys[pr * kb + e] : 0u;
-      const bool pass = e < cnt && key >= accept;
-      const uint64_t m = ballot(pass);
-      if (pass) keys[n + popc64(m & lt)] = key;
-      n += popc64(m);
-      if (n + 64 > cap) {
-        lds_wait();
-        accept = wave_trim_keys<P>(keys, n, kb) + 1u;
-        n = kb;
-      }
-    }
-  }
-  lds_wait();
-  uint32_t tau = 0u;
-  int ties = 0;
-  const bool all = total <= kb;  // fewer candidates than K_B: keep every one
-  if (!all) {
-    int above;
-    tau = wave_kth_largest<P>(keys, n, kb, &above);
-    ties = kb - above;
-  }
-  int32_t* dst = sel + ((long long)s * n_groups + g) * kb;
-  int32_t* dst2 = topk_out ? topk_out + ((long long)s * n_groups + g) * kb : nullptr;
-  int n_out = 0, t_seen = 0;
-  for (int ch = 0; ch < n_slices; ++ch) {
-    const long long pr = ((long long)s * n_slices + ch) * n_groups + g;
-    const int cnt = part_cnt[pr];
-    for (int base = 0; base < cnt; base += 64) {
-      const int e = base + l;
-      const bool v = e < cnt;
-      const uint32_t key = v ? part_keys[pr * kb + e] : 0u;
-      const int32_t id = v ? (int32_t)part_ids[pr * kb + e] : 0;
-      const bool gt = v && (all || key > tau);
-      const bool eq = v && !all && key == tau;
-      const uint64_t em = ballot(eq);
-      const bool keep = gt || (eq && t_seen + popc64(em & lt) < ties);
-      const uint64_t km = ballot(keep);
-      if (keep) {
-        const int pos = n_out + popc64(km & lt);
-        dst[pos] = id;
-        if (dst2) dst2[pos] = id;
-      }
-      n_out += popc64(km);
-      t_seen += popc64(em);
-    }
-  }
-  for (int e = n_out + l; e < kb; e += 64) {
-    dst[e] = -1;
-    if (dst2) dst2[e] = -1;
-  }
+  if (valid_o)
+    for (int e = n_out + l16; e < kb; e += 16) out_row[e] = -1;
 }
 
 namespace {
@@ -525,12 +409,6 @@ size_t index_topk_lds_min(int kb) {
   return cap > 0 ? select_lds_bytes(1, cap) : kGfx950LdsBytes + 1;
 }
 
-size_t decode_select_lds(int n_groups, int kb) {
-  const int waves = (n_groups + 3) / 4;
-  const int cap = select_cap(waves, kb, kGfx950LdsBytes);
-  return cap > 0 ? select_lds_bytes(waves, cap) : kGfx950LdsBytes + 1;
-}
-
 hipError_t launch_index_topk(const uint16_t* qi, const float* w, const uint16_t* kbar, int32_t* topk, int n_tokens,
                              int n_groups, int block, int kb, hipStream_t stream) {
   const long long n_rows = (long long)n_tokens * n_groups;
@@ -544,11 +422,11 @@ hipError_t launch_index_topk(const uint16_t* qi, const float* w, const uint16_t*
   const int pk = keys_per_lane(cap);
 #define SGQA_TOPK_CASE(WV, PK)                                                                                   \
   if (waves == WV && pk == PK) {                                                                                 \
-    hipError_t e = hipFuncSetAttribute((const void*)k_select<WV, false, PK>,                                     \
+    hipError_t e = hipFuncSetAttribute((const void*)k_select<WV, PK>,                                     \
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                    \
     if (e != hipSuccess) return e;                                                                               \
-    hipLaunchKernelGGL((k_select<WV, false, PK>), dim3((unsigned)grid), dim3(WV * 64), lds, stream, qi, w, kbar, \
-                       topk, nullptr, nullptr, nullptr, n_tokens, n_groups, block, kb, cap, 0, 0);               \
+    hipLaunchKernelGGL((k_select<WV, PK>), dim3((unsigned)grid), dim3(WV * 64), lds, stream, qi, w, kbar,       \
+                       topk, n_tokens, n_groups, block, kb, cap);                                                 \
     return hipGetLastError();                                                                                    \
   }
   SGQA_TOPK_CASE(8, 16)
@@ -561,80 +439,6 @@ hipError_t launch_index_topk(const uint16_t* qi, const float* w, const uint16_t*
   SGQA_TOPK_CASE(1, 32)
   SGQA_TOPK_CASE(1, 64)
 #undef SGQA_TOPK_CASE
-  return hipErrorInvalidValue;
-  return hipGetLastError();
-}
-
-int decode_slice_len() { return 1024; }
-
-int decode_slice_count(int n_tokens, int block) {
-  const int c = (n_tokens - 1) / block;
-  const int n = (c + decode_slice_len() - 1) / decode_slice_len();
-  return n < 1 ? 1 : n;
-}
-
-size_t decode_select_ws_bytes(int n_seqs, int n_tokens, int n_groups, int block, int kb) {
-  const size_t n_sl = (size_t)decode_slice_count(n_tokens, block);
-  return (size_t)n_seqs * n_sl * n_groups * ((size_t)kb * 8 + 4);
-}
-
-hipError_t launch_decode_select(const uint16_t* qi, const float* w, const uint16_t* kbar, int32_t* sel,
-                                int32_t* topk_out, void* ws, int n_seqs, int n_tokens, int n_groups, int block, int kb,
-                                hipStream_t stream) {
-  const int n_slices = decode_slice_count(n_tokens, block);
-  const size_t n_lists = (size_t)n_seqs * n_slices * n_groups;
-  uint32_t* part_keys = reinterpret_cast<uint32_t*>(ws);
-  uint32_t* part_ids = part_keys + n_lists * kb;
-  int32_t* part_cnt = reinterpret_cast<int32_t*>(part_ids + n_lists * kb);
-  const size_t budget = (size_t)max_lds_per_block();
-  const int waves = (n_groups + 3) / 4;
-  const int cap = select_cap(waves, kb, budget);
-  if (cap == 0) return hipErrorInvalidValue;
-  const size_t lds = select_lds_bytes(waves, cap);
-  const long long grid = (long long)n_seqs * n_slices;
-  const int pk = keys_per_lane(cap);
-  hipError_t e = hipErrorInvalidValue;
-#define SGQA_DSEL_CASE(WV, PK)                                                                                   \
-  if (waves == WV && pk == PK) {                                                                                 \
-    e = hipFuncSetAttribute((const void*)k_select<WV, true, PK>, hipFuncAttributeMaxDynamicSharedMemorySize,     \
-                            (int)lds);                                                                           \
-    if (e != hipSuccess) return e;                                                                               \
-    hipLaunchKernelGGL((k_select<WV, true, PK>), dim3((unsigned)grid), dim3(WV * 64), lds, stream, qi, w, kbar,  \
-                       nullptr, part_keys, part_ids, part_cnt, n_tokens, n_groups, block, kb, cap, n_slices,     \
-                       decode_slice_len());                                                                      \
-    e = hipGetLastError();                                                                                       \
-  }
-  SGQA_DSEL_CASE(1, 16)
-  SGQA_DSEL_CASE(1, 32)
-  SGQA_DSEL_CASE(1, 64)
-  SGQA_DSEL_CASE(2, 16)
-  SGQA_DSEL_CASE(2, 32)
-  SGQA_DSEL_CASE(2, 64)
-  SGQA_DSEL_CASE(3, 16)
-  SGQA_DSEL_CASE(3, 32)
-  SGQA_DSEL_CASE(4, 16)
-  SGQA_DSEL_CASE(4, 32)
-#undef SGQA_DSEL_CASE
-  if (e != hipSuccess) return e;
-  int mcap = 2 * kb + 64;
-  if (mcap > 4096) mcap = 4096;
-  const int mpk = keys_per_lane(mcap);
-  const size_t mlds = (size_t)mcap * 4;
-#define SGQA_MERGE_CASE(PK)                                                                                       \
-  if (mpk == PK) {                                                                                                \
-    if (mlds > 65536) {                                                                                           \
-      e = hipFuncSetAttribute((const void*)k_select_merge<PK>, hipFuncAttributeMaxDynamicSharedMemorySize,        \
-                              (int)mlds);                                                                         \
-      if (e != hipSuccess) return e;                                                                              \
-    }                                                                                                             \
-    hipLaunchKernelGGL(k_select_merge<PK>, dim3((unsigned)(n_seqs * n_groups)), dim3(64), mlds, stream,          \
-                       part_keys, part_ids, part_cnt, sel, topk_out, n_groups, kb, mcap, n_slices);               \
-    return hipGetLastError();                                                                                     \
-  }
-  SGQA_MERGE_CASE(16)
-  SGQA_MERGE_CASE(32)
-  SGQA_MERGE_CASE(64)
-#undef SGQA_MERGE_CASE
   return hipErrorInvalidValue;
 }
 

@@ -60,7 +60,7 @@ float scale_of(const sgqa_params* p) {
 }
 
 // Checks shared by the calls; `need` selects which groups of fields matter.
-enum { NEED_INDEX = 1, NEED_ATTN = 2, NEED_SELECT = 4, NEED_UNION = 8, NEED_LIST = 16, NEED_DSELECT = 32 };
+enum { NEED_INDEX = 1, NEED_ATTN = 2, NEED_SELECT = 4, NEED_UNION = 8, NEED_LIST = 16, NEED_DECODE = 32 };
 
 int check_params(const sgqa_params* p, int need, bool prefill) {
   if (!p) return SGQA_ERR_NULL;
@@ -80,8 +80,7 @@ int check_params(const sgqa_params* p, int need, bool prefill) {
     if (p->n_kv_heads > 16) return SGQA_ERR_SHAPE;
     if (index_topk_lds_min(kb_of(p)) > kGfx950LdsBytes) return SGQA_ERR_SHAPE;
   }
-  if (need & NEED_DSELECT) {
-    if (decode_select_lds(p->n_kv_heads, kb_of(p)) > kGfx950LdsBytes) return SGQA_ERR_SHAPE;
+  if (need & NEED_DECODE) {
     if (decode_attend_lds(kb_of(p)) > kGfx950LdsBytes) return SGQA_ERR_SHAPE;
   }
   if (need & NEED_UNION) {
@@ -204,7 +203,7 @@ int sgqa_workspace_size(const sgqa_params* p, int op, size_t* bytes) {
       if (st == SGQA_OK) *bytes = prefill_layout(p, nullptr).bytes;
       return st;
     case SGQA_OP_DECODE:
-      st = check_params(p, NEED_INDEX | NEED_SELECT | NEED_DSELECT | NEED_ATTN, false);
+      st = check_params(p, NEED_INDEX | NEED_SELECT | NEED_DECODE | NEED_ATTN, false);
       if (st == SGQA_OK) *bytes = decode_layout(p, nullptr).bytes;
       return st;
     default:
@@ -215,7 +214,7 @@ int sgqa_workspace_size(const sgqa_params* p, int op, size_t* bytes) {
 int sgqa_compress(const sgqa_params* p, const sgqa_bf16* idx_k, sgqa_bf16* blk_k, sgqa_stream stream) {
   int st = check_params(p, NEED_INDEX, false);
   if (st) return st;
-  if (!idx_k || !blk_k) return SGQA_ERR_NULL;
+  if (!idx_k || (!blk_k && p->n_tokens >= p->block)) return SGQA_ERR_NULL;  // N < B: nothing to write
   if (!aligned16(idx_k) || !aligned16(blk_k)) return SGQA_ERR_ALIGN;
   if (!device_ok()) return SGQA_ERR_DEVICE;
   return status_of(launch_compress(idx_k, blk_k, p->n_seqs, p->n_tokens, p->idx_dim, p->block, (hipStream_t)stream));
@@ -286,7 +285,7 @@ int sgqa_prefill(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k, c
 int sgqa_decode(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k_cache, const sgqa_bf16* v_cache,
                 const sgqa_bf16* blk_k, const sgqa_bf16* idx_q, const float* idx_w, int32_t* topk_out,
                 sgqa_bf16* out, void* ws, size_t ws_bytes, sgqa_stream stream) {
-  int st = check_params(p, NEED_INDEX | NEED_SELECT | NEED_DSELECT | NEED_ATTN, false);
+  int st = check_params(p, NEED_INDEX | NEED_SELECT | NEED_DECODE | NEED_ATTN, false);
   if (st) return st;
   if (!q || !k_cache || !v_cache || !idx_q || !idx_w || !out || (!blk_k && p->n_tokens > p->block))
     return SGQA_ERR_NULL;

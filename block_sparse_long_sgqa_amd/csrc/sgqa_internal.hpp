@@ -41,7 +41,6 @@ hipError_t launch_decode_attend(const uint16_t* q, const uint16_t* kc, const uin
 
 // LDS a launch needs (validation rejects shapes that do not fit before anything is enqueued).
 size_t index_topk_lds_min(int kb);
-size_t decode_select_lds(int n_groups, int kb);
 size_t decode_attend_lds(int kb);
 size_t attend_lds_bytes_for(int n_tokens, int block);
 constexpr size_t kGfx950LdsBytes = 160 * 1024;

@@ -106,7 +106,7 @@ int sgqa_workspace_size(const sgqa_params* p, int op, size_t* bytes);
  *   blk_k  [S][floor(N/B)][d_I] bf16 out: blk_k[s][b][d] = bf16_rne(sum_{j<B} idx_k[s][b*B+j][d] / B),
  *                                    summed in fp32 in ascending j. A trailing partial block is not
  *                                    compressed (it can only ever be a query's own block).
- * Uses p->n_seqs, n_tokens, idx_dim, block. No workspace. */
+ * Uses p->n_seqs, n_tokens, idx_dim, block; blk_k may be NULL when N < B. No workspace. */
 int sgqa_compress(const sgqa_params* p, const sgqa_bf16* idx_k, sgqa_bf16* blk_k, sgqa_stream stream);
 
 /* Indexer scores and per-query top-k ("Reducing indexer's cost"; Figure 3: the selection is

@@ -209,8 +209,13 @@ def test_prefill_dense_when_k_covers_context(sg):
     assert_close_attention(out, want, "prefill dense")
 
 
-@pytest.mark.parametrize("L,S,G,kb_tokens,B", [(203, 3, 2, 48, 8), (4096 + 5, 4, 8, 4096, 8), (9000, 2, 8, 2048, 8),
-                                               (3000, 2, 1, 256, 4)])
+@pytest.mark.parametrize("L,S,G,kb_tokens,B", [
+    (203, 3, 2, 48, 8), (4096 + 5, 4, 8, 4096, 8), (9000, 2, 8, 2048, 8), (3000, 2, 1, 256, 4),
+    (5, 2, 2, 48, 8),          # L < B: no candidate block, only the own block's tokens
+    (9, 1, 2, 48, 8),          # exactly one candidate block
+    (12 * 8 + 1, 2, 10, 4096, 8),  # K_B > c: every candidate selected; G = 10 is not a multiple of 8
+    (150001, 1, 2, 1024, 1),   # c > 65536: the selection is reduced over segments, then picked again
+])
 def test_decode_matches_oracle(sg, L, S, G, kb_tokens, B):
     wl = datagen.DECODE.replace(name=f"dec_{L}_{S}_{G}", n_tokens=L, n_seqs=S, n_q_heads=8 * G, n_kv_heads=G,
                                 topk_tokens=kb_tokens, block=B)
