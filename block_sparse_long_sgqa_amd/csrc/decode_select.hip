@@ -18,13 +18,14 @@
 //    head sum). Scores leave as order-preserving 32-bit keys (0 = no candidate) in one row per
 //    (sequence, group). The K dimension is permuted (lane half h takes dims 32h..32h+31), the same
 //    way in A and B, so every lane reads 64 contiguous bytes of a block key.
-//  * k_dpick: one 1024-thread workgroup per (row, segment of up to 65536 keys), P <= 64 keys per
+//  * k_dpick: one 1024-thread workgroup per (row, segment of up to 32768 keys), P <= 32 keys per
 //    thread in registers, thread t holding entries tP..tP+P-1 (ascending block ids). The K_B-th
-//    largest key tau is found exactly by a 4-way search over the 32-bit key range (three
-//    thresholds per workgroup barrier, counted with wave ballots). One scan of the per-thread
-//    counts (above tau, equal to tau) gives every selected entry its output slot, in ascending id:
-//    everything above tau and the lowest ids equal to tau.
-//  * Longer rows (c > 65536) are reduced segment by segment: a segment's own top-K_B list always
+//    largest key tau is found exactly by histogram rounds (256 buckets of a power-of-two width per
+//    round, LDS atomics, one wave scans the counts from the top), first over the per-thread maxima,
+//    whose K_B-th largest bounds tau from below, then over the keys between that bound and the
+//    maximum. One scan of the per-entry flags (above tau, equal to tau) gives every selected entry
+//    its output slot, in ascending id: everything above tau and the lowest ids equal to tau.
+//  * Longer rows (c > 32768) are reduced segment by segment: a segment's own top-K_B list always
 //    contains every entry of the row's top-K_B that falls in it, so picking again over the
 //    concatenated (key, id) lists gives the same set; levels repeat until one segment is left.
 #include "sgqa_device.hpp"
@@ -41,7 +42,7 @@ constexpr int kScoreWaves = 4;
 constexpr int kScoreBlocksPerWg = kScoreBlocksPerWave * kScoreWaves;  // 512
 constexpr int kPickThreads = 1024;
 constexpr int kPickWaves = kPickThreads / 64;
-constexpr int kSegMax = kPickThreads * 64;                  // 65536 keys per pick workgroup
+constexpr int kSegMax = kPickThreads * 32;                  // 32768 keys per pick workgroup
 
 // Key row stride of the score buffer: whole score workgroups, so the pick may read up to it.
 long long score_stride(int c) { return ((long long)(c > 0 ? c : 0) + kScoreBlocksPerWg - 1) / kScoreBlocksPerWg * kScoreBlocksPerWg; }
@@ -113,12 +114,115 @@ __global__ __launch_bounds__(256) void k_dscore(const uint16_t* __restrict__ qi,
   }
 }
 
+// ------------------------------------------------------------------------------ pick helpers
+
+constexpr int kBuckets = 256;
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor(v, off, 64));
+  return v;
+}
+
+// Sum / maximum over the 16 lanes of each row (DPP row shifts: lane 15 of the row ends up with
+// the total), read from lane 15.
+__device__ __forceinline__ uint32_t lanes16_sum(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+}
+
+__device__ __forceinline__ uint32_t lanes16_max(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+}
+
+// Workgroup reduction of wave-uniform values: two sums and two maxima, one barrier. Lanes 0..15
+// of every wave read the 16 wave partials and reduce them across the row.
+__device__ __forceinline__ void block_reduce(uint32_t (*red)[4], uint32_t a, uint32_t b, uint32_t mx0, uint32_t mx1,
+                                             uint32_t (&out)[4]) {
+  const int l = lane_id();
+  if (l == 0) {
+    const u32x4 v = {a, b, mx0, mx1};
+    *reinterpret_cast<u32x4*>(red[threadIdx.x >> 6]) = v;
+  }
+  __syncthreads();
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (l < kPickWaves) v = *reinterpret_cast<const u32x4*>(red[l]);
+  out[0] = lanes16_sum(v[0]);
+  out[1] = lanes16_sum(v[1]);
+  out[2] = lanes16_max(v[2]);
+  out[3] = lanes16_max(v[3]);
+}
+
+// Histogram select of the kb-th largest value of a multiset spread over the workgroup's threads.
+// for_each(f) calls f(x) for every value x this thread holds (0 = absent). Requires
+// count(>= lo) >= kb > count(>= hi) = c_hi. Every round splits [lo, hi) into 256 equal power-of-two
+// buckets, counts the values of each (LDS atomics), and keeps the bucket where the running count
+// from the top reaches kb. Returns tau, the largest t with count(>= t) >= kb, and writes
+// count(>= tau + 1) to gt. `round` carries the parity of the histogram buffers across calls: the
+// buffer a round fills was cleared during the round before (both are clear at the start).
+template <typename ForEach>
+__device__ __forceinline__ uint32_t bucket_select(uint64_t lo, uint64_t hi, uint32_t c_hi, uint32_t kb,
+                                                  uint32_t (*hist)[kBuckets], uint32_t* bc, int& round,
+                                                  ForEach for_each, uint32_t& gt) {
+  const int l = lane_id();
+  while (hi - lo > 1) {
+    const uint64_t span = hi - lo;
+    const int bits = 64 - __clzll((long long)(span - 1));  // ceil(log2(span))
+    const int shift = bits > 8 ? bits - 8 : 0;
+    uint32_t* h = hist[round & 1];
+    if (threadIdx.x < kBuckets) hist[(round + 1) & 1][threadIdx.x] = 0u;
+    for_each([&](uint32_t x) {
+      if (x >= lo && x < hi) atomicAdd(&h[(uint32_t)((x - lo) >> shift)], 1u);
+    });
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      // Lane l holds buckets 4l..4l+3; S(b) = c_hi + (values in buckets >= b) = count(>= lo + b << shift).
+      const u32x4 hv = *reinterpret_cast<const u32x4*>(h + 4 * l);
+      const uint32_t local = hv[0] + hv[1] + hv[2] + hv[3];
+      const uint32_t above = wave_suffix_sum(local) - local + c_hi;  // S(4l + 4)
+      const uint32_t s3 = above + hv[3], s2 = s3 + hv[2], s1 = s2 + hv[1], s0 = s1 + hv[0];
+      const uint64_t m = ballot(s0 >= kb);  // S is non-increasing: lanes 0 .. l* (never empty)
+      if (l == 63 - __clzll((long long)m)) {
+        const int j = s3 >= kb ? 3 : (s2 >= kb ? 2 : (s1 >= kb ? 1 : 0));
+        bc[0] = (uint32_t)(4 * l + j);
+        bc[1] = j == 3 ? above : (j == 2 ? s3 : (j == 1 ? s2 : s1));  // S(b + 1)
+      }
+    }
+    __syncthreads();
+    const uint64_t nlo = lo + ((uint64_t)bc[0] << shift);
+    const uint64_t nhi = nlo + (1ull << shift);
+    c_hi = bc[1];
+    lo = nlo;
+    hi = nhi < hi ? nhi : hi;
+    ++round;
+  }
+  gt = c_hi;
+  return (uint32_t)lo;
+}
+
 // Exact top-K_B of one segment of one row. keys: row r, segment sg holds entries
 // [sg * seg_len, min(n, (sg + 1) * seg_len)) at keys + r * row_stride + sg * seg_len (padding up to
 // the next multiple of 4 is readable). ids: the entries' block ids (same indexing), or null when the
 // id is the entry index. Output either the final selection (sel, topk_out: [row][kb]) or, with
 // out_keys, the segment's list (out_keys / out_ids: [row][n_seg][out_stride], key 0 / id -1 padding
 // from the list's length up to out_stride, a multiple of 4 so that lists stay 16-byte aligned).
+//
+// tau is bounded from below first: the K_B-th largest of the per-thread maxima v has at least K_B
+// keys at or above it, so tau >= v, and few keys lie in [v, max] (typically a small multiple of
+// K_B), which keeps the histogram rounds over the keys cheap and their buckets spread.
 template <int P>
 __global__ __launch_bounds__(kPickThreads) void k_dpick(const uint32_t* __restrict__ keys, long long row_stride,
                                                         const int32_t* __restrict__ ids, int n, int seg_len,
@@ -127,8 +231,10 @@ __global__ __launch_bounds__(kPickThreads) void k_dpick(const uint32_t* __restri
                                                         int32_t* __restrict__ topk_out,
                                                         uint32_t* __restrict__ out_keys,
                                                         int32_t* __restrict__ out_ids) {
-  __shared__ uint32_t red[2][kPickWaves][4];
+  __shared__ __align__(16) uint32_t red[kPickWaves][4];
+  __shared__ __align__(16) uint32_t hist[2][kBuckets];
   __shared__ uint32_t scan_tot[kPickWaves];
+  __shared__ uint32_t bc[2];
   const long long row = blockIdx.x / n_seg;
   const int sg = blockIdx.x % n_seg;
   const int t = threadIdx.x, wave = t >> 6, l = lane_id();
@@ -145,76 +251,53 @@ __global__ __launch_bounds__(kPickThreads) void k_dpick(const uint32_t* __restri
 #pragma unroll
     for (int x = 0; x < 4; ++x) k[4 * q + x] = (e + x < len) ? v[x] : 0u;
   }
+  if (t < kBuckets) {
+    hist[0][t] = 0u;
+    hist[1][t] = 0u;
+  }
 
-  // Block-wide counts of keys >= each of three thresholds (threshold 0 counts nothing useful and
-  // is never asked for). One barrier per call: the two buffers alternate.
-  int call = 0;
-  auto count3 = [&](uint32_t a, uint32_t b, uint32_t cth, uint32_t (&out)[3]) {
-    uint32_t ca = 0, cb = 0, cc = 0;
+  uint32_t my_max = 0, my_valid = 0;
 #pragma unroll
-    for (int j = 0; j < P; ++j) {
-      ca += popc64(ballot(k[j] >= a));
-      cb += popc64(ballot(k[j] >= b));
-      cc += popc64(ballot(k[j] >= cth));
-    }
-    const int buf = call & 1;
-    ++call;
-    if (l == 0) {
-      red[buf][wave][0] = ca;
-      red[buf][wave][1] = cb;
-      red[buf][wave][2] = cc;
-    }
-    __syncthreads();
-    out[0] = out[1] = out[2] = 0;
-#pragma unroll
-    for (int wv = 0; wv < kPickWaves; ++wv) {
-      out[0] += red[buf][wv][0];
-      out[1] += red[buf][wv][1];
-      out[2] += red[buf][wv][2];
-    }
-  };
+  for (int j = 0; j < P; ++j) {
+    my_max = max(my_max, k[j]);
+    my_valid += k[j] != 0u ? 1u : 0u;
+  }
+  uint32_t r4[4];
+  block_reduce(red, wave_sum_u32(my_valid), (uint32_t)popc64(ballot(my_max != 0u)), wave_max_u32(my_max),
+               wave_max_u32(~my_max), r4);
+  const uint32_t n_valid = r4[0];          // keys present
+  const uint32_t n_thr = r4[1];            // threads holding at least one key
+  const uint64_t hi0 = (uint64_t)r4[2] + 1;  // count(>= hi0) = 0
+  const uint32_t min_max = ~r4[3];         // smallest per-thread maximum
 
-  uint32_t cnt[3];
-  count3(1u, 1u, 1u, cnt);
-  const uint32_t n_valid = cnt[0];
-  uint32_t tau = 0;     // selected: keys > tau, and the first need_eq keys == tau (id order)
+  uint32_t tau = 0;      // selected: keys > tau, and the first need_eq keys == tau (id order)
   uint32_t need_eq = 0;
   if (n_valid > (uint32_t)kb) {
-    // Invariant: count(>= lo) >= kb > count(>= hi); the answer is lo once hi = lo + 1.
-    uint64_t lo = 1, hi = 1ull << 32;
-    while (hi - lo > 1) {
-      const uint64_t d = hi - lo;
-      const uint64_t m1 = lo + d / 4, m2 = lo + d / 2, m3 = lo + (3 * d) / 4;
-      count3((uint32_t)m1, (uint32_t)m2, (uint32_t)m3, cnt);
-      if (cnt[2] >= (uint32_t)kb) {
-        lo = m3;
-      } else if (cnt[1] >= (uint32_t)kb) {
-        lo = m2;
-        hi = m3;
-      } else if (cnt[0] >= (uint32_t)kb) {
-        lo = m1;
-        hi = m2;
-      } else {
-        hi = m1;
-      }
-    }
-    tau = (uint32_t)lo;
-    uint32_t gt_total = 0;
-    if (tau != 0xFFFFFFFFu) {
-      count3(tau + 1, tau + 1, tau + 1, cnt);
-      gt_total = cnt[0];
-    }
+    int round = 0;
+    uint64_t v = 1;
+    uint32_t unused;
+    if (kb <= kPickThreads && n_thr >= (uint32_t)kb)
+      v = bucket_select(min_max > 0u ? min_max : 1u, hi0, 0u, (uint32_t)kb, hist, bc, round,
+                        [&](auto&& f) { f(my_max); }, unused);
+    uint32_t gt_total;
+    tau = bucket_select(v, hi0, 0u, (uint32_t)kb, hist, bc, round,
+                        [&](auto&& f) {
+#pragma unroll
+                          for (int j = 0; j < P; ++j) f(k[j]);
+                        },
+                        gt_total);
     need_eq = (uint32_t)kb - gt_total;
   }
 
-  // Output slot of an entry = (# above tau before it) + min(# equal to tau before it, need_eq).
+  // Output slot of an entry = (# above tau before it) + min(# equal to tau before it, need_eq),
+  // counted in ascending id order.
   uint32_t my_gt = 0, my_eq = 0;
 #pragma unroll
   for (int j = 0; j < P; ++j) {
     my_gt += k[j] > tau ? 1u : 0u;
     my_eq += (k[j] == tau && tau != 0u) ? 1u : 0u;
   }
-  // Per-wave totals fit 16 bits (at most 64 P = 4096), so the wave scan runs on packed pairs.
+  // Per-wave totals fit 16 bits (at most 64 P = 2048), so the wave scan runs on packed pairs.
   const uint32_t incl = wave_prefix_sum(my_gt | (my_eq << 16));
   uint32_t gt_pre = (incl & 0xFFFFu) - my_gt;
   uint32_t eq_pre = (incl >> 16) - my_eq;
@@ -222,13 +305,13 @@ __global__ __launch_bounds__(kPickThreads) void k_dpick(const uint32_t* __restri
   __syncthreads();
   uint32_t gt_all = 0, eq_all = 0;
   for (int wv = 0; wv < kPickWaves; ++wv) {
-    const uint32_t v = scan_tot[wv];
+    const uint32_t x = scan_tot[wv];
     if (wv < wave) {
-      gt_pre += v & 0xFFFFu;
-      eq_pre += v >> 16;
+      gt_pre += x & 0xFFFFu;
+      eq_pre += x >> 16;
     }
-    gt_all += v & 0xFFFFu;
-    eq_all += v >> 16;
+    gt_all += x & 0xFFFFu;
+    eq_all += x >> 16;
   }
   const uint32_t n_sel = gt_all + min(eq_all, need_eq);
 
@@ -238,29 +321,31 @@ __global__ __launch_bounds__(kPickThreads) void k_dpick(const uint32_t* __restri
   uint32_t* lk = final_out ? nullptr : out_keys + (row * n_seg + sg) * out_stride;
   int32_t* li = final_out ? nullptr : out_ids + (row * n_seg + sg) * out_stride;
   const int id_base = sg * seg_len;
+  if (my_gt + my_eq != 0u) {
 #pragma unroll
-  for (int j = 0; j < P; ++j) {
-    const uint32_t kj = k[j];
-    bool take = false;
-    uint32_t pos = 0;
-    if (kj > tau) {
-      take = true;
-      pos = gt_pre + min(eq_pre, need_eq);
-      ++gt_pre;
-    } else if (kj == tau && tau != 0u) {
-      take = eq_pre < need_eq;
-      pos = gt_pre + eq_pre;
-      ++eq_pre;
-    }
-    if (take) {
-      const int e = e0 + j;
-      const int32_t id = ids ? ids[base + e] : id_base + e;
-      if (final_out) {
-        sel_row[pos] = id;
-        if (top_row) top_row[pos] = id;
-      } else {
-        lk[pos] = kj;
-        li[pos] = id;
+    for (int j = 0; j < P; ++j) {
+      const uint32_t kx = k[j];
+      bool take = false;
+      uint32_t slot = 0;
+      if (kx > tau) {
+        take = true;
+        slot = gt_pre + min(eq_pre, need_eq);
+        ++gt_pre;
+      } else if (kx == tau && tau != 0u) {
+        take = eq_pre < need_eq;
+        slot = gt_pre + eq_pre;
+        ++eq_pre;
+      }
+      if (take) {
+        const int e = e0 + j;
+        const int32_t id = ids ? ids[base + e] : id_base + e;
+        if (final_out) {
+          sel_row[slot] = id;
+          if (top_row) top_row[slot] = id;
+        } else {
+          lk[slot] = kx;
+          li[slot] = id;
+        }
       }
     }
   }
@@ -278,8 +363,7 @@ __global__ __launch_bounds__(kPickThreads) void k_dpick(const uint32_t* __restri
 int pick_p(int n) {
   if (n <= kPickThreads * 8) return 8;
   if (n <= kPickThreads * 16) return 16;
-  if (n <= kPickThreads * 32) return 32;
-  return 64;
+  return 32;
 }
 
 int list_stride(int kb) { return (kb + 3) / 4 * 4; }
@@ -292,7 +376,7 @@ hipError_t launch_pick(const uint32_t* keys, long long row_stride, const int32_t
     seg_len = kPickThreads * p;
     n_seg = 1;
   } else {
-    p = 64;
+    p = 32;
     seg_len = kSegMax;
     n_seg = (n + kSegMax - 1) / kSegMax;
   }
@@ -306,7 +390,6 @@ hipError_t launch_pick(const uint32_t* keys, long long row_stride, const int32_t
   SGQA_PICK_CASE(8)
   SGQA_PICK_CASE(16)
   SGQA_PICK_CASE(32)
-  SGQA_PICK_CASE(64)
 #undef SGQA_PICK_CASE
   return hipErrorInvalidValue;
 }

@@ -214,7 +214,8 @@ def test_prefill_dense_when_k_covers_context(sg):
     (5, 2, 2, 48, 8),          # L < B: no candidate block, only the own block's tokens
     (9, 1, 2, 48, 8),          # exactly one candidate block
     (12 * 8 + 1, 2, 10, 4096, 8),  # K_B > c: every candidate selected; G = 10 is not a multiple of 8
-    (150001, 1, 2, 1024, 1),   # c > 65536: the selection is reduced over segments, then picked again
+    (150001, 1, 2, 1024, 1),   # c > 32768: the selection is reduced over segments, then picked again
+    (20000, 1, 2, 2048, 1),    # K_B = 2048 > 1024 threads: no per-thread-maximum bound
 ])
 def test_decode_matches_oracle(sg, L, S, G, kb_tokens, B):
     wl = datagen.DECODE.replace(name=f"dec_{L}_{S}_{G}", n_tokens=L, n_seqs=S, n_q_heads=8 * G, n_kv_heads=G,
@@ -235,3 +236,28 @@ def test_decode_matches_oracle(sg, L, S, G, kb_tokens, B):
     np.testing.assert_array_equal(bits(blk), kbar)
     np.testing.assert_array_equal(topk.cpu().numpy(), want_sel)
     assert_close_attention(out, want_out, f"decode L={L}")
+
+
+def test_decode_all_scores_tied(sg):
+    # Zero indexer queries: every candidate scores 0, so the selection is the K_B lowest block ids
+    # and the keys above the search's lower bound are far too many to compact.
+    L, S, G, B = 40000, 2, 2, 8
+    wl = datagen.DECODE.replace(name="dec_tied", n_tokens=L, n_seqs=S, n_q_heads=8 * G, n_kv_heads=G,
+                                topk_tokens=4096, block=B)
+    p = params_of(wl)
+    x = datagen.decode_inputs(wl)
+    x["qi"] = torch.zeros_like(x["qi"])
+    kbar = oracle.compress(bits(x["ki_cache"]), B)
+    want_sel, want_out = oracle.decode(x["q"], x["k_cache"], x["v_cache"], kbar, x["qi"], x["w"], B, p.kb)
+    assert (want_sel == np.arange(p.kb, dtype=np.int32)).all()
+    say("decode with every score tied")
+    xd = to_dev(x)
+    blk = torch.empty((S, L // B, 64), dtype=torch.bfloat16, device="cuda")
+    sg.sgqa_compress(p, xd["ki_cache"], blk)
+    out = torch.empty((S, p.n_q_heads, 128), dtype=torch.bfloat16, device="cuda")
+    topk = torch.empty((S, G, p.kb), dtype=torch.int32, device="cuda")
+    ws = sg.workspace(p, sg.SGQA_OP_DECODE)
+    sg.sgqa_decode(p, xd["q"], xd["k_cache"], xd["v_cache"], blk, xd["qi"], xd["w"], out, ws, topk_out=topk)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(topk.cpu().numpy(), want_sel)
+    assert_close_attention(out, want_out, "decode tied")
