@@ -88,9 +88,11 @@ __device__ __forceinline__ int v_phys(int row, int p) { return p ^ ((row & 3) <<
 struct LaneOffsets {
   int k;     // K A-operand: key row (l % 32), 16-byte piece (l / 32); + kt * 32 rows + ks * 32 B
   int v[4];  // V transposing read for d-tile dt: row 4 * khalf + (s16 / 4), d 32 dt + 16 dgrp + 4 (s16 % 4)
+  int tok;   // the chunk's token table
 };
 
-__device__ __forceinline__ LaneOffsets lane_offsets() {
+// v_tile: byte offset of the V tile inside a stage (the token table follows it).
+__device__ __forceinline__ LaneOffsets lane_offsets(int v_tile = kKTileBytes) {
   const int l = lane_id();
   LaneOffsets o;
   o.k = (l & 31) * kKRowBytes + (l >> 5) * 16;
@@ -99,18 +101,27 @@ __device__ __forceinline__ LaneOffsets lane_offsets() {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
     const int piece = 4 * dt + 2 * (grp & 1) + ((s16 & 3) >> 1);
-    o.v[dt] = kKTileBytes + row * 256 + 16 * v_phys(row, piece) + 8 * (s16 & 1);
+    o.v[dt] = v_tile + row * 256 + 16 * v_phys(row, piece) + 8 * (s16 & 1);
   }
+  o.tok = v_tile + kVTileBytes;
   return o;
 }
 
+struct NoOp {
+  __device__ void operator()() const {}
+};
+
 // One 64-key chunk for the QT Q tiles of this wave.
-//   stage: K tile, V tile (row-major, 272-byte rows), token table (INT_MAX = invalid key)
+//   stage: K tile, V tile (row-major, 272-byte rows), token table (INT_MAX = invalid key), at the
+//          offsets of lo
 //   row_pos[qt]: query position of this lane's Q row in tile qt (for the causal mask)
-template <int QT>
+//   KREG: the K operands come from kreg[ks * 2 + kt] (registers) instead of the K tile; after()
+//         runs once the score products have consumed them.
+template <int QT, bool KREG = false, typename After = NoOp>
 __device__ __forceinline__ void attn_chunk(const uint8_t* stage, const LaneOffsets& lo, const bf16x8 (&qreg)[QT][8],
                                            AttnState<QT>& st, float scale_log2, bool masked,
-                                           const int (&row_pos)[QT]) {
+                                           const int (&row_pos)[QT], const bf16x8* kreg = nullptr,
+                                           After after = After()) {
   const int l = lane_id();
   const int hi = l >> 5;
   f32x16 s[QT][2];
@@ -120,28 +131,38 @@ __device__ __forceinline__ void attn_chunk(const uint8_t* stage, const LaneOffse
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int j = 0; j < 16; ++j) s[qt][kt][j] = 0.0f;
-  // S^T = K Q^T: the K operands of step ks+1 are read while the MFMAs of step ks run.
-  const uint8_t* kp = stage + lo.k;
-  bf16x8 ka[2][2];
-  ka[0][0] = *reinterpret_cast<const bf16x8*>(kp);
-  ka[0][1] = *reinterpret_cast<const bf16x8*>(kp + 32 * kKRowBytes);
+  if constexpr (KREG) {
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    if (ks < 7) {
-      ka[(ks + 1) & 1][0] = *reinterpret_cast<const bf16x8*>(kp + (ks + 1) * 32);
-      ka[(ks + 1) & 1][1] = *reinterpret_cast<const bf16x8*>(kp + 32 * kKRowBytes + (ks + 1) * 32);
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) s[qt][kt] = mfma32(kreg[ks * 2 + kt], qreg[qt][ks], s[qt][kt]);
+  } else {
+    // S^T = K Q^T: the K operands of step ks+1 are read while the MFMAs of step ks run.
+    const uint8_t* kp = stage + lo.k;
+    bf16x8 ka[2][2];
+    ka[0][0] = *reinterpret_cast<const bf16x8*>(kp);
+    ka[0][1] = *reinterpret_cast<const bf16x8*>(kp + 32 * kKRowBytes);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      if (ks < 7) {
+        ka[(ks + 1) & 1][0] = *reinterpret_cast<const bf16x8*>(kp + (ks + 1) * 32);
+        ka[(ks + 1) & 1][1] = *reinterpret_cast<const bf16x8*>(kp + 32 * kKRowBytes + (ks + 1) * 32);
+      }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) s[qt][kt] = mfma32(ka[ks & 1][kt], qreg[qt][ks], s[qt][kt]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) s[qt][kt] = mfma32(ka[ks & 1][kt], qreg[qt][ks], s[qt][kt]);
-    __builtin_amdgcn_sched_barrier(0);
   }
+  after();
 
   // Tokens of this lane's keys: key kt*32 + 8*a + 4*hi + (0..3), four consecutive ints.
   int4 tk[2][4];
   if (masked) {
-    const int* tok = reinterpret_cast<const int*>(stage + kKTileBytes + kVTileBytes);
+    const int* tok = reinterpret_cast<const int*>(stage + (KREG ? lo.tok : kKTileBytes + kVTileBytes));
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -481,10 +502,49 @@ hipError_t launch_attend(const uint16_t* q, const uint16_t* k, const uint16_t* v
 
 // ------------------------------------------------------------------------------------ decode
 
+constexpr int kDecVStage = kVTileBytes + kKeys * 4;  // decode: V tile + token table of a chunk
+
+// Decode gather of one wave: the V tile of one chunk (16 wave-wide global_load_lds, layout as in
+// chunk_issue) and its token table.
+template <typename TokFn>
+__device__ __forceinline__ void v_issue_wave(uint8_t* vst, const uint16_t* vbase, TokFn tok_of) {
+  const int l = lane_id();
+#pragma unroll
+  for (int ti = 0; ti < kVTileInsts; ++ti) {
+    const int slot = ti * 64 + l;
+    const int row = slot >> 4;
+    const int piece = v_phys(row, slot & 15);
+    int tkn = tok_of(row);
+    if (tkn < 0) tkn = 0;
+    __builtin_amdgcn_global_load_lds((const void*)(vbase + (long long)tkn * kD + piece * 8),
+                                     (lds_void*)(vst + ti * 1024), 16, 0, 0);
+  }
+  const int t = tok_of(l);
+  reinterpret_cast<int*>(vst + kVTileBytes)[l] = t >= 0 ? t : 0x7FFFFFFF;
+}
+
+// The K operands of one chunk straight from global memory into registers: the A operand of
+// S^T = K Q^T for key tile kt and step ks is key row 32 kt + (l % 32), elements 16 ks + 8 (l / 32)
+// .. +7, i.e. 16 contiguous bytes of one cached key.
+template <typename TokFn>
+__device__ __forceinline__ void k_load_regs(bf16x8 (&kreg)[16], const uint16_t* kbase, TokFn tok_of) {
+  const int l = lane_id();
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    int tkn = tok_of(32 * kt + (l & 31));
+    if (tkn < 0) tkn = 0;
+    const uint16_t* src = kbase + (long long)tkn * kD + 8 * (l >> 5);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) kreg[ks * 2 + kt] = *reinterpret_cast<const bf16x8*>(src + 16 * ks);
+  }
+}
+
 // Decode attention: one workgroup of 4 waves per (sequence s, group g). The attended blocks are
-// Sel(s,g) (ascending) plus the own block; wave w streams chunks w, w+4, ... through its own LDS
-// buffer (HBM-bound: four independent chunk streams per CU keep enough bytes in flight), keeps its
-// own online-softmax state for the r heads (one 32-row tile, r <= 32 rows used), and the four
+// Sel(s,g) (ascending) plus the own block; wave w handles chunks w, w+4, ... Decode is a gather at
+// HBM rate, so the loop is built to keep bytes in flight: the K operands of a chunk go straight
+// into registers (issued as soon as the previous chunk's score products have read theirs), and
+// the V tiles, which need the transposing LDS reads, are double-buffered per wave. Each wave keeps
+// its own online-softmax state for the r heads (one 32-row tile, r <= 32 rows used); the four
 // states are merged in LDS into the bf16 output.
 __global__ __launch_bounds__(256) void k_decode_attend(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
                                                        const uint16_t* __restrict__ vc,
@@ -494,8 +554,8 @@ __global__ __launch_bounds__(256) void k_decode_attend(const uint16_t* __restric
   constexpr int kWavesD = 4;
   extern __shared__ __align__(16) uint8_t smem[];
   const int wave = threadIdx.x >> 6;
-  uint8_t* stage = smem + wave * kStageBytes;  // this wave's K tile, V tile, token table
-  int* blocks = reinterpret_cast<int*>(smem + kWavesD * kStageBytes);  // kb + 1 entries
+  uint8_t* vbuf[2] = {smem + wave * 2 * kDecVStage, smem + wave * 2 * kDecVStage + kDecVStage};
+  int* blocks = reinterpret_cast<int*>(smem + kWavesD * 2 * kDecVStage);  // kb + 1 entries
   __shared__ int n_sel_shared;
 
   const int s = blockIdx.x / n_groups, g = blockIdx.x % n_groups;
@@ -540,26 +600,43 @@ __global__ __launch_bounds__(256) void k_decode_attend(const uint16_t* __restric
   const uint16_t* vbase = vc + seq_off;
   const int n_keys = (n_sel + 1) * block;
   const int n_chunks = (n_keys + kKeys - 1) / kKeys;
-  const LaneOffsets lo = lane_offsets();
-  for (int c = wave; c < n_chunks; c += kWavesD) {
-    auto tok_at = [&](int key) -> int {
+  const LaneOffsets lo = lane_offsets(0);
+  auto tok_in = [&](int c) {
+    return [&, c](int key) -> int {
       const int kp = c * kKeys + key;
       if (kp >= n_keys) return -1;
       const int tk = (blocks[kp >> block_shift] << block_shift) + (kp & (block - 1));
       return tk < ctx ? tk : -1;
     };
-    chunk_issue<64>(stage, kbase, vbase, tok_at);
-    wait_vm();
+  };
+  bf16x8 kreg[16];
+  if (wave < n_chunks) {
+    v_issue_wave(vbuf[0], vbase, tok_in(wave));
+    k_load_regs(kreg, kbase, tok_in(wave));
+  }
+  int i = 0;
+  for (int c = wave; c < n_chunks; c += kWavesD, ++i) {
+    const int cn = c + kWavesD;
+    if (cn < n_chunks) {
+      v_issue_wave(vbuf[(i + 1) & 1], vbase, tok_in(cn));
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // V and K of chunk c landed; V of cn flies
+    } else {
+      wait_vm();
+    }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    attn_chunk<1>(stage, lo, qreg, st, scale_log2, true, row_pos);
+    // Only the last chunk holds the own block (and the padding past the list): the Sel blocks are
+    // all below it, hence visible to the query.
+    attn_chunk<1, true>(vbuf[i & 1], lo, qreg, st, scale_log2, c == n_chunks - 1, row_pos, kreg, [&]() {
+      if (cn < n_chunks) k_load_regs(kreg, kbase, tok_in(cn));
+    });
   }
 
-  // Merge the four wave states: O^T tiles to LDS (reusing the wave's stage), then 256 threads
+  // Merge the four wave states: O^T tiles to LDS (reusing the wave's buffers), then 256 threads
   // combine r x 128 outputs.
   const float l_all = st.l[0] + __shfl_xor(st.l[0], 32, 64);
-  float* o_lds = reinterpret_cast<float*>(stage);  // [32 rows][128]
-  float* ml_lds = reinterpret_cast<float*>(smem + kWavesD * kStageBytes) + (kb + 1);  // [4][32][2]
-  __syncthreads();  // every wave is done with its stage
+  float* o_lds = reinterpret_cast<float*>(vbuf[0]);  // [32 rows][128]
+  float* ml_lds = reinterpret_cast<float*>(blocks) + (kb + 1);  // [4][32][2]
+  __syncthreads();  // every wave is done with its buffers
   {
     const int row = l & 31;
 #pragma unroll
@@ -583,13 +660,13 @@ __global__ __launch_bounds__(256) void k_decode_attend(const uint16_t* __restric
     for (int w = 0; w < kWavesD; ++w) {
       const float f = fast_exp2(ml_lds[(w * 32 + row) * 2] - m);
       den += ml_lds[(w * 32 + row) * 2 + 1] * f;
-      num += reinterpret_cast<const float*>(smem + w * kStageBytes)[row * kD + d] * f;
+      num += reinterpret_cast<const float*>(smem + w * 2 * kDecVStage)[row * kD + d] * f;
     }
     out[((long long)s * n_q_heads + g * r + row) * kD + d] = (uint16_t)f32_to_bf16_bits(num / den);
   }
 }
 
-size_t decode_attend_lds(int kb) { return (size_t)4 * kStageBytes + (size_t)(kb + 1) * 4 + 4 * 32 * 2 * 4; }
+size_t decode_attend_lds(int kb) { return (size_t)4 * 2 * kDecVStage + (size_t)(kb + 1) * 4 + 4 * 32 * 2 * 4; }
 
 hipError_t launch_decode_attend(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, const int32_t* sel,
                                 uint16_t* out, int n_seqs, int ctx, int n_q_heads, int n_groups, int block, int kb,
