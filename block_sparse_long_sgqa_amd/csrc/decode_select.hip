@@ -195,7 +195,11 @@ __device__ __forceinline__ uint32_t bucket_select(uint64_t lo, uint64_t hi, uint
       const uint32_t above = wave_suffix_sum(local) - local + c_hi;  // S(4l + 4)
       const uint32_t s3 = above + hv[3], s2 = s3 + hv[2], s1 = s2 + hv[1], s0 = s1 + hv[0];
       const uint64_t m = ballot(s0 >= kb);  // S is non-increasing: lanes 0 .. l* (never empty)
-      if (l == 63 - __clzll((long long)m)) {
+      if (m == 0 && l == 0) {                 // count(>= lo) < kb cannot happen; end the search
+        bc[0] = 0u;
+        bc[1] = kb;
+      }
+      if (m != 0 && l == 63 - __clzll((long long)m)) {
         const int j = s3 >= kb ? 3 : (s2 >= kb ? 2 : (s1 >= kb ? 1 : 0));
         bc[0] = (uint32_t)(4 * l + j);
         bc[1] = j == 3 ? above : (j == 2 ? s3 : (j == 1 ? s2 : s1));  // S(b + 1)
@@ -204,9 +208,10 @@ __device__ __forceinline__ uint32_t bucket_select(uint64_t lo, uint64_t hi, uint
     __syncthreads();
     const uint64_t nlo = lo + ((uint64_t)bc[0] << shift);
     const uint64_t nhi = nlo + (1ull << shift);
-    c_hi = bc[1];
+    const bool stop = bc[1] >= kb;  // only from the impossible case above
+    c_hi = stop ? 0u : bc[1];
     lo = nlo;
-    hi = nhi < hi ? nhi : hi;
+    hi = stop ? lo + 1 : (nhi < hi ? nhi : hi);
     ++round;
   }
   gt = c_hi;

@@ -25,6 +25,8 @@
 //  * Pass 2 recomputes the scores and emits, in ascending block order, every candidate with
 //    s > tau plus the lowest-id candidates with s == tau (ballot + popcount compaction).
 //  * Decode selection (one query, many candidates) is shaped differently and lives on its own.
+#include <type_traits>
+
 #include "sgqa_device.hpp"
 #include "sgqa_internal.hpp"
 
@@ -36,15 +38,31 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kIdxHeads = 4;
 constexpr int kIdxDim = 64;
-constexpr int kChunk = 128;                        // candidate blocks per stage
+#ifndef SGQA_TOPK_CHUNK
+#define SGQA_TOPK_CHUNK 128
+#endif
+#ifndef SGQA_TOPK_WGS_PER_CU
+#define SGQA_TOPK_WGS_PER_CU 1
+#endif
+constexpr int kChunk = SGQA_TOPK_CHUNK;            // candidate blocks per stage
 constexpr int kKRowBytes = 144;                    // 128 B block key + 16 B pad
 constexpr int kKSlots = kKRowBytes / 16;           // 9 slots of 16 B per row, the last is padding
 constexpr int kStageBytes = kChunk * kKRowBytes;   // 18432 B
 constexpr int kStageInsts = kChunk * kKSlots / 64;  // 18 wave-wide 16-byte loads per stage
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr int kListPad = 16;                       // words between row lists (spreads LDS banks)
 
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Inclusive prefix sum over the 16 lanes of each row (DPP row shifts; rows are lanes 16q..16q+15).
+__device__ __forceinline__ uint32_t row16_prefix(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  return v;
+}
 
 // Inverse of score_key (canonical +0).
 __device__ __forceinline__ float key_to_score(uint32_t k) {
@@ -76,10 +94,14 @@ __device__ __forceinline__ int keys_count_ge(const KeyRegs<P>& r, uint32_t t) { 
   return cnt;
 }
 
-// The K-th largest of the n listed keys (1 <= K <= n <= 64 P) and the number of keys above it,
-// by binary search over the 32-bit key between the list's minimum and maximum.
+// The K-th largest of the n listed keys (1 <= K <= n <= 64 P) and the number of keys above it.
+// Histogram select over [min, max] of the list: every round splits the live key range into 256
+// equal power-of-two buckets, counts the keys of each bucket with LDS atomics into hist (256 words
+// owned by this wave; LDS operations of one wave complete in order, so no barrier is needed),
+// and keeps the bucket where the running count from the top reaches K.
 template <int P>
-__device__ __forceinline__ uint32_t keys_kth_largest(const KeyRegs<P>& r, int K, int* n_above) {
+__device__ __forceinline__ uint32_t keys_kth_largest(const KeyRegs<P>& r, int K, int* n_above, uint32_t* hist) {
+  const int l = lane_id();
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
 #pragma unroll
   for (int j = 0; j < P; ++j) {
@@ -91,33 +113,57 @@ __device__ __forceinline__ uint32_t keys_kth_largest(const KeyRegs<P>& r, int K,
     mn = min(mn, (uint32_t)__shfl_xor((int)mn, off, 64));
     mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
   }
-  // Largest t in [mn, mx] with count(>= t) >= K; count(>= mn) = n >= K holds throughout.
-  uint32_t lo = mn, hi = mx;
-  while (lo < hi) {
-    const uint32_t mid = lo + (uint32_t)(((uint64_t)hi - lo + 1) >> 1);
-    if (keys_count_ge(r, mid) >= K)
-      lo = mid;
-    else
-      hi = mid - 1;
+  if (mx == 0u || K < 1) {  // no keys listed: nothing to select (callers never ask for this)
+    *n_above = 0;
+    return 0u;
   }
-  *n_above = (lo == 0xFFFFFFFFu) ? 0 : keys_count_ge(r, lo + 1);
-  return lo;
+  // Invariant: count(>= lo) >= K > count(>= hi) = c_hi.
+  uint64_t lo = mn, hi = (uint64_t)mx + 1;
+  uint32_t c_hi = 0;
+  while (hi - lo > 1) {
+    const int bits = 64 - __clzll((long long)(hi - lo - 1));
+    const int shift = bits > 8 ? bits - 8 : 0;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(hist + 4 * l) = z;
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      const uint32_t x = r.k[j];
+      if (x >= lo && x < hi) atomicAdd(&hist[(uint32_t)((x - lo) >> shift)], 1u);
+    }
+    const u32x4 hv = *reinterpret_cast<const u32x4*>(hist + 4 * l);
+    const uint32_t local = hv[0] + hv[1] + hv[2] + hv[3];
+    const uint32_t above = wave_suffix_sum(local) - local + c_hi;  // count(>= bucket 4l + 4)
+    const uint32_t s3 = above + hv[3], s2 = s3 + hv[2], s1 = s2 + hv[1], s0 = s1 + hv[0];
+    const uint64_t m = ballot(s0 >= (uint32_t)K);  // lanes 0 .. l*, never empty while n >= K
+    if (m == 0) break;                              // fewer than K keys listed: keep lo
+    const int ls = 63 - __clzll((long long)m);
+    const int j = s3 >= (uint32_t)K ? 3 : (s2 >= (uint32_t)K ? 2 : (s1 >= (uint32_t)K ? 1 : 0));
+    const uint32_t s_next = j == 3 ? above : (j == 2 ? s3 : (j == 1 ? s2 : s1));
+    const int bsel = readlane(4 * l + j, ls);
+    c_hi = readlane(s_next, ls);
+    lo += (uint64_t)bsel << shift;
+    const uint64_t nhi = lo + (1ull << shift);
+    hi = nhi < hi ? nhi : hi;
+  }
+  *n_above = (int)c_hi;
+  return (uint32_t)lo;
 }
 
 template <int P>
-__device__ __forceinline__ uint32_t wave_kth_largest(const uint32_t* keys, int n, int K, int* n_above) {
+__device__ __forceinline__ uint32_t wave_kth_largest(const uint32_t* keys, int n, int K, int* n_above,
+                                                     uint32_t* hist) {
   KeyRegs<P> r;
   keys_load(r, keys, n);
-  return keys_kth_largest(r, K, n_above);
+  return keys_kth_largest(r, K, n_above, hist);
 }
 
 // Trim a key list to the multiset of its K largest keys (K < n); returns the K-th largest key.
 template <int P>
-__device__ __forceinline__ uint32_t wave_trim_keys(uint32_t* keys, int n, int K) {
+__device__ __forceinline__ uint32_t wave_trim_keys(uint32_t* keys, int n, int K, uint32_t* hist) {
   KeyRegs<P> r;
   keys_load(r, keys, n);
   int above;
-  const uint32_t tau = keys_kth_largest(r, K, &above);
+  const uint32_t tau = keys_kth_largest(r, K, &above, hist);
   const int l = lane_id();
   const uint64_t lt = lanemask_lt();
   int wr = 0;
@@ -146,13 +192,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* stage = smem;                                                        // 2 x kStageBytes
   uint32_t* keys_all = reinterpret_cast<uint32_t*>(smem + 2 * kStageBytes);     // 4*WAVES x cap
+  const int lstride = cap + kListPad;                                          // words per row list
+  uint32_t* hist = keys_all + (size_t)WAVES * 4 * lstride + (threadIdx.x >> 6) * 256;  // this wave's 256 words
 
   constexpr int kRowsPerWg = WAVES * 4;
   const int wave = threadIdx.x >> 6;
   const int l = lane_id();
   const int quarter = l >> 4;
   const int l16 = l & 15;
-  const uint32_t lt16 = (1u << l16) - 1u;
 
   const long long wg = (long long)gridDim.x - 1 - blockIdx.x;  // largest rows first
   const long long r0 = wg * kRowsPerWg;
@@ -205,37 +252,69 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
   float w4[4];
   for (int j = 0; j < 4; ++j) w4[j] = w[g_o * kIdxHeads + j];
 
-  // Stage issue: 18 wave-wide loads of 64 slots; slot s = row s / 9, piece s % 9 (piece 8 = pad).
-  // Row r of the stage holds candidate block lo + (v0 + r) * stride + off.
+  // Stage issue: 18 wave-wide loads of 64 slots; slot s = stage row s / 9, piece s % 9 (piece 8 =
+  // pad). Stage row R = 16 ct + j holds candidate v0 + kTiles j + ct, so that tile ct (rows 16 ct ..
+  // 16 ct + 15, read by lanes j = l % 16) gives lane j the candidates kTiles j .. kTiles j + 7 of
+  // the chunk in ascending order over the tiles. Candidate v is block lo + v * stride + off. The
+  // (row, piece) of this lane's slots do not change from chunk to chunk.
+  constexpr int kTiles = kChunk / 16;
+  constexpr int kIssuePerWave = (kStageInsts + WAVES - 1) / WAVES;
+  int is_row[kIssuePerWave], is_piece[kIssuePerWave];
+#pragma unroll
+  for (int x = 0; x < kIssuePerWave; ++x) {
+    const int slot = (wave + x * WAVES) * 64 + l;
+    is_row[x] = slot / kKSlots;
+    const int piece = slot - is_row[x] * kKSlots;
+    is_piece[x] = piece == kKSlots - 1 ? 0 : piece;
+  }
   auto issue = [&](int v0, int buf, int stride, int off, int n_virt) {
-    for (int ii = wave; ii < kStageInsts; ii += WAVES) {
-      const int slot = ii * 64 + l;
-      const int row = slot / kKSlots;
-      int piece = slot - row * kKSlots;
-      if (piece == kKSlots - 1) piece = 0;
-      const int v = v0 + row;
-      int b = lo + v * stride + off;
-      if (v >= n_virt || b >= n_blocks) b = 0;  // beyond the candidates: any valid key (never used)
-      __builtin_amdgcn_global_load_lds((const void*)(kbar + (long long)b * kIdxDim + piece * 8),
-                                       (lds_void*)(stage + buf * kStageBytes + ii * 1024), 16, 0, 0);
+#pragma unroll
+    for (int x = 0; x < kIssuePerWave; ++x) {
+      const int ii = wave + x * WAVES;
+      if (ii < kStageInsts) {
+        const int v = v0 + (is_row[x] & 15) * kTiles + (is_row[x] >> 4);
+        int b = lo + v * stride + off;
+        if (v >= n_virt || b >= n_blocks) b = 0;  // beyond the candidates: any valid key (never used)
+        __builtin_amdgcn_global_load_lds((const void*)(kbar + (long long)b * kIdxDim + is_piece[x] * 8),
+                                         (lds_void*)(stage + buf * kStageBytes + ii * 1024), 16, 0, 0);
+      }
     }
   };
   const int boff = l16 * kKRowBytes + quarter * 16;  // B operand: row l16 of a 16-block tile
-  auto score_of = [&](const uint8_t* sb, int ct) -> float {
-    const uint8_t* p = sb + ct * 16 * kKRowBytes + boff;
-    const bf16x8 b_lo = *reinterpret_cast<const bf16x8*>(p);
-    const bf16x8 b_hi = *reinterpret_cast<const bf16x8*>(p + 64);
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    acc = mfma16(a_op[0], b_lo, acc);
-    acc = mfma16(a_op[1], b_hi, acc);
-    float s = 0.0f;
+  // Scores of one staged chunk: all operand reads first, then all products, then the per-lane
+  // ReLU / weight / head sum, so that LDS and matrix-core latencies overlap across the 8 tiles.
+  auto chunk_scores = [&](const uint8_t* sb, float (&sc)[kTiles]) {
+    bf16x8 b_lo[kTiles], b_hi[kTiles];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s += w4[j] * __builtin_amdgcn_fmed3f(acc[j], 0.0f, 3.402823466e38f);  // ReLU
-    return s;
+    for (int ct = 0; ct < kTiles; ++ct) {
+      const uint8_t* p = sb + ct * 16 * kKRowBytes + boff;
+      b_lo[ct] = *reinterpret_cast<const bf16x8*>(p);
+      b_hi[ct] = *reinterpret_cast<const bf16x8*>(p + 64);
+    }
+    f32x4 acc[kTiles];
+#pragma unroll
+    for (int ct = 0; ct < kTiles; ++ct) {
+      const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+      acc[ct] = mfma16(a_op[0], b_lo[ct], z);
+    }
+#pragma unroll
+    for (int ct = 0; ct < kTiles; ++ct) acc[ct] = mfma16(a_op[1], b_hi[ct], acc[ct]);
+#pragma unroll
+    for (int ct = 0; ct < kTiles; ++ct) {
+      float s = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s += w4[j] * __builtin_amdgcn_fmed3f(acc[ct][j], 0.0f, 3.402823466e38f);  // ReLU
+      sc[ct] = s;
+    }
   };
+  // Smallest candidate bound over this wave's rows: chunks entirely below it need no checks.
+  int hi_wave = hi_lane;
+#pragma unroll
+  for (int off = 16; off <= 32; off <<= 1) hi_wave = min(hi_wave, __shfl_xor(hi_wave, off, 64));
   // Streams candidates v in [0, n_virt) (block lo + v * stride + off) through the double-buffered
-  // stage; body(score, block, valid) runs for every (row, candidate) pair of this lane, after(..)
-  // once per chunk.
+  // stage. For every chunk, body(sc, v_first, full) gets this lane's 8 scores, for candidates
+  // v_first .. v_first + 7 (ascending), and whether every candidate of the wave's rows in the chunk
+  // is valid (a compile-time tag); after() runs once per chunk.
   auto stream = [&](int n_virt, int stride, int off, auto&& body, auto&& after) {
     const int n_ch = (n_virt + kChunk - 1) / kChunk;
     if (n_ch > 0) issue(0, 0, stride, off, n_virt);
@@ -243,31 +322,47 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
       wait_vm();
       __syncthreads();
       if (n + 1 < n_ch) issue((n + 1) * kChunk, (n + 1) & 1, stride, off, n_virt);
-      const uint8_t* sb = stage + (n & 1) * kStageBytes;
-#pragma unroll 2
-      for (int ct = 0; ct < kChunk / 16; ++ct) {
-        const float sc = score_of(sb, ct);
-        const int v = n * kChunk + ct * 16 + l16;
-        const int b = lo + v * stride + off;
-        body(sc, b, v < n_virt && b < hi_lane);
-      }
+      float sc[kTiles];
+      chunk_scores(stage + (n & 1) * kStageBytes, sc);
+      const int v_end = (n + 1) * kChunk;
+      const int v_first = n * kChunk + l16 * kTiles;
+      if (v_end <= n_virt && lo + (v_end - 1) * stride + off < hi_wave)
+        body(sc, v_first, std::true_type());
+      else
+        body(sc, v_first, std::false_type());
       after();
     }
     __syncthreads();  // the stage buffers are free again
   };
+  // Validity of this lane's candidate v_first + ct.
+  auto valid_at = [&](int v, int n_virt, int stride, int off) -> bool {
+    return v < n_virt && lo + v * stride + off < hi_lane;
+  };
   const int n_all = hi_all - lo;
 
-  uint32_t* my_keys = keys_all + (size_t)(wave * 4 + quarter) * cap;
+  uint32_t* my_keys = keys_all + (size_t)(wave * 4 + quarter) * lstride;
   int n_cnt = 0;            // keys in this lane's row list (uniform over the quarter)
   float accept = kNegInf;   // scores >= accept are kept
-  auto append = [&](float sc, int b, bool valid) {
-    const bool pass = valid && sc >= accept;
-    const uint64_t m = ballot(pass);
-    if (m) {
-      const uint32_t m16 = (uint32_t)(m >> (16 * quarter)) & 0xFFFFu;
-      if (pass) my_keys[n_cnt + __popc(m16 & lt16)] = score_key(sc);
-      n_cnt += __popc(m16);
+  // Keys of the scores >= accept join the row's list (any order); positions from a prefix count
+  // over the row's 16 lanes.
+  int s_n_virt = 0, s_stride = 1, s_off = 0;  // the current stream's candidate mapping
+  auto append = [&](const float (&sc)[kTiles], int v_first, auto full_t) {
+    constexpr bool kFull = decltype(full_t)::value;
+    uint32_t pm = 0;  // bit ct: candidate v_first + ct passes
+#pragma unroll
+    for (int ct = 0; ct < kTiles; ++ct) {
+      const bool ok = kFull || valid_at(v_first + ct, s_n_virt, s_stride, s_off);
+      pm |= (ok && sc[ct] >= accept) ? (1u << ct) : 0u;
     }
+    if (!ballot(pm != 0u)) return;
+    const uint32_t cnt = __popc(pm);
+    const uint32_t incl = row16_prefix(cnt);
+    const uint32_t total = __shfl(incl, l | 15, 64);
+    uint32_t pos = n_cnt + incl - cnt;
+#pragma unroll
+    for (int ct = 0; ct < kTiles; ++ct)
+      if (pm & (1u << ct)) my_keys[pos++] = score_key(sc[ct]);
+    n_cnt += total;
   };
   auto trim_full = [&]() {  // trim the rows whose list could overflow on the next chunk
     const uint64_t need_m = ballot(n_cnt + kChunk > cap);
@@ -276,7 +371,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
       for (int q = 0; q < 4; ++q) {
         if ((need_m >> (16 * q)) & 1ull) {
           const int nq = readlane(n_cnt, 16 * q);
-          const uint32_t tau = wave_trim_keys<P>(keys_all + (size_t)(wave * 4 + q) * cap, nq, kb);
+          const uint32_t tau = wave_trim_keys<P>(keys_all + (size_t)(wave * 4 + q) * lstride, nq, kb, hist);
           if (quarter == q) {
             n_cnt = kb;
             accept = key_to_score(tau);
@@ -295,6 +390,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
   const int stride = n_all > 2 * kb ? (n_all + sample_max - 1) / sample_max : 0;
   if (stride > 1) {
     const int n_virt = (n_all - stride / 2 + stride - 1) / stride;
+    s_n_virt = n_virt;
+    s_stride = stride;
+    s_off = stride / 2;
     stream(n_virt, stride, stride / 2, append, nothing);
     lds_wait();
     float est = kNegInf;
@@ -304,7 +402,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
       const int ks = cq > 0 ? (int)(((long long)2 * kb * nq + cq - 1) / cq) : 0;
       if (cq > 2 * kb && ks >= 1 && ks < nq) {
         int above;
-        const uint32_t t = wave_kth_largest<P>(keys_all + (size_t)(wave * 4 + q) * cap, nq, ks, &above);
+        const uint32_t t = wave_kth_largest<P>(keys_all + (size_t)(wave * 4 + q) * lstride, nq, ks, &above, hist);
         if (quarter == q) est = key_to_score(t);
       }
     }
@@ -313,6 +411,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
   }
 
   // ------------------------------------------------------------------ pass 1: tau and ties
+  s_n_virt = n_all;
+  s_stride = 1;
+  s_off = 0;
   stream(n_all, 1, 0, append, trim_full);
   lds_wait();
   // A row whose starting threshold was above its K_B-th score kept fewer than K_B keys: rescan
@@ -343,7 +444,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
     const int cq = readlane(n_cand, 16 * q);
     if (cq > kb) {
       int above;
-      const uint32_t tau = wave_kth_largest<P>(keys_all + (size_t)(wave * 4 + q) * cap, nq, kb, &above);
+      const uint32_t tau = wave_kth_largest<P>(keys_all + (size_t)(wave * 4 + q) * lstride, nq, kb, &above, hist);
       if (quarter == q) {
         tau_f = key_to_score(tau);
         ties = kb - above;
@@ -353,36 +454,60 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
 
   // ------------------------------------------------------------------ pass 2: emit in order
   int n_out = 0, t_seen = 0;  // uniform over the quarter
+  // The selection is staged in the row's (now unused) key list and written out at the end: global
+  // stores inside the loop would make every chunk's vmcnt wait for them as well.
   int32_t* out_row = valid_o ? topk + ((long long)g_o * n_tokens + row_o / n_groups) * kb : nullptr;
-  auto emit = [&](float sc, int b, bool valid) {
-    const bool gt = valid && sc > tau_f;
-    const bool eq = valid && sc == tau_f;
-    const uint32_t em16 = (uint32_t)(ballot(eq) >> (16 * quarter)) & 0xFFFFu;
-    const bool keep = gt || (eq && t_seen + __popc(em16 & lt16) < ties);
-    const uint32_t km16 = (uint32_t)(ballot(keep) >> (16 * quarter)) & 0xFFFFu;
-    if (keep) {
-      const int pos = n_out + __popc(km16 & lt16);
-      out_row[pos] = b;
+  int32_t* sel_lds = reinterpret_cast<int32_t*>(my_keys);
+  // Candidates above tau, and the first `ties` equal to tau, in ascending block order: this lane's
+  // 8 candidates follow those of lanes with a lower l % 16 in the same row.
+  auto emit = [&](const float (&sc)[kTiles], int v_first, auto full_t) {
+    constexpr bool kFull = decltype(full_t)::value;
+    uint32_t gm = 0, em = 0;
+#pragma unroll
+    for (int ct = 0; ct < kTiles; ++ct) {
+      const bool ok = kFull || valid_at(v_first + ct, n_all, 1, 0);
+      gm |= (ok && sc[ct] > tau_f) ? (1u << ct) : 0u;
+      em |= (ok && sc[ct] == tau_f) ? (1u << ct) : 0u;
     }
-    n_out += __popc(km16);
-    t_seen += __popc(em16);
+    if (!ballot((gm | em) != 0u)) return;
+    const uint32_t ng = __popc(gm), ne = __popc(em);
+    const uint32_t incl = row16_prefix(ng | (ne << 16));  // row totals <= 128 each
+    const uint32_t total = __shfl(incl, l | 15, 64);
+    const int g_before = (int)((incl & 0xFFFFu) - ng), e_before = (int)((incl >> 16) - ne);
+    const int rem = max(0, ties - t_seen);  // ties still to take
+    int pos = n_out + g_before + min(e_before, rem);
+    int e_rank = e_before;
+#pragma unroll
+    for (int ct = 0; ct < kTiles; ++ct) {
+      if (gm & (1u << ct)) {
+        sel_lds[pos++] = lo + v_first + ct;
+      } else if (em & (1u << ct)) {
+        if (e_rank < rem) sel_lds[pos++] = lo + v_first + ct;
+        ++e_rank;
+      }
+    }
+    n_out += (int)(total & 0xFFFFu) + min((int)(total >> 16), rem);
+    t_seen += (int)(total >> 16);
   };
   stream(n_all, 1, 0, emit, nothing);
-  // Padding / counts.
+  lds_wait();
   if (valid_o)
-    for (int e = n_out + l16; e < kb; e += 16) out_row[e] = -1;
+    for (int e = l16; e < kb; e += 16) out_row[e] = e < n_out ? sel_lds[e] : -1;
 }
 
 namespace {
 
-size_t select_lds_bytes(int waves, int cap) { return (size_t)2 * kStageBytes + (size_t)waves * 4 * cap * 4; }
+// Stage buffers, the rows' key lists and one 256-word histogram per wave.
+size_t select_lds_bytes(int waves, int cap) {
+  return (size_t)2 * kStageBytes + (size_t)waves * 4 * (cap + kListPad) * 4 + (size_t)waves * 1024;
+}
 
 // Largest list capacity (multiple of 64) that fits `waves` in the LDS budget, capped at a size
 // where trims are rare; 0 below the minimum (K_B plus one chunk of appends plus slack).
 int select_cap(int waves, int kb, size_t lds_budget) {
-  const long long avail = (long long)lds_budget - 2LL * kStageBytes - 256;  // 256 B: static LDS
+  const long long avail = (long long)lds_budget - 2LL * kStageBytes - 256 - waves * 1024LL;  // 256 B: static LDS
   if (avail <= 0) return 0;
-  int cap = (int)(avail / ((long long)waves * 4 * 4)) / 64 * 64;
+  int cap = (int)(avail / ((long long)waves * 4 * 4) - kListPad) / 64 * 64;
   const int need = kb + kChunk + 64;
   const int enough = ((4 * kb + kChunk > need ? 4 * kb + kChunk : need) + 63) / 64 * 64;
   if (cap > enough) cap = enough;
@@ -413,8 +538,12 @@ hipError_t launch_index_topk(const uint16_t* qi, const float* w, const uint16_t*
                              int n_groups, int block, int kb, hipStream_t stream) {
   const long long n_rows = (long long)n_tokens * n_groups;
   if (n_rows == 0) return hipSuccess;
-  const size_t budget = (size_t)max_lds_per_block();
+  const size_t budget = (size_t)max_lds_per_block() / SGQA_TOPK_WGS_PER_CU;
+#ifdef SGQA_TOPK_WAVES
+  const int waves = select_cap(SGQA_TOPK_WAVES, kb, budget) > 0 ? SGQA_TOPK_WAVES : 0;
+#else
   const int waves = prefill_waves(kb, budget);
+#endif
   if (waves == 0) return hipErrorInvalidValue;
   const int cap = select_cap(waves, kb, budget);
   const size_t lds = select_lds_bytes(waves, cap);
