@@ -26,6 +26,8 @@
 //  * Launch order is XCD-aware: consecutive workgroup ids go to different XCDs, so the
 //    (tile, group) pairs are dealt round-robin over the 8 XCDs and all parts of one pair (same K/V
 //    stream) land on the same XCD's L2; with G = 8 every XCD serves one KV group.
+#include <type_traits>
+
 #include "sgqa_device.hpp"
 #include "sgqa_internal.hpp"
 
@@ -117,11 +119,13 @@ struct NoOp {
 //   row_pos[qt]: query position of this lane's Q row in tile qt (for the causal mask)
 //   KREG: the K operands come from kreg[ks * 2 + kt] (registers) instead of the K tile; after()
 //         runs once the score products have consumed them.
-template <int QT, bool KREG = false, typename After = NoOp>
+//   MASK: 0 = no key of the chunk can be masked, 1 = apply the mask, 2 = decided by `masked`.
+template <int QT, int MASK = 2, bool KREG = false, typename After = NoOp>
 __device__ __forceinline__ void attn_chunk(const uint8_t* stage, const LaneOffsets& lo, const bf16x8 (&qreg)[QT][8],
-                                           AttnState<QT>& st, float scale_log2, bool masked,
+                                           AttnState<QT>& st, float scale_log2, bool masked_rt,
                                            const int (&row_pos)[QT], const bf16x8* kreg = nullptr,
                                            After after = After()) {
+  const bool masked = MASK == 2 ? masked_rt : MASK == 1;
   const int l = lane_id();
   const int hi = l >> 5;
   f32x16 s[QT][2];
@@ -139,21 +143,24 @@ __device__ __forceinline__ void attn_chunk(const uint8_t* stage, const LaneOffse
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) s[qt][kt] = mfma32(kreg[ks * 2 + kt], qreg[qt][ks], s[qt][kt]);
   } else {
-    // S^T = K Q^T: the K operands of step ks+1 are read while the MFMAs of step ks run.
+    // S^T = K Q^T: the K operands of step ks+2 are read while the MFMAs of step ks run.
     const uint8_t* kp = stage + lo.k;
-    bf16x8 ka[2][2];
-    ka[0][0] = *reinterpret_cast<const bf16x8*>(kp);
-    ka[0][1] = *reinterpret_cast<const bf16x8*>(kp + 32 * kKRowBytes);
+    bf16x8 ka[3][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      ka[ks][0] = *reinterpret_cast<const bf16x8*>(kp + ks * 32);
+      ka[ks][1] = *reinterpret_cast<const bf16x8*>(kp + 32 * kKRowBytes + ks * 32);
+    }
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      if (ks < 7) {
-        ka[(ks + 1) & 1][0] = *reinterpret_cast<const bf16x8*>(kp + (ks + 1) * 32);
-        ka[(ks + 1) & 1][1] = *reinterpret_cast<const bf16x8*>(kp + 32 * kKRowBytes + (ks + 1) * 32);
+      if (ks < 6) {
+        ka[(ks + 2) % 3][0] = *reinterpret_cast<const bf16x8*>(kp + (ks + 2) * 32);
+        ka[(ks + 2) % 3][1] = *reinterpret_cast<const bf16x8*>(kp + 32 * kKRowBytes + (ks + 2) * 32);
       }
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt) s[qt][kt] = mfma32(ka[ks & 1][kt], qreg[qt][ks], s[qt][kt]);
+        for (int qt = 0; qt < QT; ++qt) s[qt][kt] = mfma32(ka[ks % 3][kt], qreg[qt][ks], s[qt][kt]);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -224,14 +231,15 @@ __device__ __forceinline__ void attn_chunk(const uint8_t* stage, const LaneOffse
     const i16x8 cat = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(bf16x8, cat);
   };
-  bf16x8 va[2];
+  bf16x8 va[3];
   va[0] = vread(0);
+  va[1] = vread(1);
 #pragma unroll
   for (int step = 0; step < 16; ++step) {
-    if (step < 15) va[(step + 1) & 1] = vread(step + 1);
+    if (step < 14) va[(step + 2) % 3] = vread(step + 2);
     const int dt = step >> 2, ss = step & 3;
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) st.o[qt][dt] = mfma32(va[step & 1], pb[qt][ss], st.o[qt][dt]);
+    for (int qt = 0; qt < QT; ++qt) st.o[qt][dt] = mfma32(va[step % 3], pb[qt][ss], st.o[qt][dt]);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -419,23 +427,78 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
     return tk < n_tokens ? tk : -1;
   };
 
+  // Gather slots of this lane (the same in every chunk): instruction ii of the 17 + 16 wave-wide
+  // loads of a stage (layout as in chunk_issue) is issued by wave ii % WAVES.
+  constexpr int kInsts = kKTileInsts + kVTileInsts;
+  constexpr int kIssuePerWave = (kInsts + WAVES - 1) / WAVES;
+  int is_row[kIssuePerWave], is_src[kIssuePerWave], is_dst[kIssuePerWave];
+  bool is_vt[kIssuePerWave];  // the slot belongs to the V tile (wave-uniform)
+#pragma unroll
+  for (int xi = 0; xi < kIssuePerWave; ++xi) {
+    const int inst = wave + xi * WAVES;
+    const bool is_v = inst >= kKTileInsts;
+    const int ti = is_v ? inst - kKTileInsts : inst;
+    const int sl = ti * 64 + l;
+    int row, piece;
+    if (is_v) {
+      row = sl >> 4;
+      piece = v_phys(row, sl & 15);
+    } else {
+      row = sl / kKSlotsPerRow;
+      piece = sl - row * kKSlotsPerRow;
+      if (piece == 16) piece = 0;  // padding slot: any in-bounds data
+    }
+    is_row[xi] = row;
+    is_src[xi] = piece * 8;  // elements from the row start
+    is_dst[xi] = (is_v ? kKTileBytes : 0) + ti * 1024;
+    is_vt[xi] = is_v;
+  }
+  auto issue = [&](int n, uint8_t* sb) {
+#pragma unroll
+    for (int xi = 0; xi < kIssuePerWave; ++xi) {
+      if (wave + xi * WAVES < kInsts) {
+        int tkn = tok_at(n, is_row[xi]);
+        if (tkn < 0) tkn = 0;
+        const uint16_t* base = is_vt[xi] ? vbase : kbase;
+        __builtin_amdgcn_global_load_lds((const void*)(base + is_src[xi] + (long long)tkn * kD),
+                                         (lds_void*)(sb + is_dst[xi]), 16, 0, 0);
+      }
+    }
+    if (threadIdx.x < kKeys) {
+      const int tk = tok_at(n, (int)threadIdx.x);
+      reinterpret_cast<int*>(sb + kKTileBytes + kVTileBytes)[threadIdx.x] = tk >= 0 ? tk : 0x7FFFFFFF;
+    }
+  };
+  // Chunks from n_first_masked on can hold a key above this wave's first query or past the list
+  // (tokens ascend with the chunk index); the chunks before them need no mask.
+  auto needs_mask = [&](int n) -> bool {
+    if ((n + 1) * kKeys > n_keys) return true;
+    const int last_kp = (n + 1) * kKeys - 1;
+    const int last_tok = ((int)list[last_kp >> block_shift] << block_shift) + (last_kp & (block - 1));
+    return last_tok > wave_i_min;
+  };
+  int n_first_masked = n_chunks;
+  while (n_first_masked > 0 && needs_mask(n_first_masked - 1)) --n_first_masked;
+
   const LaneOffsets lo = lane_offsets();
-  if (n_chunks > 0) chunk_issue<NT>(stage, kbase, vbase, [&](int key) { return tok_at(0, key); });
+  if (n_chunks > 0) issue(0, stage);
   wait_vm();
   __syncthreads();
-  for (int n = 0; n < n_chunks; ++n) {
+  // One loop step: start the gather of chunk n + 1, run chunk n (unless the wave has no rows),
+  // then wait for the gather and for every wave to be done with chunk n's buffer.
+  auto run = [&](int n, auto mask_t) {
     const int buf = n & 1;
-    const bool has_next = n + 1 < n_chunks;
-    if (has_next)
-      chunk_issue<NT>(stage + (buf ^ 1) * kStageBytes, kbase, vbase, [&](int key) { return tok_at(n + 1, key); });
-    const uint8_t* sb = stage + buf * kStageBytes;
-    // The chunk's last valid key has the largest token; mask only if it can exceed a query.
-    const int last_kp = min((n + 1) * kKeys, n_keys) - 1;
-    const int last_tok = ((int)list[last_kp >> block_shift] << block_shift) + (last_kp & (block - 1));
-    const bool masked = ((n + 1) * kKeys > n_keys) || (last_tok > wave_i_min);
-    if (wave_i_min != 0x7FFFFFFF) attn_chunk<QT>(sb, lo, qreg, st, scale_log2, masked, row_pos);
+    if (n + 1 < n_chunks) issue(n + 1, stage + (buf ^ 1) * kStageBytes);
+    constexpr int kMask = decltype(mask_t)::value;
+    if (kMask >= 0) attn_chunk<QT, kMask>(stage + buf * kStageBytes, lo, qreg, st, scale_log2, kMask == 1, row_pos);
     wait_vm();
     __syncthreads();
+  };
+  if (wave_i_min != 0x7FFFFFFF) {
+    for (int n = 0; n < n_first_masked; ++n) run(n, std::integral_constant<int, 0>());
+    for (int n = n_first_masked; n < n_chunks; ++n) run(n, std::integral_constant<int, 1>());
+  } else {
+    for (int n = 0; n < n_chunks; ++n) run(n, std::integral_constant<int, -1>());
   }
 
   // out[i][h][d] = O^T[d][row] / l
@@ -626,7 +689,7 @@ __global__ __launch_bounds__(256) void k_decode_attend(const uint16_t* __restric
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     // Only the last chunk holds the own block (and the padding past the list): the Sel blocks are
     // all below it, hence visible to the query.
-    attn_chunk<1, true>(vbuf[i & 1], lo, qreg, st, scale_log2, c == n_chunks - 1, row_pos, kreg, [&]() {
+    attn_chunk<1, 2, true>(vbuf[i & 1], lo, qreg, st, scale_log2, c == n_chunks - 1, row_pos, kreg, [&]() {
       if (cn < n_chunks) k_load_regs(kreg, kbase, tok_in(cn));
     });
   }
