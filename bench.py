@@ -39,6 +39,7 @@ def parse():
     ap.add_argument("--workload", default="long_prefill_128k")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ablation", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -154,8 +155,7 @@ def bench_prefill(sg, datagen, torch, wl, steps, warmup):
     r = p.n_q_heads // p.n_kv_heads
     attn_flops = 4.0 * p.head_dim * pairs * r
     n_blocks = p.n_tokens // p.block
-    q_, r_ = divmod(p.n_tokens, p.block)   # sum_i floor(i/B) in closed form
-    scored = p.n_kv_heads * (p.block * q_ * (q_ - 1) // 2 + r_ * q_)
+    scored = scored_candidates(p.n_tokens, p.block, p.n_kv_heads)
     index_flops = 2.0 * p.idx_heads * p.idx_dim * scored
     ucount = o["ucount"].double()
     inflation = float((ucount.mean() * p.block / (p.topk_tokens + p.union_tile)).item())
@@ -225,6 +225,112 @@ def bench_decode(sg, datagen, torch, steps, warmup):
         "cache_compress": {"ms": compress_ms, "bytes": cache_build_bytes,
                            "GB_per_s": cache_build_bytes / (compress_ms / 1e3) / 1e9},
     }
+
+
+def scored_candidates(n_tokens: int, block: int, n_groups: int) -> int:
+    """Sum over queries i < N of c(i) = floor(i/B), times the groups: the (row, block) pairs scored."""
+    q_, r_ = divmod(n_tokens, block)
+    return n_groups * (block * q_ * (q_ - 1) // 2 + r_ * q_)
+
+
+def token_coverage(torch, sel1, selb, block: int, i_min: int = 0, rows_per_chunk: int = 4096) -> float:
+    """Mean over rows (g, i >= i_min) of |T1 & TB| / |T1|: T1 = the token-level selection plus token i,
+    TB = the tokens of the block-level selection plus the own block's visible tokens (every token of
+    T1 is <= i, so a T1 token is covered iff its block is selected or is i's own block).
+    sel1 [G, N, K1] token ids, selb [G, N, KB] block ids, both -1 padded (GPU tensors)."""
+    G, N, _ = sel1.shape
+    nbc = (N + block - 1) // block
+    total = 0.0
+    rows = 0
+    for g in range(G):
+        for i0 in range(i_min, N, rows_per_chunk):
+            i1 = min(N, i0 + rows_per_chunk)
+            s1 = sel1[g, i0:i1].long()
+            sb = selb[g, i0:i1].long()
+            R = i1 - i0
+            inb = torch.zeros((R, nbc + 1), dtype=torch.bool, device=sel1.device)
+            inb.scatter_(1, torch.where(sb >= 0, sb, torch.full_like(sb, nbc)), True)
+            own = (torch.arange(i0, i1, device=sel1.device) // block).unsqueeze(1)
+            inb.scatter_(1, own, True)
+            valid = s1 >= 0
+            hit = torch.gather(inb, 1, torch.where(valid, s1 // block, torch.full_like(s1, nbc))) & valid
+            cov = (hit.sum(1).double() + 1.0) / (valid.sum(1).double() + 1.0)  # + token i itself
+            total += float(cov.sum().item())
+            rows += R
+    return total / rows
+
+
+def bench_ablation(sg, datagen, torch, steps, warmup):
+    """Granularity ablation on the 32K prefill inputs: index + top-k at (B = 1, k = 2048) against
+    compress + index + top-k at (B = 8, k = 4096), on the same indexer queries and keys."""
+    wl = datagen.PREFILL
+    x = datagen.prefill_inputs(wl, device="cuda")
+    N, G = wl.n_tokens, wl.n_kv_heads
+    out = {}
+    sels = {}
+    for B, k in ((1, 2048), (8, 4096)):
+        p = sg.Params(n_tokens=N, n_q_heads=wl.n_q_heads, n_kv_heads=G, block=B, topk_tokens=k,
+                      union_tile=wl.union_tile)
+        blk = torch.empty((N // B, p.idx_dim), dtype=torch.bfloat16, device="cuda")
+        topk = torch.empty((G, N, p.kb), dtype=torch.int32, device="cuda")
+
+        def run():
+            if B > 1:
+                sg.sgqa_compress(p, x["ki"], blk)
+                sg.sgqa_index_topk(p, x["qi"], x["w"], blk, topk)
+            else:  # B = 1: the block keys are the index keys themselves
+                sg.sgqa_index_topk(p, x["qi"], x["w"], x["ki"], topk)
+
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        out[f"B{B}_k{k}_ms"] = e0.elapsed_time(e1) / steps
+        out[f"B{B}_k{k}_scored_pairs"] = scored_candidates(N, B, G)
+        sels[B] = topk
+    out["time_ratio_B1_over_B8"] = out["B1_k2048_ms"] / out["B8_k4096_ms"]
+    out["count_ratio_B1_over_B8"] = out["B1_k2048_scored_pairs"] / out["B8_k4096_scored_pairs"]
+    out["token_coverage_B8_vs_B1"] = token_coverage(torch, sels[1], sels[8], 8)
+    out["token_coverage_B8_vs_B1_rows_past_k"] = token_coverage(torch, sels[1], sels[8], 8, i_min=4096)
+    out["workload"] = "prefill_32k inputs (C1), B=1 k=2048 vs B=8 k=4096"
+    del x, sels
+    torch.cuda.empty_cache()
+    return out
+
+
+def achieved_peaks(torch):
+    """Reference rates measured on this GPU next to the published peaks: a 2 GiB device copy (bytes
+    read + written) and a large bf16 GEMM (the vendor library)."""
+    a = torch.empty(1 << 30, dtype=torch.int16, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    m = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    n = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    for _ in range(3):
+        b.copy_(a)
+        torch.matmul(m, n)
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    e[0].record()
+    for _ in range(10):
+        b.copy_(a)
+    e[1].record()
+    for _ in range(10):
+        torch.matmul(m, n)
+    e[2].record()
+    torch.cuda.synchronize()
+    copy_s = e[0].elapsed_time(e[1]) / 10 / 1e3
+    gemm_s = e[1].elapsed_time(e[2]) / 10 / 1e3
+    res = {"copy_GB_per_s": 2 * a.numel() * 2 / copy_s / 1e9, "spec_hbm_GB_per_s": PEAK_HBM_GBS,
+           "gemm_bf16_TFLOP_per_s": 2.0 * 8192 ** 3 / gemm_s / 1e12, "spec_bf16_TFLOP_per_s": PEAK_BF16_TFLOPS}
+    del a, b, m, n
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(oracle, datagen, torch, np, res, wl):
@@ -338,6 +444,10 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_decode:
         line["decode"] = bench_decode(sg, datagen, torch, args.steps, args.warmup)
+    if not args.no_ablation:
+        log("granularity ablation on the 32K inputs")
+        line["ablation"] = bench_ablation(sg, datagen, torch, 3, 1)
+        line["achieved_peaks"] = achieved_peaks(torch)
     print(json.dumps(line), flush=True)
 
 
