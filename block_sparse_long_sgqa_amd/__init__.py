@@ -36,7 +36,14 @@ SGQA_OP_DECODE = 5
 
 # Every symbol include/sgqa.h declares.
 EXPORTED = ("sgqa_abi_version", "sgqa_status_string", "sgqa_workspace_size", "sgqa_compress", "sgqa_index_topk",
-            "sgqa_union", "sgqa_attend", "sgqa_prefill", "sgqa_decode")
+            "sgqa_union", "sgqa_attend", "sgqa_prefill", "sgqa_decode", "sgqa_decode_varlen", "sgqa_append")
+
+
+class sgqa_pages(ctypes.Structure):
+    """Mirror of `sgqa_pages` in include/sgqa.h (paged K/V cache descriptor)."""
+
+    _fields_ = [("table", ctypes.c_void_p), ("max_pages", ctypes.c_int32), ("page_tokens", ctypes.c_int32),
+                ("n_pages", ctypes.c_int32)]
 
 
 class SgqaError(RuntimeError):
@@ -123,7 +130,11 @@ def lib() -> ctypes.CDLL:
         L.sgqa_attend.argtypes = [PP, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.sgqa_prefill.argtypes = [PP, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.sgqa_decode.argtypes = [PP, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
-        for name in ("sgqa_compress", "sgqa_index_topk", "sgqa_union", "sgqa_attend", "sgqa_prefill", "sgqa_decode"):
+        PG = ctypes.POINTER(sgqa_pages)
+        L.sgqa_decode_varlen.argtypes = [PP, P, P, P, PG, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.sgqa_append.argtypes = [PP, P, P, P, P, P, P, PG, P, P, P]
+        for name in ("sgqa_compress", "sgqa_index_topk", "sgqa_union", "sgqa_attend", "sgqa_prefill", "sgqa_decode",
+                     "sgqa_decode_varlen", "sgqa_append"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -236,6 +247,59 @@ def sgqa_decode(p: Params, q, k_cache, v_cache, blk_k, idx_q, idx_w, out, ws, to
             _ptr(out, "out", torch.bfloat16, (S, Hq, D)))
     _check(lib().sgqa_decode(ctypes.byref(p.c()), *args, _ptr(ws, "ws", torch.uint8), ws.numel(),
                              _stream(stream)), "sgqa_decode")
+
+
+class Pages:
+    """A paged K/V cache: `table` [S][max_pages] int32 on the GPU, pools [n_pages][G][page_tokens][D]."""
+
+    def __init__(self, table, page_tokens: int, n_pages: int):
+        self.table = table
+        self.page_tokens = page_tokens
+        self.n_pages = n_pages
+
+    def c(self, n_seqs: int) -> sgqa_pages:
+        t = _ptr(self.table, "page table", torch.int32)
+        if self.table.dim() != 2 or self.table.shape[0] != n_seqs:
+            raise ValueError(f"page table: expected [{n_seqs}][max_pages], got {tuple(self.table.shape)}")
+        return sgqa_pages(t.value, self.table.shape[1], self.page_tokens, self.n_pages)
+
+
+def _cache_shape(p: Params, pages: Optional[Pages]):
+    if pages is None:
+        return (p.n_seqs, p.n_kv_heads, p.n_tokens, p.head_dim)
+    return (pages.n_pages, p.n_kv_heads, pages.page_tokens, p.head_dim)
+
+
+def sgqa_decode_varlen(p: Params, q, k_cache, v_cache, blk_k, idx_q, idx_w, seq_lens, out, ws, pages=None,
+                       topk_out=None, stream=None) -> None:
+    S, C, Hq, G, D = p.n_seqs, p.n_tokens, p.n_q_heads, p.n_kv_heads, p.head_dim
+    shp = _cache_shape(p, pages)
+    pg = pages.c(S) if pages is not None else None
+    args = (_ptr(q, "q", torch.bfloat16, (S, Hq, D)), _ptr(k_cache, "k_cache", torch.bfloat16, shp),
+            _ptr(v_cache, "v_cache", torch.bfloat16, shp), ctypes.byref(pg) if pg is not None else None,
+            _ptr(blk_k, "blk_k", torch.bfloat16, (S, C // p.block, p.idx_dim)),
+            _ptr(idx_q, "idx_q", torch.bfloat16, (S, G, p.idx_heads, p.idx_dim)),
+            _ptr(idx_w, "idx_w", torch.float32, (G, p.idx_heads)),
+            _ptr(seq_lens, "seq_lens", torch.int32, (S,)),
+            _ptr(topk_out, "topk_out", torch.int32, (S, G, p.kb)),
+            _ptr(out, "out", torch.bfloat16, (S, Hq, D)))
+    _check(lib().sgqa_decode_varlen(ctypes.byref(p.c()), *args, _ptr(ws, "ws", torch.uint8), ws.numel(),
+                                    _stream(stream)), "sgqa_decode_varlen")
+
+
+def sgqa_append(p: Params, k_new, v_new, idx_k_new, positions, k_cache, v_cache, idx_k_cache, blk_k, pages=None,
+                stream=None) -> None:
+    S, C, G, D = p.n_seqs, p.n_tokens, p.n_kv_heads, p.head_dim
+    shp = _cache_shape(p, pages)
+    pg = pages.c(S) if pages is not None else None
+    args = (_ptr(k_new, "k_new", torch.bfloat16, (S, G, D)), _ptr(v_new, "v_new", torch.bfloat16, (S, G, D)),
+            _ptr(idx_k_new, "idx_k_new", torch.bfloat16, (S, p.idx_dim)),
+            _ptr(positions, "positions", torch.int32, (S,)),
+            _ptr(k_cache, "k_cache", torch.bfloat16, shp), _ptr(v_cache, "v_cache", torch.bfloat16, shp),
+            ctypes.byref(pg) if pg is not None else None,
+            _ptr(idx_k_cache, "idx_k_cache", torch.bfloat16, (S, C, p.idx_dim)),
+            _ptr(blk_k, "blk_k", torch.bfloat16, (S, C // p.block, p.idx_dim)))
+    _check(lib().sgqa_append(ctypes.byref(p.c()), *args, _stream(stream)), "sgqa_append")
 
 
 # ------------------------------------------------------------------------------------ helpers

@@ -569,8 +569,8 @@ constexpr int kDecVStage = kVTileBytes + kKeys * 4;  // decode: V tile + token t
 
 // Decode gather of one wave: the V tile of one chunk (16 wave-wide global_load_lds, layout as in
 // chunk_issue) and its token table.
-template <typename TokFn>
-__device__ __forceinline__ void v_issue_wave(uint8_t* vst, const uint16_t* vbase, TokFn tok_of) {
+template <typename TokFn, typename RowFn>
+__device__ __forceinline__ void v_issue_wave(uint8_t* vst, RowFn row_of, TokFn tok_of) {
   const int l = lane_id();
 #pragma unroll
   for (int ti = 0; ti < kVTileInsts; ++ti) {
@@ -579,8 +579,7 @@ __device__ __forceinline__ void v_issue_wave(uint8_t* vst, const uint16_t* vbase
     const int piece = v_phys(row, slot & 15);
     int tkn = tok_of(row);
     if (tkn < 0) tkn = 0;
-    __builtin_amdgcn_global_load_lds((const void*)(vbase + (long long)tkn * kD + piece * 8),
-                                     (lds_void*)(vst + ti * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(row_of(tkn) + piece * 8), (lds_void*)(vst + ti * 1024), 16, 0, 0);
   }
   const int t = tok_of(l);
   reinterpret_cast<int*>(vst + kVTileBytes)[l] = t >= 0 ? t : 0x7FFFFFFF;
@@ -589,14 +588,14 @@ __device__ __forceinline__ void v_issue_wave(uint8_t* vst, const uint16_t* vbase
 // The K operands of one chunk straight from global memory into registers: the A operand of
 // S^T = K Q^T for key tile kt and step ks is key row 32 kt + (l % 32), elements 16 ks + 8 (l / 32)
 // .. +7, i.e. 16 contiguous bytes of one cached key.
-template <typename TokFn>
-__device__ __forceinline__ void k_load_regs(bf16x8 (&kreg)[16], const uint16_t* kbase, TokFn tok_of) {
+template <typename TokFn, typename RowFn>
+__device__ __forceinline__ void k_load_regs(bf16x8 (&kreg)[16], RowFn row_of, TokFn tok_of) {
   const int l = lane_id();
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
     int tkn = tok_of(32 * kt + (l & 31));
     if (tkn < 0) tkn = 0;
-    const uint16_t* src = kbase + (long long)tkn * kD + 8 * (l >> 5);
+    const uint16_t* src = row_of(tkn) + 8 * (l >> 5);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) kreg[ks * 2 + kt] = *reinterpret_cast<const bf16x8*>(src + 16 * ks);
   }
@@ -609,11 +608,21 @@ __device__ __forceinline__ void k_load_regs(bf16x8 (&kreg)[16], const uint16_t* 
 // the V tiles, which need the transposing LDS reads, are double-buffered per wave. Each wave keeps
 // its own online-softmax state for the r heads (one 32-row tile, r <= 32 rows used); the four
 // states are merged in LDS into the bf16 output.
+//
+// Caches: dense [S][G][cap][D] per sequence (PAGED = false), or pools [n_pages][G][page][D] with the
+// position t of sequence s in page table[s * max_pages + t / page] (PAGED = true; page = 1 << page_shift,
+// a multiple of B, so a block never straddles two pages; entries outside [0, n_pages) are clamped, so
+// a bad table reads wrong data but never outside the pool). The context length of sequence s is
+// lens[s] clamped to [1, cap] (cap for every sequence when lens is null).
+template <bool PAGED>
 __global__ __launch_bounds__(256) void k_decode_attend(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
                                                        const uint16_t* __restrict__ vc,
                                                        const int32_t* __restrict__ sel, uint16_t* __restrict__ out,
-                                                       int ctx, int n_q_heads, int n_groups, int block,
-                                                       int block_shift, int kb, float scale_log2) {
+                                                       int cap, int n_q_heads, int n_groups, int block,
+                                                       int block_shift, int kb, float scale_log2,
+                                                       const int32_t* __restrict__ lens,
+                                                       const int32_t* __restrict__ table, int max_pages,
+                                                       int page_shift, int n_pages) {
   constexpr int kWavesD = 4;
   extern __shared__ __align__(16) uint8_t smem[];
   const int wave = threadIdx.x >> 6;
@@ -624,6 +633,8 @@ __global__ __launch_bounds__(256) void k_decode_attend(const uint16_t* __restric
   const int s = blockIdx.x / n_groups, g = blockIdx.x % n_groups;
   const int r = n_q_heads / n_groups;
   const int l = lane_id();
+  int ctx = lens ? lens[s] : cap;
+  ctx = ctx < 1 ? 1 : (ctx > cap ? cap : ctx);
   const int i_q = ctx - 1;
   const int own = i_q / block;
 
@@ -658,9 +669,17 @@ __global__ __launch_bounds__(256) void k_decode_attend(const uint16_t* __restric
   }
   AttnState<1> st;
   state_init(st);
-  const long long seq_off = ((long long)s * n_groups + g) * ctx * kD;
-  const uint16_t* kbase = kc + seq_off;
-  const uint16_t* vbase = vc + seq_off;
+  // Row of token t (of this sequence and group) in the K and V caches, as an element offset.
+  const int32_t* ptab = PAGED ? table + (long long)s * max_pages : nullptr;
+  const long long seq_off = PAGED ? 0 : ((long long)s * n_groups + g) * cap * kD;
+  auto row_off = [&](int t) -> long long {
+    if (!PAGED) return seq_off + (long long)t * kD;
+    int pg = ptab[t >> page_shift];
+    pg = pg < 0 ? 0 : (pg >= n_pages ? n_pages - 1 : pg);
+    return ((((long long)pg * n_groups + g) << page_shift) + (t & ((1 << page_shift) - 1))) * kD;
+  };
+  auto krow = [&](int t) -> const uint16_t* { return kc + row_off(t); };
+  auto vrow = [&](int t) -> const uint16_t* { return vc + row_off(t); };
   const int n_keys = (n_sel + 1) * block;
   const int n_chunks = (n_keys + kKeys - 1) / kKeys;
   const LaneOffsets lo = lane_offsets(0);
@@ -674,14 +693,14 @@ __global__ __launch_bounds__(256) void k_decode_attend(const uint16_t* __restric
   };
   bf16x8 kreg[16];
   if (wave < n_chunks) {
-    v_issue_wave(vbuf[0], vbase, tok_in(wave));
-    k_load_regs(kreg, kbase, tok_in(wave));
+    v_issue_wave(vbuf[0], vrow, tok_in(wave));
+    k_load_regs(kreg, krow, tok_in(wave));
   }
   int i = 0;
   for (int c = wave; c < n_chunks; c += kWavesD, ++i) {
     const int cn = c + kWavesD;
     if (cn < n_chunks) {
-      v_issue_wave(vbuf[(i + 1) & 1], vbase, tok_in(cn));
+      v_issue_wave(vbuf[(i + 1) & 1], vrow, tok_in(cn));
       asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // V and K of chunk c landed; V of cn flies
     } else {
       wait_vm();
@@ -690,7 +709,7 @@ __global__ __launch_bounds__(256) void k_decode_attend(const uint16_t* __restric
     // Only the last chunk holds the own block (and the padding past the list): the Sel blocks are
     // all below it, hence visible to the query.
     attn_chunk<1, 2, true>(vbuf[i & 1], lo, qreg, st, scale_log2, c == n_chunks - 1, row_pos, kreg, [&]() {
-      if (cn < n_chunks) k_load_regs(kreg, kbase, tok_in(cn));
+      if (cn < n_chunks) k_load_regs(kreg, krow, tok_in(cn));
     });
   }
 
@@ -733,14 +752,21 @@ size_t decode_attend_lds(int kb) { return (size_t)4 * 2 * kDecVStage + (size_t)(
 
 hipError_t launch_decode_attend(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, const int32_t* sel,
                                 uint16_t* out, int n_seqs, int ctx, int n_q_heads, int n_groups, int block, int kb,
-                                float scale, hipStream_t stream) {
+                                float scale, const int32_t* lens, const PageTable& pages, hipStream_t stream) {
   const size_t lds = decode_attend_lds(kb);
   if (lds > (size_t)max_lds_per_block()) return hipErrorInvalidValue;
-  hipError_t e = hipFuncSetAttribute((const void*)k_decode_attend, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const void* fn = pages.table ? (const void*)k_decode_attend<true> : (const void*)k_decode_attend<false>;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const float scale_log2 = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(k_decode_attend, dim3((unsigned)(n_seqs * n_groups)), dim3(256), lds, stream, q, kc, vc, sel, out,
-                     ctx, n_q_heads, n_groups, block, __builtin_ctz(block), kb, scale_log2);
+  const dim3 grid((unsigned)(n_seqs * n_groups));
+  if (pages.table)
+    hipLaunchKernelGGL(k_decode_attend<true>, grid, dim3(256), lds, stream, q, kc, vc, sel, out, ctx, n_q_heads,
+                       n_groups, block, __builtin_ctz(block), kb, scale_log2, lens, pages.table, pages.max_pages,
+                       __builtin_ctz(pages.page_tokens), pages.n_pages);
+  else
+    hipLaunchKernelGGL(k_decode_attend<false>, grid, dim3(256), lds, stream, q, kc, vc, sel, out, ctx, n_q_heads,
+                       n_groups, block, __builtin_ctz(block), kb, scale_log2, lens, nullptr, 0, 0, 0);
   return hipGetLastError();
 }
 

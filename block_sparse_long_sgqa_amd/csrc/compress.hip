@@ -86,4 +86,80 @@ hipError_t launch_compress(const uint16_t* ki, uint16_t* kbar, int n_seqs, int n
   return hipGetLastError();
 }
 
+// Incremental decode: append the token at position j = pos[s] of every sequence s (one workgroup per
+// sequence). K/V rows go to the dense cache [S][G][cap][D] or to the pool page table[s][j / page]
+// ([n_pages][G][page][D]; a page entry outside [0, n_pages) skips the K/V write); the index key goes to
+// idx_cache [S][cap][d_I]; when j closes a block (j % B == B - 1) the block key of block j / B is
+// formed with the arithmetic of k_compress (fp32 sum of the B keys in ascending position, times
+// 1/B, one rounding to bf16), the new key taken from registers rather than re-read.
+__global__ __launch_bounds__(256) void k_append(const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+                                                const uint16_t* __restrict__ idx_new, const int32_t* __restrict__ pos,
+                                                uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
+                                                const int32_t* __restrict__ table, int max_pages, int page_shift,
+                                                int n_pages, uint16_t* __restrict__ idx_cache,
+                                                uint16_t* __restrict__ kbar, int cap, int n_groups, int idx_dim,
+                                                int block) {
+  constexpr int kD = 128;
+  const int s = blockIdx.x;
+  const int j = pos[s];
+  if (j < 0 || j >= cap) return;
+  const int t = threadIdx.x;
+  long long pg = -1;
+  if (table) {
+    pg = table[(long long)s * max_pages + (j >> page_shift)];
+    if (pg >= n_pages) pg = -1;
+  }
+  const bool write_kv = !table || pg >= 0;
+  if (write_kv) {
+    for (int x = t; x < n_groups * (kD / 8); x += blockDim.x) {
+      const int g = x / (kD / 8), pc = x % (kD / 8);
+      const long long row = table ? (((pg * n_groups + g) << page_shift) + (j & ((1 << page_shift) - 1)))
+                                  : (((long long)s * n_groups + g) * cap + j);
+      const long long src = ((long long)s * n_groups + g) * kD + pc * 8;
+      *reinterpret_cast<u32x4*>(kc + row * kD + pc * 8) = *reinterpret_cast<const u32x4*>(k_new + src);
+      *reinterpret_cast<u32x4*>(vc + row * kD + pc * 8) = *reinterpret_cast<const u32x4*>(v_new + src);
+    }
+  }
+  const int chunks = idx_dim / 8;
+  if (t < chunks) {
+    const u32x4 nv = *reinterpret_cast<const u32x4*>(idx_new + (long long)s * idx_dim + t * 8);
+    *reinterpret_cast<u32x4*>(idx_cache + ((long long)s * cap + j) * idx_dim + t * 8) = nv;
+    if (j % block == block - 1) {
+      float acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+      for (int r = j - block + 1; r < j; ++r) {
+        const u32x4 rv = *reinterpret_cast<const u32x4*>(idx_cache + ((long long)s * cap + r) * idx_dim + t * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += bf16_bits_to_f32(rv[e] & 0xFFFFu);
+          acc[2 * e + 1] += bf16_bits_to_f32(rv[e] >> 16);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += bf16_bits_to_f32(nv[e] & 0xFFFFu);
+        acc[2 * e + 1] += bf16_bits_to_f32(nv[e] >> 16);
+      }
+      const float inv = 1.0f / (float)block;
+      u32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+      const long long nb = cap / block;
+      *reinterpret_cast<u32x4*>(kbar + ((long long)s * nb + j / block) * idx_dim + t * 8) = o;
+    }
+  }
+}
+
+hipError_t launch_append(const uint16_t* k_new, const uint16_t* v_new, const uint16_t* idx_new, const int32_t* pos,
+                         uint16_t* kc, uint16_t* vc, const PageTable& pages, uint16_t* idx_cache, uint16_t* kbar,
+                         int n_seqs, int cap, int n_groups, int idx_dim, int block, hipStream_t stream) {
+  if (n_seqs == 0) return hipSuccess;
+  const int page_shift = pages.table ? __builtin_ctz(pages.page_tokens) : 0;
+  hipLaunchKernelGGL(k_append, dim3((unsigned)n_seqs), dim3(256), 0, stream, k_new, v_new, idx_new, pos, kc, vc,
+                     pages.table, pages.max_pages, page_shift, pages.n_pages, idx_cache, kbar, cap, n_groups, idx_dim,
+                     block);
+  return hipGetLastError();
+}
+
 }  // namespace sgqa

@@ -47,12 +47,21 @@ constexpr int kSegMax = kPickThreads * 32;                  // 32768 keys per pi
 // Key row stride of the score buffer: whole score workgroups, so the pick may read up to it.
 long long score_stride(int c) { return ((long long)(c > 0 ? c : 0) + kScoreBlocksPerWg - 1) / kScoreBlocksPerWg * kScoreBlocksPerWg; }
 
+// Candidates of sequence s: c = floor((L_s - 1) / B) with L_s = lens[s] clamped to [1, cap], or
+// L_s = cap for every sequence when lens is null.
+__device__ __forceinline__ int seq_candidates(const int32_t* lens, int s, int cap, int block) {
+  int len = lens ? lens[s] : cap;
+  len = len < 1 ? 1 : (len > cap ? cap : len);
+  return (len - 1) / block;
+}
+
 // Grid: (sequence, 512-block range). Rows of the output: keys[(s * G + g) * stride + b].
 __global__ __launch_bounds__(256) void k_dscore(const uint16_t* __restrict__ qi, const float* __restrict__ w,
                                                 const uint16_t* __restrict__ kbar_all, uint32_t* __restrict__ keys,
-                                                int n_groups, long long kbar_rows, int c, long long stride,
-                                                int wg_per_seq) {
+                                                int n_groups, long long kbar_rows, const int32_t* __restrict__ lens,
+                                                int cap, int block, long long stride, int wg_per_seq) {
   const int s = blockIdx.x / wg_per_seq;
+  const int c = seq_candidates(lens, s, cap, block);
   const int part = blockIdx.x % wg_per_seq;
   const int wave = threadIdx.x >> 6;
   const int l = lane_id();
@@ -228,10 +237,14 @@ __device__ __forceinline__ uint32_t bucket_select(uint64_t lo, uint64_t hi, uint
 // tau is bounded from below first: the K_B-th largest of the per-thread maxima v has at least K_B
 // keys at or above it, so tau >= v, and few keys lie in [v, max] (typically a small multiple of
 // K_B), which keeps the histogram rounds over the keys cheap and their buckets spread.
+// lens (first level only): row r = s * G + g has seq_candidates(lens, s, cap, block) entries instead
+// of n.
 template <int P>
 __global__ __launch_bounds__(kPickThreads) void k_dpick(const uint32_t* __restrict__ keys, long long row_stride,
                                                         const int32_t* __restrict__ ids, int n, int seg_len,
                                                         int n_seg, int kb, int out_stride,
+                                                        const int32_t* __restrict__ lens, int n_groups, int cap,
+                                                        int block,
                                                         int32_t* __restrict__ sel,
                                                         int32_t* __restrict__ topk_out,
                                                         uint32_t* __restrict__ out_keys,
@@ -244,7 +257,8 @@ __global__ __launch_bounds__(kPickThreads) void k_dpick(const uint32_t* __restri
   const int sg = blockIdx.x % n_seg;
   const int t = threadIdx.x, wave = t >> 6, l = lane_id();
   const long long base = row * row_stride + (long long)sg * seg_len;
-  const int len = min(seg_len, n - sg * seg_len);
+  const int n_row = lens ? seq_candidates(lens, (int)(row / n_groups), cap, block) : n;
+  const int len = max(0, min(seg_len, n_row - sg * seg_len));
   const int e0 = t * P;
 
   uint32_t k[P];
@@ -374,7 +388,8 @@ int pick_p(int n) {
 int list_stride(int kb) { return (kb + 3) / 4 * 4; }
 
 hipError_t launch_pick(const uint32_t* keys, long long row_stride, const int32_t* ids, int n, int n_rows, int kb,
-                       int32_t* sel, int32_t* topk_out, uint32_t* out_keys, int32_t* out_ids, hipStream_t stream) {
+                       int32_t* sel, int32_t* topk_out, uint32_t* out_keys, int32_t* out_ids, const int32_t* lens,
+                       int n_groups, int cap, int block, hipStream_t stream) {
   int seg_len, n_seg, p;
   if (n <= kSegMax) {
     p = pick_p(n);
@@ -389,7 +404,7 @@ hipError_t launch_pick(const uint32_t* keys, long long row_stride, const int32_t
 #define SGQA_PICK_CASE(PP)                                                                                   \
   if (p == PP) {                                                                                             \
     hipLaunchKernelGGL(k_dpick<PP>, grid, dim3(kPickThreads), 0, stream, keys, row_stride, ids, n, seg_len,  \
-                       n_seg, kb, out_keys ? list_stride(kb) : kb, sel, topk_out, out_keys, out_ids);                                         \
+                       n_seg, kb, out_keys ? list_stride(kb) : kb, lens, n_groups, cap, block, sel, topk_out, out_keys, out_ids);                                         \
     return hipGetLastError();                                                                                \
   }
   SGQA_PICK_CASE(8)
@@ -437,7 +452,7 @@ size_t decode_select_ws_bytes(int n_seqs, int n_tokens, int n_groups, int block,
 
 hipError_t launch_decode_select(const uint16_t* qi, const float* w, const uint16_t* kbar, int32_t* sel,
                                 int32_t* topk_out, void* ws, int n_seqs, int n_tokens, int n_groups, int block, int kb,
-                                hipStream_t stream) {
+                                const int32_t* lens, hipStream_t stream) {
   const int c = (n_tokens - 1) / block;
   const int n_rows = n_seqs * n_groups;
   if (n_rows == 0) return hipSuccess;
@@ -446,7 +461,8 @@ hipError_t launch_decode_select(const uint16_t* qi, const float* w, const uint16
   if (c > 0) {
     const int wg_per_seq = (int)(stride / kScoreBlocksPerWg);
     hipLaunchKernelGGL(k_dscore, dim3((unsigned)((long long)n_seqs * wg_per_seq)), dim3(kScoreWaves * 64), 0, stream,
-                       qi, w, kbar, lay.keys, n_groups, (long long)(n_tokens / block), c, stride, wg_per_seq);
+                       qi, w, kbar, lay.keys, n_groups, (long long)(n_tokens / block), lens, n_tokens, block, stride,
+                       wg_per_seq);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -456,19 +472,23 @@ hipError_t launch_decode_select(const uint16_t* qi, const float* w, const uint16
   long long row_stride = stride;
   int n = c;
   int level = 0;
+  const int32_t* lv_lens = lens;  // only the first level has per-sequence lengths
   while (n > kSegMax) {
     const int n_seg = (n + kSegMax - 1) / kSegMax;
     uint32_t* ok = lay.list_keys[level & 1];
     int32_t* oi = lay.list_ids[level & 1];
-    hipError_t e = launch_pick(keys, row_stride, ids, n, n_rows, kb, nullptr, nullptr, ok, oi, stream);
+    hipError_t e = launch_pick(keys, row_stride, ids, n, n_rows, kb, nullptr, nullptr, ok, oi, lv_lens, n_groups,
+                               n_tokens, block, stream);
     if (e != hipSuccess) return e;
     keys = ok;
     ids = oi;
     n = n_seg * list_stride(kb);
     row_stride = (long long)n_seg * list_stride(kb);
+    lv_lens = nullptr;
     ++level;
   }
-  return launch_pick(keys, row_stride, ids, n, n_rows, kb, sel, topk_out, nullptr, nullptr, stream);
+  return launch_pick(keys, row_stride, ids, n, n_rows, kb, sel, topk_out, nullptr, nullptr, lv_lens, n_groups, n_tokens,
+                     block, stream);
 }
 
 }  // namespace sgqa

@@ -282,27 +282,88 @@ int sgqa_prefill(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k, c
   return status_of(e);
 }
 
-int sgqa_decode(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k_cache, const sgqa_bf16* v_cache,
-                const sgqa_bf16* blk_k, const sgqa_bf16* idx_q, const float* idx_w, int32_t* topk_out,
-                sgqa_bf16* out, void* ws, size_t ws_bytes, sgqa_stream stream) {
+namespace {
+
+// Checks of a paged-cache descriptor (null = dense caches); on success fills `out`.
+int check_pages(const sgqa_params* p, const sgqa_pages* pg, PageTable* out) {
+  *out = PageTable();
+  if (!pg) return SGQA_OK;
+  if (!pg->table) return SGQA_ERR_NULL;
+  if (!aligned16(pg->table)) return SGQA_ERR_ALIGN;
+  const int pt = pg->page_tokens;
+  if (pt < p->block || (pt & (pt - 1)) != 0) return SGQA_ERR_SHAPE;
+  if (pg->max_pages < 1 || (long long)pg->max_pages * pt < p->n_tokens || pg->n_pages < 1) return SGQA_ERR_SHAPE;
+  out->table = pg->table;
+  out->max_pages = pg->max_pages;
+  out->page_tokens = pt;
+  out->n_pages = pg->n_pages;
+  return SGQA_OK;
+}
+
+// Shared body of sgqa_decode and sgqa_decode_varlen.
+int decode_impl(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k_cache, const sgqa_bf16* v_cache,
+                const sgqa_pages* pages, const sgqa_bf16* blk_k, const sgqa_bf16* idx_q, const float* idx_w,
+                const int32_t* seq_lens, int32_t* topk_out, sgqa_bf16* out, void* ws, size_t ws_bytes,
+                sgqa_stream stream) {
   int st = check_params(p, NEED_INDEX | NEED_SELECT | NEED_DECODE | NEED_ATTN, false);
   if (st) return st;
   if (!q || !k_cache || !v_cache || !idx_q || !idx_w || !out || (!blk_k && p->n_tokens > p->block))
     return SGQA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(blk_k) || !aligned16(idx_q) ||
-      !aligned16(idx_w) || !aligned16(topk_out) || !aligned16(out) || !aligned16(ws))
+      !aligned16(idx_w) || !aligned16(topk_out) || !aligned16(out) || !aligned16(ws) || !aligned16(seq_lens))
     return SGQA_ERR_ALIGN;
+  PageTable pt;
+  st = check_pages(p, pages, &pt);
+  if (st) return st;
   const DecodeWs l = decode_layout(p, ws);
   if (!ws || ws_bytes < l.bytes) return SGQA_ERR_WORKSPACE;
   if (!device_ok()) return SGQA_ERR_DEVICE;
   hipStream_t s = (hipStream_t)stream;
   const int kb = kb_of(p);
   hipError_t e = launch_decode_select(idx_q, idx_w, blk_k, l.sel, topk_out, l.select_ws, p->n_seqs, p->n_tokens,
-                                      p->n_kv_heads, p->block, kb, s);
+                                      p->n_kv_heads, p->block, kb, seq_lens, s);
   if (e == hipSuccess)
     e = launch_decode_attend(q, k_cache, v_cache, l.sel, out, p->n_seqs, p->n_tokens, p->n_q_heads,
-                             p->n_kv_heads, p->block, kb, scale_of(p), s);
+                             p->n_kv_heads, p->block, kb, scale_of(p), seq_lens, pt, s);
   return status_of(e);
+}
+
+}  // namespace
+
+int sgqa_decode(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k_cache, const sgqa_bf16* v_cache,
+                const sgqa_bf16* blk_k, const sgqa_bf16* idx_q, const float* idx_w, int32_t* topk_out,
+                sgqa_bf16* out, void* ws, size_t ws_bytes, sgqa_stream stream) {
+  return decode_impl(p, q, k_cache, v_cache, nullptr, blk_k, idx_q, idx_w, nullptr, topk_out, out, ws, ws_bytes,
+                     stream);
+}
+
+int sgqa_decode_varlen(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k_cache,
+                       const sgqa_bf16* v_cache, const sgqa_pages* pages, const sgqa_bf16* blk_k,
+                       const sgqa_bf16* idx_q, const float* idx_w, const int32_t* seq_lens, int32_t* topk_out,
+                       sgqa_bf16* out, void* ws, size_t ws_bytes, sgqa_stream stream) {
+  if (!seq_lens) return SGQA_ERR_NULL;
+  return decode_impl(p, q, k_cache, v_cache, pages, blk_k, idx_q, idx_w, seq_lens, topk_out, out, ws, ws_bytes,
+                     stream);
+}
+
+int sgqa_append(const sgqa_params* p, const sgqa_bf16* k_new, const sgqa_bf16* v_new, const sgqa_bf16* idx_k_new,
+                const int32_t* positions, sgqa_bf16* k_cache, sgqa_bf16* v_cache, const sgqa_pages* pages,
+                sgqa_bf16* idx_k_cache, sgqa_bf16* blk_k, sgqa_stream stream) {
+  int st = check_params(p, NEED_INDEX, false);
+  if (st) return st;
+  if (p->head_dim != 128 || p->n_kv_heads < 1) return SGQA_ERR_SHAPE;
+  if (!k_new || !v_new || !idx_k_new || !positions || !k_cache || !v_cache || !idx_k_cache ||
+      (!blk_k && p->n_tokens >= p->block))
+    return SGQA_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(idx_k_new) || !aligned16(positions) ||
+      !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(idx_k_cache) || !aligned16(blk_k))
+    return SGQA_ERR_ALIGN;
+  PageTable pt;
+  st = check_pages(p, pages, &pt);
+  if (st) return st;
+  if (!device_ok()) return SGQA_ERR_DEVICE;
+  return status_of(launch_append(k_new, v_new, idx_k_new, positions, k_cache, v_cache, pt, idx_k_cache, blk_k,
+                                 p->n_seqs, p->n_tokens, p->n_kv_heads, p->idx_dim, p->block, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -9,6 +9,23 @@
 
 namespace sgqa {
 
+// A paged K/V cache: pools [n_pages][G][page_tokens][D], position t of sequence s in pool page
+// table[s * max_pages + t / page_tokens] (page_tokens a power of two, a multiple of B). table ==
+// nullptr means dense per-sequence caches [S][G][capacity][D].
+struct PageTable {
+  const int32_t* table = nullptr;
+  int max_pages = 0;
+  int page_tokens = 0;
+  int n_pages = 0;
+};
+
+// Append one token per sequence to the decode caches (see sgqa_append): K/V at position pos[s]
+// (dense or paged), the index key into idx_cache [S][cap][d_I], and the block key into
+// kbar [S][cap/B][d_I] when the token completes its block. pos[s] outside [0, cap) skips s.
+hipError_t launch_append(const uint16_t* k_new, const uint16_t* v_new, const uint16_t* idx_new, const int32_t* pos,
+                         uint16_t* kc, uint16_t* vc, const PageTable& pages, uint16_t* idx_cache, uint16_t* kbar,
+                         int n_seqs, int cap, int n_groups, int idx_dim, int block, hipStream_t stream);
+
 // Block compression: ki [S][N][dI] -> kbar [S][N/B][dI].
 hipError_t launch_compress(const uint16_t* ki, uint16_t* kbar, int n_seqs, int n_tokens, int idx_dim, int block,
                            hipStream_t stream);
@@ -27,17 +44,18 @@ hipError_t launch_attend(const uint16_t* q, const uint16_t* k, const uint16_t* v
                          int tile, float scale, hipStream_t stream);
 
 // Decode selection: K-bar cache [S][L/B][64], qi [S][G][4][64] -> sel [S][G][kb] (and topk_out if not
-// null). Uses decode_select_ws_bytes() of workspace.
+// null). lens (device, nullable): per-sequence context lengths (clamped to [1, n_tokens]); null =
+// n_tokens for every sequence. Uses decode_select_ws_bytes() of workspace.
 size_t decode_select_ws_bytes(int n_seqs, int n_tokens, int n_groups, int block, int kb);
 hipError_t launch_decode_select(const uint16_t* qi, const float* w, const uint16_t* kbar, int32_t* sel,
                                 int32_t* topk_out, void* ws, int n_seqs, int n_tokens, int n_groups, int block, int kb,
-                                hipStream_t stream);
+                                const int32_t* lens, hipStream_t stream);
 
 // Decode attention over Sel + own block, one workgroup per (sequence, group), straight into
 // out [S][Hq][D] (no workspace).
 hipError_t launch_decode_attend(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, const int32_t* sel,
-                                uint16_t* out, int n_seqs, int ctx, int n_q_heads, int n_groups,
-                                int block, int kb, float scale, hipStream_t stream);
+                                uint16_t* out, int n_seqs, int ctx, int n_q_heads, int n_groups, int block, int kb,
+                                float scale, const int32_t* lens, const PageTable& pages, hipStream_t stream);
 
 // LDS a launch needs (validation rejects shapes that do not fit before anything is enqueued).
 size_t index_topk_lds_min(int kb);

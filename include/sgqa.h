@@ -172,6 +172,60 @@ int sgqa_decode(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k_cac
                 const float* idx_w, int32_t* topk_out, sgqa_bf16* out, void* ws, size_t ws_bytes,
                 sgqa_stream stream);
 
+/* ---------------------------------------------------------------- incremental / varlen decode
+ * The decode call above takes one context length L = n_tokens for every sequence and dense caches.
+ * A serving loop needs per-sequence lengths, caches that grow one token per step, and paged K/V
+ * storage. The method is unchanged: the selection of sequence s runs at its own last position
+ * L_s - 1 over its blocks b < floor((L_s - 1)/B), exactly as in sgqa_decode.
+ */
+
+/* Paged K/V cache. The pools hold pages of `page_tokens` consecutive positions of one sequence for
+ * every group: pool layout [n_pages][G][page_tokens][D] bf16. Position t of sequence s lives in pool
+ * page table[s * max_pages + t / page_tokens]. page_tokens must be a power of two and a multiple of
+ * B (a block never straddles two pages); max_pages * page_tokens >= p->n_tokens (the capacity).
+ * table is DEVICE memory [S][max_pages] int32. The table entries of positions < L_s must lie in
+ * [0, n_pages): the kernels clamp other values, so a bad table yields wrong results but never an
+ * access outside the pools (sgqa_append skips the K/V write of a token whose entry is out of range). */
+typedef struct sgqa_pages {
+  const int32_t* table;
+  int32_t max_pages;
+  int32_t page_tokens;
+  int32_t n_pages;
+} sgqa_pages;
+
+/* Decode with per-sequence context lengths ("Inside Step 5 Preview", Sparse GQA, Figure 3 and the
+ * paragraph "Reducing indexer's cost": the same selection and attended set as sgqa_decode, each
+ * sequence at its own last position).
+ *   p->n_tokens   capacity C of the per-sequence caches (positions 0 .. C-1)
+ *   seq_lens      [S] int32 DEVICE: L_s, the context length of sequence s including its query
+ *                 token, 1 <= L_s <= C (values outside are clamped into [1, C])
+ *   k_cache, v_cache  pages == NULL: dense [S][G][C][D]; else the pools described by *pages
+ *   blk_k         [S][floor(C/B)][d_I]: block keys of the complete blocks of every sequence (from
+ *                 sgqa_compress or sgqa_append); blocks at or past floor((L_s-1)/B) are not read
+ *   q, idx_q, idx_w, topk_out, out   as in sgqa_decode
+ * Workspace: sgqa_workspace_size(p, SGQA_OP_DECODE). With every L_s = C and dense caches the result
+ * is bit-identical to sgqa_decode. */
+int sgqa_decode_varlen(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k_cache,
+                       const sgqa_bf16* v_cache, const sgqa_pages* pages, const sgqa_bf16* blk_k,
+                       const sgqa_bf16* idx_q, const float* idx_w, const int32_t* seq_lens, int32_t* topk_out,
+                       sgqa_bf16* out, void* ws, size_t ws_bytes, sgqa_stream stream);
+
+/* Append one token to every sequence's caches (the cache side of incremental decode; block keys as
+ * in sgqa_compress, "Reducing indexer's cost").
+ *   positions     [S] int32 DEVICE: position j_s of the new token of sequence s (usually its old
+ *                 length); sequences with j_s outside [0, p->n_tokens) are left untouched
+ *   k_new, v_new  [S][G][D] bf16: the token's K and V rows -> k_cache / v_cache at position j_s
+ *                 (dense [S][G][C][D], or the page of *pages)
+ *   idx_k_new     [S][d_I] bf16: the token's shared index key -> idx_k_cache [S][C][d_I]
+ *   blk_k         [S][floor(C/B)][d_I]: when j_s % B == B-1 the new token completes block j_s / B,
+ *                 and its block key is written with the arithmetic of sgqa_compress (bit-identical)
+ * Uses p->n_seqs, n_tokens (= C), n_kv_heads, head_dim, idx_dim, block. No workspace. The previous
+ * B-1 index keys of a completing block must already be in idx_k_cache (earlier calls or a prefill
+ * copy on the same stream). */
+int sgqa_append(const sgqa_params* p, const sgqa_bf16* k_new, const sgqa_bf16* v_new, const sgqa_bf16* idx_k_new,
+                const int32_t* positions, sgqa_bf16* k_cache, sgqa_bf16* v_cache, const sgqa_pages* pages,
+                sgqa_bf16* idx_k_cache, sgqa_bf16* blk_k, sgqa_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

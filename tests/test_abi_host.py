@@ -119,3 +119,39 @@ def test_binding_refuses_host_tensors(sg):
     ki = torch.zeros((64, 64), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         sg.sgqa_compress(p, ki, torch.zeros((8, 64), dtype=torch.bfloat16))
+
+
+def test_varlen_decode_and_append_validation(sg):
+    lib = sg.lib()
+    nul = ctypes.c_void_p(0)
+    buf = (ctypes.c_uint8 * 64)()
+    a = ctypes.c_void_p((ctypes.addressof(buf) + 15) // 16 * 16)
+    d = _p(n_tokens=4096, n_seqs=4, union_tile=1)
+    dp = ctypes.byref(d.c())
+    # seq_lens is required by the varlen call
+    assert lib.sgqa_decode_varlen(dp, a, a, a, None, a, a, a, nul, nul, a, a, 1 << 40, nul) == sg.SGQA_ERR_NULL
+
+    def pages(table, max_pages, page_tokens, n_pages):
+        return ctypes.byref(sg.sgqa_pages(table.value, max_pages, page_tokens, n_pages))
+
+    def varlen(pg):
+        return lib.sgqa_decode_varlen(dp, a, a, a, pg, a, a, a, a, nul, a, a, 1 << 40, nul)
+
+    assert varlen(pages(nul, 64, 64, 100)) == sg.SGQA_ERR_NULL                 # no table
+    assert varlen(pages(a, 64, 48, 100)) == sg.SGQA_ERR_SHAPE                  # page not a power of two
+    assert varlen(pages(a, 64, 4, 100)) == sg.SGQA_ERR_SHAPE                   # page smaller than B = 8
+    assert varlen(pages(a, 63, 64, 100)) == sg.SGQA_ERR_SHAPE                  # max_pages * page < capacity
+    assert varlen(pages(a, 64, 64, 0)) == sg.SGQA_ERR_SHAPE                    # empty pool
+    # a valid descriptor gets as far as the workspace check
+    assert lib.sgqa_decode_varlen(dp, a, a, a, pages(a, 64, 64, 100), a, a, a, a, nul, a, a, 16, nul) \
+        == sg.SGQA_ERR_WORKSPACE
+
+    def append(pg, pos=a, idx_cache=a):
+        return lib.sgqa_append(dp, a, a, a, pos, a, a, pg, idx_cache, a, nul)
+
+    assert append(None, pos=nul) == sg.SGQA_ERR_NULL
+    assert append(None, idx_cache=nul) == sg.SGQA_ERR_NULL
+    assert append(None, pos=ctypes.c_void_p(a.value + 4)) == sg.SGQA_ERR_ALIGN
+    assert append(pages(a, 64, 12, 100)) == sg.SGQA_ERR_SHAPE
+    bad_dim = _p(n_tokens=4096, n_seqs=4, union_tile=1, head_dim=64)
+    assert lib.sgqa_append(ctypes.byref(bad_dim.c()), a, a, a, a, a, a, None, a, a, nul) == sg.SGQA_ERR_SHAPE
