@@ -211,6 +211,7 @@ def bench_decode(sg, datagen, torch, steps, warmup):
     qo_bytes = 2 * p.n_seqs * p.n_q_heads * p.head_dim * 2
     step_bytes = gather_bytes + index_bytes + qo_bytes
     cache_build_bytes = p.n_seqs * p.n_tokens * p.idx_dim * 2 * (1 + 1 / p.block)
+    varlen = bench_decode_varlen(sg, torch, p, y, blk, out, ws, steps, warmup)
     del y
     return {
         "metric": "decode tok/s",
@@ -224,6 +225,7 @@ def bench_decode(sg, datagen, torch, steps, warmup):
                      "traffic": None, "algorithmic_bytes_per_step": step_bytes},
         "cache_compress": {"ms": compress_ms, "bytes": cache_build_bytes,
                            "GB_per_s": cache_build_bytes / (compress_ms / 1e3) / 1e9},
+        "varlen": varlen,
     }
 
 
@@ -329,6 +331,73 @@ def achieved_peaks(torch):
     res = {"copy_GB_per_s": 2 * a.numel() * 2 / copy_s / 1e9, "spec_hbm_GB_per_s": PEAK_HBM_GBS,
            "gemm_bf16_TFLOP_per_s": 2.0 * 8192 ** 3 / gemm_s / 1e12, "spec_bf16_TFLOP_per_s": PEAK_BF16_TFLOPS}
     del a, b, m, n
+    torch.cuda.empty_cache()
+    return res
+
+
+def decode_step_bytes(p, lens) -> int:
+    """Algorithmic bytes of one decode step at per-sequence lengths: the block keys of every candidate,
+    the K/V rows of Sel + own block, q in and out."""
+    total = 0
+    for L in lens:
+        c = (L - 1) // p.block
+        kb = min(p.kb, c)
+        own = L - (L - 1) // p.block * p.block
+        total += c * p.idx_dim * 2 + p.n_kv_heads * (kb * p.block + own) * p.head_dim * 2 * 2
+    return total + 2 * len(lens) * p.n_q_heads * p.head_dim * 2
+
+
+def bench_decode_varlen(sg, torch, p, y, blk, out, ws, steps, warmup):
+    """Incremental-decode calls on the decode workload's shapes: varlen decode with sequence lengths
+    drawn uniformly from [L/2, L] (seeded), on the dense caches and on a paged pool (64-token pages,
+    shuffled page table), and one sgqa_append of a token per sequence."""
+    S, C = p.n_seqs, p.n_tokens
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20261202)
+    lens = torch.randint(C // 2, C + 1, (S,), generator=g, device="cuda", dtype=torch.int32)
+    lens_l = [int(v) for v in lens.cpu()]
+    bytes_step = decode_step_bytes(p, lens_l)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    res = {"lens": "uniform in [L/2, L], seeded", "mean_len": sum(lens_l) / S}
+    ms = timed(lambda: sg.sgqa_decode_varlen(p, y["q"], y["k_cache"], y["v_cache"], blk, y["qi"], y["w"], lens, out, ws))
+    res["dense"] = {"ms_per_step": ms, "tokens_per_s": S / (ms / 1e3),
+                    "GB_per_s": bytes_step / (ms / 1e3) / 1e9, "hbm_frac": bytes_step / (ms / 1e3) / 1e9 / PEAK_HBM_GBS}
+    # Paged pool: its own data (the throughput does not depend on the values).
+    pt = 64
+    per = C // pt
+    n_pages = S * per
+    pool_shape = (n_pages, p.n_kv_heads, pt, p.head_dim)
+    kpool = torch.empty(pool_shape, dtype=torch.bfloat16, device="cuda").normal_(generator=g)
+    vpool = torch.empty(pool_shape, dtype=torch.bfloat16, device="cuda").normal_(generator=g)
+    table = torch.randperm(n_pages, generator=g, device="cuda").to(torch.int32).view(S, per)
+    pages = sg.Pages(table, pt, n_pages)
+    ms = timed(lambda: sg.sgqa_decode_varlen(p, y["q"], kpool, vpool, blk, y["qi"], y["w"], lens, out, ws,
+                                             pages=pages))
+    res["paged_64"] = {"ms_per_step": ms, "tokens_per_s": S / (ms / 1e3),
+                       "GB_per_s": bytes_step / (ms / 1e3) / 1e9,
+                       "hbm_frac": bytes_step / (ms / 1e3) / 1e9 / PEAK_HBM_GBS}
+    # Append of one token per sequence into the paged pool (positions = lens - 1, in place).
+    idx_cache = y["ki_cache"]
+    k_new = torch.empty((S, p.n_kv_heads, p.head_dim), dtype=torch.bfloat16, device="cuda").normal_(generator=g)
+    i_new = y["ki_cache"][:, 0].contiguous()
+    pos = lens - 1
+    ms = timed(lambda: sg.sgqa_append(p, k_new, k_new, i_new, pos, kpool, vpool, idx_cache, blk, pages=pages))
+    res["append_ms"] = ms
+    res["step_bytes"] = bytes_step
+    del kpool, vpool
     torch.cuda.empty_cache()
     return res
 

@@ -569,17 +569,17 @@ constexpr int kDecVStage = kVTileBytes + kKeys * 4;  // decode: V tile + token t
 
 // Decode gather of one wave: the V tile of one chunk (16 wave-wide global_load_lds, layout as in
 // chunk_issue) and its token table.
-template <typename TokFn, typename RowFn>
-__device__ __forceinline__ void v_issue_wave(uint8_t* vst, RowFn row_of, TokFn tok_of) {
+// off_of(key) is the element offset (from `base`) of the row of key `key` of the chunk.
+template <typename TokFn, typename OffFn>
+__device__ __forceinline__ void v_issue_wave(uint8_t* vst, const uint16_t* base, OffFn off_of, TokFn tok_of) {
   const int l = lane_id();
 #pragma unroll
   for (int ti = 0; ti < kVTileInsts; ++ti) {
     const int slot = ti * 64 + l;
     const int row = slot >> 4;
     const int piece = v_phys(row, slot & 15);
-    int tkn = tok_of(row);
-    if (tkn < 0) tkn = 0;
-    __builtin_amdgcn_global_load_lds((const void*)(row_of(tkn) + piece * 8), (lds_void*)(vst + ti * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(base + off_of(row) + piece * 8), (lds_void*)(vst + ti * 1024), 16,
+                                     0, 0);
   }
   const int t = tok_of(l);
   reinterpret_cast<int*>(vst + kVTileBytes)[l] = t >= 0 ? t : 0x7FFFFFFF;
@@ -588,14 +588,12 @@ __device__ __forceinline__ void v_issue_wave(uint8_t* vst, RowFn row_of, TokFn t
 // The K operands of one chunk straight from global memory into registers: the A operand of
 // S^T = K Q^T for key tile kt and step ks is key row 32 kt + (l % 32), elements 16 ks + 8 (l / 32)
 // .. +7, i.e. 16 contiguous bytes of one cached key.
-template <typename TokFn, typename RowFn>
-__device__ __forceinline__ void k_load_regs(bf16x8 (&kreg)[16], RowFn row_of, TokFn tok_of) {
+template <typename OffFn>
+__device__ __forceinline__ void k_load_regs(bf16x8 (&kreg)[16], const uint16_t* base, OffFn off_of) {
   const int l = lane_id();
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
-    int tkn = tok_of(32 * kt + (l & 31));
-    if (tkn < 0) tkn = 0;
-    const uint16_t* src = row_of(tkn) + 8 * (l >> 5);
+    const uint16_t* src = base + off_of(32 * kt + (l & 31)) + 8 * (l >> 5);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) kreg[ks * 2 + kt] = *reinterpret_cast<const bf16x8*>(src + 16 * ks);
   }
@@ -628,6 +626,7 @@ __global__ __launch_bounds__(256) void k_decode_attend(const uint16_t* __restric
   const int wave = threadIdx.x >> 6;
   uint8_t* vbuf[2] = {smem + wave * 2 * kDecVStage, smem + wave * 2 * kDecVStage + kDecVStage};
   int* blocks = reinterpret_cast<int*>(smem + kWavesD * 2 * kDecVStage);  // kb + 1 entries
+  int* prow = blocks + (kb + 1);  // paged: pool row of each entry's first token (kb + 1 entries)
   __shared__ int n_sel_shared;
 
   const int s = blockIdx.x / n_groups, g = blockIdx.x % n_groups;
@@ -647,7 +646,16 @@ __global__ __launch_bounds__(256) void k_decode_attend(const uint16_t* __restric
   }
   __syncthreads();
   const int n_sel = n_sel_shared;
-  for (int e = threadIdx.x; e <= n_sel; e += blockDim.x) blocks[e] = e < n_sel ? srow[e] : own;
+  for (int e = threadIdx.x; e <= n_sel; e += blockDim.x) {
+    const int b = e < n_sel ? srow[e] : own;
+    blocks[e] = b;
+    if (PAGED) {  // a block lies inside one page (the page size is a multiple of B)
+      const int tb = b << block_shift;
+      int pg = table[(long long)s * max_pages + (tb >> page_shift)];
+      pg = pg < 0 ? 0 : (pg >= n_pages ? n_pages - 1 : pg);
+      prow[e] = ((pg * n_groups + g) << page_shift) + (tb & ((1 << page_shift) - 1));
+    }
+  }
   __syncthreads();
 
   bf16x8 qreg[1][8];
@@ -669,18 +677,19 @@ __global__ __launch_bounds__(256) void k_decode_attend(const uint16_t* __restric
   }
   AttnState<1> st;
   state_init(st);
-  // Row of token t (of this sequence and group) in the K and V caches, as an element offset.
-  const int32_t* ptab = PAGED ? table + (long long)s * max_pages : nullptr;
   const long long seq_off = PAGED ? 0 : ((long long)s * n_groups + g) * cap * kD;
-  auto row_off = [&](int t) -> long long {
-    if (!PAGED) return seq_off + (long long)t * kD;
-    int pg = ptab[t >> page_shift];
-    pg = pg < 0 ? 0 : (pg >= n_pages ? n_pages - 1 : pg);
-    return ((((long long)pg * n_groups + g) << page_shift) + (t & ((1 << page_shift) - 1))) * kD;
-  };
-  auto krow = [&](int t) -> const uint16_t* { return kc + row_off(t); };
-  auto vrow = [&](int t) -> const uint16_t* { return vc + row_off(t); };
   const int n_keys = (n_sel + 1) * block;
+  // Element offset of the cache row of key `key` of chunk c (keys past the list read a valid row;
+  // the token table masks them).
+  auto off_in = [&](int c) {
+    return [&, c](int key) -> long long {
+      const int kp = c * kKeys + key;
+      if (kp >= n_keys) return seq_off;
+      const int e = kp >> block_shift, j = kp & (block - 1);
+      if (PAGED) return ((long long)prow[e] + j) * kD;
+      return seq_off + (long long)((blocks[e] << block_shift) + j) * kD;
+    };
+  };
   const int n_chunks = (n_keys + kKeys - 1) / kKeys;
   const LaneOffsets lo = lane_offsets(0);
   auto tok_in = [&](int c) {
@@ -693,14 +702,14 @@ __global__ __launch_bounds__(256) void k_decode_attend(const uint16_t* __restric
   };
   bf16x8 kreg[16];
   if (wave < n_chunks) {
-    v_issue_wave(vbuf[0], vrow, tok_in(wave));
-    k_load_regs(kreg, krow, tok_in(wave));
+    v_issue_wave(vbuf[0], vc, off_in(wave), tok_in(wave));
+    k_load_regs(kreg, kc, off_in(wave));
   }
   int i = 0;
   for (int c = wave; c < n_chunks; c += kWavesD, ++i) {
     const int cn = c + kWavesD;
     if (cn < n_chunks) {
-      v_issue_wave(vbuf[(i + 1) & 1], vrow, tok_in(cn));
+      v_issue_wave(vbuf[(i + 1) & 1], vc, off_in(cn), tok_in(cn));
       asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // V and K of chunk c landed; V of cn flies
     } else {
       wait_vm();
@@ -709,7 +718,7 @@ __global__ __launch_bounds__(256) void k_decode_attend(const uint16_t* __restric
     // Only the last chunk holds the own block (and the padding past the list): the Sel blocks are
     // all below it, hence visible to the query.
     attn_chunk<1, 2, true>(vbuf[i & 1], lo, qreg, st, scale_log2, c == n_chunks - 1, row_pos, kreg, [&]() {
-      if (cn < n_chunks) k_load_regs(kreg, krow, tok_in(cn));
+      if (cn < n_chunks) k_load_regs(kreg, kc, off_in(cn));
     });
   }
 
@@ -717,7 +726,7 @@ __global__ __launch_bounds__(256) void k_decode_attend(const uint16_t* __restric
   // combine r x 128 outputs.
   const float l_all = st.l[0] + __shfl_xor(st.l[0], 32, 64);
   float* o_lds = reinterpret_cast<float*>(vbuf[0]);  // [32 rows][128]
-  float* ml_lds = reinterpret_cast<float*>(blocks) + (kb + 1);  // [4][32][2]
+  float* ml_lds = reinterpret_cast<float*>(blocks) + 2 * (kb + 1);  // [4][32][2]
   __syncthreads();  // every wave is done with its buffers
   {
     const int row = l & 31;
@@ -748,7 +757,9 @@ __global__ __launch_bounds__(256) void k_decode_attend(const uint16_t* __restric
   }
 }
 
-size_t decode_attend_lds(int kb) { return (size_t)4 * 2 * kDecVStage + (size_t)(kb + 1) * 4 + 4 * 32 * 2 * 4; }
+// Four waves' double-buffered V stages, the entry list and the paged rows (2 x (kb + 1) ints), and the
+// merge's (max, sum) pairs.
+size_t decode_attend_lds(int kb) { return (size_t)4 * 2 * kDecVStage + (size_t)2 * (kb + 1) * 4 + 4 * 32 * 2 * 4; }
 
 hipError_t launch_decode_attend(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, const int32_t* sel,
                                 uint16_t* out, int n_seqs, int ctx, int n_q_heads, int n_groups, int block, int kb,

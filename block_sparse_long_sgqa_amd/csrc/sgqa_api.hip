@@ -293,6 +293,7 @@ int check_pages(const sgqa_params* p, const sgqa_pages* pg, PageTable* out) {
   const int pt = pg->page_tokens;
   if (pt < p->block || (pt & (pt - 1)) != 0) return SGQA_ERR_SHAPE;
   if (pg->max_pages < 1 || (long long)pg->max_pages * pt < p->n_tokens || pg->n_pages < 1) return SGQA_ERR_SHAPE;
+  if ((long long)pg->n_pages * p->n_kv_heads * pt > 0x7FFFFFFFLL) return SGQA_ERR_SHAPE;  // pool rows index in int32
   out->table = pg->table;
   out->max_pages = pg->max_pages;
   out->page_tokens = pt;

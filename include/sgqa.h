@@ -182,8 +182,8 @@ int sgqa_decode(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k_cac
 /* Paged K/V cache. The pools hold pages of `page_tokens` consecutive positions of one sequence for
  * every group: pool layout [n_pages][G][page_tokens][D] bf16. Position t of sequence s lives in pool
  * page table[s * max_pages + t / page_tokens]. page_tokens must be a power of two and a multiple of
- * B (a block never straddles two pages); max_pages * page_tokens >= p->n_tokens (the capacity).
- * table is DEVICE memory [S][max_pages] int32. The table entries of positions < L_s must lie in
+ * B (a block never straddles two pages); max_pages * page_tokens >= p->n_tokens (the capacity);
+ * n_pages * G * page_tokens < 2^31 (pool rows are indexed in 32 bits). table is DEVICE memory [S][max_pages] int32. The table entries of positions < L_s must lie in
  * [0, n_pages): the kernels clamp other values, so a bad table yields wrong results but never an
  * access outside the pools (sgqa_append skips the K/V write of a token whose entry is out of range). */
 typedef struct sgqa_pages {
