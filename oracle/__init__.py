@@ -52,6 +52,10 @@ def _load():
         lib.orc_attend.restype = None
         lib.orc_decode.argtypes = [I, I, I, I, I, I, I, I, I, D, P, P, P, P, P, P, I, P, P, P]
         lib.orc_decode.restype = None
+        lib.orc_decode_f8.argtypes = [I, I, I, I, I, I, I, I, I, D, P, P, P, P, P, P, P, I, P, P, P]
+        lib.orc_decode_f8.restype = None
+        lib.orc_fp8_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+        lib.orc_fp8_e4m3_to_f64.restype = ctypes.c_double
         lib.orc_coverage.argtypes = [I, I, I, I, I, P, P, I]
         lib.orc_coverage.restype = D
         _lib = lib
@@ -73,6 +77,21 @@ def _u16(a) -> np.ndarray:
         a = a.view(np.uint16)
     if a.dtype != np.uint16:
         raise TypeError(f"expected uint16 bf16 bits, got {a.dtype}")
+    return a
+
+
+def _u8(a) -> np.ndarray:
+    """Host uint8 codes of an FP8 array (numpy uint8, or a torch uint8 / float8 tensor)."""
+    if hasattr(a, "detach"):
+        import torch
+
+        a = a.detach().cpu().contiguous()
+        if a.dtype != torch.uint8:
+            a = a.view(torch.uint8)
+        a = a.numpy()
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint8:
+        raise TypeError(f"expected uint8 FP8 codes, got {a.dtype}")
     return a
 
 
@@ -209,6 +228,36 @@ def decode(q, k_cache, v_cache, kbar, qi, w, block: int, kb: int, scale: float =
     out = np.empty((n, Hq, D), dtype=np.float64)
     _load().orc_decode(S, L, Hq, G, D, HI, dI, block, kb, float(scale), _p(q), _p(k_cache), _p(v_cache),
                        _p(kbar), _p(qi), _p(w), n, sp, _p(topk), _p(out))
+    return topk, out
+
+
+def fp8_e4m3_to_f64(code: int) -> float:
+    """Value of one OCP FP8 E4M3 code (0..255)."""
+    return float(_load().orc_fp8_e4m3_to_f64(int(code)))
+
+
+def decode_fp8(q, k8, v8, kv_scale, kbar, qi, w, block: int, kb: int, scale: float = 0.0, seqs=None):
+    """decode() with FP8 E4M3 K/V caches k8, v8 [S][G][L][D] (uint8 codes) and kv_scale [S][G][2] fp32
+    (key scale, value scale): the attended rows are code value * scale."""
+    q = _u16(q)
+    k8 = _u8(k8)
+    v8 = _u8(v8)
+    kv_scale = _f32(kv_scale)
+    kbar = _u16(kbar)
+    qi = _u16(qi)
+    w = _f32(w)
+    S, Hq, D = q.shape
+    _, G, L, _ = k8.shape
+    HI, dI = qi.shape[2], qi.shape[3]
+    if seqs is None:
+        n, sp = S, None
+    else:
+        seqs = _i32(seqs)
+        n, sp = int(seqs.shape[0]), _p(seqs)
+    topk = np.empty((n, G, kb), dtype=np.int32)
+    out = np.empty((n, Hq, D), dtype=np.float64)
+    _load().orc_decode_f8(S, L, Hq, G, D, HI, dI, block, kb, float(scale), _p(q), _p(k8), _p(v8), _p(kv_scale),
+                          _p(kbar), _p(qi), _p(w), n, sp, _p(topk), _p(out))
     return topk, out
 
 

@@ -13,6 +13,7 @@
  *                block size"                      -> k tokens = k/B blocks; token coverage (orc_coverage)
  *     Figure 3 caption                            -> shared index keys, per-KV-group selection, own
  *                                                    block read causally (orc_attend, orc_decode)
+ *     the pages' FP8 KV cache (deployment notes)  -> orc_fp8_e4m3_to_f64, orc_decode_f8
  *
  * The pages do not fix the indexer's form. The reading used here (and by the library) is:
  *   block key   kbar[b] = bf16_rne(mean of the B index keys of block b)       (complete blocks only)
@@ -291,6 +292,94 @@ void orc_decode(int S, int L, int Hq, int G, int D, int HI, int dI, int B, int K
         int h = g * r + hh;
         orc_attend_list(D, scale, q + ((size_t)s * Hq + h) * D, kb, vb, toks, nt, logit,
                         out + ((size_t)x * Hq + h) * D);
+      }
+      free(toks);
+      free(logit);
+      free(sc);
+      free(sel);
+    }
+  }
+}
+
+/* ---------------------------------------------------------------- FP8 K/V decode -------------- */
+
+/* OCP FP8 E4M3 ("e4m3fn"), the storage format of the FP8 K/V cache: 1 sign bit, 4 exponent bits
+ * (bias 7), 3 mantissa bits; exponent field 0 encodes subnormals m * 2^-9; there are no infinities
+ * and S.1111.111 is NaN. Written from the format's definition. */
+double orc_fp8_e4m3_to_f64(uint8_t b) {
+  int sgn = (b >> 7) & 1, e = (b >> 3) & 15, m = b & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m, -9);
+  else
+    v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return sgn ? -v : v;
+}
+
+/* orc_attend_list for a cache row in FP8: element d of key row t is k8[t][d] * ks (and of the value
+ * row v8[t][d] * vs). Same definition, same order of operations. */
+static void orc_attend_list_f8(int D, double scale, const uint16_t* qv, const uint8_t* kbase, double ks,
+                               const uint8_t* vbase, double vs, const int32_t* toks, int nt, double* logit,
+                               double* out) {
+  double mx = -INFINITY;
+  for (int x = 0; x < nt; ++x) {
+    const uint8_t* kr = kbase + (size_t)toks[x] * D;
+    double dot = 0.0;
+    for (int d = 0; d < D; ++d) dot += orc_bf16_to_f64(qv[d]) * (orc_fp8_e4m3_to_f64(kr[d]) * ks);
+    logit[x] = scale * dot;
+    if (logit[x] > mx) mx = logit[x];
+  }
+  double den = 0.0;
+  for (int x = 0; x < nt; ++x) {
+    logit[x] = exp(logit[x] - mx);
+    den += logit[x];
+  }
+  for (int d = 0; d < D; ++d) out[d] = 0.0;
+  for (int x = 0; x < nt; ++x) {
+    const uint8_t* vr = vbase + (size_t)toks[x] * D;
+    double p = logit[x] / den;
+    for (int d = 0; d < D; ++d) out[d] += p * (orc_fp8_e4m3_to_f64(vr[d]) * vs);
+  }
+}
+
+/* orc_decode with FP8 K/V caches k8, v8 [S][G][L][D] and one scale per (sequence, group) for each:
+ * kv_scale [S][G][2] = (key scale, value scale). Selection is unchanged (it reads only the bf16
+ * index keys); the attended rows are the dequantized K/V. */
+void orc_decode_f8(int S, int L, int Hq, int G, int D, int HI, int dI, int B, int KB, double scale,
+                   const uint16_t* q, const uint8_t* kc, const uint8_t* vc, const float* kv_scale,
+                   const uint16_t* kbar, const uint16_t* qi, const float* w, int nseq, const int32_t* seqs,
+                   int32_t* topk_out, double* out) {
+  int r = Hq / G;
+  int NB = L / B;
+  int i = L - 1;
+  (void)S;
+  int c = i / B;
+  if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  for (int x = 0; x < nseq; ++x) {
+    for (int g = 0; g < G; ++g) {
+      int s = seqs ? seqs[x] : x;
+      double* sc = (double*)malloc(sizeof(double) * (size_t)(c > 0 ? c : 1));
+      int32_t* sel = (int32_t*)malloc(sizeof(int32_t) * (size_t)KB);
+      orc_block_scores(HI, dI, qi + ((size_t)s * G + g) * HI * dI, w + (size_t)g * HI,
+                       kbar + (size_t)s * NB * dI, c, sc);
+      orc_select(c, sc, KB, sel);
+      if (topk_out) memcpy(topk_out + ((size_t)x * G + g) * KB, sel, sizeof(int32_t) * (size_t)KB);
+      int32_t* toks = (int32_t*)malloc(sizeof(int32_t) * (size_t)(KB * B + B));
+      double* logit = (double*)malloc(sizeof(double) * (size_t)(KB * B + B));
+      int nt = 0;
+      for (int e = 0; e < KB && sel[e] >= 0; ++e)
+        for (int j = 0; j < B; ++j) toks[nt++] = sel[e] * B + j;
+      for (int j = c * B; j <= i; ++j) toks[nt++] = j;
+      const uint8_t* kb = kc + ((size_t)s * G + g) * (size_t)L * D;
+      const uint8_t* vb = vc + ((size_t)s * G + g) * (size_t)L * D;
+      double ks = kv_scale[((size_t)s * G + g) * 2 + 0];
+      double vs = kv_scale[((size_t)s * G + g) * 2 + 1];
+      for (int hh = 0; hh < r; ++hh) {
+        int h = g * r + hh;
+        orc_attend_list_f8(D, scale, q + ((size_t)s * Hq + h) * D, kb, ks, vb, vs, toks, nt, logit,
+                           out + ((size_t)x * Hq + h) * D);
       }
       free(toks);
       free(logit);

@@ -364,3 +364,56 @@ def test_coverage_brute_force_and_dense_case(orc):
     d1 = orc.index_topk(qi, w, orc.compress(ki, 1), 1, 256)
     d8 = orc.index_topk(qi, w, orc.compress(ki, 8), 8, 32)
     assert orc.coverage(d1, d8, 8) == 1.0
+
+
+# ------------------------------------------------------------------------------------ FP8 K/V decode
+
+def test_fp8_e4m3_codes(orc):
+    # Hand values from the format's definition, then all 256 codes against torch's float8_e4m3fn.
+    assert orc.fp8_e4m3_to_f64(0x38) == 1.0
+    assert orc.fp8_e4m3_to_f64(0x7E) == 448.0
+    assert orc.fp8_e4m3_to_f64(0x01) == 2.0 ** -9
+    assert orc.fp8_e4m3_to_f64(0x08) == 2.0 ** -6
+    assert orc.fp8_e4m3_to_f64(0xC4) == -3.0
+    z = orc.fp8_e4m3_to_f64(0x80)
+    assert z == 0.0 and np.signbit(z)
+    assert np.isnan(orc.fp8_e4m3_to_f64(0x7F)) and np.isnan(orc.fp8_e4m3_to_f64(0xFF))
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    got = np.array([orc.fp8_e4m3_to_f64(c) for c in range(256)])
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(got[ok], ref[ok])
+
+
+def _fp8_exact_case(seed=11):
+    """Small decode inputs whose K/V are FP8 codes; returns codes and their bf16 image (exact)."""
+    wl = datagen.DECODE.replace(name="orc_fp8", n_tokens=300, n_seqs=2, n_q_heads=16, n_kv_heads=2,
+                                topk_tokens=64, block=8)
+    x = datagen.decode_inputs(wl)
+    g = torch.Generator().manual_seed(seed)
+    # codes with exponent fields 1..13 (normal, |v| <= 240): exactly representable in bf16
+    def codes(shape):
+        e = torch.randint(1, 14, shape, generator=g)
+        m = torch.randint(0, 8, shape, generator=g)
+        sg = torch.randint(0, 2, shape, generator=g)
+        return (sg * 128 + e * 8 + m).to(torch.uint8)
+    k8 = codes(x["k_cache"].shape)
+    v8 = codes(x["v_cache"].shape)
+    return wl, x, k8, v8
+
+
+def test_decode_fp8_reduces_to_bf16_decode(orc):
+    # Power-of-two scales keep code * scale exact in bf16, so orc_decode_f8 must equal orc_decode on
+    # the dequantized caches. Different key and value scales catch a swapped scale.
+    wl, x, k8, v8 = _fp8_exact_case()
+    S, G = wl.n_seqs, wl.n_kv_heads
+    kv_scale = torch.tensor([[[0.5, 4.0], [2.0, 0.25]]] * S, dtype=torch.float32)[:, :G]
+    kb16 = (k8.view(torch.float8_e4m3fn).float() * kv_scale[:, :, 0, None, None]).to(torch.bfloat16)
+    vb16 = (v8.view(torch.float8_e4m3fn).float() * kv_scale[:, :, 1, None, None]).to(torch.bfloat16)
+    assert torch.equal(kb16.float(), k8.view(torch.float8_e4m3fn).float() * kv_scale[:, :, 0, None, None])
+    kbar = orc.compress(bits(x["ki_cache"]), wl.block)
+    kb = wl.topk_tokens // wl.block
+    sel8, out8 = orc.decode_fp8(x["q"], k8, v8, kv_scale, kbar, x["qi"], x["w"], wl.block, kb)
+    sel, out = orc.decode(x["q"], kb16, vb16, kbar, x["qi"], x["w"], wl.block, kb)
+    np.testing.assert_array_equal(sel8, sel)
+    np.testing.assert_allclose(out8, out, rtol=0, atol=1e-12)
