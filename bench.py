@@ -212,6 +212,8 @@ def bench_decode(sg, datagen, torch, steps, warmup):
     step_bytes = gather_bytes + index_bytes + qo_bytes
     cache_build_bytes = p.n_seqs * p.n_tokens * p.idx_dim * 2 * (1 + 1 / p.block)
     varlen = bench_decode_varlen(sg, torch, p, y, blk, out, ws, steps, warmup)
+    fp8 = bench_decode_fp8(sg, datagen, torch, wl, p, y, blk, out, ws, steps, warmup,
+                           gather_bytes // 2 + index_bytes + qo_bytes)
     del y
     return {
         "metric": "decode tok/s",
@@ -226,6 +228,7 @@ def bench_decode(sg, datagen, torch, steps, warmup):
         "cache_compress": {"ms": compress_ms, "bytes": cache_build_bytes,
                            "GB_per_s": cache_build_bytes / (compress_ms / 1e3) / 1e9},
         "varlen": varlen,
+        "fp8": fp8,
     }
 
 
@@ -400,6 +403,34 @@ def bench_decode_varlen(sg, torch, p, y, blk, out, ws, steps, warmup):
     del kpool, vpool
     torch.cuda.empty_cache()
     return res
+
+
+def bench_decode_fp8(sg, datagen, torch, wl, p, y, blk, out, ws, steps, warmup, step_bytes):
+    """The decode step of the same workload over FP8 E4M3 K/V caches (sgqa_decode_fp8, dense, every
+    sequence at full length): the K/V gather reads half the bytes of the bf16 step."""
+    del y["k_cache"], y["v_cache"]
+    torch.cuda.empty_cache()
+    f = datagen.fp8_caches(wl, device="cuda")
+
+    def step():
+        sg.sgqa_decode_fp8(p, y["q"], f["k8"], f["v8"], f["kv_scale"], blk, y["qi"], y["w"], out, ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del f
+    torch.cuda.empty_cache()
+    return {"ms_per_step": ms, "tokens_per_s": p.n_seqs / (ms / 1e3), "step_bytes": step_bytes,
+            "GB_per_s": step_bytes / (ms / 1e3) / 1e9,
+            "hbm_frac": step_bytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS}
 
 
 def cpu_baseline(oracle, datagen, torch, np, res, wl):

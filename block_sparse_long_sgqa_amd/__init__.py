@@ -36,7 +36,8 @@ SGQA_OP_DECODE = 5
 
 # Every symbol include/sgqa.h declares.
 EXPORTED = ("sgqa_abi_version", "sgqa_status_string", "sgqa_workspace_size", "sgqa_compress", "sgqa_index_topk",
-            "sgqa_union", "sgqa_attend", "sgqa_prefill", "sgqa_decode", "sgqa_decode_varlen", "sgqa_append")
+            "sgqa_union", "sgqa_attend", "sgqa_prefill", "sgqa_decode", "sgqa_decode_varlen", "sgqa_append",
+            "sgqa_decode_fp8")
 
 
 class sgqa_pages(ctypes.Structure):
@@ -133,8 +134,9 @@ def lib() -> ctypes.CDLL:
         PG = ctypes.POINTER(sgqa_pages)
         L.sgqa_decode_varlen.argtypes = [PP, P, P, P, PG, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.sgqa_append.argtypes = [PP, P, P, P, P, P, P, PG, P, P, P]
+        L.sgqa_decode_fp8.argtypes = [PP, P, P, P, P, PG, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         for name in ("sgqa_compress", "sgqa_index_topk", "sgqa_union", "sgqa_attend", "sgqa_prefill", "sgqa_decode",
-                     "sgqa_decode_varlen", "sgqa_append"):
+                     "sgqa_decode_varlen", "sgqa_append", "sgqa_decode_fp8"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -300,6 +302,32 @@ def sgqa_append(p: Params, k_new, v_new, idx_k_new, positions, k_cache, v_cache,
             _ptr(idx_k_cache, "idx_k_cache", torch.bfloat16, (S, C, p.idx_dim)),
             _ptr(blk_k, "blk_k", torch.bfloat16, (S, C // p.block, p.idx_dim)))
     _check(lib().sgqa_append(ctypes.byref(p.c()), *args, _stream(stream)), "sgqa_append")
+
+
+def _codes(t, name: str, shape):
+    """FP8 E4M3 cache as its uint8 codes (a float8_e4m3fn tensor is reinterpreted, never converted)."""
+    if isinstance(t, torch.Tensor) and t.dtype == torch.float8_e4m3fn:
+        t = t.view(torch.uint8)
+    return _ptr(t, name, torch.uint8, shape)
+
+
+def sgqa_decode_fp8(p: Params, q, k_cache, v_cache, kv_scale, blk_k, idx_q, idx_w, out, ws, seq_lens=None,
+                    pages=None, topk_out=None, stream=None) -> None:
+    """Decode over FP8 E4M3 K/V caches (uint8 codes or float8_e4m3fn) with kv_scale [S][G][2] fp32."""
+    S, C, Hq, G, D = p.n_seqs, p.n_tokens, p.n_q_heads, p.n_kv_heads, p.head_dim
+    shp = _cache_shape(p, pages)
+    pg = pages.c(S) if pages is not None else None
+    args = (_ptr(q, "q", torch.bfloat16, (S, Hq, D)), _codes(k_cache, "k_cache", shp),
+            _codes(v_cache, "v_cache", shp), _ptr(kv_scale, "kv_scale", torch.float32, (S, G, 2)),
+            ctypes.byref(pg) if pg is not None else None,
+            _ptr(blk_k, "blk_k", torch.bfloat16, (S, C // p.block, p.idx_dim)),
+            _ptr(idx_q, "idx_q", torch.bfloat16, (S, G, p.idx_heads, p.idx_dim)),
+            _ptr(idx_w, "idx_w", torch.float32, (G, p.idx_heads)),
+            _ptr(seq_lens, "seq_lens", torch.int32, (S,)),
+            _ptr(topk_out, "topk_out", torch.int32, (S, G, p.kb)),
+            _ptr(out, "out", torch.bfloat16, (S, Hq, D)))
+    _check(lib().sgqa_decode_fp8(ctypes.byref(p.c()), *args, _ptr(ws, "ws", torch.uint8), ws.numel(),
+                                 _stream(stream)), "sgqa_decode_fp8")
 
 
 # ------------------------------------------------------------------------------------ helpers

@@ -599,6 +599,55 @@ __device__ __forceinline__ void k_load_regs(bf16x8 (&kreg)[16], const uint16_t* 
   }
 }
 
+// Attended block list of one (sequence s, group g) into LDS: blocks[0 .. n_sel-1] = Sel(s,g)
+// (ascending), blocks[n_sel] = the own block; paged caches also get prow[e], the pool row of the
+// first token of entry e (a block lies inside one page, the page size being a multiple of B). The
+// selection holds exactly n_sel = min(K_B, c) valid entries, c = floor((ctx-1)/B) candidate blocks,
+// so no pass over the list is needed to count them, and every thread issues all of its list loads
+// (and the length load) before the first wait. Entries are clamped to [0, own], so even a corrupt
+// list never addresses outside the caches or the page table. Ends with a barrier.
+template <bool PAGED>
+__device__ __forceinline__ void load_decode_list(const int32_t* __restrict__ srow, int kb, int ctx, int block_shift,
+                                                 int* blocks, int* prow, const int32_t* __restrict__ table_row,
+                                                 int page_shift, int n_pages, int n_groups, int g, int& n_sel_out) {
+  const int own = (ctx - 1) >> block_shift;
+  const int n_sel = own < kb ? own : kb;
+  n_sel_out = n_sel;
+  for (int e0 = threadIdx.x; e0 <= kb; e0 += 4 * blockDim.x) {
+    int b[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + u * blockDim.x;
+      b[u] = e < kb ? srow[e] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + u * blockDim.x;
+      const int v = e < n_sel ? b[u] : own;
+      b[u] = v < 0 ? 0 : (v > own ? own : v);
+    }
+    int pg[4];
+    if (PAGED) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        pg[u] = e0 + u * (int)blockDim.x <= n_sel ? table_row[(b[u] << block_shift) >> page_shift] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + u * blockDim.x;
+      if (e <= n_sel) {
+        blocks[e] = b[u];
+        if (PAGED) {
+          const int p = pg[u] < 0 ? 0 : (pg[u] >= n_pages ? n_pages - 1 : pg[u]);
+          const int tb = b[u] << block_shift;
+          prow[e] = ((p * n_groups + g) << page_shift) + (tb & ((1 << page_shift) - 1));
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
 // Decode attention: one workgroup of 4 waves per (sequence s, group g). The attended blocks are
 // Sel(s,g) (ascending) plus the own block; wave w handles chunks w, w+4, ... Decode is a gather at
 // HBM rate, so the loop is built to keep bytes in flight: the K operands of a chunk go straight
@@ -627,7 +676,6 @@ __global__ __launch_bounds__(256) void k_decode_attend(const uint16_t* __restric
   uint8_t* vbuf[2] = {smem + wave * 2 * kDecVStage, smem + wave * 2 * kDecVStage + kDecVStage};
   int* blocks = reinterpret_cast<int*>(smem + kWavesD * 2 * kDecVStage);  // kb + 1 entries
   int* prow = blocks + (kb + 1);  // paged: pool row of each entry's first token (kb + 1 entries)
-  __shared__ int n_sel_shared;
 
   const int s = blockIdx.x / n_groups, g = blockIdx.x % n_groups;
   const int r = n_q_heads / n_groups;
@@ -635,28 +683,6 @@ __global__ __launch_bounds__(256) void k_decode_attend(const uint16_t* __restric
   int ctx = lens ? lens[s] : cap;
   ctx = ctx < 1 ? 1 : (ctx > cap ? cap : ctx);
   const int i_q = ctx - 1;
-  const int own = i_q / block;
-
-  // Entries: Sel (ascending, -1 padded at the end) then the own block.
-  const int32_t* srow = sel + ((long long)s * n_groups + g) * kb;
-  if (wave == 0) {
-    int cnt = 0;
-    for (int base = 0; base < kb; base += 64) cnt += popc64(ballot(base + l < kb && srow[base + l] >= 0));
-    if (l == 0) n_sel_shared = cnt;
-  }
-  __syncthreads();
-  const int n_sel = n_sel_shared;
-  for (int e = threadIdx.x; e <= n_sel; e += blockDim.x) {
-    const int b = e < n_sel ? srow[e] : own;
-    blocks[e] = b;
-    if (PAGED) {  // a block lies inside one page (the page size is a multiple of B)
-      const int tb = b << block_shift;
-      int pg = table[(long long)s * max_pages + (tb >> page_shift)];
-      pg = pg < 0 ? 0 : (pg >= n_pages ? n_pages - 1 : pg);
-      prow[e] = ((pg * n_groups + g) << page_shift) + (tb & ((1 << page_shift) - 1));
-    }
-  }
-  __syncthreads();
 
   bf16x8 qreg[1][8];
   int row_pos[1];
@@ -675,19 +701,23 @@ __global__ __launch_bounds__(256) void k_decode_attend(const uint16_t* __restric
       }
     }
   }
+  int n_sel;
+  load_decode_list<PAGED>(sel + ((long long)s * n_groups + g) * kb, kb, ctx, block_shift, blocks, prow,
+                          PAGED ? table + (long long)s * max_pages : nullptr, page_shift, n_pages, n_groups, g, n_sel);
   AttnState<1> st;
   state_init(st);
   const long long seq_off = PAGED ? 0 : ((long long)s * n_groups + g) * cap * kD;
   const int n_keys = (n_sel + 1) * block;
-  // Element offset of the cache row of key `key` of chunk c (keys past the list read a valid row;
-  // the token table masks them).
+  // Element offset of the cache row of key `key` of chunk c (keys past the list or past the context
+  // read row 0; the token table masks them).
   auto off_in = [&](int c) {
     return [&, c](int key) -> long long {
       const int kp = c * kKeys + key;
       if (kp >= n_keys) return seq_off;
       const int e = kp >> block_shift, j = kp & (block - 1);
-      if (PAGED) return ((long long)prow[e] + j) * kD;
-      return seq_off + (long long)((blocks[e] << block_shift) + j) * kD;
+      if (PAGED) return ((long long)prow[e] + j) * kD;  // a block lies inside its page
+      const int tk = (blocks[e] << block_shift) + j;  // own-block rows past ctx may lie past cap: masked,
+      return seq_off + (long long)(tk < ctx ? tk : 0) * kD;  // so read row 0 instead
     };
   };
   const int n_chunks = (n_keys + kKeys - 1) / kKeys;
@@ -755,6 +785,230 @@ __global__ __launch_bounds__(256) void k_decode_attend(const uint16_t* __restric
     }
     out[((long long)s * n_q_heads + g * r + row) * kD + d] = (uint16_t)f32_to_bf16_bits(num / den);
   }
+}
+
+// ---------------------------------------------------------------------- decode over FP8 K/V caches
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled (register arrays indexed by i stay
+// in registers).
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+// The K/V caches hold OCP FP8 E4M3 codes with one scale per (sequence, group) for K and one for V
+// (kv_scale [S][G][2]); every E4M3 value is exact in bf16, so the codes are converted to bf16 and fed
+// to the same matrix-core chunk as the bf16 path, the key scale folded into the softmax exponent
+// scale and the value scale into the final normalisation. One 4-wave workgroup per (sequence, group)
+// as in k_decode_attend; per wave and chunk the K and V codes of the NEXT chunk are gathered into
+// registers while the current chunk computes: K straight into MFMA operands (the head dimension is
+// permuted so that lane half h holds dims 64h .. 64h + 63, contiguous in the cache row; Q is loaded
+// with the same permutation), V converted and written into the wave's bf16 V tile (row-major,
+// swizzled as in chunk_issue) for the transposing reads.
+template <bool PAGED, int DEPTH>
+__global__ __launch_bounds__(256) void k_decode_attend_f8(const uint16_t* __restrict__ q,
+                                                          const uint8_t* __restrict__ kc,
+                                                          const uint8_t* __restrict__ vc,
+                                                          const float* __restrict__ kv_scale,
+                                                          const int32_t* __restrict__ sel, uint16_t* __restrict__ out,
+                                                          int cap, int n_q_heads, int n_groups, int block,
+                                                          int block_shift, int kb, float scale_log2,
+                                                          const int32_t* __restrict__ lens,
+                                                          const int32_t* __restrict__ table, int max_pages,
+                                                          int page_shift, int n_pages) {
+  constexpr int kWavesD = 4;
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int wave = threadIdx.x >> 6;
+  uint8_t* vt = smem + wave * kDecVStage;  // this wave's bf16 V tile + token table
+  int* blocks = reinterpret_cast<int*>(smem + kWavesD * kDecVStage);  // kb + 1 entries
+  int* prow = blocks + (kb + 1);
+
+  const int s = blockIdx.x / n_groups, g = blockIdx.x % n_groups;
+  const int r = n_q_heads / n_groups;
+  const int l = lane_id(), h = l >> 5;
+  int ctx = lens ? lens[s] : cap;
+  ctx = ctx < 1 ? 1 : (ctx > cap ? cap : ctx);
+  const int i_q = ctx - 1;
+  const float k_scale = kv_scale[((long long)s * n_groups + g) * 2 + 0];
+  const float v_scale = kv_scale[((long long)s * n_groups + g) * 2 + 1];
+
+  // Q (B operand of S^T) with the permuted head dimension: step ks, lane half h -> dims 64h + 8ks.
+  bf16x8 qreg[1][8];
+  int row_pos[1];
+  {
+    const int hh = l & 31;
+    const bool valid = hh < r;
+    row_pos[0] = valid ? i_q : -1;
+    const uint16_t* src = q + ((long long)s * n_q_heads + g * r + (valid ? hh : 0)) * kD + 64 * h;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      if (valid) {
+        qreg[0][ks] = *reinterpret_cast<const bf16x8*>(src + 8 * ks);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qreg[0][ks][e] = (__bf16)0.0f;
+      }
+    }
+  }
+  int n_sel;
+  load_decode_list<PAGED>(sel + ((long long)s * n_groups + g) * kb, kb, ctx, block_shift, blocks, prow,
+                          PAGED ? table + (long long)s * max_pages : nullptr, page_shift, n_pages, n_groups, g, n_sel);
+  AttnState<1> st;
+  state_init(st);
+  const long long seq_off = PAGED ? 0 : ((long long)s * n_groups + g) * cap * kD;
+  const int n_keys = (n_sel + 1) * block;
+  const int n_chunks = (n_keys + kKeys - 1) / kKeys;
+  const LaneOffsets lo = lane_offsets(0);
+  // Byte offset of the cache row of key `key` of chunk c; keys past the list or the context (and
+  // chunks past the last) read row 0, which the token table masks. Branch-free, so every gather
+  // issues the same loads.
+  auto off_of = [&](int c, int key) -> long long {
+    const int kp = c * kKeys + key;
+    const bool in = kp < n_keys;
+    const int e = in ? kp >> block_shift : 0, j = kp & (block - 1);
+    if (PAGED) return in ? ((long long)prow[e] + j) * kD : 0;
+    const int tk = (blocks[e] << block_shift) + j;
+    return seq_off + (long long)(in && tk < ctx ? tk : 0) * kD;
+  };
+  auto tok_of = [&](int c, int key) -> int {
+    const int kp = c * kKeys + key;
+    if (kp >= n_keys) return -1;
+    const int tk = (blocks[kp >> block_shift] << block_shift) + (kp & (block - 1));
+    return tk < ctx ? tk : -1;
+  };
+  // Gathers of one chunk into register set d: K, key row 32 kt + (l % 32), bytes 64h .. 64h + 63
+  // (4 x 16 B); V, row 8w + l / 8 for w < 8, bytes 16 (l % 8) .. + 15. DEPTH sets are in flight,
+  // the chunks c + 4, c + 8, ... of this wave; the compiler's counter waits release each set.
+  u32x4 k8[DEPTH][2][4];
+  u32x4 v8[DEPTH][8];
+  auto gather = [&](auto dd, int c) {
+    constexpr int d = decltype(dd)::value;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const uint8_t* src = kc + off_of(c, 32 * kt + (l & 31)) + 64 * h;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) k8[d][kt][j] = *reinterpret_cast<const u32x4*>(src + 16 * j);
+    }
+#pragma unroll
+    for (int w = 0; w < 8; ++w)
+      v8[d][w] = *reinterpret_cast<const u32x4*>(vc + off_of(c, 8 * w + (l >> 3)) + 16 * (l & 7));
+  };
+  auto cvt8 = [](uint32_t w0, uint32_t w1) -> bf16x8 {  // 8 codes (little-endian) -> 8 bf16
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+    const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+    const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+    const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+    bf16x8 o;
+    o[0] = a[0]; o[1] = a[1]; o[2] = b[0]; o[3] = b[1];
+    o[4] = c[0]; o[5] = c[1]; o[6] = d[0]; o[7] = d[1];
+    return o;
+  };
+  bf16x8 kreg[16];
+  const float sl2 = scale_log2 * k_scale;
+  // One chunk from register set d: V codes -> bf16 V tile (the layout chunk_issue gives the V
+  // tile) and the token table, K codes -> MFMA operands; then set d is refilled with chunk
+  // c + 4 DEPTH (always issued, past the end it reads row 0, so that the number of loads between
+  // a set's issue and its use is the same on every path and the counter waits stay partial).
+  auto step = [&](auto dd, int c) {
+    constexpr int d = decltype(dd)::value;
+    const bool live = c < n_chunks;  // wave-uniform
+    if (live) {
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const int row = 8 * w + (l >> 3), piece = 2 * (l & 7);
+        *reinterpret_cast<bf16x8*>(vt + row * 256 + 16 * v_phys(row, piece)) = cvt8(v8[d][w].x, v8[d][w].y);
+        *reinterpret_cast<bf16x8*>(vt + row * 256 + 16 * v_phys(row, piece + 1)) = cvt8(v8[d][w].z, v8[d][w].w);
+      }
+      const int t = tok_of(c, l);
+      reinterpret_cast<int*>(vt + kVTileBytes)[l] = t >= 0 ? t : 0x7FFFFFFF;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          kreg[(2 * j) * 2 + kt] = cvt8(k8[d][kt][j].x, k8[d][kt][j].y);
+          kreg[(2 * j + 1) * 2 + kt] = cvt8(k8[d][kt][j].z, k8[d][kt][j].w);
+        }
+    }
+    gather(dd, c + DEPTH * kWavesD);
+    if (live) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      attn_chunk<1, 2, true>(vt, lo, qreg, st, sl2, c == n_chunks - 1, row_pos, kreg);
+    }
+  };
+  if (wave < n_chunks) {
+    static_for<DEPTH>([&](auto dd) { gather(dd, wave + decltype(dd)::value * kWavesD); });
+    for (int c0 = wave; c0 < n_chunks; c0 += DEPTH * kWavesD)
+      static_for<DEPTH>([&](auto dd) { step(dd, c0 + decltype(dd)::value * kWavesD); });
+  }
+
+  // Merge the four wave states (as in k_decode_attend), the value scale applied once at the end.
+  const float l_all = st.l[0] + __shfl_xor(st.l[0], 32, 64);
+  float* o_lds = reinterpret_cast<float*>(vt);  // [32 rows][128]
+  float* ml_lds = reinterpret_cast<float*>(blocks) + 2 * (kb + 1);  // [4][32][2]
+  __syncthreads();
+  {
+    const int row = l & 31;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int d = dt * 32 + 8 * (j >> 2) + 4 * (l >> 5) + (j & 3);
+        o_lds[row * kD + d] = st.o[0][dt][j];
+      }
+    if (l < 32) {
+      ml_lds[(wave * 32 + row) * 2 + 0] = st.m[0];
+      ml_lds[(wave * 32 + row) * 2 + 1] = l_all;
+    }
+  }
+  __syncthreads();
+  for (int x = threadIdx.x; x < r * kD; x += blockDim.x) {
+    const int row = x / kD, d = x % kD;
+    float m = -1.0e30f;
+    for (int w = 0; w < kWavesD; ++w) m = fmaxf(m, ml_lds[(w * 32 + row) * 2]);
+    float num = 0.0f, den = 0.0f;
+    for (int w = 0; w < kWavesD; ++w) {
+      const float f = fast_exp2(ml_lds[(w * 32 + row) * 2] - m);
+      den += ml_lds[(w * 32 + row) * 2 + 1] * f;
+      num += reinterpret_cast<const float*>(smem + w * kDecVStage)[row * kD + d] * f;
+    }
+    out[((long long)s * n_q_heads + g * r + row) * kD + d] = (uint16_t)f32_to_bf16_bits(num / den * v_scale);
+  }
+}
+
+// Chunks of FP8 codes in flight per wave (register sets of 32 VGPRs each). One set already keeps
+// the gather at the rate of a bare gather loop: a second one measured no faster.
+#ifndef SGQA_F8_DEPTH
+#define SGQA_F8_DEPTH 1
+#endif
+constexpr int kF8Depth = SGQA_F8_DEPTH;
+
+size_t decode_attend_f8_lds(int kb) { return (size_t)4 * kDecVStage + (size_t)2 * (kb + 1) * 4 + 4 * 32 * 2 * 4; }
+
+hipError_t launch_decode_attend_f8(const uint16_t* q, const uint8_t* kc, const uint8_t* vc, const float* kv_scale,
+                                   const int32_t* sel, uint16_t* out, int n_seqs, int ctx, int n_q_heads,
+                                   int n_groups, int block, int kb, float scale, const int32_t* lens,
+                                   const PageTable& pages, hipStream_t stream) {
+  const size_t lds = decode_attend_f8_lds(kb);
+  if (lds > (size_t)max_lds_per_block()) return hipErrorInvalidValue;
+  const void* fn = pages.table ? (const void*)k_decode_attend_f8<true, kF8Depth>
+                                : (const void*)k_decode_attend_f8<false, kF8Depth>;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const float scale_log2 = scale * 1.4426950408889634f;
+  const dim3 grid((unsigned)(n_seqs * n_groups));
+  if (pages.table)
+    hipLaunchKernelGGL((k_decode_attend_f8<true, kF8Depth>), grid, dim3(256), lds, stream, q, kc, vc, kv_scale, sel,
+                       out, ctx, n_q_heads, n_groups, block, __builtin_ctz(block), kb, scale_log2, lens, pages.table,
+                       pages.max_pages, __builtin_ctz(pages.page_tokens), pages.n_pages);
+  else
+    hipLaunchKernelGGL((k_decode_attend_f8<false, kF8Depth>), grid, dim3(256), lds, stream, q, kc, vc, kv_scale, sel,
+                       out, ctx, n_q_heads, n_groups, block, __builtin_ctz(block), kb, scale_log2, lens, nullptr, 0,
+                       0, 0);
+  return hipGetLastError();
 }
 
 // Four waves' double-buffered V stages, the entry list and the paged rows (2 x (kb + 1) ints), and the

@@ -301,17 +301,21 @@ int check_pages(const sgqa_params* p, const sgqa_pages* pg, PageTable* out) {
   return SGQA_OK;
 }
 
-// Shared body of sgqa_decode and sgqa_decode_varlen.
-int decode_impl(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k_cache, const sgqa_bf16* v_cache,
-                const sgqa_pages* pages, const sgqa_bf16* blk_k, const sgqa_bf16* idx_q, const float* idx_w,
-                const int32_t* seq_lens, int32_t* topk_out, sgqa_bf16* out, void* ws, size_t ws_bytes,
-                sgqa_stream stream) {
+// Shared body of sgqa_decode, sgqa_decode_varlen and sgqa_decode_fp8 (kv_scale != nullptr: the caches
+// hold FP8 E4M3 codes).
+int decode_impl(const sgqa_params* p, const sgqa_bf16* q, const void* k_cache, const void* v_cache,
+                const float* kv_scale, const sgqa_pages* pages, const sgqa_bf16* blk_k, const sgqa_bf16* idx_q,
+                const float* idx_w, const int32_t* seq_lens, int32_t* topk_out, sgqa_bf16* out, void* ws,
+                size_t ws_bytes, sgqa_stream stream) {
+  const bool fp8 = kv_scale != nullptr;
   int st = check_params(p, NEED_INDEX | NEED_SELECT | NEED_DECODE | NEED_ATTN, false);
   if (st) return st;
+  if (fp8 && decode_attend_f8_lds(kb_of(p)) > kGfx950LdsBytes) return SGQA_ERR_SHAPE;
   if (!q || !k_cache || !v_cache || !idx_q || !idx_w || !out || (!blk_k && p->n_tokens > p->block))
     return SGQA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(blk_k) || !aligned16(idx_q) ||
-      !aligned16(idx_w) || !aligned16(topk_out) || !aligned16(out) || !aligned16(ws) || !aligned16(seq_lens))
+      !aligned16(idx_w) || !aligned16(topk_out) || !aligned16(out) || !aligned16(ws) || !aligned16(seq_lens) ||
+      !aligned16(kv_scale))
     return SGQA_ERR_ALIGN;
   PageTable pt;
   st = check_pages(p, pages, &pt);
@@ -323,9 +327,14 @@ int decode_impl(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k_cac
   const int kb = kb_of(p);
   hipError_t e = launch_decode_select(idx_q, idx_w, blk_k, l.sel, topk_out, l.select_ws, p->n_seqs, p->n_tokens,
                                       p->n_kv_heads, p->block, kb, seq_lens, s);
-  if (e == hipSuccess)
-    e = launch_decode_attend(q, k_cache, v_cache, l.sel, out, p->n_seqs, p->n_tokens, p->n_q_heads,
-                             p->n_kv_heads, p->block, kb, scale_of(p), seq_lens, pt, s);
+  if (e == hipSuccess && fp8)
+    e = launch_decode_attend_f8(q, static_cast<const uint8_t*>(k_cache), static_cast<const uint8_t*>(v_cache),
+                                kv_scale, l.sel, out, p->n_seqs, p->n_tokens, p->n_q_heads, p->n_kv_heads,
+                                p->block, kb, scale_of(p), seq_lens, pt, s);
+  else if (e == hipSuccess)
+    e = launch_decode_attend(q, static_cast<const sgqa_bf16*>(k_cache), static_cast<const sgqa_bf16*>(v_cache),
+                             l.sel, out, p->n_seqs, p->n_tokens, p->n_q_heads, p->n_kv_heads, p->block, kb,
+                             scale_of(p), seq_lens, pt, s);
   return status_of(e);
 }
 
@@ -334,8 +343,8 @@ int decode_impl(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k_cac
 int sgqa_decode(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k_cache, const sgqa_bf16* v_cache,
                 const sgqa_bf16* blk_k, const sgqa_bf16* idx_q, const float* idx_w, int32_t* topk_out,
                 sgqa_bf16* out, void* ws, size_t ws_bytes, sgqa_stream stream) {
-  return decode_impl(p, q, k_cache, v_cache, nullptr, blk_k, idx_q, idx_w, nullptr, topk_out, out, ws, ws_bytes,
-                     stream);
+  return decode_impl(p, q, k_cache, v_cache, nullptr, nullptr, blk_k, idx_q, idx_w, nullptr, topk_out, out, ws,
+                     ws_bytes, stream);
 }
 
 int sgqa_decode_varlen(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k_cache,
@@ -343,8 +352,17 @@ int sgqa_decode_varlen(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16
                        const sgqa_bf16* idx_q, const float* idx_w, const int32_t* seq_lens, int32_t* topk_out,
                        sgqa_bf16* out, void* ws, size_t ws_bytes, sgqa_stream stream) {
   if (!seq_lens) return SGQA_ERR_NULL;
-  return decode_impl(p, q, k_cache, v_cache, pages, blk_k, idx_q, idx_w, seq_lens, topk_out, out, ws, ws_bytes,
-                     stream);
+  return decode_impl(p, q, k_cache, v_cache, nullptr, pages, blk_k, idx_q, idx_w, seq_lens, topk_out, out, ws,
+                     ws_bytes, stream);
+}
+
+int sgqa_decode_fp8(const sgqa_params* p, const sgqa_bf16* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                    const float* kv_scale, const sgqa_pages* pages, const sgqa_bf16* blk_k,
+                    const sgqa_bf16* idx_q, const float* idx_w, const int32_t* seq_lens, int32_t* topk_out,
+                    sgqa_bf16* out, void* ws, size_t ws_bytes, sgqa_stream stream) {
+  if (!kv_scale) return SGQA_ERR_NULL;
+  return decode_impl(p, q, k_cache, v_cache, kv_scale, pages, blk_k, idx_q, idx_w, seq_lens, topk_out, out, ws,
+                     ws_bytes, stream);
 }
 
 int sgqa_append(const sgqa_params* p, const sgqa_bf16* k_new, const sgqa_bf16* v_new, const sgqa_bf16* idx_k_new,

@@ -60,6 +60,14 @@ hipError_t launch_decode_attend(const uint16_t* q, const uint16_t* kc, const uin
 // LDS a launch needs (validation rejects shapes that do not fit before anything is enqueued).
 size_t index_topk_lds_min(int kb);
 size_t decode_attend_lds(int kb);
+size_t decode_attend_f8_lds(int kb);
+
+// Decode attention over FP8 E4M3 K/V caches (uint8 codes, same layouts as the bf16 caches) with
+// kv_scale [S][G][2] fp32 (key scale, value scale).
+hipError_t launch_decode_attend_f8(const uint16_t* q, const uint8_t* kc, const uint8_t* vc, const float* kv_scale,
+                                   const int32_t* sel, uint16_t* out, int n_seqs, int ctx, int n_q_heads,
+                                   int n_groups, int block, int kb, float scale, const int32_t* lens,
+                                   const PageTable& pages, hipStream_t stream);
 size_t attend_lds_bytes_for(int n_tokens, int block);
 constexpr size_t kGfx950LdsBytes = 160 * 1024;
 

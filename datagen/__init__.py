@@ -9,6 +9,10 @@ Value recipes (shared by every workload):
   * index queries / keys: integers uniform in {-4, ..., 4}, stored exactly in bf16, so block means
     and fp32 score sums are exact (every intermediate is a multiple of 1/B well inside 2^24).
   * indexer weights w[g][h]: 1 (tiny) or uniform in {1, 2}.
+  * FP8 K/V caches: N(0, 16^2) drawn in fp32 and converted to E4M3 codes by torch's float8_e4m3fn
+    cast (nearest-even; |x| <= 448 always holds in practice), stored as uint8; scales per
+    (sequence, group) and K/V uniform in [1/32, 1/16] fp32, so the attended rows have a standard
+    deviation of 0.5 .. 1.
   * "adjacent-token correlated" index queries: for every (group, head) an anchor vector per
     segment of 256 queries; every coordinate of a query is redrawn independently with probability
     rho (default 1/8). rho = 1 gives independent queries (stress case).
@@ -197,6 +201,23 @@ def decode_inputs(wl: Workload, device="cpu", seed0: int = SEED0, n_seqs: Option
         "qi": index_queries(wl, d, S),
         "w": d.weights(),
     }
+
+
+def fp8_caches(wl: Workload, device="cpu", seed0: int = SEED0, n_seqs: Optional[int] = None) -> dict:
+    """FP8 E4M3 K/V caches for a decode workload: k8, v8 [S][G][L][D] uint8 codes and kv_scale
+    [S][G][2] fp32 (key scale, value scale). Drawn one sequence at a time."""
+    d = _Draw(wl, device, seed0)
+    S = wl.n_seqs if n_seqs is None else n_seqs
+    L, G, D = wl.n_tokens, wl.n_kv_heads, wl.head_dim
+    k8 = torch.empty((S, G, L, D), dtype=torch.uint8, device=d.device)
+    v8 = torch.empty((S, G, L, D), dtype=torch.uint8, device=d.device)
+    for s in range(S):
+        for name, dst in (("k8", k8), ("v8", v8)):
+            x = torch.randn((G, L, D), generator=d.gen(f"{name}/{s}"), device=d.device, dtype=torch.float32)
+            dst[s] = (x * 16.0).to(torch.float8_e4m3fn).view(torch.uint8)
+            del x
+    u = torch.rand((S, G, 2), generator=d.gen("kv_scale"), device=d.device, dtype=torch.float32)
+    return {"k8": k8, "v8": v8, "kv_scale": (1.0 + u) / 32.0}
 
 
 def default_scale(head_dim: int) -> float:

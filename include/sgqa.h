@@ -226,6 +226,31 @@ int sgqa_append(const sgqa_params* p, const sgqa_bf16* k_new, const sgqa_bf16* v
                 const int32_t* positions, sgqa_bf16* k_cache, sgqa_bf16* v_cache, const sgqa_pages* pages,
                 sgqa_bf16* idx_k_cache, sgqa_bf16* blk_k, sgqa_stream stream);
 
+/* ---------------------------------------------------------------- FP8 K/V cache decode
+ * The pages serve the model with an FP8 K/V cache to raise the effective cache capacity ("Inside
+ * Step 5 Preview", Agentic RL, High-Throughput and Low-Redundancy Infrastructure). The selection is
+ * unchanged (the index keys and block keys stay bf16); only the gather of the attended K/V rows
+ * reads 1-byte codes, which halves the bytes of the decode's dominant kernel.
+ *
+ * Decode as sgqa_decode_varlen with FP8 E4M3 K/V caches:
+ *   k_cache, v_cache  uint8 OCP E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ *                 the all-ones exponent with all-ones mantissa is NaN, there is no infinity), same
+ *                 layouts as the bf16 caches: dense [S][G][C][D], or the pools of *pages
+ *                 ([n_pages][G][page_tokens][D], one byte per element)
+ *   kv_scale      [S][G][2] fp32 DEVICE: the key and value scale of (sequence s, group g); the
+ *                 attended rows are code value * scale (NaN codes propagate into the output)
+ *   seq_lens      [S] int32 DEVICE, or NULL: every sequence at the full capacity C = p->n_tokens
+ *   pages         NULL for dense caches
+ *   q, blk_k, idx_q, idx_w, topk_out, out   as in sgqa_decode
+ * Every E4M3 value is exact in bf16 and the scales are applied in fp32 (the key scale inside the
+ * softmax exponent, the value scale to the normalised output), so the result is that of the decode
+ * over the dequantised rows up to fp32 rounding order. kv_scale == NULL -> SGQA_ERR_NULL.
+ * Workspace: sgqa_workspace_size(p, SGQA_OP_DECODE). */
+int sgqa_decode_fp8(const sgqa_params* p, const sgqa_bf16* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                    const float* kv_scale, const sgqa_pages* pages, const sgqa_bf16* blk_k,
+                    const sgqa_bf16* idx_q, const float* idx_w, const int32_t* seq_lens, int32_t* topk_out,
+                    sgqa_bf16* out, void* ws, size_t ws_bytes, sgqa_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -155,3 +155,24 @@ def test_varlen_decode_and_append_validation(sg):
     assert append(pages(a, 64, 12, 100)) == sg.SGQA_ERR_SHAPE
     bad_dim = _p(n_tokens=4096, n_seqs=4, union_tile=1, head_dim=64)
     assert lib.sgqa_append(ctypes.byref(bad_dim.c()), a, a, a, a, a, a, None, a, a, nul) == sg.SGQA_ERR_SHAPE
+
+
+def test_fp8_decode_validation(sg):
+    lib = sg.lib()
+    nul = ctypes.c_void_p(0)
+    buf = (ctypes.c_uint8 * 64)()
+    a = ctypes.c_void_p((ctypes.addressof(buf) + 15) // 16 * 16)
+    d = _p(n_tokens=4096, n_seqs=4, union_tile=1)
+    dp = ctypes.byref(d.c())
+
+    def fp8(scale=a, lens=nul, pg=None, ws_bytes=1 << 40, q=a):
+        return lib.sgqa_decode_fp8(dp, q, a, a, scale, pg, a, a, a, lens, nul, a, a, ws_bytes, nul)
+
+    assert fp8(scale=nul) == sg.SGQA_ERR_NULL                                   # kv_scale is required
+    assert fp8(q=nul) == sg.SGQA_ERR_NULL
+    assert fp8(scale=ctypes.c_void_p(a.value + 4)) == sg.SGQA_ERR_ALIGN
+    bad = ctypes.byref(sg.sgqa_pages(a.value, 64, 48, 100))
+    assert fp8(pg=bad) == sg.SGQA_ERR_SHAPE
+    # dense and varlen descriptors get as far as the workspace check
+    assert fp8(ws_bytes=16) == sg.SGQA_ERR_WORKSPACE
+    assert fp8(lens=a, ws_bytes=16) == sg.SGQA_ERR_WORKSPACE
