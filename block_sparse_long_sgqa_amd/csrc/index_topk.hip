@@ -16,14 +16,16 @@
 //  * Block keys stream through LDS in chunks of 128 blocks, gathered with global_load_lds into
 //    double-buffered 144-byte rows (16 B of padding spread the MFMA operand reads over all banks);
 //    each chunk feeds every row of the workgroup.
-//  * Pass 1 finds, per row, the exact K_B-th largest score tau and how many candidates equal to
-//    tau belong to the selection. Each row keeps in LDS only the keys of candidates scoring above
-//    an acceptance threshold; when the list could overflow it is trimmed to the multiset of its
-//    K_B largest keys and the threshold rises to the new K_B-th key (a rejected candidate is
-//    already beaten by K_B others). The K-th largest key is found by binary search over the
-//    order-preserving 32-bit key, counting with wave ballots (no atomics).
-//  * Pass 2 recomputes the scores and emits, in ascending block order, every candidate with
-//    s > tau plus the lowest-id candidates with s == tau (ballot + popcount compaction).
+//  * Exact selection without a score matrix, in three streaming passes over the candidates:
+//    pass 0 lists a strided sample of each row's keys (all of them when few) -- a complete list
+//    gives the K_B-th key at once, a sample the key range where it must lie; pass 1 counts the
+//    keys of that range into 256 power-of-two buckets per row (LDS atomics) and moves to the
+//    bucket holding the K_B-th key, repeating on a finer scale while that bucket is wide and
+//    crowded; pass 2 emits, in ascending block order, every candidate above the bucket plus the
+//    bucket's members -- the first `take` of them when the bucket is one key (lowest ids win
+//    ties), or all of them flagged, with their keys listed, when it is wider; the flagged ones are
+//    then settled by an exact select over the listed keys. Scores are recomputed in every pass
+//    (the stream of block keys through LDS is cheap next to storing them).
 //  * Decode selection (one query, many candidates) is shaped differently and lives on its own.
 #include <type_traits>
 
@@ -50,7 +52,8 @@ constexpr int kKSlots = kKRowBytes / 16;           // 9 slots of 16 B per row, t
 constexpr int kStageBytes = kChunk * kKRowBytes;   // 18432 B
 constexpr int kStageInsts = kChunk * kKSlots / 64;  // 18 wave-wide 16-byte loads per stage
 constexpr float kNegInf = -__builtin_huge_valf();
-constexpr int kListPad = 16;                       // words between row lists (spreads LDS banks)
+constexpr int kListPad = 16;                       // words between row regions (spreads LDS banks)
+constexpr int kSideCap = 192;                      // bucket members listed per row in the emit pass
 
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -64,9 +67,13 @@ __device__ __forceinline__ uint32_t row16_prefix(uint32_t v) {
   return v;
 }
 
-// Inverse of score_key (canonical +0).
-__device__ __forceinline__ float key_to_score(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+// The value of the last lane of each 16-lane row, for every lane of the row (four lane reads
+// instead of an LDS permute).
+__device__ __forceinline__ uint32_t row16_total(uint32_t incl) {
+  const uint32_t t0 = __builtin_amdgcn_readlane(incl, 15), t1 = __builtin_amdgcn_readlane(incl, 31);
+  const uint32_t t2 = __builtin_amdgcn_readlane(incl, 47), t3 = __builtin_amdgcn_readlane(incl, 63);
+  const int q = lane_id() >> 4;
+  return q == 0 ? t0 : (q == 1 ? t1 : (q == 2 ? t2 : t3));
 }
 
 // A key list in registers: lane l holds entries l, l + 64, ... (P per lane; absent entries are 0,
@@ -149,51 +156,25 @@ __device__ __forceinline__ uint32_t keys_kth_largest(const KeyRegs<P>& r, int K,
   return (uint32_t)lo;
 }
 
-template <int P>
-__device__ __forceinline__ uint32_t wave_kth_largest(const uint32_t* keys, int n, int K, int* n_above,
-                                                     uint32_t* hist) {
-  KeyRegs<P> r;
-  keys_load(r, keys, n);
-  return keys_kth_largest(r, K, n_above, hist);
-}
-
-// Trim a key list to the multiset of its K largest keys (K < n); returns the K-th largest key.
-template <int P>
-__device__ __forceinline__ uint32_t wave_trim_keys(uint32_t* keys, int n, int K, uint32_t* hist) {
-  KeyRegs<P> r;
-  keys_load(r, keys, n);
-  int above;
-  const uint32_t tau = keys_kth_largest(r, K, &above, hist);
-  const int l = lane_id();
-  const uint64_t lt = lanemask_lt();
-  int wr = 0;
-#pragma unroll
-  for (int j = 0; j < P; ++j) {
-    const bool keep = r.k[j] > tau;
-    const uint64_t m = ballot(keep);
-    if (keep) keys[wr + popc64(m & lt)] = r.k[j];
-    wr += popc64(m);
-  }
-  for (int e = wr + l; e < K; e += 64) keys[e] = tau;  // the tied keys that stay
-  lds_wait();
-  (void)above;
-  return tau;
-}
-
 }  // namespace
 
 // Row = (i, g) flattened as i*G + g (largest rows first); candidates [0, c(i)); output the
 // ascending ids into topk [G][N][K_B] (-1 padded).
+//
+// LDS: the double-buffered stage, then per row a region A of kb + kSideCap words (the sample keys
+// of pass 0, later the row's output list) and a region B of 256 words (the histogram of pass 1,
+// the scratch of a list select, later the keys of the threshold bucket's members), kListPad words
+// apart.
 template <int WAVES, int P>
 __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restrict__ qi, const float* __restrict__ w,
                                                        const uint16_t* __restrict__ kbar,
                                                        int32_t* __restrict__ topk, int n_tokens, int n_groups,
-                                                       int block, int kb, int cap) {
+                                                       int block, int kb) {
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* stage = smem;                                                        // 2 x kStageBytes
-  uint32_t* keys_all = reinterpret_cast<uint32_t*>(smem + 2 * kStageBytes);     // 4*WAVES x cap
-  const int lstride = cap + kListPad;                                          // words per row list
-  uint32_t* hist = keys_all + (size_t)WAVES * 4 * lstride + (threadIdx.x >> 6) * 256;  // this wave's 256 words
+  const int out_cap = (kb + 3) / 4 * 4 + kSideCap;                             // region A words
+  const int rstride = out_cap + 256 + kListPad;                                // words per row
+  uint32_t* rows_lds = reinterpret_cast<uint32_t*>(smem + 2 * kStageBytes);
 
   constexpr int kRowsPerWg = WAVES * 4;
   const int wave = threadIdx.x >> 6;
@@ -340,199 +321,310 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
   };
   const int n_all = hi_all - lo;
 
-  uint32_t* my_keys = keys_all + (size_t)(wave * 4 + quarter) * lstride;
-  int n_cnt = 0;            // keys in this lane's row list (uniform over the quarter)
-  float accept = kNegInf;   // scores >= accept are kept
-  // Keys of the scores >= accept join the row's list (any order); positions from a prefix count
-  // over the row's 16 lanes.
-  int s_n_virt = 0, s_stride = 1, s_off = 0;  // the current stream's candidate mapping
-  auto append = [&](const float (&sc)[kTiles], int v_first, auto full_t) {
+  uint32_t* my_a = rows_lds + (size_t)(wave * 4 + quarter) * rstride;  // this lane's row: region A
+  uint32_t* my_b = my_a + out_cap;                                       // region B
+  auto row_a = [&](int q) { return rows_lds + (size_t)(wave * 4 + q) * rstride; };
+  auto row_b = [&](int q) { return rows_lds + (size_t)(wave * 4 + q) * rstride + out_cap; };
+
+  // ------------------------------------------------------------------ pass 0: sample
+  // Every row's candidates, or a strided sample of them when there are more than sample_cap, go
+  // into region A. A complete list gives the exact K_B-th key at once; a sample gives the range
+  // for the histogram of pass 1.
+  const int sample_cap = min(512, out_cap) / 64 * 64;
+  const int stride = n_all > sample_cap ? (n_all + sample_cap - 1) / sample_cap : 1;
+  const int s_off = stride / 2;
+  const int s_virt = (n_all - s_off + stride - 1) / stride;
+  int n_cnt = 0;  // keys listed for this lane's row (uniform over the quarter)
+  auto append_all = [&](const float (&sc)[kTiles], int v_first, auto full_t) {
     constexpr bool kFull = decltype(full_t)::value;
-    uint32_t pm = 0;  // bit ct: candidate v_first + ct passes
+    uint32_t pm = 0;
 #pragma unroll
-    for (int ct = 0; ct < kTiles; ++ct) {
-      const bool ok = kFull || valid_at(v_first + ct, s_n_virt, s_stride, s_off);
-      pm |= (ok && sc[ct] >= accept) ? (1u << ct) : 0u;
-    }
+    for (int ct = 0; ct < kTiles; ++ct)
+      pm |= (kFull || valid_at(v_first + ct, s_virt, stride, s_off)) ? (1u << ct) : 0u;
     if (!ballot(pm != 0u)) return;
     const uint32_t cnt = __popc(pm);
     const uint32_t incl = row16_prefix(cnt);
-    const uint32_t total = __shfl(incl, l | 15, 64);
+    const uint32_t total = row16_total(incl);
     uint32_t pos = n_cnt + incl - cnt;
 #pragma unroll
     for (int ct = 0; ct < kTiles; ++ct)
-      if (pm & (1u << ct)) my_keys[pos++] = score_key(sc[ct]);
+      if (pm & (1u << ct)) my_a[pos++] = score_key(sc[ct]);
     n_cnt += total;
-  };
-  auto trim_full = [&]() {  // trim the rows whose list could overflow on the next chunk
-    const uint64_t need_m = ballot(n_cnt + kChunk > cap);
-    if (need_m) {
-      lds_wait();
-      for (int q = 0; q < 4; ++q) {
-        if ((need_m >> (16 * q)) & 1ull) {
-          const int nq = readlane(n_cnt, 16 * q);
-          const uint32_t tau = wave_trim_keys<P>(keys_all + (size_t)(wave * 4 + q) * lstride, nq, kb, hist);
-          if (quarter == q) {
-            n_cnt = kb;
-            accept = key_to_score(tau);
-          }
-        }
-      }
-    }
   };
   auto nothing = [&]() {};
 
-  // ------------------------------------------------------------------ pass 0: starting threshold
-  // A strided sample of every row's candidates gives a conservative estimate of the K_B-th score:
-  // the sample quantile at which about 2*K_B candidates are expected above. It only sets where
-  // pass 1 starts keeping keys; a row whose estimate turns out too high is rescanned from -inf.
-  const int sample_max = min(512, cap - kChunk);
-  const int stride = n_all > 2 * kb ? (n_all + sample_max - 1) / sample_max : 0;
-  if (stride > 1) {
-    const int n_virt = (n_all - stride / 2 + stride - 1) / stride;
-    s_n_virt = n_virt;
-    s_stride = stride;
-    s_off = stride / 2;
-    stream(n_virt, stride, stride / 2, append, nothing);
-    lds_wait();
-    float est = kNegInf;
-    for (int q = 0; q < 4; ++q) {
-      const int nq = readlane(n_cnt, 16 * q);     // samples of row q
-      const int cq = readlane(n_cand, 16 * q);    // candidates of row q
-      const int ks = cq > 0 ? (int)(((long long)2 * kb * nq + cq - 1) / cq) : 0;
-      if (cq > 2 * kb && ks >= 1 && ks < nq) {
-        int above;
-        const uint32_t t = wave_kth_largest<P>(keys_all + (size_t)(wave * 4 + q) * lstride, nq, ks, &above, hist);
-        if (quarter == q) est = key_to_score(t);
-      }
-    }
-    accept = est;
-    n_cnt = 0;
-  }
+  // Row state (uniform over the row's 16 lanes). Modes: every candidate selected; ties (keys above
+  // t_hi selected, the first `take` keys equal to t_lo = t_hi in block order too); bucket (keys
+  // above t_hi selected, keys in [t_lo, t_hi] listed for an exact select after the emit pass);
+  // histogram (the threshold bucket is not narrow enough yet).
+  enum { kAll = 0, kTies = 1, kBucket = 2, kHist = 3 };
+  int mode = kAll;
+  uint32_t t_lo = 1u, t_hi = 0u;
+  int take = 0;                 // kTies: equal keys to take; kBucket / kHist: keys still to select
+  uint32_t h_lo = 0u, h_hi = 0xFFFFFFFFu;  // kHist: keys in [h_lo, h_hi] are bucketed ...
+  int h_shift = 0;              // ... into bucket (key - h_lo) >> h_shift
+  bool h_open = false;          // ... except that with an open range bucket 255 takes every key above
 
-  // ------------------------------------------------------------------ pass 1: tau and ties
-  s_n_virt = n_all;
-  s_stride = 1;
-  s_off = 0;
-  stream(n_all, 1, 0, append, trim_full);
+  stream(s_virt, stride, s_off, append_all, nothing);
   lds_wait();
-  // A row whose starting threshold was above its K_B-th score kept fewer than K_B keys: rescan
-  // those rows from -inf (the other rows keep their lists and take nothing new).
-  {
-    __shared__ int redo;
-    if (threadIdx.x == 0) redo = 0;
-    __syncthreads();
-    const bool failed = n_cand > kb && n_cnt < kb;
-    if (ballot(failed) && l == 0) redo = 1;
-    __syncthreads();
-    if (redo) {
-      if (failed) {
-        n_cnt = 0;
-        accept = kNegInf;
-      } else {
-        accept = __builtin_huge_valf();
-      }
-      stream(n_all, 1, 0, append, trim_full);
-      lds_wait();
-    }
-  }
-  // Exact threshold per row: select everything when the row has at most K_B candidates.
-  float tau_f = kNegInf;
-  int ties = 0;
   for (int q = 0; q < 4; ++q) {
     const int nq = readlane(n_cnt, 16 * q);
     const int cq = readlane(n_cand, 16 * q);
-    if (cq > kb) {
+    if (cq <= kb) continue;  // every candidate is selected
+    uint32_t* ka = row_a(q);
+    KeyRegs<8> r;
+    keys_load(r, ka, nq);
+    if (stride == 1) {  // complete list: the exact K_B-th key and its ties
       int above;
-      const uint32_t tau = wave_kth_largest<P>(keys_all + (size_t)(wave * 4 + q) * lstride, nq, kb, &above, hist);
+      const uint32_t tau = keys_kth_largest(r, kb, &above, row_b(q));
       if (quarter == q) {
-        tau_f = key_to_score(tau);
-        ties = kb - above;
+        mode = kTies;
+        t_lo = t_hi = tau;
+        take = kb - above;
+      }
+    } else {
+      // Histogram range: from the sample key with about 4 K_B candidates expected at or above it
+      // (the lowest sample key if that is more than the sample) up to the largest sample key.
+      int ks = (int)(((long long)4 * kb * nq + cq - 1) / cq);
+      ks = ks < 1 ? 1 : (ks > nq ? nq : ks);
+      int above;
+      const uint32_t lo_k = keys_kth_largest(r, ks, &above, row_b(q));
+      uint32_t mx = 0u;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mx = max(mx, r.k[j]);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
+      const uint64_t width = (uint64_t)mx - lo_k + 1;
+      const int bits = 64 - __clzll((long long)(width - 1 | 1));
+      if (quarter == q) {
+        mode = kHist;
+        take = kb;
+        h_lo = lo_k;
+        h_hi = 0xFFFFFFFFu;
+        h_open = true;
+        h_shift = bits > 8 ? bits - 8 : 0;
+      }
+    }
+  }
+
+  // ------------------------------------------------------------------ pass 1: histograms
+  // Rows still in histogram mode count their keys in [h_lo, h_hi] per bucket (LDS atomics into
+  // region B), then move to the bucket that holds their K_B-th key: a one-key bucket gives the
+  // exact threshold (ties mode), a bucket of at most kSideCap keys is listed in the emit pass
+  // (bucket mode), a larger one is histogrammed again on a 256 times finer scale.
+  __shared__ int any_hist;
+  for (;;) {
+    if (threadIdx.x == 0) any_hist = 0;
+    __syncthreads();
+    if (ballot(mode == kHist) && l == 0) any_hist = 1;
+    __syncthreads();
+    if (!any_hist) break;
+    if (mode == kHist) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(my_b + 64 * j + 4 * l16) = z;
+    }
+    const bool hist_row = mode == kHist;
+    auto count = [&](const float (&sc)[kTiles], int v_first, auto full_t) {
+      constexpr bool kFull = decltype(full_t)::value;
+      if (!ballot(hist_row)) return;
+#pragma unroll
+      for (int ct = 0; ct < kTiles; ++ct) {
+        const uint32_t key = score_key(sc[ct]);
+        const bool ok = hist_row && (kFull || valid_at(v_first + ct, n_all, 1, 0)) && key >= h_lo && key <= h_hi;
+        if (ok) {
+          uint32_t bk = (key - h_lo) >> h_shift;
+          bk = bk > 255u ? 255u : bk;
+          atomicAdd(&my_b[bk], 1u);
+        }
+      }
+    };
+    stream(n_all, 1, 0, count, nothing);
+    lds_wait();
+    for (int q = 0; q < 4; ++q) {
+      if (readlane((int)(mode == kHist), 16 * q) == 0) continue;
+      const int need = readlane(take, 16 * q);
+      const uint32_t lo_q = readlane(h_lo, 16 * q), hi_q = readlane(h_hi, 16 * q);
+      const int sh_q = readlane(h_shift, 16 * q);
+      const bool open_q = readlane((int)h_open, 16 * q) != 0;
+      const u32x4 hv = *reinterpret_cast<const u32x4*>(row_b(q) + 4 * l);
+      const uint32_t local = hv[0] + hv[1] + hv[2] + hv[3];
+      const uint32_t above = wave_suffix_sum(local) - local;  // keys in buckets >= 4l + 4
+      const uint32_t s3 = above + hv[3], s2 = s3 + hv[2], s1 = s2 + hv[1], s0 = s1 + hv[0];
+      const uint64_t m = ballot(s0 >= (uint32_t)need);
+      if (m == 0) {
+        // Fewer than `need` keys in the range. On the first histogram the sampled lower end was too
+        // high: count every key >= 1 on a coarse scale next time. When that range already held
+        // every key >= 1, the remaining keys are 0 (only a NaN score maps there): the K_B-th key is
+        // 0 and the first (need - count) of them in block order complete the selection.
+        const bool full_range = lo_q == 1u && hi_q == 0xFFFFFFFFu && !open_q;
+        const int in_range = (int)readlane(s0, 0);
+        if (quarter == q) {
+          if (full_range) {
+            mode = kTies;
+            t_lo = t_hi = 0u;
+            take = need - in_range;
+          } else {
+            h_lo = 1u;
+            h_hi = 0xFFFFFFFFu;
+            h_open = false;
+            h_shift = 24;
+          }
+        }
+        continue;
+      }
+      const int ls = 63 - __clzll((long long)m);
+      const int j = s3 >= (uint32_t)need ? 3 : (s2 >= (uint32_t)need ? 2 : (s1 >= (uint32_t)need ? 1 : 0));
+      const uint32_t s_next = j == 3 ? above : (j == 2 ? s3 : (j == 1 ? s2 : s1));
+      const uint32_t in_b = j == 3 ? hv[3] : (j == 2 ? hv[2] : (j == 1 ? hv[1] : hv[0]));
+      const int bsel = readlane(4 * l + j, ls);
+      const int need2 = need - (int)readlane(s_next, ls);  // keys still to select inside the bucket
+      const int cnt_b = (int)readlane(in_b, ls);
+      const uint64_t b_lo = (uint64_t)lo_q + ((uint64_t)bsel << sh_q);
+      uint64_t b_hi = (open_q && bsel == 255) ? 0xFFFFFFFFull : b_lo + (1ull << sh_q) - 1;
+      if (b_hi > hi_q) b_hi = hi_q;
+      if (quarter == q) {
+        take = need2;
+        if (b_hi == b_lo) {
+          mode = kTies;
+          t_lo = t_hi = (uint32_t)b_lo;
+        } else if (cnt_b <= kSideCap) {
+          mode = kBucket;
+          t_lo = (uint32_t)b_lo;
+          t_hi = (uint32_t)b_hi;
+        } else {
+          const uint64_t width = b_hi - b_lo + 1;
+          const int bits = 64 - __clzll((long long)(width - 1));
+          h_lo = (uint32_t)b_lo;
+          h_hi = (uint32_t)b_hi;
+          h_open = false;
+          h_shift = bits > 8 ? bits - 8 : 0;
+        }
       }
     }
   }
 
   // ------------------------------------------------------------------ pass 2: emit in order
-  int n_out = 0, t_seen = 0;  // uniform over the quarter
-  // The selection is staged in the row's (now unused) key list and written out at the end: global
-  // stores inside the loop would make every chunk's vmcnt wait for them as well.
-  int32_t* out_row = valid_o ? topk + ((long long)g_o * n_tokens + row_o / n_groups) * kb : nullptr;
-  int32_t* sel_lds = reinterpret_cast<int32_t*>(my_keys);
-  // Candidates above tau, and the first `ties` equal to tau, in ascending block order: this lane's
-  // 8 candidates follow those of lanes with a lower l % 16 in the same row.
+  // In block order, every candidate above t_hi, and the candidates in [t_lo, t_hi]: in ties mode the
+  // first `take` of them, in bucket mode all of them, flagged (bit 31) in the output list with their
+  // keys listed in region B, to be decided once the bucket's exact threshold is known.
+  const bool all_row = mode == kAll;
+  const bool bucket_row = mode == kBucket;
+  int n_out = 0, t_seen = 0, n_side = 0;  // uniform over the quarter
+  int32_t* out_a = reinterpret_cast<int32_t*>(my_a);
   auto emit = [&](const float (&sc)[kTiles], int v_first, auto full_t) {
     constexpr bool kFull = decltype(full_t)::value;
     uint32_t gm = 0, em = 0;
+    uint32_t keys[kTiles];
 #pragma unroll
     for (int ct = 0; ct < kTiles; ++ct) {
       const bool ok = kFull || valid_at(v_first + ct, n_all, 1, 0);
-      gm |= (ok && sc[ct] > tau_f) ? (1u << ct) : 0u;
-      em |= (ok && sc[ct] == tau_f) ? (1u << ct) : 0u;
+      keys[ct] = score_key(sc[ct]);
+      gm |= (ok && (all_row || keys[ct] > t_hi)) ? (1u << ct) : 0u;
+      em |= (ok && !all_row && keys[ct] >= t_lo && keys[ct] <= t_hi) ? (1u << ct) : 0u;
     }
     if (!ballot((gm | em) != 0u)) return;
     const uint32_t ng = __popc(gm), ne = __popc(em);
     const uint32_t incl = row16_prefix(ng | (ne << 16));  // row totals <= 128 each
-    const uint32_t total = __shfl(incl, l | 15, 64);
+    const uint32_t total = row16_total(incl);
     const int g_before = (int)((incl & 0xFFFFu) - ng), e_before = (int)((incl >> 16) - ne);
-    const int rem = max(0, ties - t_seen);  // ties still to take
+    const int rem = bucket_row ? 0x7FFFFFFF : max(0, take - t_seen);  // members still to take
+    // This lane takes its first min(ne, rem - e_before) members (all of them in bucket mode).
+    const int k_take = min((int)ne, max(0, rem - e_before));
+    uint32_t et = 0u;
+    for (uint32_t t = em, j = 0; j < (uint32_t)k_take; ++j) {
+      et |= t & (0u - t);
+      t &= t - 1u;
+    }
+    uint32_t sm = gm | et;
     int pos = n_out + g_before + min(e_before, rem);
-    int e_rank = e_before;
+    int side = n_side + e_before;
+    // Taken candidates in ascending order; the loop runs as often as the busiest lane takes one.
+    while (sm) {
+      const int ct = __builtin_ctz(sm);
+      sm &= sm - 1u;
+      const bool flag = bucket_row && ((em >> ct) & 1u);
+      out_a[pos++] = (lo + v_first + ct) | (flag ? (int)0x80000000u : 0);
+      if (flag) {
+        uint32_t key = keys[0];
 #pragma unroll
-    for (int ct = 0; ct < kTiles; ++ct) {
-      if (gm & (1u << ct)) {
-        sel_lds[pos++] = lo + v_first + ct;
-      } else if (em & (1u << ct)) {
-        if (e_rank < rem) sel_lds[pos++] = lo + v_first + ct;
-        ++e_rank;
+        for (int j = 1; j < kTiles; ++j) key = ct == j ? keys[j] : key;
+        my_b[side++] = key;
       }
     }
-    n_out += (int)(total & 0xFFFFu) + min((int)(total >> 16), rem);
-    t_seen += (int)(total >> 16);
+    const int tot_e = (int)(total >> 16);
+    n_out += (int)(total & 0xFFFFu) + min(tot_e, rem);
+    t_seen += tot_e;
+    n_side += bucket_row ? tot_e : 0;
   };
   stream(n_all, 1, 0, emit, nothing);
   lds_wait();
-  if (valid_o)
-    for (int e = l16; e < kb; e += 16) out_row[e] = e < n_out ? sel_lds[e] : -1;
+
+  // ------------------------------------------------------------------ output
+  // Bucket rows: the exact threshold tau among the listed bucket keys (binary search on the key,
+  // counting with ballots), then the flagged entries with key > tau and the first (need - above)
+  // with key == tau stay. Every row is written out in order, -1 padded.
+  for (int q = 0; q < 4; ++q) {
+    const long long row = r0 + wave * 4 + q;
+    if (row >= n_rows) break;
+    const int i = (int)(row / n_groups), g = (int)(row % n_groups);
+    int32_t* out = topk + ((long long)g * n_tokens + i) * kb;
+    const int32_t* list = reinterpret_cast<const int32_t*>(row_a(q));
+    const int nq = readlane(n_out, 16 * q);
+    if (readlane((int)bucket_row, 16 * q) == 0) {
+      for (int e = l; e < kb; e += 64) out[e] = e < nq ? list[e] : -1;
+      continue;
+    }
+    const uint32_t* sk = row_b(q);
+    const int ns = readlane(n_side, 16 * q);
+    const int need = readlane(take, 16 * q);
+    KeyRegs<kSideCap / 64> r;
+    keys_load(r, sk, ns);
+    // tau = the largest t with count(keys >= t) >= need.
+    uint32_t tau = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t t = tau | (1u << bit);
+      if (keys_count_ge(r, t) >= need) tau = t;
+    }
+    const int ties = need - keys_count_ge(r, tau + 1u);  // tau < 2^32 - 1: a listed key is above it
+    int wr = 0, j_side = 0, t_cnt = 0;
+    for (int e0 = 0; e0 < nq; e0 += 64) {
+      const int e = e0 + l;
+      const int32_t v = e < nq ? list[e] : 0;
+      const bool flagged = e < nq && v < 0;
+      const uint64_t fm = ballot(flagged);
+      const int js = j_side + popc64(fm & lanemask_lt());
+      const uint32_t key = flagged ? sk[js] : 0u;
+      const bool tie = flagged && key == tau;
+      const uint64_t tm = ballot(tie);
+      const int tr = t_cnt + popc64(tm & lanemask_lt());
+      const bool keep = e < nq && (!flagged || key > tau || (tie && tr < ties));
+      const uint64_t km = ballot(keep);
+      if (keep) out[wr + popc64(km & lanemask_lt())] = v & 0x7FFFFFFF;
+      wr += popc64(km);
+      j_side += popc64(fm);
+      t_cnt += popc64(tm);
+    }
+    for (int e = wr + l; e < kb; e += 64) out[e] = -1;
+  }
 }
 
 namespace {
 
-// Stage buffers, the rows' key lists and one 256-word histogram per wave.
-size_t select_lds_bytes(int waves, int cap) {
-  return (size_t)2 * kStageBytes + (size_t)waves * 4 * (cap + kListPad) * 4 + (size_t)waves * 1024;
+// Stage buffers and the per-row regions.
+size_t select_lds_bytes(int waves, int kb) {
+  return (size_t)2 * kStageBytes + (size_t)waves * 4 * ((kb + 3) / 4 * 4 + kSideCap + 256 + kListPad) * 4;
 }
-
-// Largest list capacity (multiple of 64) that fits `waves` in the LDS budget, capped at a size
-// where trims are rare; 0 below the minimum (K_B plus one chunk of appends plus slack).
-int select_cap(int waves, int kb, size_t lds_budget) {
-  const long long avail = (long long)lds_budget - 2LL * kStageBytes - 256 - waves * 1024LL;  // 256 B: static LDS
-  if (avail <= 0) return 0;
-  int cap = (int)(avail / ((long long)waves * 4 * 4) - kListPad) / 64 * 64;
-  const int need = kb + kChunk + 64;
-  const int enough = ((4 * kb + kChunk > need ? 4 * kb + kChunk : need) + 63) / 64 * 64;
-  if (cap > enough) cap = enough;
-  if (cap > 4096) cap = 4096;  // trims hold at most 64 keys per lane in registers
-  // Prefer the smaller register footprint when it still leaves room for K_B + a chunk or more.
-  if (cap > 1024 && 1024 >= 2 * kb + kChunk) cap = 1024;
-  if (cap > 2048 && 2048 >= 2 * kb + kChunk) cap = 2048;
-  return cap >= need ? cap : 0;
-}
-
-// Keys per lane a trim holds in registers for a list capacity.
-int keys_per_lane(int cap) { return cap <= 1024 ? 16 : (cap <= 2048 ? 32 : 64); }
 
 int prefill_waves(int kb, size_t lds_budget) {
   for (int wv = 8; wv >= 1; wv >>= 1)
-    if (select_cap(wv, kb, lds_budget) > 0) return wv;
+    if (select_lds_bytes(wv, kb) + 256 <= lds_budget) return wv;  // 256 B: static LDS
   return 0;
 }
 
 }  // namespace
 
-size_t index_topk_lds_min(int kb) {
-  const int cap = select_cap(1, kb, kGfx950LdsBytes);
-  return cap > 0 ? select_lds_bytes(1, cap) : kGfx950LdsBytes + 1;
-}
+size_t index_topk_lds_min(int kb) { return select_lds_bytes(1, kb) + 256; }
 
 hipError_t launch_index_topk(const uint16_t* qi, const float* w, const uint16_t* kbar, int32_t* topk, int n_tokens,
                              int n_groups, int block, int kb, hipStream_t stream) {
@@ -540,33 +632,26 @@ hipError_t launch_index_topk(const uint16_t* qi, const float* w, const uint16_t*
   if (n_rows == 0) return hipSuccess;
   const size_t budget = (size_t)max_lds_per_block() / SGQA_TOPK_WGS_PER_CU;
 #ifdef SGQA_TOPK_WAVES
-  const int waves = select_cap(SGQA_TOPK_WAVES, kb, budget) > 0 ? SGQA_TOPK_WAVES : 0;
+  const int waves = select_lds_bytes(SGQA_TOPK_WAVES, kb) + 256 <= budget ? SGQA_TOPK_WAVES : 0;
 #else
   const int waves = prefill_waves(kb, budget);
 #endif
   if (waves == 0) return hipErrorInvalidValue;
-  const int cap = select_cap(waves, kb, budget);
-  const size_t lds = select_lds_bytes(waves, cap);
+  const size_t lds = select_lds_bytes(waves, kb);
   const long long grid = (n_rows + waves * 4 - 1) / (waves * 4);
-  const int pk = keys_per_lane(cap);
-#define SGQA_TOPK_CASE(WV, PK)                                                                                   \
-  if (waves == WV && pk == PK) {                                                                                 \
-    hipError_t e = hipFuncSetAttribute((const void*)k_select<WV, PK>,                                     \
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                    \
+#define SGQA_TOPK_CASE(WV)                                                                                       \
+  if (waves == WV) {                                                                                             \
+    hipError_t e = hipFuncSetAttribute((const void*)k_select<WV, 8>, hipFuncAttributeMaxDynamicSharedMemorySize,  \
+                                       (int)lds);                                                                \
     if (e != hipSuccess) return e;                                                                               \
-    hipLaunchKernelGGL((k_select<WV, PK>), dim3((unsigned)grid), dim3(WV * 64), lds, stream, qi, w, kbar,       \
-                       topk, n_tokens, n_groups, block, kb, cap);                                                 \
+    hipLaunchKernelGGL((k_select<WV, 8>), dim3((unsigned)grid), dim3(WV * 64), lds, stream, qi, w, kbar, topk,    \
+                       n_tokens, n_groups, block, kb);                                                           \
     return hipGetLastError();                                                                                    \
   }
-  SGQA_TOPK_CASE(8, 16)
-  SGQA_TOPK_CASE(4, 16)
-  SGQA_TOPK_CASE(4, 32)
-  SGQA_TOPK_CASE(2, 16)
-  SGQA_TOPK_CASE(2, 32)
-  SGQA_TOPK_CASE(2, 64)
-  SGQA_TOPK_CASE(1, 16)
-  SGQA_TOPK_CASE(1, 32)
-  SGQA_TOPK_CASE(1, 64)
+  SGQA_TOPK_CASE(8)
+  SGQA_TOPK_CASE(4)
+  SGQA_TOPK_CASE(2)
+  SGQA_TOPK_CASE(1)
 #undef SGQA_TOPK_CASE
   return hipErrorInvalidValue;
 }
