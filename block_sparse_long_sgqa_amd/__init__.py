@@ -37,7 +37,7 @@ SGQA_OP_DECODE = 5
 # Every symbol include/sgqa.h declares.
 EXPORTED = ("sgqa_abi_version", "sgqa_status_string", "sgqa_workspace_size", "sgqa_compress", "sgqa_index_topk",
             "sgqa_union", "sgqa_attend", "sgqa_prefill", "sgqa_decode", "sgqa_decode_varlen", "sgqa_append",
-            "sgqa_decode_fp8")
+            "sgqa_decode_fp8", "sgqa_index_union")
 
 
 class sgqa_pages(ctypes.Structure):
@@ -135,8 +135,9 @@ def lib() -> ctypes.CDLL:
         L.sgqa_decode_varlen.argtypes = [PP, P, P, P, PG, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.sgqa_append.argtypes = [PP, P, P, P, P, P, P, PG, P, P, P]
         L.sgqa_decode_fp8.argtypes = [PP, P, P, P, P, PG, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.sgqa_index_union.argtypes = [PP, P, P, P, P, P, P, ctypes.c_size_t, P]
         for name in ("sgqa_compress", "sgqa_index_topk", "sgqa_union", "sgqa_attend", "sgqa_prefill", "sgqa_decode",
-                     "sgqa_decode_varlen", "sgqa_append", "sgqa_decode_fp8"):
+                     "sgqa_decode_varlen", "sgqa_append", "sgqa_decode_fp8", "sgqa_index_union"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -213,6 +214,18 @@ def sgqa_union(p: Params, topk, umask, ucount, stream=None) -> None:
             _ptr(umask, "umask", torch.int32, (G, p.n_tiles, p.n_words)),
             _ptr(ucount, "ucount", torch.int32, (G, p.n_tiles)))
     _check(lib().sgqa_union(ctypes.byref(p.c()), *args, _stream(stream)), "sgqa_union")
+
+
+def sgqa_index_union(p: Params, idx_q, idx_w, blk_k, umask, ucount, ws=None, stream=None) -> None:
+    N, G = p.n_tokens, p.n_kv_heads
+    args = (_ptr(idx_q, "idx_q", torch.bfloat16, (N, G, p.idx_heads, p.idx_dim)),
+            _ptr(idx_w, "idx_w", torch.float32, (G, p.idx_heads)),
+            _ptr(blk_k, "blk_k", torch.bfloat16, (N // p.block, p.idx_dim)),
+            _ptr(umask, "umask", torch.int32, (G, p.n_tiles, p.n_words)),
+            _ptr(ucount, "ucount", torch.int32, (G, p.n_tiles)))
+    wsp = _ptr(ws, "ws", torch.uint8)
+    _check(lib().sgqa_index_union(ctypes.byref(p.c()), *args, wsp, ws.numel() if ws is not None else 0,
+                                  _stream(stream)), "sgqa_index_union")
 
 
 def sgqa_attend(p: Params, q, k, v, umask, ucount, out, ws=None, stream=None) -> None:

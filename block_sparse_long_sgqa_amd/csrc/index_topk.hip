@@ -9,8 +9,8 @@
 // Sel(i,g) = the first min(K_B, c(i)) candidates in the order (s descending, b ascending).
 //
 // Design (gfx950)
-//  * A workgroup owns 4*WAVES consecutive rows (4 per wave). One 16x16x32 bf16 MFMA takes
-//    A = (4 rows x 4 indexer heads) x 32 dims and B = 32 dims x 16 blocks; after the two K-steps
+//  * A workgroup owns 4*WAVES rows (4 per wave): one group, consecutive queries. One 16x16x32
+//    bf16 MFMA takes A = (4 rows x 4 indexer heads) x 32 dims and B = 32 dims x 16 blocks; after the two K-steps
 //    of d_I = 64 every lane holds the 4 head dots of one (row, block) pair and forms the score
 //    locally (ReLU, weights, head sum): no cross-lane traffic, no score matrix in memory.
 //  * Block keys stream through LDS in chunks of 128 blocks, gathered with global_load_lds into
@@ -158,18 +158,24 @@ __device__ __forceinline__ uint32_t keys_kth_largest(const KeyRegs<P>& r, int K,
 
 }  // namespace
 
-// Row = (i, g) flattened as i*G + g (largest rows first); candidates [0, c(i)); output the
-// ascending ids into topk [G][N][K_B] (-1 padded).
+// A workgroup owns the rows (i, g) of one group g and 4*WAVES consecutive queries i (the heaviest
+// query ranges are launched first); candidates [0, c(i)); output the ascending ids into
+// topk [G][N][K_B] (-1 padded).
 //
 // LDS: the double-buffered stage, then per row a region A of kb + kSideCap words (the sample keys
 // of pass 0, later the row's output list) and a region B of 256 words (the histogram of pass 1,
 // the scratch of a list select, later the keys of the threshold bucket's members), kListPad words
 // apart.
-template <int WAVES, int P>
+//
+// UNION: instead of writing topk, every selected id and the row's own block are ORed into the
+// tile-union bitmask umask [G][T][W] (bit b % 32 of word b / 32 of row (g, floor(i / tile))), which
+// the caller has zeroed: the fused index -> union path that never materialises topk.
+template <int WAVES, int P, bool UNION>
 __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restrict__ qi, const float* __restrict__ w,
                                                        const uint16_t* __restrict__ kbar,
                                                        int32_t* __restrict__ topk, int n_tokens, int n_groups,
-                                                       int block, int kb) {
+                                                       int block, int kb, uint32_t* __restrict__ umask, int tile,
+                                                       int n_tiles, int n_words) {
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* stage = smem;                                                        // 2 x kStageBytes
   const int out_cap = (kb + 3) / 4 * 4 + kSideCap;                             // region A words
@@ -182,34 +188,42 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
   const int quarter = l >> 4;
   const int l16 = l & 15;
 
-  const long long wg = (long long)gridDim.x - 1 - blockIdx.x;  // largest rows first
-  const long long r0 = wg * kRowsPerWg;
-  const long long n_rows = (long long)n_tokens * n_groups;
-  const long long r_last = (r0 + kRowsPerWg - 1 < n_rows) ? r0 + kRowsPerWg - 1 : n_rows - 1;
+  // Workgroup = (group g, queries i0 .. i0 + 4*WAVES - 1), the heaviest query ranges first; the
+  // row of lane quarter q of wave w is query i0 + 4w + q.
+  const long long wg = (long long)gridDim.x - 1 - blockIdx.x;
+  const int g_wg = (int)(wg % n_groups);
+  const int i0 = (int)(wg / n_groups) * kRowsPerWg;
+  const int i_last = min(i0 + kRowsPerWg, n_tokens) - 1;
   const int lo = 0;
-  const int hi_all = (int)(r_last / n_groups) / block;  // the last row has the most candidates
+  const int hi_all = i_last / block;  // the last row has the most candidates
   const int n_blocks = n_tokens / block;
 
-  auto row_group = [&](long long row) -> int { return (int)(row % n_groups); };
-  auto row_qi = [&](long long row) -> long long { return row; };
-  auto row_hi = [&](long long row) -> int { return (int)(row / n_groups) / block; };
-
-  // The row whose scores this lane produces: row `quarter` of the wave.
-  const long long row_o = r0 + wave * 4 + quarter;
-  const bool valid_o = row_o < n_rows;
-  const int g_o = valid_o ? row_group(row_o) : 0;
-  const int hi_lane = valid_o ? row_hi(row_o) : 0;
+  const int i_o = i0 + wave * 4 + quarter;
+  const bool valid_o = i_o < n_tokens;
+  const int g_o = g_wg;
+  const int hi_lane = valid_o ? i_o / block : 0;
   const int n_cand = max(0, hi_lane - lo);  // candidates of this lane's row
 
+  // The union mask row of (i, g).
+  auto mask_row = [&](int i, int g) -> uint32_t* {
+    return umask + ((long long)g * n_tiles + i / tile) * n_words;
+  };
   if (hi_all <= kb) {
     // Every row has at most K_B candidates: all of them are selected.
     for (int q = 0; q < 4; ++q) {
-      const long long row = r0 + wave * 4 + q;
-      if (row >= n_rows) break;
-      const int i = (int)(row / n_groups), g = (int)(row % n_groups);
+      const int i = i0 + wave * 4 + q, g = g_wg;
+      if (i >= n_tokens) break;
       const int c = i / block;
-      int32_t* out = topk + ((long long)g * n_tokens + i) * kb;
-      for (int e = l; e < kb; e += 64) out[e] = e < c ? e : -1;
+      if constexpr (UNION) {  // blocks 0 .. c: the selection and the own block, a word at a time
+        uint32_t* m = mask_row(i, g);
+        for (int wd = l; wd <= (c >> 5); wd += 64) {
+          const int hi_bit = c - 32 * wd;  // bits 0 .. hi_bit of this word
+          atomicOr(&m[wd], hi_bit >= 31 ? 0xFFFFFFFFu : ((2u << hi_bit) - 1u));
+        }
+      } else {
+        int32_t* out = topk + ((long long)g * n_tokens + i) * kb;
+        for (int e = l; e < kb; e += 64) out[e] = e < c ? e : -1;
+      }
     }
     return;
   }
@@ -217,10 +231,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
   // A operand: row (l16 / 4) of this wave, head (l16 % 4), dims 8*quarter + 32*ks.
   bf16x8 a_op[2];
   {
-    const long long row_a = r0 + wave * 4 + (l16 >> 2);
+    const int ia = i0 + wave * 4 + (l16 >> 2);
     const int head = l16 & 3;
-    if (row_a < n_rows) {
-      const uint16_t* src = qi + (row_qi(row_a) * kIdxHeads + head) * kIdxDim + 8 * quarter;
+    if (ia < n_tokens) {
+      const uint16_t* src = qi + (((long long)ia * n_groups + g_wg) * kIdxHeads + head) * kIdxDim + 8 * quarter;
       a_op[0] = *reinterpret_cast<const bf16x8*>(src);
       a_op[1] = *reinterpret_cast<const bf16x8*>(src + 32);
     } else {
@@ -564,15 +578,31 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
   // Bucket rows: the exact threshold tau among the listed bucket keys (binary search on the key,
   // counting with ballots), then the flagged entries with key > tau and the first (need - above)
   // with key == tau stay. Every row is written out in order, -1 padded.
+  // Union output: the tiles this workgroup's queries fall in are ORed together in LDS (the stage
+  // buffers are free now) and each non-zero word is then ORed into umask once; when they do not fit,
+  // every bit goes to umask directly.
+  const int t0 = i0 / tile, n_wt = i_last / tile - t0 + 1;
+  const bool lds_union = UNION && (long long)n_wt * n_words * 4 <= 2LL * kStageBytes;
+  uint32_t* umask_lds = reinterpret_cast<uint32_t*>(stage);
+  if (lds_union) {
+    for (int x = threadIdx.x; x < n_wt * n_words; x += blockDim.x) umask_lds[x] = 0u;
+    __syncthreads();
+  }
   for (int q = 0; q < 4; ++q) {
-    const long long row = r0 + wave * 4 + q;
-    if (row >= n_rows) break;
-    const int i = (int)(row / n_groups), g = (int)(row % n_groups);
-    int32_t* out = topk + ((long long)g * n_tokens + i) * kb;
+    const int i = i0 + wave * 4 + q, g = g_wg;
+    if (i >= n_tokens) break;
+    int32_t* out = UNION ? nullptr : topk + ((long long)g * n_tokens + i) * kb;
+    uint32_t* mrow = !UNION ? nullptr : (lds_union ? umask_lds + (i / tile - t0) * n_words : mask_row(i, g));
+    auto put_bit = [&](int b) { atomicOr(&mrow[b >> 5], 1u << (b & 31)); };
+    if (UNION && l == 0) put_bit(i / block);  // the own block
     const int32_t* list = reinterpret_cast<const int32_t*>(row_a(q));
     const int nq = readlane(n_out, 16 * q);
     if (readlane((int)bucket_row, 16 * q) == 0) {
-      for (int e = l; e < kb; e += 64) out[e] = e < nq ? list[e] : -1;
+      if constexpr (UNION) {
+        for (int e = l; e < nq; e += 64) put_bit(list[e]);
+      } else {
+        for (int e = l; e < kb; e += 64) out[e] = e < nq ? list[e] : -1;
+      }
       continue;
     }
     const uint32_t* sk = row_b(q);
@@ -600,12 +630,25 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
       const int tr = t_cnt + popc64(tm & lanemask_lt());
       const bool keep = e < nq && (!flagged || key > tau || (tie && tr < ties));
       const uint64_t km = ballot(keep);
-      if (keep) out[wr + popc64(km & lanemask_lt())] = v & 0x7FFFFFFF;
+      if (keep) {
+        if constexpr (UNION)
+          put_bit(v & 0x7FFFFFFF);
+        else
+          out[wr + popc64(km & lanemask_lt())] = v & 0x7FFFFFFF;
+      }
       wr += popc64(km);
       j_side += popc64(fm);
       t_cnt += popc64(tm);
     }
-    for (int e = wr + l; e < kb; e += 64) out[e] = -1;
+    if constexpr (!UNION)
+      for (int e = wr + l; e < kb; e += 64) out[e] = -1;
+  }
+  if (lds_union) {
+    __syncthreads();
+    for (int x = threadIdx.x; x < n_wt * n_words; x += blockDim.x) {
+      const uint32_t m = umask_lds[x];
+      if (m) atomicOr(mask_row((t0 + x / n_words) * tile, g_wg) + x % n_words, m);
+    }
   }
 }
 
@@ -626,8 +669,13 @@ int prefill_waves(int kb, size_t lds_budget) {
 
 size_t index_topk_lds_min(int kb) { return select_lds_bytes(1, kb) + 256; }
 
-hipError_t launch_index_topk(const uint16_t* qi, const float* w, const uint16_t* kbar, int32_t* topk, int n_tokens,
-                             int n_groups, int block, int kb, hipStream_t stream) {
+namespace {
+
+// One launch of k_select; topk (UNION = false) or the zeroed umask (UNION = true) receives the
+// selections.
+template <bool UNION>
+hipError_t launch_select(const uint16_t* qi, const float* w, const uint16_t* kbar, int32_t* topk, uint32_t* umask,
+                         int n_tokens, int n_groups, int block, int kb, int tile, hipStream_t stream) {
   const long long n_rows = (long long)n_tokens * n_groups;
   if (n_rows == 0) return hipSuccess;
   const size_t budget = (size_t)max_lds_per_block() / SGQA_TOPK_WGS_PER_CU;
@@ -638,14 +686,16 @@ hipError_t launch_index_topk(const uint16_t* qi, const float* w, const uint16_t*
 #endif
   if (waves == 0) return hipErrorInvalidValue;
   const size_t lds = select_lds_bytes(waves, kb);
-  const long long grid = (n_rows + waves * 4 - 1) / (waves * 4);
+  const long long grid = (long long)n_groups * ((n_tokens + waves * 4 - 1) / (waves * 4));
+  const int n_tiles = (n_tokens + tile - 1) / tile;
+  const int n_words = ((n_tokens + block - 1) / block + 31) / 32;
 #define SGQA_TOPK_CASE(WV)                                                                                       \
   if (waves == WV) {                                                                                             \
-    hipError_t e = hipFuncSetAttribute((const void*)k_select<WV, 8>, hipFuncAttributeMaxDynamicSharedMemorySize,  \
-                                       (int)lds);                                                                \
+    hipError_t e = hipFuncSetAttribute((const void*)k_select<WV, 8, UNION>,                                     \
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                    \
     if (e != hipSuccess) return e;                                                                               \
-    hipLaunchKernelGGL((k_select<WV, 8>), dim3((unsigned)grid), dim3(WV * 64), lds, stream, qi, w, kbar, topk,    \
-                       n_tokens, n_groups, block, kb);                                                           \
+    hipLaunchKernelGGL((k_select<WV, 8, UNION>), dim3((unsigned)grid), dim3(WV * 64), lds, stream, qi, w, kbar,  \
+                       topk, n_tokens, n_groups, block, kb, umask, tile, n_tiles, n_words);                      \
     return hipGetLastError();                                                                                    \
   }
   SGQA_TOPK_CASE(8)
@@ -654,6 +704,24 @@ hipError_t launch_index_topk(const uint16_t* qi, const float* w, const uint16_t*
   SGQA_TOPK_CASE(1)
 #undef SGQA_TOPK_CASE
   return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_index_topk(const uint16_t* qi, const float* w, const uint16_t* kbar, int32_t* topk, int n_tokens,
+                             int n_groups, int block, int kb, hipStream_t stream) {
+  return launch_select<false>(qi, w, kbar, topk, nullptr, n_tokens, n_groups, block, kb, 1, stream);
+}
+
+hipError_t launch_index_union(const uint16_t* qi, const float* w, const uint16_t* kbar, uint32_t* umask,
+                              int32_t* ucount, int n_tokens, int n_groups, int block, int kb, int tile,
+                              hipStream_t stream) {
+  const int n_tiles = (n_tokens + tile - 1) / tile;
+  const int n_words = ((n_tokens + block - 1) / block + 31) / 32;
+  hipError_t e = launch_fill_zero(umask, (long long)n_groups * n_tiles * n_words, stream);
+  if (e == hipSuccess) e = launch_select<true>(qi, w, kbar, nullptr, umask, n_tokens, n_groups, block, kb, tile, stream);
+  if (e == hipSuccess) e = launch_mask_count(umask, ucount, (long long)n_groups * n_tiles, n_words, stream);
+  return e;
 }
 
 }  // namespace sgqa

@@ -109,7 +109,8 @@ struct PrefillWs {
   size_t bytes;
 };
 
-PrefillWs prefill_layout(const sgqa_params* p, void* ws) {
+// Prefill workspace: kbar, [topk (masked variant only)], umask, ucount.
+PrefillWs prefill_layout(const sgqa_params* p, void* ws, bool with_topk) {
   const long long N = p->n_tokens, G = p->n_kv_heads;
   const long long NB = N / p->block, T = (N + p->union_tile - 1) / p->union_tile;
   const long long nbc = (N + p->block - 1) / p->block, W = (nbc + 31) / 32;
@@ -118,8 +119,8 @@ PrefillWs prefill_layout(const sgqa_params* p, void* ws) {
   uint8_t* b = reinterpret_cast<uint8_t*>(ws);
   l.kbar = reinterpret_cast<uint16_t*>(b ? b + off : nullptr);
   off += round_up((size_t)NB * p->idx_dim * 2);
-  l.topk = reinterpret_cast<int32_t*>(b ? b + off : nullptr);
-  off += round_up((size_t)G * N * kb_of(p) * 4);
+  l.topk = reinterpret_cast<int32_t*>(b && with_topk ? b + off : nullptr);
+  if (with_topk) off += round_up((size_t)G * N * kb_of(p) * 4);
   l.umask = reinterpret_cast<uint32_t*>(b ? b + off : nullptr);
   off += round_up((size_t)G * T * W * 4);
   l.ucount = reinterpret_cast<int32_t*>(b ? b + off : nullptr);
@@ -200,7 +201,7 @@ int sgqa_workspace_size(const sgqa_params* p, int op, size_t* bytes) {
       return st;
     case SGQA_OP_PREFILL:
       st = check_params(p, NEED_INDEX | NEED_SELECT | NEED_UNION | NEED_ATTN | NEED_LIST, true);
-      if (st == SGQA_OK) *bytes = prefill_layout(p, nullptr).bytes;
+      if (st == SGQA_OK) *bytes = prefill_layout(p, nullptr, false).bytes;
       return st;
     case SGQA_OP_DECODE:
       st = check_params(p, NEED_INDEX | NEED_SELECT | NEED_DECODE | NEED_ATTN, false);
@@ -243,6 +244,20 @@ int sgqa_union(const sgqa_params* p, const int32_t* topk, uint32_t* umask, int32
                                 (hipStream_t)stream));
 }
 
+int sgqa_index_union(const sgqa_params* p, const sgqa_bf16* idx_q, const float* idx_w, const sgqa_bf16* blk_k,
+                     uint32_t* umask, int32_t* ucount, void* ws, size_t ws_bytes, sgqa_stream stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int st = check_params(p, NEED_SELECT | NEED_UNION, true);
+  if (st) return st;
+  if (!idx_q || !idx_w || !umask || !ucount || (!blk_k && p->n_tokens >= p->block)) return SGQA_ERR_NULL;
+  if (!aligned16(idx_q) || !aligned16(idx_w) || !aligned16(blk_k) || !aligned16(umask) || !aligned16(ucount))
+    return SGQA_ERR_ALIGN;
+  if (!device_ok()) return SGQA_ERR_DEVICE;
+  return status_of(launch_index_union(idx_q, idx_w, blk_k, umask, ucount, p->n_tokens, p->n_kv_heads, p->block,
+                                      kb_of(p), p->union_tile, (hipStream_t)stream));
+}
+
 int sgqa_attend(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k, const sgqa_bf16* v,
                 const uint32_t* umask, const int32_t* ucount, sgqa_bf16* out, void* ws, size_t ws_bytes,
                 sgqa_stream stream) {
@@ -267,15 +282,14 @@ int sgqa_prefill(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k, c
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(idx_q) || !aligned16(idx_w) ||
       !aligned16(idx_k) || !aligned16(out) || !aligned16(ws))
     return SGQA_ERR_ALIGN;
-  const PrefillWs l = prefill_layout(p, ws);
+  const PrefillWs l = prefill_layout(p, ws, false);
   if (!ws || ws_bytes < l.bytes) return SGQA_ERR_WORKSPACE;
   if (!device_ok()) return SGQA_ERR_DEVICE;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = launch_compress(idx_k, l.kbar, 1, p->n_tokens, p->idx_dim, p->block, s);
   if (e == hipSuccess)
-    e = launch_index_topk(idx_q, idx_w, l.kbar, l.topk, p->n_tokens, p->n_kv_heads, p->block, kb_of(p), s);
-  if (e == hipSuccess)
-    e = launch_union(l.topk, l.umask, l.ucount, p->n_tokens, p->n_kv_heads, p->block, kb_of(p), p->union_tile, s);
+    e = launch_index_union(idx_q, idx_w, l.kbar, l.umask, l.ucount, p->n_tokens, p->n_kv_heads, p->block, kb_of(p),
+                           p->union_tile, s);
   if (e == hipSuccess)
     e = launch_attend(q, k, v, l.umask, l.ucount, out, p->n_tokens, p->n_q_heads, p->n_kv_heads, p->block,
                       p->union_tile, scale_of(p), s);

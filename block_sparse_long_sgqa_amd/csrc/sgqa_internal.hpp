@@ -35,6 +35,14 @@ hipError_t launch_index_topk(const uint16_t* qi, const float* w, const uint16_t*
                              int n_groups, int block, int kb, hipStream_t stream);
 
 // Tile union: topk [G][N][kb] -> umask [G][T][W], ucount [G][T].
+// Fused index -> union: the selections go straight into the (zeroed here) tile-union mask, then
+// its popcounts; topk is never written.
+hipError_t launch_index_union(const uint16_t* qi, const float* w, const uint16_t* kbar, uint32_t* umask,
+                              int32_t* ucount, int n_tokens, int n_groups, int block, int kb, int tile,
+                              hipStream_t stream);
+hipError_t launch_fill_zero(uint32_t* dst, long long n, hipStream_t stream);
+hipError_t launch_mask_count(const uint32_t* umask, int32_t* ucount, long long n_rows, int n_words,
+                             hipStream_t stream);
 hipError_t launch_union(const int32_t* topk, uint32_t* umask, int32_t* ucount, int n_tokens, int n_groups, int block,
                         int kb, int tile, hipStream_t stream);
 

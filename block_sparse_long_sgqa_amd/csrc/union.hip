@@ -98,4 +98,39 @@ hipError_t launch_union(const int32_t* topk, uint32_t* umask, int32_t* ucount, i
   return hipGetLastError();
 }
 
+// Zero n words (a kernel rather than a memset node, so that the fused path can be captured in a
+// graph).
+__global__ __launch_bounds__(256) void k_fill_zero(uint32_t* __restrict__ dst, long long n) {
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  for (long long x = (long long)blockIdx.x * blockDim.x + threadIdx.x; x < n; x += stride) dst[x] = 0u;
+}
+
+hipError_t launch_fill_zero(uint32_t* dst, long long n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  long long grid = (n + 255) / 256;
+  if (grid > 4096) grid = 4096;
+  hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)grid), dim3(256), 0, stream, dst, n);
+  return hipGetLastError();
+}
+
+// ucount[r] = popcount of mask row r (n_words words); one workgroup per row.
+__global__ __launch_bounds__(256) void k_mask_count(const uint32_t* __restrict__ umask, int32_t* __restrict__ ucount,
+                                                    int n_words) {
+  __shared__ uint32_t wave_sums[4];
+  const uint32_t* src = umask + (long long)blockIdx.x * n_words;
+  uint32_t pc = 0;
+  for (int x = threadIdx.x; x < n_words; x += blockDim.x) pc += __popc(src[x]);
+  for (int off = 32; off >= 1; off >>= 1) pc += __shfl_xor(pc, off, 64);
+  if (lane_id() == 0) wave_sums[threadIdx.x >> 6] = pc;
+  __syncthreads();
+  if (threadIdx.x == 0) ucount[blockIdx.x] = (int32_t)(wave_sums[0] + wave_sums[1] + wave_sums[2] + wave_sums[3]);
+}
+
+hipError_t launch_mask_count(const uint32_t* umask, int32_t* ucount, long long n_rows, int n_words,
+                             hipStream_t stream) {
+  if (n_rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_mask_count, dim3((unsigned)n_rows), dim3(256), 0, stream, umask, ucount, n_words);
+  return hipGetLastError();
+}
+
 }  // namespace sgqa

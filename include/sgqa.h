@@ -131,6 +131,16 @@ int sgqa_index_topk(const sgqa_params* p, const sgqa_bf16* idx_q, const float* i
 int sgqa_union(const sgqa_params* p, const int32_t* topk, uint32_t* umask, int32_t* ucount,
                sgqa_stream stream);
 
+/* Fused selection and union (same sources as sgqa_index_topk and sgqa_union): the per-query
+ * selections go straight into the tile-union bitmask, so the [G][N][K_B] topk array is never
+ * written (it is the largest intermediate of the prefill: 2 GiB at N = 131072, G = 8, K_B = 512).
+ *   idx_q, idx_w, blk_k  as in sgqa_index_topk
+ *   umask, ucount        out, as in sgqa_union; bit-identical to sgqa_index_topk + sgqa_union
+ * No workspace (pass NULL/0). */
+int sgqa_index_union(const sgqa_params* p, const sgqa_bf16* idx_q, const float* idx_w,
+                     const sgqa_bf16* blk_k, uint32_t* umask, int32_t* ucount, void* ws, size_t ws_bytes,
+                     sgqa_stream stream);
+
 /* Gathered-block causal GQA attention over the tile unions (Figure 3: the attention main path
  * loads the uncompressed K/V of the chosen history blocks and, for the query's own block, only
  * the positions the causal mask lets it see).
@@ -145,9 +155,10 @@ int sgqa_attend(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k, co
                 const uint32_t* umask, const int32_t* ucount, sgqa_bf16* out, void* ws,
                 size_t ws_bytes, sgqa_stream stream);
 
-/* Whole prefill layer path on one stream: compress -> index_topk -> union -> attend, with
- * blk_k, topk, umask and ucount kept in the workspace (layouts as above). Arguments as in the
- * single calls; out [N][Hq][D] bf16. Workspace: sgqa_workspace_size(p, SGQA_OP_PREFILL). */
+/* Whole prefill layer path on one stream: compress -> fused index/union (sgqa_index_union) ->
+ * attend, with blk_k, umask and ucount kept in the workspace (layouts as above; no topk). Arguments
+ * as in the single calls; out [N][Hq][D] bf16, bit-identical to the single calls
+ * compress -> index_topk -> union -> attend. Workspace: sgqa_workspace_size(p, SGQA_OP_PREFILL). */
 int sgqa_prefill(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k, const sgqa_bf16* v,
                  const sgqa_bf16* idx_q, const float* idx_w, const sgqa_bf16* idx_k,
                  sgqa_bf16* out, void* ws, size_t ws_bytes, sgqa_stream stream);

@@ -146,6 +146,30 @@ def test_union_bit_exact(sg, name):
     np.testing.assert_array_equal(ucount.cpu().numpy(), want_cnt)
 
 
+@pytest.mark.parametrize("name", list(SMALL) + ["zero_queries", "negative_weights"])
+def test_index_union_fused_bit_exact(sg, name):
+    # The fused selection -> union path never writes topk; its mask must be the oracle's union of the
+    # oracle's selections (and so equal to sgqa_index_topk + sgqa_union).
+    wl = SMALL.get(name, SMALL["gqa_ragged"].replace(name=f"fused_{name}"))
+    x = datagen.prefill_inputs(wl)
+    if name == "zero_queries":
+        x["qi"] = torch.zeros_like(x["qi"])
+    if name == "negative_weights":
+        x["w"] = -x["w"]
+    p = params_of(wl)
+    ch = OracleChain(x, p)
+    want_mask, want_cnt = oracle.union(ch.topk(), p.n_tokens, p.block, p.union_tile)
+    say(f"index_union {name} N={p.n_tokens} B={p.block} Tq={p.union_tile}")
+    xd = to_dev(x)
+    kbar = torch.from_numpy(ch.kbar.view(np.int16)).view(torch.bfloat16).cuda()
+    umask = torch.full((p.n_kv_heads, p.n_tiles, p.n_words), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
+    ucount = torch.full((p.n_kv_heads, p.n_tiles), -7, dtype=torch.int32, device="cuda")
+    sg.sgqa_index_union(p, xd["qi"], xd["w"], kbar, umask, ucount)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(umask.cpu().numpy().view(np.uint32), want_mask)
+    np.testing.assert_array_equal(ucount.cpu().numpy(), want_cnt)
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_attend_within_tolerance(sg, name):
     wl = SMALL[name]
