@@ -50,6 +50,8 @@ def _load():
         lib.orc_union.restype = None
         lib.orc_attend.argtypes = [I, I, I, I, I, I, D, P, P, P, P, I, P, P]
         lib.orc_attend.restype = None
+        lib.orc_attend_sel.argtypes = [I, I, I, I, I, I, D, P, P, P, P, I, P, P]
+        lib.orc_attend_sel.restype = None
         lib.orc_decode.argtypes = [I, I, I, I, I, I, I, I, I, D, P, P, P, P, P, P, I, P, P, P]
         lib.orc_decode.restype = None
         lib.orc_decode_f8.argtypes = [I, I, I, I, I, I, I, I, I, D, P, P, P, P, P, P, P, I, P, P, P]
@@ -201,6 +203,26 @@ def attend(q, k, v, umask, block: int, tile: int, scale: float = 0.0, rows=None)
         nrows, rp = int(rows.shape[0]), _p(rows)
     out = np.empty((nrows, Hq, D), dtype=np.float64)
     _load().orc_attend(N, Hq, G, D, block, tile, float(scale), _p(q), _p(k), _p(v), _p(umask), nrows, rp, _p(out))
+    return out
+
+
+def attend_sel(q, k, v, topk, block: int, scale: float = 0.0, rows=None) -> np.ndarray:
+    """Each query over its own selection: q [N][Hq][D], k/v [G][N][D] bf16, topk [G][N][KB] int32
+    -> out [len(rows)][Hq][D] fp64 (tokens j <= i of Sel(i,g) and of the own block)."""
+    q = _u16(q)
+    k = _u16(k)
+    v = _u16(v)
+    topk = _i32(topk)
+    N, Hq, D = q.shape
+    G = k.shape[0]
+    KB = topk.shape[2]
+    if rows is None:
+        nrows, rp = N, None
+    else:
+        rows = _i32(rows)
+        nrows, rp = int(rows.shape[0]), _p(rows)
+    out = np.empty((nrows, Hq, D), dtype=np.float64)
+    _load().orc_attend_sel(N, Hq, G, D, block, KB, float(scale), _p(q), _p(k), _p(v), _p(topk), nrows, rp, _p(out))
     return out
 
 

@@ -14,6 +14,9 @@
  *     Figure 3 caption                            -> shared index keys, per-KV-group selection, own
  *                                                    block read causally (orc_attend, orc_decode)
  *     the pages' FP8 KV cache (deployment notes)  -> orc_fp8_e4m3_to_f64, orc_decode_f8
+ *     "Efficient implementation ..." read as
+ *     scheduling only (each query keeps its own
+ *     selection)                                  -> orc_attend_sel
  *
  * The pages do not fix the indexer's form. The reading used here (and by the library) is:
  *   block key   kbar[b] = bf16_rne(mean of the B index keys of block b)       (complete blocks only)
@@ -242,6 +245,41 @@ void orc_attend(int N, int Hq, int G, int D, int B, int Tq, double scale, const 
       int nt = 0;
       for (int j = 0; j <= i; ++j)
         if ((m[(j / B) / 32] >> ((j / B) % 32)) & 1u) toks[nt++] = j;
+      for (int hh = 0; hh < r; ++hh) {
+        int h = g * r + hh;
+        orc_attend_list(D, scale, q + ((size_t)i * Hq + h) * D, k + (size_t)g * N * D, v + (size_t)g * N * D,
+                        toks, nt, logit, out + ((size_t)x * Hq + h) * D);
+      }
+    }
+    free(toks);
+    free(logit);
+  }
+}
+
+/* Prefill attention where every query keeps its own selection: the second reading of "Efficient
+ * implementation of sparse attention", in which grouping adjacent queries only organises the work
+ * and changes no query's attended set. For head h of group g = h / (Hq/G) the token set is
+ *   J = { j <= i : floor(j/B) in Sel(i,g) or floor(j/B) = floor(i/B) }      (Figure 3 caption)
+ * topk [G][N][KB] (ascending ids, -1 padded) -> out [nrows][Hq][D] fp64 for rows[0..nrows) (NULL:
+ * all). scale <= 0 means 1/sqrt(D). */
+void orc_attend_sel(int N, int Hq, int G, int D, int B, int KB, double scale, const uint16_t* q,
+                    const uint16_t* k, const uint16_t* v, const int32_t* topk, int nrows, const int32_t* rows,
+                    double* out) {
+  int r = Hq / G;
+  if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int x = 0; x < nrows; ++x) {
+    int i = rows ? rows[x] : x;
+    int32_t* toks = (int32_t*)malloc(sizeof(int32_t) * (size_t)(i + 1));
+    double* logit = (double*)malloc(sizeof(double) * (size_t)(i + 1));
+    for (int g = 0; g < G; ++g) {
+      const int32_t* sel = topk + ((size_t)g * N + i) * KB;
+      int nt = 0;
+      for (int j = 0; j <= i; ++j) {
+        int b = j / B, in = b == i / B;
+        for (int e = 0; e < KB && !in; ++e) in = sel[e] == b;
+        if (in) toks[nt++] = j;
+      }
       for (int hh = 0; hh < r; ++hh) {
         int h = g * r + hh;
         orc_attend_list(D, scale, q + ((size_t)i * Hq + h) * D, k + (size_t)g * N * D, v + (size_t)g * N * D,

@@ -313,6 +313,49 @@ def test_attend_zero_query_is_mean_of_visible_values_and_first_row_is_v0(orc):
     np.testing.assert_allclose(out[0, :2], np.repeat(f64(v[0][:1]), 2, axis=0), atol=0)
 
 
+def test_attend_sel_matches_brute_force_per_query_sets(orc):
+    # Each query over Sel(i,g) and its own block, from an explicit numpy mask built from the
+    # selection (no union at all); a larger union tile must not change anything.
+    wl, x = _small_prefill(seed_name="attsel")
+    N, B, kb, r = 96, 4, 4, 2
+    q, k, v = bits(x["q"]), bits(x["k"]), bits(x["v"])
+    sel = orc.index_topk(bits(x["qi"]), x["w"].numpy(), orc.compress(bits(x["ki"]), B), B, kb)
+    out = orc.attend_sel(q, k, v, sel, B)
+    scale = 1 / math.sqrt(128)
+    for i in range(N):
+        for g in range(2):
+            blocks = {int(b) for b in sel[g, i] if b >= 0} | {i // B}
+            allowed = np.array([(j <= i) and (j // B in blocks) for j in range(N)])
+            want = brute_attention(q[i, g * r:(g + 1) * r], k[g], v[g], allowed, scale)
+            np.testing.assert_allclose(out[i, g * r:(g + 1) * r], want, rtol=1e-12, atol=1e-12)
+
+
+def test_attend_sel_is_union_attention_at_tile_1_and_differs_at_larger_tiles(orc):
+    # With one query per tile the union is Sel(i,g) plus the own block, so both readings agree; with
+    # a larger tile the union reading attends extra blocks (the two readings differ).
+    wl, x = _small_prefill(N=128, seed_name="attsel2")
+    N, B, kb = 128, 4, 4
+    q, k, v = bits(x["q"]), bits(x["k"]), bits(x["v"])
+    sel = orc.index_topk(bits(x["qi"]), x["w"].numpy(), orc.compress(bits(x["ki"]), B), B, kb)
+    out = orc.attend_sel(q, k, v, sel, B)
+    m1, _ = orc.union(sel, N, B, 1)
+    np.testing.assert_allclose(out, orc.attend(q, k, v, m1, B, 1), rtol=1e-12, atol=1e-13)
+    m8, _ = orc.union(sel, N, B, 8)
+    assert np.abs(out - orc.attend(q, k, v, m8, B, 8)).max() > 1e-3
+
+
+def test_attend_sel_dense_when_k_covers_context_equals_sdpa(orc):
+    wl, x = _small_prefill(N=64, Hq=4, G=2, B=8, k=64, Tq=16, seed_name="densesel")
+    q, k, v = bits(x["q"]), bits(x["k"]), bits(x["v"])
+    sel = orc.index_topk(bits(x["qi"]), x["w"].numpy(), orc.compress(bits(x["ki"]), 8), 8, 8)
+    out = orc.attend_sel(q, k, v, sel, 8)
+    qt = torch.from_numpy(f64(q)).permute(1, 0, 2)
+    kt = torch.from_numpy(f64(k)).repeat_interleave(2, dim=0)
+    vt = torch.from_numpy(f64(v)).repeat_interleave(2, dim=0)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True).permute(1, 0, 2)
+    np.testing.assert_allclose(out, ref.numpy(), rtol=1e-10, atol=1e-12)
+
+
 # ------------------------------------------------------------------------------------ decode
 
 def test_decode_equals_prefill_last_row_without_union(orc):
