@@ -33,11 +33,13 @@ SGQA_OP_UNION = 2
 SGQA_OP_ATTEND = 3
 SGQA_OP_PREFILL = 4
 SGQA_OP_DECODE = 5
+SGQA_OP_ATTEND_MASKED = 6
+SGQA_OP_PREFILL_MASKED = 7
 
 # Every symbol include/sgqa.h declares.
 EXPORTED = ("sgqa_abi_version", "sgqa_status_string", "sgqa_workspace_size", "sgqa_compress", "sgqa_index_topk",
             "sgqa_union", "sgqa_attend", "sgqa_prefill", "sgqa_decode", "sgqa_decode_varlen", "sgqa_append",
-            "sgqa_decode_fp8", "sgqa_index_union")
+            "sgqa_decode_fp8", "sgqa_index_union", "sgqa_attend_masked", "sgqa_prefill_masked")
 
 
 class sgqa_pages(ctypes.Structure):
@@ -136,8 +138,11 @@ def lib() -> ctypes.CDLL:
         L.sgqa_append.argtypes = [PP, P, P, P, P, P, P, PG, P, P, P]
         L.sgqa_decode_fp8.argtypes = [PP, P, P, P, P, PG, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.sgqa_index_union.argtypes = [PP, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.sgqa_attend_masked.argtypes = [PP, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.sgqa_prefill_masked.argtypes = [PP, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         for name in ("sgqa_compress", "sgqa_index_topk", "sgqa_union", "sgqa_attend", "sgqa_prefill", "sgqa_decode",
-                     "sgqa_decode_varlen", "sgqa_append", "sgqa_decode_fp8", "sgqa_index_union"):
+                     "sgqa_decode_varlen", "sgqa_append", "sgqa_decode_fp8", "sgqa_index_union",
+                     "sgqa_attend_masked", "sgqa_prefill_masked"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -249,6 +254,28 @@ def sgqa_prefill(p: Params, q, k, v, idx_q, idx_w, idx_k, out, ws, stream=None) 
             _ptr(out, "out", torch.bfloat16, (N, Hq, D)))
     _check(lib().sgqa_prefill(ctypes.byref(p.c()), *args, _ptr(ws, "ws", torch.uint8), ws.numel(),
                               _stream(stream)), "sgqa_prefill")
+
+
+def sgqa_attend_masked(p: Params, q, k, v, topk, umask, ucount, out, ws, stream=None) -> None:
+    N, Hq, G, D = p.n_tokens, p.n_q_heads, p.n_kv_heads, p.head_dim
+    args = (_ptr(q, "q", torch.bfloat16, (N, Hq, D)), _ptr(k, "k", torch.bfloat16, (G, N, D)),
+            _ptr(v, "v", torch.bfloat16, (G, N, D)), _ptr(topk, "topk", torch.int32, (G, N, p.kb)),
+            _ptr(umask, "umask", torch.int32, (G, p.n_tiles, p.n_words)),
+            _ptr(ucount, "ucount", torch.int32, (G, p.n_tiles)), _ptr(out, "out", torch.bfloat16, (N, Hq, D)))
+    _check(lib().sgqa_attend_masked(ctypes.byref(p.c()), *args, _ptr(ws, "ws", torch.uint8), ws.numel(),
+                                    _stream(stream)), "sgqa_attend_masked")
+
+
+def sgqa_prefill_masked(p: Params, q, k, v, idx_q, idx_w, idx_k, out, ws, stream=None) -> None:
+    N, Hq, G, D = p.n_tokens, p.n_q_heads, p.n_kv_heads, p.head_dim
+    args = (_ptr(q, "q", torch.bfloat16, (N, Hq, D)), _ptr(k, "k", torch.bfloat16, (G, N, D)),
+            _ptr(v, "v", torch.bfloat16, (G, N, D)),
+            _ptr(idx_q, "idx_q", torch.bfloat16, (N, G, p.idx_heads, p.idx_dim)),
+            _ptr(idx_w, "idx_w", torch.float32, (G, p.idx_heads)),
+            _ptr(idx_k, "idx_k", torch.bfloat16, (N, p.idx_dim)),
+            _ptr(out, "out", torch.bfloat16, (N, Hq, D)))
+    _check(lib().sgqa_prefill_masked(ctypes.byref(p.c()), *args, _ptr(ws, "ws", torch.uint8), ws.numel(),
+                                     _stream(stream)), "sgqa_prefill_masked")
 
 
 def sgqa_decode(p: Params, q, k_cache, v_cache, blk_k, idx_q, idx_w, out, ws, topk_out=None, stream=None) -> None:

@@ -55,7 +55,8 @@ constexpr int kKTileBytes = kKeys * kKRowBytes;    // 17408 B
 constexpr int kKTileInsts = kKeys * kKSlotsPerRow / 64;  // 17 wave-wide 16-byte loads fill the K tile
 constexpr int kVTileBytes = kKeys * 256;           // V rows unpadded; 16-B pieces XOR-swizzled by row
 constexpr int kVTileInsts = kVTileBytes / 1024;    // 16
-constexpr int kStageBytes = kKTileBytes + kVTileBytes + kKeys * 4;  // K, V, token table
+constexpr int kSelTableWords = 64;                 // masked variant: membership words of a chunk
+constexpr int kStageBytes = kKTileBytes + kVTileBytes + kKeys * 4 + kSelTableWords * 4;  // K, V, tokens, members
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kMinit = -1.0e30f;
 
@@ -120,11 +121,16 @@ struct NoOp {
 //   KREG: the K operands come from kreg[ks * 2 + kt] (registers) instead of the K tile; after()
 //         runs once the score products have consumed them.
 //   MASK: 0 = no key of the chunk can be masked, 1 = apply the mask, 2 = decided by `masked`.
-template <int QT, int MASK = 2, bool KREG = false, typename After = NoOp>
+//   SEL (with MASK = 1): a key also needs its block to be a member of the Q row's own set: the
+//         word mt[e * nqw + ql / 32] of the chunk's membership table holds, for block entry
+//         e = key >> bs of the chunk, one bit per query of the workgroup; ql[qt] is this lane's
+//         query index within the workgroup.
+template <int QT, int MASK = 2, bool KREG = false, typename After = NoOp, bool SEL = false>
 __device__ __forceinline__ void attn_chunk(const uint8_t* stage, const LaneOffsets& lo, const bf16x8 (&qreg)[QT][8],
                                            AttnState<QT>& st, float scale_log2, bool masked_rt,
                                            const int (&row_pos)[QT], const bf16x8* kreg = nullptr,
-                                           After after = After()) {
+                                           After after = After(), const uint32_t* mt = nullptr, int nqw = 0,
+                                           const int* ql = nullptr, int bs = 0) {
   const bool masked = MASK == 2 ? masked_rt : MASK == 1;
   const int l = lane_id();
   const int hi = l >> 5;
@@ -174,6 +180,28 @@ __device__ __forceinline__ void attn_chunk(const uint8_t* stage, const LaneOffse
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int a = 0; a < 4; ++a) tk[kt][a] = *reinterpret_cast<const int4*>(tok + kt * 32 + 8 * a + 4 * hi);
+  }
+
+  // SEL: keys outside the row's set get the invalid token, so the causal test masks them too.
+  if constexpr (SEL) {
+    static_assert(QT == 1, "the membership folds into the token table of the single Q tile");
+    const uint32_t* col = mt + (ql[0] >> 5);
+    const int sh = ql[0] & 31;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int key = kt * 32 + 8 * a + 4 * hi;
+        int4& t4 = tk[kt][a];
+        if (bs >= 2) {  // the four keys share one block
+          if (!((col[(key >> bs) * nqw] >> sh) & 1u)) t4 = make_int4(0x7FFFFFFF, 0x7FFFFFFF, 0x7FFFFFFF, 0x7FFFFFFF);
+        } else {
+          if (!((col[(key >> bs) * nqw] >> sh) & 1u)) t4.x = 0x7FFFFFFF;
+          if (!((col[((key + 1) >> bs) * nqw] >> sh) & 1u)) t4.y = 0x7FFFFFFF;
+          if (!((col[((key + 2) >> bs) * nqw] >> sh) & 1u)) t4.z = 0x7FFFFFFF;
+          if (!((col[((key + 3) >> bs) * nqw] >> sh) & 1u)) t4.w = 0x7FFFFFFF;
+        }
+      }
   }
 
   bf16x8 pb[QT][4];
@@ -314,13 +342,21 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
 
 // ------------------------------------------------------------------------------------ prefill
 
-template <int WAVES, int QT>
+// SEL: the masked-union variant. The union still decides which blocks are gathered, but every Q row
+// keeps only the keys of its own query's selection (selbits [G][N][W], bit b of row (g, i) = b in
+// Sel(i,g)) and of its own block. Per chunk, the workgroup builds a membership table (one bit per
+// (block entry of the chunk, query of the workgroup)) next to the token table, one chunk ahead like
+// the K/V gather: the selbits words are loaded before the chunk's gather is issued and turned into
+// table words (wave ballots) after the current chunk's products. SEL_LOADS (0 = no masking) is the
+// number of table bits each thread computes per chunk.
+template <int WAVES, int QT, int SEL_LOADS>
 __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                        const uint16_t* __restrict__ v,
                                                        const uint32_t* __restrict__ umask,
                                                        uint16_t* __restrict__ out, int n_tokens, int n_q_heads,
                                                        int n_groups, int block, int block_shift, int tile,
-                                                       float scale_log2, int n_words, int parts, int n_pairs) {
+                                                       float scale_log2, int n_words, int parts, int n_pairs,
+                                                       const uint32_t* __restrict__ selbits) {
   constexpr int NT = WAVES * 64;
   constexpr int kRowsWg = WAVES * 32 * QT;
   extern __shared__ __align__(16) uint8_t smem[];
@@ -480,17 +516,77 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
   int n_first_masked = n_chunks;
   while (n_first_masked > 0 && needs_mask(n_first_masked - 1)) --n_first_masked;
 
+  // SEL: queries of this workgroup, membership table words per block entry, this lane's query index.
+  const int nq = i_hi - i_lo + 1, nqw = (nq + 31) >> 5;
+  const int ents = kKeys >> block_shift;  // block entries per chunk (block <= 64)
+  const int pairs = ents * nqw * 32;      // <= SEL_LOADS per thread (chosen on the host)
+  int ql[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) ql[qt] = row_pos[qt] < 0 ? 0 : min(max(row_pos[qt] - i_lo, 0), nq - 1);
+  constexpr bool SEL = SEL_LOADS > 0;
+  constexpr int kLoads = SEL ? SEL_LOADS : 1;
+  uint32_t sel_word[kLoads];  // the selbits word of this thread's table bit j, loaded a chunk ahead
+  // Table bit pp: block entry e of chunk n, query qq of the workgroup.
+  auto sel_pair = [&](int n, int pp, int& b, int& i) -> bool {
+    const int e = pp / (nqw * 32), qq = ((pp >> 5) % nqw) * 32 + (pp & 31);
+    const int ent = n * ents + e;
+    i = i_lo + qq;
+    const bool ok = pp < pairs && qq < nq && ent < n_list && i < n_tokens;
+    b = ok ? (int)list[ent] : 0;
+    return ok;
+  };
+  auto sel_load = [&](int n) {
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      int b, i;
+      const bool ok = sel_pair(n, (int)threadIdx.x + j * (WAVES * 64), b, i);
+      sel_word[j] = ok ? selbits[((long long)g * n_tokens + i) * n_words + (b >> 5)] : 0u;
+    }
+  };
+  auto sel_store = [&](int n, uint8_t* sb) {
+    uint32_t* mt = reinterpret_cast<uint32_t*>(sb + kKTileBytes + kVTileBytes + kKeys * 4);
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      if (j * (WAVES * 64) + (int)(threadIdx.x & ~63) < pairs) {  // wave-uniform
+        const int pp = (int)threadIdx.x + j * (WAVES * 64);
+        int b, i;
+        const bool ok = sel_pair(n, pp, b, i);
+        const bool bit = ok && (((sel_word[j] >> (b & 31)) & 1u) || b == (i >> block_shift));
+        const uint64_t bl = ballot(bit);
+        if ((l & 31) == 0 && pp < pairs) mt[pp >> 5] = (uint32_t)(bl >> (l & 32));
+      }
+    }
+  };
+
   const LaneOffsets lo = lane_offsets();
-  if (n_chunks > 0) issue(0, stage);
+  if (n_chunks > 0) {
+    if constexpr (SEL) sel_load(0);
+    issue(0, stage);
+  }
   wait_vm();
+  if constexpr (SEL)
+    if (n_chunks > 0) sel_store(0, stage);
   __syncthreads();
   // One loop step: start the gather of chunk n + 1, run chunk n (unless the wave has no rows),
   // then wait for the gather and for every wave to be done with chunk n's buffer.
   auto run = [&](int n, auto mask_t) {
     const int buf = n & 1;
-    if (n + 1 < n_chunks) issue(n + 1, stage + (buf ^ 1) * kStageBytes);
+    if (n + 1 < n_chunks) {
+      if constexpr (SEL) sel_load(n + 1);
+      issue(n + 1, stage + (buf ^ 1) * kStageBytes);
+    }
     constexpr int kMask = decltype(mask_t)::value;
-    if (kMask >= 0) attn_chunk<QT, kMask>(stage + buf * kStageBytes, lo, qreg, st, scale_log2, kMask == 1, row_pos);
+    uint8_t* sbuf = stage + buf * kStageBytes;
+    if constexpr (SEL) {
+      if (kMask >= 0)
+        attn_chunk<QT, 1, false, NoOp, true>(sbuf, lo, qreg, st, scale_log2, true, row_pos, nullptr, NoOp(),
+                                            reinterpret_cast<const uint32_t*>(sbuf + kKTileBytes + kVTileBytes +
+                                                                              kKeys * 4),
+                                            nqw, ql, block_shift);
+      if (n + 1 < n_chunks) sel_store(n + 1, stage + (buf ^ 1) * kStageBytes);
+    } else {
+      if (kMask >= 0) attn_chunk<QT, kMask>(sbuf, lo, qreg, st, scale_log2, kMask == 1, row_pos);
+    }
     wait_vm();
     __syncthreads();
   };
@@ -537,10 +633,12 @@ size_t attend_lds_bytes_for(int n_tokens, int block) {
   return attend_lds_bytes(kPrefillWaves, (nbc + 7) / 8 * 8);
 }
 
-hipError_t launch_attend(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint32_t* umask,
-                         const int32_t* ucount, uint16_t* out, int n_tokens, int n_q_heads, int n_groups, int block,
-                         int tile, float scale, hipStream_t stream) {
-  (void)ucount;
+namespace {
+
+template <int SEL_LOADS>
+hipError_t launch_attend_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint32_t* umask,
+                              const uint32_t* selbits, uint16_t* out, int n_tokens, int n_q_heads, int n_groups,
+                              int block, int tile, float scale, hipStream_t stream) {
   const int n_tiles = (n_tokens + tile - 1) / tile;
   const int nbc = (n_tokens + block - 1) / block;
   const int n_words = (nbc + 31) / 32;
@@ -550,17 +648,58 @@ hipError_t launch_attend(const uint16_t* q, const uint16_t* k, const uint16_t* v
   const int parts = (tile_rows + rows_wg - 1) / rows_wg;
   const int n_pairs = n_tiles * n_groups;
   if (n_pairs == 0) return hipSuccess;
+  if (SEL_LOADS > 0 && attend_masked_loads(n_q_heads, n_groups, block) > SEL_LOADS) return hipErrorInvalidValue;
   const int list_cap = (nbc + 7) / 8 * 8;
   const size_t lds = attend_lds_bytes(kPrefillWaves, list_cap);
   if (lds > (size_t)max_lds_per_block()) return hipErrorInvalidValue;
   const long long grid = (long long)((n_pairs + 7) / 8) * 8 * parts;
   const float scale_log2 = scale * 1.4426950408889634f;
-  auto kern = k_attend<kPrefillWaves, kPrefillQT>;
+  auto kern = k_attend<kPrefillWaves, kPrefillQT, SEL_LOADS>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kPrefillWaves * 64), lds, stream, q, k, v, umask, out, n_tokens,
-                     n_q_heads, n_groups, block, __builtin_ctz(block), tile, scale_log2, n_words, parts, n_pairs);
+                     n_q_heads, n_groups, block, __builtin_ctz(block), tile, scale_log2, n_words, parts, n_pairs,
+                     selbits);
   return hipGetLastError();
+}
+
+}  // namespace
+
+// The membership table of a chunk has (64 / B) block entries times ceil(queries / 32) words, at most
+// kSelTableWords; a workgroup spans at most ceil(rows / r) + 1 queries. Returns the table bits per
+// thread (1, 2 or 4), or 0 when the table does not fit.
+int attend_masked_loads(int n_q_heads, int n_groups, int block) {
+  const int r = n_q_heads / n_groups;
+  const int rows_wg = kPrefillWaves * 32 * kPrefillQT;
+  const int span = (rows_wg + r - 1) / r + 1;
+  const int words = (kKeys / block) * ((span + 31) / 32);
+  if (words > kSelTableWords) return 0;
+  const int loads = (words * 32 + kPrefillWaves * 64 - 1) / (kPrefillWaves * 64);
+  return loads <= 1 ? 1 : (loads <= 2 ? 2 : 4);
+}
+
+hipError_t launch_attend(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint32_t* umask,
+                         const int32_t* ucount, uint16_t* out, int n_tokens, int n_q_heads, int n_groups, int block,
+                         int tile, float scale, hipStream_t stream) {
+  (void)ucount;
+  return launch_attend_impl<0>(q, k, v, umask, nullptr, out, n_tokens, n_q_heads, n_groups, block, tile, scale,
+                               stream);
+}
+
+hipError_t launch_attend_masked(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint32_t* umask,
+                                const uint32_t* selbits, uint16_t* out, int n_tokens, int n_q_heads, int n_groups,
+                                int block, int tile, float scale, hipStream_t stream) {
+  const int loads = attend_masked_loads(n_q_heads, n_groups, block);
+  if (loads == 1)
+    return launch_attend_impl<1>(q, k, v, umask, selbits, out, n_tokens, n_q_heads, n_groups, block, tile, scale,
+                                 stream);
+  if (loads == 2)
+    return launch_attend_impl<2>(q, k, v, umask, selbits, out, n_tokens, n_q_heads, n_groups, block, tile, scale,
+                                 stream);
+  if (loads == 4)
+    return launch_attend_impl<4>(q, k, v, umask, selbits, out, n_tokens, n_q_heads, n_groups, block, tile, scale,
+                                 stream);
+  return hipErrorInvalidValue;
 }
 
 // ------------------------------------------------------------------------------------ decode

@@ -60,7 +60,8 @@ float scale_of(const sgqa_params* p) {
 }
 
 // Checks shared by the calls; `need` selects which groups of fields matter.
-enum { NEED_INDEX = 1, NEED_ATTN = 2, NEED_SELECT = 4, NEED_UNION = 8, NEED_LIST = 16, NEED_DECODE = 32 };
+enum { NEED_INDEX = 1, NEED_ATTN = 2, NEED_SELECT = 4, NEED_UNION = 8, NEED_LIST = 16, NEED_DECODE = 32,
+       NEED_MASKED = 64 };
 
 int check_params(const sgqa_params* p, int need, bool prefill) {
   if (!p) return SGQA_ERR_NULL;
@@ -79,6 +80,9 @@ int check_params(const sgqa_params* p, int need, bool prefill) {
     if (p->idx_heads != 4 || p->idx_dim != 64) return SGQA_ERR_SHAPE;
     if (p->n_kv_heads > 16) return SGQA_ERR_SHAPE;
     if (index_topk_lds_min(kb_of(p)) > kGfx950LdsBytes) return SGQA_ERR_SHAPE;
+  }
+  if (need & NEED_MASKED) {
+    if (attend_masked_loads(p->n_q_heads, p->n_kv_heads, p->block) == 0) return SGQA_ERR_SHAPE;
   }
   if (need & NEED_DECODE) {
     if (decode_attend_lds(kb_of(p)) > kGfx950LdsBytes) return SGQA_ERR_SHAPE;
@@ -106,10 +110,17 @@ struct PrefillWs {
   int32_t* topk;
   uint32_t* umask;
   int32_t* ucount;
+  uint32_t* selbits;
   size_t bytes;
 };
 
-// Prefill workspace: kbar, [topk (masked variant only)], umask, ucount.
+// Bytes of the per-query selection bitmaps [G][N][W] of the masked-union attention.
+size_t selbits_bytes(const sgqa_params* p) {
+  const long long nbc = ((long long)p->n_tokens + p->block - 1) / p->block;
+  return round_up((size_t)p->n_kv_heads * p->n_tokens * ((nbc + 31) / 32) * 4);
+}
+
+// Prefill workspace: kbar, [topk (masked variant only)], umask, ucount, [selbits (masked variant)].
 PrefillWs prefill_layout(const sgqa_params* p, void* ws, bool with_topk) {
   const long long N = p->n_tokens, G = p->n_kv_heads;
   const long long NB = N / p->block, T = (N + p->union_tile - 1) / p->union_tile;
@@ -125,6 +136,8 @@ PrefillWs prefill_layout(const sgqa_params* p, void* ws, bool with_topk) {
   off += round_up((size_t)G * T * W * 4);
   l.ucount = reinterpret_cast<int32_t*>(b ? b + off : nullptr);
   off += round_up((size_t)G * T * 4);
+  l.selbits = reinterpret_cast<uint32_t*>(b && with_topk ? b + off : nullptr);
+  if (with_topk) off += selbits_bytes(p);
   l.bytes = off;
   return l;
 }
@@ -207,6 +220,14 @@ int sgqa_workspace_size(const sgqa_params* p, int op, size_t* bytes) {
       st = check_params(p, NEED_INDEX | NEED_SELECT | NEED_DECODE | NEED_ATTN, false);
       if (st == SGQA_OK) *bytes = decode_layout(p, nullptr).bytes;
       return st;
+    case SGQA_OP_ATTEND_MASKED:
+      st = check_params(p, NEED_ATTN | NEED_UNION | NEED_LIST | NEED_MASKED, true);
+      if (st == SGQA_OK) *bytes = selbits_bytes(p);
+      return st;
+    case SGQA_OP_PREFILL_MASKED:
+      st = check_params(p, NEED_INDEX | NEED_SELECT | NEED_UNION | NEED_ATTN | NEED_LIST | NEED_MASKED, true);
+      if (st == SGQA_OK) *bytes = prefill_layout(p, nullptr, true).bytes;
+      return st;
     default:
       return SGQA_ERR_SHAPE;
   }
@@ -271,6 +292,51 @@ int sgqa_attend(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k, co
   if (!device_ok()) return SGQA_ERR_DEVICE;
   return status_of(launch_attend(q, k, v, umask, ucount, out, p->n_tokens, p->n_q_heads, p->n_kv_heads, p->block,
                                  p->union_tile, scale_of(p), (hipStream_t)stream));
+}
+
+int sgqa_attend_masked(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k, const sgqa_bf16* v,
+                       const int32_t* topk, const uint32_t* umask, const int32_t* ucount, sgqa_bf16* out, void* ws,
+                       size_t ws_bytes, sgqa_stream stream) {
+  int st = check_params(p, NEED_ATTN | NEED_UNION | NEED_LIST | NEED_MASKED, true);
+  if (st) return st;
+  if (!q || !k || !v || !topk || !umask || !ucount || !out) return SGQA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(topk) || !aligned16(umask) ||
+      !aligned16(ucount) || !aligned16(out) || !aligned16(ws))
+    return SGQA_ERR_ALIGN;
+  if (!ws || ws_bytes < selbits_bytes(p)) return SGQA_ERR_WORKSPACE;
+  if (!device_ok()) return SGQA_ERR_DEVICE;
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t* selbits = static_cast<uint32_t*>(ws);
+  hipError_t e = launch_sel_bitmap(topk, selbits, p->n_tokens, p->n_kv_heads, p->block, kb_of(p), s);
+  if (e == hipSuccess)
+    e = launch_attend_masked(q, k, v, umask, selbits, out, p->n_tokens, p->n_q_heads, p->n_kv_heads, p->block,
+                             p->union_tile, scale_of(p), s);
+  return status_of(e);
+}
+
+int sgqa_prefill_masked(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k, const sgqa_bf16* v,
+                        const sgqa_bf16* idx_q, const float* idx_w, const sgqa_bf16* idx_k, sgqa_bf16* out, void* ws,
+                        size_t ws_bytes, sgqa_stream stream) {
+  int st = check_params(p, NEED_INDEX | NEED_SELECT | NEED_UNION | NEED_ATTN | NEED_LIST | NEED_MASKED, true);
+  if (st) return st;
+  if (!q || !k || !v || !idx_q || !idx_w || !idx_k || !out) return SGQA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(idx_q) || !aligned16(idx_w) ||
+      !aligned16(idx_k) || !aligned16(out) || !aligned16(ws))
+    return SGQA_ERR_ALIGN;
+  const PrefillWs l = prefill_layout(p, ws, true);
+  if (!ws || ws_bytes < l.bytes) return SGQA_ERR_WORKSPACE;
+  if (!device_ok()) return SGQA_ERR_DEVICE;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_compress(idx_k, l.kbar, 1, p->n_tokens, p->idx_dim, p->block, s);
+  if (e == hipSuccess)
+    e = launch_index_topk(idx_q, idx_w, l.kbar, l.topk, p->n_tokens, p->n_kv_heads, p->block, kb_of(p), s);
+  if (e == hipSuccess)
+    e = launch_union(l.topk, l.umask, l.ucount, p->n_tokens, p->n_kv_heads, p->block, kb_of(p), p->union_tile, s);
+  if (e == hipSuccess) e = launch_sel_bitmap(l.topk, l.selbits, p->n_tokens, p->n_kv_heads, p->block, kb_of(p), s);
+  if (e == hipSuccess)
+    e = launch_attend_masked(q, k, v, l.umask, l.selbits, out, p->n_tokens, p->n_q_heads, p->n_kv_heads, p->block,
+                             p->union_tile, scale_of(p), s);
+  return status_of(e);
 }
 
 int sgqa_prefill(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k, const sgqa_bf16* v,

@@ -43,6 +43,16 @@ hipError_t launch_index_union(const uint16_t* qi, const float* w, const uint16_t
 hipError_t launch_fill_zero(uint32_t* dst, long long n, hipStream_t stream);
 hipError_t launch_mask_count(const uint32_t* umask, int32_t* ucount, long long n_rows, int n_words,
                              hipStream_t stream);
+// Per-query selection bitmaps selbits [G][N][W] from topk (for the masked-union attention).
+hipError_t launch_sel_bitmap(const int32_t* topk, uint32_t* selbits, int n_tokens, int n_groups, int block, int kb,
+                             hipStream_t stream);
+// Masked-union attention: gathers by the union, keeps per Q row only its query's selection
+// (selbits from launch_sel_bitmap) and own block.
+hipError_t launch_attend_masked(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint32_t* umask,
+                                const uint32_t* selbits, uint16_t* out, int n_tokens, int n_q_heads, int n_groups,
+                                int block, int tile, float scale, hipStream_t stream);
+// Table bits per thread of the masked attention (1, 2 or 4); 0 = shape not supported.
+int attend_masked_loads(int n_q_heads, int n_groups, int block);
 hipError_t launch_union(const int32_t* topk, uint32_t* umask, int32_t* ucount, int n_tokens, int n_groups, int block,
                         int kb, int tile, hipStream_t stream);
 

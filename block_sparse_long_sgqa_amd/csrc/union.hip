@@ -133,4 +133,39 @@ hipError_t launch_mask_count(const uint32_t* umask, int32_t* ucount, long long n
   return hipGetLastError();
 }
 
+// Per-query selection bitmaps for the masked-union attention: selbits [G][N][W], bit b % 32 of
+// word b / 32 of row (g, i) set iff b is in Sel(i,g) (the own block is not included). One wave per
+// row; the row is assembled in LDS in windows of 512 words and written with coalesced stores.
+__global__ __launch_bounds__(256) void k_sel_bitmap(const int32_t* __restrict__ topk, uint32_t* __restrict__ selbits,
+                                                    long long n_rows, int kb, int n_words) {
+  constexpr int kWin = 512;
+  __shared__ uint32_t win[4][kWin];
+  const int wave = threadIdx.x >> 6, l = lane_id();
+  const long long row = (long long)blockIdx.x * 4 + wave;
+  if (row >= n_rows) return;  // wave-uniform; no barrier below
+  const int32_t* sel = topk + row * kb;
+  uint32_t* dst = selbits + row * n_words;
+  uint32_t* w = win[wave];
+  for (int w0 = 0; w0 < n_words; w0 += kWin) {
+    for (int x = l; x < kWin; x += 64) w[x] = 0u;
+    for (int e = l; e < kb; e += 64) {
+      const int b = sel[e];
+      const int wd = (b >> 5) - w0;
+      if (b >= 0 && wd >= 0 && wd < kWin) atomicOr(&w[wd], 1u << (b & 31));
+    }
+    const int n = n_words - w0 < kWin ? n_words - w0 : kWin;
+    for (int x = l; x < n; x += 64) dst[w0 + x] = w[x];
+  }
+}
+
+hipError_t launch_sel_bitmap(const int32_t* topk, uint32_t* selbits, int n_tokens, int n_groups, int block, int kb,
+                             hipStream_t stream) {
+  const long long n_rows = (long long)n_tokens * n_groups;
+  if (n_rows == 0) return hipSuccess;
+  const int n_words = ((n_tokens + block - 1) / block + 31) / 32;
+  hipLaunchKernelGGL(k_sel_bitmap, dim3((unsigned)((n_rows + 3) / 4)), dim3(256), 0, stream, topk, selbits, n_rows,
+                     kb, n_words);
+  return hipGetLastError();
+}
+
 }  // namespace sgqa

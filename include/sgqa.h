@@ -69,7 +69,9 @@ enum {
   SGQA_OP_UNION = 2,
   SGQA_OP_ATTEND = 3,
   SGQA_OP_PREFILL = 4,
-  SGQA_OP_DECODE = 5
+  SGQA_OP_DECODE = 5,
+  SGQA_OP_ATTEND_MASKED = 6,
+  SGQA_OP_PREFILL_MASKED = 7
 };
 
 /* Sizes of one call. Symbols: N tokens, S sequences, Hq query heads, G KV groups (KV heads),
@@ -261,6 +263,33 @@ int sgqa_decode_fp8(const sgqa_params* p, const sgqa_bf16* q, const uint8_t* k_c
                     const float* kv_scale, const sgqa_pages* pages, const sgqa_bf16* blk_k,
                     const sgqa_bf16* idx_q, const float* idx_w, const int32_t* seq_lens, int32_t* topk_out,
                     sgqa_bf16* out, void* ws, size_t ws_bytes, sgqa_stream stream);
+
+/* ---------------------------------------------------------------- masked-union variant
+ * The pages group the top-k results of adjacent prefill tokens so that overlapping K/V reads are
+ * done together ("Efficient implementation of sparse attention"). The calls above read that as:
+ * every query of a tile attends over the tile's union. The variant below reads it as scheduling
+ * only: the union decides which blocks are gathered, and every query still attends exactly its own
+ * selection plus its own block (Figure 3 caption), causally masked -- the result then does not
+ * depend on Tq (it equals the union reading at Tq = 1).
+ *
+ * Attention over the tile unions with every Q row restricted to its own query's set.
+ *   q, k, v, umask, ucount, out   as in sgqa_attend
+ *   topk   [G][N][K_B] int32  the selections (sgqa_index_topk)
+ *   out[i][h] = sum_{j in J} softmax_j(sigma * <q[i][h], k[g][j]>) v[g][j],
+ *          J = { j <= i : floor(j/B) in Sel(i,g) or floor(j/B) = floor(i/B) }
+ * Shapes: the per-chunk membership table must fit: (64/B) * ceil((256/r + 1)/32) <= 64 words
+ * (B = 8 needs r >= 2; B = 1 needs r >= 8); otherwise SGQA_ERR_SHAPE.
+ * Workspace: sgqa_workspace_size(p, SGQA_OP_ATTEND_MASKED) (per-query selection bitmaps). */
+int sgqa_attend_masked(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k, const sgqa_bf16* v,
+                       const int32_t* topk, const uint32_t* umask, const int32_t* ucount, sgqa_bf16* out,
+                       void* ws, size_t ws_bytes, sgqa_stream stream);
+
+/* Whole prefill path of the variant: compress -> index_topk -> union -> masked attention, with
+ * blk_k, topk, umask, ucount and the selection bitmaps in the workspace. Arguments as in
+ * sgqa_prefill. Workspace: sgqa_workspace_size(p, SGQA_OP_PREFILL_MASKED). */
+int sgqa_prefill_masked(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k, const sgqa_bf16* v,
+                        const sgqa_bf16* idx_q, const float* idx_w, const sgqa_bf16* idx_k,
+                        sgqa_bf16* out, void* ws, size_t ws_bytes, sgqa_stream stream);
 
 #ifdef __cplusplus
 }

@@ -176,3 +176,23 @@ def test_fp8_decode_validation(sg):
     # dense and varlen descriptors get as far as the workspace check
     assert fp8(ws_bytes=16) == sg.SGQA_ERR_WORKSPACE
     assert fp8(lens=a, ws_bytes=16) == sg.SGQA_ERR_WORKSPACE
+
+
+def test_masked_variant_shapes_and_workspace(sg):
+    r = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    p = _p()  # N 32768, G 8, B 8, r 8
+    W = (32768 // 8 + 31) // 32
+    assert sg.workspace_size(p, sg.SGQA_OP_ATTEND_MASKED) == r(8 * 32768 * W * 4)
+    assert sg.workspace_size(p, sg.SGQA_OP_PREFILL_MASKED) == \
+        sg.workspace_size(p, sg.SGQA_OP_PREFILL) + r(8 * 32768 * 512 * 4) + r(8 * 32768 * W * 4)
+    # B = 1 with r = 8: 64 block entries x 2 words per chunk do not fit the membership table.
+    bad = _p(block=1, topk_tokens=512)
+    out = ctypes.c_size_t(0)
+    assert sg.lib().sgqa_workspace_size(ctypes.byref(bad.c()), sg.SGQA_OP_ATTEND_MASKED, ctypes.byref(out)) \
+        == sg.SGQA_ERR_SHAPE
+    nul = ctypes.c_void_p(0)
+    buf = (ctypes.c_uint8 * 64)()
+    a = ctypes.c_void_p((ctypes.addressof(buf) + 15) // 16 * 16)
+    assert sg.lib().sgqa_attend_masked(ctypes.byref(bad.c()), a, a, a, a, a, a, a, a, 1 << 40, nul) == sg.SGQA_ERR_SHAPE
+    assert sg.lib().sgqa_attend_masked(ctypes.byref(p.c()), a, a, a, nul, a, a, a, a, 1 << 40, nul) == sg.SGQA_ERR_NULL
+    assert sg.lib().sgqa_attend_masked(ctypes.byref(p.c()), a, a, a, a, a, a, a, a, 16, nul) == sg.SGQA_ERR_WORKSPACE

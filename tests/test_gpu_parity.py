@@ -190,6 +190,58 @@ def test_attend_within_tolerance(sg, name):
     assert_close_attention(out[torch.from_numpy(rows).long().cuda()], want, f"attend {name}")
 
 
+@pytest.mark.parametrize("name", ["tiny", "gqa_ragged", "b4_tile24", "b16_iid", "tile1", "b64_r4"])
+def test_attend_masked_within_tolerance(sg, name):
+    # Masked-union variant: the union only decides what is gathered; each Q row attends its own
+    # query's selection and own block (oracle: attend_sel, with no union at all).
+    wl = SMALL[name]
+    p = params_of(wl)
+    x = datagen.prefill_inputs(wl)
+    ch = OracleChain(x, p)
+    sel = ch.topk()
+    umask, ucount = oracle.union(sel, p.n_tokens, p.block, p.union_tile)
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([np.arange(0, 40), np.arange(p.n_tokens - 40, p.n_tokens),
+                                     rng.integers(0, p.n_tokens, 300)])).astype(np.int32)
+    want = oracle.attend_sel(bits(x["q"]), bits(x["k"]), bits(x["v"]), sel, p.block, rows=rows)
+    say(f"attend_masked {name} N={p.n_tokens} Hq={p.n_q_heads} G={p.n_kv_heads} B={p.block} Tq={p.union_tile}")
+    xd = to_dev(x)
+    out = torch.empty((p.n_tokens, p.n_q_heads, p.head_dim), dtype=torch.bfloat16, device="cuda")
+    ws = sg.workspace(p, sg.SGQA_OP_ATTEND_MASKED)
+    sg.sgqa_attend_masked(p, xd["q"], xd["k"], xd["v"], torch.from_numpy(sel).cuda(),
+                          torch.from_numpy(umask.view(np.int32)).cuda(), torch.from_numpy(ucount).cuda(), out, ws)
+    torch.cuda.synchronize()
+    assert_close_attention(out[torch.from_numpy(rows).long().cuda()], want, f"attend_masked {name}")
+    if p.union_tile == 1:
+        # One query per tile: the union is the query's own set, so both readings give the same bits.
+        out1 = torch.empty_like(out)
+        sg.sgqa_attend(p, xd["q"], xd["k"], xd["v"], torch.from_numpy(umask.view(np.int32)).cuda(),
+                       torch.from_numpy(ucount).cuda(), out1)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), out1.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["gqa_ragged", "b4_tile24"])
+def test_prefill_masked_end_to_end(sg, name):
+    wl = SMALL[name]
+    p = params_of(wl)
+    x = datagen.prefill_inputs(wl)
+    ch = OracleChain(x, p)
+    want = oracle.attend_sel(bits(x["q"]), bits(x["k"]), bits(x["v"]), ch.topk(), p.block)
+    say(f"prefill_masked {name}")
+    xd = to_dev(x)
+    out = torch.empty((p.n_tokens, p.n_q_heads, p.head_dim), dtype=torch.bfloat16, device="cuda")
+    ws = sg.workspace(p, sg.SGQA_OP_PREFILL_MASKED)
+    sg.sgqa_prefill_masked(p, xd["q"], xd["k"], xd["v"], xd["qi"], xd["w"], xd["ki"], out, ws)
+    torch.cuda.synchronize()
+    assert_close_attention(out, want, f"prefill_masked {name}")
+    # The union reading of the same inputs differs (it attends extra blocks).
+    out_u = torch.empty_like(out)
+    sg.sgqa_prefill(p, xd["q"], xd["k"], xd["v"], xd["qi"], xd["w"], xd["ki"], out_u, sg.workspace(p, sg.SGQA_OP_PREFILL))
+    torch.cuda.synchronize()
+    assert (out_u.float() - out.float()).abs().max().item() > 1e-2
+
+
 @pytest.mark.parametrize("name", ["tiny", "gqa_ragged", "b4_tile24", "b1_token"])
 def test_prefill_end_to_end(sg, name):
     wl = SMALL[name]
