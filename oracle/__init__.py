@@ -50,6 +50,8 @@ def _load():
         lib.orc_union.restype = None
         lib.orc_attend.argtypes = [I, I, I, I, I, I, D, P, P, P, P, I, P, P]
         lib.orc_attend.restype = None
+        lib.orc_attend_bwd.argtypes = [I, I, I, I, I, I, D, P, P, P, P, P, P, P, P]
+        lib.orc_attend_bwd.restype = None
         lib.orc_attend_sel.argtypes = [I, I, I, I, I, I, D, P, P, P, P, I, P, P]
         lib.orc_attend_sel.restype = None
         lib.orc_decode.argtypes = [I, I, I, I, I, I, I, I, I, D, P, P, P, P, P, P, I, P, P, P]
@@ -204,6 +206,24 @@ def attend(q, k, v, umask, block: int, tile: int, scale: float = 0.0, rows=None)
     out = np.empty((nrows, Hq, D), dtype=np.float64)
     _load().orc_attend(N, Hq, G, D, block, tile, float(scale), _p(q), _p(k), _p(v), _p(umask), nrows, rp, _p(out))
     return out
+
+
+def attend_bwd(q, k, v, umask, dout, block: int, tile: int, scale: float = 0.0):
+    """Gradient of attend(): q/dout [N][Hq][D], k/v [G][N][D] bf16, umask [G][T][W]
+    -> (dq [N][Hq][D], dk [G][N][D], dv [G][N][D]) fp64."""
+    q = _u16(q)
+    k = _u16(k)
+    v = _u16(v)
+    dout = _u16(dout)
+    umask = np.ascontiguousarray(umask, dtype=np.uint32)
+    N, Hq, D = q.shape
+    G = k.shape[0]
+    dq = np.empty((N, Hq, D), dtype=np.float64)
+    dk = np.empty((G, N, D), dtype=np.float64)
+    dv = np.empty((G, N, D), dtype=np.float64)
+    _load().orc_attend_bwd(N, Hq, G, D, block, tile, float(scale), _p(q), _p(k), _p(v), _p(umask), _p(dout),
+                           _p(dq), _p(dk), _p(dv))
+    return dq, dk, dv
 
 
 def attend_sel(q, k, v, topk, block: int, scale: float = 0.0, rows=None) -> np.ndarray:

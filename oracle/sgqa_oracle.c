@@ -14,6 +14,9 @@
  *     Figure 3 caption                            -> shared index keys, per-KV-group selection, own
  *                                                    block read causally (orc_attend, orc_decode)
  *     the pages' FP8 KV cache (deployment notes)  -> orc_fp8_e4m3_to_f64, orc_decode_f8
+ *     training use of Sparse GQA (the pages train
+ *     with it; the gradient is that of the same
+ *     attention)                                  -> orc_attend_bwd
  *     "Efficient implementation ..." read as
  *     scheduling only (each query keeps its own
  *     selection)                                  -> orc_attend_sel
@@ -289,6 +292,81 @@ void orc_attend_sel(int N, int Hq, int G, int D, int B, int KB, double scale, co
     free(toks);
     free(logit);
   }
+}
+
+/* Gradient of the prefill attention (union reading, token sets as in orc_attend) for an upstream
+ * gradient dout [N][Hq][D] bf16: with p the row's softmax over J, o = sum_j p_j v_j,
+ *   dv_j += p_j * dout_i,   dp_j = <dout_i, v_j>,   ds_j = p_j * (dp_j - <dout_i, o_i>),
+ *   dq_i += scale * sum_j ds_j k_j,   dk_j += scale * ds_j q_i
+ * (the gradient of softmax attention, with the heads of a group summed into its K/V gradients).
+ * Outputs fp64: dq [N][Hq][D], dk, dv [G][N][D]. Sequential over rows (the K/V sums are shared). */
+void orc_attend_bwd(int N, int Hq, int G, int D, int B, int Tq, double scale, const uint16_t* q, const uint16_t* k,
+                    const uint16_t* v, const uint32_t* umask, const uint16_t* dout, double* dq, double* dk,
+                    double* dv) {
+  int T = (N + Tq - 1) / Tq;
+  int NBc = (N + B - 1) / B;
+  int W = (NBc + 31) / 32;
+  int r = Hq / G;
+  if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
+  memset(dq, 0, sizeof(double) * (size_t)N * Hq * D);
+  memset(dk, 0, sizeof(double) * (size_t)G * N * D);
+  memset(dv, 0, sizeof(double) * (size_t)G * N * D);
+  int32_t* toks = (int32_t*)malloc(sizeof(int32_t) * (size_t)N);
+  double* p = (double*)malloc(sizeof(double) * (size_t)N);
+  double* o = (double*)malloc(sizeof(double) * (size_t)D);
+  for (int i = 0; i < N; ++i) {
+    int t = i / Tq;
+    for (int g = 0; g < G; ++g) {
+      const uint32_t* m = umask + ((size_t)g * T + t) * W;
+      int nt = 0;
+      for (int j = 0; j <= i; ++j)
+        if ((m[(j / B) / 32] >> ((j / B) % 32)) & 1u) toks[nt++] = j;
+      const uint16_t* kg = k + (size_t)g * N * D;
+      const uint16_t* vg = v + (size_t)g * N * D;
+      for (int hh = 0; hh < r; ++hh) {
+        int h = g * r + hh;
+        const uint16_t* qi = q + ((size_t)i * Hq + h) * D;
+        const uint16_t* doi = dout + ((size_t)i * Hq + h) * D;
+        /* softmax over the row's tokens */
+        double mx = -INFINITY;
+        for (int x = 0; x < nt; ++x) {
+          double dot = 0.0;
+          for (int d = 0; d < D; ++d) dot += orc_bf16_to_f64(qi[d]) * orc_bf16_to_f64(kg[(size_t)toks[x] * D + d]);
+          p[x] = scale * dot;
+          if (p[x] > mx) mx = p[x];
+        }
+        double den = 0.0;
+        for (int x = 0; x < nt; ++x) {
+          p[x] = exp(p[x] - mx);
+          den += p[x];
+        }
+        for (int d = 0; d < D; ++d) o[d] = 0.0;
+        for (int x = 0; x < nt; ++x) {
+          p[x] /= den;
+          for (int d = 0; d < D; ++d) o[d] += p[x] * orc_bf16_to_f64(vg[(size_t)toks[x] * D + d]);
+        }
+        double delta = 0.0;
+        for (int d = 0; d < D; ++d) delta += orc_bf16_to_f64(doi[d]) * o[d];
+        for (int x = 0; x < nt; ++x) {
+          const size_t jo = (size_t)toks[x] * D;
+          double dp = 0.0;
+          for (int d = 0; d < D; ++d) dp += orc_bf16_to_f64(doi[d]) * orc_bf16_to_f64(vg[jo + d]);
+          const double ds = p[x] * (dp - delta);
+          double* dqi = dq + ((size_t)i * Hq + h) * D;
+          double* dkj = dk + (size_t)g * N * D + jo;
+          double* dvj = dv + (size_t)g * N * D + jo;
+          for (int d = 0; d < D; ++d) {
+            dqi[d] += scale * ds * orc_bf16_to_f64(kg[jo + d]);
+            dkj[d] += scale * ds * orc_bf16_to_f64(qi[d]);
+            dvj[d] += p[x] * orc_bf16_to_f64(doi[d]);
+          }
+        }
+      }
+    }
+  }
+  free(toks);
+  free(p);
+  free(o);
 }
 
 /* ---------------------------------------------------------------- decode ----------------------- */

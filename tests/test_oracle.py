@@ -356,6 +356,58 @@ def test_attend_sel_dense_when_k_covers_context_equals_sdpa(orc):
     np.testing.assert_allclose(out, ref.numpy(), rtol=1e-10, atol=1e-12)
 
 
+def _torch_attention_grads(q, k, v, dout, allowed, r, scale):
+    """fp64 autograd of softmax attention with a boolean mask [N][N] per group (allowed[g]);
+    q/dout [N][Hq][D], k/v [G][N][D] (bf16 bits) -> dq, dk, dv as numpy fp64."""
+    qt = torch.from_numpy(f64(q)).permute(1, 0, 2).clone().requires_grad_(True)   # [Hq][N][D]
+    kt = torch.from_numpy(f64(k)).clone().requires_grad_(True)                    # [G][N][D]
+    vt = torch.from_numpy(f64(v)).clone().requires_grad_(True)
+    mask = torch.from_numpy(np.repeat(allowed, r, axis=0))                        # [Hq][N][N]
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt.repeat_interleave(r, dim=0),
+                                                         vt.repeat_interleave(r, dim=0), attn_mask=mask, scale=scale)
+    o.backward(torch.from_numpy(f64(dout)).permute(1, 0, 2))
+    return qt.grad.permute(1, 0, 2).numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+def test_attend_bwd_matches_torch_autograd_on_union_masks(orc):
+    wl, x = _small_prefill(seed_name="bwd")
+    N, B, Tq, kb, r, G = 96, 4, 8, 4, 2, 2
+    q, k, v = bits(x["q"]), bits(x["k"]), bits(x["v"])
+    dout = bits(torch.randn((N, 4, 128), generator=torch.Generator().manual_seed(3)).to(torch.bfloat16))
+    sel = orc.index_topk(bits(x["qi"]), x["w"].numpy(), orc.compress(bits(x["ki"]), B), B, kb)
+    umask, _ = orc.union(sel, N, B, Tq)
+    dq, dk, dv = orc.attend_bwd(q, k, v, umask, dout, B, Tq)
+    allowed = np.zeros((G, N, N), dtype=bool)
+    for g in range(G):
+        for i in range(N):
+            t = i // Tq
+            for j in range(i + 1):
+                allowed[g, i, j] = (umask[g, t, (j // B) // 32] >> ((j // B) % 32)) & 1
+    tq, tk, tv = _torch_attention_grads(q, k, v, dout, allowed, r, 1 / math.sqrt(128))
+    np.testing.assert_allclose(dq, tq, rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(dk, tk, rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(dv, tv, rtol=1e-9, atol=1e-11)
+    # A key block outside every union that could see it gets no gradient at all.
+    seen = np.zeros((G, N), dtype=bool)
+    for g in range(G):
+        seen[g] = allowed[g].any(axis=0)
+    assert (dk[~seen] == 0).all() and (dv[~seen] == 0).all()
+
+
+def test_attend_bwd_dense_equals_causal_sdpa_autograd(orc):
+    wl, x = _small_prefill(N=64, Hq=4, G=2, B=8, k=64, Tq=16, seed_name="bwddense")
+    q, k, v = bits(x["q"]), bits(x["k"]), bits(x["v"])
+    dout = bits(torch.randn((64, 4, 128), generator=torch.Generator().manual_seed(4)).to(torch.bfloat16))
+    sel = orc.index_topk(bits(x["qi"]), x["w"].numpy(), orc.compress(bits(x["ki"]), 8), 8, 8)
+    umask, _ = orc.union(sel, 64, 8, 16)
+    dq, dk, dv = orc.attend_bwd(q, k, v, umask, dout, 8, 16)
+    causal = np.tril(np.ones((64, 64), dtype=bool))
+    tq, tk, tv = _torch_attention_grads(q, k, v, dout, np.stack([causal, causal]), 2, 1 / math.sqrt(128))
+    np.testing.assert_allclose(dq, tq, rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(dk, tk, rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(dv, tv, rtol=1e-9, atol=1e-11)
+
+
 # ------------------------------------------------------------------------------------ decode
 
 def test_decode_equals_prefill_last_row_without_union(orc):
