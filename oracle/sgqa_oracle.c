@@ -299,7 +299,9 @@ void orc_attend_sel(int N, int Hq, int G, int D, int B, int KB, double scale, co
  *   dv_j += p_j * dout_i,   dp_j = <dout_i, v_j>,   ds_j = p_j * (dp_j - <dout_i, o_i>),
  *   dq_i += scale * sum_j ds_j k_j,   dk_j += scale * ds_j q_i
  * (the gradient of softmax attention, with the heads of a group summed into its K/V gradients).
- * Outputs fp64: dq [N][Hq][D], dk, dv [G][N][D]. Sequential over rows (the K/V sums are shared). */
+ * Outputs fp64: dq [N][Hq][D], dk, dv [G][N][D]. Two passes, each over independent outputs: per row
+ * (softmax max, denominator, delta = <dout_i, o_i>, and dq_i), then per key (dk_j, dv_j summed over
+ * the rows whose set holds j, in ascending row order). */
 void orc_attend_bwd(int N, int Hq, int G, int D, int B, int Tq, double scale, const uint16_t* q, const uint16_t* k,
                     const uint16_t* v, const uint32_t* umask, const uint16_t* dout, double* dq, double* dk,
                     double* dv) {
@@ -308,65 +310,118 @@ void orc_attend_bwd(int N, int Hq, int G, int D, int B, int Tq, double scale, co
   int W = (NBc + 31) / 32;
   int r = Hq / G;
   if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
-  memset(dq, 0, sizeof(double) * (size_t)N * Hq * D);
-  memset(dk, 0, sizeof(double) * (size_t)G * N * D);
-  memset(dv, 0, sizeof(double) * (size_t)G * N * D);
-  int32_t* toks = (int32_t*)malloc(sizeof(int32_t) * (size_t)N);
-  double* p = (double*)malloc(sizeof(double) * (size_t)N);
-  double* o = (double*)malloc(sizeof(double) * (size_t)D);
+  size_t nq = (size_t)N * Hq * D, nk = (size_t)G * N * D;
+  double* qf = (double*)malloc(sizeof(double) * nq);
+  double* of = (double*)malloc(sizeof(double) * nq);  /* dout */
+  double* kf = (double*)malloc(sizeof(double) * nk);
+  double* vf = (double*)malloc(sizeof(double) * nk);
+  double* rmax = (double*)malloc(sizeof(double) * (size_t)N * Hq);
+  double* rden = (double*)malloc(sizeof(double) * (size_t)N * Hq);
+  double* rdel = (double*)malloc(sizeof(double) * (size_t)N * Hq);
+  for (size_t x = 0; x < nq; ++x) {
+    qf[x] = orc_bf16_to_f64(q[x]);
+    of[x] = orc_bf16_to_f64(dout[x]);
+  }
+  for (size_t x = 0; x < nk; ++x) {
+    kf[x] = orc_bf16_to_f64(k[x]);
+    vf[x] = orc_bf16_to_f64(v[x]);
+  }
+  /* pass 1: rows */
+#pragma omp parallel for schedule(dynamic, 1)
   for (int i = 0; i < N; ++i) {
     int t = i / Tq;
+    double* lg = (double*)malloc(sizeof(double) * (size_t)(i + 1));
+    int32_t* toks = (int32_t*)malloc(sizeof(int32_t) * (size_t)(i + 1));
+    double* o = (double*)malloc(sizeof(double) * (size_t)D);
     for (int g = 0; g < G; ++g) {
       const uint32_t* m = umask + ((size_t)g * T + t) * W;
       int nt = 0;
       for (int j = 0; j <= i; ++j)
         if ((m[(j / B) / 32] >> ((j / B) % 32)) & 1u) toks[nt++] = j;
-      const uint16_t* kg = k + (size_t)g * N * D;
-      const uint16_t* vg = v + (size_t)g * N * D;
       for (int hh = 0; hh < r; ++hh) {
         int h = g * r + hh;
-        const uint16_t* qi = q + ((size_t)i * Hq + h) * D;
-        const uint16_t* doi = dout + ((size_t)i * Hq + h) * D;
-        /* softmax over the row's tokens */
+        const double* qi = qf + ((size_t)i * Hq + h) * D;
+        const double* di = of + ((size_t)i * Hq + h) * D;
         double mx = -INFINITY;
         for (int x = 0; x < nt; ++x) {
+          const double* kr = kf + ((size_t)g * N + toks[x]) * D;
           double dot = 0.0;
-          for (int d = 0; d < D; ++d) dot += orc_bf16_to_f64(qi[d]) * orc_bf16_to_f64(kg[(size_t)toks[x] * D + d]);
-          p[x] = scale * dot;
-          if (p[x] > mx) mx = p[x];
+          for (int d = 0; d < D; ++d) dot += qi[d] * kr[d];
+          lg[x] = scale * dot;
+          if (lg[x] > mx) mx = lg[x];
         }
         double den = 0.0;
-        for (int x = 0; x < nt; ++x) {
-          p[x] = exp(p[x] - mx);
-          den += p[x];
-        }
+        for (int x = 0; x < nt; ++x) den += exp(lg[x] - mx);
         for (int d = 0; d < D; ++d) o[d] = 0.0;
         for (int x = 0; x < nt; ++x) {
-          p[x] /= den;
-          for (int d = 0; d < D; ++d) o[d] += p[x] * orc_bf16_to_f64(vg[(size_t)toks[x] * D + d]);
+          const double p = exp(lg[x] - mx) / den;
+          const double* vr = vf + ((size_t)g * N + toks[x]) * D;
+          for (int d = 0; d < D; ++d) o[d] += p * vr[d];
         }
         double delta = 0.0;
-        for (int d = 0; d < D; ++d) delta += orc_bf16_to_f64(doi[d]) * o[d];
+        for (int d = 0; d < D; ++d) delta += di[d] * o[d];
+        double* dqi = dq + ((size_t)i * Hq + h) * D;
+        for (int d = 0; d < D; ++d) dqi[d] = 0.0;
         for (int x = 0; x < nt; ++x) {
-          const size_t jo = (size_t)toks[x] * D;
+          const double p = exp(lg[x] - mx) / den;
+          const double* kr = kf + ((size_t)g * N + toks[x]) * D;
+          const double* vr = vf + ((size_t)g * N + toks[x]) * D;
           double dp = 0.0;
-          for (int d = 0; d < D; ++d) dp += orc_bf16_to_f64(doi[d]) * orc_bf16_to_f64(vg[jo + d]);
-          const double ds = p[x] * (dp - delta);
-          double* dqi = dq + ((size_t)i * Hq + h) * D;
-          double* dkj = dk + (size_t)g * N * D + jo;
-          double* dvj = dv + (size_t)g * N * D + jo;
+          for (int d = 0; d < D; ++d) dp += di[d] * vr[d];
+          const double ds = p * (dp - delta);
+          for (int d = 0; d < D; ++d) dqi[d] += scale * ds * kr[d];
+        }
+        rmax[(size_t)i * Hq + h] = mx;
+        rden[(size_t)i * Hq + h] = den;
+        rdel[(size_t)i * Hq + h] = delta;
+      }
+    }
+    free(lg);
+    free(toks);
+    free(o);
+  }
+  /* pass 2: keys */
+#pragma omp parallel for collapse(2) schedule(dynamic, 16)
+  for (int g = 0; g < G; ++g) {
+    for (int j = 0; j < N; ++j) {
+      const double* kr = kf + ((size_t)g * N + j) * D;
+      const double* vr = vf + ((size_t)g * N + j) * D;
+      double* dkj = dk + ((size_t)g * N + j) * D;
+      double* dvj = dv + ((size_t)g * N + j) * D;
+      for (int d = 0; d < D; ++d) {
+        dkj[d] = 0.0;
+        dvj[d] = 0.0;
+      }
+      const int b = j / B;
+      for (int i = j; i < N; ++i) {
+        const uint32_t* m = umask + ((size_t)g * T + i / Tq) * W;
+        if (!((m[b / 32] >> (b % 32)) & 1u)) continue;
+        for (int hh = 0; hh < r; ++hh) {
+          int h = g * r + hh;
+          const double* qi = qf + ((size_t)i * Hq + h) * D;
+          const double* di = of + ((size_t)i * Hq + h) * D;
+          double dot = 0.0, dp = 0.0;
           for (int d = 0; d < D; ++d) {
-            dqi[d] += scale * ds * orc_bf16_to_f64(kg[jo + d]);
-            dkj[d] += scale * ds * orc_bf16_to_f64(qi[d]);
-            dvj[d] += p[x] * orc_bf16_to_f64(doi[d]);
+            dot += qi[d] * kr[d];
+            dp += di[d] * vr[d];
+          }
+          const double p = exp(scale * dot - rmax[(size_t)i * Hq + h]) / rden[(size_t)i * Hq + h];
+          const double ds = p * (dp - rdel[(size_t)i * Hq + h]);
+          for (int d = 0; d < D; ++d) {
+            dvj[d] += p * di[d];
+            dkj[d] += scale * ds * qi[d];
           }
         }
       }
     }
   }
-  free(toks);
-  free(p);
-  free(o);
+  free(qf);
+  free(of);
+  free(kf);
+  free(vf);
+  free(rmax);
+  free(rden);
+  free(rdel);
 }
 
 /* ---------------------------------------------------------------- decode ----------------------- */
