@@ -35,11 +35,13 @@ SGQA_OP_PREFILL = 4
 SGQA_OP_DECODE = 5
 SGQA_OP_ATTEND_MASKED = 6
 SGQA_OP_PREFILL_MASKED = 7
+SGQA_OP_ATTEND_BWD = 8
 
 # Every symbol include/sgqa.h declares.
 EXPORTED = ("sgqa_abi_version", "sgqa_status_string", "sgqa_workspace_size", "sgqa_compress", "sgqa_index_topk",
             "sgqa_union", "sgqa_attend", "sgqa_prefill", "sgqa_decode", "sgqa_decode_varlen", "sgqa_append",
-            "sgqa_decode_fp8", "sgqa_index_union", "sgqa_attend_masked", "sgqa_prefill_masked")
+            "sgqa_decode_fp8", "sgqa_index_union", "sgqa_attend_masked", "sgqa_prefill_masked",
+            "sgqa_attend_fwd", "sgqa_attend_bwd")
 
 
 class sgqa_pages(ctypes.Structure):
@@ -140,9 +142,11 @@ def lib() -> ctypes.CDLL:
         L.sgqa_index_union.argtypes = [PP, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.sgqa_attend_masked.argtypes = [PP, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.sgqa_prefill_masked.argtypes = [PP, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.sgqa_attend_fwd.argtypes = [PP, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.sgqa_attend_bwd.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         for name in ("sgqa_compress", "sgqa_index_topk", "sgqa_union", "sgqa_attend", "sgqa_prefill", "sgqa_decode",
                      "sgqa_decode_varlen", "sgqa_append", "sgqa_decode_fp8", "sgqa_index_union",
-                     "sgqa_attend_masked", "sgqa_prefill_masked"):
+                     "sgqa_attend_masked", "sgqa_prefill_masked", "sgqa_attend_fwd", "sgqa_attend_bwd"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -254,6 +258,29 @@ def sgqa_prefill(p: Params, q, k, v, idx_q, idx_w, idx_k, out, ws, stream=None) 
             _ptr(out, "out", torch.bfloat16, (N, Hq, D)))
     _check(lib().sgqa_prefill(ctypes.byref(p.c()), *args, _ptr(ws, "ws", torch.uint8), ws.numel(),
                               _stream(stream)), "sgqa_prefill")
+
+
+def sgqa_attend_fwd(p: Params, q, k, v, umask, ucount, out, lse, stream=None) -> None:
+    N, Hq, G, D = p.n_tokens, p.n_q_heads, p.n_kv_heads, p.head_dim
+    args = (_ptr(q, "q", torch.bfloat16, (N, Hq, D)), _ptr(k, "k", torch.bfloat16, (G, N, D)),
+            _ptr(v, "v", torch.bfloat16, (G, N, D)),
+            _ptr(umask, "umask", torch.int32, (G, p.n_tiles, p.n_words)),
+            _ptr(ucount, "ucount", torch.int32, (G, p.n_tiles)), _ptr(out, "out", torch.bfloat16, (N, Hq, D)),
+            _ptr(lse, "lse", torch.float32, (N, Hq)))
+    _check(lib().sgqa_attend_fwd(ctypes.byref(p.c()), *args, None, 0, _stream(stream)), "sgqa_attend_fwd")
+
+
+def sgqa_attend_bwd(p: Params, q, k, v, umask, ucount, out, lse, dout, dq, dk, dv, ws, stream=None) -> None:
+    N, Hq, G, D = p.n_tokens, p.n_q_heads, p.n_kv_heads, p.head_dim
+    args = (_ptr(q, "q", torch.bfloat16, (N, Hq, D)), _ptr(k, "k", torch.bfloat16, (G, N, D)),
+            _ptr(v, "v", torch.bfloat16, (G, N, D)),
+            _ptr(umask, "umask", torch.int32, (G, p.n_tiles, p.n_words)),
+            _ptr(ucount, "ucount", torch.int32, (G, p.n_tiles)), _ptr(out, "out", torch.bfloat16, (N, Hq, D)),
+            _ptr(lse, "lse", torch.float32, (N, Hq)), _ptr(dout, "dout", torch.bfloat16, (N, Hq, D)),
+            _ptr(dq, "dq", torch.bfloat16, (N, Hq, D)), _ptr(dk, "dk", torch.bfloat16, (G, N, D)),
+            _ptr(dv, "dv", torch.bfloat16, (G, N, D)))
+    _check(lib().sgqa_attend_bwd(ctypes.byref(p.c()), *args, _ptr(ws, "ws", torch.uint8), ws.numel(),
+                                 _stream(stream)), "sgqa_attend_bwd")
 
 
 def sgqa_attend_masked(p: Params, q, k, v, topk, umask, ucount, out, ws, stream=None) -> None:

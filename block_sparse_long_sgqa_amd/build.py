@@ -15,7 +15,8 @@ import sys
 _HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(_HERE, "csrc")
 LIB = os.path.join(_HERE, "libsgqa.so")
-SOURCES = ["sgqa_api.hip", "compress.hip", "index_topk.hip", "decode_select.hip", "union.hip", "attend.hip"]
+SOURCES = ["sgqa_api.hip", "compress.hip", "index_topk.hip", "decode_select.hip", "union.hip", "attend.hip",
+           "attend_bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

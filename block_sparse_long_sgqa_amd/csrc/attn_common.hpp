@@ -1,0 +1,313 @@
+// attn_common.hpp -- device helpers shared by the forward and backward gathered-block attention
+// kernels: tile geometry, the MFMA chunk of the online-softmax forward, LDS layouts and gathers.
+// Everything lives in an unnamed namespace: each translation unit gets its own copy.
+#pragma once
+
+#include <type_traits>
+
+#include "sgqa_device.hpp"
+#include "sgqa_internal.hpp"
+
+namespace sgqa {
+
+namespace {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kD = 128;
+constexpr int kKeys = 64;                          // keys per chunk
+constexpr int kKRowBytes = 272;                    // K row: 256 B + 16 B pad (bank spread for 16-B reads)
+constexpr int kKSlotsPerRow = kKRowBytes / 16;     // 17 slots of 16 B, the last one is padding
+constexpr int kKTileBytes = kKeys * kKRowBytes;    // 17408 B
+constexpr int kKTileInsts = kKeys * kKSlotsPerRow / 64;  // 17 wave-wide 16-byte loads fill the K tile
+constexpr int kVTileBytes = kKeys * 256;           // V rows unpadded; 16-B pieces XOR-swizzled by row
+constexpr int kVTileInsts = kVTileBytes / 1024;    // 16
+constexpr int kSelTableWords = 64;                 // masked variant: membership words of a chunk
+constexpr int kStageBytes = kKTileBytes + kVTileBytes + kKeys * 4 + kSelTableWords * 4;  // K, V, tokens, members
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kMinit = -1.0e30f;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int QT>
+struct AttnState {
+  f32x16 o[QT][4];  // O^T tiles: [d-tile][32 d x 32 rows], column = this lane's row
+  float m[QT];      // running max (log2 domain), identical in lanes l and l^32
+  float l[QT];      // this lane's part of the running denominator (lanes l and l^32 hold halves)
+};
+
+template <int QT>
+__device__ __forceinline__ void state_init(AttnState<QT>& st) {
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) st.o[qt][dt][j] = 0.0f;
+    st.m[qt] = kMinit;
+    st.l[qt] = 0.0f;
+  }
+}
+
+// Physical 16-byte piece of logical piece p in V row `row`: XOR with 4 * (row % 4). A transposing
+// read phase (32 lanes) touches 4 consecutive rows x 4 consecutive pieces; the swizzle spreads them
+// over all 16 piece positions, i.e. all 64 banks once.
+__device__ __forceinline__ int v_phys(int row, int p) { return p ^ ((row & 3) << 2); }
+
+// Per-lane LDS byte offsets inside a stage (constant over the chunks).
+struct LaneOffsets {
+  int k;     // K A-operand: key row (l % 32), 16-byte piece (l / 32); + kt * 32 rows + ks * 32 B
+  int v[4];  // V transposing read for d-tile dt: row 4 * khalf + (s16 / 4), d 32 dt + 16 dgrp + 4 (s16 % 4)
+  int tok;   // the chunk's token table
+};
+
+// v_tile: byte offset of the V tile inside a stage (the token table follows it).
+__device__ __forceinline__ LaneOffsets lane_offsets(int v_tile = kKTileBytes) {
+  const int l = lane_id();
+  LaneOffsets o;
+  o.k = (l & 31) * kKRowBytes + (l >> 5) * 16;
+  const int grp = l >> 4, s16 = l & 15;
+  const int row = 4 * (grp >> 1) + (s16 >> 2);  // + 16 ss + 8 r (multiples of 4: same swizzle)
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    const int piece = 4 * dt + 2 * (grp & 1) + ((s16 & 3) >> 1);
+    o.v[dt] = v_tile + row * 256 + 16 * v_phys(row, piece) + 8 * (s16 & 1);
+  }
+  o.tok = v_tile + kVTileBytes;
+  return o;
+}
+
+struct NoOp {
+  __device__ void operator()() const {}
+};
+
+// One 64-key chunk for the QT Q tiles of this wave.
+//   stage: K tile, V tile (row-major, 272-byte rows), token table (INT_MAX = invalid key), at the
+//          offsets of lo
+//   row_pos[qt]: query position of this lane's Q row in tile qt (for the causal mask)
+//   KREG: the K operands come from kreg[ks * 2 + kt] (registers) instead of the K tile; after()
+//         runs once the score products have consumed them.
+//   MASK: 0 = no key of the chunk can be masked, 1 = apply the mask, 2 = decided by `masked`.
+//   SEL (with MASK = 1): a key also needs its block to be a member of the Q row's own set: the
+//         word mt[e * nqw + ql / 32] of the chunk's membership table holds, for block entry
+//         e = key >> bs of the chunk, one bit per query of the workgroup; ql[qt] is this lane's
+//         query index within the workgroup.
+template <int QT, int MASK = 2, bool KREG = false, typename After = NoOp, bool SEL = false>
+__device__ __forceinline__ void attn_chunk(const uint8_t* stage, const LaneOffsets& lo, const bf16x8 (&qreg)[QT][8],
+                                           AttnState<QT>& st, float scale_log2, bool masked_rt,
+                                           const int (&row_pos)[QT], const bf16x8* kreg = nullptr,
+                                           After after = After(), const uint32_t* mt = nullptr, int nqw = 0,
+                                           const int* ql = nullptr, int bs = 0) {
+  const bool masked = MASK == 2 ? masked_rt : MASK == 1;
+  const int l = lane_id();
+  const int hi = l >> 5;
+  f32x16 s[QT][2];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s[qt][kt][j] = 0.0f;
+  if constexpr (KREG) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) s[qt][kt] = mfma32(kreg[ks * 2 + kt], qreg[qt][ks], s[qt][kt]);
+  } else {
+    // S^T = K Q^T: the K operands of step ks+2 are read while the MFMAs of step ks run.
+    const uint8_t* kp = stage + lo.k;
+    bf16x8 ka[3][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      ka[ks][0] = *reinterpret_cast<const bf16x8*>(kp + ks * 32);
+      ka[ks][1] = *reinterpret_cast<const bf16x8*>(kp + 32 * kKRowBytes + ks * 32);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      if (ks < 6) {
+        ka[(ks + 2) % 3][0] = *reinterpret_cast<const bf16x8*>(kp + (ks + 2) * 32);
+        ka[(ks + 2) % 3][1] = *reinterpret_cast<const bf16x8*>(kp + 32 * kKRowBytes + (ks + 2) * 32);
+      }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) s[qt][kt] = mfma32(ka[ks % 3][kt], qreg[qt][ks], s[qt][kt]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  after();
+
+  // Tokens of this lane's keys: key kt*32 + 8*a + 4*hi + (0..3), four consecutive ints.
+  int4 tk[2][4];
+  if (masked) {
+    const int* tok = reinterpret_cast<const int*>(stage + (KREG ? lo.tok : kKTileBytes + kVTileBytes));
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) tk[kt][a] = *reinterpret_cast<const int4*>(tok + kt * 32 + 8 * a + 4 * hi);
+  }
+
+  // SEL: keys outside the row's set get the invalid token, so the causal test masks them too.
+  if constexpr (SEL) {
+    static_assert(QT == 1, "the membership folds into the token table of the single Q tile");
+    const uint32_t* col = mt + (ql[0] >> 5);
+    const int sh = ql[0] & 31;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int key = kt * 32 + 8 * a + 4 * hi;
+        int4& t4 = tk[kt][a];
+        if (bs >= 2) {  // the four keys share one block
+          if (!((col[(key >> bs) * nqw] >> sh) & 1u)) t4 = make_int4(0x7FFFFFFF, 0x7FFFFFFF, 0x7FFFFFFF, 0x7FFFFFFF);
+        } else {
+          if (!((col[(key >> bs) * nqw] >> sh) & 1u)) t4.x = 0x7FFFFFFF;
+          if (!((col[((key + 1) >> bs) * nqw] >> sh) & 1u)) t4.y = 0x7FFFFFFF;
+          if (!((col[((key + 2) >> bs) * nqw] >> sh) & 1u)) t4.z = 0x7FFFFFFF;
+          if (!((col[((key + 3) >> bs) * nqw] >> sh) & 1u)) t4.w = 0x7FFFFFFF;
+        }
+      }
+  }
+
+  bf16x8 pb[QT][4];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        float x = s[qt][kt][j];
+        if (masked) {
+          const int4 t4 = tk[kt][j >> 2];
+          const int t = (j & 3) == 0 ? t4.x : (j & 3) == 1 ? t4.y : (j & 3) == 2 ? t4.z : t4.w;
+          if (t > row_pos[qt]) x = kNegInf;
+        }
+        s[qt][kt][j] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(st.m[qt], mx * scale_log2);
+    if (ballot(m_new > st.m[qt])) {  // rescale only when some row's max moved
+      const float alpha = fast_exp2(st.m[qt] - m_new);
+      st.l[qt] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) st.o[qt][dt][j] *= alpha;
+      st.m[qt] = m_new;
+    }
+    float sum = 0.0f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float p = fast_exp2(__builtin_fmaf(s[qt][kt][j], scale_log2, -m_new));
+        s[qt][kt][j] = p;
+        sum += p;
+      }
+    st.l[qt] += sum;
+#pragma unroll
+    for (int ss = 0; ss < 4; ++ss)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[qt][ss][e] = (__bf16)s[qt][ss >> 1][8 * (ss & 1) + e];
+  }
+
+  // O^T += V^T P^T. The V^T operand of lane l (row d, 8 keys) comes from two transposing reads,
+  // each returning 4 keys of this lane's d, in the key order the score registers already have.
+  auto vread = [&](int step) -> bf16x8 {
+    const int dt = step >> 2, ss = step & 3;
+    const uint8_t* a0 = stage + lo.v[dt] + (16 * ss) * 256;
+    const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
+    const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0 + 8 * 256));
+    const i16x8 cat = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, cat);
+  };
+  bf16x8 va[3];
+  va[0] = vread(0);
+  va[1] = vread(1);
+#pragma unroll
+  for (int step = 0; step < 16; ++step) {
+    if (step < 14) va[(step + 2) % 3] = vread(step + 2);
+    const int dt = step >> 2, ss = step & 3;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) st.o[qt][dt] = mfma32(va[step % 3], pb[qt][ss], st.o[qt][dt]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Gather one chunk of 64 keys straight from global memory into the K and V tiles of `stage`
+// (global_load_lds: every wave-wide instruction fills 64 consecutive 16-byte slots). K: slot s of
+// the tile is row s / 17, piece s % 17 (piece 16 is padding). V: slot s is row s / 16, physical
+// piece s % 16, holding logical piece v_phys(row, s % 16). Invalid keys read row 0 of the group
+// (finite data, always masked out through the token table). The waves of the workgroup split the
+// 17 + 16 instructions; the first wave writes the token table.
+template <int NT, typename TokFn>
+__device__ __forceinline__ void chunk_issue(uint8_t* stage, const uint16_t* kbase, const uint16_t* vbase,
+                                            TokFn tok_of) {
+  constexpr int kWaves = NT / 64;
+  constexpr int kInsts = kKTileInsts + kVTileInsts;
+  const int l = lane_id();
+  // NT == 64: one wave fills the stage alone (it may be any wave of a larger workgroup).
+  const int tid = kWaves == 1 ? l : (int)threadIdx.x;
+  const int wave = kWaves == 1 ? 0 : (int)threadIdx.x >> 6;
+#pragma unroll
+  for (int x = 0; x < (kInsts + kWaves - 1) / kWaves; ++x) {
+    const int inst = wave + x * kWaves;
+    if (inst < kInsts) {
+      const bool is_v = inst >= kKTileInsts;
+      const int ti = is_v ? inst - kKTileInsts : inst;
+      const int slot = ti * 64 + l;
+      int row, piece;
+      if (is_v) {
+        row = slot >> 4;
+        piece = v_phys(row, slot & 15);
+      } else {
+        row = slot / kKSlotsPerRow;
+        piece = slot - row * kKSlotsPerRow;
+        if (piece == 16) piece = 0;  // padding slot: any in-bounds data
+      }
+      int tkn = tok_of(row);
+      if (tkn < 0) tkn = 0;
+      const uint16_t* src = (is_v ? vbase : kbase) + (long long)tkn * kD + piece * 8;
+      uint8_t* dst = stage + (is_v ? kKTileBytes : 0) + ti * 1024;
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)dst, 16, 0, 0);
+    }
+  }
+  if (tid < kKeys) {
+    const int t = tok_of(tid);
+    reinterpret_cast<int*>(stage + kKTileBytes + kVTileBytes)[tid] = t >= 0 ? t : 0x7FFFFFFF;
+  }
+}
+
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Block-wide exclusive scan of one value per thread (NT threads); returns the exclusive prefix and
+// writes the total to *total. `scratch` holds NT/64 ints of LDS.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
+  const int l = lane_id(), wave = threadIdx.x >> 6;
+  const int incl = (int)wave_prefix_sum((uint32_t)v);
+  if (l == 63) scratch[wave] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int x = 0; x < NT / 64; ++x) {
+    const int s = scratch[x];
+    if (x < wave) before += s;
+    all += s;
+  }
+  __syncthreads();
+  *total = all;
+  return before + incl - v;
+}
+
+}  // namespace
+
+}  // namespace sgqa

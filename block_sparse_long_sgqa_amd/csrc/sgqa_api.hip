@@ -61,7 +61,7 @@ float scale_of(const sgqa_params* p) {
 
 // Checks shared by the calls; `need` selects which groups of fields matter.
 enum { NEED_INDEX = 1, NEED_ATTN = 2, NEED_SELECT = 4, NEED_UNION = 8, NEED_LIST = 16, NEED_DECODE = 32,
-       NEED_MASKED = 64 };
+       NEED_MASKED = 64, NEED_BWD = 128 };
 
 int check_params(const sgqa_params* p, int need, bool prefill) {
   if (!p) return SGQA_ERR_NULL;
@@ -80,6 +80,9 @@ int check_params(const sgqa_params* p, int need, bool prefill) {
     if (p->idx_heads != 4 || p->idx_dim != 64) return SGQA_ERR_SHAPE;
     if (p->n_kv_heads > 16) return SGQA_ERR_SHAPE;
     if (index_topk_lds_min(kb_of(p)) > kGfx950LdsBytes) return SGQA_ERR_SHAPE;
+  }
+  if (need & NEED_BWD) {
+    if (attend_bwd_lds_dq(p->n_tokens, p->block) > kGfx950LdsBytes) return SGQA_ERR_SHAPE;
   }
   if (need & NEED_MASKED) {
     if (attend_masked_loads(p->n_q_heads, p->n_kv_heads, p->block) == 0) return SGQA_ERR_SHAPE;
@@ -220,6 +223,10 @@ int sgqa_workspace_size(const sgqa_params* p, int op, size_t* bytes) {
       st = check_params(p, NEED_INDEX | NEED_SELECT | NEED_DECODE | NEED_ATTN, false);
       if (st == SGQA_OK) *bytes = decode_layout(p, nullptr).bytes;
       return st;
+    case SGQA_OP_ATTEND_BWD:
+      st = check_params(p, NEED_ATTN | NEED_UNION | NEED_LIST | NEED_BWD, true);
+      if (st == SGQA_OK) *bytes = round_up((size_t)p->n_tokens * p->n_q_heads * 4);
+      return st;
     case SGQA_OP_ATTEND_MASKED:
       st = check_params(p, NEED_ATTN | NEED_UNION | NEED_LIST | NEED_MASKED, true);
       if (st == SGQA_OK) *bytes = selbits_bytes(p);
@@ -292,6 +299,39 @@ int sgqa_attend(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k, co
   if (!device_ok()) return SGQA_ERR_DEVICE;
   return status_of(launch_attend(q, k, v, umask, ucount, out, p->n_tokens, p->n_q_heads, p->n_kv_heads, p->block,
                                  p->union_tile, scale_of(p), (hipStream_t)stream));
+}
+
+int sgqa_attend_fwd(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k, const sgqa_bf16* v,
+                    const uint32_t* umask, const int32_t* ucount, sgqa_bf16* out, float* lse, void* ws,
+                    size_t ws_bytes, sgqa_stream stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int st = check_params(p, NEED_ATTN | NEED_UNION | NEED_LIST, true);
+  if (st) return st;
+  if (!q || !k || !v || !umask || !ucount || !out || !lse) return SGQA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(umask) || !aligned16(ucount) || !aligned16(out) ||
+      !aligned16(lse))
+    return SGQA_ERR_ALIGN;
+  if (!device_ok()) return SGQA_ERR_DEVICE;
+  return status_of(launch_attend(q, k, v, umask, ucount, out, p->n_tokens, p->n_q_heads, p->n_kv_heads, p->block,
+                                 p->union_tile, scale_of(p), (hipStream_t)stream, lse));
+}
+
+int sgqa_attend_bwd(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k, const sgqa_bf16* v,
+                    const uint32_t* umask, const int32_t* ucount, const sgqa_bf16* out, const float* lse,
+                    const sgqa_bf16* dout, sgqa_bf16* dq, sgqa_bf16* dk, sgqa_bf16* dv, void* ws, size_t ws_bytes,
+                    sgqa_stream stream) {
+  int st = check_params(p, NEED_ATTN | NEED_UNION | NEED_LIST | NEED_BWD, true);
+  if (st) return st;
+  if (!q || !k || !v || !umask || !ucount || !out || !lse || !dout || !dq || !dk || !dv) return SGQA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(umask) || !aligned16(ucount) || !aligned16(out) ||
+      !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(ws))
+    return SGQA_ERR_ALIGN;
+  if (!ws || ws_bytes < round_up((size_t)p->n_tokens * p->n_q_heads * 4)) return SGQA_ERR_WORKSPACE;
+  if (!device_ok()) return SGQA_ERR_DEVICE;
+  return status_of(launch_attend_bwd(q, k, v, umask, out, lse, dout, dq, dk, dv, static_cast<float*>(ws),
+                                     p->n_tokens, p->n_q_heads, p->n_kv_heads, p->block, p->union_tile, scale_of(p),
+                                     (hipStream_t)stream));
 }
 
 int sgqa_attend_masked(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k, const sgqa_bf16* v,

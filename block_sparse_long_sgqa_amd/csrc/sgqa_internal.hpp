@@ -57,9 +57,18 @@ hipError_t launch_union(const int32_t* topk, uint32_t* umask, int32_t* ucount, i
                         int kb, int tile, hipStream_t stream);
 
 // Gathered-block prefill attention over the tile unions.
+// lse (optional, [N][Hq] fp32): base-2 log-sum-exp of every row's scaled logits, for the backward.
 hipError_t launch_attend(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint32_t* umask,
                          const int32_t* ucount, uint16_t* out, int n_tokens, int n_q_heads, int n_groups, int block,
-                         int tile, float scale, hipStream_t stream);
+                         int tile, float scale, hipStream_t stream, float* lse = nullptr);
+
+// Backward of launch_attend given its output and lse: dq [N][Hq][D], dk/dv [G][N][D] (bf16), from
+// dout [N][Hq][D]; delta [N][Hq] fp32 is scratch (rowwise <dout, out>).
+hipError_t launch_attend_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint32_t* umask,
+                             const uint16_t* out, const float* lse, const uint16_t* dout, uint16_t* dq, uint16_t* dk,
+                             uint16_t* dv, float* delta, int n_tokens, int n_q_heads, int n_groups, int block,
+                             int tile, float scale, hipStream_t stream);
+size_t attend_bwd_lds_dq(int n_tokens, int block);
 
 // Decode selection: K-bar cache [S][L/B][64], qi [S][G][4][64] -> sel [S][G][kb] (and topk_out if not
 // null). lens (device, nullable): per-sequence context lengths (clamped to [1, n_tokens]); null =

@@ -71,7 +71,8 @@ enum {
   SGQA_OP_PREFILL = 4,
   SGQA_OP_DECODE = 5,
   SGQA_OP_ATTEND_MASKED = 6,
-  SGQA_OP_PREFILL_MASKED = 7
+  SGQA_OP_PREFILL_MASKED = 7,
+  SGQA_OP_ATTEND_BWD = 8
 };
 
 /* Sizes of one call. Symbols: N tokens, S sequences, Hq query heads, G KV groups (KV heads),
@@ -263,6 +264,31 @@ int sgqa_decode_fp8(const sgqa_params* p, const sgqa_bf16* q, const uint8_t* k_c
                     const float* kv_scale, const sgqa_pages* pages, const sgqa_bf16* blk_k,
                     const sgqa_bf16* idx_q, const float* idx_w, const int32_t* seq_lens, int32_t* topk_out,
                     sgqa_bf16* out, void* ws, size_t ws_bytes, sgqa_stream stream);
+
+/* ---------------------------------------------------------------- training: attention gradient
+ * Sparse GQA is used in training ("Inside Step 5 Preview", Sparse GQA, and the training sections):
+ * the gradient below is that of sgqa_attend for fixed selections (the selection and the indexer get
+ * no gradient; the pages leave the indexer's training signal open).
+ *
+ * Forward of sgqa_attend that also returns, for every row, the base-2 log-sum-exp of its scaled
+ * logits: lse[i][h] = log2( sum_{j in J} 2^(sigma * log2(e) * <q[i][h], k[g][j]>) ). Same arguments
+ * and result as sgqa_attend otherwise; lse [N][Hq] fp32 DEVICE. No workspace. */
+int sgqa_attend_fwd(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k, const sgqa_bf16* v,
+                    const uint32_t* umask, const int32_t* ucount, sgqa_bf16* out, float* lse, void* ws,
+                    size_t ws_bytes, sgqa_stream stream);
+
+/* Gradient of sgqa_attend for an upstream gradient dout [N][Hq][D] bf16, given the forward's out and
+ * lse (sgqa_attend_fwd). With p the row's softmax over J and delta_i = <dout_i, out_i>:
+ *   dv[g][j] = sum over rows (i, h of g) with j in J of p_ij dout[i][h]
+ *   dk[g][j] = sigma * sum over those rows of p_ij (<dout[i][h], v[g][j]> - delta_i) q[i][h]
+ *   dq[i][h] = sigma * sum_{j in J} p_ij (<dout[i][h], v[g][j]> - delta_i) k[g][j]
+ * dq [N][Hq][D], dk, dv [G][N][D] bf16 out (fp32 sums, one bf16 rounding; keys no row attends get 0).
+ * Deterministic: every sum has a fixed order (no floating-point atomics). Workspace:
+ * sgqa_workspace_size(p, SGQA_OP_ATTEND_BWD) (the deltas). */
+int sgqa_attend_bwd(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k, const sgqa_bf16* v,
+                    const uint32_t* umask, const int32_t* ucount, const sgqa_bf16* out, const float* lse,
+                    const sgqa_bf16* dout, sgqa_bf16* dq, sgqa_bf16* dk, sgqa_bf16* dv, void* ws,
+                    size_t ws_bytes, sgqa_stream stream);
 
 /* ---------------------------------------------------------------- masked-union variant
  * The pages group the top-k results of adjacent prefill tokens so that overlapping K/V reads are

@@ -1,0 +1,136 @@
+"""Attention gradient on the GPU (sgqa_attend_fwd + sgqa_attend_bwd) against the oracle's attend_bwd.
+
+Bar: the gradients are sums of many bf16-rounded products (P and dS enter the matrix cores as
+bf16, as do q, k, v, dout), so they are compared relative to each tensor's scale: with s = the
+largest |reference| of the tensor, max |got - ref| <= 2e-2 s and mean |got - ref| <= 2e-3 s.
+A bf16 operand carries a relative rounding error of at most 2^-9 ~ 2e-3; a sum of n such terms with
+cancellation (the dS of a row sum to 0) keeps its absolute error near 2^-9 * sqrt(n) * term size,
+well inside 2e-2 s for the sizes here. Full-size runs check exact invariants instead.
+"""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+from tests.gpu_common import OracleChain, bits, bf16_to_f64, params_of, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+MAX_REL = 2e-2
+MEAN_REL = 2e-3
+
+
+# Backward cases: several tiles and ragged tails for every block size of interest, sized so that
+# the fp64 oracle gradient takes seconds.
+BWD = {
+    "tiny": datagen.TINY,
+    "g2_b8": datagen.PREFILL.replace(name="bwd_g2_b8", n_tokens=1200 + 5, n_q_heads=16, n_kv_heads=2,
+                                     topk_tokens=256, union_tile=64),
+    "b4_tile24": datagen.PREFILL.replace(name="bwd_b4", n_tokens=900, n_q_heads=16, n_kv_heads=2, block=4,
+                                         topk_tokens=128, union_tile=24),
+    "b1_token": datagen.PREFILL.replace(name="bwd_b1", n_tokens=600, n_q_heads=8, n_kv_heads=1, block=1,
+                                        topk_tokens=64, union_tile=16),
+    "b16_iid": datagen.PREFILL.replace(name="bwd_b16", n_tokens=1000 + 17, n_q_heads=32, n_kv_heads=4, block=16,
+                                       topk_tokens=256, union_tile=32, qi_mode="iid"),
+    "tile1": datagen.PREFILL.replace(name="bwd_t1", n_tokens=500, n_q_heads=8, n_kv_heads=1, topk_tokens=64,
+                                     union_tile=1),
+    "b64_r4": datagen.PREFILL.replace(name="bwd_b64", n_tokens=1100 + 3, n_q_heads=16, n_kv_heads=4, block=64,
+                                      topk_tokens=256, union_tile=128),
+}
+
+
+@pytest.fixture(scope="module")
+def sg():
+    import block_sparse_long_sgqa_amd as sg
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    sg.lib()
+    return sg
+
+
+def assert_close_grad(got_bf16, want, what):
+    got = bf16_to_f64(bits(got_bf16)).reshape(want.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite"
+    scale = max(1e-6, float(np.abs(want).max()))
+    err = np.abs(got - want)
+    say(f"{what}: scale={scale:.3e} max_rel={err.max() / scale:.3e} mean_rel={err.mean() / scale:.3e}")
+    assert err.max() <= MAX_REL * scale, f"{what}: max error {err.max()} (scale {scale})"
+    assert err.mean() <= MEAN_REL * scale, f"{what}: mean error {err.mean()} (scale {scale})"
+
+
+def run_fwd_bwd(sg, p, xd, umask, ucount, dout):
+    N, Hq, G, D = p.n_tokens, p.n_q_heads, p.n_kv_heads, p.head_dim
+    out = torch.empty((N, Hq, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((N, Hq), dtype=torch.float32, device="cuda")
+    sg.sgqa_attend_fwd(p, xd["q"], xd["k"], xd["v"], umask, ucount, out, lse)
+    dq = torch.empty((N, Hq, D), dtype=torch.bfloat16, device="cuda")
+    dk = torch.empty((G, N, D), dtype=torch.bfloat16, device="cuda")
+    dv = torch.empty((G, N, D), dtype=torch.bfloat16, device="cuda")
+    ws = sg.workspace(p, sg.SGQA_OP_ATTEND_BWD)
+    sg.sgqa_attend_bwd(p, xd["q"], xd["k"], xd["v"], umask, ucount, out, lse, dout, dq, dk, dv, ws)
+    torch.cuda.synchronize()
+    return out, lse, dq, dk, dv
+
+
+@pytest.mark.parametrize("name", list(BWD))
+def test_attend_bwd_matches_oracle(sg, name):
+    wl = BWD[name]
+    p = params_of(wl)
+    x = datagen.prefill_inputs(wl)
+    ch = OracleChain(x, p)
+    umask, ucount = oracle.union(ch.topk(), p.n_tokens, p.block, p.union_tile)
+    g = torch.Generator().manual_seed(7)
+    dout = torch.randn((p.n_tokens, p.n_q_heads, p.head_dim), generator=g).to(torch.bfloat16)
+    say(f"attend_bwd {name} N={p.n_tokens} Hq={p.n_q_heads} G={p.n_kv_heads} B={p.block} Tq={p.union_tile}")
+    want_dq, want_dk, want_dv = oracle.attend_bwd(bits(x["q"]), bits(x["k"]), bits(x["v"]), umask, bits(dout),
+                                                  p.block, p.union_tile)
+    xd = to_dev(x)
+    um = torch.from_numpy(umask.view(np.int32)).cuda()
+    uc = torch.from_numpy(ucount).cuda()
+    out, lse, dq, dk, dv = run_fwd_bwd(sg, p, xd, um, uc, dout.cuda())
+    # The forward with lse is the forward.
+    ref = torch.empty_like(out)
+    sg.sgqa_attend(p, xd["q"], xd["k"], xd["v"], um, uc, ref)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    assert_close_grad(dq, want_dq, f"dq {name}")
+    assert_close_grad(dk, want_dk, f"dk {name}")
+    assert_close_grad(dv, want_dv, f"dv {name}")
+    # Deterministic: a second run gives the same bits.
+    _, _, dq2, dk2, dv2 = run_fwd_bwd(sg, p, xd, um, uc, dout.cuda())
+    for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["prefill_32k"])
+def test_attend_bwd_full_size_invariants(sg, name):
+    # At full size: sum_j dv[g][j] = sum over the group's rows of dout (each row's p sums to 1), and
+    # sum_j dk[g][j] = 0 (each row's dS sums to 0), to within the bf16 rounding of the summands.
+    wl = datagen.WORKLOADS[name]
+    p = params_of(wl)
+    x = datagen.prefill_inputs(wl, device="cuda")
+    say(f"attend_bwd {name}: selection and union")
+    umask = torch.empty((p.n_kv_heads, p.n_tiles, p.n_words), dtype=torch.int32, device="cuda")
+    ucount = torch.empty((p.n_kv_heads, p.n_tiles), dtype=torch.int32, device="cuda")
+    blk = torch.empty((p.n_tokens // p.block, p.idx_dim), dtype=torch.bfloat16, device="cuda")
+    sg.sgqa_compress(p, x["ki"], blk)
+    sg.sgqa_index_union(p, x["qi"], x["w"], blk, umask, ucount)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    dout = torch.randn((p.n_tokens, p.n_q_heads, p.head_dim), generator=gen, device="cuda").to(torch.bfloat16)
+    say(f"attend_bwd {name}: forward + backward")
+    out, lse, dq, dk, dv = run_fwd_bwd(sg, p, x, umask, ucount, dout)
+    r = p.n_q_heads // p.n_kv_heads
+    want_dv = dout.float().view(p.n_tokens, p.n_kv_heads, r, p.head_dim).sum(dim=(0, 2))  # [G][D]
+    got_dv = dv.float().sum(dim=1)
+    dv_scale = dv.float().abs().max().item()
+    err = (got_dv - want_dv).abs().max().item()
+    say(f"sum dv error {err:.3e} (|dv| max {dv_scale:.3e})")
+    assert err <= 2e-3 * dv_scale * p.n_tokens ** 0.5
+    got_dk = dk.float().sum(dim=1)
+    dk_scale = dk.float().abs().max().item()
+    err = got_dk.abs().max().item()
+    say(f"sum dk {err:.3e} (|dk| max {dk_scale:.3e})")
+    assert err <= 2e-3 * dk_scale * p.n_tokens ** 0.5
+    assert torch.isfinite(dq.float()).all()
