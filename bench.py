@@ -151,6 +151,7 @@ def bench_prefill(sg, datagen, torch, wl, steps, warmup):
         for k, v in enumerate(tm.spans()):
             stage_ms[k] += v / steps
     same = bool(torch.equal(out_full.view(torch.int16), o["out"].view(torch.int16)))
+    variants = bench_variants(sg, torch, p, x, o, steps, warmup)
     pairs = attended_pairs(o["umask"], p.n_tokens, p.block, p.union_tile)
     r = p.n_q_heads // p.n_kv_heads
     attn_flops = 4.0 * p.head_dim * pairs * r
@@ -174,8 +175,56 @@ def bench_prefill(sg, datagen, torch, wl, steps, warmup):
         "compress_bytes": compress_bytes,
         "union_bytes": union_bytes,
         "n_blocks": n_blocks,
+        "variants": variants,
         "x": x,
     }
+    return res
+
+
+def bench_variants(sg, torch, p, x, o, steps, warmup):
+    """The other prefill calls on the same inputs: the fused selection -> union (what sgqa_prefill
+    runs), the masked-union prefill, and the training pair sgqa_attend_fwd + sgqa_attend_bwd."""
+    def timed(fn, n_steps):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n_steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n_steps
+
+    N, Hq, G, D = p.n_tokens, p.n_q_heads, p.n_kv_heads, p.head_dim
+    res = {}
+    m2 = torch.empty_like(o["umask"])
+    c2 = torch.empty_like(o["ucount"])
+    res["index_union_fused_ms"] = timed(lambda: sg.sgqa_index_union(p, x["qi"], x["w"], o["blk_k"], m2, c2), steps)
+    res["index_union_fused_identical"] = bool(torch.equal(m2, o["umask"]) and torch.equal(c2, o["ucount"]))
+    del m2, c2
+    out = torch.empty((N, Hq, D), dtype=torch.bfloat16, device="cuda")
+    ws = sg.workspace(p, sg.SGQA_OP_PREFILL_MASKED)
+    res["prefill_masked_ms"] = timed(
+        lambda: sg.sgqa_prefill_masked(p, x["q"], x["k"], x["v"], x["qi"], x["w"], x["ki"], out, ws), max(1, steps // 3))
+    del ws
+    torch.cuda.empty_cache()
+    lse = torch.empty((N, Hq), dtype=torch.float32, device="cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20261202)
+    dout = torch.randn((N, Hq, D), generator=gen, device="cuda").to(torch.bfloat16)
+    dq = torch.empty_like(out)
+    dk = torch.empty((G, N, D), dtype=torch.bfloat16, device="cuda")
+    dv = torch.empty_like(dk)
+    ws = sg.workspace(p, sg.SGQA_OP_ATTEND_BWD)
+    res["attend_fwd_lse_ms"] = timed(
+        lambda: sg.sgqa_attend_fwd(p, x["q"], x["k"], x["v"], o["umask"], o["ucount"], out, lse), steps)
+    res["attend_bwd_ms"] = timed(
+        lambda: sg.sgqa_attend_bwd(p, x["q"], x["k"], x["v"], o["umask"], o["ucount"], out, lse, dout, dq, dk, dv, ws),
+        max(1, steps // 3))
+    del out, lse, dout, dq, dk, dv, ws
+    torch.cuda.empty_cache()
     return res
 
 
@@ -531,6 +580,10 @@ def main():
             "union": {"bound": "hbm", "GB_per_s": res["union_bytes"] / (st["union"] / 1e3) / 1e9},
             "attend": {"bound": "mfma", "TFLOP_per_s": attn_tflops},
         },
+        "variants": dict(res["variants"], **{
+            # the four gradient products dV = P^T dO, dP = dO V^T, dQ = dS K, dK = dS^T Q over the
+            # attended pairs (the score recompute is not counted)
+            "attend_bwd_TFLOP_per_s": 2.0 * res["attn_flops"] / (res["variants"]["attend_bwd_ms"] / 1e3) / 1e12}),
         "union_inflation": res["union_inflation"],
         "attended_pairs": res["attended_pairs"],
         "prefill_matches_single_calls": res["prefill_matches_single_calls"],

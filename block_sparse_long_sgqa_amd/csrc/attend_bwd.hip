@@ -31,7 +31,8 @@ namespace sgqa {
 
 namespace {
 
-constexpr int kBwdWaves = SGQA_BWD_WAVES;
+constexpr int kBwdWaves = SGQA_BWD_WAVES;  // dk/dv workgroup (one wave per SIMD)
+constexpr int kDqWaves = 8;                 // dq workgroup (two waves per SIMD, as the forward)
 // dq stage: padded K tile, padded V tile, swizzled K tile, token table.
 constexpr int kDqKs = 2 * kKTileBytes;                          // swizzled K tile offset
 constexpr int kDqTok = kDqKs + kVTileBytes;                     // token table offset
@@ -524,7 +525,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void k_bwd_dkdv(const uint16_t* __r
 
 size_t attend_bwd_lds_dq(int n_tokens, int block) {
   const int nbc = (n_tokens + block - 1) / block;
-  return (size_t)2 * kDqStageBytes + 16 * ((kBwdWaves + 4) / 4) + (size_t)((nbc + 7) / 8 * 8) * 2;
+  return (size_t)2 * kDqStageBytes + 16 * ((kDqWaves + 4) / 4) + (size_t)((nbc + 7) / 8 * 8) * 2;
 }
 
 hipError_t launch_attend_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint32_t* umask,
@@ -544,17 +545,17 @@ hipError_t launch_attend_bwd(const uint16_t* q, const uint16_t* k, const uint16_
   const int r = n_q_heads / n_groups;
   const float scale_log2 = scale * 1.4426950408889634f;
   {
-    const int rows_wg = kBwdWaves * 32;
+    const int rows_wg = kDqWaves * 32;
     const int tile_rows = (tile < n_tokens ? tile : n_tokens) * r;
     const int parts = (tile_rows + rows_wg - 1) / rows_wg;
     const int n_pairs = n_tiles * n_groups;
     const size_t lds = attend_bwd_lds_dq(n_tokens, block);
     if (lds > (size_t)max_lds_per_block()) return hipErrorInvalidValue;
     const long long grid = (long long)((n_pairs + 7) / 8) * 8 * parts;
-    auto kern = k_bwd_dq<kBwdWaves>;
+    auto kern = k_bwd_dq<kDqWaves>;
     e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBwdWaves * 64), lds, stream, q, k, v, umask, lse, delta,
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kDqWaves * 64), lds, stream, q, k, v, umask, lse, delta,
                        dout, dq, n_tokens, n_q_heads, n_groups, block, __builtin_ctz(block), tile, scale,
                        scale_log2, n_words, parts, n_pairs);
     e = hipGetLastError();
