@@ -35,7 +35,15 @@
 
 #include "attn_common.hpp"
 
+
 namespace sgqa {
+
+namespace {
+// Prefill LDS held in separate variables (two K tiles, two V tiles, four token tables, two
+// membership tables, the scan words): with one variable per tile the compiler can tell the
+// gathers into one tile from the reads of the other and does not make the reads wait for them.
+constexpr int kAttnStaticBytes = 2 * kKTileBytes + 2 * kVTileBytes + 4 * kKeys * 4 + 2 * kSelTableWords * 4 + 64;
+}  // namespace
 
 
 // ------------------------------------------------------------------------------------ prefill
@@ -58,10 +66,16 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
                                                        float* __restrict__ lse) {
   constexpr int NT = WAVES * 64;
   constexpr int kRowsWg = WAVES * 32 * QT;
+  static_assert(WAVES + 1 <= 16, "scan words");
+  __shared__ __align__(16) uint8_t k_tile0[kKTileBytes];  // K tiles of the even / odd chunks
+  __shared__ __align__(16) uint8_t k_tile1[kKTileBytes];
+  __shared__ __align__(16) uint8_t v_tile0[kVTileBytes];  // V tiles of the even / odd chunks
+  __shared__ __align__(16) uint8_t v_tile1[kVTileBytes];
+  __shared__ __align__(16) int toks[4 * kKeys];                // token tables of chunks n % 4
+  __shared__ __align__(16) uint32_t mtabs[2 * kSelTableWords];  // membership tables of chunks n % 2
+  __shared__ int scan[16];
   extern __shared__ __align__(16) uint8_t smem[];
-  uint8_t* stage = smem;                                            // 2 x kStageBytes
-  int* scan = reinterpret_cast<int*>(smem + 2 * kStageBytes);       // WAVES + 1 ints (padded to 16)
-  uint16_t* list = reinterpret_cast<uint16_t*>(smem + 2 * kStageBytes + 16 * ((WAVES + 4) / 4));
+  uint16_t* list = reinterpret_cast<uint16_t*>(smem);
 
   // XCD-aware decode of the workgroup id into (pair, part).
   const int x = blockIdx.x;
@@ -146,6 +160,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
   const uint16_t* vbase = v + (long long)g * n_tokens * kD;
   const int n_keys = n_list * block;
   const int n_chunks = (n_keys + kKeys - 1) / kKeys;
+  static_assert(WAVES % 2 == 0, "two wave groups");
   // Smallest query of this wave (masking is needed once a chunk reaches past it).
   int wave_i_min = 0x7FFFFFFF;
 #pragma unroll
@@ -155,26 +170,30 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
   }
   (void)i_lo;
 
-  auto tok_at = [&](int chunk, int key) -> int {
+  // Token of key `key` of chunk `chunk` (-1 past the list or the sequence).
+  auto tok_at = [&](int chunk, int key) __attribute__((always_inline)) -> int {
     const int kp = chunk * kKeys + key;
     if (kp >= n_keys) return -1;
     const int tk = ((int)list[kp >> block_shift] << block_shift) + (kp & (block - 1));
     return tk < n_tokens ? tk : -1;
   };
 
-  // Gather slots of this lane (the same in every chunk): instruction ii of the 17 + 16 wave-wide
-  // loads of a stage (layout as in chunk_issue) is issued by wave ii % WAVES.
+  // Gathers. Loop step n fetches the K tile of chunk n + 1 and the V tile of chunk n with 17 + 16
+  // wave-wide LDS-direct loads (the tile gather layout); instruction ii goes to wave ii % kIssuers
+  // of wave group 0, which spreads its share over the K steps of its score products (an LDS-direct
+  // load holds up the issuing wave while the memory pipeline drains, so issuing them in one burst
+  // stalls every wave). Each lane takes the tokens of its rows from the chunks' token tables,
+  // which the first wave writes two steps ahead.
+  // The masked variant keeps more state in registers and issues in one burst at the start of the
+  // step from every wave instead.
+  constexpr bool kSpread = SEL_LOADS == 0;
   constexpr int kInsts = kKTileInsts + kVTileInsts;
-  constexpr int kIssuePerWave = (kInsts + WAVES - 1) / WAVES;
-  int is_row[kIssuePerWave], is_src[kIssuePerWave], is_dst[kIssuePerWave];
-  bool is_vt[kIssuePerWave];  // the slot belongs to the V tile (wave-uniform)
-#pragma unroll
-  for (int xi = 0; xi < kIssuePerWave; ++xi) {
-    const int inst = wave + xi * WAVES;
-    const bool is_v = inst >= kKTileInsts;
-    const int ti = is_v ? inst - kKTileInsts : inst;
-    const int sl = ti * 64 + l;
-    int row, piece;
+  constexpr int kIssuers = kSpread ? WAVES / 2 : WAVES;
+  constexpr int kPer = (kInsts + kIssuers - 1) / kIssuers;  // loads per issuing wave
+  static_assert(kPer <= 9, "at most one load per K step plus one");
+  auto slot_of = [&](int ii, int& row, int& piece) __attribute__((always_inline)) {
+    const bool is_v = ii >= kKTileInsts;
+    const int sl = (is_v ? ii - kKTileInsts : ii) * 64 + l;
     if (is_v) {
       row = sl >> 4;
       piece = v_phys(row, sl & 15);
@@ -183,25 +202,37 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
       piece = sl - row * kKSlotsPerRow;
       if (piece == 16) piece = 0;  // padding slot: any in-bounds data
     }
-    is_row[xi] = row;
-    is_src[xi] = piece * 8;  // elements from the row start
-    is_dst[xi] = (is_v ? kKTileBytes : 0) + ti * 1024;
-    is_vt[xi] = is_v;
-  }
-  auto issue = [&](int n, uint8_t* sb) {
+  };
+  // Tokens of this wave's loads of step n (all table reads before the first load, which writes LDS).
+  auto gather_tokens = [&](int n, int (&tq)[kPer]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int xi = 0; xi < kIssuePerWave; ++xi) {
-      if (wave + xi * WAVES < kInsts) {
-        int tkn = tok_at(n, is_row[xi]);
-        if (tkn < 0) tkn = 0;
-        const uint16_t* base = is_vt[xi] ? vbase : kbase;
-        __builtin_amdgcn_global_load_lds((const void*)(base + is_src[xi] + (long long)tkn * kD),
-                                         (lds_void*)(sb + is_dst[xi]), 16, 0, 0);
-      }
+    for (int xi = 0; xi < kPer; ++xi) {
+      const int ii = wave + xi * kIssuers;
+      int row, piece;
+      slot_of(ii, row, piece);
+      const int t = (ii >= kKTileInsts ? toks + (n & 3) * kKeys : toks + ((n + 1) & 3) * kKeys)[row];
+      tq[xi] = t == 0x7FFFFFFF ? 0 : t;
     }
-    if (threadIdx.x < kKeys) {
-      const int tk = tok_at(n, (int)threadIdx.x);
-      reinterpret_cast<int*>(sb + kKTileBytes + kVTileBytes)[threadIdx.x] = tk >= 0 ? tk : 0x7FFFFFFF;
+  };
+  // Load xi of this wave for step n: K rows of chunk n + 1 into kdst (if k_on), V rows of chunk n
+  // into vdst (if v_on).
+  auto gather_one = [&](int xi, const int (&tq)[kPer], uint8_t* kdst, uint8_t* vdst, bool k_on,
+                        bool v_on) __attribute__((always_inline)) {
+    const int ii = wave + xi * kIssuers;
+    const bool is_v = ii >= kKTileInsts;
+    if (ii < kInsts && (is_v ? v_on : k_on)) {
+      int row, piece;
+      slot_of(ii, row, piece);
+      const uint16_t* base = is_v ? vbase : kbase;
+      uint8_t* dst = (is_v ? vdst : kdst) + (is_v ? ii - kKTileInsts : ii) * 1024;
+      __builtin_amdgcn_global_load_lds((const void*)(base + piece * 8 + (long long)tq[xi] * kD), (lds_void*)dst, 16,
+                                       0, 0);
+    }
+  };
+  auto write_tokens = [&](int c) __attribute__((always_inline)) {  // token table of chunk c
+    if (threadIdx.x < kKeys && c < n_chunks) {
+      const int tk = tok_at(c, (int)threadIdx.x);
+      toks[(c & 3) * kKeys + threadIdx.x] = tk >= 0 ? tk : 0x7FFFFFFF;
     }
   };
   // Chunks from n_first_masked on can hold a key above this wave's first query or past the list
@@ -224,9 +255,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
   for (int qt = 0; qt < QT; ++qt) ql[qt] = row_pos[qt] < 0 ? 0 : min(max(row_pos[qt] - i_lo, 0), nq - 1);
   constexpr bool SEL = SEL_LOADS > 0;
   constexpr int kLoads = SEL ? SEL_LOADS : 1;
+  // Operand reads in flight ahead of the products (fewer in the masked variant, which holds the
+  // membership state in registers).
+  constexpr int kKAhead = SEL ? 2 : kKReadsAhead;
+  constexpr int kVAhead = SEL ? 2 : kVReadsAhead;
   uint32_t sel_word[kLoads];  // the selbits word of this thread's table bit j, loaded a chunk ahead
   // Table bit pp: block entry e of chunk n, query qq of the workgroup.
-  auto sel_pair = [&](int n, int pp, int& b, int& i) -> bool {
+  auto sel_pair = [&](int n, int pp, int& b, int& i) __attribute__((always_inline)) -> bool {
     const int e = pp / (nqw * 32), qq = ((pp >> 5) % nqw) * 32 + (pp & 31);
     const int ent = n * ents + e;
     i = i_lo + qq;
@@ -234,7 +269,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
     b = ok ? (int)list[ent] : 0;
     return ok;
   };
-  auto sel_load = [&](int n) {
+  auto sel_load = [&](int n) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
       int b, i;
@@ -242,8 +277,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
       sel_word[j] = ok ? selbits[((long long)g * n_tokens + i) * n_words + (b >> 5)] : 0u;
     }
   };
-  auto sel_store = [&](int n, uint8_t* sb) {
-    uint32_t* mt = reinterpret_cast<uint32_t*>(sb + kKTileBytes + kVTileBytes + kKeys * 4);
+  auto sel_store = [&](int n) __attribute__((always_inline)) {
+    uint32_t* mt = mtabs + (n & 1) * kSelTableWords;
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
       if (j * (WAVES * 64) + (int)(threadIdx.x & ~63) < pairs) {  // wave-uniform
@@ -257,43 +292,109 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
     }
   };
 
-  const LaneOffsets lo = lane_offsets();
-  if (n_chunks > 0) {
-    if constexpr (SEL) sel_load(0);
-    issue(0, stage);
-  }
-  wait_vm();
-  if constexpr (SEL)
-    if (n_chunks > 0) sel_store(0, stage);
-  __syncthreads();
-  // One loop step: start the gather of chunk n + 1, run chunk n (unless the wave has no rows),
-  // then wait for the gather and for every wave to be done with chunk n's buffer.
-  auto run = [&](int n, auto mask_t) {
-    const int buf = n & 1;
-    if (n + 1 < n_chunks) {
-      if constexpr (SEL) sel_load(n + 1);
-      issue(n + 1, stage + (buf ^ 1) * kStageBytes);
-    }
-    constexpr int kMask = decltype(mask_t)::value;
-    uint8_t* sbuf = stage + buf * kStageBytes;
+  // Two wave groups take turns on each SIMD (wave w and wave w + WAVES / 2 share one): while one
+  // group runs the matrix-core products of a chunk, the other runs the softmax of its previous
+  // chunk. Half-period 2n: the gathers of K(n + 1) and V(n) start; group 0 computes S(n) and
+  // P(n - 1) V(n - 1), group 1 the softmax of chunk n - 1. Half-period 2n + 1: group 0 the softmax
+  // of chunk n, group 1 S(n) and P(n - 1) V(n - 1); the membership table of chunk n + 1 is built;
+  // then every wave waits for its gathers and the workgroup syncs. A K tile is read up to
+  // half-period 2n + 1, a V tile up to 2n + 3, a token table (written in step n - 2) up to 2n + 2
+  // and a membership table from 2n + 1 to 2n + 2: two K, two V, four token and two membership
+  // slots suffice.
+  const LaneOffsets lo = lane_offsets(0);
+  const bool has_rows = wave_i_min != 0x7FFFFFFF;
+  const int grp = wave / (WAVES / 2);
+  f32x16 s[QT][2];
+  bf16x8 pb[QT][4];
+  auto softmax = [&](int n) __attribute__((always_inline)) {
+    if (!has_rows || n < 0 || n >= n_chunks) return;
+    const int* tk = toks + (n & 3) * kKeys;
     if constexpr (SEL) {
-      if (kMask >= 0)
-        attn_chunk<QT, 1, false, NoOp, true>(sbuf, lo, qreg, st, scale_log2, true, row_pos, nullptr, NoOp(),
-                                            reinterpret_cast<const uint32_t*>(sbuf + kKTileBytes + kVTileBytes +
-                                                                              kKeys * 4),
-                                            nqw, ql, block_shift);
-      if (n + 1 < n_chunks) sel_store(n + 1, stage + (buf ^ 1) * kStageBytes);
+      chunk_softmax<QT, 1, true>(s, tk, st, scale_log2, true, row_pos, pb, mtabs + (n & 1) * kSelTableWords, nqw,
+                                 ql, block_shift);
     } else {
-      if (kMask >= 0) attn_chunk<QT, kMask>(sbuf, lo, qreg, st, scale_log2, kMask == 1, row_pos);
+      if (n >= n_first_masked)
+        chunk_softmax<QT, 1>(s, tk, st, scale_log2, true, row_pos, pb);
+      else
+        chunk_softmax<QT, 0>(s, tk, st, scale_log2, false, row_pos, pb);
     }
+  };
+  // One loop step n; P = n % 2 picks the tiles (compile-time, so that every access names its tile).
+  auto step = [&](auto parity, int n) __attribute__((always_inline)) {
+    constexpr int P = decltype(parity)::value;
+    uint8_t* k_cur = P ? k_tile1 : k_tile0;   // K(n)
+    uint8_t* k_next = P ? k_tile0 : k_tile1;  // K(n + 1)
+    uint8_t* v_cur = P ? v_tile1 : v_tile0;   // V(n)
+    uint8_t* v_prev = P ? v_tile0 : v_tile1;  // V(n - 1)
+    const bool k_on = n + 1 < n_chunks, v_on = n < n_chunks;
+    // S(n) and P(n - 1) V(n - 1) at raised wave priority; group 0 also issues the step's gathers.
+    auto products = [&]() __attribute__((always_inline)) {
+      const bool issuing = kSpread && grp == 0 && n < n_chunks;
+      int tq[kPer];
+      if (issuing) gather_tokens(n, tq);
+      if (!has_rows) {
+        if (issuing)
+#pragma unroll
+          for (int xi = 0; xi < kPer; ++xi) gather_one(xi, tq, k_next, v_cur, k_on, v_on);
+        return;
+      }
+      __builtin_amdgcn_s_setprio(1);
+      if (n < n_chunks) {
+        auto hook = [&](int ks) __attribute__((always_inline)) {
+          if (!issuing) return;
+          gather_one(ks, tq, k_next, v_cur, k_on, v_on);
+          if (ks == 7)
+#pragma unroll
+            for (int xi = 8; xi < kPer; ++xi) gather_one(xi, tq, k_next, v_cur, k_on, v_on);
+        };
+        score_products<QT, decltype(hook), kKAhead>(k_cur, lo, qreg, s, hook);
+      }
+      if (n >= 1) pv_products<QT, kVAhead>(v_prev, lo, pb, st);
+      __builtin_amdgcn_s_setprio(0);
+    };
+    if constexpr (SEL)
+      if (n + 1 < n_chunks) sel_load(n + 1);
+    if (!kSpread && n < n_chunks) {
+      int tq[kPer];
+      gather_tokens(n, tq);
+#pragma unroll
+      for (int xi = 0; xi < kPer; ++xi) gather_one(xi, tq, k_next, v_cur, k_on, v_on);
+    }
+    if (grp == 0) {
+      products();
+      write_tokens(n + 2);
+    } else {
+      softmax(n - 1);
+    }
+    __builtin_amdgcn_s_barrier();
+    if (grp == 0)
+      softmax(n);
+    else
+      products();
+    if constexpr (SEL)
+      if (n + 1 < n_chunks) sel_store(n + 1);
     wait_vm();
     __syncthreads();
   };
-  if (wave_i_min != 0x7FFFFFFF) {
-    for (int n = 0; n < n_first_masked; ++n) run(n, std::integral_constant<int, 0>());
-    for (int n = n_first_masked; n < n_chunks; ++n) run(n, std::integral_constant<int, 1>());
-  } else {
-    for (int n = 0; n < n_chunks; ++n) run(n, std::integral_constant<int, -1>());
+  if (n_chunks > 0) {
+    if constexpr (SEL) sel_load(0);
+    write_tokens(0);
+    write_tokens(1);
+    __syncthreads();
+    if (!kSpread || grp == 0) {  // the K tile of chunk 0
+      int tq[kPer];
+      gather_tokens(-1, tq);
+#pragma unroll
+      for (int xi = 0; xi < kPer; ++xi) gather_one(xi, tq, k_tile0, v_tile0, true, false);
+    }
+    wait_vm();
+    if constexpr (SEL) sel_store(0);
+    __syncthreads();
+  }
+  const int n_steps = n_chunks + (n_chunks > 0);
+  for (int n = 0; n < n_steps; n += 2) {
+    step(std::integral_constant<int, 0>(), n);
+    if (n + 1 < n_steps) step(std::integral_constant<int, 1>(), n + 1);
   }
 
   // out[i][h][d] = O^T[d][row] / l
@@ -324,14 +425,13 @@ namespace {
 constexpr int kPrefillWaves = SGQA_ATTN_WAVES;
 constexpr int kPrefillQT = SGQA_ATTN_QT;
 
-size_t attend_lds_bytes(int waves, int list_cap) {
-  return (size_t)2 * kStageBytes + 16 * ((waves + 4) / 4) + (size_t)list_cap * 2;
-}
+// Dynamic LDS of the prefill kernel: the block list.
+size_t attend_lds_bytes(int list_cap) { return (size_t)list_cap * 2; }
 }  // namespace
 
 size_t attend_lds_bytes_for(int n_tokens, int block) {
   const int nbc = (n_tokens + block - 1) / block;
-  return attend_lds_bytes(kPrefillWaves, (nbc + 7) / 8 * 8);
+  return kAttnStaticBytes + attend_lds_bytes((nbc + 7) / 8 * 8);
 }
 
 namespace {
@@ -351,8 +451,8 @@ hipError_t launch_attend_impl(const uint16_t* q, const uint16_t* k, const uint16
   if (n_pairs == 0) return hipSuccess;
   if (SEL_LOADS > 0 && attend_masked_loads(n_q_heads, n_groups, block) > SEL_LOADS) return hipErrorInvalidValue;
   const int list_cap = (nbc + 7) / 8 * 8;
-  const size_t lds = attend_lds_bytes(kPrefillWaves, list_cap);
-  if (lds > (size_t)max_lds_per_block()) return hipErrorInvalidValue;
+  const size_t lds = attend_lds_bytes(list_cap);
+  if (kAttnStaticBytes + lds > (size_t)max_lds_per_block()) return hipErrorInvalidValue;
   const long long grid = (long long)((n_pairs + 7) / 8) * 8 * parts;
   const float scale_log2 = scale * 1.4426950408889634f;
   auto kern = k_attend<kPrefillWaves, kPrefillQT, SEL_LOADS>;
@@ -407,8 +507,8 @@ hipError_t launch_attend_masked(const uint16_t* q, const uint16_t* k, const uint
 
 constexpr int kDecVStage = kVTileBytes + kKeys * 4;  // decode: V tile + token table of a chunk
 
-// Decode gather of one wave: the V tile of one chunk (16 wave-wide global_load_lds, layout as in
-// chunk_issue) and its token table.
+// Decode gather of one wave: the V tile of one chunk (16 wave-wide global_load_lds, tile gather
+// layout) and its token table.
 // off_of(key) is the element offset (from `base`) of the row of key `key` of the chunk.
 template <typename TokFn, typename OffFn>
 __device__ __forceinline__ void v_issue_wave(uint8_t* vst, const uint16_t* base, OffFn off_of, TokFn tok_of) {
@@ -647,7 +747,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 // registers while the current chunk computes: K straight into MFMA operands (the head dimension is
 // permuted so that lane half h holds dims 64h .. 64h + 63, contiguous in the cache row; Q is loaded
 // with the same permutation), V converted and written into the wave's bf16 V tile (row-major,
-// swizzled as in chunk_issue) for the transposing reads.
+// swizzled as in the tile gather layout) for the transposing reads.
 template <bool PAGED, int DEPTH>
 __global__ __launch_bounds__(256) void k_decode_attend_f8(const uint16_t* __restrict__ q,
                                                           const uint8_t* __restrict__ kc,
@@ -749,7 +849,7 @@ __global__ __launch_bounds__(256) void k_decode_attend_f8(const uint16_t* __rest
   };
   bf16x8 kreg[16];
   const float sl2 = scale_log2 * k_scale;
-  // One chunk from register set d: V codes -> bf16 V tile (the layout chunk_issue gives the V
+  // One chunk from register set d: V codes -> bf16 V tile (the tile gather layout of the V
   // tile) and the token table, K codes -> MFMA operands; then set d is refilled with chunk
   // c + 4 DEPTH (always issued, past the end it reads row 0, so that the number of loads between
   // a set's issue and its use is the same on every path and the counter waits stay partial).

@@ -8,6 +8,7 @@
 #include "sgqa_device.hpp"
 #include "sgqa_internal.hpp"
 
+
 namespace sgqa {
 
 namespace {
@@ -26,8 +27,10 @@ constexpr int kKTileInsts = kKeys * kKSlotsPerRow / 64;  // 17 wave-wide 16-byte
 constexpr int kVTileBytes = kKeys * 256;           // V rows unpadded; 16-B pieces XOR-swizzled by row
 constexpr int kVTileInsts = kVTileBytes / 1024;    // 16
 constexpr int kSelTableWords = 64;                 // masked variant: membership words of a chunk
-constexpr int kStageBytes = kKTileBytes + kVTileBytes + kKeys * 4 + kSelTableWords * 4;  // K, V, tokens, members
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr int kKReadsAhead = 3;   // K-operand steps read ahead of the score products
+constexpr int kVReadsAhead = 4;   // V-operand steps read ahead of the value products
+constexpr float kLazyLog2 = 8.0f;  // the running maximum moves only when a row's grows by more
 constexpr float kMinit = -1.0e30f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -83,69 +86,69 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int v_tile = kKTileBytes) {
 struct NoOp {
   __device__ void operator()() const {}
 };
+struct NoHook {
+  __device__ void operator()(int) const {}
+};
 
-// One 64-key chunk for the QT Q tiles of this wave.
-//   stage: K tile, V tile (row-major, 272-byte rows), token table (INT_MAX = invalid key), at the
-//          offsets of lo
-//   row_pos[qt]: query position of this lane's Q row in tile qt (for the causal mask)
-//   KREG: the K operands come from kreg[ks * 2 + kt] (registers) instead of the K tile; after()
-//         runs once the score products have consumed them.
-//   MASK: 0 = no key of the chunk can be masked, 1 = apply the mask, 2 = decided by `masked`.
-//   SEL (with MASK = 1): a key also needs its block to be a member of the Q row's own set: the
-//         word mt[e * nqw + ql / 32] of the chunk's membership table holds, for block entry
-//         e = key >> bs of the chunk, one bit per query of the workgroup; ql[qt] is this lane's
-//         query index within the workgroup.
-template <int QT, int MASK = 2, bool KREG = false, typename After = NoOp, bool SEL = false>
-__device__ __forceinline__ void attn_chunk(const uint8_t* stage, const LaneOffsets& lo, const bf16x8 (&qreg)[QT][8],
-                                           AttnState<QT>& st, float scale_log2, bool masked_rt,
-                                           const int (&row_pos)[QT], const bf16x8* kreg = nullptr,
-                                           After after = After(), const uint32_t* mt = nullptr, int nqw = 0,
-                                           const int* ql = nullptr, int bs = 0) {
-  const bool masked = MASK == 2 ? masked_rt : MASK == 1;
-  const int l = lane_id();
-  const int hi = l >> 5;
-  f32x16 s[QT][2];
+// S^T = K Q^T for the 64 keys of a K tile (ktile + lo.k is this lane's first operand): the K
+// operands of step ks+2 are read while the MFMAs of step ks run.
+// hook(ks) runs after the products of step ks (other work to spread between them).
+template <int QT, typename Hook = NoHook, int PF = kKReadsAhead>
+__device__ __forceinline__ void score_products(const uint8_t* ktile, const LaneOffsets& lo,
+                                               const bf16x8 (&qreg)[QT][8], f32x16 (&s)[QT][2],
+                                               Hook hook = Hook()) {
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int j = 0; j < 16; ++j) s[qt][kt][j] = 0.0f;
-  if constexpr (KREG) {
+  const uint8_t* kp = ktile + lo.k;
+  bf16x8 ka[PF + 1][2];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) s[qt][kt] = mfma32(kreg[ks * 2 + kt], qreg[qt][ks], s[qt][kt]);
-  } else {
-    // S^T = K Q^T: the K operands of step ks+2 are read while the MFMAs of step ks run.
-    const uint8_t* kp = stage + lo.k;
-    bf16x8 ka[3][2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      ka[ks][0] = *reinterpret_cast<const bf16x8*>(kp + ks * 32);
-      ka[ks][1] = *reinterpret_cast<const bf16x8*>(kp + 32 * kKRowBytes + ks * 32);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      if (ks < 6) {
-        ka[(ks + 2) % 3][0] = *reinterpret_cast<const bf16x8*>(kp + (ks + 2) * 32);
-        ka[(ks + 2) % 3][1] = *reinterpret_cast<const bf16x8*>(kp + 32 * kKRowBytes + (ks + 2) * 32);
-      }
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) s[qt][kt] = mfma32(ka[ks % 3][kt], qreg[qt][ks], s[qt][kt]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  for (int ks = 0; ks < PF; ++ks) {
+    ka[ks][0] = *reinterpret_cast<const bf16x8*>(kp + ks * 32);
+    ka[ks][1] = *reinterpret_cast<const bf16x8*>(kp + 32 * kKRowBytes + ks * 32);
   }
-  after();
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    if (ks + PF < 8) {
+      ka[(ks + PF) % (PF + 1)][0] = *reinterpret_cast<const bf16x8*>(kp + (ks + PF) * 32);
+      ka[(ks + PF) % (PF + 1)][1] = *reinterpret_cast<const bf16x8*>(kp + 32 * kKRowBytes + (ks + PF) * 32);
+    }
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) s[qt][kt] = mfma32(ka[ks % (PF + 1)][kt], qreg[qt][ks], s[qt][kt]);
+    __builtin_amdgcn_sched_barrier(0);
+    hook(ks);
+  }
+}
+
+// Online softmax of one chunk's scores s (S^T tiles: lane column = Q row, 32 keys per tile) into
+// the bf16 probabilities pb (the B operands of the V products); rescales the running state.
+//   tok: the chunk's token table (INT_MAX = invalid key); row_pos[qt]: query position of this
+//        lane's Q row in tile qt (for the causal mask)
+//   MASK: 0 = no key of the chunk can be masked, 1 = apply the mask, 2 = decided by masked_rt.
+//   SEL (with MASK = 1): a key also needs its block to be a member of the Q row's own set: the
+//        word mt[e * nqw + ql / 32] of the chunk's membership table holds, for block entry
+//        e = key >> bs of the chunk, one bit per query of the workgroup; ql[qt] is this lane's
+//        query index within the workgroup.
+// The running maximum only moves when some row's maximum grows by more than kLazyLog2 (log2
+// units): most chunks then skip the rescale of O. The probabilities stay below 2^kLazyLog2, which
+// fp32 sums and bf16 operands carry with the same relative precision as values below 1, and the
+// final normalisation uses the same maximum, so the result is unchanged up to rounding.
+template <int QT, int MASK = 2, bool SEL = false>
+__device__ __forceinline__ void chunk_softmax(f32x16 (&s)[QT][2], const int* tok, AttnState<QT>& st,
+                                              float scale_log2, bool masked_rt, const int (&row_pos)[QT],
+                                              bf16x8 (&pb)[QT][4], const uint32_t* mt = nullptr, int nqw = 0,
+                                              const int* ql = nullptr, int bs = 0) {
+  const bool masked = MASK == 2 ? masked_rt : MASK == 1;
+  const int hi = lane_id() >> 5;
 
   // Tokens of this lane's keys: key kt*32 + 8*a + 4*hi + (0..3), four consecutive ints.
   int4 tk[2][4];
   if (masked) {
-    const int* tok = reinterpret_cast<const int*>(stage + (KREG ? lo.tok : kKTileBytes + kVTileBytes));
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -174,7 +177,6 @@ __device__ __forceinline__ void attn_chunk(const uint8_t* stage, const LaneOffse
       }
   }
 
-  bf16x8 pb[QT][4];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     float mx = kNegInf;
@@ -194,7 +196,7 @@ __device__ __forceinline__ void attn_chunk(const uint8_t* stage, const LaneOffse
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = fmaxf(st.m[qt], mx * scale_log2);
-    if (ballot(m_new > st.m[qt])) {  // rescale only when some row's max moved
+    if (ballot(m_new > st.m[qt] + kLazyLog2)) {
       const float alpha = fast_exp2(st.m[qt] - m_new);
       st.l[qt] *= alpha;
 #pragma unroll
@@ -203,88 +205,91 @@ __device__ __forceinline__ void attn_chunk(const uint8_t* stage, const LaneOffse
         for (int j = 0; j < 16; ++j) st.o[qt][dt][j] *= alpha;
       st.m[qt] = m_new;
     }
-    float sum = 0.0f;
+    const float m_use = st.m[qt];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float p = fast_exp2(__builtin_fmaf(s[qt][kt][j], scale_log2, -m_new));
-        s[qt][kt][j] = p;
-        sum += p;
-      }
-    st.l[qt] += sum;
+      for (int j = 0; j < 16; ++j) s[qt][kt][j] = fast_exp2(__builtin_fmaf(s[qt][kt][j], scale_log2, -m_use));
 #pragma unroll
     for (int ss = 0; ss < 4; ++ss)
 #pragma unroll
       for (int e = 0; e < 8; ++e) pb[qt][ss][e] = (__bf16)s[qt][ss >> 1][8 * (ss & 1) + e];
+    float sum = 0.0f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sum += s[qt][kt][j];
+    st.l[qt] += sum;
   }
+}
 
-  // O^T += V^T P^T. The V^T operand of lane l (row d, 8 keys) comes from two transposing reads,
-  // each returning 4 keys of this lane's d, in the key order the score registers already have.
+// O^T += V^T P^T. The V^T operand of lane l (row d, 8 keys) comes from two transposing reads, each
+// returning 4 keys of this lane's d, in the key order the score registers already have; vbase +
+// lo.v[dt] addresses this lane's first read of d-tile dt.
+template <int QT, int PF = kVReadsAhead>
+__device__ __forceinline__ void pv_products(const uint8_t* vbase, const LaneOffsets& lo, const bf16x8 (&pb)[QT][4],
+                                            AttnState<QT>& st) {
   auto vread = [&](int step) -> bf16x8 {
     const int dt = step >> 2, ss = step & 3;
-    const uint8_t* a0 = stage + lo.v[dt] + (16 * ss) * 256;
+    const uint8_t* a0 = vbase + lo.v[dt] + (16 * ss) * 256;
     const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
     const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0 + 8 * 256));
     const i16x8 cat = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(bf16x8, cat);
   };
-  bf16x8 va[3];
-  va[0] = vread(0);
-  va[1] = vread(1);
+  bf16x8 va[PF + 1];
+#pragma unroll
+  for (int step = 0; step < PF; ++step) va[step] = vread(step);
 #pragma unroll
   for (int step = 0; step < 16; ++step) {
-    if (step < 14) va[(step + 2) % 3] = vread(step + 2);
+    if (step + PF < 16) va[(step + PF) % (PF + 1)] = vread(step + PF);
     const int dt = step >> 2, ss = step & 3;
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) st.o[qt][dt] = mfma32(va[step % 3], pb[qt][ss], st.o[qt][dt]);
+    for (int qt = 0; qt < QT; ++qt) st.o[qt][dt] = mfma32(va[step % (PF + 1)], pb[qt][ss], st.o[qt][dt]);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Gather one chunk of 64 keys straight from global memory into the K and V tiles of `stage`
-// (global_load_lds: every wave-wide instruction fills 64 consecutive 16-byte slots). K: slot s of
-// the tile is row s / 17, piece s % 17 (piece 16 is padding). V: slot s is row s / 16, physical
-// piece s % 16, holding logical piece v_phys(row, s % 16). Invalid keys read row 0 of the group
-// (finite data, always masked out through the token table). The waves of the workgroup split the
-// 17 + 16 instructions; the first wave writes the token table.
-template <int NT, typename TokFn>
-__device__ __forceinline__ void chunk_issue(uint8_t* stage, const uint16_t* kbase, const uint16_t* vbase,
-                                            TokFn tok_of) {
-  constexpr int kWaves = NT / 64;
-  constexpr int kInsts = kKTileInsts + kVTileInsts;
-  const int l = lane_id();
-  // NT == 64: one wave fills the stage alone (it may be any wave of a larger workgroup).
-  const int tid = kWaves == 1 ? l : (int)threadIdx.x;
-  const int wave = kWaves == 1 ? 0 : (int)threadIdx.x >> 6;
+// One 64-key chunk for the QT Q tiles of this wave, all phases in order.
+//   stage: K tile, V tile, token table at the offsets of lo
+//   KREG: the K operands come from kreg[ks * 2 + kt] (registers) instead of the K tile; after()
+//         runs once the score products have consumed them.
+//   MASK, SEL and the membership arguments: as for chunk_softmax.
+template <int QT, int MASK = 2, bool KREG = false, typename After = NoOp, bool SEL = false>
+__device__ __forceinline__ void attn_chunk(const uint8_t* stage, const LaneOffsets& lo, const bf16x8 (&qreg)[QT][8],
+                                           AttnState<QT>& st, float scale_log2, bool masked_rt,
+                                           const int (&row_pos)[QT], const bf16x8* kreg = nullptr,
+                                           After after = After(), const uint32_t* mt = nullptr, int nqw = 0,
+                                           const int* ql = nullptr, int bs = 0) {
+  f32x16 s[QT][2];
+  if constexpr (KREG) {
 #pragma unroll
-  for (int x = 0; x < (kInsts + kWaves - 1) / kWaves; ++x) {
-    const int inst = wave + x * kWaves;
-    if (inst < kInsts) {
-      const bool is_v = inst >= kKTileInsts;
-      const int ti = is_v ? inst - kKTileInsts : inst;
-      const int slot = ti * 64 + l;
-      int row, piece;
-      if (is_v) {
-        row = slot >> 4;
-        piece = v_phys(row, slot & 15);
-      } else {
-        row = slot / kKSlotsPerRow;
-        piece = slot - row * kKSlotsPerRow;
-        if (piece == 16) piece = 0;  // padding slot: any in-bounds data
-      }
-      int tkn = tok_of(row);
-      if (tkn < 0) tkn = 0;
-      const uint16_t* src = (is_v ? vbase : kbase) + (long long)tkn * kD + piece * 8;
-      uint8_t* dst = stage + (is_v ? kKTileBytes : 0) + ti * 1024;
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)dst, 16, 0, 0);
-    }
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) s[qt][kt][j] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) s[qt][kt] = mfma32(kreg[ks * 2 + kt], qreg[qt][ks], s[qt][kt]);
+  } else {
+    score_products<QT>(stage, lo, qreg, s);
   }
-  if (tid < kKeys) {
-    const int t = tok_of(tid);
-    reinterpret_cast<int*>(stage + kKTileBytes + kVTileBytes)[tid] = t >= 0 ? t : 0x7FFFFFFF;
-  }
+  after();
+  const int* tok = reinterpret_cast<const int*>(stage + (KREG ? lo.tok : kKTileBytes + kVTileBytes));
+  bf16x8 pb[QT][4];
+  chunk_softmax<QT, MASK, SEL>(s, tok, st, scale_log2, masked_rt, row_pos, pb, mt, nqw, ql, bs);
+  pv_products<QT>(stage, lo, pb, st);
 }
+
+// Tile gather layout. A chunk's 64 keys are gathered straight from global memory into the K and V
+// tiles (global_load_lds: every wave-wide instruction fills 64 consecutive 16-byte slots). K: slot s
+// of the tile is row s / 17, piece s % 17 (piece 16 is padding). V: slot s is row s / 16, physical
+// piece s % 16, holding logical piece v_phys(row, s % 16). Invalid keys read row 0 of the group
+// (finite data, always masked out through the token table).
 
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
