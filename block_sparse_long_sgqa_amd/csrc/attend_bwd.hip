@@ -33,10 +33,9 @@ namespace {
 
 constexpr int kBwdWaves = SGQA_BWD_WAVES;  // dk/dv workgroup (one wave per SIMD)
 constexpr int kDqWaves = 8;                 // dq workgroup (two waves per SIMD, as the forward)
-// dq stage: padded K tile, padded V tile, swizzled K tile, token table.
+// dq stage: padded K tile, padded V tile, swizzled K tile.
 constexpr int kDqKs = 2 * kKTileBytes;                          // swizzled K tile offset
-constexpr int kDqTok = kDqKs + kVTileBytes;                     // token table offset
-constexpr int kDqStageBytes = kDqTok + kKeys * 4;
+constexpr int kDqStageBytes = kDqKs + kVTileBytes;              // one stage
 constexpr int kDqInsts = 2 * kKTileInsts + kVTileInsts;         // 17 + 17 + 16 wave-wide loads
 
 // Two 4x16 transposing reads at `a0` and 8 rows below: the A operand of a (d x rows) product whose
@@ -81,10 +80,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_bwd_dq(const uint16_t* __restric
                                                        int n_words, int parts, int n_pairs) {
   constexpr int NT = WAVES * 64;
   constexpr int kRowsWg = WAVES * 32;
+  // The two stages and the token tables are variables of their own (see the forward kernel: the
+  // compiler then does not make the reads of one stage wait for the gathers into the other).
+  static_assert(WAVES + 1 <= 16, "scan words");
+  __shared__ __align__(16) uint8_t stage0[kDqStageBytes];
+  __shared__ __align__(16) uint8_t stage1[kDqStageBytes];
+  __shared__ __align__(16) int toks[4 * kKeys];  // token tables of chunks n % 4
+  __shared__ int scan[16];
   extern __shared__ __align__(16) uint8_t smem[];
-  uint8_t* stage = smem;                                             // 2 x kDqStageBytes
-  int* scan = reinterpret_cast<int*>(smem + 2 * kDqStageBytes);      // WAVES ints (padded to 16)
-  uint16_t* list = reinterpret_cast<uint16_t*>(smem + 2 * kDqStageBytes + 16 * ((WAVES + 4) / 4));
+  uint16_t* list = reinterpret_cast<uint16_t*>(smem);
 
   const int x = blockIdx.x;
   const int slot = x >> 3, xcd = x & 7;
@@ -179,45 +183,56 @@ __global__ __launch_bounds__(WAVES * 64) void k_bwd_dq(const uint16_t* __restric
     const int tk = ((int)list[kp >> block_shift] << block_shift) + (kp & (block - 1));
     return tk < n_tokens ? tk : -1;
   };
-  // Gather of one chunk: padded K (instructions 0..16), padded V (17..33), swizzled K (34..49).
-  auto issue = [&](int n, uint8_t* sb) {
-    for (int inst = wave; inst < kDqInsts; inst += WAVES) {
-      int tile_id, ti;
-      if (inst < kKTileInsts) {
-        tile_id = 0;
-        ti = inst;
-      } else if (inst < 2 * kKTileInsts) {
-        tile_id = 1;
-        ti = inst - kKTileInsts;
-      } else {
-        tile_id = 2;
-        ti = inst - 2 * kKTileInsts;
-      }
-      const int sl = ti * 64 + l;
-      int rw, piece;
-      if (tile_id < 2) {
-        rw = sl / kKSlotsPerRow;
-        piece = sl - rw * kKSlotsPerRow;
-        if (piece == 16) piece = 0;  // padding slot: any in-bounds data
-      } else {
-        rw = sl >> 4;
-        piece = v_phys(rw, sl & 15);
-      }
-      int tkn = tok_at(n, rw);
-      if (tkn < 0) tkn = 0;
-      const uint16_t* src = (tile_id == 1 ? vbase : kbase) + (long long)tkn * kD + piece * 8;
-      uint8_t* dst = sb + (tile_id == 0 ? 0 : (tile_id == 1 ? kKTileBytes : kDqKs)) + ti * 1024;
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)dst, 16, 0, 0);
+  // Gather of one chunk into stage sb: padded K (instructions 0..16), padded V (17..33), swizzled K
+  // (34..49); instruction ii goes to wave ii % WAVES. The rows' tokens come from the chunk's token
+  // table (written two chunks ahead by the first wave), all read before the first gather.
+  constexpr int kPer = (kDqInsts + WAVES - 1) / WAVES;
+  auto slot_of = [&](int inst, int& rw, int& piece) __attribute__((always_inline)) {
+    const int tile_id = inst < kKTileInsts ? 0 : (inst < 2 * kKTileInsts ? 1 : 2);
+    const int sl = (inst - tile_id * kKTileInsts) * 64 + l;
+    if (tile_id < 2) {
+      rw = sl / kKSlotsPerRow;
+      piece = sl - rw * kKSlotsPerRow;
+      if (piece == 16) piece = 0;  // padding slot: any in-bounds data
+    } else {
+      rw = sl >> 4;
+      piece = v_phys(rw, sl & 15);
     }
-    if (threadIdx.x < kKeys) {
-      const int tk = tok_at(n, (int)threadIdx.x);
-      reinterpret_cast<int*>(sb + kDqTok)[threadIdx.x] = tk >= 0 ? tk : 0x7FFFFFFF;
+  };
+  auto issue = [&](int n, uint8_t* sb) __attribute__((always_inline)) {
+    const int* tab = toks + (n & 3) * kKeys;
+    int tkn[kPer];
+#pragma unroll
+    for (int xi = 0; xi < kPer; ++xi) {
+      int rw, piece;
+      slot_of(wave + xi * WAVES, rw, piece);
+      const int t = tab[rw & (kKeys - 1)];
+      tkn[xi] = t == 0x7FFFFFFF ? 0 : t;
+    }
+#pragma unroll
+    for (int xi = 0; xi < kPer; ++xi) {
+      const int inst = wave + xi * WAVES;
+      if (inst < kDqInsts) {
+        int rw, piece;
+        slot_of(inst, rw, piece);
+        const int tile_id = inst < kKTileInsts ? 0 : (inst < 2 * kKTileInsts ? 1 : 2);
+        const int ti = inst - tile_id * kKTileInsts;
+        const uint16_t* src = (tile_id == 1 ? vbase : kbase) + (long long)tkn[xi] * kD + piece * 8;
+        uint8_t* dst = sb + (tile_id == 0 ? 0 : (tile_id == 1 ? kKTileBytes : kDqKs)) + ti * 1024;
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)dst, 16, 0, 0);
+      }
+    }
+  };
+  auto write_tokens = [&](int c) __attribute__((always_inline)) {  // token table of chunk c
+    if (threadIdx.x < kKeys && c < n_chunks) {
+      const int tk = tok_at(c, (int)threadIdx.x);
+      toks[(c & 3) * kKeys + threadIdx.x] = tk >= 0 ? tk : 0x7FFFFFFF;
     }
   };
 
   const LaneOffsets lo = lane_offsets(kDqKs);
   const int hi = l >> 5;
-  auto chunk = [&](const uint8_t* sb) {
+  auto chunk = [&](const uint8_t* sb, const int* tok) __attribute__((always_inline)) {
     // S^T = K Q^T and dP^T = V dO^T.
     f32x16 s[2], dp[2];
 #pragma unroll
@@ -240,7 +255,6 @@ __global__ __launch_bounds__(WAVES * 64) void k_bwd_dq(const uint16_t* __restric
       }
     }
     // dS^T = P^T (dP^T - delta), P^T from the forward's log-sum-exp; masked keys give 0.
-    const int* tok = reinterpret_cast<const int*>(sb + kDqTok);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -267,15 +281,25 @@ __global__ __launch_bounds__(WAVES * 64) void k_bwd_dq(const uint16_t* __restric
     }
   };
 
-  if (n_chunks > 0) issue(0, stage);
-  wait_vm();
-  __syncthreads();
-  for (int n = 0; n < n_chunks; ++n) {
-    const int buf = n & 1;
-    if (n + 1 < n_chunks) issue(n + 1, stage + (buf ^ 1) * kDqStageBytes);
-    chunk(stage + buf * kDqStageBytes);
+  // Step n: start the gather of chunk n + 1 and write the token table of chunk n + 2, compute chunk
+  // n, wait for the gather, sync. P = n % 2 picks the stages at compile time.
+  auto step = [&](auto parity, int n) __attribute__((always_inline)) {
+    constexpr int P = decltype(parity)::value;
+    if (n + 1 < n_chunks) issue(n + 1, P ? stage0 : stage1);
+    write_tokens(n + 2);
+    chunk(P ? stage1 : stage0, toks + (n & 3) * kKeys);
     wait_vm();
     __syncthreads();
+  };
+  write_tokens(0);
+  write_tokens(1);
+  __syncthreads();
+  if (n_chunks > 0) issue(0, stage0);
+  wait_vm();
+  __syncthreads();
+  for (int n = 0; n < n_chunks; n += 2) {
+    step(std::integral_constant<int, 0>(), n);
+    if (n + 1 < n_chunks) step(std::integral_constant<int, 1>(), n + 1);
   }
 
   // dq[i][h][d] = sigma * dQ^T[d][row]
@@ -299,9 +323,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_bwd_dq(const uint16_t* __restric
 namespace {
 constexpr int kTileWin = 256;                  // tiles listed per scan window
 constexpr int kRowTileBytes = 32 * 256;        // 32 rows x 128 bf16, swizzled like the forward's V tile
-// Per wave: two buffers of (Q rows, dO rows, query / lse / delta of each row), then the tile window.
-constexpr int kRgBytes = 2 * kRowTileBytes + 3 * 32 * 4;
-constexpr int kWaveBytes = 2 * kRgBytes + kTileWin * 8;
+constexpr int kRgBytes = 2 * kRowTileBytes;    // Q rows, then dO rows
 }  // namespace
 
 __global__ __launch_bounds__(kBwdWaves * 64) void k_bwd_dkdv(const uint16_t* __restrict__ q,
@@ -315,11 +337,20 @@ __global__ __launch_bounds__(kBwdWaves * 64) void k_bwd_dkdv(const uint16_t* __r
                                                              int n_tokens, int n_q_heads, int n_groups, int block,
                                                              int block_shift, int tile, float scale,
                                                              float scale_log2, int n_words) {
-  extern __shared__ __align__(16) uint8_t smem[];
+  // Per wave: two row-group buffers (Q and dO rows; each row's query, lse and delta), the tile
+  // window. Every buffer is a variable of its own, so the compiler can tell the gathers into one
+  // from the reads of the other and waits only for the loads a read needs.
+  __shared__ __align__(16) uint8_t rows0[kBwdWaves][kRgBytes];
+  __shared__ __align__(16) uint8_t rows1[kBwdWaves][kRgBytes];
+  __shared__ __align__(16) float lsde0[kBwdWaves][64];  // lse of the 32 rows, then delta
+  __shared__ __align__(16) float lsde1[kBwdWaves][64];
+  __shared__ __align__(16) int qrow0[kBwdWaves][32];    // query of each row (-1 past the tile)
+  __shared__ __align__(16) int qrow1[kBwdWaves][32];
+  __shared__ int win_tile_all[kBwdWaves][kTileWin];
+  __shared__ uint32_t win_bits_all[kBwdWaves][kTileWin];
   const int wave = threadIdx.x >> 6, l = lane_id(), hi = l >> 5;
-  uint8_t* wbase = smem + wave * kWaveBytes;
-  int* win_tile = reinterpret_cast<int*>(wbase + 2 * kRgBytes);
-  uint32_t* win_bits = reinterpret_cast<uint32_t*>(win_tile + kTileWin);
+  int* win_tile = win_tile_all[wave];
+  uint32_t* win_bits = win_bits_all[wave];
 
   const int chunks_per_g = (n_tokens + 32 * kBwdWaves - 1) / (32 * kBwdWaves);
   const int g = blockIdx.x / chunks_per_g;
@@ -339,6 +370,9 @@ __global__ __launch_bounds__(kBwdWaves * 64) void k_bwd_dkdv(const uint16_t* __r
       kb[ks] = *reinterpret_cast<const bf16x8*>(k + base + 16 * ks);
       vb[ks] = *reinterpret_cast<const bf16x8*>(v + base + 16 * ks);
     }
+    // Wait for them here (vmcnt(0), a wait the compiler sees): otherwise it cannot tell how many
+    // loads were issued after them on the way into the loop and waits for all at every product.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
   }
   f32x16 adk[4], adv[4];  // dK^T, dV^T tiles [d-tile][32 d x 32 keys], column = this lane's key
 #pragma unroll
@@ -362,21 +396,17 @@ __global__ __launch_bounds__(kBwdWaves * 64) void k_bwd_dkdv(const uint16_t* __r
     const int i0 = t * tile;
     return ((i0 + tile <= n_tokens) ? tile : n_tokens - i0) * r;
   };
-  auto issue_rg = [&](int t, int rg, int buf) {
-    uint8_t* b = wbase + buf * kRgBytes;
+  // Every load in flight is an LDS-direct load (the row values too), so the compiler can count
+  // them in order and wait for one buffer's loads while the other's stay in flight.
+  auto issue_rg = [&](int t, int rg, uint8_t* b, float* lsde, int* qrow) __attribute__((always_inline)) {
     const int nrows = rg_rows(t);
-    // The row values first: their wait (before the LDS writes below) then leaves the 16 row loads
-    // of this group in flight.
-    int qi = -1;
-    float ls = 0.0f, de = 0.0f;
     if (l < 32) {
       const int rho = rg * 32 + l;
-      if (rho < nrows) {
-        qi = t * tile + rho / r;
-        const long long rix = (long long)qi * n_q_heads + g * r + rho % r;
-        ls = lse[rix];
-        de = delta[rix];
-      }
+      const int rr = rho < nrows ? rho : 0;
+      const long long rix = (long long)(t * tile + rr / r) * n_q_heads + g * r + rr % r;
+      __builtin_amdgcn_global_load_lds((const void*)(lse + rix), (lds_void*)lsde, 4, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(delta + rix), (lds_void*)(lsde + 32), 4, 0, 0);
+      qrow[l] = rho < nrows ? t * tile + rho / r : -1;
     }
 #pragma unroll
     for (int ti = 0; ti < 8; ++ti) {
@@ -390,18 +420,11 @@ __global__ __launch_bounds__(kBwdWaves * 64) void k_bwd_dkdv(const uint16_t* __r
       __builtin_amdgcn_global_load_lds((const void*)(dout + src_row * kD + piece * 8),
                                        (lds_void*)(b + kRowTileBytes + ti * 1024), 16, 0, 0);
     }
-    if (l < 32) {
-      int* meta = reinterpret_cast<int*>(b + 2 * kRowTileBytes);
-      meta[l] = qi;
-      reinterpret_cast<float*>(meta + 32)[l] = ls;
-      reinterpret_cast<float*>(meta + 64)[l] = de;
-    }
   };
   // One row group from buffer `buf`: member = this lane's key block is in the tile's union.
-  auto compute_rg = [&](int buf, bool member) {
-    const uint8_t* b = wbase + buf * kRgBytes;
+  auto compute_rg = [&](const uint8_t* b, const float* lsde, const int* qrow, bool member)
+                        __attribute__((always_inline)) {
     const uint8_t* dob = b + kRowTileBytes;
-    const int* meta = reinterpret_cast<const int*>(b + 2 * kRowTileBytes);
     // S = Q K^T, dP = dO V^T: A operands row (l % 32), logical piece 2 ks + (l / 32).
     f32x16 s, dp;
 #pragma unroll
@@ -419,9 +442,9 @@ __global__ __launch_bounds__(kBwdWaves * 64) void k_bwd_dkdv(const uint16_t* __r
     // Rows of score j: 8 (j / 4) + 4 hi + (j % 4).
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      const int4 qi4 = *reinterpret_cast<const int4*>(meta + 8 * a + 4 * hi);
-      const float4 ls4 = *reinterpret_cast<const float4*>(meta + 32 + 8 * a + 4 * hi);
-      const float4 de4 = *reinterpret_cast<const float4*>(meta + 64 + 8 * a + 4 * hi);
+      const int4 qi4 = *reinterpret_cast<const int4*>(qrow + 8 * a + 4 * hi);
+      const float4 ls4 = *reinterpret_cast<const float4*>(lsde + 8 * a + 4 * hi);
+      const float4 de4 = *reinterpret_cast<const float4*>(lsde + 32 + 8 * a + 4 * hi);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int qi = c == 0 ? qi4.x : (c == 1 ? qi4.y : (c == 2 ? qi4.z : qi4.w));
@@ -452,55 +475,82 @@ __global__ __launch_bounds__(kBwdWaves * 64) void k_bwd_dkdv(const uint16_t* __r
       }
   };
 
-  // Walk the tiles t >= the first one holding a query >= j0, a window of kTileWin at a time; list
-  // those whose union holds one of the wave's blocks, then their row groups that reach a query >= j0.
+  // Work items: the row groups, in order, of the tiles t >= the first one holding a query >= j0
+  // whose union holds one of the wave's blocks (listed a window of kTileWin tiles at a time), that
+  // reach a query >= j0.
   const int t_first = j0 / tile;
-  int pend_t = -1, pend_rg = 0, pend_buf = 0;
-  uint32_t pend_bits = 0u;
-  for (int tw = t_first; tw < n_tiles; tw += kTileWin) {
-    int n_win = 0;
-    for (int t0 = tw; t0 < tw + kTileWin && t0 < n_tiles; t0 += 64) {
-      const int t = t0 + l;
-      uint32_t bits = 0u;
-      if (t < n_tiles && t < tw + kTileWin)
-        bits = umask[((long long)g * n_tiles + t) * n_words + (b0 >> 5)] & wmask;
-      const uint64_t m = ballot(bits != 0u);
-      if (bits) {
-        const int pos = n_win + popc64(m & lanemask_lt());
-        win_tile[pos] = t;
-        win_bits[pos] = bits;
-      }
-      n_win += popc64(m);
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    for (int e = 0; e < n_win; ++e) {
-      const int t = win_tile[e];
-      const uint32_t bits = win_bits[e];
-      const int nrows = rg_rows(t);
-      for (int rg = 0; rg * 32 < nrows; ++rg) {
-        const int last_q = t * tile + min(rg * 32 + 31, nrows - 1) / r;
-        if (last_q < j0) continue;  // every key of the wave is past every query of the group
-        // Software pipeline: issue this group, then compute the pending one.
-        const int buf = pend_t < 0 ? 0 : pend_buf ^ 1;
-        issue_rg(t, rg, buf);
-        if (pend_t >= 0) {
-          asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // the pending group's 16 loads landed
-          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-          compute_rg(pend_buf, ((pend_bits >> ((b0 & 31) + my_blk)) & 1u) != 0u);
+  int tw = t_first, n_win = 0, e_win = 0, rg_next = 0;
+  auto next_item = [&](int& it_t, int& it_rg, uint32_t& it_bits) __attribute__((always_inline)) -> bool {
+    while (true) {
+      if (e_win >= n_win) {
+        if (tw >= n_tiles) return false;
+        n_win = 0;
+        for (int t0 = tw; t0 < tw + kTileWin && t0 < n_tiles; t0 += 64) {
+          const int t = t0 + l;
+          uint32_t bits = 0u;
+          if (t < n_tiles && t < tw + kTileWin)
+            bits = umask[((long long)g * n_tiles + t) * n_words + (b0 >> 5)] & wmask;
+          const uint64_t m = ballot(bits != 0u);
+          if (bits) {
+            const int pos = n_win + popc64(m & lanemask_lt());
+            win_tile[pos] = t;
+            win_bits[pos] = bits;
+          }
+          n_win += popc64(m);
         }
-        pend_t = t;
-        pend_rg = rg;
-        pend_buf = buf;
-        pend_bits = bits;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        tw += kTileWin;
+        e_win = 0;
+        rg_next = 0;
+        continue;
       }
+      const int t = win_tile[e_win];
+      const int nrows = rg_rows(t);
+      if (rg_next * 32 >= nrows) {
+        ++e_win;
+        rg_next = 0;
+        continue;
+      }
+      const int rg = rg_next++;
+      const int last_q = t * tile + min(rg * 32 + 31, nrows - 1) / r;
+      if (last_q < j0) continue;  // every key of the wave is past every query of the group
+      it_t = t;
+      it_rg = rg;
+      it_bits = win_bits[e_win];
+      return true;
     }
+  };
+  auto is_member = [&](uint32_t bits) -> bool { return ((bits >> ((b0 & 31) + my_blk)) & 1u) != 0u; };
+  // Software pipeline over two buffers: the next item's rows are in flight while an item is
+  // computed. The waits are explicit: an item's 18 loads (2 row-value loads, then 16 row loads)
+  // were issued before the next item's, so at most the next item's last 16 may still be pending.
+  auto wait_item = [&](bool next_issued) __attribute__((always_inline)) {
+    if (next_issued)
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else
+      wait_vm();
+  };
+  uint8_t* rb0 = rows0[wave];
+  uint8_t* rb1 = rows1[wave];
+  float* ld0 = lsde0[wave];
+  float* ld1 = lsde1[wave];
+  int* qr0 = qrow0[wave];
+  int* qr1 = qrow1[wave];
+  int ta, rga, tb, rgb;
+  uint32_t bitsa, bitsb;
+  bool ha = next_item(ta, rga, bitsa);
+  if (ha) issue_rg(ta, rga, rb0, ld0, qr0);
+  while (ha) {
+    const bool hb = next_item(tb, rgb, bitsb);
+    if (hb) issue_rg(tb, rgb, rb1, ld1, qr1);
+    wait_item(hb);
+    compute_rg(rb0, ld0, qr0, is_member(bitsa));
+    if (!hb) break;
+    ha = next_item(ta, rga, bitsa);
+    if (ha) issue_rg(ta, rga, rb0, ld0, qr0);
+    wait_item(ha);
+    compute_rg(rb1, ld1, qr1, is_member(bitsb));
   }
-  if (pend_t >= 0) {
-    wait_vm();
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    compute_rg(pend_buf, ((pend_bits >> ((b0 & 31) + my_blk)) & 1u) != 0u);
-  }
-  (void)pend_rg;
 
   // dk[g][key][d] = sigma * dK^T[d][key], dv[g][key][d] = dV^T[d][key].
   if (key_ok) {
@@ -523,9 +573,15 @@ __global__ __launch_bounds__(kBwdWaves * 64) void k_bwd_dkdv(const uint16_t* __r
 
 // ------------------------------------------------------------------------------------ launch
 
-size_t attend_bwd_lds_dq(int n_tokens, int block) {
+// Static LDS of the dq kernel (two stages, four token tables, scan words) and its dynamic part (the
+// block list).
+constexpr size_t kDqStaticBytes = 2 * (size_t)kDqStageBytes + 4 * kKeys * 4 + 64;
+size_t attend_bwd_dq_list_bytes(int n_tokens, int block) {
   const int nbc = (n_tokens + block - 1) / block;
-  return (size_t)2 * kDqStageBytes + 16 * ((kDqWaves + 4) / 4) + (size_t)((nbc + 7) / 8 * 8) * 2;
+  return (size_t)((nbc + 7) / 8 * 8) * 2;
+}
+size_t attend_bwd_lds_dq(int n_tokens, int block) {
+  return kDqStaticBytes + attend_bwd_dq_list_bytes(n_tokens, block);
 }
 
 hipError_t launch_attend_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint32_t* umask,
@@ -549,8 +605,8 @@ hipError_t launch_attend_bwd(const uint16_t* q, const uint16_t* k, const uint16_
     const int tile_rows = (tile < n_tokens ? tile : n_tokens) * r;
     const int parts = (tile_rows + rows_wg - 1) / rows_wg;
     const int n_pairs = n_tiles * n_groups;
-    const size_t lds = attend_bwd_lds_dq(n_tokens, block);
-    if (lds > (size_t)max_lds_per_block()) return hipErrorInvalidValue;
+    if (attend_bwd_lds_dq(n_tokens, block) > (size_t)max_lds_per_block()) return hipErrorInvalidValue;
+    const size_t lds = attend_bwd_dq_list_bytes(n_tokens, block);
     const long long grid = (long long)((n_pairs + 7) / 8) * 8 * parts;
     auto kern = k_bwd_dq<kDqWaves>;
     e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -563,10 +619,7 @@ hipError_t launch_attend_bwd(const uint16_t* q, const uint16_t* k, const uint16_
   }
   {
     const int chunks_per_g = (n_tokens + 32 * kBwdWaves - 1) / (32 * kBwdWaves);
-    const size_t lds = (size_t)kBwdWaves * kWaveBytes;
-    e = hipFuncSetAttribute((const void*)k_bwd_dkdv, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_bwd_dkdv, dim3((unsigned)(chunks_per_g * n_groups)), dim3(kBwdWaves * 64), lds, stream, q,
+    hipLaunchKernelGGL(k_bwd_dkdv, dim3((unsigned)(chunks_per_g * n_groups)), dim3(kBwdWaves * 64), 0, stream, q,
                        k, v, umask, lse, delta, dout, dk, dv, n_tokens, n_q_heads, n_groups, block,
                        __builtin_ctz(block), tile, scale, scale_log2, n_words);
     e = hipGetLastError();
