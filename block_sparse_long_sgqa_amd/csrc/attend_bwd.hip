@@ -357,6 +357,10 @@ __global__ __launch_bounds__(kBwdWaves * 64) void k_bwd_dkdv(const uint16_t* __r
   const int j0 = ((blockIdx.x % chunks_per_g) * kBwdWaves + wave) * 32;  // this wave's keys j0 .. j0 + 31
   if (j0 >= n_tokens) return;  // wave-uniform; the waves never synchronise with each other
   const int r = n_q_heads / n_groups;
+  // x / r for the row indices of a tile, 0 <= x < tile * r: the high word of x * ceil(2^32 / r),
+  // exact while x * (r - 1) < 2^32 (checked on the host for x = tile * r).
+  const uint32_t r_magic = r > 1 ? (uint32_t)((0x100000000ull + (uint32_t)r - 1u) / (uint32_t)r) : 0u;
+  auto div_r = [&](int x) -> int { return r > 1 ? (int)__umulhi((uint32_t)x, r_magic) : x; };
   const int n_tiles = (n_tokens + tile - 1) / tile;
   const int key = j0 + (l & 31);
   const bool key_ok = key < n_tokens;
@@ -396,29 +400,72 @@ __global__ __launch_bounds__(kBwdWaves * 64) void k_bwd_dkdv(const uint16_t* __r
     const int i0 = t * tile;
     return ((i0 + tile <= n_tokens) ? tile : n_tokens - i0) * r;
   };
-  // Every load in flight is an LDS-direct load (the row values too), so the compiler can count
-  // them in order and wait for one buffer's loads while the other's stay in flight.
-  auto issue_rg = [&](int t, int rg, uint8_t* b, float* lsde, int* qrow) __attribute__((always_inline)) {
+  // Row group `rg` of tile `t`: its Q and dO rows (swizzled row-major like the forward's V tile)
+  // and each row's query, lse and delta are loaded into registers while the previous group is
+  // computed, then stored into the group's buffer. (LDS-direct loads hold the single wave of the
+  // SIMD up for ~120 cycles each; these loads do not.)
+  // Row rho of a tile's rows lies (rho / r) * Hq + rho % r rows past the tile's first row of group
+  // g. When r divides 32 this splits into a part per row group and a part per row within the group
+  // (fixed for each lane), so the per-item address work is one add per row.
+  const bool r_div32 = (32 % r) == 0;
+  int frow[8];
+#pragma unroll
+  for (int ti = 0; ti < 8; ++ti) {
+    const int rw = 4 * ti + (l >> 4);
+    frow[ti] = (rw / r) * n_q_heads + rw % r;
+  }
+  const int lrow = l & 31;
+  const int frow_l = (lrow / r) * n_q_heads + lrow % r, fq_l = lrow / r;
+  auto load_rg = [&](int t, int rg, u32x4 (&sq)[8], u32x4 (&sd)[8], float& ls, float& de, int& qi)
+                     __attribute__((always_inline)) {
     const int nrows = rg_rows(t);
-    if (l < 32) {
-      const int rho = rg * 32 + l;
-      const int rr = rho < nrows ? rho : 0;
-      const long long rix = (long long)(t * tile + rr / r) * n_q_heads + g * r + rr % r;
-      __builtin_amdgcn_global_load_lds((const void*)(lse + rix), (lds_void*)lsde, 4, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(delta + rix), (lds_void*)(lsde + 32), 4, 0, 0);
-      qrow[l] = rho < nrows ? t * tile + rho / r : -1;
+    const long long tbase = (long long)(t * tile) * n_q_heads + g * r;  // row 0 of the tile, group g
+    long long gbase = 0;                                              // row rg * 32 (r | 32)
+    if (r_div32) gbase = tbase + (long long)(rg * (32 / r)) * n_q_heads;
+    {
+      const int rho = rg * 32 + lrow;
+      long long rix;
+      int qq;
+      if (r_div32) {
+        qq = rg * (32 / r) + fq_l;
+        rix = rho < nrows ? gbase + frow_l : tbase;
+      } else {
+        const int rr = rho < nrows ? rho : 0;
+        qq = div_r(rr);
+        rix = tbase + (long long)qq * n_q_heads + (rr - qq * r);
+      }
+      ls = lse[rix];
+      de = delta[rix];
+      qi = rho < nrows ? t * tile + qq : -1;
     }
 #pragma unroll
     for (int ti = 0; ti < 8; ++ti) {
       const int rw = 4 * ti + (l >> 4);
       const int rho = rg * 32 + rw;
-      const int rr = rho < nrows ? rho : 0;
-      const long long src_row = (long long)(t * tile + rr / r) * n_q_heads + g * r + rr % r;
+      long long src_row;
+      if (r_div32) {
+        src_row = rho < nrows ? gbase + frow[ti] : tbase;
+      } else {
+        const int rr = rho < nrows ? rho : 0;
+        const int qq = div_r(rr);
+        src_row = tbase + (long long)qq * n_q_heads + (rr - qq * r);
+      }
       const int piece = v_phys(rw, l & 15);
-      __builtin_amdgcn_global_load_lds((const void*)(q + src_row * kD + piece * 8), (lds_void*)(b + ti * 1024), 16,
-                                       0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(dout + src_row * kD + piece * 8),
-                                       (lds_void*)(b + kRowTileBytes + ti * 1024), 16, 0, 0);
+      sq[ti] = *reinterpret_cast<const u32x4*>(q + src_row * kD + piece * 8);
+      sd[ti] = *reinterpret_cast<const u32x4*>(dout + src_row * kD + piece * 8);
+    }
+  };
+  auto store_rg = [&](uint8_t* b, float* lsde, int* qrow, const u32x4 (&sq)[8], const u32x4 (&sd)[8], float ls,
+                      float de, int qi) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ti = 0; ti < 8; ++ti) {
+      *reinterpret_cast<u32x4*>(b + ti * 1024 + 16 * l) = sq[ti];
+      *reinterpret_cast<u32x4*>(b + kRowTileBytes + ti * 1024 + 16 * l) = sd[ti];
+    }
+    if (l < 32) {
+      lsde[l] = ls;
+      lsde[32 + l] = de;
+      qrow[l] = qi;
     }
   };
   // One row group from buffer `buf`: member = this lane's key block is in the tile's union.
@@ -432,12 +479,24 @@ __global__ __launch_bounds__(kBwdWaves * 64) void k_bwd_dkdv(const uint16_t* __r
       s[j] = 0.0f;
       dp[j] = 0.0f;
     }
+    // The operands of step ks + 2 are read while the products of step ks run.
     const int arow = l & 31;
+    auto off_of = [&](int ks) { return arow * 256 + 16 * v_phys(arow, 2 * ks + hi); };
+    bf16x8 qa[3], da[3];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      qa[ks] = *reinterpret_cast<const bf16x8*>(b + off_of(ks));
+      da[ks] = *reinterpret_cast<const bf16x8*>(dob + off_of(ks));
+    }
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const int off = arow * 256 + 16 * v_phys(arow, 2 * ks + hi);
-      s = mfma32(*reinterpret_cast<const bf16x8*>(b + off), kb[ks], s);
-      dp = mfma32(*reinterpret_cast<const bf16x8*>(dob + off), vb[ks], dp);
+      if (ks + 2 < 8) {
+        qa[(ks + 2) % 3] = *reinterpret_cast<const bf16x8*>(b + off_of(ks + 2));
+        da[(ks + 2) % 3] = *reinterpret_cast<const bf16x8*>(dob + off_of(ks + 2));
+      }
+      s = mfma32(qa[ks % 3], kb[ks], s);
+      dp = mfma32(da[ks % 3], vb[ks], dp);
+      __builtin_amdgcn_sched_barrier(0);
     }
     // Rows of score j: 8 (j / 4) + 4 hi + (j % 4).
 #pragma unroll
@@ -465,14 +524,25 @@ __global__ __launch_bounds__(kBwdWaves * 64) void k_bwd_dkdv(const uint16_t* __r
         pp[ss][e] = (__bf16)s[8 * ss + e];
         pd[ss][e] = (__bf16)dp[8 * ss + e];
       }
-    // dV^T += dO^T P, dK^T += Q^T dS.
+    // dV^T += dO^T P, dK^T += Q^T dS; step = 2 dt + ss, operands read two steps ahead.
+    auto tr_op = [&](const uint8_t* base, int step) { return tr_read(base + lo.v[step >> 1] + (16 * (step & 1)) * 256); };
+    bf16x8 oa[3], qt[3];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int st = 0; st < 2; ++st) {
+      oa[st] = tr_op(dob, st);
+      qt[st] = tr_op(b, st);
+    }
 #pragma unroll
-      for (int ss = 0; ss < 2; ++ss) {
-        adv[dt] = mfma32(tr_read(dob + lo.v[dt] + (16 * ss) * 256), pp[ss], adv[dt]);
-        adk[dt] = mfma32(tr_read(b + lo.v[dt] + (16 * ss) * 256), pd[ss], adk[dt]);
+    for (int st = 0; st < 8; ++st) {
+      if (st + 2 < 8) {
+        oa[(st + 2) % 3] = tr_op(dob, st + 2);
+        qt[(st + 2) % 3] = tr_op(b, st + 2);
       }
+      const int dt = st >> 1, ss = st & 1;
+      adv[dt] = mfma32(oa[st % 3], pp[ss], adv[dt]);
+      adk[dt] = mfma32(qt[st % 3], pd[ss], adk[dt]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   // Work items: the row groups, in order, of the tiles t >= the first one holding a query >= j0
@@ -480,6 +550,9 @@ __global__ __launch_bounds__(kBwdWaves * 64) void k_bwd_dkdv(const uint16_t* __r
   // reach a query >= j0.
   const int t_first = j0 / tile;
   int tw = t_first, n_win = 0, e_win = 0, rg_next = 0;
+  int cur_t = 0, cur_nrows = 0;  // the window entry e_win (read when e_win moves)
+  uint32_t cur_bits = 0u;
+  bool cur_stale = true;
   auto next_item = [&](int& it_t, int& it_rg, uint32_t& it_bits) __attribute__((always_inline)) -> bool {
     while (true) {
       if (e_win >= n_win) {
@@ -502,34 +575,32 @@ __global__ __launch_bounds__(kBwdWaves * 64) void k_bwd_dkdv(const uint16_t* __r
         tw += kTileWin;
         e_win = 0;
         rg_next = 0;
+        cur_stale = true;
         continue;
       }
-      const int t = win_tile[e_win];
-      const int nrows = rg_rows(t);
-      if (rg_next * 32 >= nrows) {
+      if (cur_stale) {
+        cur_t = win_tile[e_win];
+        cur_bits = win_bits[e_win];
+        cur_nrows = rg_rows(cur_t);
+        cur_stale = false;
+      }
+      if (rg_next * 32 >= cur_nrows) {
         ++e_win;
         rg_next = 0;
+        cur_stale = true;
         continue;
       }
       const int rg = rg_next++;
-      const int last_q = t * tile + min(rg * 32 + 31, nrows - 1) / r;
+      const int last_q = cur_t * tile + div_r(min(rg * 32 + 31, cur_nrows - 1));
       if (last_q < j0) continue;  // every key of the wave is past every query of the group
-      it_t = t;
+      it_t = cur_t;
       it_rg = rg;
-      it_bits = win_bits[e_win];
+      it_bits = cur_bits;
       return true;
     }
   };
   auto is_member = [&](uint32_t bits) -> bool { return ((bits >> ((b0 & 31) + my_blk)) & 1u) != 0u; };
-  // Software pipeline over two buffers: the next item's rows are in flight while an item is
-  // computed. The waits are explicit: an item's 18 loads (2 row-value loads, then 16 row loads)
-  // were issued before the next item's, so at most the next item's last 16 may still be pending.
-  auto wait_item = [&](bool next_issued) __attribute__((always_inline)) {
-    if (next_issued)
-      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    else
-      wait_vm();
-  };
+  // Software pipeline over two buffers: the next item's rows are loaded while an item is computed.
   uint8_t* rb0 = rows0[wave];
   uint8_t* rb1 = rows1[wave];
   float* ld0 = lsde0[wave];
@@ -538,18 +609,24 @@ __global__ __launch_bounds__(kBwdWaves * 64) void k_bwd_dkdv(const uint16_t* __r
   int* qr1 = qrow1[wave];
   int ta, rga, tb, rgb;
   uint32_t bitsa, bitsb;
+  u32x4 sq[8], sd[8];
+  float sls, sde;
+  int sqi;
   bool ha = next_item(ta, rga, bitsa);
-  if (ha) issue_rg(ta, rga, rb0, ld0, qr0);
+  if (ha) {
+    load_rg(ta, rga, sq, sd, sls, sde, sqi);
+    store_rg(rb0, ld0, qr0, sq, sd, sls, sde, sqi);
+  }
   while (ha) {
     const bool hb = next_item(tb, rgb, bitsb);
-    if (hb) issue_rg(tb, rgb, rb1, ld1, qr1);
-    wait_item(hb);
+    if (hb) load_rg(tb, rgb, sq, sd, sls, sde, sqi);
     compute_rg(rb0, ld0, qr0, is_member(bitsa));
     if (!hb) break;
+    store_rg(rb1, ld1, qr1, sq, sd, sls, sde, sqi);
     ha = next_item(ta, rga, bitsa);
-    if (ha) issue_rg(ta, rga, rb0, ld0, qr0);
-    wait_item(ha);
+    if (ha) load_rg(ta, rga, sq, sd, sls, sde, sqi);
     compute_rg(rb1, ld1, qr1, is_member(bitsb));
+    if (ha) store_rg(rb0, ld0, qr0, sq, sd, sls, sde, sqi);
   }
 
   // dk[g][key][d] = sigma * dK^T[d][key], dv[g][key][d] = dV^T[d][key].
@@ -590,6 +667,11 @@ hipError_t launch_attend_bwd(const uint16_t* q, const uint16_t* k, const uint16_
                              int tile, float scale, hipStream_t stream) {
   const long long n_rows = (long long)n_tokens * n_q_heads;
   if (n_rows == 0) return hipSuccess;
+  {  // the dk/dv kernel divides row indices by r with a multiply-high (see k_bwd_dkdv)
+    const long long rr = n_q_heads / n_groups;
+    const long long tr = (long long)(tile < n_tokens ? tile : n_tokens) * rr;
+    if (tr * (rr - 1) >= (1LL << 32)) return hipErrorInvalidValue;
+  }
   hipLaunchKernelGGL(k_bwd_delta, dim3((unsigned)((n_rows + 15) / 16)), dim3(256), 0, stream, out, dout, delta,
                      n_rows);
   hipError_t e = hipGetLastError();

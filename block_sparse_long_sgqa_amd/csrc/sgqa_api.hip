@@ -83,6 +83,9 @@ int check_params(const sgqa_params* p, int need, bool prefill) {
   }
   if (need & NEED_BWD) {
     if (attend_bwd_lds_dq(p->n_tokens, p->block) > kGfx950LdsBytes) return SGQA_ERR_SHAPE;
+    const long long r = p->n_kv_heads > 0 ? p->n_q_heads / p->n_kv_heads : 1;
+    const long long tile = p->union_tile < p->n_tokens ? p->union_tile : p->n_tokens;
+    if (tile * r * (r - 1) >= (1LL << 32)) return SGQA_ERR_SHAPE;  // row-index division in dk/dv
   }
   if (need & NEED_MASKED) {
     if (attend_masked_loads(p->n_q_heads, p->n_kv_heads, p->block) == 0) return SGQA_ERR_SHAPE;

@@ -284,7 +284,8 @@ int sgqa_attend_fwd(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k
  *   dq[i][h] = sigma * sum_{j in J} p_ij (<dout[i][h], v[g][j]> - delta_i) k[g][j]
  * dq [N][Hq][D], dk, dv [G][N][D] bf16 out (fp32 sums, one bf16 rounding; keys no row attends get 0).
  * Deterministic: every sum has a fixed order (no floating-point atomics). Workspace:
- * sgqa_workspace_size(p, SGQA_OP_ATTEND_BWD) (the deltas). */
+ * sgqa_workspace_size(p, SGQA_OP_ATTEND_BWD) (the deltas). Shapes as sgqa_attend, and
+ * min(Tq, N) * r * (r - 1) < 2^32 with r = Hq / G (otherwise SGQA_ERR_SHAPE). */
 int sgqa_attend_bwd(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k, const sgqa_bf16* v,
                     const uint32_t* umask, const int32_t* ucount, const sgqa_bf16* out, const float* lse,
                     const sgqa_bf16* dout, sgqa_bf16* dq, sgqa_bf16* dk, sgqa_bf16* dv, void* ws,
