@@ -45,15 +45,20 @@ def parse():
     return ap.parse_args()
 
 
-def profiled_traffic(kernel: str, workload: str, source: str):
+# The files the prefill attention kernel is built from (the traffic profile is tied to their contents).
+ATTEND_SOURCES = ("block_sparse_long_sgqa_amd/csrc/attend.hip", "block_sparse_long_sgqa_amd/csrc/attn_common.hpp")
+
+
+def profiled_traffic(kernel: str, workload: str, sources):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 summary (FETCH_SIZE + WRITE_SIZE,
-    calibrated), or None when there is none or the kernel source changed since it was taken."""
+    calibrated), or None when there is none or the kernel's sources changed since it was taken."""
     import hashlib
 
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
     if not os.path.exists(path):
         return None
-    cur = hashlib.sha256(open(os.path.join(ROOT, source), "rb").read()).hexdigest()[:16]
+    blob = b"".join(open(os.path.join(ROOT, src), "rb").read() for src in sources)
+    cur = hashlib.sha256(blob).hexdigest()[:16]
     for line in open(path):
         if line.startswith(f"traffic {kernel} "):
             kv = dict(t.split("=", 1) for t in line.split()[2:])
@@ -570,7 +575,7 @@ def main():
                    "topk_tokens": p.topk_tokens, "union_tile": p.union_tile, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": "attend", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": profiled_traffic("attend", "long_prefill_128k", "block_sparse_long_sgqa_amd/csrc/attend.hip")
+                     "traffic": profiled_traffic("attend", "long_prefill_128k", ATTEND_SOURCES)
                      if wl.name == "long_prefill_128k" else None,
                      "algorithmic_flops_per_launch": res["attn_flops"]},
         "stages_ms": st,
