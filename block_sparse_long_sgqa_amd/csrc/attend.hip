@@ -179,18 +179,26 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
   };
 
   // Gathers. Loop step n fetches the K tile of chunk n + 1 and the V tile of chunk n with 17 + 16
-  // wave-wide LDS-direct loads (the tile gather layout); instruction ii goes to wave ii % kIssuers
-  // of wave group 0, which spreads its share over the K steps of its score products (an LDS-direct
-  // load holds up the issuing wave while the memory pipeline drains, so issuing them in one burst
-  // stalls every wave). Each lane takes the tokens of its rows from the chunks' token tables,
-  // which the first wave writes two steps ahead.
+  // wave-wide LDS-direct loads (the tile gather layout). A wave spreads its share over the K steps of
+  // its score products (an LDS-direct load holds up the issuing wave while the memory pipeline
+  // drains, so issuing them in one burst stalls every wave). Each lane takes the tokens of its rows
+  // from the chunks' token tables, which the first wave writes two steps ahead.
   // The masked variant keeps more state in registers and issues in one burst at the start of the
   // step from every wave instead.
   constexpr bool kSpread = SEL_LOADS == 0;
   constexpr int kInsts = kKTileInsts + kVTileInsts;
+  // Spread: group 0 issues loads 16 .. 32 (the last K load and the V tile) during its products in
+  // the first half-period, group 1 loads 0 .. 15 (K) during its products in the second (they land
+  // before the end of the step all the same; an even split measured ~4 % faster than group 0
+  // issuing all). Burst: every wave, load ii to wave ii % WAVES.
+  constexpr int kG1Insts = kSpread ? 16 : 0;
   constexpr int kIssuers = kSpread ? WAVES / 2 : WAVES;
-  constexpr int kPer = (kInsts + kIssuers - 1) / kIssuers;  // loads per issuing wave
+  constexpr int kPer0 = (kInsts - kG1Insts + kIssuers - 1) / kIssuers;
+  constexpr int kPer1 = (kG1Insts + kIssuers - 1) / kIssuers;
+  constexpr int kPer = kPer0 > kPer1 ? kPer0 : kPer1;  // loads per issuing wave (at most)
   static_assert(kPer <= 9, "at most one load per K step plus one");
+  const int ii_first = kSpread ? (wave < WAVES / 2 ? kG1Insts + wave : wave - WAVES / 2) : wave;
+  const int ii_end = kSpread ? (wave < WAVES / 2 ? kInsts : kG1Insts) : kInsts;
   auto slot_of = [&](int ii, int& row, int& piece) __attribute__((always_inline)) {
     const bool is_v = ii >= kKTileInsts;
     const int sl = (is_v ? ii - kKTileInsts : ii) * 64 + l;
@@ -207,10 +215,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
   auto gather_tokens = [&](int n, int (&tq)[kPer]) __attribute__((always_inline)) {
 #pragma unroll
     for (int xi = 0; xi < kPer; ++xi) {
-      const int ii = wave + xi * kIssuers;
+      const int ii = ii_first + xi * kIssuers;
       int row, piece;
       slot_of(ii, row, piece);
-      const int t = (ii >= kKTileInsts ? toks + (n & 3) * kKeys : toks + ((n + 1) & 3) * kKeys)[row];
+      const int t = (ii >= kKTileInsts ? toks + (n & 3) * kKeys : toks + ((n + 1) & 3) * kKeys)[row & (kKeys - 1)];
       tq[xi] = t == 0x7FFFFFFF ? 0 : t;
     }
   };
@@ -218,9 +226,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
   // into vdst (if v_on).
   auto gather_one = [&](int xi, const int (&tq)[kPer], uint8_t* kdst, uint8_t* vdst, bool k_on,
                         bool v_on) __attribute__((always_inline)) {
-    const int ii = wave + xi * kIssuers;
+    const int ii = ii_first + xi * kIssuers;
     const bool is_v = ii >= kKTileInsts;
-    if (ii < kInsts && (is_v ? v_on : k_on)) {
+    if (ii < ii_end && (is_v ? v_on : k_on)) {
       int row, piece;
       slot_of(ii, row, piece);
       const uint16_t* base = is_v ? vbase : kbase;
@@ -294,10 +302,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
 
   // Two wave groups take turns on each SIMD (wave w and wave w + WAVES / 2 share one): while one
   // group runs the matrix-core products of a chunk, the other runs the softmax of its previous
-  // chunk. Half-period 2n: the gathers of K(n + 1) and V(n) start; group 0 computes S(n) and
-  // P(n - 1) V(n - 1), group 1 the softmax of chunk n - 1. Half-period 2n + 1: group 0 the softmax
-  // of chunk n, group 1 S(n) and P(n - 1) V(n - 1); the membership table of chunk n + 1 is built;
-  // then every wave waits for its gathers and the workgroup syncs. A K tile is read up to
+  // chunk. Half-period 2n: group 0 computes S(n) and P(n - 1) V(n - 1) and starts its share of the
+  // gathers of K(n + 1) and V(n), group 1 runs the softmax of chunk n - 1. Half-period 2n + 1:
+  // group 0 the softmax of chunk n, group 1 S(n) and P(n - 1) V(n - 1) and the rest of the
+  // gathers; the membership table of chunk n + 1 is built; then every wave waits for its gathers
+  // and the workgroup syncs. A K tile is read up to
   // half-period 2n + 1, a V tile up to 2n + 3, a token table (written in step n - 2) up to 2n + 2
   // and a membership table from 2n + 1 to 2n + 2: two K, two V, four token and two membership
   // slots suffice.
@@ -327,9 +336,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
     uint8_t* v_cur = P ? v_tile1 : v_tile0;   // V(n)
     uint8_t* v_prev = P ? v_tile0 : v_tile1;  // V(n - 1)
     const bool k_on = n + 1 < n_chunks, v_on = n < n_chunks;
-    // S(n) and P(n - 1) V(n - 1) at raised wave priority; group 0 also issues the step's gathers.
+    // S(n) and P(n - 1) V(n - 1) at raised wave priority, with this wave's share of the gathers.
     auto products = [&]() __attribute__((always_inline)) {
-      const bool issuing = kSpread && grp == 0 && n < n_chunks;
+      const bool issuing = kSpread && (grp == 0 || kG1Insts > 0) && n < n_chunks;
       int tq[kPer];
       if (issuing) gather_tokens(n, tq);
       if (!has_rows) {
@@ -381,7 +390,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
     write_tokens(0);
     write_tokens(1);
     __syncthreads();
-    if (!kSpread || grp == 0) {  // the K tile of chunk 0
+    if (!kSpread || grp == 0 || kG1Insts > 0) {  // the K tile of chunk 0
       int tq[kPer];
       gather_tokens(-1, tq);
 #pragma unroll

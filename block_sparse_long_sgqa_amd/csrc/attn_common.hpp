@@ -194,7 +194,7 @@ __device__ __forceinline__ void chunk_softmax(f32x16 (&s)[QT][2], const int* tok
         mx = fmaxf(mx, x);
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = max_of_halves(mx);
     const float m_new = fmaxf(st.m[qt], mx * scale_log2);
     if (ballot(m_new > st.m[qt] + kLazyLog2)) {
       const float alpha = fast_exp2(st.m[qt] - m_new);

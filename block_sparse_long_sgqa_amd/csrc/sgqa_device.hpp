@@ -90,6 +90,13 @@ __device__ __forceinline__ uint32_t wave_prefix_sum(uint32_t v) {
   return v;
 }
 
+// max(x of lane l, x of lane l ^ 32) in every lane, through one v_permlane32_swap (a register swap
+// of the two wave halves) instead of an LDS permute.
+__device__ __forceinline__ float max_of_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
