@@ -178,64 +178,85 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
     return tk < n_tokens ? tk : -1;
   };
 
-  // Gathers. Loop step n fetches the K tile of chunk n + 1 and the V tile of chunk n with 17 + 16
-  // wave-wide LDS-direct loads (the tile gather layout). A wave spreads its share over the K steps of
-  // its score products (an LDS-direct load holds up the issuing wave while the memory pipeline
-  // drains, so issuing them in one burst stalls every wave). Each lane takes the tokens of its rows
-  // from the chunks' token tables, which the first wave writes two steps ahead.
-  // The masked variant keeps more state in registers and issues in one burst at the start of the
-  // step from every wave instead.
-  constexpr bool kSpread = SEL_LOADS == 0;
-  constexpr int kInsts = kKTileInsts + kVTileInsts;
-  // Spread: group 0 issues loads 16 .. 32 (the last K load and the V tile) during its products in
-  // the first half-period, group 1 loads 0 .. 15 (K) during its products in the second (they land
-  // before the end of the step all the same; an even split measured ~4 % faster than group 0
-  // issuing all). Burst: every wave, load ii to wave ii % WAVES.
-  constexpr int kG1Insts = kSpread ? 16 : 0;
-  constexpr int kIssuers = kSpread ? WAVES / 2 : WAVES;
-  constexpr int kPer0 = (kInsts - kG1Insts + kIssuers - 1) / kIssuers;
-  constexpr int kPer1 = (kG1Insts + kIssuers - 1) / kIssuers;
-  constexpr int kPer = kPer0 > kPer1 ? kPer0 : kPer1;  // loads per issuing wave (at most)
-  static_assert(kPer <= 9, "at most one load per K step plus one");
-  const int ii_first = kSpread ? (wave < WAVES / 2 ? kG1Insts + wave : wave - WAVES / 2) : wave;
-  const int ii_end = kSpread ? (wave < WAVES / 2 ? kInsts : kG1Insts) : kInsts;
+  // Gathers. Loop step n fetches the K tile of chunk n + 1 and the V tile of chunk n. Each lane
+  // takes the tokens of its rows from the chunks' token tables, which the first wave writes two steps
+  // ahead; invalid keys read row 0 of the group (finite data, masked out through the token table).
+  //  * Plain variant, register-staged: at the start of the step every wave loads its share of the
+  //    16 + 16 wave-wide 16-byte loads (1 KiB each) into registers, and after the mid-step barrier it
+  //    writes them to the tiles. The loads fly during the first half-period; unlike LDS-direct loads
+  //    they do not hold up the issuing wave, and the compiler has no LDS write in flight to wait for
+  //    before the operand reads (spreading them over the products, or issuing them from the softmax
+  //    group only, measured slower). K load i, lane l fills row (64 i + l) / 16, piece (64 i + l) % 16
+  //    (the padding piece of a K row is never written); V load i, lane l fills V slot 64 i + l of the
+  //    tile gather layout.
+  //  * Masked variant: LDS-direct loads (tile gather layout, 17 + 16 instructions) in one burst at the
+  //    start of the step; it holds the membership state in registers and has none to stage with.
+  constexpr bool kStaged = SEL_LOADS == 0;
+  constexpr int kKInsts = kStaged ? kKeys * kD * 2 / 1024 : kKTileInsts;
+  constexpr int kInsts = kKInsts + kVTileInsts;
+  constexpr int kPer = (kInsts + WAVES - 1) / WAVES;  // loads per wave: load xi is load wave + xi * WAVES
+  // Staged: loads 0 .. kKPer - 1 of every wave are K loads, the rest V loads.
+  constexpr int kKPer = kKInsts / WAVES;
+  static_assert(!kStaged || (kKInsts % WAVES == 0 && kInsts % WAVES == 0), "staged loads split evenly");
   auto slot_of = [&](int ii, int& row, int& piece) __attribute__((always_inline)) {
-    const bool is_v = ii >= kKTileInsts;
-    const int sl = (is_v ? ii - kKTileInsts : ii) * 64 + l;
+    const bool is_v = ii >= kKInsts;
+    const int sl = (is_v ? ii - kKInsts : ii) * 64 + l;
     if (is_v) {
       row = sl >> 4;
       piece = v_phys(row, sl & 15);
+    } else if (kStaged) {
+      row = sl >> 4;
+      piece = sl & 15;
     } else {
       row = sl / kKSlotsPerRow;
       piece = sl - row * kKSlotsPerRow;
       if (piece == 16) piece = 0;  // padding slot: any in-bounds data
     }
   };
-  // Tokens of this wave's loads of step n (all table reads before the first load, which writes LDS).
-  auto gather_tokens = [&](int n, int (&tq)[kPer]) __attribute__((always_inline)) {
+  auto load_on = [&](int ii, bool k_on, bool v_on) __attribute__((always_inline)) -> bool {
+    return ii < kInsts && (ii >= kKInsts ? v_on : k_on);
+  };
+  // Tokens of this wave's loads of step n (all table reads before the first load). Without a chunk
+  // n + 1 (k_on false) the K loads take token 0 (the staged variant loads and stores them anyway:
+  // that K tile is never read).
+  auto gather_tokens = [&](int n, int (&tq)[kPer], bool k_on) __attribute__((always_inline)) {
 #pragma unroll
     for (int xi = 0; xi < kPer; ++xi) {
-      const int ii = ii_first + xi * kIssuers;
+      const int ii = wave + xi * WAVES;
       int row, piece;
       slot_of(ii, row, piece);
-      const int t = (ii >= kKTileInsts ? toks + (n & 3) * kKeys : toks + ((n + 1) & 3) * kKeys)[row & (kKeys - 1)];
-      tq[xi] = t == 0x7FFFFFFF ? 0 : t;
+      const bool is_v = ii >= kKInsts;
+      const int t = (is_v ? toks + (n & 3) * kKeys : toks + ((n + 1) & 3) * kKeys)[row & (kKeys - 1)];
+      tq[xi] = (t == 0x7FFFFFFF || !(is_v || k_on)) ? 0 : t;
     }
   };
-  // Load xi of this wave for step n: K rows of chunk n + 1 into kdst (if k_on), V rows of chunk n
-  // into vdst (if v_on).
+  auto src_of = [&](int ii, int tk) __attribute__((always_inline)) -> const uint16_t* {
+    int row, piece;
+    slot_of(ii, row, piece);
+    return (ii >= kKInsts ? vbase : kbase) + piece * 8 + (long long)tk * kD;
+  };
+  // Masked variant: load xi of this wave for step n, K rows of chunk n + 1 into kdst (if k_on), V
+  // rows of chunk n into vdst (if v_on), LDS-direct.
   auto gather_one = [&](int xi, const int (&tq)[kPer], uint8_t* kdst, uint8_t* vdst, bool k_on,
                         bool v_on) __attribute__((always_inline)) {
-    const int ii = ii_first + xi * kIssuers;
-    const bool is_v = ii >= kKTileInsts;
-    if (ii < ii_end && (is_v ? v_on : k_on)) {
-      int row, piece;
-      slot_of(ii, row, piece);
-      const uint16_t* base = is_v ? vbase : kbase;
-      uint8_t* dst = (is_v ? vdst : kdst) + (is_v ? ii - kKTileInsts : ii) * 1024;
-      __builtin_amdgcn_global_load_lds((const void*)(base + piece * 8 + (long long)tq[xi] * kD), (lds_void*)dst, 16,
-                                       0, 0);
+    const int ii = wave + xi * WAVES;
+    if (load_on(ii, k_on, v_on)) {
+      const bool is_v = ii >= kKInsts;
+      uint8_t* dst = (is_v ? vdst : kdst) + (is_v ? ii - kKInsts : ii) * 1024;
+      __builtin_amdgcn_global_load_lds((const void*)src_of(ii, tq[xi]), (lds_void*)dst, 16, 0, 0);
     }
+  };
+  // Plain variant: the same loads into registers, and their stores into the tiles (unconditional, so
+  // that the compiler keeps the stores together after the barrier).
+  auto stage_load = [&](int xi, const int (&tq)[kPer], u32x4& d) __attribute__((always_inline)) {
+    d = *reinterpret_cast<const u32x4*>(src_of(wave + xi * WAVES, tq[xi]));
+  };
+  auto stage_store = [&](int xi, const u32x4& d, uint8_t* kdst, uint8_t* vdst) __attribute__((always_inline)) {
+    const int ii = wave + xi * WAVES;
+    const bool is_v = xi >= kKPer;
+    const int sl = (is_v ? ii - kKInsts : ii) * 64 + l;
+    uint8_t* dst = is_v ? vdst + 16 * sl : kdst + (sl >> 4) * kKRowBytes + 16 * (sl & 15);
+    *reinterpret_cast<u32x4*>(dst) = d;
   };
   auto write_tokens = [&](int c) __attribute__((always_inline)) {  // token table of chunk c
     if (threadIdx.x < kKeys && c < n_chunks) {
@@ -302,11 +323,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
 
   // Two wave groups take turns on each SIMD (wave w and wave w + WAVES / 2 share one): while one
   // group runs the matrix-core products of a chunk, the other runs the softmax of its previous
-  // chunk. Half-period 2n: group 0 computes S(n) and P(n - 1) V(n - 1) and starts its share of the
-  // gathers of K(n + 1) and V(n), group 1 runs the softmax of chunk n - 1. Half-period 2n + 1:
-  // group 0 the softmax of chunk n, group 1 S(n) and P(n - 1) V(n - 1) and the rest of the
-  // gathers; the membership table of chunk n + 1 is built; then every wave waits for its gathers
-  // and the workgroup syncs. A K tile is read up to
+  // chunk. Step n starts the gathers of K(n + 1) and V(n). Half-period 2n: group 0 computes S(n) and
+  // P(n - 1) V(n - 1), group 1 runs the softmax of chunk n - 1. Then the staged gathers are written
+  // to the tiles. Half-period 2n + 1: group 0 the softmax of chunk n, group 1 S(n) and
+  // P(n - 1) V(n - 1); the membership table of chunk n + 1 is built; then the workgroup syncs (the
+  // LDS-direct gathers are waited for first). A K tile is read up to
   // half-period 2n + 1, a V tile up to 2n + 3, a token table (written in step n - 2) up to 2n + 2
   // and a membership table from 2n + 1 to 2n + 2: two K, two V, four token and two membership
   // slots suffice.
@@ -336,38 +357,27 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
     uint8_t* v_cur = P ? v_tile1 : v_tile0;   // V(n)
     uint8_t* v_prev = P ? v_tile0 : v_tile1;  // V(n - 1)
     const bool k_on = n + 1 < n_chunks, v_on = n < n_chunks;
-    // S(n) and P(n - 1) V(n - 1) at raised wave priority, with this wave's share of the gathers.
+    // S(n) and P(n - 1) V(n - 1) at raised wave priority.
     auto products = [&]() __attribute__((always_inline)) {
-      const bool issuing = kSpread && (grp == 0 || kG1Insts > 0) && n < n_chunks;
-      int tq[kPer];
-      if (issuing) gather_tokens(n, tq);
-      if (!has_rows) {
-        if (issuing)
-#pragma unroll
-          for (int xi = 0; xi < kPer; ++xi) gather_one(xi, tq, k_next, v_cur, k_on, v_on);
-        return;
-      }
+      if (!has_rows) return;
       __builtin_amdgcn_s_setprio(1);
-      if (n < n_chunks) {
-        auto hook = [&](int ks) __attribute__((always_inline)) {
-          if (!issuing) return;
-          gather_one(ks, tq, k_next, v_cur, k_on, v_on);
-          if (ks == 7)
-#pragma unroll
-            for (int xi = 8; xi < kPer; ++xi) gather_one(xi, tq, k_next, v_cur, k_on, v_on);
-        };
-        score_products<QT, decltype(hook), kKAhead>(k_cur, lo, qreg, s, hook);
-      }
+      if (n < n_chunks) score_products<QT, NoHook, kKAhead>(k_cur, lo, qreg, s);
       if (n >= 1) pv_products<QT, kVAhead>(v_prev, lo, pb, st);
       __builtin_amdgcn_s_setprio(0);
     };
     if constexpr (SEL)
       if (n + 1 < n_chunks) sel_load(n + 1);
-    if (!kSpread && n < n_chunks) {
+    u32x4 stg[kStaged ? kPer : 1];
+    if (n < n_chunks) {
       int tq[kPer];
-      gather_tokens(n, tq);
+      gather_tokens(n, tq, k_on);
 #pragma unroll
-      for (int xi = 0; xi < kPer; ++xi) gather_one(xi, tq, k_next, v_cur, k_on, v_on);
+      for (int xi = 0; xi < kPer; ++xi) {
+        if constexpr (kStaged)
+          stage_load(xi, tq, stg[xi]);
+        else
+          gather_one(xi, tq, k_next, v_cur, k_on, v_on);
+      }
     }
     if (grp == 0) {
       products();
@@ -376,13 +386,17 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
       softmax(n - 1);
     }
     __builtin_amdgcn_s_barrier();
+    if constexpr (kStaged)
+      if (n < n_chunks)
+#pragma unroll
+        for (int xi = 0; xi < kPer; ++xi) stage_store(xi, stg[xi], k_next, v_cur);
     if (grp == 0)
       softmax(n);
     else
       products();
     if constexpr (SEL)
       if (n + 1 < n_chunks) sel_store(n + 1);
-    wait_vm();
+    if constexpr (!kStaged) wait_vm();
     __syncthreads();
   };
   if (n_chunks > 0) {
@@ -390,16 +404,28 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
     write_tokens(0);
     write_tokens(1);
     __syncthreads();
-    if (!kSpread || grp == 0 || kG1Insts > 0) {  // the K tile of chunk 0
+    {  // the K tile of chunk 0
       int tq[kPer];
-      gather_tokens(-1, tq);
+      gather_tokens(-1, tq, true);
+      if constexpr (kStaged) {  // the K loads only
+        u32x4 stg[kKPer > 0 ? kKPer : 1];
 #pragma unroll
-      for (int xi = 0; xi < kPer; ++xi) gather_one(xi, tq, k_tile0, v_tile0, true, false);
+        for (int xi = 0; xi < kKPer; ++xi) stage_load(xi, tq, stg[xi]);
+#pragma unroll
+        for (int xi = 0; xi < kKPer; ++xi) stage_store(xi, stg[xi], k_tile0, v_tile0);
+      } else {
+#pragma unroll
+        for (int xi = 0; xi < kPer; ++xi) gather_one(xi, tq, k_tile0, v_tile0, true, false);
+        wait_vm();
+      }
     }
-    wait_vm();
     if constexpr (SEL) sel_store(0);
     __syncthreads();
   }
+  // Every global load so far (Q operands, the prologue) has landed, as a wait the compiler sees:
+  // otherwise it assumes them in flight at the loop head and waits for all loads (the staged
+  // gathers included) before the first operand of every step.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   const int n_steps = n_chunks + (n_chunks > 0);
   for (int n = 0; n < n_steps; n += 2) {
     step(std::integral_constant<int, 0>(), n);
