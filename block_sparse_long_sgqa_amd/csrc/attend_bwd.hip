@@ -36,7 +36,6 @@ constexpr int kDqWaves = 8;                 // dq workgroup (two waves per SIMD,
 // dq stage: padded K tile, padded V tile, swizzled K tile.
 constexpr int kDqKs = 2 * kKTileBytes;                          // swizzled K tile offset
 constexpr int kDqStageBytes = kDqKs + kVTileBytes;              // one stage
-constexpr int kDqInsts = 2 * kKTileInsts + kVTileInsts;         // 17 + 17 + 16 wave-wide loads
 
 // Two 4x16 transposing reads at `a0` and 8 rows below: the A operand of a (d x rows) product whose
 // B operand is packed from score registers (see the forward's O^T += V^T P^T).
@@ -183,43 +182,47 @@ __global__ __launch_bounds__(WAVES * 64) void k_bwd_dq(const uint16_t* __restric
     const int tk = ((int)list[kp >> block_shift] << block_shift) + (kp & (block - 1));
     return tk < n_tokens ? tk : -1;
   };
-  // Gather of one chunk into stage sb: padded K (instructions 0..16), padded V (17..33), swizzled K
-  // (34..49); instruction ii goes to wave ii % WAVES. The rows' tokens come from the chunk's token
-  // table (written two chunks ahead by the first wave), all read before the first gather.
-  constexpr int kPer = (kDqInsts + WAVES - 1) / WAVES;
-  auto slot_of = [&](int inst, int& rw, int& piece) __attribute__((always_inline)) {
-    const int tile_id = inst < kKTileInsts ? 0 : (inst < 2 * kKTileInsts ? 1 : 2);
-    const int sl = (inst - tile_id * kKTileInsts) * 64 + l;
-    if (tile_id < 2) {
-      rw = sl / kKSlotsPerRow;
-      piece = sl - rw * kKSlotsPerRow;
-      if (piece == 16) piece = 0;  // padding slot: any in-bounds data
-    } else {
-      rw = sl >> 4;
-      piece = v_phys(rw, sl & 15);
-    }
-  };
-  auto issue = [&](int n, uint8_t* sb) __attribute__((always_inline)) {
+  // Gather of one chunk into a stage, staged through registers: 16 K and 16 V wave-wide 16-byte
+  // loads (1 KiB each), four per wave (load xi of a wave is load wave + xi * WAVES; 0 .. 15 are K).
+  // Load i, lane l holds row (64 i + l) / 16, piece (64 i + l) % 16 of its tensor; a K slice is
+  // stored twice, into the padded K tile and into the swizzled one (physical piece v_phys(row, p)
+  // holds logical piece p), a V slice into the padded V tile. The loads fly while the current chunk
+  // is computed (LDS-direct loads would hold up the issuing wave and keep the compiler from
+  // overlapping the operand reads). The rows' tokens come from the chunk's token table (written two
+  // chunks ahead by the first wave), all read before the first load.
+  constexpr int kDqLoads = 2 * kKeys * kD * 2 / 1024;  // 32
+  constexpr int kPer = kDqLoads / WAVES;
+  constexpr int kKPer = kPer / 2;
+  static_assert(kDqLoads % WAVES == 0 && kPer % 2 == 0, "K and V loads split evenly over the waves");
+  u32x4 stg[kPer];
+  auto load_chunk = [&](int n) __attribute__((always_inline)) {
     const int* tab = toks + (n & 3) * kKeys;
     int tkn[kPer];
 #pragma unroll
     for (int xi = 0; xi < kPer; ++xi) {
-      int rw, piece;
-      slot_of(wave + xi * WAVES, rw, piece);
-      const int t = tab[rw & (kKeys - 1)];
+      const int ii = wave + xi * WAVES;
+      const int sl = (xi < kKPer ? ii : ii - kDqLoads / 2) * 64 + l;
+      const int t = tab[sl >> 4];
       tkn[xi] = t == 0x7FFFFFFF ? 0 : t;
     }
 #pragma unroll
     for (int xi = 0; xi < kPer; ++xi) {
-      const int inst = wave + xi * WAVES;
-      if (inst < kDqInsts) {
-        int rw, piece;
-        slot_of(inst, rw, piece);
-        const int tile_id = inst < kKTileInsts ? 0 : (inst < 2 * kKTileInsts ? 1 : 2);
-        const int ti = inst - tile_id * kKTileInsts;
-        const uint16_t* src = (tile_id == 1 ? vbase : kbase) + (long long)tkn[xi] * kD + piece * 8;
-        uint8_t* dst = sb + (tile_id == 0 ? 0 : (tile_id == 1 ? kKTileBytes : kDqKs)) + ti * 1024;
-        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)dst, 16, 0, 0);
+      const int ii = wave + xi * WAVES;
+      const int sl = (xi < kKPer ? ii : ii - kDqLoads / 2) * 64 + l;
+      stg[xi] = *reinterpret_cast<const u32x4*>((xi < kKPer ? kbase : vbase) + (long long)tkn[xi] * kD + (sl & 15) * 8);
+    }
+  };
+  auto store_chunk = [&](uint8_t* sb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int xi = 0; xi < kPer; ++xi) {
+      const int ii = wave + xi * WAVES;
+      const int sl = (xi < kKPer ? ii : ii - kDqLoads / 2) * 64 + l;
+      const int row = sl >> 4, piece = sl & 15;
+      if (xi < kKPer) {
+        *reinterpret_cast<u32x4*>(sb + row * kKRowBytes + 16 * piece) = stg[xi];
+        *reinterpret_cast<u32x4*>(sb + kDqKs + row * 256 + 16 * v_phys(row, piece)) = stg[xi];
+      } else {
+        *reinterpret_cast<u32x4*>(sb + kKTileBytes + row * kKRowBytes + 16 * piece) = stg[xi];
       }
     }
   };
@@ -285,18 +288,23 @@ __global__ __launch_bounds__(WAVES * 64) void k_bwd_dq(const uint16_t* __restric
   // n, wait for the gather, sync. P = n % 2 picks the stages at compile time.
   auto step = [&](auto parity, int n) __attribute__((always_inline)) {
     constexpr int P = decltype(parity)::value;
-    if (n + 1 < n_chunks) issue(n + 1, P ? stage0 : stage1);
+    if (n + 1 < n_chunks) load_chunk(n + 1);
     write_tokens(n + 2);
     chunk(P ? stage1 : stage0, toks + (n & 3) * kKeys);
-    wait_vm();
+    if (n + 1 < n_chunks) store_chunk(P ? stage0 : stage1);
     __syncthreads();
   };
   write_tokens(0);
   write_tokens(1);
   __syncthreads();
-  if (n_chunks > 0) issue(0, stage0);
-  wait_vm();
+  if (n_chunks > 0) {
+    load_chunk(0);
+    store_chunk(stage0);
+  }
   __syncthreads();
+  // Every global load so far (Q, dO, lse, delta, chunk 0) has landed, as a wait the compiler sees:
+  // otherwise it takes them as in flight inside the loop and waits for the staged loads as well.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   for (int n = 0; n < n_chunks; n += 2) {
     step(std::integral_constant<int, 0>(), n);
     if (n + 1 < n_chunks) step(std::integral_constant<int, 1>(), n + 1);
