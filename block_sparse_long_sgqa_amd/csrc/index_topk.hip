@@ -51,7 +51,6 @@ constexpr int kKRowBytes = 144;                    // 128 B block key + 16 B pad
 constexpr int kKSlots = kKRowBytes / 16;           // 9 slots of 16 B per row, the last is padding
 constexpr int kStageBytes = kChunk * kKRowBytes;   // 18432 B
 constexpr int kStageInsts = kChunk * kKSlots / 64;  // 18 wave-wide 16-byte loads per stage
-constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kListPad = 16;                       // words between row regions (spreads LDS banks)
 constexpr int kSideCap = 192;                      // bucket members listed per row in the emit pass
 
