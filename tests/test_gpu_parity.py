@@ -264,6 +264,26 @@ def test_prefill_end_to_end(sg, name):
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
 
 
+@pytest.mark.parametrize("n", [8, 9, 63, 65, 130])
+def test_prefill_short_sequences(sg, n):
+    # Sequences of one block up to a few chunks: single-chunk unions, ragged last blocks and tiles,
+    # queries with no candidate block at all (i < B).
+    wl = datagen.PREFILL.replace(name=f"short_{n}", n_tokens=n, n_q_heads=16, n_kv_heads=2, block=8,
+                                 topk_tokens=64, union_tile=16)
+    p = params_of(wl)
+    x = datagen.prefill_inputs(wl)
+    ch = OracleChain(x, p)
+    umask, _ = oracle.union(ch.topk(), p.n_tokens, p.block, p.union_tile)
+    want = oracle.attend(bits(x["q"]), bits(x["k"]), bits(x["v"]), umask, p.block, p.union_tile)
+    say(f"prefill short N={n}")
+    xd = to_dev(x)
+    out = torch.empty((p.n_tokens, p.n_q_heads, p.head_dim), dtype=torch.bfloat16, device="cuda")
+    ws = sg.workspace(p, sg.SGQA_OP_PREFILL)
+    sg.sgqa_prefill(p, xd["q"], xd["k"], xd["v"], xd["qi"], xd["w"], xd["ki"], out, ws)
+    torch.cuda.synchronize()
+    assert_close_attention(out, want, f"prefill short N={n}")
+
+
 def test_prefill_dense_when_k_covers_context(sg):
     # k >= N: selection is everything, the path is dense causal GQA attention (oracle pinned to SDPA).
     wl = datagen.PREFILL.replace(name="dense_e2e", n_tokens=1024 + 8, n_q_heads=16, n_kv_heads=2,
