@@ -264,10 +264,11 @@ def test_prefill_end_to_end(sg, name):
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
 
 
-@pytest.mark.parametrize("n", [8, 9, 63, 65, 130])
+@pytest.mark.parametrize("n", [1, 5, 8, 9, 63, 65, 130])
 def test_prefill_short_sequences(sg, n):
-    # Sequences of one block up to a few chunks: single-chunk unions, ragged last blocks and tiles,
-    # queries with no candidate block at all (i < B).
+    # Sequences shorter than one block up to a few chunks: no complete block at all (N < B, nothing
+    # to compress or select), single-chunk unions, ragged last blocks and tiles, queries with no
+    # candidate block (i < B).
     wl = datagen.PREFILL.replace(name=f"short_{n}", n_tokens=n, n_q_heads=16, n_kv_heads=2, block=8,
                                  topk_tokens=64, union_tile=16)
     p = params_of(wl)
