@@ -37,6 +37,11 @@ BWD = {
                                      union_tile=1),
     "b64_r4": datagen.PREFILL.replace(name="bwd_b64", n_tokens=1100 + 3, n_q_heads=16, n_kv_heads=4, block=64,
                                       topk_tokens=256, union_tile=128),
+    # Shorter than one block, and one key past a chunk.
+    "short_5": datagen.PREFILL.replace(name="bwd_short5", n_tokens=5, n_q_heads=16, n_kv_heads=2,
+                                       topk_tokens=64, union_tile=16),
+    "short_65": datagen.PREFILL.replace(name="bwd_short65", n_tokens=65, n_q_heads=16, n_kv_heads=2,
+                                        topk_tokens=64, union_tile=16),
 }
 
 
