@@ -283,6 +283,13 @@ def test_prefill_short_sequences(sg, n):
     sg.sgqa_prefill(p, xd["q"], xd["k"], xd["v"], xd["qi"], xd["w"], xd["ki"], out, ws)
     torch.cuda.synchronize()
     assert_close_attention(out, want, f"prefill short N={n}")
+    # The masked-union reading of the same inputs: each row its own selection and own block.
+    want_sel = oracle.attend_sel(bits(x["q"]), bits(x["k"]), bits(x["v"]), ch.topk(), p.block)
+    out_m = torch.empty_like(out)
+    sg.sgqa_prefill_masked(p, xd["q"], xd["k"], xd["v"], xd["qi"], xd["w"], xd["ki"], out_m,
+                           sg.workspace(p, sg.SGQA_OP_PREFILL_MASKED))
+    torch.cuda.synchronize()
+    assert_close_attention(out_m, want_sel, f"prefill_masked short N={n}")
 
 
 def test_prefill_dense_when_k_covers_context(sg):
