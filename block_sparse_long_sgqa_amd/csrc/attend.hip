@@ -26,12 +26,6 @@
 //  * Launch order is XCD-aware: consecutive workgroup ids go to different XCDs, so the
 //    (tile, group) pairs are dealt round-robin over the 8 XCDs and all parts of one pair (same K/V
 //    stream) land on the same XCD's L2; with G = 8 every XCD serves one KV group.
-#ifndef SGQA_ATTN_WAVES
-#define SGQA_ATTN_WAVES 8
-#endif
-#ifndef SGQA_ATTN_QT
-#define SGQA_ATTN_QT 1
-#endif
 
 #include "attn_common.hpp"
 
@@ -457,8 +451,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
 }
 
 namespace {
-constexpr int kPrefillWaves = SGQA_ATTN_WAVES;
-constexpr int kPrefillQT = SGQA_ATTN_QT;
+constexpr int kPrefillWaves = 8;
+constexpr int kPrefillQT = 1;
 
 // Dynamic LDS of the prefill kernel: the block list.
 size_t attend_lds_bytes(int list_cap) { return (size_t)list_cap * 2; }
@@ -491,8 +485,6 @@ hipError_t launch_attend_impl(const uint16_t* q, const uint16_t* k, const uint16
   const long long grid = (long long)((n_pairs + 7) / 8) * 8 * parts;
   const float scale_log2 = scale * 1.4426950408889634f;
   auto kern = k_attend<kPrefillWaves, kPrefillQT, SEL_LOADS>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kPrefillWaves * 64), lds, stream, q, k, v, umask, out, n_tokens,
                      n_q_heads, n_groups, block, __builtin_ctz(block), tile, scale_log2, n_words, parts, n_pairs,
                      selbits, lse);
@@ -956,10 +948,7 @@ __global__ __launch_bounds__(256) void k_decode_attend_f8(const uint16_t* __rest
 
 // Chunks of FP8 codes in flight per wave (register sets of 32 VGPRs each). One set already keeps
 // the gather at the rate of a bare gather loop: a second one measured no faster.
-#ifndef SGQA_F8_DEPTH
-#define SGQA_F8_DEPTH 1
-#endif
-constexpr int kF8Depth = SGQA_F8_DEPTH;
+constexpr int kF8Depth = 1;
 
 size_t decode_attend_f8_lds(int kb) { return (size_t)4 * kDecVStage + (size_t)2 * (kb + 1) * 4 + 4 * 32 * 2 * 4; }
 
@@ -969,10 +958,6 @@ hipError_t launch_decode_attend_f8(const uint16_t* q, const uint8_t* kc, const u
                                    const PageTable& pages, hipStream_t stream) {
   const size_t lds = decode_attend_f8_lds(kb);
   if (lds > (size_t)max_lds_per_block()) return hipErrorInvalidValue;
-  const void* fn = pages.table ? (const void*)k_decode_attend_f8<true, kF8Depth>
-                                : (const void*)k_decode_attend_f8<false, kF8Depth>;
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
   const float scale_log2 = scale * 1.4426950408889634f;
   const dim3 grid((unsigned)(n_seqs * n_groups));
   if (pages.table)
@@ -995,9 +980,6 @@ hipError_t launch_decode_attend(const uint16_t* q, const uint16_t* kc, const uin
                                 float scale, const int32_t* lens, const PageTable& pages, hipStream_t stream) {
   const size_t lds = decode_attend_lds(kb);
   if (lds > (size_t)max_lds_per_block()) return hipErrorInvalidValue;
-  const void* fn = pages.table ? (const void*)k_decode_attend<true> : (const void*)k_decode_attend<false>;
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
   const float scale_log2 = scale * 1.4426950408889634f;
   const dim3 grid((unsigned)(n_seqs * n_groups));
   if (pages.table)
@@ -1008,6 +990,22 @@ hipError_t launch_decode_attend(const uint16_t* q, const uint16_t* kc, const uin
     hipLaunchKernelGGL(k_decode_attend<false>, grid, dim3(256), lds, stream, q, kc, vc, sel, out, ctx, n_q_heads,
                        n_groups, block, __builtin_ctz(block), kb, scale_log2, lens, nullptr, 0, 0, 0);
   return hipGetLastError();
+}
+
+hipError_t prepare_attend_kernels(int lds_max) {
+  const void* fns[] = {(const void*)k_attend<kPrefillWaves, kPrefillQT, 0>,
+                       (const void*)k_attend<kPrefillWaves, kPrefillQT, 1>,
+                       (const void*)k_attend<kPrefillWaves, kPrefillQT, 2>,
+                       (const void*)k_attend<kPrefillWaves, kPrefillQT, 4>,
+                       (const void*)k_decode_attend<true>,
+                       (const void*)k_decode_attend<false>,
+                       (const void*)k_decode_attend_f8<true, kF8Depth>,
+                       (const void*)k_decode_attend_f8<false, kF8Depth>};
+  for (const void* fn : fns) {
+    const hipError_t e = allow_full_lds(fn, lds_max);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace sgqa

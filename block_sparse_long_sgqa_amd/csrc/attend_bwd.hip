@@ -21,17 +21,13 @@
 //    gathered into the wave's swizzled LDS tiles (double-buffered, one group ahead), S = Q K^T and
 //    dP = dO V^T give P and dS with the keys in the lane columns, and dV^T += dO^T P,
 //    dK^T += Q^T dS take dO^T and Q^T transposed from LDS.
-#ifndef SGQA_BWD_WAVES
-#define SGQA_BWD_WAVES 4
-#endif
-
 #include "attn_common.hpp"
 
 namespace sgqa {
 
 namespace {
 
-constexpr int kBwdWaves = SGQA_BWD_WAVES;  // dk/dv workgroup (one wave per SIMD)
+constexpr int kBwdWaves = 4;  // dk/dv workgroup (one wave per SIMD)
 constexpr int kDqWaves = 8;                 // dq workgroup (two waves per SIMD, as the forward)
 // dq stage: padded K tile, padded V tile, swizzled K tile.
 constexpr int kDqKs = 2 * kKTileBytes;                          // swizzled K tile offset
@@ -699,8 +695,6 @@ hipError_t launch_attend_bwd(const uint16_t* q, const uint16_t* k, const uint16_
     const size_t lds = attend_bwd_dq_list_bytes(n_tokens, block);
     const long long grid = (long long)((n_pairs + 7) / 8) * 8 * parts;
     auto kern = k_bwd_dq<kDqWaves>;
-    e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kDqWaves * 64), lds, stream, q, k, v, umask, lse, delta,
                        dout, dq, n_tokens, n_q_heads, n_groups, block, __builtin_ctz(block), tile, scale,
                        scale_log2, n_words, parts, n_pairs);
@@ -716,5 +710,7 @@ hipError_t launch_attend_bwd(const uint16_t* q, const uint16_t* k, const uint16_
   }
   return e;
 }
+
+hipError_t prepare_attend_bwd_kernels(int lds_max) { return allow_full_lds((const void*)k_bwd_dq<kDqWaves>, lds_max); }
 
 }  // namespace sgqa

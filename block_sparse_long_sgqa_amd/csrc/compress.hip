@@ -3,7 +3,9 @@
 // "Inside Step 5 Preview", section Sparse GQA, paragraph "Reducing indexer's cost" and Figure 3:
 // the index keys of B adjacent positions are merged into one block key. Here the merge is the
 // mean, rounded once to bf16: kbar[s][b][d] = bf16_rne((sum_{j<B} ki[s][b*B+j][d]) * (1/B)),
-// summed in fp32 in ascending j (1/B is a power of two, so the scaling is exact).
+// summed in fp64 in ascending j (1/B is a power of two, so the scaling is exact). The fp64 sum of
+// up to 64 bf16 values is exact unless their exponents span more than ~40 binades, so the block
+// key is the exact mean rounded once.
 //
 // HBM-bound: every thread owns 8 consecutive dims (16 B) of one block and streams the B rows of
 // that block; 8 lanes cover one 128-byte row, so each wave reads 8 blocks' rows with full 128-byte
@@ -19,7 +21,7 @@ __global__ __launch_bounds__(256) void k_compress(const uint16_t* __restrict__ k
                                                   long long n_items) {
   const int block = BLOCK > 0 ? BLOCK : dyn_block;
   const int chunks = idx_dim >> 3;  // 16-byte pieces per row
-  const float inv = 1.0f / (float)block;
+  const double inv = 1.0 / (double)block;
   for (long long item = (long long)blockIdx.x * blockDim.x + threadIdx.x; item < n_items;
        item += (long long)gridDim.x * blockDim.x) {
     const int c = (int)(item % chunks);
@@ -27,9 +29,9 @@ __global__ __launch_bounds__(256) void k_compress(const uint16_t* __restrict__ k
     const long long s = sb / n_blocks;
     const long long b = sb - s * n_blocks;
     const uint16_t* src = ki + ((s * n_tokens + b * block) * idx_dim + c * 8);
-    float acc[8];
+    double acc[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0;
     if (BLOCK > 0) {
       u32x4 rows[BLOCK > 0 ? BLOCK : 1];
 #pragma unroll
@@ -38,8 +40,8 @@ __global__ __launch_bounds__(256) void k_compress(const uint16_t* __restrict__ k
       for (int j = 0; j < BLOCK; ++j) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          acc[2 * e] += bf16_bits_to_f32(rows[j][e] & 0xFFFFu);
-          acc[2 * e + 1] += bf16_bits_to_f32(rows[j][e] >> 16);
+          acc[2 * e] += (double)bf16_bits_to_f32(rows[j][e] & 0xFFFFu);
+          acc[2 * e + 1] += (double)bf16_bits_to_f32(rows[j][e] >> 16);
         }
       }
     } else {
@@ -47,14 +49,15 @@ __global__ __launch_bounds__(256) void k_compress(const uint16_t* __restrict__ k
         u32x4 r = *reinterpret_cast<const u32x4*>(src + (long long)j * idx_dim);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          acc[2 * e] += bf16_bits_to_f32(r[e] & 0xFFFFu);
-          acc[2 * e + 1] += bf16_bits_to_f32(r[e] >> 16);
+          acc[2 * e] += (double)bf16_bits_to_f32(r[e] & 0xFFFFu);
+          acc[2 * e + 1] += (double)bf16_bits_to_f32(r[e] >> 16);
         }
       }
     }
     u32x4 o;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+    for (int e = 0; e < 4; ++e)
+      o[e] = f64_to_bf16_bits(acc[2 * e] * inv) | (f64_to_bf16_bits(acc[2 * e + 1] * inv) << 16);
     *reinterpret_cast<u32x4*>(kbar + (sb * idx_dim + c * 8)) = o;
   }
 }
@@ -90,7 +93,7 @@ hipError_t launch_compress(const uint16_t* ki, uint16_t* kbar, int n_seqs, int n
 // sequence). K/V rows go to the dense cache [S][G][cap][D] or to the pool page table[s][j / page]
 // ([n_pages][G][page][D]; a page entry outside [0, n_pages) skips the K/V write); the index key goes to
 // idx_cache [S][cap][d_I]; when j closes a block (j % B == B - 1) the block key of block j / B is
-// formed with the arithmetic of k_compress (fp32 sum of the B keys in ascending position, times
+// formed with the arithmetic of k_compress (fp64 sum of the B keys in ascending position, times
 // 1/B, one rounding to bf16), the new key taken from registers rather than re-read.
 __global__ __launch_bounds__(256) void k_append(const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
                                                 const uint16_t* __restrict__ idx_new, const int32_t* __restrict__ pos,
@@ -125,26 +128,27 @@ __global__ __launch_bounds__(256) void k_append(const uint16_t* __restrict__ k_n
     const u32x4 nv = *reinterpret_cast<const u32x4*>(idx_new + (long long)s * idx_dim + t * 8);
     *reinterpret_cast<u32x4*>(idx_cache + ((long long)s * cap + j) * idx_dim + t * 8) = nv;
     if (j % block == block - 1) {
-      float acc[8];
+      double acc[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+      for (int e = 0; e < 8; ++e) acc[e] = 0.0;
       for (int r = j - block + 1; r < j; ++r) {
         const u32x4 rv = *reinterpret_cast<const u32x4*>(idx_cache + ((long long)s * cap + r) * idx_dim + t * 8);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          acc[2 * e] += bf16_bits_to_f32(rv[e] & 0xFFFFu);
-          acc[2 * e + 1] += bf16_bits_to_f32(rv[e] >> 16);
+          acc[2 * e] += (double)bf16_bits_to_f32(rv[e] & 0xFFFFu);
+          acc[2 * e + 1] += (double)bf16_bits_to_f32(rv[e] >> 16);
         }
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        acc[2 * e] += bf16_bits_to_f32(nv[e] & 0xFFFFu);
-        acc[2 * e + 1] += bf16_bits_to_f32(nv[e] >> 16);
+        acc[2 * e] += (double)bf16_bits_to_f32(nv[e] & 0xFFFFu);
+        acc[2 * e + 1] += (double)bf16_bits_to_f32(nv[e] >> 16);
       }
-      const float inv = 1.0f / (float)block;
+      const double inv = 1.0 / (double)block;
       u32x4 o;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+      for (int e = 0; e < 4; ++e)
+        o[e] = f64_to_bf16_bits(acc[2 * e] * inv) | (f64_to_bf16_bits(acc[2 * e + 1] * inv) << 16);
       const long long nb = cap / block;
       *reinterpret_cast<u32x4*>(kbar + ((long long)s * nb + j / block) * idx_dim + t * 8) = o;
     }

@@ -40,13 +40,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kIdxHeads = 4;
 constexpr int kIdxDim = 64;
-#ifndef SGQA_TOPK_CHUNK
-#define SGQA_TOPK_CHUNK 128
-#endif
-#ifndef SGQA_TOPK_WGS_PER_CU
-#define SGQA_TOPK_WGS_PER_CU 1
-#endif
-constexpr int kChunk = SGQA_TOPK_CHUNK;            // candidate blocks per stage
+constexpr int kChunk = 128;                        // candidate blocks per stage
 constexpr int kKRowBytes = 144;                    // 128 B block key + 16 B pad
 constexpr int kKSlots = kKRowBytes / 16;           // 9 slots of 16 B per row, the last is padding
 constexpr int kStageBytes = kChunk * kKRowBytes;   // 18432 B
@@ -677,12 +671,7 @@ hipError_t launch_select(const uint16_t* qi, const float* w, const uint16_t* kba
                          int n_tokens, int n_groups, int block, int kb, int tile, hipStream_t stream) {
   const long long n_rows = (long long)n_tokens * n_groups;
   if (n_rows == 0) return hipSuccess;
-  const size_t budget = (size_t)max_lds_per_block() / SGQA_TOPK_WGS_PER_CU;
-#ifdef SGQA_TOPK_WAVES
-  const int waves = select_lds_bytes(SGQA_TOPK_WAVES, kb) + 256 <= budget ? SGQA_TOPK_WAVES : 0;
-#else
-  const int waves = prefill_waves(kb, budget);
-#endif
+  const int waves = prefill_waves(kb, (size_t)max_lds_per_block());
   if (waves == 0) return hipErrorInvalidValue;
   const size_t lds = select_lds_bytes(waves, kb);
   const long long grid = (long long)n_groups * ((n_tokens + waves * 4 - 1) / (waves * 4));
@@ -690,9 +679,6 @@ hipError_t launch_select(const uint16_t* qi, const float* w, const uint16_t* kba
   const int n_words = ((n_tokens + block - 1) / block + 31) / 32;
 #define SGQA_TOPK_CASE(WV)                                                                                       \
   if (waves == WV) {                                                                                             \
-    hipError_t e = hipFuncSetAttribute((const void*)k_select<WV, 8, UNION>,                                     \
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                    \
-    if (e != hipSuccess) return e;                                                                               \
     hipLaunchKernelGGL((k_select<WV, 8, UNION>), dim3((unsigned)grid), dim3(WV * 64), lds, stream, qi, w, kbar,  \
                        topk, n_tokens, n_groups, block, kb, umask, tile, n_tiles, n_words);                      \
     return hipGetLastError();                                                                                    \
@@ -706,6 +692,18 @@ hipError_t launch_select(const uint16_t* qi, const float* w, const uint16_t* kba
 }
 
 }  // namespace
+
+hipError_t prepare_index_topk_kernels(int lds_max) {
+  const void* fns[] = {(const void*)k_select<8, 8, false>, (const void*)k_select<4, 8, false>,
+                       (const void*)k_select<2, 8, false>, (const void*)k_select<1, 8, false>,
+                       (const void*)k_select<8, 8, true>,  (const void*)k_select<4, 8, true>,
+                       (const void*)k_select<2, 8, true>,  (const void*)k_select<1, 8, true>};
+  for (const void* fn : fns) {
+    const hipError_t e = allow_full_lds(fn, lds_max);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
 
 hipError_t launch_index_topk(const uint16_t* qi, const float* w, const uint16_t* kbar, int32_t* topk, int n_tokens,
                              int n_groups, int block, int kb, hipStream_t stream) {

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/sgqa.h"
 #include "sgqa_internal.hpp"
 
@@ -12,8 +14,16 @@ namespace sgqa {
 namespace {
 
 constexpr int kMaxDevices = 64;
-int g_lds_max[kMaxDevices];  // 0 = not queried yet
-int g_is_gfx950[kMaxDevices];  // 0 = unknown, 1 = yes, -1 = no
+
+// Facts about one device, filled once (std::call_once) on the first call that runs with it current:
+// whether it is a gfx950, its LDS limit per workgroup, and the dynamic-LDS attribute of every
+// kernel (set here, before any launch, so that a call never fails between two of its launches).
+struct DeviceState {
+  std::once_flag once;
+  int status = SGQA_ERR_DEVICE;
+  int lds_max = 65536;
+};
+DeviceState g_device[kMaxDevices];
 
 int current_device() {
   int dev = -1;
@@ -21,31 +31,51 @@ int current_device() {
   return (dev >= 0 && dev < kMaxDevices) ? dev : -1;
 }
 
+DeviceState* device_state() {
+  const int dev = current_device();
+  if (dev < 0) return nullptr;
+  DeviceState& d = g_device[dev];
+  std::call_once(d.once, [&d, dev] {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return;
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return;
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0) v = 65536;
+    d.lds_max = v;
+    d.status = prepare_kernels(v) == hipSuccess ? SGQA_OK : SGQA_ERR_HIP;
+  });
+  return &d;
+}
+
+// SGQA_OK when the current device is a gfx950 whose kernels are set up, else the status to return.
+int device_ready() {
+  const DeviceState* d = device_state();
+  return d ? d->status : SGQA_ERR_DEVICE;
+}
+
 }  // namespace
 
 int max_lds_per_block() {
-  const int dev = current_device();
-  if (dev < 0) return 65536;
-  if (g_lds_max[dev] == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0) v = 65536;
-    g_lds_max[dev] = v;
-  }
-  return g_lds_max[dev];
+  const DeviceState* d = device_state();
+  return d ? d->lds_max : 65536;
+}
+
+hipError_t allow_full_lds(const void* fn, int lds_max) {
+  hipFuncAttributes a;
+  hipError_t e = hipFuncGetAttributes(&a, fn);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds_max - (int)a.sharedSizeBytes);
+}
+
+hipError_t prepare_kernels(int lds_max) {
+  hipError_t e = prepare_index_topk_kernels(lds_max);
+  if (e == hipSuccess) e = prepare_union_kernels(lds_max);
+  if (e == hipSuccess) e = prepare_attend_kernels(lds_max);
+  if (e == hipSuccess) e = prepare_attend_bwd_kernels(lds_max);
+  return e;
 }
 
 namespace {
-
-bool device_ok() {
-  const int dev = current_device();
-  if (dev < 0) return false;
-  if (g_is_gfx950[dev] == 0) {
-    hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return false;
-    g_is_gfx950[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
-  }
-  return g_is_gfx950[dev] == 1;
-}
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0u; }
 
@@ -248,7 +278,7 @@ int sgqa_compress(const sgqa_params* p, const sgqa_bf16* idx_k, sgqa_bf16* blk_k
   if (st) return st;
   if (!idx_k || (!blk_k && p->n_tokens >= p->block)) return SGQA_ERR_NULL;  // N < B: nothing to write
   if (!aligned16(idx_k) || !aligned16(blk_k)) return SGQA_ERR_ALIGN;
-  if (!device_ok()) return SGQA_ERR_DEVICE;
+  if ((st = device_ready()) != SGQA_OK) return st;
   return status_of(launch_compress(idx_k, blk_k, p->n_seqs, p->n_tokens, p->idx_dim, p->block, (hipStream_t)stream));
 }
 
@@ -260,7 +290,7 @@ int sgqa_index_topk(const sgqa_params* p, const sgqa_bf16* idx_q, const float* i
   if (st) return st;
   if (!idx_q || !idx_w || !topk || (!blk_k && p->n_tokens >= p->block)) return SGQA_ERR_NULL;
   if (!aligned16(idx_q) || !aligned16(idx_w) || !aligned16(blk_k) || !aligned16(topk)) return SGQA_ERR_ALIGN;
-  if (!device_ok()) return SGQA_ERR_DEVICE;
+  if ((st = device_ready()) != SGQA_OK) return st;
   return status_of(launch_index_topk(idx_q, idx_w, blk_k, topk, p->n_tokens, p->n_kv_heads, p->block, kb_of(p),
                                      (hipStream_t)stream));
 }
@@ -270,7 +300,7 @@ int sgqa_union(const sgqa_params* p, const int32_t* topk, uint32_t* umask, int32
   if (st) return st;
   if (!topk || !umask || !ucount) return SGQA_ERR_NULL;
   if (!aligned16(topk) || !aligned16(umask) || !aligned16(ucount)) return SGQA_ERR_ALIGN;
-  if (!device_ok()) return SGQA_ERR_DEVICE;
+  if ((st = device_ready()) != SGQA_OK) return st;
   return status_of(launch_union(topk, umask, ucount, p->n_tokens, p->n_kv_heads, p->block, kb_of(p), p->union_tile,
                                 (hipStream_t)stream));
 }
@@ -284,7 +314,7 @@ int sgqa_index_union(const sgqa_params* p, const sgqa_bf16* idx_q, const float* 
   if (!idx_q || !idx_w || !umask || !ucount || (!blk_k && p->n_tokens >= p->block)) return SGQA_ERR_NULL;
   if (!aligned16(idx_q) || !aligned16(idx_w) || !aligned16(blk_k) || !aligned16(umask) || !aligned16(ucount))
     return SGQA_ERR_ALIGN;
-  if (!device_ok()) return SGQA_ERR_DEVICE;
+  if ((st = device_ready()) != SGQA_OK) return st;
   return status_of(launch_index_union(idx_q, idx_w, blk_k, umask, ucount, p->n_tokens, p->n_kv_heads, p->block,
                                       kb_of(p), p->union_tile, (hipStream_t)stream));
 }
@@ -299,7 +329,7 @@ int sgqa_attend(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k, co
   if (!q || !k || !v || !umask || !ucount || !out) return SGQA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(umask) || !aligned16(ucount) || !aligned16(out))
     return SGQA_ERR_ALIGN;
-  if (!device_ok()) return SGQA_ERR_DEVICE;
+  if ((st = device_ready()) != SGQA_OK) return st;
   return status_of(launch_attend(q, k, v, umask, ucount, out, p->n_tokens, p->n_q_heads, p->n_kv_heads, p->block,
                                  p->union_tile, scale_of(p), (hipStream_t)stream));
 }
@@ -315,7 +345,7 @@ int sgqa_attend_fwd(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(umask) || !aligned16(ucount) || !aligned16(out) ||
       !aligned16(lse))
     return SGQA_ERR_ALIGN;
-  if (!device_ok()) return SGQA_ERR_DEVICE;
+  if ((st = device_ready()) != SGQA_OK) return st;
   return status_of(launch_attend(q, k, v, umask, ucount, out, p->n_tokens, p->n_q_heads, p->n_kv_heads, p->block,
                                  p->union_tile, scale_of(p), (hipStream_t)stream, lse));
 }
@@ -331,7 +361,7 @@ int sgqa_attend_bwd(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k
       !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(ws))
     return SGQA_ERR_ALIGN;
   if (!ws || ws_bytes < round_up((size_t)p->n_tokens * p->n_q_heads * 4)) return SGQA_ERR_WORKSPACE;
-  if (!device_ok()) return SGQA_ERR_DEVICE;
+  if ((st = device_ready()) != SGQA_OK) return st;
   return status_of(launch_attend_bwd(q, k, v, umask, out, lse, dout, dq, dk, dv, static_cast<float*>(ws),
                                      p->n_tokens, p->n_q_heads, p->n_kv_heads, p->block, p->union_tile, scale_of(p),
                                      (hipStream_t)stream));
@@ -347,7 +377,7 @@ int sgqa_attend_masked(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16
       !aligned16(ucount) || !aligned16(out) || !aligned16(ws))
     return SGQA_ERR_ALIGN;
   if (!ws || ws_bytes < selbits_bytes(p)) return SGQA_ERR_WORKSPACE;
-  if (!device_ok()) return SGQA_ERR_DEVICE;
+  if ((st = device_ready()) != SGQA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   uint32_t* selbits = static_cast<uint32_t*>(ws);
   hipError_t e = launch_sel_bitmap(topk, selbits, p->n_tokens, p->n_kv_heads, p->block, kb_of(p), s);
@@ -368,7 +398,7 @@ int sgqa_prefill_masked(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf1
     return SGQA_ERR_ALIGN;
   const PrefillWs l = prefill_layout(p, ws, true);
   if (!ws || ws_bytes < l.bytes) return SGQA_ERR_WORKSPACE;
-  if (!device_ok()) return SGQA_ERR_DEVICE;
+  if ((st = device_ready()) != SGQA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = launch_compress(idx_k, l.kbar, 1, p->n_tokens, p->idx_dim, p->block, s);
   if (e == hipSuccess)
@@ -393,7 +423,7 @@ int sgqa_prefill(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k, c
     return SGQA_ERR_ALIGN;
   const PrefillWs l = prefill_layout(p, ws, false);
   if (!ws || ws_bytes < l.bytes) return SGQA_ERR_WORKSPACE;
-  if (!device_ok()) return SGQA_ERR_DEVICE;
+  if ((st = device_ready()) != SGQA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = launch_compress(idx_k, l.kbar, 1, p->n_tokens, p->idx_dim, p->block, s);
   if (e == hipSuccess)
@@ -445,7 +475,7 @@ int decode_impl(const sgqa_params* p, const sgqa_bf16* q, const void* k_cache, c
   if (st) return st;
   const DecodeWs l = decode_layout(p, ws);
   if (!ws || ws_bytes < l.bytes) return SGQA_ERR_WORKSPACE;
-  if (!device_ok()) return SGQA_ERR_DEVICE;
+  if ((st = device_ready()) != SGQA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   const int kb = kb_of(p);
   hipError_t e = launch_decode_select(idx_q, idx_w, blk_k, l.sel, topk_out, l.select_ws, p->n_seqs, p->n_tokens,
@@ -503,7 +533,7 @@ int sgqa_append(const sgqa_params* p, const sgqa_bf16* k_new, const sgqa_bf16* v
   PageTable pt;
   st = check_pages(p, pages, &pt);
   if (st) return st;
-  if (!device_ok()) return SGQA_ERR_DEVICE;
+  if ((st = device_ready()) != SGQA_OK) return st;
   return status_of(launch_append(k_new, v_new, idx_k_new, positions, k_cache, v_cache, pt, idx_k_cache, blk_k,
                                  p->n_seqs, p->n_tokens, p->n_kv_heads, p->idx_dim, p->block, (hipStream_t)stream));
 }

@@ -44,6 +44,30 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
+// fp64 -> bf16 bits, rounded once to nearest even, from the bit pattern of x: the 52-bit fraction
+// is cut to 7 bits with round-half-even on the 45 dropped bits (a carry moves into the exponent);
+// values below the smallest normal bf16 (2^-126) are multiples of 2^-133, rounded as the integer
+// rint(|x| * 2^133), whose bits are the subnormal encoding (128 gives the smallest normal). Results
+// past the largest finite bf16 become infinity; NaN gives the quiet NaN 0x7FC0.
+__device__ __forceinline__ uint32_t f64_to_bf16_bits(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const uint32_t sign = (uint32_t)(u >> 48) & 0x8000u;
+  const uint64_t a = u & 0x7FFFFFFFFFFFFFFFull;
+  const int dexp = (int)(a >> 52);
+  if (dexp == 0x7FF) return (a << 12) != 0 ? 0x7FC0u : (sign | 0x7F80u);
+  if (dexp < 1023 - 126) {  // below 2^-126 (zero and double subnormals included)
+    const double n = rint(ldexp(__longlong_as_double((long long)a), 133));
+    return sign | (uint32_t)n;
+  }
+  uint64_t q = a >> 45;  // sign-free exponent and the top 7 fraction bits
+  const uint64_t rem = a & ((1ull << 45) - 1);
+  const uint64_t half = 1ull << 44;
+  if (rem > half || (rem == half && (q & 1u))) ++q;
+  const int fexp = (int)(q >> 7) - 1023 + 127;
+  if (fexp >= 255) return sign | 0x7F80u;
+  return sign | ((uint32_t)fexp << 7) | (uint32_t)(q & 0x7Fu);
+}
+
 // Order-preserving unsigned key of an fp32 score: a larger score gives a larger key; -0 and +0 map
 // to the same key. (Non-negative floats get the top bit set; negative floats are bit-inverted.)
 __device__ __forceinline__ uint32_t score_key(float s) {

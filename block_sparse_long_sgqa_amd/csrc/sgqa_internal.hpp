@@ -101,4 +101,13 @@ constexpr size_t kGfx950LdsBytes = 160 * 1024;
 // Largest dynamic LDS allocation one workgroup may use on the current device (bytes).
 int max_lds_per_block();
 
+// Once per device, before any launch: let every kernel that takes dynamic LDS use all that is left
+// beside its static LDS (lds_max = the device's limit per workgroup). One function per kernel file.
+hipError_t allow_full_lds(const void* fn, int lds_max);
+hipError_t prepare_kernels(int lds_max);
+hipError_t prepare_index_topk_kernels(int lds_max);
+hipError_t prepare_union_kernels(int lds_max);
+hipError_t prepare_attend_kernels(int lds_max);
+hipError_t prepare_attend_bwd_kernels(int lds_max);
+
 }  // namespace sgqa

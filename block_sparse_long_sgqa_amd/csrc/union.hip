@@ -80,6 +80,8 @@ __global__ __launch_bounds__(256) void k_union(const int32_t* __restrict__ topk,
   }
 }
 
+hipError_t prepare_union_kernels(int lds_max) { return allow_full_lds((const void*)k_union, lds_max); }
+
 hipError_t launch_union(const int32_t* topk, uint32_t* umask, int32_t* ucount, int n_tokens, int n_groups, int block,
                         int kb, int tile, hipStream_t stream) {
   const int n_tiles = (n_tokens + tile - 1) / tile;
@@ -88,10 +90,6 @@ hipError_t launch_union(const int32_t* topk, uint32_t* umask, int32_t* ucount, i
   const long long grid = (long long)n_tiles * n_groups;
   if (grid == 0) return hipSuccess;
   const size_t lds = (size_t)n_words * 4;
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_union, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
   const int vec4 = (kb % 4 == 0) ? 1 : 0;
   hipLaunchKernelGGL(k_union, dim3((unsigned)grid), dim3(256), lds, stream, topk, umask, ucount, n_tokens, n_tiles,
                      block, kb, tile, n_words, vec4, nbc);

@@ -22,8 +22,11 @@ Value recipes (shared by every workload):
     before the segment, so top-k concentrates on planted spans.
 
 Determinism: every tensor has its own seed derived from (seed0, workload name, tensor name).
-A tensor drawn on the CPU is identical on every machine with this torch version. Large workloads
-are drawn on the GPU (torch's Philox generator) and copied to the host for checking.
+A tensor drawn on the CPU is identical on every machine with this torch version. The indexer inputs
+of a prefill workload (index queries, index keys, weights) are always drawn on the CPU and then
+moved, so stored digests of the oracle's full selections can be recomputed from them anywhere;
+q, k, v and the decode caches of large workloads are drawn on the GPU (torch's Philox generator)
+and copied to the host where they are checked.
 """
 from __future__ import annotations
 
@@ -72,8 +75,10 @@ LONG_PREFILL = Workload("long_prefill_128k", 131072, 64, 8, 128, 4, 64, 8, 4096,
 DECODE = Workload("decode_256k", 262144, 64, 8, 128, 4, 64, 8, 4096, 1, n_seqs=32, decode=True, qi_mode="iid")
 ABLATION_B1 = PREFILL.replace(name="ablation_32k_b1_k2048", block=1, topk_tokens=2048)
 ABLATION_B8 = PREFILL.replace(name="ablation_32k_b8_k4096")
+# rho = 1: neighbouring queries are unrelated, so the tile unions are nearly dense (stress case).
+PREFILL_IID = PREFILL.replace(name="prefill_32k_iid", rho=1.0)
 
-WORKLOADS = {w.name: w for w in (TINY, PREFILL, LONG_PREFILL, DECODE, ABLATION_B1, ABLATION_B8)}
+WORKLOADS = {w.name: w for w in (TINY, PREFILL, LONG_PREFILL, DECODE, ABLATION_B1, ABLATION_B8, PREFILL_IID)}
 
 
 def tensor_seed(seed0: int, workload: str, tensor: str) -> int:
@@ -165,19 +170,26 @@ def index_queries(wl: Workload, draw: _Draw, n_rows: int, tensor: str = "qi") ->
     return torch.where(redraw, fresh, base).to(torch.bfloat16)
 
 
+def index_inputs(wl: Workload, seed0: int = SEED0) -> dict:
+    """The indexer inputs of one prefill layer, drawn on the CPU: qi [N][G][HI][dI], ki [N][dI]
+    (bf16) and w [G][HI] (fp32)."""
+    h = _Draw(wl, "cpu", seed0)
+    return {"qi": index_queries(wl, h, wl.n_tokens), "ki": index_keys(wl, h), "w": h.weights()}
+
+
 def prefill_inputs(wl: Workload, device="cpu", seed0: int = SEED0) -> dict:
     """All inputs of one prefill layer: q [N][Hq][D], k/v [G][N][D], qi [N][G][HI][dI],
-    ki [N][dI] (bf16) and w [G][HI] (fp32)."""
+    ki [N][dI] (bf16) and w [G][HI] (fp32). The indexer inputs come from index_inputs()."""
     d = _Draw(wl, device, seed0)
     N, Hq, G, D = wl.n_tokens, wl.n_q_heads, wl.n_kv_heads, wl.head_dim
-    return {
+    x = {
         "q": d.normal_bf16("q", (N, Hq, D)),
         "k": d.normal_bf16("k", (G, N, D)),
         "v": d.normal_bf16("v", (G, N, D)),
-        "qi": index_queries(wl, d, N),
-        "ki": index_keys(wl, d),
-        "w": d.weights(),
     }
+    for name, t in index_inputs(wl, seed0).items():
+        x[name] = t.to(d.device)
+    return x
 
 
 def decode_inputs(wl: Workload, device="cpu", seed0: int = SEED0, n_seqs: Optional[int] = None) -> dict:

@@ -26,11 +26,15 @@
  *     comes only from the caller's workspace `ws` of `ws_bytes`, sized by sgqa_workspace_size.
  *   - Calls are asynchronous on `stream` (a hipStream_t; 0 = the null stream). Nothing is copied
  *     between host and device and nothing synchronizes the device.
- *   - Arguments are validated on the host BEFORE anything is enqueued: a nonzero status means no
- *     work was launched. A fault inside a kernel surfaces at the caller's next synchronization.
+ *   - Arguments are validated on the host BEFORE anything is enqueued, and every kernel's launch
+ *     attributes are set once per device before its first launch: any nonzero status other than
+ *     SGQA_ERR_HIP means no work was launched. SGQA_ERR_HIP (the runtime refused a launch) may
+ *     leave the earlier kernels of a multi-kernel call (prefill, decode) enqueued. A fault inside
+ *     a kernel surfaces at the caller's next synchronization.
  *   - Results are deterministic: the same inputs give the same bits (no floating-point atomics).
- *   - Calls keep no state; calls on different streams may run concurrently if their outputs and
- *     workspaces do not overlap.
+ *   - Calls keep no state beyond per-device facts filled once (thread-safe) on first use; calls on
+ *     different streams or host threads may run concurrently if their outputs and workspaces do
+ *     not overlap.
  *   - v1 limits: head_dim == 128, idx_heads == 4, idx_dim == 64, block a power of two <= 64,
  *     topk_tokens a positive multiple of block with topk_tokens/block <= 2048, n_q_heads a multiple
  *     of n_kv_heads, n_q_heads/n_kv_heads <= 16, n_tokens >= 1, union_tile >= 1.
@@ -107,8 +111,9 @@ int sgqa_workspace_size(const sgqa_params* p, int op, size_t* bytes);
  * and Figure 3: one shared set of index keys is merged block by block into block keys).
  *   idx_k  [S][N][d_I]        bf16   shared index keys of every token
  *   blk_k  [S][floor(N/B)][d_I] bf16 out: blk_k[s][b][d] = bf16_rne(sum_{j<B} idx_k[s][b*B+j][d] / B),
- *                                    summed in fp32 in ascending j. A trailing partial block is not
- *                                    compressed (it can only ever be a query's own block).
+ *                                    summed in fp64 in ascending j and rounded once (nearest even;
+ *                                    NaN -> 0x7FC0). A trailing partial block is not compressed (it
+ *                                    can only ever be a query's own block).
  * Uses p->n_seqs, n_tokens, idx_dim, block; blk_k may be NULL when N < B. No workspace. */
 int sgqa_compress(const sgqa_params* p, const sgqa_bf16* idx_k, sgqa_bf16* blk_k, sgqa_stream stream);
 

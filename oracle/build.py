@@ -13,8 +13,10 @@ def build(verbose: bool = False) -> str:
     out = os.path.join(_HERE, "liboracle.so")
     tmp = out + ".tmp"
     # -ffp-contract=off: every product and sum is rounded as written (no fused multiply-add).
-    cmd = ["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared",
-           "-Wall", "-Wextra", "-o", tmp, src, "-lm"]
+    # -fno-semantic-interposition: calls to the exported bf16 helpers inside the library may be
+    # inlined (with -fPIC they would otherwise go through the PLT); the arithmetic is unchanged.
+    cmd = ["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fno-semantic-interposition",
+           "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra", "-o", tmp, src, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

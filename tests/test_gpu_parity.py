@@ -55,8 +55,8 @@ def test_compress_bit_exact(sg, name):
 
 
 def test_compress_multi_sequence_and_normal_data(sg):
-    # S sequences at once (the decode cache build); N(0,1) keys: the fp32 sum may round once more than
-    # the fp64 oracle, so at most one bf16 ulp apart, and identical on almost every element.
+    # S sequences at once (the decode cache build) on N(0,1) keys: bit-exact (both sides sum in fp64
+    # in ascending position and round once).
     S, N, B = 3, 4096 + 24, 8
     g = torch.Generator().manual_seed(5)
     ki = torch.randn((S, N, 64), generator=g).to(torch.bfloat16)
@@ -66,10 +66,36 @@ def test_compress_multi_sequence_and_normal_data(sg):
     say("compress S=3 normal data")
     sg.sgqa_compress(p, ki.cuda(), out)
     torch.cuda.synchronize()
-    got = bits(out).astype(np.int32)
-    diff = np.abs(got - want.astype(np.int32))
-    assert diff.max() <= 1
-    assert (diff == 0).mean() > 0.99
+    np.testing.assert_array_equal(bits(out), want)
+
+
+@pytest.mark.parametrize("B", [1, 2, 8, 32])
+def test_compress_bit_exact_any_bf16(sg, B):
+    """Arbitrary finite bf16 keys: subnormals, exponents spread over the whole range inside one
+    block, infinities and exact rounding ties (pairs one bf16 ulp apart average to a tie)."""
+    rng = np.random.default_rng(100 + B)
+    S, N = 2, 96 * B + max(B - 1, 1) // 2
+    raw = rng.integers(0, 0x7F80, size=(S, N, 64), dtype=np.uint16)        # finite magnitudes
+    raw |= (rng.integers(0, 2, size=raw.shape, dtype=np.uint16) << 15)    # signs
+    nb = N // B
+    sub = rng.integers(0, 0x0080, size=(S, N, 64), dtype=np.uint16)       # subnormal magnitudes
+    raw[:, : (nb // 4) * B] = sub[:, : (nb // 4) * B]
+    if B >= 2:
+        lo = rng.integers(0x3F00, 0x4100, size=(S, N // 2, 64), dtype=np.uint16) & 0xFFFE
+        ties = np.stack([lo, lo + 1], axis=2).reshape(S, -1, 64)         # x and x + 1 ulp
+        r0 = (nb // 4) * B
+        r1 = min(N, r0 + (nb // 4) * B)
+        raw[:, r0:r1] = ties[:, r0:r1]
+    raw[0, 5, 3] = 0x7F80                                                  # +inf
+    raw[1, 7, 9] = 0xFF80                                                  # -inf
+    want = oracle.compress(raw, B)
+    ki = torch.from_numpy(raw.view(np.int16)).view(torch.bfloat16).cuda()
+    p = sg.Params(n_tokens=N, n_q_heads=8, n_kv_heads=1, block=B, n_seqs=S)
+    out = torch.empty((S, nb, 64), dtype=torch.bfloat16, device="cuda")
+    say(f"compress arbitrary bf16 B={B} N={N}")
+    sg.sgqa_compress(p, ki, out)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(out), want)
 
 
 def run_topk(sg, p, xd, kbar_dev):
