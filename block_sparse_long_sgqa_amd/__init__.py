@@ -26,6 +26,10 @@ SGQA_ERR_ALIGN = 3
 SGQA_ERR_WORKSPACE = 4
 SGQA_ERR_DEVICE = 5
 SGQA_ERR_HIP = 6
+SGQA_ERR_SCRATCH = 7
+
+# Scratch the library holds per GPU for sgqa_decode_noalloc.
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 SGQA_OP_COMPRESS = 0
 SGQA_OP_INDEX_TOPK = 1
@@ -41,7 +45,7 @@ SGQA_OP_ATTEND_BWD = 8
 EXPORTED = ("sgqa_abi_version", "sgqa_status_string", "sgqa_workspace_size", "sgqa_compress", "sgqa_index_topk",
             "sgqa_union", "sgqa_attend", "sgqa_prefill", "sgqa_decode", "sgqa_decode_varlen", "sgqa_append",
             "sgqa_decode_fp8", "sgqa_index_union", "sgqa_attend_masked", "sgqa_prefill_masked",
-            "sgqa_attend_fwd", "sgqa_attend_bwd")
+            "sgqa_attend_fwd", "sgqa_attend_bwd", "sgqa_decode_noalloc")
 
 
 class sgqa_pages(ctypes.Structure):
@@ -135,6 +139,7 @@ def lib() -> ctypes.CDLL:
         L.sgqa_attend.argtypes = [PP, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.sgqa_prefill.argtypes = [PP, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.sgqa_decode.argtypes = [PP, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.sgqa_decode_noalloc.argtypes = [PP, P, P, P, P, P, P, P, P, P]
         PG = ctypes.POINTER(sgqa_pages)
         L.sgqa_decode_varlen.argtypes = [PP, P, P, P, PG, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.sgqa_append.argtypes = [PP, P, P, P, P, P, P, PG, P, P, P]
@@ -146,7 +151,8 @@ def lib() -> ctypes.CDLL:
         L.sgqa_attend_bwd.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         for name in ("sgqa_compress", "sgqa_index_topk", "sgqa_union", "sgqa_attend", "sgqa_prefill", "sgqa_decode",
                      "sgqa_decode_varlen", "sgqa_append", "sgqa_decode_fp8", "sgqa_index_union",
-                     "sgqa_attend_masked", "sgqa_prefill_masked", "sgqa_attend_fwd", "sgqa_attend_bwd"):
+                     "sgqa_attend_masked", "sgqa_prefill_masked", "sgqa_attend_fwd", "sgqa_attend_bwd",
+                     "sgqa_decode_noalloc"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -316,6 +322,20 @@ def sgqa_decode(p: Params, q, k_cache, v_cache, blk_k, idx_q, idx_w, out, ws, to
             _ptr(out, "out", torch.bfloat16, (S, Hq, D)))
     _check(lib().sgqa_decode(ctypes.byref(p.c()), *args, _ptr(ws, "ws", torch.uint8), ws.numel(),
                              _stream(stream)), "sgqa_decode")
+
+
+def sgqa_decode_noalloc(p: Params, q, k_cache, v_cache, blk_k, idx_q, idx_w, out, topk_out=None,
+                        stream=None) -> None:
+    """sgqa_decode with the library's own per-GPU scratch instead of a workspace (allocates nothing)."""
+    S, L, Hq, G, D = p.n_seqs, p.n_tokens, p.n_q_heads, p.n_kv_heads, p.head_dim
+    args = (_ptr(q, "q", torch.bfloat16, (S, Hq, D)), _ptr(k_cache, "k_cache", torch.bfloat16, (S, G, L, D)),
+            _ptr(v_cache, "v_cache", torch.bfloat16, (S, G, L, D)),
+            _ptr(blk_k, "blk_k", torch.bfloat16, (S, L // p.block, p.idx_dim)),
+            _ptr(idx_q, "idx_q", torch.bfloat16, (S, G, p.idx_heads, p.idx_dim)),
+            _ptr(idx_w, "idx_w", torch.float32, (G, p.idx_heads)),
+            _ptr(topk_out, "topk_out", torch.int32, (S, G, p.kb)),
+            _ptr(out, "out", torch.bfloat16, (S, Hq, D)))
+    _check(lib().sgqa_decode_noalloc(ctypes.byref(p.c()), *args, _stream(stream)), "sgqa_decode_noalloc")
 
 
 class Pages:

@@ -15,6 +15,11 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 
+// Scratch of sgqa_decode_noalloc: one copy per GPU, allocated when the library's code object loads
+// on that GPU. Host code never passes `scratch` itself to a kernel (on the host it is only a stand-in
+// for the symbol); it uses the device address resolved per device in device_state().
+static __device__ __align__(256) uint8_t scratch[SGQA_NOALLOC_SCRATCH_BYTES];
+
 // Facts about one device, filled once (std::call_once) on the first call that runs with it current:
 // whether it is a gfx950, its LDS limit per workgroup, and the dynamic-LDS attribute of every
 // kernel (set here, before any launch, so that a call never fails between two of its launches).
@@ -22,6 +27,7 @@ struct DeviceState {
   std::once_flag once;
   int status = SGQA_ERR_DEVICE;
   int lds_max = 65536;
+  void* scratch = nullptr;  // this device's address of `scratch` (null if it could not be resolved)
 };
 DeviceState g_device[kMaxDevices];
 
@@ -43,6 +49,8 @@ DeviceState* device_state() {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0) v = 65536;
     d.lds_max = v;
     d.status = prepare_kernels(v) == hipSuccess ? SGQA_OK : SGQA_ERR_HIP;
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess) d.scratch = ptr;
   });
   return &d;
 }
@@ -223,6 +231,8 @@ const char* sgqa_status_string(int status) {
       return "the current device is not a gfx950 GPU";
     case SGQA_ERR_HIP:
       return "the HIP runtime reported an error while launching";
+    case SGQA_ERR_SCRATCH:
+      return "the call needs more scratch than the library's static buffer holds (SGQA_NOALLOC_SCRATCH_BYTES)";
     default:
       return "unknown status";
   }
@@ -498,6 +508,19 @@ int sgqa_decode(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k_cac
                 sgqa_bf16* out, void* ws, size_t ws_bytes, sgqa_stream stream) {
   return decode_impl(p, q, k_cache, v_cache, nullptr, nullptr, blk_k, idx_q, idx_w, nullptr, topk_out, out, ws,
                      ws_bytes, stream);
+}
+
+int sgqa_decode_noalloc(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k_cache,
+                        const sgqa_bf16* v_cache, const sgqa_bf16* blk_k, const sgqa_bf16* idx_q, const float* idx_w,
+                        int32_t* topk_out, sgqa_bf16* out, sgqa_stream stream) {
+  int st = check_params(p, NEED_INDEX | NEED_SELECT | NEED_DECODE | NEED_ATTN, false);
+  if (st) return st;
+  if (decode_layout(p, nullptr).bytes > (size_t)SGQA_NOALLOC_SCRATCH_BYTES) return SGQA_ERR_SCRATCH;
+  if ((st = device_ready()) != SGQA_OK) return st;
+  void* ws = device_state()->scratch;
+  if (!ws) return SGQA_ERR_HIP;
+  return decode_impl(p, q, k_cache, v_cache, nullptr, nullptr, blk_k, idx_q, idx_w, nullptr, topk_out, out, ws,
+                     (size_t)SGQA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int sgqa_decode_varlen(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k_cache,

@@ -63,7 +63,8 @@ enum {
   SGQA_ERR_ALIGN = 3,      /* a tensor pointer is not 16-byte aligned */
   SGQA_ERR_WORKSPACE = 4,  /* workspace missing or smaller than sgqa_workspace_size */
   SGQA_ERR_DEVICE = 5,     /* the current device is not a gfx950 GPU, or no device */
-  SGQA_ERR_HIP = 6         /* the HIP runtime reported an error while launching */
+  SGQA_ERR_HIP = 6,        /* the HIP runtime reported an error while launching */
+  SGQA_ERR_SCRATCH = 7     /* sgqa_decode_noalloc: the call needs more scratch than the library holds */
 };
 
 /* Operation selectors for sgqa_workspace_size. */
@@ -190,6 +191,26 @@ int sgqa_decode(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k_cac
                 const sgqa_bf16* v_cache, const sgqa_bf16* blk_k, const sgqa_bf16* idx_q,
                 const float* idx_w, int32_t* topk_out, sgqa_bf16* out, void* ws, size_t ws_bytes,
                 sgqa_stream stream);
+
+/* ---------------------------------------------------------------- decode without allocation
+ * For callers that cannot allocate device memory around a call: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation. Same arguments, result and errors as
+ * sgqa_decode, minus the workspace: the scratch (selection, scores, segment lists) lives in a buffer
+ * of SGQA_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it is loaded on, until the
+ * process ends. The output is bit-identical to sgqa_decode's.
+ *   - Sizes whose decode workspace (sgqa_workspace_size(p, SGQA_OP_DECODE)) exceeds
+ *     SGQA_NOALLOC_SCRATCH_BYTES return SGQA_ERR_SCRATCH before anything is enqueued (e.g. the
+ *     32 x 262144-token decode needs ~33 MiB and fits; S * G * ceil(c / 512) * 512 * 4 bytes of scores
+ *     must stay below the limit, c = floor((L-1)/B)).
+ *   - The call allocates nothing and frees nothing (no hipMalloc/hipFree, no allocating routine).
+ *   - Every call on one GPU shares that GPU's buffer, which keeps the last call's contents: calls that
+ *     overlap in time on one GPU (different streams, or host threads without ordering) RACE on it and
+ *     must be ordered by the caller. Its kernels overwrite every scratch entry before reading it, so
+ *     nothing needs clearing between calls. */
+#define SGQA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int sgqa_decode_noalloc(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k_cache,
+                        const sgqa_bf16* v_cache, const sgqa_bf16* blk_k, const sgqa_bf16* idx_q,
+                        const float* idx_w, int32_t* topk_out, sgqa_bf16* out, sgqa_stream stream);
 
 /* ---------------------------------------------------------------- incremental / varlen decode
  * The decode call above takes one context length L = n_tokens for every sequence and dense caches.

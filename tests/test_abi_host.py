@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(sg):
 
 def test_abi_version_and_status_strings(sg):
     assert sg.lib().sgqa_abi_version() == 1
-    for code in range(7):
+    for code in range(8):
         assert len(sg.status_string(code)) > 0
     assert sg.status_string(0) == "ok"
     assert sg.status_string(99) == "unknown status"
@@ -196,3 +196,13 @@ def test_masked_variant_shapes_and_workspace(sg):
     assert sg.lib().sgqa_attend_masked(ctypes.byref(bad.c()), a, a, a, a, a, a, a, a, 1 << 40, nul) == sg.SGQA_ERR_SHAPE
     assert sg.lib().sgqa_attend_masked(ctypes.byref(p.c()), a, a, a, nul, a, a, a, a, 1 << 40, nul) == sg.SGQA_ERR_NULL
     assert sg.lib().sgqa_attend_masked(ctypes.byref(p.c()), a, a, a, a, a, a, a, a, 16, nul) == sg.SGQA_ERR_WORKSPACE
+
+
+def test_noalloc_decode_rejects_oversized_calls_on_the_host(sg):
+    """Sizes whose decode scratch exceeds the library's static buffer fail before any device work."""
+    p = _p(n_tokens=1 << 20, n_seqs=64, union_tile=1)
+    assert sg.workspace_size(p, sg.SGQA_OP_DECODE) > sg.NOALLOC_SCRATCH_BYTES
+    fake = 1 << 20  # never dereferenced: the size check comes first
+    st = sg.lib().sgqa_decode_noalloc(p.c(), *([fake] * 6), None, fake, None)
+    assert st == sg.SGQA_ERR_SCRATCH, sg.status_string(st)
+    assert "scratch" in sg.status_string(st)
