@@ -22,6 +22,9 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# Per-file extras. The top-k kernel post-processes every matrix-core result with vector ALU ops:
+# keeping the accumulators in VGPRs (instead of AGPRs) saves a register move per score element.
+FILE_FLAGS = {"index_topk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def build(verbose: bool = False) -> str:
@@ -30,7 +33,7 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src: str) -> str:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)

@@ -10,23 +10,32 @@
 //
 // Design (gfx950)
 //  * A workgroup owns 4*WAVES rows (4 per wave): one group, consecutive queries. One 16x16x32
-//    bf16 MFMA takes A = (4 rows x 4 indexer heads) x 32 dims and B = 32 dims x 16 blocks; after the two K-steps
-//    of d_I = 64 every lane holds the 4 head dots of one (row, block) pair and forms the score
-//    locally (ReLU, weights, head sum): no cross-lane traffic, no score matrix in memory.
-//  * Block keys stream through LDS in chunks of 128 blocks, gathered with global_load_lds into
+//    bf16 MFMA takes A = (4 rows x 4 indexer heads) x 32 dims and B = 32 dims x 16 blocks; after
+//    the two K-steps of d_I = 64 every lane holds the 4 head dots of one (row, block) pair and
+//    forms the score locally (ReLU, weights, head sum): no cross-lane traffic, no score matrix.
+//  * Block keys stream through LDS in chunks of 128 blocks, staged through registers into
 //    double-buffered 144-byte rows (16 B of padding spread the MFMA operand reads over all banks);
-//    each chunk feeds every row of the workgroup.
-//  * Exact selection without a score matrix, in three streaming passes over the candidates:
-//    pass 0 lists a strided sample of each row's keys (all of them when few) -- a complete list
-//    gives the K_B-th key at once, a sample the key range where it must lie; pass 1 counts the
-//    keys of that range into 256 power-of-two buckets per row (LDS atomics) and moves to the
-//    bucket holding the K_B-th key, repeating on a finer scale while that bucket is wide and
-//    crowded; pass 2 emits, in ascending block order, every candidate above the bucket plus the
-//    bucket's members -- the first `take` of them when the bucket is one key (lowest ids win
-//    ties), or all of them flagged, with their keys listed, when it is wider; the flagged ones are
-//    then settled by an exact select over the listed keys. Scores are recomputed in every pass
-//    (the stream of block keys through LDS is cheap next to storing them).
+//    each chunk feeds every row of the workgroup. Lane j of a row sees candidates 8j .. 8j+7 of a
+//    chunk, so ascending block order is lane-major.
+//  * Exact selection in ONE streaming pass over the candidates, with a buffer per row in LDS of
+//    C >= K_B + 128 entries (order key, block id), filled in ascending block order:
+//    - a strided sample of at most 512 candidates per row (the same blocks for the whole
+//      workgroup) gives a threshold tau0 with, by a margin of several standard deviations of the
+//      sample quantile, at least K_B candidates at or above it; rows with at most C candidates
+//      take every candidate instead;
+//    - the pass appends every candidate whose fp32 score is not below the row's threshold (one
+//      compare per candidate; the order key is formed only for appended ones). A chunk that
+//      would overflow a buffer first cuts it to exactly its K_B best entries (key descending,
+//      among equal keys the earliest = lowest block ids) and raises the row's threshold to
+//      "strictly above the K_B-th key": nothing below it can enter the final top-K_B any more;
+//    - a row whose sampled threshold let fewer than min(K_B, c) candidates through (a
+//      many-sigma event) runs the pass again taking every candidate;
+//    - each buffer is finally cut to its K_B best and written out (still in ascending order).
+//    A cut finds the K-th largest key by a bitwise binary search whose counts are wave ballots
+//    (no LDS atomics), then compacts the buffer in place with ballot prefix counts.
 //  * Decode selection (one query, many candidates) is shaped differently and lives on its own.
+#include <math.h>
+
 #include <type_traits>
 
 #include "sgqa_device.hpp"
@@ -36,20 +45,22 @@ namespace sgqa {
 
 namespace {
 
-typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kIdxHeads = 4;
 constexpr int kIdxDim = 64;
 constexpr int kChunk = 128;                        // candidate blocks per stage
 constexpr int kKRowBytes = 144;                    // 128 B block key + 16 B pad
-constexpr int kKSlots = kKRowBytes / 16;           // 9 slots of 16 B per row, the last is padding
 constexpr int kStageBytes = kChunk * kKRowBytes;   // 18432 B
-constexpr int kStageInsts = kChunk * kKSlots / 64;  // 18 wave-wide 16-byte loads per stage
-constexpr int kListPad = 16;                       // words between row regions (spreads LDS banks)
-constexpr int kSideCap = 192;                      // bucket members listed per row in the emit pass
+constexpr int kSampleCap = 512;                    // sampled candidates per row
+constexpr int kStaticLds = 256;                    // bound on the kernel's static LDS
+constexpr int kRowPad = 16;                        // pad entries after every row buffer
+constexpr int kHistBuckets = 128;                  // buckets of a select round (scratch per wave)
+// Width of the sample margin: tau0 is the sample key with (mean + kSampleSigmas * sd + 1) sample
+// keys at or above it, mean and sd those of the number of sample keys at or above the true
+// K_B-th key.
+constexpr float kSampleSigmas = 3.0f;
 
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Inclusive prefix sum over the 16 lanes of each row (DPP row shifts; rows are lanes 16q..16q+15).
 __device__ __forceinline__ uint32_t row16_prefix(uint32_t v) {
@@ -60,87 +71,97 @@ __device__ __forceinline__ uint32_t row16_prefix(uint32_t v) {
   return v;
 }
 
-// The value of the last lane of each 16-lane row, for every lane of the row (four lane reads
-// instead of an LDS permute).
+// The value of the last lane of each 16-lane row, for every lane of the row (one DPP broadcast
+// of lane 15 within each row, row_newbcast:15).
 __device__ __forceinline__ uint32_t row16_total(uint32_t incl) {
-  const uint32_t t0 = __builtin_amdgcn_readlane(incl, 15), t1 = __builtin_amdgcn_readlane(incl, 31);
-  const uint32_t t2 = __builtin_amdgcn_readlane(incl, 47), t3 = __builtin_amdgcn_readlane(incl, 63);
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl, 0x15F, 0xF, 0xF, false);
+}
+
+// Wave-wide minimum / maximum / sum of a per-lane value, in every lane: a DPP reduction inside
+// each 16-lane row (lanes shifted in from outside the row keep their own value) and four lane
+// reads -- no LDS round trips.
+__device__ __forceinline__ uint32_t wave_min_fast(uint32_t v) {
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x111, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x112, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x114, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x118, 0xF, 0xF, false));
+  return min(min((uint32_t)__builtin_amdgcn_readlane((int)v, 15), (uint32_t)__builtin_amdgcn_readlane((int)v, 31)),
+             min((uint32_t)__builtin_amdgcn_readlane((int)v, 47), (uint32_t)__builtin_amdgcn_readlane((int)v, 63)));
+}
+__device__ __forceinline__ uint32_t wave_max_fast(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x111, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x112, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x114, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x118, 0xF, 0xF, false));
+  return max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 15), (uint32_t)__builtin_amdgcn_readlane((int)v, 31)),
+             max((uint32_t)__builtin_amdgcn_readlane((int)v, 47), (uint32_t)__builtin_amdgcn_readlane((int)v, 63)));
+}
+// Sum over the lanes above this one (exclusive suffix sum), and the wave total.
+__device__ __forceinline__ uint32_t wave_suffix_excl(uint32_t v, uint32_t* total) {
+  const uint32_t incl = row16_prefix(v);
+  const uint32_t r0 = __builtin_amdgcn_readlane((int)incl, 15), r1 = __builtin_amdgcn_readlane((int)incl, 31);
+  const uint32_t r2 = __builtin_amdgcn_readlane((int)incl, 47), r3 = __builtin_amdgcn_readlane((int)incl, 63);
   const int q = lane_id() >> 4;
-  return q == 0 ? t0 : (q == 1 ? t1 : (q == 2 ? t2 : t3));
+  const uint32_t before = (q > 0 ? r0 : 0u) + (q > 1 ? r1 : 0u) + (q > 2 ? r2 : 0u);
+  *total = r0 + r1 + r2 + r3;
+  return *total - (before + incl);
 }
 
-// A key list in registers: lane l holds entries l, l + 64, ... (P per lane; absent entries are 0,
-// which no finite score maps to).
-template <int P>
-struct KeyRegs {
-  uint32_t k[P];
-};
+// The fp32 bits / value whose order key (score_key) is k.
+__device__ __forceinline__ uint32_t key_bits(uint32_t k) { return (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k; }
+__device__ __forceinline__ float key_to_float(uint32_t k) { return __uint_as_float(key_bits(k)); }
 
-template <int P>
-__device__ __forceinline__ void keys_load(KeyRegs<P>& r, const uint32_t* keys, int n) {
-  const int l = lane_id();
-#pragma unroll
-  for (int j = 0; j < P; ++j) {
-    const int e = j * 64 + l;
-    r.k[j] = e < n ? keys[e] : 0u;
-  }
+// Order key of a buffered score (its raw fp32 bits): score_key, with the one bit pattern that
+// maps to 0 (a NaN) moved to 1, so that 0 can mark an absent entry; and back to fp32 bits.
+__device__ __forceinline__ uint32_t kept_key(uint32_t raw) {
+  const uint32_t k = score_key(__uint_as_float(raw));
+  return k > 1u ? k : 1u;
 }
 
-template <int P>
-__device__ __forceinline__ int keys_count_ge(const KeyRegs<P>& r, uint32_t t) {  // t >= 1
-  int cnt = 0;
-#pragma unroll
-  for (int j = 0; j < P; ++j) cnt += popc64(ballot(r.k[j] >= t));
-  return cnt;
+// Row threshold for "order key >= t" as an fp32 value thr: a score s passes iff !(s < thr) (NaN
+// scores always pass and are ordered by their keys later). Keys above that of +inf give +inf
+// (such candidates are dropped by the next cut).
+__device__ __forceinline__ float threshold_of(uint32_t t) {
+  return t > 0xFF800000u ? __builtin_inff() : key_to_float(t);
 }
 
-// The K-th largest of the n listed keys (1 <= K <= n <= 64 P) and the number of keys above it.
-// Histogram select over [min, max] of the list: every round splits the live key range into 256
-// equal power-of-two buckets, counts the keys of each bucket with LDS atomics into hist (256 words
-// owned by this wave; LDS operations of one wave complete in order, so no barrier is needed),
-// and keeps the bucket where the running count from the top reaches K.
+// The K-th largest listed key (lane l holds entries j * 64 + l; absent ones are 0): the largest t
+// with count(>= t) >= K (1 <= K <= keys present); *n_above gets count(> t). Histogram rounds over
+// the live key range: every round splits it into kHistBuckets equal power-of-two buckets, counts
+// the keys of each (LDS atomics into hist, this wave's scratch; the LDS operations of one wave
+// complete in order) and keeps the bucket where the running count from the top reaches K.
 template <int P>
-__device__ __forceinline__ uint32_t keys_kth_largest(const KeyRegs<P>& r, int K, int* n_above, uint32_t* hist) {
+__device__ __forceinline__ uint32_t kth_largest(const uint32_t (&k)[P], int K, int* n_above, uint32_t* hist) {
   const int l = lane_id();
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
 #pragma unroll
   for (int j = 0; j < P; ++j) {
-    if (r.k[j]) mn = min(mn, r.k[j]);
-    mx = max(mx, r.k[j]);
+    if (k[j]) mn = min(mn, k[j]);
+    mx = max(mx, k[j]);
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, off, 64));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
-  }
-  if (mx == 0u || K < 1) {  // no keys listed: nothing to select (callers never ask for this)
-    *n_above = 0;
-    return 0u;
-  }
+  mn = wave_min_fast(mn);
+  mx = wave_max_fast(mx);
   // Invariant: count(>= lo) >= K > count(>= hi) = c_hi.
   uint64_t lo = mn, hi = (uint64_t)mx + 1;
   uint32_t c_hi = 0;
   while (hi - lo > 1) {
     const int bits = 64 - __clzll((long long)(hi - lo - 1));
-    const int shift = bits > 8 ? bits - 8 : 0;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    *reinterpret_cast<u32x4*>(hist + 4 * l) = z;
+    const int shift = bits > 7 ? bits - 7 : 0;
+    *reinterpret_cast<uint2*>(hist + 2 * l) = make_uint2(0u, 0u);
 #pragma unroll
     for (int j = 0; j < P; ++j) {
-      const uint32_t x = r.k[j];
+      const uint32_t x = k[j];
       if (x >= lo && x < hi) atomicAdd(&hist[(uint32_t)((x - lo) >> shift)], 1u);
     }
-    const u32x4 hv = *reinterpret_cast<const u32x4*>(hist + 4 * l);
-    const uint32_t local = hv[0] + hv[1] + hv[2] + hv[3];
-    const uint32_t above = wave_suffix_sum(local) - local + c_hi;  // count(>= bucket 4l + 4)
-    const uint32_t s3 = above + hv[3], s2 = s3 + hv[2], s1 = s2 + hv[1], s0 = s1 + hv[0];
-    const uint64_t m = ballot(s0 >= (uint32_t)K);  // lanes 0 .. l*, never empty while n >= K
-    if (m == 0) break;                              // fewer than K keys listed: keep lo
+    const uint2 hv = *reinterpret_cast<const uint2*>(hist + 2 * l);
+    uint32_t tot;
+    const uint32_t above = wave_suffix_excl(hv.x + hv.y, &tot) + c_hi;  // count(>= bucket 2l + 2)
+    const uint32_t s1 = above + hv.y, s0 = s1 + hv.x;
+    const uint64_t m = ballot(s0 >= (uint32_t)K);  // lanes 0 .. l*, never empty
     const int ls = 63 - __clzll((long long)m);
-    const int j = s3 >= (uint32_t)K ? 3 : (s2 >= (uint32_t)K ? 2 : (s1 >= (uint32_t)K ? 1 : 0));
-    const uint32_t s_next = j == 3 ? above : (j == 2 ? s3 : (j == 1 ? s2 : s1));
-    const int bsel = readlane(4 * l + j, ls);
-    c_hi = readlane(s_next, ls);
+    const int j = s1 >= (uint32_t)K ? 1 : 0;
+    const int bsel = __builtin_amdgcn_readlane(2 * l + j, ls);
+    c_hi = (uint32_t)__builtin_amdgcn_readlane((int)(j ? above : s1), ls);
     lo += (uint64_t)bsel << shift;
     const uint64_t nhi = lo + (1ull << shift);
     hi = nhi < hi ? nhi : hi;
@@ -149,34 +170,84 @@ __device__ __forceinline__ uint32_t keys_kth_largest(const KeyRegs<P>& r, int K,
   return (uint32_t)lo;
 }
 
+// Cuts one row's buffer (fp32 score bits kb_, ids ib_; n entries in ascending block order) to its
+// K best entries -- keys descending, among equal keys the earliest -- in place and in order, with
+// the whole wave. Requires n > K >= 1 and n <= 64 P. Returns the K-th key. hist: this wave's
+// kHistBuckets words of LDS scratch.
+template <int P, typename IdT>
+__device__ __forceinline__ uint32_t cut_to(uint32_t* kb_, IdT* ib_, int n, int K, uint32_t* hist) {
+  const int l = lane_id();
+  uint32_t k[P], id[P];
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    const int e = j * 64 + l;
+    k[j] = e < n ? kept_key(kb_[e]) : 0u;
+    id[j] = e < n ? (uint32_t)ib_[e] : 0u;
+  }
+  int above;
+  const uint32_t tau = kth_largest(k, K, &above, hist);
+  const int need = K - above;  // entries equal to tau that stay: the first ones
+  const uint64_t lt = lanemask_lt();
+  int wpos = 0, tseen = 0;
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    const bool eq = k[j] == tau;  // absent entries are 0 < tau
+    const uint64_t em = ballot(eq);
+    const bool keep = k[j] > tau || (eq && tseen + popc64(em & lt) < need);
+    const uint64_t km = ballot(keep);
+    if (keep) {
+      const int dst = wpos + popc64(km & lt);
+      kb_[dst] = key_bits(k[j]);
+      ib_[dst] = (IdT)id[j];
+    }
+    wpos += popc64(km);
+    tseen += popc64(em);
+  }
+  return tau;
+}
+
+// The keys of a list of fp32 score bits in registers (for the sample threshold): lane l holds
+// entries l, l + 64, ...
+template <int P>
+__device__ __forceinline__ void keys_load(uint32_t (&k)[P], const uint32_t* bits, int n) {
+  const int l = lane_id();
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    const int e = j * 64 + l;
+    k[j] = e < n ? kept_key(bits[e]) : 0u;
+  }
+}
+
 }  // namespace
 
 // A workgroup owns the rows (i, g) of one group g and 4*WAVES consecutive queries i (the heaviest
 // query ranges are launched first); candidates [0, c(i)); output the ascending ids into
 // topk [G][N][K_B] (-1 padded).
 //
-// LDS: the double-buffered stage, then per row a region A of kb + kSideCap words (the sample keys
-// of pass 0, later the row's output list) and a region B of 256 words (the histogram of pass 1,
-// the scratch of a list select, later the keys of the threshold bucket's members), kListPad words
-// apart.
+// LDS: the double-buffered stage, every wave's select scratch, then per row a buffer of C = 64 P fp32 score bits and, after all
+// rows' scores, their block ids (IdT: uint16 when every block id fits, else int32). Each row buffer
+// is followed by kRowPad pad entries: lane j of the row writes the candidates it does not keep to
+// pad entry j (the append is branch-free), and the pad staggers the rows' LDS banks.
 //
 // UNION: instead of writing topk, every selected id and the row's own block are ORed into the
 // tile-union bitmask umask [G][T][W] (bit b % 32 of word b / 32 of row (g, floor(i / tile))), which
 // the caller has zeroed: the fused index -> union path that never materialises topk.
-template <int WAVES, int P, bool UNION>
+template <int WAVES, int P, typename IdT, bool UNION>
 __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restrict__ qi, const float* __restrict__ w,
                                                        const uint16_t* __restrict__ kbar,
                                                        int32_t* __restrict__ topk, int n_tokens, int n_groups,
                                                        int block, int kb, uint32_t* __restrict__ umask, int tile,
                                                        int n_tiles, int n_words) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  uint8_t* stage = smem;                                                        // 2 x kStageBytes
-  const int out_cap = (kb + 3) / 4 * 4 + kSideCap;                             // region A words
-  const int rstride = out_cap + 256 + kListPad;                                // words per row
-  uint32_t* rows_lds = reinterpret_cast<uint32_t*>(smem + 2 * kStageBytes);
-
+  constexpr int C = 64 * P;
+  constexpr int CS = C + kRowPad;  // row stride in entries
   constexpr int kRowsPerWg = WAVES * 4;
-  const int wave = threadIdx.x >> 6;
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint8_t* stage = smem;  // 2 x kStageBytes
+  uint32_t* hist_lds = reinterpret_cast<uint32_t*>(smem + 2 * kStageBytes);  // WAVES x kHistBuckets
+  uint32_t* keys_lds = hist_lds + WAVES * kHistBuckets;
+  IdT* ids_lds = reinterpret_cast<IdT*>(keys_lds + kRowsPerWg * CS);
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
   const int l = lane_id();
   const int quarter = l >> 4;
   const int l16 = l & 15;
@@ -239,34 +310,47 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
   }
   float w4[4];
   for (int j = 0; j < 4; ++j) w4[j] = w[g_o * kIdxHeads + j];
+  // Wait for these loads here, where the compiler sees it: otherwise it assumes them in flight at
+  // every stream step and waits for the next chunk's loads before the first product.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
-  // Stage issue: 18 wave-wide loads of 64 slots; slot s = stage row s / 9, piece s % 9 (piece 8 =
-  // pad). Stage row R = 16 ct + j holds candidate v0 + kTiles j + ct, so that tile ct (rows 16 ct ..
-  // 16 ct + 15, read by lanes j = l % 16) gives lane j the candidates kTiles j .. kTiles j + 7 of
-  // the chunk in ascending order over the tiles. Candidate v is block lo + v * stride + off. The
-  // (row, piece) of this lane's slots do not change from chunk to chunk.
+  // Stage fill: 16 wave-wide 16-byte loads per chunk; slot s = stage row s / 8, piece s % 8. Stage
+  // row R = 16 ct + j holds candidate v0 + kTiles j + ct, so that tile ct (rows 16 ct .. 16 ct + 15,
+  // read by lanes j = l % 16) gives lane j the candidates kTiles j .. kTiles j + 7 of the chunk in
+  // ascending order over the tiles. Candidate v is block lo + v * stride + off. The (row, piece) of
+  // this lane's slots do not change from chunk to chunk. The next chunk's keys are loaded into
+  // registers at the start of a step and written to its stage buffer at the end: an LDS-direct load
+  // would hold the issuing wave, and with them in flight every LDS read would wait for all of them.
   constexpr int kTiles = kChunk / 16;
-  constexpr int kIssuePerWave = (kStageInsts + WAVES - 1) / WAVES;
-  int is_row[kIssuePerWave], is_piece[kIssuePerWave];
+  constexpr int kFillLoads = kChunk * 8 / 64;
+  constexpr int kFillPerWave = (kFillLoads + WAVES - 1) / WAVES;
+  int fl_v[kFillPerWave], fl_piece[kFillPerWave], fl_lds[kFillPerWave];
 #pragma unroll
-  for (int x = 0; x < kIssuePerWave; ++x) {
+  for (int x = 0; x < kFillPerWave; ++x) {
     const int slot = (wave + x * WAVES) * 64 + l;
-    is_row[x] = slot / kKSlots;
-    const int piece = slot - is_row[x] * kKSlots;
-    is_piece[x] = piece == kKSlots - 1 ? 0 : piece;
+    const int row = slot >> 3;
+    fl_piece[x] = slot & 7;
+    fl_v[x] = (row & 15) * kTiles + (row >> 4);
+    fl_lds[x] = row * kKRowBytes + fl_piece[x] * 16;
   }
-  auto issue = [&](int v0, int buf, int stride, int off, int n_virt) {
+  u32x4 fill[kFillPerWave];
+  auto fetch = [&](int v0, int stride, int off, int n_virt) {
+    // Whole chunk inside the candidates and the block keys: no per-slot checks.
+    const bool whole = v0 + kChunk <= n_virt && lo + (v0 + kChunk - 1) * stride + off < n_blocks;
 #pragma unroll
-    for (int x = 0; x < kIssuePerWave; ++x) {
-      const int ii = wave + x * WAVES;
-      if (ii < kStageInsts) {
-        const int v = v0 + (is_row[x] & 15) * kTiles + (is_row[x] >> 4);
+    for (int x = 0; x < kFillPerWave; ++x) {
+      if (wave + x * WAVES < kFillLoads) {
+        const int v = v0 + fl_v[x];
         int b = lo + v * stride + off;
-        if (v >= n_virt || b >= n_blocks) b = 0;  // beyond the candidates: any valid key (never used)
-        __builtin_amdgcn_global_load_lds((const void*)(kbar + (long long)b * kIdxDim + is_piece[x] * 8),
-                                         (lds_void*)(stage + buf * kStageBytes + ii * 1024), 16, 0, 0);
+        if (!whole && (v >= n_virt || b >= n_blocks)) b = 0;  // beyond the candidates: any valid key
+        fill[x] = *reinterpret_cast<const u32x4*>(kbar + (uint32_t)(b * kIdxDim + fl_piece[x] * 8));
       }
     }
+  };
+  auto deposit = [&](int buf) {
+#pragma unroll
+    for (int x = 0; x < kFillPerWave; ++x)
+      if (wave + x * WAVES < kFillLoads) *reinterpret_cast<u32x4*>(stage + buf * kStageBytes + fl_lds[x]) = fill[x];
   };
   const int boff = l16 * kKRowBytes + quarter * 16;  // B operand: row l16 of a 16-block tile
   // Scores of one staged chunk: all operand reads first, then all products, then the per-lane
@@ -300,16 +384,20 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
 #pragma unroll
   for (int off = 16; off <= 32; off <<= 1) hi_wave = min(hi_wave, __shfl_xor(hi_wave, off, 64));
   // Streams candidates v in [0, n_virt) (block lo + v * stride + off) through the double-buffered
-  // stage. For every chunk, body(sc, v_first, full) gets this lane's 8 scores, for candidates
-  // v_first .. v_first + 7 (ascending), and whether every candidate of the wave's rows in the chunk
-  // is valid (a compile-time tag); after() runs once per chunk.
+  // stage: chunk n+1's keys are loaded into registers at the start of step n and written to its
+  // buffer at the end (that buffer's last reads were in step n-1, before the barrier). For every
+  // chunk, body(sc, v_first, full) gets this lane's 8 scores, for candidates v_first .. v_first + 7
+  // (ascending), and whether every candidate of the wave's rows in the chunk is valid (a
+  // compile-time tag); after() runs once per chunk.
   auto stream = [&](int n_virt, int stride, int off, auto&& body, auto&& after) {
     const int n_ch = (n_virt + kChunk - 1) / kChunk;
-    if (n_ch > 0) issue(0, 0, stride, off, n_virt);
+    if (n_ch > 0) {
+      fetch(0, stride, off, n_virt);
+      deposit(0);
+    }
     for (int n = 0; n < n_ch; ++n) {
-      wait_vm();
-      __syncthreads();
-      if (n + 1 < n_ch) issue((n + 1) * kChunk, (n + 1) & 1, stride, off, n_virt);
+      __syncthreads();  // stage n is complete; the other buffer's last reader has passed
+      if (n + 1 < n_ch) fetch((n + 1) * kChunk, stride, off, n_virt);
       float sc[kTiles];
       chunk_scores(stage + (n & 1) * kStageBytes, sc);
       const int v_end = (n + 1) * kChunk;
@@ -319,6 +407,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
       else
         body(sc, v_first, std::false_type());
       after();
+      if (n + 1 < n_ch) deposit((n + 1) & 1);
     }
     __syncthreads();  // the stage buffers are free again
   };
@@ -328,252 +417,135 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
   };
   const int n_all = hi_all - lo;
 
-  uint32_t* my_a = rows_lds + (size_t)(wave * 4 + quarter) * rstride;  // this lane's row: region A
-  uint32_t* my_b = my_a + out_cap;                                       // region B
-  auto row_a = [&](int q) { return rows_lds + (size_t)(wave * 4 + q) * rstride; };
-  auto row_b = [&](int q) { return rows_lds + (size_t)(wave * 4 + q) * rstride + out_cap; };
-
-  // ------------------------------------------------------------------ pass 0: sample
-  // Every row's candidates, or a strided sample of them when there are more than sample_cap, go
-  // into region A. A complete list gives the exact K_B-th key at once; a sample gives the range
-  // for the histogram of pass 1.
-  const int sample_cap = min(512, out_cap) / 64 * 64;
-  const int stride = n_all > sample_cap ? (n_all + sample_cap - 1) / sample_cap : 1;
-  const int s_off = stride / 2;
-  const int s_virt = (n_all - s_off + stride - 1) / stride;
-  int n_cnt = 0;  // keys listed for this lane's row (uniform over the quarter)
-  auto append_all = [&](const float (&sc)[kTiles], int v_first, auto full_t) {
-    constexpr bool kFull = decltype(full_t)::value;
-    uint32_t pm = 0;
-#pragma unroll
-    for (int ct = 0; ct < kTiles; ++ct)
-      pm |= (kFull || valid_at(v_first + ct, s_virt, stride, s_off)) ? (1u << ct) : 0u;
-    if (!ballot(pm != 0u)) return;
-    const uint32_t cnt = __popc(pm);
-    const uint32_t incl = row16_prefix(cnt);
-    const uint32_t total = row16_total(incl);
-    uint32_t pos = n_cnt + incl - cnt;
-#pragma unroll
-    for (int ct = 0; ct < kTiles; ++ct)
-      if (pm & (1u << ct)) my_a[pos++] = score_key(sc[ct]);
-    n_cnt += total;
-  };
+  uint32_t* my_k = keys_lds + (size_t)(wave * 4 + quarter) * CS;  // this lane's row buffer
+  IdT* my_i = ids_lds + (size_t)(wave * 4 + quarter) * CS;
+  auto row_k = [&](int q) { return keys_lds + (size_t)(wave * 4 + q) * CS; };
+  auto row_i = [&](int q) { return ids_lds + (size_t)(wave * 4 + q) * CS; };
+  const uint32_t pad_pos = C + l16;  // this lane's pad entry
   auto nothing = [&]() {};
+  uint32_t* hist = hist_lds + wave * kHistBuckets;  // this wave's select scratch
 
-  // Row state (uniform over the row's 16 lanes). Modes: every candidate selected; ties (keys above
-  // t_hi selected, the first `take` keys equal to t_lo = t_hi in block order too); bucket (keys
-  // above t_hi selected, keys in [t_lo, t_hi] listed for an exact select after the emit pass);
-  // histogram (the threshold bucket is not narrow enough yet).
-  enum { kAll = 0, kTies = 1, kBucket = 2, kHist = 3 };
-  int mode = kAll;
-  uint32_t t_lo = 1u, t_hi = 0u;
-  int take = 0;                 // kTies: equal keys to take; kBucket / kHist: keys still to select
-  uint32_t h_lo = 0u, h_hi = 0xFFFFFFFFu;  // kHist: keys in [h_lo, h_hi] are bucketed ...
-  int h_shift = 0;              // ... into bucket (key - h_lo) >> h_shift
-  bool h_open = false;          // ... except that with an open range bucket 255 takes every key above
+  // Row state, uniform over the row's 16 lanes: the threshold (a score s passes iff !(s < thr)),
+  // the number of buffered entries, and whether the row takes part in the current pass.
+  float thr = -__builtin_inff();
+  int n_cnt = 0;
+  bool active = true;
 
-  stream(s_virt, stride, s_off, append_all, nothing);
-  lds_wait();
-  for (int q = 0; q < 4; ++q) {
-    const int nq = readlane(n_cnt, 16 * q);
-    const int cq = readlane(n_cand, 16 * q);
-    if (cq <= kb) continue;  // every candidate is selected
-    uint32_t* ka = row_a(q);
-    KeyRegs<8> r;
-    keys_load(r, ka, nq);
-    if (stride == 1) {  // complete list: the exact K_B-th key and its ties
-      int above;
-      const uint32_t tau = keys_kth_largest(r, kb, &above, row_b(q));
-      if (quarter == q) {
-        mode = kTies;
-        t_lo = t_hi = tau;
-        take = kb - above;
-      }
-    } else {
-      // Histogram range: from the sample key with about 4 K_B candidates expected at or above it
-      // (the lowest sample key if that is more than the sample) up to the largest sample key.
-      int ks = (int)(((long long)4 * kb * nq + cq - 1) / cq);
-      ks = ks < 1 ? 1 : (ks > nq ? nq : ks);
-      int above;
-      const uint32_t lo_k = keys_kth_largest(r, ks, &above, row_b(q));
-      uint32_t mx = 0u;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) mx = max(mx, r.k[j]);
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
-      const uint64_t width = (uint64_t)mx - lo_k + 1;
-      const int bits = 64 - __clzll((long long)(width - 1 | 1));
-      if (quarter == q) {
-        mode = kHist;
-        take = kb;
-        h_lo = lo_k;
-        h_hi = 0xFFFFFFFFu;
-        h_open = true;
-        h_shift = bits > 8 ? bits - 8 : 0;
-      }
-    }
-  }
-
-  // ------------------------------------------------------------------ pass 1: histograms
-  // Rows still in histogram mode count their keys in [h_lo, h_hi] per bucket (LDS atomics into
-  // region B), then move to the bucket that holds their K_B-th key: a one-key bucket gives the
-  // exact threshold (ties mode), a bucket of at most kSideCap keys is listed in the emit pass
-  // (bucket mode), a larger one is histogrammed again on a 256 times finer scale.
-  __shared__ int any_hist;
-  for (;;) {
-    if (threadIdx.x == 0) any_hist = 0;
-    __syncthreads();
-    if (ballot(mode == kHist) && l == 0) any_hist = 1;
-    __syncthreads();
-    if (!any_hist) break;
-    if (mode == kHist) {
-      const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(my_b + 64 * j + 4 * l16) = z;
-    }
-    const bool hist_row = mode == kHist;
-    auto count = [&](const float (&sc)[kTiles], int v_first, auto full_t) {
+  // ------------------------------------------------------------------ sample
+  // A strided sample of the candidates (the same blocks for every row of the workgroup) goes into
+  // the row buffers; for every row with more than C candidates its keys give the threshold tau0.
+  if (n_all > C) {
+    const int sample_cap = min(kSampleCap, C) / 64 * 64;
+    const int stride = (n_all + sample_cap - 1) / sample_cap;
+    const int s_off = stride / 2;
+    const int s_virt = (n_all - s_off + stride - 1) / stride;
+    auto append_sample = [&](const float (&sc)[kTiles], int v_first, auto full_t) {
       constexpr bool kFull = decltype(full_t)::value;
-      if (!ballot(hist_row)) return;
+      bool f[kTiles];
+      uint32_t cnt = 0;
 #pragma unroll
       for (int ct = 0; ct < kTiles; ++ct) {
-        const uint32_t key = score_key(sc[ct]);
-        const bool ok = hist_row && (kFull || valid_at(v_first + ct, n_all, 1, 0)) && key >= h_lo && key <= h_hi;
-        if (ok) {
-          uint32_t bk = (key - h_lo) >> h_shift;
-          bk = bk > 255u ? 255u : bk;
-          atomicAdd(&my_b[bk], 1u);
-        }
+        f[ct] = kFull || valid_at(v_first + ct, s_virt, stride, s_off);
+        cnt += f[ct] ? 1u : 0u;
       }
+      const uint32_t incl = row16_prefix(cnt);
+      uint32_t pos = n_cnt + incl - cnt;
+#pragma unroll
+      for (int ct = 0; ct < kTiles; ++ct) {
+        my_k[f[ct] ? pos : pad_pos] = __float_as_uint(sc[ct]);
+        pos += f[ct] ? 1u : 0u;
+      }
+      n_cnt += row16_total(incl);
     };
-    stream(n_all, 1, 0, count, nothing);
+    stream(s_virt, stride, s_off, append_sample, nothing);
     lds_wait();
+
     for (int q = 0; q < 4; ++q) {
-      if (readlane((int)(mode == kHist), 16 * q) == 0) continue;
-      const int need = readlane(take, 16 * q);
-      const uint32_t lo_q = readlane(h_lo, 16 * q), hi_q = readlane(h_hi, 16 * q);
-      const int sh_q = readlane(h_shift, 16 * q);
-      const bool open_q = readlane((int)h_open, 16 * q) != 0;
-      const u32x4 hv = *reinterpret_cast<const u32x4*>(row_b(q) + 4 * l);
-      const uint32_t local = hv[0] + hv[1] + hv[2] + hv[3];
-      const uint32_t above = wave_suffix_sum(local) - local;  // keys in buckets >= 4l + 4
-      const uint32_t s3 = above + hv[3], s2 = s3 + hv[2], s1 = s2 + hv[1], s0 = s1 + hv[0];
-      const uint64_t m = ballot(s0 >= (uint32_t)need);
-      if (m == 0) {
-        // Fewer than `need` keys in the range. On the first histogram the sampled lower end was too
-        // high: count every key >= 1 on a coarse scale next time. When that range already held
-        // every key >= 1, the remaining keys are 0 (only a NaN score maps there): the K_B-th key is
-        // 0 and the first (need - count) of them in block order complete the selection.
-        const bool full_range = lo_q == 1u && hi_q == 0xFFFFFFFFu && !open_q;
-        const int in_range = (int)readlane(s0, 0);
-        if (quarter == q) {
-          if (full_range) {
-            mode = kTies;
-            t_lo = t_hi = 0u;
-            take = need - in_range;
-          } else {
-            h_lo = 1u;
-            h_hi = 0xFFFFFFFFu;
-            h_open = false;
-            h_shift = 24;
-          }
-        }
-        continue;
-      }
-      const int ls = 63 - __clzll((long long)m);
-      const int j = s3 >= (uint32_t)need ? 3 : (s2 >= (uint32_t)need ? 2 : (s1 >= (uint32_t)need ? 1 : 0));
-      const uint32_t s_next = j == 3 ? above : (j == 2 ? s3 : (j == 1 ? s2 : s1));
-      const uint32_t in_b = j == 3 ? hv[3] : (j == 2 ? hv[2] : (j == 1 ? hv[1] : hv[0]));
-      const int bsel = readlane(4 * l + j, ls);
-      const int need2 = need - (int)readlane(s_next, ls);  // keys still to select inside the bucket
-      const int cnt_b = (int)readlane(in_b, ls);
-      const uint64_t b_lo = (uint64_t)lo_q + ((uint64_t)bsel << sh_q);
-      uint64_t b_hi = (open_q && bsel == 255) ? 0xFFFFFFFFull : b_lo + (1ull << sh_q) - 1;
-      if (b_hi > hi_q) b_hi = hi_q;
-      if (quarter == q) {
-        take = need2;
-        if (b_hi == b_lo) {
-          mode = kTies;
-          t_lo = t_hi = (uint32_t)b_lo;
-        } else if (cnt_b <= kSideCap) {
-          mode = kBucket;
-          t_lo = (uint32_t)b_lo;
-          t_hi = (uint32_t)b_hi;
-        } else {
-          const uint64_t width = b_hi - b_lo + 1;
-          const int bits = 64 - __clzll((long long)(width - 1));
-          h_lo = (uint32_t)b_lo;
-          h_hi = (uint32_t)b_hi;
-          h_open = false;
-          h_shift = bits > 8 ? bits - 8 : 0;
-        }
-      }
+      const int cq = readlane(n_cand, 16 * q);
+      if (cq <= C) continue;  // the row takes every candidate
+      const int nq = readlane(n_cnt, 16 * q);
+      const float p = (float)kb / (float)cq;
+      const float mean = (float)nq * p;
+      const int ks = (int)ceilf(mean + kSampleSigmas * sqrtf(mean * (1.0f - p))) + 1;
+      if (ks >= nq) continue;  // the sample cannot bound the threshold: take every candidate
+      uint32_t sk[kSampleCap / 64];
+      keys_load(sk, row_k(q), nq);
+      int unused;
+      const uint32_t tau0 = kth_largest(sk, ks, &unused, hist);
+      if (quarter == q) thr = threshold_of(tau0);
     }
+    n_cnt = 0;
   }
 
-  // ------------------------------------------------------------------ pass 2: emit in order
-  // In block order, every candidate above t_hi, and the candidates in [t_lo, t_hi]: in ties mode the
-  // first `take` of them, in bucket mode all of them, flagged (bit 31) in the output list with their
-  // keys listed in region B, to be decided once the bucket's exact threshold is known.
-  const bool all_row = mode == kAll;
-  const bool bucket_row = mode == kBucket;
-  int n_out = 0, t_seen = 0, n_side = 0;  // uniform over the quarter
-  int32_t* out_a = reinterpret_cast<int32_t*>(my_a);
-  auto emit = [&](const float (&sc)[kTiles], int v_first, auto full_t) {
+  // ------------------------------------------------------------------ the pass
+  // Every candidate that passes its row's threshold is appended, in ascending block order. A
+  // chunk that would overflow a row's buffer first cuts it to the K_B best and raises the row's
+  // threshold past the K_B-th key.
+  auto append = [&](const float (&sc)[kTiles], int v_first, auto full_t) {
     constexpr bool kFull = decltype(full_t)::value;
-    uint32_t gm = 0, em = 0;
-    uint32_t keys[kTiles];
+    bool f[kTiles];
+    uint32_t cnt = 0;
+    auto filter = [&]() {
+      cnt = 0;
+#pragma unroll
+      for (int ct = 0; ct < kTiles; ++ct) {
+        f[ct] = active && (kFull || v_first + ct < n_cand) && !(sc[ct] < thr);
+        cnt += f[ct] ? 1u : 0u;
+      }
+    };
+    filter();
+    uint32_t incl = row16_prefix(cnt);
+    int tot = (int)row16_total(incl);
+    if (ballot(n_cnt + tot > C)) {
+      lds_wait();
+      for (int q = 0; q < 4; ++q) {
+        if (readlane((int)(n_cnt + tot > C), 16 * q) == 0) continue;
+        const uint32_t tau = cut_to<P, IdT>(row_k(q), row_i(q), readlane(n_cnt, 16 * q), kb, hist);
+        if (quarter == q) {
+          n_cnt = kb;
+          thr = tau == 0xFFFFFFFFu ? __builtin_inff() : threshold_of(tau + 1u);
+        }
+      }
+      filter();
+      incl = row16_prefix(cnt);
+      tot = (int)row16_total(incl);
+    }
+    // Kept candidates go to consecutive entries, the others to this lane's pad entry.
+    uint32_t pos = n_cnt + incl - cnt;
+    const uint32_t id0 = (uint32_t)(lo + v_first);
 #pragma unroll
     for (int ct = 0; ct < kTiles; ++ct) {
-      const bool ok = kFull || valid_at(v_first + ct, n_all, 1, 0);
-      keys[ct] = score_key(sc[ct]);
-      gm |= (ok && (all_row || keys[ct] > t_hi)) ? (1u << ct) : 0u;
-      em |= (ok && !all_row && keys[ct] >= t_lo && keys[ct] <= t_hi) ? (1u << ct) : 0u;
+      const uint32_t e = f[ct] ? pos : pad_pos;
+      my_k[e] = __float_as_uint(sc[ct]);
+      my_i[e] = (IdT)(id0 + ct);
+      pos += f[ct] ? 1u : 0u;
     }
-    if (!ballot((gm | em) != 0u)) return;
-    const uint32_t ng = __popc(gm), ne = __popc(em);
-    const uint32_t incl = row16_prefix(ng | (ne << 16));  // row totals <= 128 each
-    const uint32_t total = row16_total(incl);
-    const int g_before = (int)((incl & 0xFFFFu) - ng), e_before = (int)((incl >> 16) - ne);
-    const int rem = bucket_row ? 0x7FFFFFFF : max(0, take - t_seen);  // members still to take
-    // This lane takes its first min(ne, rem - e_before) members (all of them in bucket mode).
-    const int k_take = min((int)ne, max(0, rem - e_before));
-    uint32_t et = 0u;
-    for (uint32_t t = em, j = 0; j < (uint32_t)k_take; ++j) {
-      et |= t & (0u - t);
-      t &= t - 1u;
-    }
-    uint32_t sm = gm | et;
-    int pos = n_out + g_before + min(e_before, rem);
-    int side = n_side + e_before;
-    // Taken candidates in ascending order; the loop runs as often as the busiest lane takes one.
-    while (sm) {
-      const int ct = __builtin_ctz(sm);
-      sm &= sm - 1u;
-      const bool flag = bucket_row && ((em >> ct) & 1u);
-      out_a[pos++] = (lo + v_first + ct) | (flag ? (int)0x80000000u : 0);
-      if (flag) {
-        uint32_t key = keys[0];
-#pragma unroll
-        for (int j = 1; j < kTiles; ++j) key = ct == j ? keys[j] : key;
-        my_b[side++] = key;
-      }
-    }
-    const int tot_e = (int)(total >> 16);
-    n_out += (int)(total & 0xFFFFu) + min(tot_e, rem);
-    t_seen += tot_e;
-    n_side += bucket_row ? tot_e : 0;
+    n_cnt += tot;
   };
-  stream(n_all, 1, 0, emit, nothing);
-  lds_wait();
+  stream(n_all, 1, 0, append, nothing);
+
+  // A row whose sampled threshold let too few candidates through takes every candidate again.
+  __shared__ int any_redo;
+  if (threadIdx.x == 0) any_redo = 0;
+  __syncthreads();
+  const bool redo = valid_o && n_cnt < min(kb, n_cand);
+  if (ballot(redo) && l == 0) any_redo = 1;
+  __syncthreads();
+  if (any_redo) {
+    active = redo;
+    if (redo) {
+      thr = -__builtin_inff();
+      n_cnt = 0;
+    }
+    stream(n_all, 1, 0, append, nothing);
+  }
 
   // ------------------------------------------------------------------ output
-  // Bucket rows: the exact threshold tau among the listed bucket keys (binary search on the key,
-  // counting with ballots), then the flagged entries with key > tau and the first (need - above)
-  // with key == tau stay. Every row is written out in order, -1 padded.
-  // Union output: the tiles this workgroup's queries fall in are ORed together in LDS (the stage
-  // buffers are free now) and each non-zero word is then ORed into umask once; when they do not fit,
-  // every bit goes to umask directly.
+  // Every buffer is cut to its K_B best and written out in order (-1 padded), or its ids and the
+  // row's own block are ORed into the union mask. Union output: the tiles this workgroup's queries
+  // fall in are ORed together in LDS (the stage buffers are free now) and each non-zero word is
+  // then ORed into umask once; when they do not fit, every bit goes to umask directly.
+  lds_wait();
   const int t0 = i0 / tile, n_wt = i_last / tile - t0 + 1;
   const bool lds_union = UNION && (long long)n_wt * n_words * 4 <= 2LL * kStageBytes;
   uint32_t* umask_lds = reinterpret_cast<uint32_t*>(stage);
@@ -584,57 +556,22 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
   for (int q = 0; q < 4; ++q) {
     const int i = i0 + wave * 4 + q, g = g_wg;
     if (i >= n_tokens) break;
-    int32_t* out = UNION ? nullptr : topk + ((long long)g * n_tokens + i) * kb;
-    uint32_t* mrow = !UNION ? nullptr : (lds_union ? umask_lds + (i / tile - t0) * n_words : mask_row(i, g));
-    auto put_bit = [&](int b) { atomicOr(&mrow[b >> 5], 1u << (b & 31)); };
-    if (UNION && l == 0) put_bit(i / block);  // the own block
-    const int32_t* list = reinterpret_cast<const int32_t*>(row_a(q));
-    const int nq = readlane(n_out, 16 * q);
-    if (readlane((int)bucket_row, 16 * q) == 0) {
-      if constexpr (UNION) {
-        for (int e = l; e < nq; e += 64) put_bit(list[e]);
-      } else {
-        for (int e = l; e < kb; e += 64) out[e] = e < nq ? list[e] : -1;
-      }
-      continue;
+    int nq = readlane(n_cnt, 16 * q);
+    if (nq > kb) {
+      cut_to<P, IdT>(row_k(q), row_i(q), nq, kb, hist);
+      nq = kb;
+      lds_wait();
     }
-    const uint32_t* sk = row_b(q);
-    const int ns = readlane(n_side, 16 * q);
-    const int need = readlane(take, 16 * q);
-    KeyRegs<kSideCap / 64> r;
-    keys_load(r, sk, ns);
-    // tau = the largest t with count(keys >= t) >= need.
-    uint32_t tau = 0u;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t t = tau | (1u << bit);
-      if (keys_count_ge(r, t) >= need) tau = t;
+    const IdT* list = row_i(q);
+    if constexpr (UNION) {
+      uint32_t* mrow = lds_union ? umask_lds + (i / tile - t0) * n_words : mask_row(i, g);
+      auto put_bit = [&](int b) { atomicOr(&mrow[b >> 5], 1u << (b & 31)); };
+      if (l == 0) put_bit(i / block);  // the own block
+      for (int e = l; e < nq; e += 64) put_bit((int)list[e]);
+    } else {
+      int32_t* out = topk + ((long long)g * n_tokens + i) * kb;
+      for (int e = l; e < kb; e += 64) out[e] = e < nq ? (int32_t)list[e] : -1;
     }
-    const int ties = need - keys_count_ge(r, tau + 1u);  // tau < 2^32 - 1: a listed key is above it
-    int wr = 0, j_side = 0, t_cnt = 0;
-    for (int e0 = 0; e0 < nq; e0 += 64) {
-      const int e = e0 + l;
-      const int32_t v = e < nq ? list[e] : 0;
-      const bool flagged = e < nq && v < 0;
-      const uint64_t fm = ballot(flagged);
-      const int js = j_side + popc64(fm & lanemask_lt());
-      const uint32_t key = flagged ? sk[js] : 0u;
-      const bool tie = flagged && key == tau;
-      const uint64_t tm = ballot(tie);
-      const int tr = t_cnt + popc64(tm & lanemask_lt());
-      const bool keep = e < nq && (!flagged || key > tau || (tie && tr < ties));
-      const uint64_t km = ballot(keep);
-      if (keep) {
-        if constexpr (UNION)
-          put_bit(v & 0x7FFFFFFF);
-        else
-          out[wr + popc64(km & lanemask_lt())] = v & 0x7FFFFFFF;
-      }
-      wr += popc64(km);
-      j_side += popc64(fm);
-      t_cnt += popc64(tm);
-    }
-    if constexpr (!UNION)
-      for (int e = wr + l; e < kb; e += 64) out[e] = -1;
   }
   if (lds_union) {
     __syncthreads();
@@ -647,20 +584,36 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
 
 namespace {
 
-// Stage buffers and the per-row regions.
-size_t select_lds_bytes(int waves, int kb) {
-  return (size_t)2 * kStageBytes + (size_t)waves * 4 * ((kb + 3) / 4 * 4 + kSideCap + 256 + kListPad) * 4;
+// The shapes a launch can take: WAVES waves of 4 rows, buffers of 64 P entries, 16- or 32-bit ids.
+// Each fits the gfx950 LDS with the stage; the first whose buffer holds K_B + 128 entries is used.
+struct SelectShape {
+  int waves, p;
+  bool id32;
+};
+constexpr SelectShape kShapes[] = {{4, 20, false}, {2, 40, false}, {4, 14, true}, {1, 60, true}};
+
+size_t select_lds_bytes(const SelectShape& s) {
+  return (size_t)2 * kStageBytes + (size_t)s.waves * kHistBuckets * 4 +
+         (size_t)s.waves * 4 * (64 * s.p + kRowPad) * (4 + (s.id32 ? 4 : 2));
 }
 
-int prefill_waves(int kb, size_t lds_budget) {
-  for (int wv = 8; wv >= 1; wv >>= 1)
-    if (select_lds_bytes(wv, kb) + 256 <= lds_budget) return wv;  // 256 B: static LDS
-  return 0;
+// The shape for K_B blocks out of n_blocks complete blocks, or null when none fits.
+const SelectShape* select_shape(int kb, int n_blocks) {
+  const bool id32 = n_blocks > 65536;
+  for (const SelectShape& s : kShapes)
+    if (s.id32 == id32 && 64 * s.p >= kb + 128 && select_lds_bytes(s) + kStaticLds <= kGfx950LdsBytes) return &s;
+  return nullptr;
 }
 
 }  // namespace
 
-size_t index_topk_lds_min(int kb) { return select_lds_bytes(1, kb) + 256; }
+size_t index_topk_lds_min(int kb) {
+  // Selection is possible for this K_B at every sequence length (both id widths).
+  const SelectShape* a = select_shape(kb, 1);
+  const SelectShape* b = select_shape(kb, 1 << 30);
+  if (!a || !b) return kGfx950LdsBytes + 1;
+  return select_lds_bytes(*a) + kStaticLds;
+}
 
 namespace {
 
@@ -671,33 +624,35 @@ hipError_t launch_select(const uint16_t* qi, const float* w, const uint16_t* kba
                          int n_tokens, int n_groups, int block, int kb, int tile, hipStream_t stream) {
   const long long n_rows = (long long)n_tokens * n_groups;
   if (n_rows == 0) return hipSuccess;
-  const int waves = prefill_waves(kb, (size_t)max_lds_per_block());
-  if (waves == 0) return hipErrorInvalidValue;
-  const size_t lds = select_lds_bytes(waves, kb);
-  const long long grid = (long long)n_groups * ((n_tokens + waves * 4 - 1) / (waves * 4));
+  const SelectShape* s = select_shape(kb, n_tokens / block);
+  if (!s) return hipErrorInvalidValue;
+  const size_t lds = select_lds_bytes(*s);
+  if (lds + kStaticLds > (size_t)max_lds_per_block()) return hipErrorInvalidValue;
+  const int rows_wg = s->waves * 4;
+  const long long grid = (long long)n_groups * ((n_tokens + rows_wg - 1) / rows_wg);
   const int n_tiles = (n_tokens + tile - 1) / tile;
   const int n_words = ((n_tokens + block - 1) / block + 31) / 32;
-#define SGQA_TOPK_CASE(WV)                                                                                       \
-  if (waves == WV) {                                                                                             \
-    hipLaunchKernelGGL((k_select<WV, 8, UNION>), dim3((unsigned)grid), dim3(WV * 64), lds, stream, qi, w, kbar,  \
-                       topk, n_tokens, n_groups, block, kb, umask, tile, n_tiles, n_words);                      \
+#define SGQA_SELECT_CASE(WV, PP, IDT)                                                                            \
+  if (s->waves == WV && s->p == PP && s->id32 == std::is_same<IDT, int32_t>::value) {                          \
+    hipLaunchKernelGGL((k_select<WV, PP, IDT, UNION>), dim3((unsigned)grid), dim3(WV * 64), lds, stream, qi, w, \
+                       kbar, topk, n_tokens, n_groups, block, kb, umask, tile, n_tiles, n_words);                \
     return hipGetLastError();                                                                                    \
   }
-  SGQA_TOPK_CASE(8)
-  SGQA_TOPK_CASE(4)
-  SGQA_TOPK_CASE(2)
-  SGQA_TOPK_CASE(1)
-#undef SGQA_TOPK_CASE
+  SGQA_SELECT_CASE(4, 20, uint16_t)
+  SGQA_SELECT_CASE(2, 40, uint16_t)
+  SGQA_SELECT_CASE(4, 14, int32_t)
+  SGQA_SELECT_CASE(1, 60, int32_t)
+#undef SGQA_SELECT_CASE
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t prepare_index_topk_kernels(int lds_max) {
-  const void* fns[] = {(const void*)k_select<8, 8, false>, (const void*)k_select<4, 8, false>,
-                       (const void*)k_select<2, 8, false>, (const void*)k_select<1, 8, false>,
-                       (const void*)k_select<8, 8, true>,  (const void*)k_select<4, 8, true>,
-                       (const void*)k_select<2, 8, true>,  (const void*)k_select<1, 8, true>};
+  const void* fns[] = {(const void*)k_select<4, 20, uint16_t, false>, (const void*)k_select<2, 40, uint16_t, false>,
+                       (const void*)k_select<4, 14, int32_t, false>,  (const void*)k_select<1, 60, int32_t, false>,
+                       (const void*)k_select<4, 20, uint16_t, true>,  (const void*)k_select<2, 40, uint16_t, true>,
+                       (const void*)k_select<4, 14, int32_t, true>,   (const void*)k_select<1, 60, int32_t, true>};
   for (const void* fn : fns) {
     const hipError_t e = allow_full_lds(fn, lds_max);
     if (e != hipSuccess) return e;
