@@ -40,6 +40,7 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ablation", action="store_true")
+    ap.add_argument("--no-other-prefill", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -66,6 +67,19 @@ def profiled_traffic(kernel: str, workload: str, sources):
     return None
 
 
+# The files the decode step's kernels are built from.
+DECODE_SOURCES = ("block_sparse_long_sgqa_amd/csrc/decode_select.hip", "block_sparse_long_sgqa_amd/csrc/attend.hip",
+                  "block_sparse_long_sgqa_amd/csrc/attn_common.hpp")
+
+
+def profiled_decode_traffic(workload: str):
+    """HBM bytes of one decode step (every kernel of sgqa_decode, calibrated FETCH_SIZE + WRITE_SIZE)
+    from the committed rocprofv3 summary, or None (none, or the sources changed since)."""
+    if workload != "decode_256k":
+        return None
+    return profiled_traffic("decode_step", workload, DECODE_SOURCES)
+
+
 def attended_pairs(umask, n_tokens: int, block: int, tile: int) -> int:
     """sum over (i, g) of |J(i,g)|: causally visible tokens of the tile union (exact count)."""
     import torch
@@ -82,6 +96,30 @@ def attended_pairs(umask, n_tokens: int, block: int, tile: int) -> int:
         below = torch.where(c > 0, cum[t, (c - 1).clamp(min=0)], torch.zeros_like(c, dtype=torch.int32))
         total += int((below.to(torch.int64) * block + (i - c * block + 1)).sum())
     return total
+
+
+def flush_caches(torch, scratch):
+    """Read a 1 GiB scratch buffer (a sum over it): evicts the 256 MiB last-level cache and every L2
+    so that the next kernel reads its inputs from HBM. A read, not a write: after a write the caches
+    hold dirty lines whose write-back would be charged to the timed kernel."""
+    scratch.sum()
+
+
+def cold_ms(torch, fn, reps: int, scratch) -> float:
+    """Median over reps of one call of fn with the caches flushed before it (HIP events around the
+    call alone)."""
+    times = []
+    for _ in range(reps):
+        flush_caches(torch, scratch)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    times.sort()
+    return times[len(times) // 2]
 
 
 class Timer:
@@ -156,6 +194,9 @@ def bench_prefill(sg, datagen, torch, wl, steps, warmup):
         for k, v in enumerate(tm.spans()):
             stage_ms[k] += v / steps
     same = bool(torch.equal(out_full.view(torch.int16), o["out"].view(torch.int16)))
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    union_cold_ms = cold_ms(torch, lambda: sg.sgqa_union(p, o["topk"], o["umask"], o["ucount"]), 10, scratch)
+    del scratch
     variants = bench_variants(sg, torch, p, x, o, steps, warmup)
     pairs = attended_pairs(o["umask"], p.n_tokens, p.block, p.union_tile)
     r = p.n_q_heads // p.n_kv_heads
@@ -179,10 +220,64 @@ def bench_prefill(sg, datagen, torch, wl, steps, warmup):
         "union_inflation": inflation,
         "compress_bytes": compress_bytes,
         "union_bytes": union_bytes,
+        "union_cold_ms": union_cold_ms,
         "n_blocks": n_blocks,
         "variants": variants,
         "x": x,
     }
+    return res
+
+
+def bench_prefill_light(sg, datagen, torch, wl, steps, warmup):
+    """A prefill workload other than the headline one: the whole layer through sgqa_prefill, the
+    per-stage times of the single calls, the attention's matrix-core rate and the union inflation."""
+    p = sg.Params(n_tokens=wl.n_tokens, n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads, block=wl.block,
+                  topk_tokens=wl.topk_tokens, union_tile=wl.union_tile)
+    x = datagen.prefill_inputs(wl, device="cuda")
+    o = sg.alloc_prefill_outputs(p)
+    ws = sg.workspace(p, sg.SGQA_OP_PREFILL)
+    out_full = torch.empty_like(o["out"])
+    calls = [lambda: sg.sgqa_compress(p, x["ki"], o["blk_k"]),
+             lambda: sg.sgqa_index_topk(p, x["qi"], x["w"], o["blk_k"], o["topk"]),
+             lambda: sg.sgqa_union(p, o["topk"], o["umask"], o["ucount"]),
+             lambda: sg.sgqa_attend(p, x["q"], x["k"], x["v"], o["umask"], o["ucount"], o["out"])]
+    for _ in range(warmup):
+        sg.sgqa_prefill(p, x["q"], x["k"], x["v"], x["qi"], x["w"], x["ki"], out_full, ws)
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        sg.sgqa_prefill(p, x["q"], x["k"], x["v"], x["qi"], x["w"], x["ki"], out_full, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / steps
+    stage = [0.0] * 4
+    for _ in range(steps):
+        tm = Timer(torch)
+        tm.mark()
+        for c in calls:
+            c()
+            tm.mark()
+        torch.cuda.synchronize()
+        for k, v in enumerate(tm.spans()):
+            stage[k] += v / steps
+    st = dict(zip(["compress", "index_topk", "union", "attend"], stage))
+    pairs = attended_pairs(o["umask"], p.n_tokens, p.block, p.union_tile)
+    attn_flops = 4.0 * p.head_dim * pairs * (p.n_q_heads // p.n_kv_heads)
+    index_flops = 2.0 * p.idx_heads * p.idx_dim * scored_candidates(p.n_tokens, p.block, p.n_kv_heads)
+    inflation = float((o["ucount"].double().mean() * p.block / (p.topk_tokens + p.union_tile)).item())
+    res = {"workload": wl.name, "n_tokens": p.n_tokens, "union_tile": p.union_tile, "rho": wl.rho,
+           "ms_per_step": ms_step, "tokens_per_s": p.n_tokens / (ms_step / 1e3), "stages_ms": st,
+           "attend_TFLOP_per_s": attn_flops / (st["attend"] / 1e3) / 1e12,
+           "attend_frac_of_bf16_peak": attn_flops / (st["attend"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+           "index_topk_TFLOP_per_s": index_flops / (st["index_topk"] / 1e3) / 1e12,
+           "union_inflation": inflation, "attended_pairs": pairs,
+           "prefill_matches_single_calls": bool(torch.equal(out_full.view(torch.int16), o["out"].view(torch.int16)))}
+    del x, o, ws, out_full
+    torch.cuda.empty_cache()
     return res
 
 
@@ -233,8 +328,11 @@ def bench_variants(sg, torch, p, x, o, steps, warmup):
     return res
 
 
-def bench_decode(sg, datagen, torch, steps, warmup):
-    wl = datagen.DECODE
+def bench_decode(sg, datagen, torch, steps, warmup, wl=None, extras=True):
+    """The decode step (and, with extras, the cache build, varlen/paged/FP8 decode). The roofline is
+    taken on the cold step (caches flushed before every rep: the step's 134 MB of block keys would
+    otherwise stay in the 256 MiB last-level cache between steps); the warm mean is reported too."""
+    wl = wl or datagen.DECODE
     p = sg.Params(n_tokens=wl.n_tokens, n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads, block=wl.block,
                   topk_tokens=wl.topk_tokens, union_tile=1, n_seqs=wl.n_seqs)
     t0 = time.time()
@@ -258,32 +356,43 @@ def bench_decode(sg, datagen, torch, steps, warmup):
     ev[2].record()
     torch.cuda.synchronize()
     compress_ms = ev[0].elapsed_time(ev[1]) / steps
-    step_ms = ev[1].elapsed_time(ev[2]) / steps
+    warm_ms = ev[1].elapsed_time(ev[2]) / steps
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    step_ms = cold_ms(torch, lambda: sg.sgqa_decode(p, y["q"], y["k_cache"], y["v_cache"], blk, y["qi"], y["w"], out,
+                                                    ws), max(steps, 10), scratch)
+    compress_cold_ms = cold_ms(torch, lambda: sg.sgqa_compress(p, y["ki_cache"], blk), max(steps, 10), scratch)
+    del scratch
     c = (p.n_tokens - 1) // p.block
     gather_bytes = p.n_seqs * p.n_kv_heads * (p.kb + 1) * p.block * p.head_dim * 2 * 2
     index_bytes = p.n_seqs * c * p.idx_dim * 2
     qo_bytes = 2 * p.n_seqs * p.n_q_heads * p.head_dim * 2
     step_bytes = gather_bytes + index_bytes + qo_bytes
     cache_build_bytes = p.n_seqs * p.n_tokens * p.idx_dim * 2 * (1 + 1 / p.block)
-    varlen = bench_decode_varlen(sg, torch, p, y, blk, out, ws, steps, warmup)
-    fp8 = bench_decode_fp8(sg, datagen, torch, wl, p, y, blk, out, ws, steps, warmup,
-                           gather_bytes // 2 + index_bytes + qo_bytes)
-    del y
-    return {
+    res = {
         "metric": "decode tok/s",
         "value": p.n_seqs / (step_ms / 1e3),
         "unit": "tokens/s",
         "ms_per_step": step_ms,
+        "timing": "cold: median of single steps, a 1 GiB read before each flushes the caches",
+        "warm_ms_per_step": warm_ms,
         "config": {"workload": wl.name, "n_seqs": p.n_seqs, "ctx": p.n_tokens, "n_q_heads": p.n_q_heads,
                    "n_kv_heads": p.n_kv_heads, "block": p.block, "topk_tokens": p.topk_tokens},
         "roofline": {"bound": "hbm", "achieved": step_bytes / (step_ms / 1e3) / 1e9, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": step_bytes / (step_ms / 1e3) / 1e9 / PEAK_HBM_GBS,
-                     "traffic": None, "algorithmic_bytes_per_step": step_bytes},
+                     "traffic": profiled_decode_traffic(wl.name), "algorithmic_bytes_per_step": step_bytes},
+        "warm_roofline_frac": step_bytes / (warm_ms / 1e3) / 1e9 / PEAK_HBM_GBS,
         "cache_compress": {"ms": compress_ms, "bytes": cache_build_bytes,
-                           "GB_per_s": cache_build_bytes / (compress_ms / 1e3) / 1e9},
-        "varlen": varlen,
-        "fp8": fp8,
+                           "GB_per_s": cache_build_bytes / (compress_ms / 1e3) / 1e9,
+                           "cold_ms": compress_cold_ms,
+                           "cold_GB_per_s": cache_build_bytes / (compress_cold_ms / 1e3) / 1e9},
     }
+    if extras:
+        res["varlen"] = bench_decode_varlen(sg, torch, p, y, blk, out, ws, steps, warmup)
+        res["fp8"] = bench_decode_fp8(sg, datagen, torch, wl, p, y, blk, out, ws, steps, warmup,
+                                      gather_bytes // 2 + index_bytes + qo_bytes)
+    del y
+    torch.cuda.empty_cache()
+    return res
 
 
 def scored_candidates(n_tokens: int, block: int, n_groups: int) -> int:
@@ -487,10 +596,40 @@ def bench_decode_fp8(sg, datagen, torch, wl, p, y, blk, out, ws, steps, warmup, 
             "hbm_frac": step_bytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS}
 
 
-def cpu_baseline(oracle, datagen, torch, np, res, wl):
+def host_cpu() -> dict:
+    """Model, sockets, cores and hardware threads of the host (lscpu, else /proc/cpuinfo)."""
+    import subprocess
+
+    info = {}
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            k, _, v = line.partition(":")
+            info[k.strip()] = v.strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    model = info.get("Model name")
+    if not model and os.path.exists("/proc/cpuinfo"):
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    res = {"model": model, "sockets": info.get("Socket(s)"), "cores_per_socket": info.get("Core(s) per socket"),
+           "threads_per_core": info.get("Thread(s) per core"), "cpus_online": info.get("CPU(s)") or os.cpu_count()}
+    try:
+        res["cpus_usable"] = len(os.sched_getaffinity(0))
+    except AttributeError:
+        pass
+    return res
+
+
+def cpu_baseline(oracle, datagen, torch, np, res, wl, decode_res):
     """The oracle as it is, on a bounded sample of the same prefill: whole union tiles spread over
-    the sequence (mean position ~ N/2), every group; index + top-k, union and attention of every
-    query of the sampled tiles (plus the block compression of the whole sequence)."""
+    the sequence (mean position ~ N/2), every group; each stage wall-clocked on its own (block
+    compression of the whole sequence, index + top-k of every query of the sampled tiles, the union
+    (a pass over the whole [G][N][K_B] selection array), attention of the sampled queries), with the
+    GPU's time for the same work (stage time scaled to the sampled rows) and the speed-up. Plus the
+    oracle's decode of one sequence of the decode workload against the GPU step per sequence."""
     import numpy as np  # noqa: F811
 
     p = res["p"]
@@ -507,19 +646,50 @@ def cpu_baseline(oracle, datagen, torch, np, res, wl):
     rows = np.concatenate([np.arange(t * p.union_tile, min(p.n_tokens, (t + 1) * p.union_tile)) for t in tiles])
     rows = rows.astype(np.int32)
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
+    wall = {}
     t0 = time.perf_counter()
     kbar = oracle.compress(host["ki"], p.block)
+    wall["compress"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
     sel = oracle.index_topk(host["qi"], w, kbar, p.block, p.kb, rows=rows)
+    wall["index_topk"] = time.perf_counter() - t0
     full = np.full((p.n_kv_heads, p.n_tokens, p.kb), -1, dtype=np.int32)
     full[:, rows] = sel
+    t0 = time.perf_counter()
     umask, _ = oracle.union(full, p.n_tokens, p.block, p.union_tile)
+    wall["union"] = time.perf_counter() - t0
+    del full
+    t0 = time.perf_counter()
     oracle.attend(host["q"], host["k"], host["v"], umask, p.block, p.union_tile, rows=rows)
-    dt = time.perf_counter() - t0
-    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(rows)} queries = {n_sample_tiles} whole union tiles of {p.union_tile} spread over "
-                      f"the {p.n_tokens}-token sequence (tiles {tiles}), all {p.n_kv_heads} groups and "
-                      f"{p.n_q_heads} heads; compress of all keys + index/top-k + union + attention; "
-                      f"{dt:.1f} s wall"}
+    wall["attend"] = time.perf_counter() - t0
+    dt = sum(wall.values())
+    frac = len(rows) / p.n_tokens  # the GPU's share of a stage for the sampled rows
+    st = res["stage_ms"]
+    gpu = {"compress": st["compress"] / 1e3, "index_topk": st["index_topk"] / 1e3 * frac, "union": st["union"] / 1e3,
+           "attend": st["attend"] / 1e3 * frac}
+    stages = {k: {"oracle_s": wall[k], "gpu_s": gpu[k], "speedup": wall[k] / gpu[k] if gpu[k] > 0 else None}
+              for k in wall}
+    out = {"value": len(rows) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{len(rows)} queries = {n_sample_tiles} whole union tiles of {p.union_tile} spread over "
+                     f"the {p.n_tokens}-token sequence (tiles {tiles}), all {p.n_kv_heads} groups and "
+                     f"{p.n_q_heads} heads; compress of all keys + index/top-k + union + attention; "
+                     f"{dt:.1f} s wall",
+           "stages": stages, "host": host_cpu()}
+    if decode_res is not None:
+        wl_d = datagen.DECODE
+        y = datagen.decode_inputs(wl_d, device="cuda", n_seqs=1)
+        t0 = time.perf_counter()
+        kbar_d = oracle.compress(bits(y["ki_cache"]), wl_d.block)
+        oracle.decode(bits(y["q"]), bits(y["k_cache"]), bits(y["v_cache"]), kbar_d, bits(y["qi"]), y["w"],
+                      wl_d.block, wl_d.kb)
+        dd = time.perf_counter() - t0
+        gpu_seq = decode_res["ms_per_step"] / 1e3 / decode_res["config"]["n_seqs"]
+        out["decode"] = {"oracle_s_per_sequence": dd, "gpu_s_per_sequence": gpu_seq, "speedup": dd / gpu_seq,
+                         "sample": f"1 sequence of the {wl_d.name} workload (L={wl_d.n_tokens}): block keys of the "
+                                   f"whole cache, selection and attention"}
+        del y
+        torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -591,17 +761,33 @@ def main():
             "attend_bwd_TFLOP_per_s": 2.0 * res["attn_flops"] / (res["variants"]["attend_bwd_ms"] / 1e3) / 1e12}),
         "union_inflation": res["union_inflation"],
         "attended_pairs": res["attended_pairs"],
+        "union_cold": {"ms": res["union_cold_ms"],
+                       "GB_per_s": res["union_bytes"] / (res["union_cold_ms"] / 1e3) / 1e9},
         "prefill_matches_single_calls": res["prefill_matches_single_calls"],
     }
+    decode_res = None
+    if not args.no_decode:
+        keep = {k: res[k] for k in ("p", "x", "stage_ms")}
+        del res
+        torch.cuda.empty_cache()
+        decode_res = bench_decode(sg, datagen, torch, args.steps, args.warmup)
+        line["decode"] = decode_res
+        log("decode at L=131072 (the metric's 128K context)")
+        line["decode"]["ctx_131072"] = bench_decode(sg, datagen, torch, args.steps, args.warmup,
+                                                     wl=datagen.DECODE.replace(name="decode_128k", n_tokens=131072),
+                                                     extras=False)
+        res = keep
     if not args.no_cpu_baseline:
         import oracle
 
         log("timing the CPU oracle on a bounded sample")
-        line["cpu_baseline"] = cpu_baseline(oracle, datagen, torch, np, res, wl)
+        line["cpu_baseline"] = cpu_baseline(oracle, datagen, torch, np, res, wl, decode_res)
     del res
     torch.cuda.empty_cache()
-    if not args.no_decode:
-        line["decode"] = bench_decode(sg, datagen, torch, args.steps, args.warmup)
+    if not args.no_other_prefill and wl.name == "long_prefill_128k":
+        log("other prefill workloads: 32K and the 32K i.i.d.-query stress row")
+        line["other_prefill"] = {w.name: bench_prefill_light(sg, datagen, torch, w, args.steps, args.warmup)
+                                 for w in (datagen.PREFILL, datagen.PREFILL_IID)}
     if not args.no_ablation:
         log("granularity ablation on the 32K inputs")
         line["ablation"] = bench_ablation(sg, datagen, torch, 3, 1)

@@ -127,17 +127,8 @@ __global__ __launch_bounds__(256) void k_dscore(const uint16_t* __restrict__ qi,
 
 constexpr int kBuckets = 256;
 
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor(v, off, 64));
-  return v;
-}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) { return wave_sum_dpp(v); }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) { return wave_max_dpp(v); }
 
 // Sum / maximum over the 16 lanes of each row (DPP row shifts: lane 15 of the row ends up with
 // the total), read from lane 15.

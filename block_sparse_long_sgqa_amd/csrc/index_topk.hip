@@ -62,40 +62,12 @@ constexpr float kSampleSigmas = 3.0f;
 
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// Inclusive prefix sum over the 16 lanes of each row (DPP row shifts; rows are lanes 16q..16q+15).
-__device__ __forceinline__ uint32_t row16_prefix(uint32_t v) {
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
-  return v;
-}
-
 // The value of the last lane of each 16-lane row, for every lane of the row (one DPP broadcast
 // of lane 15 within each row, row_newbcast:15).
 __device__ __forceinline__ uint32_t row16_total(uint32_t incl) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl, 0x15F, 0xF, 0xF, false);
 }
 
-// Wave-wide minimum / maximum / sum of a per-lane value, in every lane: a DPP reduction inside
-// each 16-lane row (lanes shifted in from outside the row keep their own value) and four lane
-// reads -- no LDS round trips.
-__device__ __forceinline__ uint32_t wave_min_fast(uint32_t v) {
-  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x111, 0xF, 0xF, false));
-  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x112, 0xF, 0xF, false));
-  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x114, 0xF, 0xF, false));
-  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x118, 0xF, 0xF, false));
-  return min(min((uint32_t)__builtin_amdgcn_readlane((int)v, 15), (uint32_t)__builtin_amdgcn_readlane((int)v, 31)),
-             min((uint32_t)__builtin_amdgcn_readlane((int)v, 47), (uint32_t)__builtin_amdgcn_readlane((int)v, 63)));
-}
-__device__ __forceinline__ uint32_t wave_max_fast(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x111, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x112, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x114, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x118, 0xF, 0xF, false));
-  return max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 15), (uint32_t)__builtin_amdgcn_readlane((int)v, 31)),
-             max((uint32_t)__builtin_amdgcn_readlane((int)v, 47), (uint32_t)__builtin_amdgcn_readlane((int)v, 63)));
-}
 // Sum over the lanes above this one (exclusive suffix sum), and the wave total.
 __device__ __forceinline__ uint32_t wave_suffix_excl(uint32_t v, uint32_t* total) {
   const uint32_t incl = row16_prefix(v);
@@ -139,8 +111,8 @@ __device__ __forceinline__ uint32_t kth_largest(const uint32_t (&k)[P], int K, i
     if (k[j]) mn = min(mn, k[j]);
     mx = max(mx, k[j]);
   }
-  mn = wave_min_fast(mn);
-  mx = wave_max_fast(mx);
+  mn = wave_min_dpp(mn);
+  mx = wave_max_dpp(mx);
   // Invariant: count(>= lo) >= K > count(>= hi) = c_hi.
   uint64_t lo = mn, hi = (uint64_t)mx + 1;
   uint32_t c_hi = 0;

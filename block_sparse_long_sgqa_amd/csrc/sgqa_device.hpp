@@ -92,26 +92,55 @@ __device__ __forceinline__ T readlane(T v, int l) {
   return __shfl(v, l, 64);
 }
 
-// Inclusive suffix sum across the 64 lanes: lane l gets sum_{l' >= l} v[l'].
-__device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    uint32_t o = __shfl_down(v, off, 64);
-    if (l + off < 64) v += o;
-  }
+// Inclusive prefix sum over the 16 lanes of each row (DPP row shifts; rows are lanes 16q..16q+15;
+// lanes shifted in from outside the row contribute 0).
+__device__ __forceinline__ uint32_t row16_prefix(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
   return v;
 }
 
-// Inclusive prefix sum across the 64 lanes.
+// Inclusive prefix sum across the 64 lanes: the row prefix sums plus the totals of the rows
+// before (three lane reads) -- no LDS permutes.
 __device__ __forceinline__ uint32_t wave_prefix_sum(uint32_t v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    uint32_t o = __shfl_up(v, off, 64);
-    if (l >= off) v += o;
-  }
-  return v;
+  const uint32_t incl = row16_prefix(v);
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)incl, 15);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)incl, 31);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)incl, 47);
+  const int q = lane_id() >> 4;
+  return incl + (q > 0 ? r0 : 0u) + (q > 1 ? r1 : 0u) + (q > 2 ? r2 : 0u);
+}
+
+// Inclusive suffix sum across the 64 lanes: lane l gets sum_{l' >= l} v[l'].
+__device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t v) {
+  const uint32_t incl = wave_prefix_sum(v);
+  return (uint32_t)__builtin_amdgcn_readlane((int)incl, 63) - incl + v;
+}
+
+// Wave-wide sum / maximum of a per-lane value, in every lane: a DPP reduction inside each 16-lane
+// row and four lane reads.
+__device__ __forceinline__ uint32_t wave_sum_dpp(uint32_t v) {
+  const uint32_t incl = row16_prefix(v);
+  return (uint32_t)__builtin_amdgcn_readlane((int)incl, 15) + (uint32_t)__builtin_amdgcn_readlane((int)incl, 31) +
+         (uint32_t)__builtin_amdgcn_readlane((int)incl, 47) + (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+}
+__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x111, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x112, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x114, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x118, 0xF, 0xF, false));
+  return max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 15), (uint32_t)__builtin_amdgcn_readlane((int)v, 31)),
+             max((uint32_t)__builtin_amdgcn_readlane((int)v, 47), (uint32_t)__builtin_amdgcn_readlane((int)v, 63)));
+}
+__device__ __forceinline__ uint32_t wave_min_dpp(uint32_t v) {
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x111, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x112, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x114, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x118, 0xF, 0xF, false));
+  return min(min((uint32_t)__builtin_amdgcn_readlane((int)v, 15), (uint32_t)__builtin_amdgcn_readlane((int)v, 31)),
+             min((uint32_t)__builtin_amdgcn_readlane((int)v, 47), (uint32_t)__builtin_amdgcn_readlane((int)v, 63)));
 }
 
 // max(x of lane l, x of lane l ^ 32) in every lane, through one v_permlane32_swap (a register swap
