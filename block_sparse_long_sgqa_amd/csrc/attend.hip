@@ -57,7 +57,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
                                                        int n_groups, int block, int block_shift, int tile,
                                                        float scale_log2, int n_words, int parts, int n_pairs,
                                                        const uint32_t* __restrict__ selbits,
-                                                       float* __restrict__ lse) {
+                                                       float* __restrict__ lse, int list_cap) {
   constexpr int NT = WAVES * 64;
   constexpr int kRowsWg = WAVES * 32 * QT;
   static_assert(WAVES + 1 <= 16, "scan words");
@@ -69,7 +69,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
   __shared__ __align__(16) uint32_t mtabs[2 * kSelTableWords];  // membership tables of chunks n % 2
   __shared__ int scan[16];
   extern __shared__ __align__(16) uint8_t smem[];
-  uint16_t* list = reinterpret_cast<uint16_t*>(smem);
+  uint32_t* list = reinterpret_cast<uint32_t*>(smem);  // one segment of the block list
 
   // XCD-aware decode of the workgroup id into (pair, part).
   const int x = blockIdx.x;
@@ -91,39 +91,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
   const int i_lo = i0 + row0 / r, i_hi = i0 + row_last / r;
   const int c_hi = i_hi / block;  // no block above the last query's own block is visible
 
-  // Expand U(t,g) restricted to blocks <= c_hi into the ascending list.
-  int n_list;
-  {
-    const uint32_t* mrow = umask + ((long long)g * n_tiles + t) * n_words;
-    const int n_w = c_hi / 32 + 1;
-    const int per = (n_w + NT - 1) / NT;
-    const int w0 = threadIdx.x * per;
-    int cnt = 0;
-    for (int e = 0; e < per; ++e) {
-      const int wd = w0 + e;
-      if (wd < n_w) {
-        uint32_t m = mrow[wd];
-        if (wd == n_w - 1 && (c_hi & 31) != 31) m &= (2u << (c_hi & 31)) - 1u;
-        cnt += __popc(m);
-      }
-    }
-    int total;
-    int pos = block_exclusive_scan<NT>(cnt, scan, &total);
-    for (int e = 0; e < per; ++e) {
-      const int wd = w0 + e;
-      if (wd < n_w) {
-        uint32_t m = mrow[wd];
-        if (wd == n_w - 1 && (c_hi & 31) != 31) m &= (2u << (c_hi & 31)) - 1u;
-        while (m) {
-          const int b = __ffs(m) - 1;
-          m &= m - 1u;
-          list[pos++] = (uint16_t)(wd * 32 + b);
-        }
-      }
-    }
-    n_list = total;
-    __syncthreads();
-  }
+  // U(t,g) restricted to blocks <= c_hi as an ascending list of block ids. LDS holds a window of
+  // list_cap consecutive entries starting at rank win_lo; the window moves on at the end of a step
+  // when the next token table would need an entry past it (only unions longer than list_cap).
+  const uint32_t* mrow = umask + ((long long)g * n_tiles + t) * n_words;
+  int win_lo = 0, n_list = 0;
+  union_list_fill<NT>(mrow, c_hi, list, 0, list_cap, scan, &n_list);
+  __syncthreads();
 
   // Q operand (B of S^T): lane column = Q row (l % 32) of tile qt; 8 k-steps of 16 dims.
   bf16x8 qreg[QT][8];
@@ -168,7 +142,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
   auto tok_at = [&](int chunk, int key) __attribute__((always_inline)) -> int {
     const int kp = chunk * kKeys + key;
     if (kp >= n_keys) return -1;
-    const int tk = ((int)list[kp >> block_shift] << block_shift) + (kp & (block - 1));
+    const int tk = ((int)list[(kp >> block_shift) - win_lo] << block_shift) + (kp & (block - 1));
     return tk < n_tokens ? tk : -1;
   };
 
@@ -258,16 +232,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
       toks[(c & 3) * kKeys + threadIdx.x] = tk >= 0 ? tk : 0x7FFFFFFF;
     }
   };
-  // Chunks from n_first_masked on can hold a key above this wave's first query or past the list
-  // (tokens ascend with the chunk index); the chunks before them need no mask.
-  auto needs_mask = [&](int n) -> bool {
-    if ((n + 1) * kKeys > n_keys) return true;
-    const int last_kp = (n + 1) * kKeys - 1;
-    const int last_tok = ((int)list[last_kp >> block_shift] << block_shift) + (last_kp & (block - 1));
-    return last_tok > wave_i_min;
-  };
-  int n_first_masked = n_chunks;
-  while (n_first_masked > 0 && needs_mask(n_first_masked - 1)) --n_first_masked;
+  // A chunk needs the causal / tail mask when its last key lies above this wave's first query or
+  // past the list (tokens ascend with the chunk index): its token table's last entry says so.
+  auto needs_mask = [&](int n) -> bool { return toks[(n & 3) * kKeys + kKeys - 1] > wave_i_min; };
 
   // SEL: queries of this workgroup, membership table words per block entry, this lane's query index.
   const int nq = i_hi - i_lo + 1, nqw = (nq + 31) >> 5;
@@ -289,7 +256,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
     const int ent = n * ents + e;
     i = i_lo + qq;
     const bool ok = pp < pairs && qq < nq && ent < n_list && i < n_tokens;
-    b = ok ? (int)list[ent] : 0;
+    b = ok ? (int)list[ent - win_lo] : 0;
     return ok;
   };
   auto sel_load = [&](int n) __attribute__((always_inline)) {
@@ -337,7 +304,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
       chunk_softmax<QT, 1, true>(s, tk, st, scale_log2, true, row_pos, pb, mtabs + (n & 1) * kSelTableWords, nqw,
                                  ql, block_shift);
     } else {
-      if (n >= n_first_masked)
+      if (needs_mask(n))
         chunk_softmax<QT, 1>(s, tk, st, scale_log2, true, row_pos, pb);
       else
         chunk_softmax<QT, 0>(s, tk, st, scale_log2, false, row_pos, pb);
@@ -392,6 +359,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
       if (n + 1 < n_chunks) sel_store(n + 1);
     if constexpr (!kStaged) wait_vm();
     __syncthreads();
+    // Step n + 1 writes the token table of chunk n + 3 and builds the membership table of chunk
+    // n + 2: move the window to start at chunk n + 2 when chunk n + 3 reaches past it.
+    if (n + 3 < n_chunks && (((n + 4) * kKeys - 1) >> block_shift) >= win_lo + list_cap) {
+      int unused;
+      win_lo = ((n + 2) * kKeys) >> block_shift;
+      union_list_fill<NT>(mrow, c_hi, list, win_lo, list_cap, scan, &unused);
+      __syncthreads();
+    }
   };
   if (n_chunks > 0) {
     if constexpr (SEL) sel_load(0);
@@ -454,13 +429,21 @@ namespace {
 constexpr int kPrefillWaves = 8;
 constexpr int kPrefillQT = 1;
 
-// Dynamic LDS of the prefill kernel: the block list.
-size_t attend_lds_bytes(int list_cap) { return (size_t)list_cap * 2; }
+// Dynamic LDS of the prefill kernel: one segment of the block list, 32-bit ids. The segment holds
+// the whole union whenever N / B <= kAttnListCap (every B = 8 sequence up to 128K tokens); longer
+// unions are attended segment by segment. The cap is a multiple of the block entries of a chunk.
+constexpr int kAttnListCap = 16384;
+static_assert(kAttnStaticBytes + 4 * kAttnListCap <= kGfx950LdsBytes, "list segment fits the LDS");
+int attend_list_cap(int n_tokens, int block) {
+  const long long nbc = ((long long)n_tokens + block - 1) / block;
+  const long long cap = (nbc + 63) / 64 * 64;
+  return cap < kAttnListCap ? (int)cap : kAttnListCap;
+}
+size_t attend_lds_bytes(int list_cap) { return (size_t)list_cap * 4; }
 }  // namespace
 
 size_t attend_lds_bytes_for(int n_tokens, int block) {
-  const int nbc = (n_tokens + block - 1) / block;
-  return kAttnStaticBytes + attend_lds_bytes((nbc + 7) / 8 * 8);
+  return kAttnStaticBytes + attend_lds_bytes(attend_list_cap(n_tokens, block));
 }
 
 namespace {
@@ -479,7 +462,7 @@ hipError_t launch_attend_impl(const uint16_t* q, const uint16_t* k, const uint16
   const int n_pairs = n_tiles * n_groups;
   if (n_pairs == 0) return hipSuccess;
   if (SEL_LOADS > 0 && attend_masked_loads(n_q_heads, n_groups, block) > SEL_LOADS) return hipErrorInvalidValue;
-  const int list_cap = (nbc + 7) / 8 * 8;
+  const int list_cap = attend_list_cap(n_tokens, block);
   const size_t lds = attend_lds_bytes(list_cap);
   if (kAttnStaticBytes + lds > (size_t)max_lds_per_block()) return hipErrorInvalidValue;
   const long long grid = (long long)((n_pairs + 7) / 8) * 8 * parts;
@@ -487,7 +470,7 @@ hipError_t launch_attend_impl(const uint16_t* q, const uint16_t* k, const uint16
   auto kern = k_attend<kPrefillWaves, kPrefillQT, SEL_LOADS>;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kPrefillWaves * 64), lds, stream, q, k, v, umask, out, n_tokens,
                      n_q_heads, n_groups, block, __builtin_ctz(block), tile, scale_log2, n_words, parts, n_pairs,
-                     selbits, lse);
+                     selbits, lse, list_cap);
   return hipGetLastError();
 }
 

@@ -72,7 +72,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_bwd_dq(const uint16_t* __restric
                                                        const uint16_t* __restrict__ dout, uint16_t* __restrict__ dq,
                                                        int n_tokens, int n_q_heads, int n_groups, int block,
                                                        int block_shift, int tile, float scale, float scale_log2,
-                                                       int n_words, int parts, int n_pairs) {
+                                                       int n_words, int parts, int n_pairs, int list_cap) {
   constexpr int NT = WAVES * 64;
   constexpr int kRowsWg = WAVES * 32;
   // The two stages and the token tables are variables of their own (see the forward kernel: the
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_bwd_dq(const uint16_t* __restric
   __shared__ __align__(16) int toks[4 * kKeys];  // token tables of chunks n % 4
   __shared__ int scan[16];
   extern __shared__ __align__(16) uint8_t smem[];
-  uint16_t* list = reinterpret_cast<uint16_t*>(smem);
+  uint32_t* list = reinterpret_cast<uint32_t*>(smem);  // one segment of the block list
 
   const int x = blockIdx.x;
   const int slot = x >> 3, xcd = x & 7;
@@ -102,39 +102,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_bwd_dq(const uint16_t* __restric
   const int row_last = (row0 + kRowsWg <= tile_rows ? row0 + kRowsWg : tile_rows) - 1;
   const int c_hi = (i0 + row_last / r) / block;
 
-  // U(t,g) restricted to blocks <= c_hi, as an ascending list (as in the forward).
-  int n_list;
-  {
-    const uint32_t* mrow = umask + ((long long)g * n_tiles + t) * n_words;
-    const int n_w = c_hi / 32 + 1;
-    const int per = (n_w + NT - 1) / NT;
-    const int w0 = threadIdx.x * per;
-    int cnt = 0;
-    for (int e = 0; e < per; ++e) {
-      const int wd = w0 + e;
-      if (wd < n_w) {
-        uint32_t m = mrow[wd];
-        if (wd == n_w - 1 && (c_hi & 31) != 31) m &= (2u << (c_hi & 31)) - 1u;
-        cnt += __popc(m);
-      }
-    }
-    int total;
-    int pos = block_exclusive_scan<NT>(cnt, scan, &total);
-    for (int e = 0; e < per; ++e) {
-      const int wd = w0 + e;
-      if (wd < n_w) {
-        uint32_t m = mrow[wd];
-        if (wd == n_w - 1 && (c_hi & 31) != 31) m &= (2u << (c_hi & 31)) - 1u;
-        while (m) {
-          const int b = __ffs(m) - 1;
-          m &= m - 1u;
-          list[pos++] = (uint16_t)(wd * 32 + b);
-        }
-      }
-    }
-    n_list = total;
-    __syncthreads();
-  }
+  // U(t,g) restricted to blocks <= c_hi: a window of list_cap entries from rank win_lo, moved on
+  // at the end of a step when the next token table needs an entry past it (as in the forward).
+  const uint32_t* mrow = umask + ((long long)g * n_tiles + t) * n_words;
+  int win_lo = 0, n_list = 0;
+  union_list_fill<NT>(mrow, c_hi, list, 0, list_cap, scan, &n_list);
+  __syncthreads();
 
   // This lane's Q row (column l % 32 of the wave's tile): Q and dO as B operands, lse and delta.
   const int row = row0 + wave * 32 + (l & 31);
@@ -175,7 +148,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_bwd_dq(const uint16_t* __restric
   auto tok_at = [&](int chunk, int key) -> int {
     const int kp = chunk * kKeys + key;
     if (kp >= n_keys) return -1;
-    const int tk = ((int)list[kp >> block_shift] << block_shift) + (kp & (block - 1));
+    const int tk = ((int)list[(kp >> block_shift) - win_lo] << block_shift) + (kp & (block - 1));
     return tk < n_tokens ? tk : -1;
   };
   // Gather of one chunk into a stage, staged through registers: 16 K and 16 V wave-wide 16-byte
@@ -289,6 +262,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_bwd_dq(const uint16_t* __restric
     chunk(P ? stage1 : stage0, toks + (n & 3) * kKeys);
     if (n + 1 < n_chunks) store_chunk(P ? stage0 : stage1);
     __syncthreads();
+    // Step n + 1 writes the token table of chunk n + 3: move the window to start at chunk n + 2
+    // when chunk n + 3 reaches past it.
+    if (n + 3 < n_chunks && (((n + 4) * kKeys - 1) >> block_shift) >= win_lo + list_cap) {
+      int unused;
+      win_lo = ((n + 2) * kKeys) >> block_shift;
+      union_list_fill<NT>(mrow, c_hi, list, win_lo, list_cap, scan, &unused);
+      __syncthreads();
+    }
   };
   write_tokens(0);
   write_tokens(1);
@@ -657,10 +638,15 @@ __global__ __launch_bounds__(kBwdWaves * 64) void k_bwd_dkdv(const uint16_t* __r
 // Static LDS of the dq kernel (two stages, four token tables, scan words) and its dynamic part (the
 // block list).
 constexpr size_t kDqStaticBytes = 2 * (size_t)kDqStageBytes + 4 * kKeys * 4 + 64;
-size_t attend_bwd_dq_list_bytes(int n_tokens, int block) {
-  const int nbc = (n_tokens + block - 1) / block;
-  return (size_t)((nbc + 7) / 8 * 8) * 2;
+// One segment of the block list (32-bit ids), as in the forward; a multiple of a chunk's entries.
+constexpr int kDqListCap = 12288;
+static_assert(kDqStaticBytes + 4 * kDqListCap <= kGfx950LdsBytes, "list segment fits the LDS");
+int dq_list_cap(int n_tokens, int block) {
+  const long long nbc = ((long long)n_tokens + block - 1) / block;
+  const long long cap = (nbc + 63) / 64 * 64;
+  return cap < kDqListCap ? (int)cap : kDqListCap;
 }
+size_t attend_bwd_dq_list_bytes(int n_tokens, int block) { return (size_t)dq_list_cap(n_tokens, block) * 4; }
 size_t attend_bwd_lds_dq(int n_tokens, int block) {
   return kDqStaticBytes + attend_bwd_dq_list_bytes(n_tokens, block);
 }
@@ -697,7 +683,7 @@ hipError_t launch_attend_bwd(const uint16_t* q, const uint16_t* k, const uint16_
     auto kern = k_bwd_dq<kDqWaves>;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kDqWaves * 64), lds, stream, q, k, v, umask, lse, delta,
                        dout, dq, n_tokens, n_q_heads, n_groups, block, __builtin_ctz(block), tile, scale,
-                       scale_log2, n_words, parts, n_pairs);
+                       scale_log2, n_words, parts, n_pairs, dq_list_cap(n_tokens, block));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -313,6 +313,56 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
   return before + incl - v;
 }
 
+// The union U(t,g) restricted to blocks <= c_hi, handed out as ascending lists of absolute block
+// ids in segments of at most `cap` entries, so that the LDS list has a fixed size however long the
+// sequence is (a tile's union can hold tens of thousands of blocks at a 1M-token context).
+// union_list_fill writes the ids of ranks [lo, lo + cap) (rank = position in the whole ascending
+// list) to list[0 ..), sets *total to the size of the whole list (wave-uniform) and returns how
+// many ids it wrote. Every thread owns consecutive words of the mask row and finds the rank of
+// its first set bit with a workgroup scan on each call, so nothing per thread is kept between
+// segments. The caller syncs the workgroup before the list is read, and after the last read
+// before the next fill.
+template <int NT>
+__device__ __forceinline__ int union_list_fill(const uint32_t* mrow, int c_hi, uint32_t* list, int lo, int cap,
+                                               int* scan, int* total) {
+  const int n_w = c_hi / 32 + 1;
+  const int per = (n_w + NT - 1) / NT;
+  const int w0 = (int)threadIdx.x * per;
+  auto word = [&](int wd) __attribute__((always_inline)) -> uint32_t {
+    uint32_t m = mrow[wd];
+    if (wd == n_w - 1 && (c_hi & 31) != 31) m &= (2u << (c_hi & 31)) - 1u;
+    return m;
+  };
+  int cnt = 0;
+  for (int e = 0; e < per; ++e) {
+    const int wd = w0 + e;
+    if (wd < n_w) cnt += __popc(word(wd));
+  }
+  int all;
+  int rank = block_exclusive_scan<NT>(cnt, scan, &all);
+  all = __builtin_amdgcn_readfirstlane(all);
+  *total = all;
+  const int hi = lo + cap;
+  for (int e = 0; e < per && rank < hi; ++e) {
+    const int wd = w0 + e;
+    if (wd >= n_w) break;
+    uint32_t m = word(wd);
+    const int c = __popc(m);
+    if (rank + c <= lo) {
+      rank += c;
+      continue;
+    }
+    while (m && rank < hi) {
+      const int b = __ffs(m) - 1;
+      m &= m - 1u;
+      if (rank >= lo) list[rank - lo] = (uint32_t)(wd * 32 + b);
+      ++rank;
+    }
+  }
+  const int left = all - lo;
+  return left < cap ? left : cap;
+}
+
 }  // namespace
 
 }  // namespace sgqa

@@ -140,8 +140,7 @@ int check_params(const sgqa_params* p, int need, bool prefill) {
     if (p->n_q_heads / p->n_kv_heads > 16) return SGQA_ERR_SHAPE;
   }
   if (need & NEED_LIST) {
-    // Prefill attention keeps the tile's ascending block list as 16-bit ids in LDS.
-    if ((long long)(p->n_tokens + p->block - 1) / p->block > 32768) return SGQA_ERR_SHAPE;
+    // Prefill attention walks the tile's block list in fixed-size LDS segments (any length).
     if (attend_lds_bytes_for(p->n_tokens, p->block) > kGfx950LdsBytes) return SGQA_ERR_SHAPE;
   }
   return SGQA_OK;

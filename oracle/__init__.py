@@ -52,6 +52,8 @@ def _load():
         lib.orc_attend.restype = None
         lib.orc_attend_bwd.argtypes = [I, I, I, I, I, I, D, P, P, P, P, P, P, P, P]
         lib.orc_attend_bwd.restype = None
+        lib.orc_attend_bwd_part.argtypes = [I, I, I, I, I, I, D, P, P, P, P, P, I, P, P, I, I, I, P, P]
+        lib.orc_attend_bwd_part.restype = None
         lib.orc_attend_sel.argtypes = [I, I, I, I, I, I, D, P, P, P, P, I, P, P]
         lib.orc_attend_sel.restype = None
         lib.orc_decode.argtypes = [I, I, I, I, I, I, I, I, I, D, P, P, P, P, P, P, I, P, P, P]
@@ -224,6 +226,29 @@ def attend_bwd(q, k, v, umask, dout, block: int, tile: int, scale: float = 0.0):
     _load().orc_attend_bwd(N, Hq, G, D, block, tile, float(scale), _p(q), _p(k), _p(v), _p(umask), _p(dout),
                            _p(dq), _p(dk), _p(dv))
     return dq, dk, dv
+
+
+def attend_bwd_part(q, k, v, umask, dout, block: int, tile: int, rows, g0: int, key_lo: int, key_hi: int,
+                    scale: float = 0.0):
+    """attend_bwd() on a subset: dq of the listed rows [len(rows)][Hq][D], and dk, dv of group g0's
+    keys key_lo .. key_hi - 1 [key_hi - key_lo][D] over every row that attends them (fp64)."""
+    q = _u16(q)
+    k = _u16(k)
+    v = _u16(v)
+    dout = _u16(dout)
+    umask = np.ascontiguousarray(umask, dtype=np.uint32)
+    rows = _i32(rows)
+    N, Hq, D = q.shape
+    G = k.shape[0]
+    assert 0 <= g0 < G and 0 <= key_lo <= key_hi <= N
+    nr = int(rows.shape[0])
+    dq = np.empty((nr, Hq, D), dtype=np.float64)
+    nk = key_hi - key_lo
+    dk = np.empty((max(nk, 1), D), dtype=np.float64)
+    dv = np.empty((max(nk, 1), D), dtype=np.float64)
+    _load().orc_attend_bwd_part(N, Hq, G, D, block, tile, float(scale), _p(q), _p(k), _p(v), _p(umask), _p(dout),
+                                nr, _p(rows), _p(dq), g0, key_lo, key_hi, _p(dk), _p(dv))
+    return dq, dk[:nk], dv[:nk]
 
 
 def attend_sel(q, k, v, topk, block: int, scale: float = 0.0, rows=None) -> np.ndarray:

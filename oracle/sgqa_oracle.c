@@ -16,7 +16,8 @@
  *     the pages' FP8 KV cache (deployment notes)  -> orc_fp8_e4m3_to_f64, orc_decode_f8
  *     training use of Sparse GQA (the pages train
  *     with it; the gradient is that of the same
- *     attention)                                  -> orc_attend_bwd
+ *     attention)                                  -> orc_attend_bwd, orc_attend_bwd_part (the
+ *                                                    same gradient on sampled rows / keys)
  *     "Efficient implementation ..." read as
  *     scheduling only (each query keeps its own
  *     selection)                                  -> orc_attend_sel
@@ -299,9 +300,82 @@ void orc_attend_sel(int N, int Hq, int G, int D, int B, int KB, double scale, co
  *   dv_j += p_j * dout_i,   dp_j = <dout_i, v_j>,   ds_j = p_j * (dp_j - <dout_i, o_i>),
  *   dq_i += scale * sum_j ds_j k_j,   dk_j += scale * ds_j q_i
  * (the gradient of softmax attention, with the heads of a group summed into its K/V gradients).
- * Outputs fp64: dq [N][Hq][D], dk, dv [G][N][D]. Two passes, each over independent outputs: per row
- * (softmax max, denominator, delta = <dout_i, o_i>, and dq_i), then per key (dk_j, dv_j summed over
- * the rows whose set holds j, in ascending row order). */
+ * Two kinds of independent outputs: per row (softmax max, denominator, delta = <dout_i, o_i>, and
+ * dq_i), then per key (dk_j, dv_j summed over the rows whose set holds j, in ascending row order). */
+
+/* Row i's token set J(i,g) (tokens j <= i whose block is in U(tile(i), g)) into toks; returns its
+ * size. */
+static int orc_row_tokens(int i, int B, const uint32_t* mrow, int32_t* toks) {
+  int nt = 0;
+  for (int j = 0; j <= i; ++j)
+    if ((mrow[(j / B) / 32] >> ((j / B) % 32)) & 1u) toks[nt++] = j;
+  return nt;
+}
+
+/* One (row, head): qi, di = the row's q and dout (fp64), kg, vg = the group's keys and values [N][D]
+ * (fp64), toks[0..nt) its token set; lg, o: scratch of nt and D doubles. Returns the softmax
+ * maximum, denominator and delta; writes dq_i to dqi unless it is NULL. */
+static void orc_bwd_row(int D, double scale, const double* qi, const double* di, const double* kg, const double* vg,
+                        const int32_t* toks, int nt, double* lg, double* o, double* mx_out, double* den_out,
+                        double* del_out, double* dqi) {
+  double mx = -INFINITY;
+  for (int x = 0; x < nt; ++x) {
+    const double* kr = kg + (size_t)toks[x] * D;
+    double dot = 0.0;
+    for (int d = 0; d < D; ++d) dot += qi[d] * kr[d];
+    lg[x] = scale * dot;
+    if (lg[x] > mx) mx = lg[x];
+  }
+  double den = 0.0;
+  for (int x = 0; x < nt; ++x) den += exp(lg[x] - mx);
+  for (int d = 0; d < D; ++d) o[d] = 0.0;
+  for (int x = 0; x < nt; ++x) {
+    const double p = exp(lg[x] - mx) / den;
+    const double* vr = vg + (size_t)toks[x] * D;
+    for (int d = 0; d < D; ++d) o[d] += p * vr[d];
+  }
+  double delta = 0.0;
+  for (int d = 0; d < D; ++d) delta += di[d] * o[d];
+  if (dqi) {
+    for (int d = 0; d < D; ++d) dqi[d] = 0.0;
+    for (int x = 0; x < nt; ++x) {
+      const double p = exp(lg[x] - mx) / den;
+      const double* kr = kg + (size_t)toks[x] * D;
+      const double* vr = vg + (size_t)toks[x] * D;
+      double dp = 0.0;
+      for (int d = 0; d < D; ++d) dp += di[d] * vr[d];
+      const double ds = p * (dp - delta);
+      for (int d = 0; d < D; ++d) dqi[d] += scale * ds * kr[d];
+    }
+  }
+  *mx_out = mx;
+  *den_out = den;
+  *del_out = delta;
+}
+
+/* Row i's (head's) term in key j's gradients, from the row's statistics. */
+static void orc_bwd_key_term(int D, double scale, const double* qi, const double* di, const double* kr,
+                             const double* vr, double mx, double den, double delta, double* dkj, double* dvj) {
+  double dot = 0.0, dp = 0.0;
+  for (int d = 0; d < D; ++d) {
+    dot += qi[d] * kr[d];
+    dp += di[d] * vr[d];
+  }
+  const double p = exp(scale * dot - mx) / den;
+  const double ds = p * (dp - delta);
+  for (int d = 0; d < D; ++d) {
+    dvj[d] += p * di[d];
+    dkj[d] += scale * ds * qi[d];
+  }
+}
+
+static double* orc_to_f64(const uint16_t* a, size_t n) {
+  double* f = (double*)malloc(sizeof(double) * n);
+  for (size_t x = 0; x < n; ++x) f[x] = orc_bf16_to_f64(a[x]);
+  return f;
+}
+
+/* Outputs fp64: dq [N][Hq][D], dk, dv [G][N][D]. */
 void orc_attend_bwd(int N, int Hq, int G, int D, int B, int Tq, double scale, const uint16_t* q, const uint16_t* k,
                     const uint16_t* v, const uint32_t* umask, const uint16_t* dout, double* dq, double* dk,
                     double* dv) {
@@ -311,22 +385,14 @@ void orc_attend_bwd(int N, int Hq, int G, int D, int B, int Tq, double scale, co
   int r = Hq / G;
   if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
   size_t nq = (size_t)N * Hq * D, nk = (size_t)G * N * D;
-  double* qf = (double*)malloc(sizeof(double) * nq);
-  double* of = (double*)malloc(sizeof(double) * nq);  /* dout */
-  double* kf = (double*)malloc(sizeof(double) * nk);
-  double* vf = (double*)malloc(sizeof(double) * nk);
+  double* qf = orc_to_f64(q, nq);
+  double* of = orc_to_f64(dout, nq);
+  double* kf = orc_to_f64(k, nk);
+  double* vf = orc_to_f64(v, nk);
   double* rmax = (double*)malloc(sizeof(double) * (size_t)N * Hq);
   double* rden = (double*)malloc(sizeof(double) * (size_t)N * Hq);
   double* rdel = (double*)malloc(sizeof(double) * (size_t)N * Hq);
-  for (size_t x = 0; x < nq; ++x) {
-    qf[x] = orc_bf16_to_f64(q[x]);
-    of[x] = orc_bf16_to_f64(dout[x]);
-  }
-  for (size_t x = 0; x < nk; ++x) {
-    kf[x] = orc_bf16_to_f64(k[x]);
-    vf[x] = orc_bf16_to_f64(v[x]);
-  }
-  /* pass 1: rows */
+  /* rows */
 #pragma omp parallel for schedule(dynamic, 1)
   for (int i = 0; i < N; ++i) {
     int t = i / Tq;
@@ -334,53 +400,18 @@ void orc_attend_bwd(int N, int Hq, int G, int D, int B, int Tq, double scale, co
     int32_t* toks = (int32_t*)malloc(sizeof(int32_t) * (size_t)(i + 1));
     double* o = (double*)malloc(sizeof(double) * (size_t)D);
     for (int g = 0; g < G; ++g) {
-      const uint32_t* m = umask + ((size_t)g * T + t) * W;
-      int nt = 0;
-      for (int j = 0; j <= i; ++j)
-        if ((m[(j / B) / 32] >> ((j / B) % 32)) & 1u) toks[nt++] = j;
+      const int nt = orc_row_tokens(i, B, umask + ((size_t)g * T + t) * W, toks);
       for (int hh = 0; hh < r; ++hh) {
-        int h = g * r + hh;
-        const double* qi = qf + ((size_t)i * Hq + h) * D;
-        const double* di = of + ((size_t)i * Hq + h) * D;
-        double mx = -INFINITY;
-        for (int x = 0; x < nt; ++x) {
-          const double* kr = kf + ((size_t)g * N + toks[x]) * D;
-          double dot = 0.0;
-          for (int d = 0; d < D; ++d) dot += qi[d] * kr[d];
-          lg[x] = scale * dot;
-          if (lg[x] > mx) mx = lg[x];
-        }
-        double den = 0.0;
-        for (int x = 0; x < nt; ++x) den += exp(lg[x] - mx);
-        for (int d = 0; d < D; ++d) o[d] = 0.0;
-        for (int x = 0; x < nt; ++x) {
-          const double p = exp(lg[x] - mx) / den;
-          const double* vr = vf + ((size_t)g * N + toks[x]) * D;
-          for (int d = 0; d < D; ++d) o[d] += p * vr[d];
-        }
-        double delta = 0.0;
-        for (int d = 0; d < D; ++d) delta += di[d] * o[d];
-        double* dqi = dq + ((size_t)i * Hq + h) * D;
-        for (int d = 0; d < D; ++d) dqi[d] = 0.0;
-        for (int x = 0; x < nt; ++x) {
-          const double p = exp(lg[x] - mx) / den;
-          const double* kr = kf + ((size_t)g * N + toks[x]) * D;
-          const double* vr = vf + ((size_t)g * N + toks[x]) * D;
-          double dp = 0.0;
-          for (int d = 0; d < D; ++d) dp += di[d] * vr[d];
-          const double ds = p * (dp - delta);
-          for (int d = 0; d < D; ++d) dqi[d] += scale * ds * kr[d];
-        }
-        rmax[(size_t)i * Hq + h] = mx;
-        rden[(size_t)i * Hq + h] = den;
-        rdel[(size_t)i * Hq + h] = delta;
+        const size_t ih = (size_t)i * Hq + g * r + hh;
+        orc_bwd_row(D, scale, qf + ih * D, of + ih * D, kf + (size_t)g * N * D, vf + (size_t)g * N * D, toks, nt, lg,
+                    o, &rmax[ih], &rden[ih], &rdel[ih], dq + ih * D);
       }
     }
     free(lg);
     free(toks);
     free(o);
   }
-  /* pass 2: keys */
+  /* keys */
 #pragma omp parallel for collapse(2) schedule(dynamic, 16)
   for (int g = 0; g < G; ++g) {
     for (int j = 0; j < N; ++j) {
@@ -397,26 +428,124 @@ void orc_attend_bwd(int N, int Hq, int G, int D, int B, int Tq, double scale, co
         const uint32_t* m = umask + ((size_t)g * T + i / Tq) * W;
         if (!((m[b / 32] >> (b % 32)) & 1u)) continue;
         for (int hh = 0; hh < r; ++hh) {
-          int h = g * r + hh;
-          const double* qi = qf + ((size_t)i * Hq + h) * D;
-          const double* di = of + ((size_t)i * Hq + h) * D;
-          double dot = 0.0, dp = 0.0;
-          for (int d = 0; d < D; ++d) {
-            dot += qi[d] * kr[d];
-            dp += di[d] * vr[d];
-          }
-          const double p = exp(scale * dot - rmax[(size_t)i * Hq + h]) / rden[(size_t)i * Hq + h];
-          const double ds = p * (dp - rdel[(size_t)i * Hq + h]);
-          for (int d = 0; d < D; ++d) {
-            dvj[d] += p * di[d];
-            dkj[d] += scale * ds * qi[d];
-          }
+          const size_t ih = (size_t)i * Hq + g * r + hh;
+          orc_bwd_key_term(D, scale, qf + ih * D, of + ih * D, kr, vr, rmax[ih], rden[ih], rdel[ih], dkj, dvj);
         }
       }
     }
   }
   free(qf);
   free(of);
+  free(kf);
+  free(vf);
+  free(rmax);
+  free(rden);
+  free(rdel);
+}
+
+/* The same gradient on a subset, where the whole one is out of reach: dq of the rows rows[0..nr)
+ * (dq_rows [nr][Hq][D]), and dk, dv of group g0's keys key_lo .. key_hi - 1 (dk_keys, dv_keys
+ * [key_hi - key_lo][D]) summed over every row that attends them, in ascending row order. Each
+ * output is computed term for term as in orc_attend_bwd, with the statistics of only the rows it
+ * needs. */
+void orc_attend_bwd_part(int N, int Hq, int G, int D, int B, int Tq, double scale, const uint16_t* q,
+                         const uint16_t* k, const uint16_t* v, const uint32_t* umask, const uint16_t* dout, int nr,
+                         const int32_t* rows, double* dq_rows, int g0, int key_lo, int key_hi, double* dk_keys,
+                         double* dv_keys) {
+  int T = (N + Tq - 1) / Tq;
+  int NBc = (N + B - 1) / B;
+  int W = (NBc + 31) / 32;
+  int r = Hq / G;
+  if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
+  size_t nk = (size_t)G * N * D;
+  double* kf = orc_to_f64(k, nk);
+  double* vf = orc_to_f64(v, nk);
+  /* dq rows */
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int x = 0; x < nr; ++x) {
+    const int i = rows[x], t = i / Tq;
+    double* lg = (double*)malloc(sizeof(double) * (size_t)(i + 1));
+    int32_t* toks = (int32_t*)malloc(sizeof(int32_t) * (size_t)(i + 1));
+    double* buf = (double*)malloc(sizeof(double) * (size_t)3 * D);
+    for (int g = 0; g < G; ++g) {
+      const int nt = orc_row_tokens(i, B, umask + ((size_t)g * T + t) * W, toks);
+      for (int hh = 0; hh < r; ++hh) {
+        const size_t ih = (size_t)i * Hq + g * r + hh;
+        for (int d = 0; d < D; ++d) {
+          buf[d] = orc_bf16_to_f64(q[ih * D + d]);
+          buf[D + d] = orc_bf16_to_f64(dout[ih * D + d]);
+        }
+        double mx, den, del;
+        orc_bwd_row(D, scale, buf, buf + D, kf + (size_t)g * N * D, vf + (size_t)g * N * D, toks, nt, lg, buf + 2 * D,
+                    &mx, &den, &del, dq_rows + ((size_t)x * Hq + g * r + hh) * D);
+      }
+    }
+    free(lg);
+    free(toks);
+    free(buf);
+  }
+  if (key_hi <= key_lo) {
+    free(kf);
+    free(vf);
+    return;
+  }
+  /* statistics of group g0's rows i >= key_lo whose tile union holds a block of the key range */
+  const int nrow = N - key_lo, b_lo = key_lo / B, b_hi = (key_hi - 1) / B;
+  double* rmax = (double*)malloc(sizeof(double) * (size_t)nrow * r);
+  double* rden = (double*)malloc(sizeof(double) * (size_t)nrow * r);
+  double* rdel = (double*)malloc(sizeof(double) * (size_t)nrow * r);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int i = key_lo; i < N; ++i) {
+    const uint32_t* m = umask + ((size_t)g0 * T + i / Tq) * W;
+    int hit = 0;
+    for (int b = b_lo; b <= b_hi; ++b) hit |= (int)((m[b / 32] >> (b % 32)) & 1u);
+    if (!hit) continue;
+    double* lg = (double*)malloc(sizeof(double) * (size_t)(i + 1));
+    int32_t* toks = (int32_t*)malloc(sizeof(int32_t) * (size_t)(i + 1));
+    double* buf = (double*)malloc(sizeof(double) * (size_t)3 * D);
+    const int nt = orc_row_tokens(i, B, m, toks);
+    for (int hh = 0; hh < r; ++hh) {
+      const size_t ih = (size_t)i * Hq + g0 * r + hh;
+      const size_t sx = (size_t)(i - key_lo) * r + hh;
+      for (int d = 0; d < D; ++d) {
+        buf[d] = orc_bf16_to_f64(q[ih * D + d]);
+        buf[D + d] = orc_bf16_to_f64(dout[ih * D + d]);
+      }
+      orc_bwd_row(D, scale, buf, buf + D, kf + (size_t)g0 * N * D, vf + (size_t)g0 * N * D, toks, nt, lg, buf + 2 * D,
+                  &rmax[sx], &rden[sx], &rdel[sx], NULL);
+    }
+    free(lg);
+    free(toks);
+    free(buf);
+  }
+  /* the keys */
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int j = key_lo; j < key_hi; ++j) {
+    const double* kr = kf + ((size_t)g0 * N + j) * D;
+    const double* vr = vf + ((size_t)g0 * N + j) * D;
+    double* dkj = dk_keys + (size_t)(j - key_lo) * D;
+    double* dvj = dv_keys + (size_t)(j - key_lo) * D;
+    double* buf = (double*)malloc(sizeof(double) * (size_t)2 * D);
+    for (int d = 0; d < D; ++d) {
+      dkj[d] = 0.0;
+      dvj[d] = 0.0;
+    }
+    const int b = j / B;
+    for (int i = j; i < N; ++i) {
+      const uint32_t* m = umask + ((size_t)g0 * T + i / Tq) * W;
+      if (!((m[b / 32] >> (b % 32)) & 1u)) continue;
+      for (int hh = 0; hh < r; ++hh) {
+        const size_t ih = (size_t)i * Hq + g0 * r + hh;
+        const size_t sx = (size_t)(i - key_lo) * r + hh;
+        for (int d = 0; d < D; ++d) {
+          buf[d] = orc_bf16_to_f64(q[ih * D + d]);
+          buf[D + d] = orc_bf16_to_f64(dout[ih * D + d]);
+        }
+        orc_bwd_key_term(D, scale, buf, buf + D, kr, vr, rmax[sx], rden[sx], rdel[sx], dkj, dvj);
+      }
+    }
+    free(buf);
+  }
   free(kf);
   free(vf);
   free(rmax);

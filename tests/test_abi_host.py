@@ -79,7 +79,7 @@ def test_workspace_sizes_match_layout(sg):
     dict(head_dim=64), dict(idx_heads=3), dict(idx_dim=32), dict(block=3), dict(block=128),
     dict(topk_tokens=100), dict(topk_tokens=0), dict(topk_tokens=8 * 4096), dict(n_q_heads=60),
     dict(union_tile=0), dict(n_tokens=0), dict(n_seqs=2), dict(n_kv_heads=0),
-    dict(n_q_heads=8 * 32, n_kv_heads=8), dict(n_tokens=32768 * 8 + 8),
+    dict(n_q_heads=8 * 32, n_kv_heads=8),
 ])
 def test_bad_shapes_are_rejected_before_any_launch(sg, kw):
     p = _p(**kw)
@@ -91,6 +91,20 @@ def test_bad_shapes_are_rejected_before_any_launch(sg, kw):
     a = ctypes.c_void_p((ctypes.addressof(buf) + 15) // 16 * 16)
     st = sg.lib().sgqa_prefill(ctypes.byref(p.c()), a, a, a, a, a, a, a, a, 1 << 40, nul)
     assert st == sg.SGQA_ERR_SHAPE
+
+
+@pytest.mark.parametrize("n_tokens", [262144 + 8, 1 << 20])
+def test_long_context_prefill_is_accepted(sg, n_tokens):
+    # The attention kernels walk a tile's block list in fixed-size LDS segments, so no sequence
+    # length is refused for the list; the prefill workspace is the layout at that length.
+    p = _p(n_tokens=n_tokens, union_tile=128)
+    r = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    N, G = n_tokens, 8
+    T, W = (N + 127) // 128, ((N + 7) // 8 + 31) // 32
+    assert sg.workspace_size(p, sg.SGQA_OP_PREFILL) == r(N // 8 * 64 * 2) + r(G * T * W * 4) + r(G * T * 4)
+    assert sg.workspace_size(p, sg.SGQA_OP_ATTEND) == 0
+    assert sg.workspace_size(p, sg.SGQA_OP_ATTEND_BWD) == r(N * 64 * 4)
+    assert sg.workspace_size(p, sg.SGQA_OP_INDEX_TOPK) == 0
 
 
 def test_null_and_alignment_errors(sg):

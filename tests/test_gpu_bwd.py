@@ -108,34 +108,62 @@ def test_attend_bwd_matches_oracle(sg, name):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-@pytest.mark.parametrize("name", ["prefill_32k"])
-def test_attend_bwd_full_size_invariants(sg, name):
-    # At full size: sum_j dv[g][j] = sum over the group's rows of dout (each row's p sums to 1), and
-    # sum_j dk[g][j] = 0 (each row's dS sums to 0), to within the bf16 rounding of the summands.
+# Full-size checks: key ranges near the end (their rows span many tiles, so the dk/dv kernel walks
+# long tile lists) and sampled dq rows, against the oracle's gradient on that subset.
+FULL_KEYS = {"prefill_32k": 4096 - 3, "long_prefill_128k": 2048 - 3}
+
+
+@pytest.mark.parametrize("name", ["prefill_32k", "long_prefill_128k"])
+def test_attend_bwd_full_size(sg, name):
     wl = datagen.WORKLOADS[name]
     p = params_of(wl)
+    N, Hq, G, D, Tq = p.n_tokens, p.n_q_heads, p.n_kv_heads, p.head_dim, p.union_tile
     x = datagen.prefill_inputs(wl, device="cuda")
     say(f"attend_bwd {name}: selection and union")
-    umask = torch.empty((p.n_kv_heads, p.n_tiles, p.n_words), dtype=torch.int32, device="cuda")
-    ucount = torch.empty((p.n_kv_heads, p.n_tiles), dtype=torch.int32, device="cuda")
-    blk = torch.empty((p.n_tokens // p.block, p.idx_dim), dtype=torch.bfloat16, device="cuda")
+    umask = torch.empty((G, p.n_tiles, p.n_words), dtype=torch.int32, device="cuda")
+    ucount = torch.empty((G, p.n_tiles), dtype=torch.int32, device="cuda")
+    blk = torch.empty((N // p.block, p.idx_dim), dtype=torch.bfloat16, device="cuda")
     sg.sgqa_compress(p, x["ki"], blk)
     sg.sgqa_index_union(p, x["qi"], x["w"], blk, umask, ucount)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(11)
-    dout = torch.randn((p.n_tokens, p.n_q_heads, p.head_dim), generator=gen, device="cuda").to(torch.bfloat16)
+    dout = torch.randn((N, Hq, D), generator=gen, device="cuda").to(torch.bfloat16)
     say(f"attend_bwd {name}: forward + backward")
     out, lse, dq, dk, dv = run_fwd_bwd(sg, p, x, umask, ucount, dout)
-    r = p.n_q_heads // p.n_kv_heads
-    want_dv = dout.float().view(p.n_tokens, p.n_kv_heads, r, p.head_dim).sum(dim=(0, 2))  # [G][D]
+
+    # Invariants over every key: sum_j dv[g][j] = sum over the group's rows of dout (each row's p
+    # sums to 1), and sum_j dk[g][j] = 0 (each row's dS sums to 0), to within the bf16 rounding.
+    r = Hq // G
+    want_dv = dout.float().view(N, G, r, D).sum(dim=(0, 2))  # [G][D]
     got_dv = dv.float().sum(dim=1)
     dv_scale = dv.float().abs().max().item()
     err = (got_dv - want_dv).abs().max().item()
     say(f"sum dv error {err:.3e} (|dv| max {dv_scale:.3e})")
-    assert err <= 2e-3 * dv_scale * p.n_tokens ** 0.5
+    assert err <= 2e-3 * dv_scale * N ** 0.5
     got_dk = dk.float().sum(dim=1)
     dk_scale = dk.float().abs().max().item()
     err = got_dk.abs().max().item()
     say(f"sum dk {err:.3e} (|dk| max {dk_scale:.3e})")
-    assert err <= 2e-3 * dk_scale * p.n_tokens ** 0.5
+    assert err <= 2e-3 * dk_scale * N ** 0.5
     assert torch.isfinite(dq.float()).all()
+
+    # The oracle on a subset: the union of every tile the key range's rows live in, plus two early
+    # tiles for dq rows; group g0's keys key_lo .. key_lo + 63.
+    rng = np.random.default_rng(17)
+    key_lo = N - FULL_KEYS[name]
+    key_hi = key_lo + 64
+    g0 = 3
+    tiles = np.unique(np.concatenate([np.arange(key_lo // Tq, p.n_tiles), rng.integers(0, key_lo // Tq, 2)]))
+    say(f"attend_bwd {name}: oracle unions of {len(tiles)} tiles")
+    ch = OracleChain({k: x[k].cpu() for k in ("qi", "ki", "w")}, p)
+    om, _, _, _ = ch.union_of_tiles(tiles)
+    np.testing.assert_array_equal(umask[:, torch.from_numpy(tiles).long().cuda()].cpu().numpy().view(np.uint32),
+                                  om[:, tiles])
+    rows = np.unique(np.concatenate([rng.choice(ch.tile_rows(int(t)), 2, replace=False) for t in tiles[::4]]
+                                    + [[N - 1]])).astype(np.int32)
+    say(f"attend_bwd {name}: oracle dq on {len(rows)} rows, dk/dv of group {g0} keys {key_lo}..{key_hi - 1}")
+    pq, pk, pv = oracle.attend_bwd_part(bits(x["q"]), bits(x["k"]), bits(x["v"]), om, bits(dout), p.block, Tq,
+                                        rows, g0, key_lo, key_hi)
+    assert_close_grad(dq[torch.from_numpy(rows).long().cuda()], pq, f"dq {name} sampled rows")
+    assert_close_grad(dk[g0, key_lo:key_hi], pk, f"dk {name} keys")
+    assert_close_grad(dv[g0, key_lo:key_hi], pv, f"dv {name} keys")

@@ -394,6 +394,25 @@ def test_attend_bwd_matches_torch_autograd_on_union_masks(orc):
     assert (dk[~seen] == 0).all() and (dv[~seen] == 0).all()
 
 
+def test_attend_bwd_part_equals_the_whole_gradient(orc):
+    # The subset form (sampled dq rows, one group's key range) is the full gradient's arithmetic
+    # term for term, so it must reproduce the full result exactly, for every group and for key
+    # ranges that start and end inside blocks.
+    wl, x = _small_prefill(seed_name="bwd")
+    N, B, Tq, kb = 96, 4, 8, 4
+    q, k, v = bits(x["q"]), bits(x["k"]), bits(x["v"])
+    dout = bits(torch.randn((N, 4, 128), generator=torch.Generator().manual_seed(3)).to(torch.bfloat16))
+    sel = orc.index_topk(bits(x["qi"]), x["w"].numpy(), orc.compress(bits(x["ki"]), B), B, kb)
+    umask, _ = orc.union(sel, N, B, Tq)
+    dq, dk, dv = orc.attend_bwd(q, k, v, umask, dout, B, Tq)
+    rows = np.array([0, 5, 17, 63, N - 1], dtype=np.int32)
+    for g0, lo, hi in ((0, 0, N), (1, 37, 59), (1, N - 3, N), (0, 20, 20)):
+        pq, pk, pv = orc.attend_bwd_part(q, k, v, umask, dout, B, Tq, rows, g0, lo, hi)
+        np.testing.assert_array_equal(pq, dq[rows])
+        np.testing.assert_array_equal(pk, dk[g0, lo:hi])
+        np.testing.assert_array_equal(pv, dv[g0, lo:hi])
+
+
 def test_attend_bwd_dense_equals_causal_sdpa_autograd(orc):
     wl, x = _small_prefill(N=64, Hq=4, G=2, B=8, k=64, Tq=16, seed_name="bwddense")
     q, k, v = bits(x["q"]), bits(x["k"]), bits(x["v"])
