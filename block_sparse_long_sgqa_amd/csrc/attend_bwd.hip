@@ -530,24 +530,25 @@ __global__ __launch_bounds__(kBwdWaves * 64) void k_bwd_dkdv(const uint16_t* __r
     }
   };
 
-  // Work items: the row groups, in order, of the tiles t >= the first one holding a query >= j0
-  // whose union holds one of the wave's blocks (listed a window of kTileWin tiles at a time), that
-  // reach a query >= j0.
+  // Work items: the row groups of the tiles t >= the first one holding a query >= j0 whose union
+  // holds one of the wave's blocks (listed a window of kTileWin tiles at a time), that reach a
+  // query >= j0. The tiles are walked from the last one down: the waves that start together then
+  // read the same tiles' rows at about the same time, which the caches can serve more than once.
   const int t_first = j0 / tile;
-  int tw = t_first, n_win = 0, e_win = 0, rg_next = 0;
+  int tw = n_tiles, n_win = 0, e_win = 0, rg_next = 0;  // tw: the next window ends below tile tw
   int cur_t = 0, cur_nrows = 0;  // the window entry e_win (read when e_win moves)
   uint32_t cur_bits = 0u;
   bool cur_stale = true;
   auto next_item = [&](int& it_t, int& it_rg, uint32_t& it_bits) __attribute__((always_inline)) -> bool {
     while (true) {
       if (e_win >= n_win) {
-        if (tw >= n_tiles) return false;
+        if (tw <= t_first) return false;
+        const int w_lo = tw - kTileWin > t_first ? tw - kTileWin : t_first;
         n_win = 0;
-        for (int t0 = tw; t0 < tw + kTileWin && t0 < n_tiles; t0 += 64) {
-          const int t = t0 + l;
+        for (int x0 = 0; x0 < tw - w_lo; x0 += 64) {
+          const int t = tw - 1 - (x0 + l);  // descending
           uint32_t bits = 0u;
-          if (t < n_tiles && t < tw + kTileWin)
-            bits = umask[((long long)g * n_tiles + t) * n_words + (b0 >> 5)] & wmask;
+          if (t >= w_lo) bits = umask[((long long)g * n_tiles + t) * n_words + (b0 >> 5)] & wmask;
           const uint64_t m = ballot(bits != 0u);
           if (bits) {
             const int pos = n_win + popc64(m & lanemask_lt());
@@ -557,7 +558,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void k_bwd_dkdv(const uint16_t* __r
           n_win += popc64(m);
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        tw += kTileWin;
+        tw = w_lo;
         e_win = 0;
         rg_next = 0;
         cur_stale = true;
