@@ -114,6 +114,12 @@ int check_params(const sgqa_params* p, int need, bool prefill) {
     if (p->topk_tokens < p->block || p->topk_tokens % p->block != 0) return SGQA_ERR_SHAPE;
     if (kb_of(p) > 2048) return SGQA_ERR_SHAPE;
   }
+  // Head counts first: the checks below derive r = Hq / G from them.
+  if (need & NEED_ATTN) {
+    if (p->head_dim != 128) return SGQA_ERR_SHAPE;
+    if (p->n_q_heads < 1 || p->n_q_heads % p->n_kv_heads != 0) return SGQA_ERR_SHAPE;
+    if (p->n_q_heads / p->n_kv_heads > 16) return SGQA_ERR_SHAPE;
+  }
   if (need & NEED_SELECT) {
     if (p->idx_heads != 4 || p->idx_dim != 64) return SGQA_ERR_SHAPE;
     if (p->n_kv_heads > 16) return SGQA_ERR_SHAPE;
@@ -133,11 +139,6 @@ int check_params(const sgqa_params* p, int need, bool prefill) {
   }
   if (need & NEED_UNION) {
     if (p->union_tile < 1) return SGQA_ERR_SHAPE;
-  }
-  if (need & NEED_ATTN) {
-    if (p->head_dim != 128) return SGQA_ERR_SHAPE;
-    if (p->n_q_heads < 1 || p->n_q_heads % p->n_kv_heads != 0) return SGQA_ERR_SHAPE;
-    if (p->n_q_heads / p->n_kv_heads > 16) return SGQA_ERR_SHAPE;
   }
   if (need & NEED_LIST) {
     // Prefill attention walks the tile's block list in fixed-size LDS segments (any length).
