@@ -43,6 +43,7 @@ constexpr int kScoreBlocksPerWg = kScoreBlocksPerWave * kScoreWaves;  // 512
 constexpr int kPickThreads = 1024;
 constexpr int kPickWaves = kPickThreads / 64;
 constexpr int kSegMax = kPickThreads * 32;                  // 32768 keys per pick workgroup
+constexpr int kCandCap = 8192;                              // keys listed for the exact rounds
 
 // Key row stride of the score buffer: whole score workgroups, so the pick may read up to it.
 long long score_stride(int c) { return ((long long)(c > 0 ? c : 0) + kScoreBlocksPerWg - 1) / kScoreBlocksPerWg * kScoreBlocksPerWg; }
@@ -244,6 +245,7 @@ __global__ __launch_bounds__(kPickThreads) void k_dpick(const uint32_t* __restri
   __shared__ __align__(16) uint32_t hist[2][kBuckets];
   __shared__ uint32_t scan_tot[kPickWaves];
   __shared__ uint32_t bc[2];
+  __shared__ uint32_t cand[kCandCap];  // the keys >= the lower bound of tau
   const long long row = blockIdx.x / n_seg;
   const int sg = blockIdx.x % n_seg;
   const int t = threadIdx.x, wave = t >> 6, l = lane_id();
@@ -253,13 +255,20 @@ __global__ __launch_bounds__(kPickThreads) void k_dpick(const uint32_t* __restri
   const int e0 = t * P;
 
   uint32_t k[P];
+  // Block ids of the entries (later levels), loaded with the keys: the output loop below must not
+  // load, or every one of its stores would wait for the earlier ones (one counter tracks both).
+  int32_t idv[P];
 #pragma unroll
   for (int q = 0; q < P / 4; ++q) {
     const int e = e0 + 4 * q;
-    u32x4 v = {0u, 0u, 0u, 0u};
+    u32x4 v = {0u, 0u, 0u, 0u}, vi = {0u, 0u, 0u, 0u};
     if (e < len) v = *reinterpret_cast<const u32x4*>(keys + base + e);
+    if (ids && e < len) vi = *reinterpret_cast<const u32x4*>(ids + base + e);
 #pragma unroll
-    for (int x = 0; x < 4; ++x) k[4 * q + x] = (e + x < len) ? v[x] : 0u;
+    for (int x = 0; x < 4; ++x) {
+      k[4 * q + x] = (e + x < len) ? v[x] : 0u;
+      idv[4 * q + x] = (int32_t)vi[x];
+    }
   }
   if (t < kBuckets) {
     hist[0][t] = 0u;
@@ -289,24 +298,56 @@ __global__ __launch_bounds__(kPickThreads) void k_dpick(const uint32_t* __restri
     if (kb <= kPickThreads && n_thr >= (uint32_t)kb)
       v = bucket_select(min_max > 0u ? min_max : 1u, hi0, 0u, (uint32_t)kb, hist, bc, round,
                         [&](auto&& f) { f(my_max); }, unused);
-    uint32_t gt_total;
-    tau = bucket_select(v, hi0, 0u, (uint32_t)kb, hist, bc, round,
-                        [&](auto&& f) {
+    // The keys >= v (typically one to three times K_B) are gathered into an LDS list at
+    // prefix-scan positions, so that the rounds visit only them instead of every thread's P keys;
+    // a row with more than kCandCap of them keeps the keys in registers.
+    uint32_t my_c = 0;
 #pragma unroll
-                          for (int j = 0; j < P; ++j) f(k[j]);
-                        },
-                        gt_total);
+    for (int j = 0; j < P; ++j) my_c += k[j] >= v ? 1u : 0u;
+    const uint32_t cincl = wave_prefix_sum(my_c);
+    if (l == 63) scan_tot[wave] = cincl;
+    __syncthreads();
+    uint32_t cpos = cincl - my_c, c_all = 0;
+    for (int wv = 0; wv < kPickWaves; ++wv) {
+      const uint32_t x = scan_tot[wv];
+      if (wv < wave) cpos += x;
+      c_all += x;
+    }
+    const bool listed = c_all <= (uint32_t)kCandCap;
+    if (listed && my_c != 0u) {
+#pragma unroll
+      for (int j = 0; j < P; ++j)
+        if (k[j] >= v) cand[cpos++] = k[j];
+    }
+    __syncthreads();  // the list is complete and every read of scan_tot above is done
+    uint32_t gt_total;
+    if (listed)
+      tau = bucket_select(v, hi0, 0u, (uint32_t)kb, hist, bc, round,
+                          [&](auto&& f) {
+                            for (uint32_t x = (uint32_t)t; x < c_all; x += kPickThreads) f(cand[x]);
+                          },
+                          gt_total);
+    else
+      tau = bucket_select(v, hi0, 0u, (uint32_t)kb, hist, bc, round,
+                          [&](auto&& f) {
+#pragma unroll
+                            for (int j = 0; j < P; ++j) f(k[j]);
+                          },
+                          gt_total);
     need_eq = (uint32_t)kb - gt_total;
   }
 
   // Output slot of an entry = (# above tau before it) + min(# equal to tau before it, need_eq),
   // counted in ascending id order.
-  uint32_t my_gt = 0, my_eq = 0;
+  // This thread's entries above tau and equal to tau, as bit masks (bit j = entry e0 + j).
+  static_assert(P <= 32, "entry masks are 32-bit");
+  uint32_t gtm = 0u, eqm = 0u;
 #pragma unroll
   for (int j = 0; j < P; ++j) {
-    my_gt += k[j] > tau ? 1u : 0u;
-    my_eq += (k[j] == tau && tau != 0u) ? 1u : 0u;
+    gtm |= (k[j] > tau ? 1u : 0u) << j;
+    eqm |= ((k[j] == tau && tau != 0u) ? 1u : 0u) << j;
   }
+  const uint32_t my_gt = (uint32_t)__popc(gtm), my_eq = (uint32_t)__popc(eqm);
   // Per-wave totals fit 16 bits (at most 64 P = 2048), so the wave scan runs on packed pairs.
   const uint32_t incl = wave_prefix_sum(my_gt | (my_eq << 16));
   uint32_t gt_pre = (incl & 0xFFFFu) - my_gt;
@@ -331,7 +372,30 @@ __global__ __launch_bounds__(kPickThreads) void k_dpick(const uint32_t* __restri
   uint32_t* lk = final_out ? nullptr : out_keys + (row * n_seg + sg) * out_stride;
   int32_t* li = final_out ? nullptr : out_ids + (row * n_seg + sg) * out_stride;
   const int id_base = sg * seg_len;
-  if (my_gt + my_eq != 0u) {
+  if (my_gt + my_eq != 0u && !ids && final_out) {
+    // The final selection with entry ids = entry positions: walk only the taken entries (all above
+    // tau, and the equal ones while fewer than need_eq equal entries precede them), slots from the
+    // masks.
+    const uint32_t eq_room = need_eq > eq_pre ? need_eq - eq_pre : 0u;
+    uint32_t eq_take = eqm;
+    if (my_eq > eq_room) {  // keep the lowest eq_room equal entries (eq_room < 32 here)
+      uint32_t rest = eqm;
+      for (uint32_t c = 0; c < eq_room; ++c) rest &= rest - 1u;
+      eq_take = eqm & ~rest;
+    }
+    uint32_t m = gtm | eq_take;
+    while (m) {
+      const int j = __ffs(m) - 1;
+      m &= m - 1u;
+      const uint32_t below = (1u << j) - 1u;
+      const uint32_t slot = gt_pre + (uint32_t)__popc(gtm & below) + min(eq_pre + (uint32_t)__popc(eqm & below), need_eq);
+      const int32_t id = id_base + e0 + j;
+      sel_row[slot] = id;
+      if (top_row) top_row[slot] = id;
+    }
+  } else if (my_gt + my_eq != 0u) {
+    // Segment lists (keys and ids out) and later levels (ids from the previous level's lists,
+    // loaded with the keys).
 #pragma unroll
     for (int j = 0; j < P; ++j) {
       const uint32_t kx = k[j];
@@ -348,7 +412,7 @@ __global__ __launch_bounds__(kPickThreads) void k_dpick(const uint32_t* __restri
       }
       if (take) {
         const int e = e0 + j;
-        const int32_t id = ids ? ids[base + e] : id_base + e;
+        const int32_t id = ids ? idv[j] : id_base + e;
         if (final_out) {
           sel_row[slot] = id;
           if (top_row) top_row[slot] = id;
