@@ -13,12 +13,16 @@
 //    bf16 MFMA takes A = (4 rows x 4 indexer heads) x 32 dims and B = 32 dims x 16 blocks; after
 //    the two K-steps of d_I = 64 every lane holds the 4 head dots of one (row, block) pair and
 //    forms the score locally (ReLU, weights, head sum): no cross-lane traffic, no score matrix.
-//  * Block keys stream through LDS in chunks of 128 blocks, staged through registers into
+//  * Block keys stream through LDS in chunks of 64 blocks, staged through registers into
 //    double-buffered 144-byte rows (16 B of padding spread the MFMA operand reads over all banks);
-//    each chunk feeds every row of the workgroup. Lane j of a row sees candidates 8j .. 8j+7 of a
+//    each chunk feeds every row of the workgroup. Lane j of a row sees candidates 4j .. 4j+3 of a
 //    chunk, so ascending block order is lane-major.
+//  * The selection is VALU work, and one wave per SIMD issues VALU at half the rate of two: the
+//    first shape has eight waves (32 rows) per workgroup, two per SIMD, with the row buffers sized
+//    to fit the LDS (the 64-block chunk keeps the buffer bound below small).
 //  * Exact selection in ONE streaming pass over the candidates, with a buffer per row in LDS of
-//    C >= K_B + 128 entries (order key, block id), filled in ascending block order:
+//    C >= K_B + 64 entries (order key, block id; room for K_B plus one chunk's appends), filled in
+//    ascending block order:
 //    - a strided sample of at most 512 candidates per row (the same blocks for the whole
 //      workgroup) gives a threshold tau0 with, by a margin of several standard deviations of the
 //      sample quantile, at least K_B candidates at or above it; rows with at most C candidates
@@ -31,8 +35,8 @@
 //    - a row whose sampled threshold let fewer than min(K_B, c) candidates through (a
 //      many-sigma event) runs the pass again taking every candidate;
 //    - each buffer is finally cut to its K_B best and written out (still in ascending order).
-//    A cut finds the K-th largest key by a bitwise binary search whose counts are wave ballots
-//    (no LDS atomics), then compacts the buffer in place with ballot prefix counts.
+//    A cut finds the K-th largest key by histogram rounds in the wave's own LDS scratch, then
+//    compacts the buffer in place with ballot prefix counts.
 //  * Decode selection (one query, many candidates) is shaped differently and lives on its own.
 #include <math.h>
 
@@ -48,9 +52,9 @@ namespace {
 
 constexpr int kIdxHeads = 4;
 constexpr int kIdxDim = 64;
-constexpr int kChunk = 128;                        // candidate blocks per stage
+constexpr int kChunk = 64;                         // candidate blocks per stage
 constexpr int kKRowBytes = 144;                    // 128 B block key + 16 B pad
-constexpr int kStageBytes = kChunk * kKRowBytes;   // 18432 B
+constexpr int kStageBytes = kChunk * kKRowBytes;   // 9216 B
 constexpr int kSampleCap = 512;                    // sampled candidates per row
 constexpr int kStaticLds = 256;                    // bound on the kernel's static LDS
 constexpr int kRowPad = 16;                        // pad entries after every row buffer
@@ -557,12 +561,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
 namespace {
 
 // The shapes a launch can take: WAVES waves of 4 rows, buffers of 64 P entries, 16- or 32-bit ids.
-// Each fits the gfx950 LDS with the stage; the first whose buffer holds K_B + 128 entries is used.
+// Each fits the gfx950 LDS with the stage; the first whose buffer holds K_B plus one chunk of
+// appends (K_B + kChunk entries) is used. The selection is VALU work: eight waves of one workgroup
+// (two per SIMD) issue it at twice the rate of one wave per SIMD, so the 8-wave shape comes first.
 struct SelectShape {
   int waves, p;
   bool id32;
 };
-constexpr SelectShape kShapes[] = {{4, 20, false}, {2, 40, false}, {4, 14, true}, {1, 60, true}};
+constexpr SelectShape kShapes[] = {{8, 10, false}, {4, 20, false}, {2, 40, false}, {4, 14, true}, {1, 60, true}};
 
 size_t select_lds_bytes(const SelectShape& s) {
   return (size_t)2 * kStageBytes + (size_t)s.waves * kHistBuckets * 4 +
@@ -573,7 +579,7 @@ size_t select_lds_bytes(const SelectShape& s) {
 const SelectShape* select_shape(int kb, int n_blocks) {
   const bool id32 = n_blocks > 65536;
   for (const SelectShape& s : kShapes)
-    if (s.id32 == id32 && 64 * s.p >= kb + 128 && select_lds_bytes(s) + kStaticLds <= kGfx950LdsBytes) return &s;
+    if (s.id32 == id32 && 64 * s.p >= kb + kChunk && select_lds_bytes(s) + kStaticLds <= kGfx950LdsBytes) return &s;
   return nullptr;
 }
 
@@ -610,6 +616,7 @@ hipError_t launch_select(const uint16_t* qi, const float* w, const uint16_t* kba
                        kbar, topk, n_tokens, n_groups, block, kb, umask, tile, n_tiles, n_words);                \
     return hipGetLastError();                                                                                    \
   }
+  SGQA_SELECT_CASE(8, 10, uint16_t)
   SGQA_SELECT_CASE(4, 20, uint16_t)
   SGQA_SELECT_CASE(2, 40, uint16_t)
   SGQA_SELECT_CASE(4, 14, int32_t)
@@ -621,7 +628,8 @@ hipError_t launch_select(const uint16_t* qi, const float* w, const uint16_t* kba
 }  // namespace
 
 hipError_t prepare_index_topk_kernels(int lds_max) {
-  const void* fns[] = {(const void*)k_select<4, 20, uint16_t, false>, (const void*)k_select<2, 40, uint16_t, false>,
+  const void* fns[] = {(const void*)k_select<8, 10, uint16_t, false>, (const void*)k_select<8, 10, uint16_t, true>,
+                       (const void*)k_select<4, 20, uint16_t, false>, (const void*)k_select<2, 40, uint16_t, false>,
                        (const void*)k_select<4, 14, int32_t, false>,  (const void*)k_select<1, 60, int32_t, false>,
                        (const void*)k_select<4, 20, uint16_t, true>,  (const void*)k_select<2, 40, uint16_t, true>,
                        (const void*)k_select<4, 14, int32_t, true>,   (const void*)k_select<1, 60, int32_t, true>};
