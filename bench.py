@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ablation", action="store_true")
     ap.add_argument("--no-other-prefill", action="store_true")
+    ap.add_argument("--no-1m", action="store_true", help="skip the 1M-token prefill row of the other workloads")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the decode step of the 32 x 256K workload (no variants): for the decode profiles")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -723,6 +726,13 @@ def main():
         torch.cuda.synchronize()
         del a, evict
 
+    if args.decode_only:
+        d = bench_decode(sg, datagen, torch, args.steps, args.warmup, extras=False)
+        print(json.dumps(dict(d, n_gpus=1, steps=args.steps, warmup=args.warmup, higher_is_better=True,
+                              scaling="weak", vs_baseline=None, dtype="bf16",
+                              data="synthetic (seeded; shapes and value structure of the pages' setting)")),
+              flush=True)
+        return
     res = bench_prefill(sg, datagen, torch, wl, args.steps, args.warmup)
     p = res["p"]
     st = res["stage_ms"]
@@ -788,6 +798,12 @@ def main():
         log("other prefill workloads: 32K and the 32K i.i.d.-query stress row")
         line["other_prefill"] = {w.name: bench_prefill_light(sg, datagen, torch, w, args.steps, args.warmup)
                                  for w in (datagen.PREFILL, datagen.PREFILL_IID)}
+        if not args.no_1m:
+            # The context length the pages' architecture aims at: one pass (about 2.5 s of GPU work).
+            w1m = datagen.LONG_PREFILL.replace(name="long_prefill_1m", n_tokens=1 << 20)
+            log("1M-token prefill (one timed pass)")
+            line["other_prefill"][w1m.name] = bench_prefill_light(sg, datagen, torch, w1m, 1, 1)
+            torch.cuda.empty_cache()
     if not args.no_ablation:
         log("granularity ablation on the 32K inputs")
         line["ablation"] = bench_ablation(sg, datagen, torch, 3, 1)
