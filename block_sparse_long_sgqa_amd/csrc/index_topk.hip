@@ -17,9 +17,11 @@
 //    double-buffered 144-byte rows (16 B of padding spread the MFMA operand reads over all banks);
 //    each chunk feeds every row of the workgroup. Lane j of a row sees candidates 4j .. 4j+3 of a
 //    chunk, so ascending block order is lane-major.
-//  * The selection is VALU work, and one wave per SIMD issues VALU at half the rate of two: the
-//    first shape has eight waves (32 rows) per workgroup, two per SIMD, with the row buffers sized
-//    to fit the LDS (the 64-block chunk keeps the buffer bound below small).
+//  * The selection is VALU work, and one wave per SIMD issues VALU at half the rate of two. The
+//    first shape has four waves (16 rows) per workgroup in at most 80 KiB of LDS, so two
+//    workgroups share a CU (two waves per SIMD): while the waves of one wait at a chunk barrier
+//    for a wave that is cutting its buffer, the other's keep the SIMDs busy. The 64-block chunk
+//    and 16-bit histogram counters keep the LDS that small.
 //  * Exact selection in ONE streaming pass over the candidates, with a buffer per row in LDS of
 //    C >= K_B + 64 entries (order key, block id; room for K_B plus one chunk's appends), filled in
 //    ascending block order:
@@ -29,12 +31,16 @@
 //      take every candidate instead;
 //    - the pass appends every candidate whose fp32 score is not below the row's threshold (one
 //      compare per candidate; the order key is formed only for appended ones). A chunk that
-//      would overflow a buffer first cuts it to exactly its K_B best entries (key descending,
-//      among equal keys the earliest = lowest block ids) and raises the row's threshold to
-//      "strictly above the K_B-th key": nothing below it can enter the final top-K_B any more;
+//      would overflow a buffer first cuts it: to the entries at or above a key bound t that
+//      leaves between K_B and C - 64 of them (t at or below the K_B-th key, usually found by the
+//      first histogram round), or, when ties make that impossible, to exactly its K_B best
+//      entries (key descending, among equal keys the earliest = lowest block ids) with t the
+//      K_B-th key; the row's threshold becomes "strictly above t": every candidate at or below
+//      it has K_B better ones already, so it cannot enter the final top-K_B;
 //    - a row whose sampled threshold let fewer than min(K_B, c) candidates through (a
 //      many-sigma event) runs the pass again taking every candidate;
-//    - each buffer is finally cut to its K_B best and written out (still in ascending order).
+//    - each buffer is finally cut to exactly its K_B best and written out (still in ascending
+//      order).
 //    A cut finds the K-th largest key by histogram rounds in the wave's own LDS scratch, then
 //    compacts the buffer in place with ballot prefix counts.
 //  * Decode selection (one query, many candidates) is shaped differently and lives on its own.
@@ -57,8 +63,9 @@ constexpr int kKRowBytes = 144;                    // 128 B block key + 16 B pad
 constexpr int kStageBytes = kChunk * kKRowBytes;   // 9216 B
 constexpr int kSampleCap = 512;                    // sampled candidates per row
 constexpr int kStaticLds = 256;                    // bound on the kernel's static LDS
-constexpr int kRowPad = 16;                        // pad entries after every row buffer
-constexpr int kHistBuckets = 128;                  // buckets of a select round (scratch per wave)
+constexpr int kRowPad = 1;                         // pad entry after every row buffer (bank stagger)
+constexpr int kHistBuckets = 128;                  // buckets of a select round
+constexpr int kHistWords = kHistBuckets / 2;       // 16-bit counters, two per word (scratch per wave)
 // Width of the sample margin: tau0 is the sample key with (mean + kSampleSigmas * sd + 1) sample
 // keys at or above it, mean and sd those of the number of sample keys at or above the true
 // K_B-th key.
@@ -106,8 +113,12 @@ __device__ __forceinline__ float threshold_of(uint32_t t) {
 // the live key range: every round splits it into kHistBuckets equal power-of-two buckets, counts
 // the keys of each (LDS atomics into hist, this wave's scratch; the LDS operations of one wave
 // complete in order) and keeps the bucket where the running count from the top reaches K.
+// With cap >= K the rounds may stop early, at a bucket's lower end t with K <= count(>= t) <= cap
+// (then t is a bound at or below the K-th largest key, not the key itself); *n_at gets count(>= t)
+// of the returned t when it is known to be at most cap, else a value above cap.
 template <int P>
-__device__ __forceinline__ uint32_t kth_largest(const uint32_t (&k)[P], int K, int* n_above, uint32_t* hist) {
+__device__ __forceinline__ uint32_t kth_largest(const uint32_t (&k)[P], int K, int* n_above, uint32_t* hist,
+                                                int cap = 0, int* n_at = nullptr) {
   const int l = lane_id();
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
 #pragma unroll
@@ -119,17 +130,21 @@ __device__ __forceinline__ uint32_t kth_largest(const uint32_t (&k)[P], int K, i
   mx = wave_max_dpp(mx);
   // Invariant: count(>= lo) >= K > count(>= hi) = c_hi.
   uint64_t lo = mn, hi = (uint64_t)mx + 1;
-  uint32_t c_hi = 0;
+  uint32_t c_hi = 0, c_lo = 0x7FFFFFFFu;
   while (hi - lo > 1) {
     const int bits = 64 - __clzll((long long)(hi - lo - 1));
     const int shift = bits > 7 ? bits - 7 : 0;
-    *reinterpret_cast<uint2*>(hist + 2 * l) = make_uint2(0u, 0u);
+    hist[l] = 0u;  // buckets 2l (low half) and 2l + 1 (high half)
 #pragma unroll
     for (int j = 0; j < P; ++j) {
       const uint32_t x = k[j];
-      if (x >= lo && x < hi) atomicAdd(&hist[(uint32_t)((x - lo) >> shift)], 1u);
+      if (x >= lo && x < hi) {
+        const uint32_t b = (uint32_t)((x - lo) >> shift);
+        atomicAdd(&hist[b >> 1], 1u << ((b & 1u) << 4));
+      }
     }
-    const uint2 hv = *reinterpret_cast<const uint2*>(hist + 2 * l);
+    const uint32_t hw = hist[l];
+    const uint2 hv = make_uint2(hw & 0xFFFFu, hw >> 16);
     uint32_t tot;
     const uint32_t above = wave_suffix_excl(hv.x + hv.y, &tot) + c_hi;  // count(>= bucket 2l + 2)
     const uint32_t s1 = above + hv.y, s0 = s1 + hv.x;
@@ -138,20 +153,29 @@ __device__ __forceinline__ uint32_t kth_largest(const uint32_t (&k)[P], int K, i
     const int j = s1 >= (uint32_t)K ? 1 : 0;
     const int bsel = __builtin_amdgcn_readlane(2 * l + j, ls);
     c_hi = (uint32_t)__builtin_amdgcn_readlane((int)(j ? above : s1), ls);
+    c_lo = (uint32_t)__builtin_amdgcn_readlane((int)(j ? s1 : s0), ls);  // count(>= the new lo)
     lo += (uint64_t)bsel << shift;
     const uint64_t nhi = lo + (1ull << shift);
     hi = nhi < hi ? nhi : hi;
+    if ((int)c_lo <= cap) break;
   }
   *n_above = (int)c_hi;
+  if (n_at) *n_at = (int)c_lo;
   return (uint32_t)lo;
 }
 
 // Cuts one row's buffer (fp32 score bits kb_, ids ib_; n entries in ascending block order) to its
 // K best entries -- keys descending, among equal keys the earliest -- in place and in order, with
 // the whole wave. Requires n > K >= 1 and n <= 64 P. Returns the K-th key. hist: this wave's
-// kHistBuckets words of LDS scratch.
+// kHistWords words of LDS scratch.
+// With cap > K (a cut in the middle of the stream) it may instead keep every entry whose key is at
+// least a bound t at or below the K-th key, when between K and cap entries are that large: every
+// dropped entry still has K better ones, which is all a later exact cut needs. Returns t then.
+// Either way, a candidate arriving later with a key at or below the returned value has K better
+// entries before it, and *n_kept gets the number of entries kept.
 template <int P, typename IdT>
-__device__ __forceinline__ uint32_t cut_to(uint32_t* kb_, IdT* ib_, int n, int K, uint32_t* hist) {
+__device__ __forceinline__ uint32_t cut_to(uint32_t* kb_, IdT* ib_, int n, int K, uint32_t* hist, int cap = 0,
+                                           int* n_kept = nullptr) {
   const int l = lane_id();
   uint32_t k[P], id[P];
 #pragma unroll
@@ -160,9 +184,11 @@ __device__ __forceinline__ uint32_t cut_to(uint32_t* kb_, IdT* ib_, int n, int K
     k[j] = e < n ? kept_key(kb_[e]) : 0u;
     id[j] = e < n ? (uint32_t)ib_[e] : 0u;
   }
-  int above;
-  const uint32_t tau = kth_largest(k, K, &above, hist);
-  const int need = K - above;  // entries equal to tau that stay: the first ones
+  int above, n_at;
+  const uint32_t tau = kth_largest(k, K, &above, hist, cap, &n_at);
+  const bool loose = n_at <= cap;  // keep every key >= tau
+  const int need = loose ? n : K - above;  // entries equal to tau that stay: the first ones
+  if (n_kept) *n_kept = loose ? n_at : K;
   const uint64_t lt = lanemask_lt();
   int wpos = 0, tseen = 0;
 #pragma unroll
@@ -200,10 +226,9 @@ __device__ __forceinline__ void keys_load(uint32_t (&k)[P], const uint32_t* bits
 // query ranges are launched first); candidates [0, c(i)); output the ascending ids into
 // topk [G][N][K_B] (-1 padded).
 //
-// LDS: the double-buffered stage, every wave's select scratch, then per row a buffer of C = 64 P fp32 score bits and, after all
-// rows' scores, their block ids (IdT: uint16 when every block id fits, else int32). Each row buffer
-// is followed by kRowPad pad entries: lane j of the row writes the candidates it does not keep to
-// pad entry j (the append is branch-free), and the pad staggers the rows' LDS banks.
+// LDS: the double-buffered stage, every wave's select scratch, then per row a buffer of C = 64 P
+// fp32 score bits and, after all rows' scores, their block ids (IdT: uint16 when every block id
+// fits, else int32). Row buffers are kRowPad entries apart, which staggers their LDS banks.
 //
 // UNION: instead of writing topk, every selected id and the row's own block are ORed into the
 // tile-union bitmask umask [G][T][W] (bit b % 32 of word b / 32 of row (g, floor(i / tile))), which
@@ -219,8 +244,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
   constexpr int kRowsPerWg = WAVES * 4;
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* stage = smem;  // 2 x kStageBytes
-  uint32_t* hist_lds = reinterpret_cast<uint32_t*>(smem + 2 * kStageBytes);  // WAVES x kHistBuckets
-  uint32_t* keys_lds = hist_lds + WAVES * kHistBuckets;
+  uint32_t* hist_lds = reinterpret_cast<uint32_t*>(smem + 2 * kStageBytes);  // WAVES x kHistWords
+  uint32_t* keys_lds = hist_lds + WAVES * kHistWords;
   IdT* ids_lds = reinterpret_cast<IdT*>(keys_lds + kRowsPerWg * CS);
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
@@ -329,16 +354,21 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
       if (wave + x * WAVES < kFillLoads) *reinterpret_cast<u32x4*>(stage + buf * kStageBytes + fl_lds[x]) = fill[x];
   };
   const int boff = l16 * kKRowBytes + quarter * 16;  // B operand: row l16 of a 16-block tile
-  // Scores of one staged chunk: all operand reads first, then all products, then the per-lane
-  // ReLU / weight / head sum, so that LDS and matrix-core latencies overlap across the 8 tiles.
-  auto chunk_scores = [&](const uint8_t* sb, float (&sc)[kTiles]) {
-    bf16x8 b_lo[kTiles], b_hi[kTiles];
+  // B operands of one staged chunk (every tile, both K-steps), read into registers a chunk ahead
+  // of their products: all waves read the whole stage right after a barrier, and this way that
+  // burst overlaps the previous chunk's selection work instead of delaying the products.
+  auto read_b = [&](const uint8_t* sb, bf16x8 (&b_lo)[kTiles], bf16x8 (&b_hi)[kTiles]) {
 #pragma unroll
     for (int ct = 0; ct < kTiles; ++ct) {
       const uint8_t* p = sb + ct * 16 * kKRowBytes + boff;
       b_lo[ct] = *reinterpret_cast<const bf16x8*>(p);
       b_hi[ct] = *reinterpret_cast<const bf16x8*>(p + 64);
     }
+  };
+  // Scores of one chunk: all products; then, while their results are computed, the operands of
+  // the next chunk are read into the same registers (next(), possibly nothing); then the per-lane
+  // ReLU / weight / head sum.
+  auto chunk_scores = [&](bf16x8 (&b_lo)[kTiles], bf16x8 (&b_hi)[kTiles], float (&sc)[kTiles], auto&& next) {
     f32x4 acc[kTiles];
 #pragma unroll
     for (int ct = 0; ct < kTiles; ++ct) {
@@ -347,6 +377,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
     }
 #pragma unroll
     for (int ct = 0; ct < kTiles; ++ct) acc[ct] = mfma16(a_op[1], b_hi[ct], acc[ct]);
+    next();
 #pragma unroll
     for (int ct = 0; ct < kTiles; ++ct) {
       float s = 0.0f;
@@ -360,22 +391,34 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
 #pragma unroll
   for (int off = 16; off <= 32; off <<= 1) hi_wave = min(hi_wave, __shfl_xor(hi_wave, off, 64));
   // Streams candidates v in [0, n_virt) (block lo + v * stride + off) through the double-buffered
-  // stage: chunk n+1's keys are loaded into registers at the start of step n and written to its
-  // buffer at the end (that buffer's last reads were in step n-1, before the barrier). For every
-  // chunk, body(sc, v_first, full) gets this lane's 8 scores, for candidates v_first .. v_first + 7
-  // (ascending), and whether every candidate of the wave's rows in the chunk is valid (a
-  // compile-time tag); after() runs once per chunk.
+  // stage, two chunks ahead of the products: at the start of step n the B operands of chunk n are
+  // in registers and chunk n+1 is in buffer (n+1) % 2; the step loads chunk n+2's keys into
+  // registers, issues chunk n's products, reads chunk n+1's operands into the operand registers
+  // and, after the selection work, writes chunk n+2 to buffer n % 2, whose operand reads (issued
+  // in step n-1) were waited for before the barrier that ended step n-1. The barrier at the end of
+  // the step publishes chunk n+2. For every chunk, body(sc, v_first,
+  // full) gets this lane's scores, for candidates v_first .. v_first + kTiles - 1 (ascending), and
+  // whether every candidate of the wave's rows in the chunk is valid (a compile-time tag); after()
+  // runs once per chunk.
   auto stream = [&](int n_virt, int stride, int off, auto&& body, auto&& after) {
     const int n_ch = (n_virt + kChunk - 1) / kChunk;
-    if (n_ch > 0) {
-      fetch(0, stride, off, n_virt);
-      deposit(0);
+    if (n_ch <= 0) return;
+    bf16x8 b_lo[kTiles], b_hi[kTiles];
+    fetch(0, stride, off, n_virt);
+    deposit(0);
+    if (n_ch > 1) {
+      fetch(kChunk, stride, off, n_virt);
+      deposit(1);
     }
+    __syncthreads();  // chunks 0 and 1 are staged
+    read_b(stage, b_lo, b_hi);
+    __syncthreads();  // every wave holds chunk 0's operands: buffer 0 may be refilled
     for (int n = 0; n < n_ch; ++n) {
-      __syncthreads();  // stage n is complete; the other buffer's last reader has passed
-      if (n + 1 < n_ch) fetch((n + 1) * kChunk, stride, off, n_virt);
+      if (n + 2 < n_ch) fetch((n + 2) * kChunk, stride, off, n_virt);
       float sc[kTiles];
-      chunk_scores(stage + (n & 1) * kStageBytes, sc);
+      chunk_scores(b_lo, b_hi, sc, [&]() {
+        if (n + 1 < n_ch) read_b(stage + ((n + 1) & 1) * kStageBytes, b_lo, b_hi);
+      });
       const int v_end = (n + 1) * kChunk;
       const int v_first = n * kChunk + l16 * kTiles;
       if (v_end <= n_virt && lo + (v_end - 1) * stride + off < hi_wave)
@@ -383,9 +426,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
       else
         body(sc, v_first, std::false_type());
       after();
-      if (n + 1 < n_ch) deposit((n + 1) & 1);
+      if (n + 2 < n_ch) deposit(n & 1);
+      __syncthreads();  // chunk n+2 is staged; chunk n+1's operands are in registers
     }
-    __syncthreads();  // the stage buffers are free again
   };
   // Validity of this lane's candidate v_first + ct.
   auto valid_at = [&](int v, int n_virt, int stride, int off) -> bool {
@@ -397,9 +440,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
   IdT* my_i = ids_lds + (size_t)(wave * 4 + quarter) * CS;
   auto row_k = [&](int q) { return keys_lds + (size_t)(wave * 4 + q) * CS; };
   auto row_i = [&](int q) { return ids_lds + (size_t)(wave * 4 + q) * CS; };
-  const uint32_t pad_pos = C + l16;  // this lane's pad entry
   auto nothing = [&]() {};
-  uint32_t* hist = hist_lds + wave * kHistBuckets;  // this wave's select scratch
+  uint32_t* hist = hist_lds + wave * kHistWords;  // this wave's select scratch
 
   // Row state, uniform over the row's 16 lanes: the threshold (a score s passes iff !(s < thr)),
   // the number of buffered entries, and whether the row takes part in the current pass.
@@ -428,7 +470,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
       uint32_t pos = n_cnt + incl - cnt;
 #pragma unroll
       for (int ct = 0; ct < kTiles; ++ct) {
-        my_k[f[ct] ? pos : pad_pos] = __float_as_uint(sc[ct]);
+        if (f[ct]) my_k[pos] = __float_as_uint(sc[ct]);
         pos += f[ct] ? 1u : 0u;
       }
       n_cnt += row16_total(incl);
@@ -455,8 +497,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
 
   // ------------------------------------------------------------------ the pass
   // Every candidate that passes its row's threshold is appended, in ascending block order. A
-  // chunk that would overflow a row's buffer first cuts it to the K_B best and raises the row's
-  // threshold past the K_B-th key.
+  // chunk that would overflow a row's buffer first cuts it to at most C - kChunk entries that
+  // include its K_B best, and raises the row's threshold past the cut's bound.
   auto append = [&](const float (&sc)[kTiles], int v_first, auto full_t) {
     constexpr bool kFull = decltype(full_t)::value;
     bool f[kTiles];
@@ -476,9 +518,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
       lds_wait();
       for (int q = 0; q < 4; ++q) {
         if (readlane((int)(n_cnt + tot > C), 16 * q) == 0) continue;
-        const uint32_t tau = cut_to<P, IdT>(row_k(q), row_i(q), readlane(n_cnt, 16 * q), kb, hist);
+        int kept;
+        const uint32_t tau = cut_to<P, IdT>(row_k(q), row_i(q), readlane(n_cnt, 16 * q), kb, hist, C - kChunk, &kept);
         if (quarter == q) {
-          n_cnt = kb;
+          n_cnt = kept;
           thr = tau == 0xFFFFFFFFu ? __builtin_inff() : threshold_of(tau + 1u);
         }
       }
@@ -486,14 +529,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
       incl = row16_prefix(cnt);
       tot = (int)row16_total(incl);
     }
-    // Kept candidates go to consecutive entries, the others to this lane's pad entry.
+    // Kept candidates go to consecutive entries.
     uint32_t pos = n_cnt + incl - cnt;
     const uint32_t id0 = (uint32_t)(lo + v_first);
 #pragma unroll
     for (int ct = 0; ct < kTiles; ++ct) {
-      const uint32_t e = f[ct] ? pos : pad_pos;
-      my_k[e] = __float_as_uint(sc[ct]);
-      my_i[e] = (IdT)(id0 + ct);
+      if (f[ct]) {
+        my_k[pos] = __float_as_uint(sc[ct]);
+        my_i[pos] = (IdT)(id0 + ct);
+      }
       pos += f[ct] ? 1u : 0u;
     }
     n_cnt += tot;
@@ -568,10 +612,10 @@ struct SelectShape {
   int waves, p;
   bool id32;
 };
-constexpr SelectShape kShapes[] = {{8, 10, false}, {4, 20, false}, {2, 40, false}, {4, 14, true}, {1, 60, true}};
+constexpr SelectShape kShapes[] = {{4, 10, false}, {8, 10, false}, {4, 20, false}, {2, 40, false}, {4, 14, true}, {1, 60, true}};
 
 size_t select_lds_bytes(const SelectShape& s) {
-  return (size_t)2 * kStageBytes + (size_t)s.waves * kHistBuckets * 4 +
+  return (size_t)2 * kStageBytes + (size_t)s.waves * kHistWords * 4 +
          (size_t)s.waves * 4 * (64 * s.p + kRowPad) * (4 + (s.id32 ? 4 : 2));
 }
 
@@ -616,6 +660,7 @@ hipError_t launch_select(const uint16_t* qi, const float* w, const uint16_t* kba
                        kbar, topk, n_tokens, n_groups, block, kb, umask, tile, n_tiles, n_words);                \
     return hipGetLastError();                                                                                    \
   }
+  SGQA_SELECT_CASE(4, 10, uint16_t)
   SGQA_SELECT_CASE(8, 10, uint16_t)
   SGQA_SELECT_CASE(4, 20, uint16_t)
   SGQA_SELECT_CASE(2, 40, uint16_t)
@@ -628,7 +673,8 @@ hipError_t launch_select(const uint16_t* qi, const float* w, const uint16_t* kba
 }  // namespace
 
 hipError_t prepare_index_topk_kernels(int lds_max) {
-  const void* fns[] = {(const void*)k_select<8, 10, uint16_t, false>, (const void*)k_select<8, 10, uint16_t, true>,
+  const void* fns[] = {(const void*)k_select<4, 10, uint16_t, false>, (const void*)k_select<4, 10, uint16_t, true>,
+                       (const void*)k_select<8, 10, uint16_t, false>, (const void*)k_select<8, 10, uint16_t, true>,
                        (const void*)k_select<4, 20, uint16_t, false>, (const void*)k_select<2, 40, uint16_t, false>,
                        (const void*)k_select<4, 14, int32_t, false>,  (const void*)k_select<1, 60, int32_t, false>,
                        (const void*)k_select<4, 20, uint16_t, true>,  (const void*)k_select<2, 40, uint16_t, true>,
