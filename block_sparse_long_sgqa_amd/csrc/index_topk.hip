@@ -15,13 +15,16 @@
 //    forms the score locally (ReLU, weights, head sum): no cross-lane traffic, no score matrix.
 //  * Block keys stream through LDS in chunks of 64 blocks, staged through registers into
 //    double-buffered 144-byte rows (16 B of padding spread the MFMA operand reads over all banks);
-//    each chunk feeds every row of the workgroup. Lane j of a row sees candidates 4j .. 4j+3 of a
-//    chunk, so ascending block order is lane-major.
+//    each chunk feeds every row of the workgroup, and every wave reads its operands a chunk ahead
+//    of its products. Lane j of a row sees candidates 4j .. 4j+3 of a chunk, so ascending block
+//    order is lane-major. (Loading the operands straight from the L2 cache into every wave's
+//    registers, with no stage and no barrier, measured 1.5x slower: the shared stage divides the
+//    L2 traffic by the number of waves.)
 //  * The selection is VALU work, and one wave per SIMD issues VALU at half the rate of two. The
 //    first shape has four waves (16 rows) per workgroup in at most 80 KiB of LDS, so two
 //    workgroups share a CU (two waves per SIMD): while the waves of one wait at a chunk barrier
 //    for a wave that is cutting its buffer, the other's keep the SIMDs busy. The 64-block chunk
-//    and 16-bit histogram counters keep the LDS that small.
+//    keeps the LDS that small.
 //  * Exact selection in ONE streaming pass over the candidates, with a buffer per row in LDS of
 //    C >= K_B + 64 entries (order key, block id; room for K_B plus one chunk's appends), filled in
 //    ascending block order:
@@ -32,8 +35,8 @@
 //    - the pass appends every candidate whose fp32 score is not below the row's threshold (one
 //      compare per candidate; the order key is formed only for appended ones). A chunk that
 //      would overflow a buffer first cuts it: to the entries at or above a key bound t that
-//      leaves between K_B and C - 64 of them (t at or below the K_B-th key, usually found by the
-//      first histogram round), or, when ties make that impossible, to exactly its K_B best
+//      leaves between K_B and C - 64 of them (t at or below the K_B-th key, usually found by a
+//      few probes), or, when ties make that impossible, to exactly its K_B best
 //      entries (key descending, among equal keys the earliest = lowest block ids) with t the
 //      K_B-th key; the row's threshold becomes "strictly above t": every candidate at or below
 //      it has K_B better ones already, so it cannot enter the final top-K_B;
@@ -41,8 +44,9 @@
 //      many-sigma event) runs the pass again taking every candidate;
 //    - each buffer is finally cut to exactly its K_B best and written out (still in ascending
 //      order).
-//    A cut finds the K-th largest key by histogram rounds in the wave's own LDS scratch, then
-//    compacts the buffer in place with ballot prefix counts.
+//    A cut searches the key values for its bound with the whole wave: every probe counts the
+//    keys at or above a value with ballots (no LDS, no atomics); then it compacts the buffer in
+//    place with ballot prefix counts.
 //  * Decode selection (one query, many candidates) is shaped differently and lives on its own.
 #include <math.h>
 
@@ -64,8 +68,6 @@ constexpr int kStageBytes = kChunk * kKRowBytes;   // 9216 B
 constexpr int kSampleCap = 512;                    // sampled candidates per row
 constexpr int kStaticLds = 256;                    // bound on the kernel's static LDS
 constexpr int kRowPad = 1;                         // pad entry after every row buffer (bank stagger)
-constexpr int kHistBuckets = 128;                  // buckets of a select round
-constexpr int kHistWords = kHistBuckets / 2;       // 16-bit counters, two per word (scratch per wave)
 // Width of the sample margin: tau0 is the sample key with (mean + kSampleSigmas * sd + 1) sample
 // keys at or above it, mean and sd those of the number of sample keys at or above the true
 // K_B-th key.
@@ -108,116 +110,150 @@ __device__ __forceinline__ float threshold_of(uint32_t t) {
   return t > 0xFF800000u ? __builtin_inff() : key_to_float(t);
 }
 
-// The K-th largest listed key (lane l holds entries j * 64 + l; absent ones are 0): the largest t
-// with count(>= t) >= K (1 <= K <= keys present); *n_above gets count(> t). Histogram rounds over
-// the live key range: every round splits it into kHistBuckets equal power-of-two buckets, counts
-// the keys of each (LDS atomics into hist, this wave's scratch; the LDS operations of one wave
-// complete in order) and keeps the bucket where the running count from the top reaches K.
-// With cap >= K the rounds may stop early, at a bucket's lower end t with K <= count(>= t) <= cap
-// (then t is a bound at or below the K-th largest key, not the key itself); *n_at gets count(>= t)
-// of the returned t when it is known to be at most cap, else a value above cap.
+// Number of listed keys at or above t (lane l holds entries j * 64 + l), the same in every lane:
+// ballot counts, no LDS.
+constexpr int kMaskGroup = 8;  // ballot masks held at once (2 SGPRs each)
+
 template <int P>
-__device__ __forceinline__ uint32_t kth_largest(const uint32_t (&k)[P], int K, int* n_above, uint32_t* hist,
-                                                int cap = 0, int* n_at = nullptr) {
-  const int l = lane_id();
+__device__ __forceinline__ int count_ge(const uint32_t (&k)[P], uint32_t t) {
+  int c = 0;
+#pragma unroll
+  for (int j0 = 0; j0 < P; j0 += kMaskGroup) {
+    // A group of comparisons first, each into its own mask, so that they issue back to back.
+    uint64_t m[kMaskGroup];
+#pragma unroll
+    for (int j = 0; j < kMaskGroup; ++j) m[j] = j0 + j < P ? ballot(k[j0 + j] >= t) : 0ull;
+#pragma unroll
+    for (int j = 0; j < kMaskGroup; ++j) c += popc64(m[j]);
+  }
+  return c;
+}
+
+// The K-th largest listed key (lane l holds entries j * 64 + l; absent ones are 0): the largest t
+// with count(>= t) >= K (1 <= K <= keys present); *n_above gets count(> t).
+// With cap >= K the search may stop early at a value t with K <= count(>= t) <= cap (then t is a
+// bound at or below the K-th largest key, not the key itself); *n_at gets count(>= t) of the
+// returned t when it is known to be at most cap, else a value above cap.
+// Search over key values: it keeps lo < hi with count(>= lo) >= K > count(>= hi) and probes a
+// value between them, alternately where the count, interpolated linearly between the bounds,
+// reaches the target (K, or the middle of [K, cap]) and the midpoint, so it ends within 64 probes
+// (typically a handful). When count(>= lo) is exactly K, the answer is the smallest key at or
+// above lo.
+template <int P>
+__device__ __forceinline__ uint32_t kth_largest(const uint32_t (&k)[P], int K, int* n_above, int cap = 0,
+                                                int* n_at = nullptr) {
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
 #pragma unroll
   for (int j = 0; j < P; ++j) {
-    if (k[j]) mn = min(mn, k[j]);
+    mn = min(mn, k[j] ? k[j] : 0xFFFFFFFFu);
     mx = max(mx, k[j]);
   }
   mn = wave_min_dpp(mn);
   mx = wave_max_dpp(mx);
-  // Invariant: count(>= lo) >= K > count(>= hi) = c_hi.
-  uint64_t lo = mn, hi = (uint64_t)mx + 1;
-  uint32_t c_hi = 0, c_lo = 0x7FFFFFFFu;
-  while (hi - lo > 1) {
-    const int bits = 64 - __clzll((long long)(hi - lo - 1));
-    const int shift = bits > 7 ? bits - 7 : 0;
-    hist[l] = 0u;  // buckets 2l (low half) and 2l + 1 (high half)
+  // Invariant: lo <= hm, count(>= lo) = c_lo >= K > count(>= hm + 1) = c_hi (keys are nonzero, so
+  // lo >= 1 and every span below fits 32 bits).
+  uint32_t lo = mn, hm = mx;
+  int c_lo = count_ge(k, lo), c_hi = 0;
+  const int target = cap >= K ? (K + cap) / 2 : K;
+  for (int step = 0;; ++step) {
+    if (c_lo <= cap) break;  // a bound: K <= count(>= lo) <= cap
+    if (c_lo == K) {         // the K entries at or above lo: the K-th largest is the smallest of them
+      uint32_t m = 0xFFFFFFFFu;
 #pragma unroll
-    for (int j = 0; j < P; ++j) {
-      const uint32_t x = k[j];
-      if (x >= lo && x < hi) {
-        const uint32_t b = (uint32_t)((x - lo) >> shift);
-        atomicAdd(&hist[b >> 1], 1u << ((b & 1u) << 4));
-      }
+      for (int j = 0; j < P; ++j) m = k[j] >= lo ? min(m, k[j]) : m;
+      lo = wave_min_dpp(m);
+      c_hi = lo == 0xFFFFFFFFu ? 0 : count_ge(k, lo + 1u);
+      break;
     }
-    const uint32_t hw = hist[l];
-    const uint2 hv = make_uint2(hw & 0xFFFFu, hw >> 16);
-    uint32_t tot;
-    const uint32_t above = wave_suffix_excl(hv.x + hv.y, &tot) + c_hi;  // count(>= bucket 2l + 2)
-    const uint32_t s1 = above + hv.y, s0 = s1 + hv.x;
-    const uint64_t m = ballot(s0 >= (uint32_t)K);  // lanes 0 .. l*, never empty
-    const int ls = 63 - __clzll((long long)m);
-    const int j = s1 >= (uint32_t)K ? 1 : 0;
-    const int bsel = __builtin_amdgcn_readlane(2 * l + j, ls);
-    c_hi = (uint32_t)__builtin_amdgcn_readlane((int)(j ? above : s1), ls);
-    c_lo = (uint32_t)__builtin_amdgcn_readlane((int)(j ? s1 : s0), ls);  // count(>= the new lo)
-    lo += (uint64_t)bsel << shift;
-    const uint64_t nhi = lo + (1ull << shift);
-    hi = nhi < hi ? nhi : hi;
-    if ((int)c_lo <= cap) break;
+    if (hm <= lo) break;  // count(>= lo) >= K > count(>= lo + 1) = c_hi: lo is the K-th key
+    const uint32_t span = hm - lo;  // probes lie in [lo + 1, hm]
+    uint32_t d;
+    if (step & 1) {
+      d = span / 2;
+    } else {
+      const float f = (float)(c_lo - target) * __builtin_amdgcn_rcpf((float)(c_lo - c_hi));
+      d = (uint32_t)(f * (float)span);
+    }
+    d = __builtin_amdgcn_readfirstlane(d);
+    const uint32_t t = lo + max(1u, min(d, span));
+    const int c = count_ge(k, t);
+    if (c >= K) {
+      lo = t;
+      c_lo = c;
+    } else {
+      hm = t - 1u;
+      c_hi = c;
+    }
   }
-  *n_above = (int)c_hi;
-  if (n_at) *n_at = (int)c_lo;
-  return (uint32_t)lo;
+  *n_above = c_hi;
+  if (n_at) *n_at = c_lo;
+  return lo;
 }
 
 // Cuts one row's buffer (fp32 score bits kb_, ids ib_; n entries in ascending block order) to its
 // K best entries -- keys descending, among equal keys the earliest -- in place and in order, with
-// the whole wave. Requires n > K >= 1 and n <= 64 P. Returns the K-th key. hist: this wave's
-// kHistWords words of LDS scratch.
+// the whole wave. Requires n > K >= 1 and n <= 64 P. Returns the K-th key.
 // With cap > K (a cut in the middle of the stream) it may instead keep every entry whose key is at
 // least a bound t at or below the K-th key, when between K and cap entries are that large: every
 // dropped entry still has K better ones, which is all a later exact cut needs. Returns t then.
 // Either way, a candidate arriving later with a key at or below the returned value has K better
 // entries before it, and *n_kept gets the number of entries kept.
 template <int P, typename IdT>
-__device__ __forceinline__ uint32_t cut_to(uint32_t* kb_, IdT* ib_, int n, int K, uint32_t* hist, int cap = 0,
-                                           int* n_kept = nullptr) {
+__device__ __forceinline__ uint32_t cut_to(uint32_t* kb_, IdT* ib_, int n, int K, int cap = 0, int* n_kept = nullptr) {
   const int l = lane_id();
   uint32_t k[P], id[P];
 #pragma unroll
-  for (int j = 0; j < P; ++j) {
-    const int e = j * 64 + l;
-    k[j] = e < n ? kept_key(kb_[e]) : 0u;
-    id[j] = e < n ? (uint32_t)ib_[e] : 0u;
+  for (int j = 0; j < P; ++j) {  // every entry slot is inside the buffer: load all, then mask
+    k[j] = kb_[j * 64 + l];
+    id[j] = (uint32_t)ib_[j * 64 + l];
   }
+#pragma unroll
+  for (int j = 0; j < P; ++j) k[j] = j * 64 + l < n ? kept_key(k[j]) : 0u;
   int above, n_at;
-  const uint32_t tau = kth_largest(k, K, &above, hist, cap, &n_at);
+  const uint32_t tau = kth_largest(k, K, &above, cap, &n_at);
   const bool loose = n_at <= cap;  // keep every key >= tau
-  const int need = loose ? n : K - above;  // entries equal to tau that stay: the first ones
   if (n_kept) *n_kept = loose ? n_at : K;
   const uint64_t lt = lanemask_lt();
+  const int need = K - above;  // without the loose bound: entries equal to tau that stay, the first ones
   int wpos = 0, tseen = 0;
 #pragma unroll
-  for (int j = 0; j < P; ++j) {
-    const bool eq = k[j] == tau;  // absent entries are 0 < tau
-    const uint64_t em = ballot(eq);
-    const bool keep = k[j] > tau || (eq && tseen + popc64(em & lt) < need);
-    const uint64_t km = ballot(keep);
-    if (keep) {
-      const int dst = wpos + popc64(km & lt);
-      kb_[dst] = key_bits(k[j]);
-      ib_[dst] = (IdT)id[j];
+  for (int j0 = 0; j0 < P; j0 += kMaskGroup) {
+    uint64_t km[kMaskGroup];  // the keep masks of a group of entries, then their writes
+#pragma unroll
+    for (int j = 0; j < kMaskGroup; ++j) {
+      if (j0 + j >= P) {
+        km[j] = 0ull;
+      } else if (loose) {
+        km[j] = ballot(k[j0 + j] >= tau);
+      } else {
+        const bool eq = k[j0 + j] == tau;  // absent entries are 0 < tau
+        const uint64_t em = ballot(eq);
+        km[j] = ballot(k[j0 + j] > tau || (eq && tseen + popc64(em & lt) < need));
+        tseen += popc64(em);
+      }
     }
-    wpos += popc64(km);
-    tseen += popc64(em);
+#pragma unroll
+    for (int j = 0; j < kMaskGroup; ++j) {
+      if (j0 + j < P && ((km[j] >> l) & 1u)) {
+        const int dst = wpos + popc64(km[j] & lt);
+        kb_[dst] = key_bits(k[j0 + j]);
+        ib_[dst] = (IdT)id[j0 + j];
+      }
+      wpos += popc64(km[j]);
+    }
   }
   return tau;
 }
 
 // The keys of a list of fp32 score bits in registers (for the sample threshold): lane l holds
-// entries l, l + 64, ...
+// entries l, l + 64, ...; every slot up to 64 P must be readable.
 template <int P>
 __device__ __forceinline__ void keys_load(uint32_t (&k)[P], const uint32_t* bits, int n) {
   const int l = lane_id();
 #pragma unroll
-  for (int j = 0; j < P; ++j) {
-    const int e = j * 64 + l;
-    k[j] = e < n ? kept_key(bits[e]) : 0u;
-  }
+  for (int j = 0; j < P; ++j) k[j] = bits[j * 64 + l];
+#pragma unroll
+  for (int j = 0; j < P; ++j) k[j] = j * 64 + l < n ? kept_key(k[j]) : 0u;
 }
 
 }  // namespace
@@ -226,26 +262,33 @@ __device__ __forceinline__ void keys_load(uint32_t (&k)[P], const uint32_t* bits
 // query ranges are launched first); candidates [0, c(i)); output the ascending ids into
 // topk [G][N][K_B] (-1 padded).
 //
-// LDS: the double-buffered stage, every wave's select scratch, then per row a buffer of C = 64 P
+// LDS: the double-buffered stage, then per row a buffer of C = 64 P
 // fp32 score bits and, after all rows' scores, their block ids (IdT: uint16 when every block id
 // fits, else int32). Row buffers are kRowPad entries apart, which staggers their LDS banks.
 //
 // UNION: instead of writing topk, every selected id and the row's own block are ORed into the
 // tile-union bitmask umask [G][T][W] (bit b % 32 of word b / 32 of row (g, floor(i / tile))), which
 // the caller has zeroed: the fused index -> union path that never materialises topk.
+//
+// Shapes whose LDS lets two workgroups share a CU get the register budget of two waves per SIMD
+// (which also keeps the products' results in VGPRs).
+template <int WAVES, int P, typename IdT>
+constexpr int kSelectLds = 2 * kStageBytes + WAVES * 4 * (64 * P + kRowPad) * (4 + (int)sizeof(IdT));
+template <int WAVES, int P, typename IdT>
+constexpr int kSelectWavesPerSimd = kSelectLds<WAVES, P, IdT> + kStaticLds <= kGfx950LdsBytes / 2 ? 2 : 1;
+
 template <int WAVES, int P, typename IdT, bool UNION>
-__global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restrict__ qi, const float* __restrict__ w,
-                                                       const uint16_t* __restrict__ kbar,
-                                                       int32_t* __restrict__ topk, int n_tokens, int n_groups,
-                                                       int block, int kb, uint32_t* __restrict__ umask, int tile,
-                                                       int n_tiles, int n_words) {
+__global__ __launch_bounds__(WAVES * 64, (kSelectWavesPerSimd<WAVES, P, IdT>)) void k_select(
+    const uint16_t* __restrict__ qi, const float* __restrict__ w, const uint16_t* __restrict__ kbar,
+    int32_t* __restrict__ topk, int n_tokens, int n_groups, int block, int kb, uint32_t* __restrict__ umask, int tile,
+    int n_tiles, int n_words) {
   constexpr int C = 64 * P;
   constexpr int CS = C + kRowPad;  // row stride in entries
+  static_assert(C >= kSampleCap, "a row buffer holds the sample");
   constexpr int kRowsPerWg = WAVES * 4;
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* stage = smem;  // 2 x kStageBytes
-  uint32_t* hist_lds = reinterpret_cast<uint32_t*>(smem + 2 * kStageBytes);  // WAVES x kHistWords
-  uint32_t* keys_lds = hist_lds + WAVES * kHistWords;
+  uint32_t* keys_lds = reinterpret_cast<uint32_t*>(smem + 2 * kStageBytes);
   IdT* ids_lds = reinterpret_cast<IdT*>(keys_lds + kRowsPerWg * CS);
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
@@ -390,6 +433,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
   int hi_wave = hi_lane;
 #pragma unroll
   for (int off = 16; off <= 32; off <<= 1) hi_wave = min(hi_wave, __shfl_xor(hi_wave, off, 64));
+  hi_wave = __builtin_amdgcn_readfirstlane(hi_wave);  // equal in every lane: a scalar branch below
   // Streams candidates v in [0, n_virt) (block lo + v * stride + off) through the double-buffered
   // stage, two chunks ahead of the products: at the start of step n the B operands of chunk n are
   // in registers and chunk n+1 is in buffer (n+1) % 2; the step loads chunk n+2's keys into
@@ -441,7 +485,6 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
   auto row_k = [&](int q) { return keys_lds + (size_t)(wave * 4 + q) * CS; };
   auto row_i = [&](int q) { return ids_lds + (size_t)(wave * 4 + q) * CS; };
   auto nothing = [&]() {};
-  uint32_t* hist = hist_lds + wave * kHistWords;  // this wave's select scratch
 
   // Row state, uniform over the row's 16 lanes: the threshold (a score s passes iff !(s < thr)),
   // the number of buffered entries, and whether the row takes part in the current pass.
@@ -453,7 +496,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
   // A strided sample of the candidates (the same blocks for every row of the workgroup) goes into
   // the row buffers; for every row with more than C candidates its keys give the threshold tau0.
   if (n_all > C) {
-    const int sample_cap = min(kSampleCap, C) / 64 * 64;
+    const int sample_cap = kSampleCap;
     const int stride = (n_all + sample_cap - 1) / sample_cap;
     const int s_off = stride / 2;
     const int s_virt = (n_all - s_off + stride - 1) / stride;
@@ -463,7 +506,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
       uint32_t cnt = 0;
 #pragma unroll
       for (int ct = 0; ct < kTiles; ++ct) {
-        f[ct] = kFull || valid_at(v_first + ct, s_virt, stride, s_off);
+        f[ct] = kFull | valid_at(v_first + ct, s_virt, stride, s_off);
         cnt += f[ct] ? 1u : 0u;
       }
       const uint32_t incl = row16_prefix(cnt);
@@ -489,7 +532,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
       uint32_t sk[kSampleCap / 64];
       keys_load(sk, row_k(q), nq);
       int unused;
-      const uint32_t tau0 = kth_largest(sk, ks, &unused, hist);
+      const uint32_t tau0 = kth_largest(sk, ks, &unused);
       if (quarter == q) thr = threshold_of(tau0);
     }
     n_cnt = 0;
@@ -507,7 +550,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
       cnt = 0;
 #pragma unroll
       for (int ct = 0; ct < kTiles; ++ct) {
-        f[ct] = active && (kFull || v_first + ct < n_cand) && !(sc[ct] < thr);
+        f[ct] = active & (kFull | (v_first + ct < n_cand)) & !(sc[ct] < thr);  // no branches
         cnt += f[ct] ? 1u : 0u;
       }
     };
@@ -519,7 +562,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
       for (int q = 0; q < 4; ++q) {
         if (readlane((int)(n_cnt + tot > C), 16 * q) == 0) continue;
         int kept;
-        const uint32_t tau = cut_to<P, IdT>(row_k(q), row_i(q), readlane(n_cnt, 16 * q), kb, hist, C - kChunk, &kept);
+        const uint32_t tau = cut_to<P, IdT>(row_k(q), row_i(q), readlane(n_cnt, 16 * q), kb, C - kChunk, &kept);
         if (quarter == q) {
           n_cnt = kept;
           thr = tau == 0xFFFFFFFFu ? __builtin_inff() : threshold_of(tau + 1u);
@@ -578,7 +621,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_select(const uint16_t* __restric
     if (i >= n_tokens) break;
     int nq = readlane(n_cnt, 16 * q);
     if (nq > kb) {
-      cut_to<P, IdT>(row_k(q), row_i(q), nq, kb, hist);
+      cut_to<P, IdT>(row_k(q), row_i(q), nq, kb);
       nq = kb;
       lds_wait();
     }
@@ -606,16 +649,17 @@ namespace {
 
 // The shapes a launch can take: WAVES waves of 4 rows, buffers of 64 P entries, 16- or 32-bit ids.
 // Each fits the gfx950 LDS with the stage; the first whose buffer holds K_B plus one chunk of
-// appends (K_B + kChunk entries) is used. The selection is VALU work: eight waves of one workgroup
-// (two per SIMD) issue it at twice the rate of one wave per SIMD, so the 8-wave shape comes first.
+// appends (K_B + kChunk entries) is used. The selection is VALU work, which one wave per SIMD
+// issues at half the rate of two: the first shape fits two workgroups on a CU (32-bit ids leave no
+// shape that does).
 struct SelectShape {
   int waves, p;
   bool id32;
 };
-constexpr SelectShape kShapes[] = {{4, 10, false}, {8, 10, false}, {4, 20, false}, {2, 40, false}, {4, 14, true}, {1, 60, true}};
+constexpr SelectShape kShapes[] = {{4, 10, false}, {4, 20, false}, {2, 40, false}, {4, 14, true}, {1, 60, true}};
 
 size_t select_lds_bytes(const SelectShape& s) {
-  return (size_t)2 * kStageBytes + (size_t)s.waves * kHistWords * 4 +
+  return (size_t)2 * kStageBytes +
          (size_t)s.waves * 4 * (64 * s.p + kRowPad) * (4 + (s.id32 ? 4 : 2));
 }
 
@@ -661,7 +705,6 @@ hipError_t launch_select(const uint16_t* qi, const float* w, const uint16_t* kba
     return hipGetLastError();                                                                                    \
   }
   SGQA_SELECT_CASE(4, 10, uint16_t)
-  SGQA_SELECT_CASE(8, 10, uint16_t)
   SGQA_SELECT_CASE(4, 20, uint16_t)
   SGQA_SELECT_CASE(2, 40, uint16_t)
   SGQA_SELECT_CASE(4, 14, int32_t)
@@ -674,7 +717,6 @@ hipError_t launch_select(const uint16_t* qi, const float* w, const uint16_t* kba
 
 hipError_t prepare_index_topk_kernels(int lds_max) {
   const void* fns[] = {(const void*)k_select<4, 10, uint16_t, false>, (const void*)k_select<4, 10, uint16_t, true>,
-                       (const void*)k_select<8, 10, uint16_t, false>, (const void*)k_select<8, 10, uint16_t, true>,
                        (const void*)k_select<4, 20, uint16_t, false>, (const void*)k_select<2, 40, uint16_t, false>,
                        (const void*)k_select<4, 14, int32_t, false>,  (const void*)k_select<1, 60, int32_t, false>,
                        (const void*)k_select<4, 20, uint16_t, true>,  (const void*)k_select<2, 40, uint16_t, true>,
