@@ -35,7 +35,7 @@
 //    - the pass appends every candidate whose fp32 score is not below the row's threshold (one
 //      compare per candidate; the order key is formed only for appended ones). A chunk that
 //      would overflow a buffer first cuts it: to the entries at or above a key bound t that
-//      leaves between K_B and C - 64 of them (t at or below the K_B-th key, usually found by a
+//      leaves between K_B and K_B + 32 of them (t at or below the K_B-th key, usually found by a
 //      few probes), or, when ties make that impossible, to exactly its K_B best
 //      entries (key descending, among equal keys the earliest = lowest block ids) with t the
 //      K_B-th key; the row's threshold becomes "strictly above t": every candidate at or below
@@ -66,11 +66,16 @@ constexpr int kChunk = 64;                         // candidate blocks per stage
 constexpr int kKRowBytes = 144;                    // 128 B block key + 16 B pad
 constexpr int kStageBytes = kChunk * kKRowBytes;   // 9216 B
 constexpr int kSampleCap = 512;                    // sampled candidates per row
+// A cut in the middle of the stream keeps between K_B and K_B + kCutSlack entries (at most C - kChunk,
+// so that a chunk's appends still fit): a bound found in a few probes (an exact cut, which resolves
+// ties at the K_B-th key, costs about twice as much).
+constexpr int kCutSlack = 32;
 constexpr int kStaticLds = 256;                    // bound on the kernel's static LDS
-constexpr int kRowPad = 1;                         // pad entry after every row buffer (bank stagger)
-// Width of the sample margin: tau0 is the sample key with (mean + kSampleSigmas * sd + 1) sample
-// keys at or above it, mean and sd those of the number of sample keys at or above the true
-// K_B-th key.
+constexpr int kRowPad = 16;                        // pad entries after every row buffer
+// Width of the sample margin: tau0 has at least ks = (mean + kSampleSigmas * sd + 1) sample keys
+// at or above it, mean and sd those of the number of sample keys at or above the true K_B-th key
+// (and at most ks + ks / 8 + 1: any such value bounds the threshold as safely, and the search for
+// one stops after a few probes).
 constexpr float kSampleSigmas = 3.0f;
 
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
@@ -264,7 +269,8 @@ __device__ __forceinline__ void keys_load(uint32_t (&k)[P], const uint32_t* bits
 //
 // LDS: the double-buffered stage, then per row a buffer of C = 64 P
 // fp32 score bits and, after all rows' scores, their block ids (IdT: uint16 when every block id
-// fits, else int32). Row buffers are kRowPad entries apart, which staggers their LDS banks.
+// fits, else int32). Each row buffer is followed by kRowPad pad entries: lane j of the row writes
+// the candidates it does not keep to pad entry j, so the append needs no branch.
 //
 // UNION: instead of writing topk, every selected id and the row's own block are ORed into the
 // tile-union bitmask umask [G][T][W] (bit b % 32 of word b / 32 of row (g, floor(i / tile))), which
@@ -484,6 +490,7 @@ __global__ __launch_bounds__(WAVES * 64, (kSelectWavesPerSimd<WAVES, P, IdT>)) v
   IdT* my_i = ids_lds + (size_t)(wave * 4 + quarter) * CS;
   auto row_k = [&](int q) { return keys_lds + (size_t)(wave * 4 + q) * CS; };
   auto row_i = [&](int q) { return ids_lds + (size_t)(wave * 4 + q) * CS; };
+  const uint32_t pad_pos = C + l16;  // this lane's pad entry
   auto nothing = [&]() {};
 
   // Row state, uniform over the row's 16 lanes: the threshold (a score s passes iff !(s < thr)),
@@ -513,7 +520,7 @@ __global__ __launch_bounds__(WAVES * 64, (kSelectWavesPerSimd<WAVES, P, IdT>)) v
       uint32_t pos = n_cnt + incl - cnt;
 #pragma unroll
       for (int ct = 0; ct < kTiles; ++ct) {
-        if (f[ct]) my_k[pos] = __float_as_uint(sc[ct]);
+        my_k[f[ct] ? pos : pad_pos] = __float_as_uint(sc[ct]);
         pos += f[ct] ? 1u : 0u;
       }
       n_cnt += row16_total(incl);
@@ -532,7 +539,7 @@ __global__ __launch_bounds__(WAVES * 64, (kSelectWavesPerSimd<WAVES, P, IdT>)) v
       uint32_t sk[kSampleCap / 64];
       keys_load(sk, row_k(q), nq);
       int unused;
-      const uint32_t tau0 = kth_largest(sk, ks, &unused);
+      const uint32_t tau0 = kth_largest(sk, ks, &unused, ks + ks / 8 + 1);
       if (quarter == q) thr = threshold_of(tau0);
     }
     n_cnt = 0;
@@ -540,8 +547,10 @@ __global__ __launch_bounds__(WAVES * 64, (kSelectWavesPerSimd<WAVES, P, IdT>)) v
 
   // ------------------------------------------------------------------ the pass
   // Every candidate that passes its row's threshold is appended, in ascending block order. A
-  // chunk that would overflow a row's buffer first cuts it to at most C - kChunk entries that
-  // include its K_B best, and raises the row's threshold past the cut's bound.
+  // chunk that would overflow a row's buffer first cuts it to at most min(K_B + kCutSlack, C -
+  // kChunk) entries that include its K_B best, and raises the row's threshold past the cut's bound.
+  // At most C - kChunk entries after a cut leave room for the chunk's appends (C >= K_B + kChunk).
+  const int cut_cap = min(kb + kCutSlack, C - kChunk);
   auto append = [&](const float (&sc)[kTiles], int v_first, auto full_t) {
     constexpr bool kFull = decltype(full_t)::value;
     bool f[kTiles];
@@ -562,7 +571,7 @@ __global__ __launch_bounds__(WAVES * 64, (kSelectWavesPerSimd<WAVES, P, IdT>)) v
       for (int q = 0; q < 4; ++q) {
         if (readlane((int)(n_cnt + tot > C), 16 * q) == 0) continue;
         int kept;
-        const uint32_t tau = cut_to<P, IdT>(row_k(q), row_i(q), readlane(n_cnt, 16 * q), kb, C - kChunk, &kept);
+        const uint32_t tau = cut_to<P, IdT>(row_k(q), row_i(q), readlane(n_cnt, 16 * q), kb, cut_cap, &kept);
         if (quarter == q) {
           n_cnt = kept;
           thr = tau == 0xFFFFFFFFu ? __builtin_inff() : threshold_of(tau + 1u);
@@ -572,15 +581,14 @@ __global__ __launch_bounds__(WAVES * 64, (kSelectWavesPerSimd<WAVES, P, IdT>)) v
       incl = row16_prefix(cnt);
       tot = (int)row16_total(incl);
     }
-    // Kept candidates go to consecutive entries.
+    // Kept candidates go to consecutive entries, the others to this lane's pad entry.
     uint32_t pos = n_cnt + incl - cnt;
     const uint32_t id0 = (uint32_t)(lo + v_first);
 #pragma unroll
     for (int ct = 0; ct < kTiles; ++ct) {
-      if (f[ct]) {
-        my_k[pos] = __float_as_uint(sc[ct]);
-        my_i[pos] = (IdT)(id0 + ct);
-      }
+      const uint32_t e = f[ct] ? pos : pad_pos;
+      my_k[e] = __float_as_uint(sc[ct]);
+      my_i[e] = (IdT)(id0 + ct);
       pos += f[ct] ? 1u : 0u;
     }
     n_cnt += tot;

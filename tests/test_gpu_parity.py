@@ -104,9 +104,17 @@ def run_topk(sg, p, xd, kbar_dev):
     return topk
 
 
-@pytest.mark.parametrize("name", list(SMALL))
+# Selection-only cases: K_B = 576 makes the per-row buffer exactly K_B + one chunk, so cuts in the
+# middle of the stream take their smallest room (independent queries: many of them).
+TOPK_EXTRA = {
+    "kb576_room": datagen.PREFILL.replace(name="kb576_room", n_tokens=8192 + 5, n_q_heads=16, n_kv_heads=2,
+                                          topk_tokens=4608, union_tile=64, qi_mode="iid"),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL) + list(TOPK_EXTRA))
 def test_index_topk_bit_exact(sg, name):
-    wl = SMALL[name]
+    wl = SMALL[name] if name in SMALL else TOPK_EXTRA[name]
     p = params_of(wl)
     x = datagen.prefill_inputs(wl)
     ch = OracleChain(x, p)
