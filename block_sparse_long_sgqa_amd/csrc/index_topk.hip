@@ -115,86 +115,6 @@ __device__ __forceinline__ float threshold_of(uint32_t t) {
   return t > 0xFF800000u ? __builtin_inff() : key_to_float(t);
 }
 
-// Number of listed keys at or above t (lane l holds entries j * 64 + l), the same in every lane:
-// ballot counts, no LDS.
-constexpr int kMaskGroup = 8;  // ballot masks held at once (2 SGPRs each)
-
-template <int P>
-__device__ __forceinline__ int count_ge(const uint32_t (&k)[P], uint32_t t) {
-  int c = 0;
-#pragma unroll
-  for (int j0 = 0; j0 < P; j0 += kMaskGroup) {
-    // A group of comparisons first, each into its own mask, so that they issue back to back.
-    uint64_t m[kMaskGroup];
-#pragma unroll
-    for (int j = 0; j < kMaskGroup; ++j) m[j] = j0 + j < P ? ballot(k[j0 + j] >= t) : 0ull;
-#pragma unroll
-    for (int j = 0; j < kMaskGroup; ++j) c += popc64(m[j]);
-  }
-  return c;
-}
-
-// The K-th largest listed key (lane l holds entries j * 64 + l; absent ones are 0): the largest t
-// with count(>= t) >= K (1 <= K <= keys present); *n_above gets count(> t).
-// With cap >= K the search may stop early at a value t with K <= count(>= t) <= cap (then t is a
-// bound at or below the K-th largest key, not the key itself); *n_at gets count(>= t) of the
-// returned t when it is known to be at most cap, else a value above cap.
-// Search over key values: it keeps lo < hi with count(>= lo) >= K > count(>= hi) and probes a
-// value between them, alternately where the count, interpolated linearly between the bounds,
-// reaches the target (K, or the middle of [K, cap]) and the midpoint, so it ends within 64 probes
-// (typically a handful). When count(>= lo) is exactly K, the answer is the smallest key at or
-// above lo.
-template <int P>
-__device__ __forceinline__ uint32_t kth_largest(const uint32_t (&k)[P], int K, int* n_above, int cap = 0,
-                                                int* n_at = nullptr) {
-  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-#pragma unroll
-  for (int j = 0; j < P; ++j) {
-    mn = min(mn, k[j] ? k[j] : 0xFFFFFFFFu);
-    mx = max(mx, k[j]);
-  }
-  mn = wave_min_dpp(mn);
-  mx = wave_max_dpp(mx);
-  // Invariant: lo <= hm, count(>= lo) = c_lo >= K > count(>= hm + 1) = c_hi (keys are nonzero, so
-  // lo >= 1 and every span below fits 32 bits).
-  uint32_t lo = mn, hm = mx;
-  int c_lo = count_ge(k, lo), c_hi = 0;
-  const int target = cap >= K ? (K + cap) / 2 : K;
-  for (int step = 0;; ++step) {
-    if (c_lo <= cap) break;  // a bound: K <= count(>= lo) <= cap
-    if (c_lo == K) {         // the K entries at or above lo: the K-th largest is the smallest of them
-      uint32_t m = 0xFFFFFFFFu;
-#pragma unroll
-      for (int j = 0; j < P; ++j) m = k[j] >= lo ? min(m, k[j]) : m;
-      lo = wave_min_dpp(m);
-      c_hi = lo == 0xFFFFFFFFu ? 0 : count_ge(k, lo + 1u);
-      break;
-    }
-    if (hm <= lo) break;  // count(>= lo) >= K > count(>= lo + 1) = c_hi: lo is the K-th key
-    const uint32_t span = hm - lo;  // probes lie in [lo + 1, hm]
-    uint32_t d;
-    if (step & 1) {
-      d = span / 2;
-    } else {
-      const float f = (float)(c_lo - target) * __builtin_amdgcn_rcpf((float)(c_lo - c_hi));
-      d = (uint32_t)(f * (float)span);
-    }
-    d = __builtin_amdgcn_readfirstlane(d);
-    const uint32_t t = lo + max(1u, min(d, span));
-    const int c = count_ge(k, t);
-    if (c >= K) {
-      lo = t;
-      c_lo = c;
-    } else {
-      hm = t - 1u;
-      c_hi = c;
-    }
-  }
-  *n_above = c_hi;
-  if (n_at) *n_at = c_lo;
-  return lo;
-}
-
 // Cuts one row's buffer (fp32 score bits kb_, ids ib_; n entries in ascending block order) to its
 // K best entries -- keys descending, among equal keys the earliest -- in place and in order, with
 // the whole wave. Requires n > K >= 1 and n <= 64 P. Returns the K-th key.
