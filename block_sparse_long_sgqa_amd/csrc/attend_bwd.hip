@@ -21,6 +21,9 @@
 //    gathered into the wave's swizzled LDS tiles (double-buffered, one group ahead), S = Q K^T and
 //    dP = dO V^T give P and dS with the keys in the lane columns, and dV^T += dO^T P,
 //    dK^T += Q^T dS take dO^T and Q^T transposed from LDS.
+#include <stdlib.h>
+#include <string.h>
+
 #include "attn_common.hpp"
 
 namespace sgqa {
@@ -311,6 +314,88 @@ constexpr int kRowTileBytes = 32 * 256;        // 32 rows x 128 bf16, swizzled l
 constexpr int kRgBytes = 2 * kRowTileBytes;    // Q rows, then dO rows
 }  // namespace
 
+// One 32-row group against a wave's 32 keys (lane l holds key column l % 32): from the group's Q and
+// dO rows in `b` (swizzled row-major, Q then dO), its rows' lse and delta (lsde) and queries (qrow,
+// -1 past the tile), accumulates dV^T += dO^T P and dK^T += Q^T dS (unscaled) for the keys; `take`:
+// this lane's key is attended by the group's rows (causality is tested here).
+__device__ __forceinline__ void dkdv_rows(const uint8_t* b, const float* lsde, const int* qrow, bool take, int key,
+                                          const bf16x8 (&kb)[8], const bf16x8 (&vb)[8], f32x16 (&adk)[4],
+                                          f32x16 (&adv)[4], const LaneOffsets& lo, float scale_log2) {
+  const int l = lane_id(), hi = l >> 5;
+  const uint8_t* dob = b + kRowTileBytes;
+  // S = Q K^T, dP = dO V^T: A operands row (l % 32), logical piece 2 ks + (l / 32).
+  f32x16 s, dp;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    s[j] = 0.0f;
+    dp[j] = 0.0f;
+  }
+  // The operands of step ks + 2 are read while the products of step ks run.
+  const int arow = l & 31;
+  auto off_of = [&](int ks) { return arow * 256 + 16 * v_phys(arow, 2 * ks + hi); };
+  bf16x8 qa[3], da[3];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    qa[ks] = *reinterpret_cast<const bf16x8*>(b + off_of(ks));
+    da[ks] = *reinterpret_cast<const bf16x8*>(dob + off_of(ks));
+  }
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    if (ks + 2 < 8) {
+      qa[(ks + 2) % 3] = *reinterpret_cast<const bf16x8*>(b + off_of(ks + 2));
+      da[(ks + 2) % 3] = *reinterpret_cast<const bf16x8*>(dob + off_of(ks + 2));
+    }
+    s = mfma32(qa[ks % 3], kb[ks], s);
+    dp = mfma32(da[ks % 3], vb[ks], dp);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Rows of score j: 8 (j / 4) + 4 hi + (j % 4).
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int4 qi4 = *reinterpret_cast<const int4*>(qrow + 8 * a + 4 * hi);
+    const float4 ls4 = *reinterpret_cast<const float4*>(lsde + 8 * a + 4 * hi);
+    const float4 de4 = *reinterpret_cast<const float4*>(lsde + 32 + 8 * a + 4 * hi);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int qi = c == 0 ? qi4.x : (c == 1 ? qi4.y : (c == 2 ? qi4.z : qi4.w));
+      const float ls = c == 0 ? ls4.x : (c == 1 ? ls4.y : (c == 2 ? ls4.z : ls4.w));
+      const float de = c == 0 ? de4.x : (c == 1 ? de4.y : (c == 2 ? de4.z : de4.w));
+      const int j = 4 * a + c;
+      const bool ok = take && key <= qi;  // qi = -1 for rows past the tile
+      const float p = ok ? fast_exp2(__builtin_fmaf(s[j], scale_log2, -ls)) : 0.0f;
+      s[j] = p;
+      dp[j] = p * (dp[j] - de);
+    }
+  }
+  bf16x8 pp[2], pd[2];
+#pragma unroll
+  for (int ss = 0; ss < 2; ++ss)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pp[ss][e] = (__bf16)s[8 * ss + e];
+      pd[ss][e] = (__bf16)dp[8 * ss + e];
+    }
+  // dV^T += dO^T P, dK^T += Q^T dS; step = 2 dt + ss, operands read two steps ahead.
+  auto tr_op = [&](const uint8_t* base, int step) { return tr_read(base + lo.v[step >> 1] + (16 * (step & 1)) * 256); };
+  bf16x8 oa[3], qt[3];
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    oa[st] = tr_op(dob, st);
+    qt[st] = tr_op(b, st);
+  }
+#pragma unroll
+  for (int st = 0; st < 8; ++st) {
+    if (st + 2 < 8) {
+      oa[(st + 2) % 3] = tr_op(dob, st + 2);
+      qt[(st + 2) % 3] = tr_op(b, st + 2);
+    }
+    const int dt = st >> 1, ss = st & 1;
+    adv[dt] = mfma32(oa[st % 3], pp[ss], adv[dt]);
+    adk[dt] = mfma32(qt[st % 3], pd[ss], adk[dt]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 __global__ __launch_bounds__(kBwdWaves * 64) void k_bwd_dkdv(const uint16_t* __restrict__ q,
                                                              const uint16_t* __restrict__ k,
                                                              const uint16_t* __restrict__ v,
@@ -456,78 +541,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void k_bwd_dkdv(const uint16_t* __r
   // One row group from buffer `buf`: member = this lane's key block is in the tile's union.
   auto compute_rg = [&](const uint8_t* b, const float* lsde, const int* qrow, bool member)
                         __attribute__((always_inline)) {
-    const uint8_t* dob = b + kRowTileBytes;
-    // S = Q K^T, dP = dO V^T: A operands row (l % 32), logical piece 2 ks + (l / 32).
-    f32x16 s, dp;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      s[j] = 0.0f;
-      dp[j] = 0.0f;
-    }
-    // The operands of step ks + 2 are read while the products of step ks run.
-    const int arow = l & 31;
-    auto off_of = [&](int ks) { return arow * 256 + 16 * v_phys(arow, 2 * ks + hi); };
-    bf16x8 qa[3], da[3];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      qa[ks] = *reinterpret_cast<const bf16x8*>(b + off_of(ks));
-      da[ks] = *reinterpret_cast<const bf16x8*>(dob + off_of(ks));
-    }
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      if (ks + 2 < 8) {
-        qa[(ks + 2) % 3] = *reinterpret_cast<const bf16x8*>(b + off_of(ks + 2));
-        da[(ks + 2) % 3] = *reinterpret_cast<const bf16x8*>(dob + off_of(ks + 2));
-      }
-      s = mfma32(qa[ks % 3], kb[ks], s);
-      dp = mfma32(da[ks % 3], vb[ks], dp);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // Rows of score j: 8 (j / 4) + 4 hi + (j % 4).
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int4 qi4 = *reinterpret_cast<const int4*>(qrow + 8 * a + 4 * hi);
-      const float4 ls4 = *reinterpret_cast<const float4*>(lsde + 8 * a + 4 * hi);
-      const float4 de4 = *reinterpret_cast<const float4*>(lsde + 32 + 8 * a + 4 * hi);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int qi = c == 0 ? qi4.x : (c == 1 ? qi4.y : (c == 2 ? qi4.z : qi4.w));
-        const float ls = c == 0 ? ls4.x : (c == 1 ? ls4.y : (c == 2 ? ls4.z : ls4.w));
-        const float de = c == 0 ? de4.x : (c == 1 ? de4.y : (c == 2 ? de4.z : de4.w));
-        const int j = 4 * a + c;
-        const bool ok = member && key_ok && key <= qi;  // qi = -1 for rows past the tile
-        const float p = ok ? fast_exp2(__builtin_fmaf(s[j], scale_log2, -ls)) : 0.0f;
-        s[j] = p;
-        dp[j] = p * (dp[j] - de);
-      }
-    }
-    bf16x8 pp[2], pd[2];
-#pragma unroll
-    for (int ss = 0; ss < 2; ++ss)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pp[ss][e] = (__bf16)s[8 * ss + e];
-        pd[ss][e] = (__bf16)dp[8 * ss + e];
-      }
-    // dV^T += dO^T P, dK^T += Q^T dS; step = 2 dt + ss, operands read two steps ahead.
-    auto tr_op = [&](const uint8_t* base, int step) { return tr_read(base + lo.v[step >> 1] + (16 * (step & 1)) * 256); };
-    bf16x8 oa[3], qt[3];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      oa[st] = tr_op(dob, st);
-      qt[st] = tr_op(b, st);
-    }
-#pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      if (st + 2 < 8) {
-        oa[(st + 2) % 3] = tr_op(dob, st + 2);
-        qt[(st + 2) % 3] = tr_op(b, st + 2);
-      }
-      const int dt = st >> 1, ss = st & 1;
-      adv[dt] = mfma32(oa[st % 3], pp[ss], adv[dt]);
-      adk[dt] = mfma32(qt[st % 3], pd[ss], adk[dt]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    dkdv_rows(b, lsde, qrow, member && key_ok, key, kb, vb, adk, adv, lo, scale_log2);
   };
 
   // Work items: the row groups of the tiles t >= the first one holding a query >= j0 whose union
@@ -634,6 +648,493 @@ __global__ __launch_bounds__(kBwdWaves * 64) void k_bwd_dkdv(const uint16_t* __r
   }
 }
 
+// ------------------------------------------------------------------------------------ dk, dv: tile-major
+//
+// The same sums, organised by tile: a work item is 128 consecutive entries of one union U(t,g) (the
+// union's blocks in ascending order, B tokens each), four waves of 32 keys; it streams the tile's
+// Q and dO rows once through a shared LDS double buffer, and every row's Q/dO slice serves all 128
+// keys. An item writes its keys' unscaled dK^T and dV^T columns (fp32) as one partial row per key;
+// a second kernel adds, for every key, the partial rows of the tiles that hold it in ascending tile
+// order, so the result does not depend on the scheduling. Partial rows are Σ_t |U(t,g)| B per
+// group, data dependent and up to the whole causal triangle, so the (tile, group) pairs are taken
+// in batches of at most a fixed number of rows: a planning pass on the device numbers the pairs'
+// rows and items, and batch b holds the pairs whose first row lies in [b H, (b + 1) H) with H the
+// batch size minus the largest pair; the host launches the worst-case number of batches, and the
+// kernels of an empty batch return at once.
+
+namespace {
+constexpr int kTmWaves = 4;
+constexpr int kTmKeys = kTmWaves * 32;      // union entries per work item
+constexpr int kTmRowFloats = 2 * kD;        // partial row: dK^T column, then dV^T column
+constexpr long long kTmCapRows = 1LL << 22; // partial rows per batch (4 GiB)
+constexpr int kTmMaxBatches = 1024;         // more batches than this: the key-major kernel runs
+constexpr int kTmPlanThreads = 1024;
+struct TmItem {
+  uint32_t pair, word;  // (tile, group) pair t * G + g; mask word holding the item's first block
+};
+
+// Word w of a tile's union mask restricted to the blocks <= c_hi (the tile's causal range).
+__device__ __forceinline__ uint32_t tm_word(const uint32_t* mrow, int w, int c_hi) {
+  const int wl = c_hi >> 5;
+  if (w > wl) return 0u;
+  uint32_t m = mrow[w];
+  if (w == wl && (c_hi & 31) != 31) m &= (2u << (c_hi & 31)) - 1u;
+  return m;
+}
+
+// Last block of tile t's causal range.
+__device__ __forceinline__ int tm_chi(int t, int n_tokens, int tile, int block_shift) {
+  const long long end = min((long long)n_tokens, (long long)(t + 1) * tile);
+  return (int)((end - 1) >> block_shift);
+}
+
+// Block-wide exclusive scan of a 64-bit value per thread (NT threads; scratch: NT/64 entries).
+template <int NT>
+__device__ __forceinline__ unsigned long long block_scan_u64(unsigned long long v, unsigned long long* scratch,
+                                                             unsigned long long* total) {
+  const int l = lane_id(), wave = threadIdx.x >> 6;
+  unsigned long long incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned long long o = __shfl_up(incl, off, 64);
+    if (l >= off) incl += o;
+  }
+  if (l == 63) scratch[wave] = incl;
+  __syncthreads();
+  unsigned long long before = 0, all = 0;
+  for (int x = 0; x < NT / 64; ++x) {
+    const unsigned long long s = scratch[x];
+    if (x < wave) before += s;
+    all += s;
+  }
+  __syncthreads();
+  *total = all;
+  return before + incl - v;
+}
+}  // namespace
+
+// Per (tile, group) pair: pre[pair][w] = set bits of the causal union words before w (the rank of
+// the word's first block), nblk[pair] = the union's size. One workgroup per pair.
+__global__ __launch_bounds__(256) void k_tm_prefix(const uint32_t* __restrict__ umask, uint32_t* __restrict__ pre,
+                                                   uint32_t* __restrict__ nblk, int n_tokens, int n_groups, int tile,
+                                                   int block_shift, int n_tiles, int n_words) {
+  __shared__ int scan[4];
+  const int pair = blockIdx.x;
+  const int t = pair / n_groups, g = pair - t * n_groups;
+  const int c_hi = tm_chi(t, n_tokens, tile, block_shift);
+  const int n_w = (c_hi >> 5) + 1;
+  const uint32_t* mrow = umask + ((long long)g * n_tiles + t) * n_words;
+  uint32_t* prow = pre + (long long)pair * n_words;
+  int base = 0;
+  for (int w0 = 0; w0 < n_w; w0 += 256) {
+    const int w = w0 + (int)threadIdx.x;
+    const int c = w < n_w ? __popc(tm_word(mrow, w, c_hi)) : 0;
+    int all;
+    const int ex = block_exclusive_scan<256>(c, scan, &all);
+    if (w < n_w) prow[w] = (uint32_t)(base + ex);
+    base += all;
+  }
+  if (threadIdx.x == 0) nblk[pair] = (uint32_t)base;
+}
+
+// The plan (one workgroup): over the pairs in order t * G + g, ebase = exclusive prefix of the
+// partial rows (nblk * B), ipref = exclusive prefix of the items (ceil(nblk / blocks per item)),
+// both with the totals appended; bstart[b] = first pair of batch b (pairs whose ebase lies in
+// [b * hstep, (b + 1) * hstep)), bstart[n_batches] = n_pairs.
+__global__ __launch_bounds__(kTmPlanThreads) void k_tm_plan(const uint32_t* __restrict__ nblk,
+                                                            unsigned long long* __restrict__ ebase,
+                                                            uint32_t* __restrict__ ipref, int* __restrict__ bstart,
+                                                            int n_pairs, int block_shift, long long hstep,
+                                                            int n_batches) {
+  __shared__ unsigned long long scan[kTmPlanThreads / 64];
+  const int per = (n_pairs + kTmPlanThreads - 1) / kTmPlanThreads;
+  const int p0 = (int)threadIdx.x * per;
+  const int p1 = min(n_pairs, p0 + per);
+  const int nbi = kTmKeys >> block_shift;
+  unsigned long long rows = 0, items = 0;
+  for (int p = p0; p < p1; ++p) {
+    rows += (unsigned long long)nblk[p] << block_shift;
+    items += (nblk[p] + nbi - 1) / nbi;
+  }
+  unsigned long long all_rows, all_items;
+  unsigned long long er = block_scan_u64<kTmPlanThreads>(rows, scan, &all_rows);
+  unsigned long long ei = block_scan_u64<kTmPlanThreads>(items, scan, &all_items);
+  if (p0 >= n_pairs) return;
+  const unsigned long long h = (unsigned long long)hstep;
+  // (The host sizes n_batches so that every batch index stays below it; the clamp keeps the writes
+  // inside bstart whatever the mask holds.)
+  long long b_prev = p0 == 0 ? -1 : (long long)((er - ((unsigned long long)nblk[p0 - 1] << block_shift)) / h);
+  b_prev = min(b_prev, (long long)n_batches - 1);
+  for (int p = p0; p < p1; ++p) {
+    ebase[p] = er;
+    ipref[p] = (uint32_t)ei;
+    const long long b = min((long long)(er / h), (long long)n_batches - 1);
+    for (long long x = b_prev + 1; x <= b; ++x) bstart[x] = p;
+    b_prev = b;
+    er += (unsigned long long)nblk[p] << block_shift;
+    ei += (nblk[p] + nbi - 1) / nbi;
+  }
+  if (p1 == n_pairs) {
+    ebase[n_pairs] = all_rows;
+    ipref[n_pairs] = (uint32_t)all_items;
+    for (long long x = b_prev + 1; x <= n_batches; ++x) bstart[x] = n_pairs;
+  }
+}
+
+// Work items of every pair: items[ipref[pair] + kr] = {pair, word holding block rank kr * (128 / B)}.
+__global__ __launch_bounds__(256) void k_tm_items(const uint32_t* __restrict__ umask,
+                                                  const uint32_t* __restrict__ pre,
+                                                  const uint32_t* __restrict__ ipref, TmItem* __restrict__ items,
+                                                  int n_tokens, int n_groups, int tile, int block_shift, int n_tiles,
+                                                  int n_words) {
+  const int pair = blockIdx.x;
+  const int t = pair / n_groups, g = pair - t * n_groups;
+  const int c_hi = tm_chi(t, n_tokens, tile, block_shift);
+  const int n_w = (c_hi >> 5) + 1;
+  const uint32_t* mrow = umask + ((long long)g * n_tiles + t) * n_words;
+  const uint32_t* prow = pre + (long long)pair * n_words;
+  const uint32_t base = ipref[pair];
+  const int nbi = kTmKeys >> block_shift;
+  for (int w = (int)threadIdx.x; w < n_w; w += 256) {
+    const int c = __popc(tm_word(mrow, w, c_hi));
+    if (c == 0) continue;
+    const int p = (int)prow[w];
+    for (int kr = (p + nbi - 1) / nbi; kr * nbi < p + c; ++kr) items[base + kr] = TmItem{(uint32_t)pair, (uint32_t)w};
+  }
+}
+
+// Work items of batch `batch`: every key's partial row of the item's tile (see above). A
+// persistent grid (a multiple of 8 workgroups): XCD x takes the x-th eighth of the batch's items,
+// so the items of one pair, which read the same rows, share an L2.
+__global__ __launch_bounds__(kTmWaves * 64) void k_tm_dkdv(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint32_t* __restrict__ umask, const float* __restrict__ lse, const float* __restrict__ delta,
+    const uint16_t* __restrict__ dout, const uint32_t* __restrict__ pre, const unsigned long long* __restrict__ ebase,
+    const uint32_t* __restrict__ ipref, const int* __restrict__ bstart, const TmItem* __restrict__ items,
+    float* __restrict__ part, int batch, int n_tokens, int n_q_heads, int n_groups, int block, int block_shift,
+    int tile, float scale_log2, int n_tiles, int n_words) {
+  __shared__ __align__(16) uint8_t rows0[kRgBytes];
+  __shared__ __align__(16) uint8_t rows1[kRgBytes];
+  __shared__ __align__(16) float lsde0[64];  // lse of the 32 rows, then delta
+  __shared__ __align__(16) float lsde1[64];
+  __shared__ __align__(16) int qrow0[32];    // query of each row (-1 past the tile)
+  __shared__ __align__(16) int qrow1[32];
+  __shared__ uint32_t blist[kTmKeys];        // the item's blocks
+  const int wave = threadIdx.x >> 6, l = lane_id(), hi = l >> 5;
+  const int ps = bstart[batch], pe = bstart[batch + 1];
+  if (ps >= pe) return;
+  const uint32_t it0 = ipref[ps];
+  const uint32_t n_items = ipref[pe] - it0;
+  const unsigned long long e0 = ebase[ps];
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, n_slot = gridDim.x >> 3;
+  const uint32_t i_lo = (uint32_t)(((unsigned long long)n_items * xcd) >> 3);
+  const uint32_t i_hi = (uint32_t)(((unsigned long long)n_items * (xcd + 1)) >> 3);
+
+  const int r = n_q_heads / n_groups;
+  // x / r for the row indices of a tile, as in k_bwd_dkdv (checked on the host).
+  const uint32_t r_magic = r > 1 ? (uint32_t)((0x100000000ull + (uint32_t)r - 1u) / (uint32_t)r) : 0u;
+  auto div_r = [&](int x) -> int { return r > 1 ? (int)__umulhi((uint32_t)x, r_magic) : x; };
+  const int nbi = kTmKeys >> block_shift;
+  const LaneOffsets lo = lane_offsets(0);
+  const bool r_div32 = (32 % r) == 0;
+  // This thread's share of a row group: 1-KiB slices ti = 2 wave, 2 wave + 1 of the Q and dO tiles
+  // (slice ti, lane l: row 4 ti + l / 16, physical piece l % 16, as in k_bwd_dkdv).
+  int frow[2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int rw = 4 * (2 * wave + x) + (l >> 4);
+    frow[x] = (rw / r) * n_q_heads + rw % r;
+  }
+  const int lrow = l & 31;
+  const int frow_l = (lrow / r) * n_q_heads + lrow % r, fq_l = lrow / r;
+
+  for (uint32_t ii = i_lo + slot; ii < i_hi; ii += n_slot) {
+    const uint32_t it = it0 + ii;
+    const TmItem item = items[it];
+    const int pair = (int)item.pair;
+    const int t = pair / n_groups, g = pair - t * n_groups;
+    const int kr = (int)(it - ipref[pair]);
+    const unsigned long long eb = ebase[pair];
+    const int nblk = (int)((ebase[pair + 1] - eb) >> block_shift);
+    const int r0 = kr * nbi;
+    const int n_r = min(nbi, nblk - r0);
+    const int i0 = t * tile;
+    const int c_hi = tm_chi(t, n_tokens, tile, block_shift);
+    const int nrows = (min(n_tokens, i0 + tile) - i0) * r;
+    const int n_rg = (nrows + 31) >> 5;
+
+    // Row group rg of the tile into registers (clamped to the last group: the loads past the end
+    // are repeats, never stored where they are read).
+    const long long tbase = (long long)i0 * n_q_heads + g * r;
+    auto load_rg = [&](int rg, u32x4 (&sq)[2], u32x4 (&sd)[2], float& ls, float& de, int& qi)
+                       __attribute__((always_inline)) {
+      rg = min(rg, n_rg - 1);
+      long long gbase = 0;
+      if (r_div32) gbase = tbase + (long long)(rg * (32 / r)) * n_q_heads;
+      if (wave == 0) {
+        const int rho = rg * 32 + lrow;
+        long long rix;
+        int qq;
+        if (r_div32) {
+          qq = rg * (32 / r) + fq_l;
+          rix = rho < nrows ? gbase + frow_l : tbase;
+        } else {
+          const int rr = rho < nrows ? rho : 0;
+          qq = div_r(rr);
+          rix = tbase + (long long)qq * n_q_heads + (rr - qq * r);
+        }
+        ls = lse[rix];
+        de = delta[rix];
+        qi = rho < nrows ? i0 + qq : -1;
+      }
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int rw = 4 * (2 * wave + x) + (l >> 4);
+        const int rho = rg * 32 + rw;
+        long long src_row;
+        if (r_div32) {
+          src_row = rho < nrows ? gbase + frow[x] : tbase;
+        } else {
+          const int rr = rho < nrows ? rho : 0;
+          const int qq = div_r(rr);
+          src_row = tbase + (long long)qq * n_q_heads + (rr - qq * r);
+        }
+        const int piece = v_phys(rw, l & 15);
+        sq[x] = *reinterpret_cast<const u32x4*>(q + src_row * kD + piece * 8);
+        sd[x] = *reinterpret_cast<const u32x4*>(dout + src_row * kD + piece * 8);
+      }
+    };
+    auto store_rg = [&](uint8_t* b, float* lsde, int* qrow, const u32x4 (&sq)[2], const u32x4 (&sd)[2], float ls,
+                        float de, int qi) __attribute__((always_inline)) {
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int ti = 2 * wave + x;
+        *reinterpret_cast<u32x4*>(b + ti * 1024 + 16 * l) = sq[x];
+        *reinterpret_cast<u32x4*>(b + kRowTileBytes + ti * 1024 + 16 * l) = sd[x];
+      }
+      if (wave == 0 && l < 32) {
+        lsde[l] = ls;
+        lsde[32 + l] = de;
+        qrow[l] = qi;
+      }
+    };
+    u32x4 sqa[2], sda[2], sqb[2], sdb[2];
+    float lsa = 0.0f, dea = 0.0f, lsb = 0.0f, deb = 0.0f;
+    int qia = -1, qib = -1;
+    load_rg(0, sqa, sda, lsa, dea, qia);
+    load_rg(1, sqb, sdb, lsb, deb, qib);
+
+    // The item's blocks (ranks r0 .. r0 + n_r - 1 of the union) into blist: lane l of wave 0 takes
+    // mask word item.word + l (+ 64 per round) and lists the item's ranks that fall in it.
+    if (wave == 0) {
+      const uint32_t* mrow = umask + ((long long)g * n_tiles + t) * n_words;
+      const uint32_t* prow = pre + (long long)pair * n_words;
+      const int n_w = (c_hi >> 5) + 1;
+      for (int w = (int)item.word + l;; w += 64) {
+        const bool in = w < n_w;
+        uint32_t m = in ? tm_word(mrow, w, c_hi) : 0u;
+        const int p = in ? (int)prow[w] : nblk;
+        const int c = __popc(m);
+        const int rlo = max(p, r0), rhi = min(p + c, r0 + n_r);
+        for (int s = p; s < rlo; ++s) m &= m - 1u;
+        for (int rr = rlo; rr < rhi; ++rr) {
+          blist[rr - r0] = (uint32_t)(w * 32 + __ffs(m) - 1);
+          m &= m - 1u;
+        }
+        if (__shfl(p + c, 63, 64) >= r0 + n_r) break;
+      }
+    }
+    store_rg(rows0, lsde0, qrow0, sqa, sda, lsa, dea, qia);
+    __syncthreads();
+
+    // This lane's key: entry kr * 128 + 32 wave + l % 32 of the union.
+    const int e = wave * 32 + (l & 31);
+    bool key_ok = (e >> block_shift) < n_r;
+    int key = key_ok ? (int)blist[e >> block_shift] * block + (e & (block - 1)) : 0;
+    key_ok = key_ok && key < n_tokens;
+    if (!key_ok) key = 0;
+    // Keys ascend with the entry, so lane 0 holds the wave's first key (none valid if it is not).
+    const bool wave_keys = __builtin_amdgcn_readfirstlane((int)key_ok) != 0;
+    const int key_min = __builtin_amdgcn_readfirstlane(key);
+
+    bf16x8 kb[8], vb[8];
+    {
+      const long long base = ((long long)g * n_tokens + key) * kD + 8 * hi;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        kb[ks] = *reinterpret_cast<const bf16x8*>(k + base + 16 * ks);
+        vb[ks] = *reinterpret_cast<const bf16x8*>(v + base + 16 * ks);
+      }
+    }
+    f32x16 adk[4], adv[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        adk[dt][j] = 0.0f;
+        adv[dt][j] = 0.0f;
+      }
+
+    // Step rg (P = rg % 2): group rg is in buffer P, group rg + 1 in register set 1 - P (set a for
+    // P = 1, b for P = 0); load group rg + 2 into the other set, compute rg, store rg + 1.
+    auto step = [&](auto parity, int rg) __attribute__((always_inline)) {
+      constexpr int P = decltype(parity)::value;
+      if (P == 0)
+        load_rg(rg + 2, sqa, sda, lsa, dea, qia);
+      else
+        load_rg(rg + 2, sqb, sdb, lsb, deb, qib);
+      const int last_q = i0 + div_r(min(rg * 32 + 31, nrows - 1));
+      if (wave_keys && last_q >= key_min)
+        dkdv_rows(P ? rows1 : rows0, P ? lsde1 : lsde0, P ? qrow1 : qrow0, key_ok, key, kb, vb, adk, adv, lo,
+                  scale_log2);
+      if (P == 0)
+        store_rg(rows1, lsde1, qrow1, sqb, sdb, lsb, deb, qib);
+      else
+        store_rg(rows0, lsde0, qrow0, sqa, sda, lsa, dea, qia);
+      __syncthreads();
+    };
+    for (int rg = 0; rg < n_rg; rg += 2) {
+      step(std::integral_constant<int, 0>(), rg);
+      if (rg + 1 < n_rg) step(std::integral_constant<int, 1>(), rg + 1);
+    }
+
+    // Partial row of this key: unscaled dK^T column (128 floats), then dV^T column.
+    if (key_ok) {
+      float* dst = part + ((eb - e0) + (unsigned long long)(kr * kTmKeys + e)) * kTmRowFloats;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int d = dt * 32 + 8 * a + 4 * hi;
+          *reinterpret_cast<f32x4*>(dst + d) =
+              f32x4{adk[dt][4 * a], adk[dt][4 * a + 1], adk[dt][4 * a + 2], adk[dt][4 * a + 3]};
+          *reinterpret_cast<f32x4*>(dst + kD + d) =
+              f32x4{adv[dt][4 * a], adv[dt][4 * a + 1], adv[dt][4 * a + 2], adv[dt][4 * a + 3]};
+        }
+    }
+  }
+}
+
+// acc[g][j] += the partial rows of key j from the batch's tiles, in ascending tile order (a
+// persistent grid over 64-key chunks). Wave w, step m handles key j0 + 4 m + w; lane l its floats
+// 4 l .. 4 l + 3. A tile's membership words for the chunk come 64 tiles at a time, one per lane.
+__global__ __launch_bounds__(256) void k_tm_reduce(const uint32_t* __restrict__ umask,
+                                                   const uint32_t* __restrict__ pre,
+                                                   const unsigned long long* __restrict__ ebase,
+                                                   const int* __restrict__ bstart, const float* __restrict__ part,
+                                                   float* __restrict__ acc, int batch, int n_tokens, int n_groups,
+                                                   int block_shift, int tile, int n_tiles, int n_words) {
+  const int ps = bstart[batch], pe = bstart[batch + 1];
+  if (ps >= pe) return;
+  const unsigned long long e0 = ebase[ps];
+  const int wave = threadIdx.x >> 6, l = lane_id();
+  const int cpg = (n_tokens + 63) >> 6;
+  const int n_chunks = cpg * n_groups;
+  for (int c = blockIdx.x; c < n_chunks; c += gridDim.x) {
+    const int g = c / cpg, j0 = (c - g * cpg) << 6;
+    // Tiles of this group in the batch (pairs t * G + g in [ps, pe)) that reach key j0.
+    const int t_lo = max(ps - g <= 0 ? 0 : (ps - g + n_groups - 1) / n_groups, j0 / tile);
+    const int t_hi = pe - g <= 0 ? 0 : (pe - g + n_groups - 1) / n_groups;
+    if (t_lo >= t_hi) continue;
+    const int b_first = j0 >> block_shift, b_last = (min(j0 + 63, n_tokens - 1)) >> block_shift;
+    const int wa = b_first >> 5, wb = b_last >> 5;  // wb = wa + 1 only for B = 1
+    const uint32_t ma_chunk = wb == wa ? ((b_last & 31) == 31 ? ~0u : (2u << (b_last & 31)) - 1u) &
+                                             ~((1u << (b_first & 31)) - 1u)
+                                       : ~((1u << (b_first & 31)) - 1u);
+    const uint32_t mb_chunk = wb == wa ? 0u : ((b_last & 31) == 31 ? ~0u : (2u << (b_last & 31)) - 1u);
+    bool started = false;
+    f32x4 a[16];
+    for (int tb = t_lo; tb < t_hi; tb += 64) {
+      const int tl = tb + l;
+      uint32_t wa_l = 0u, wb_l = 0u, pa_l = 0u, pb_l = 0u;
+      unsigned long long base_l = 0;
+      if (tl < t_hi) {
+        const int c_hi = tm_chi(tl, n_tokens, tile, block_shift);
+        const uint32_t* mrow = umask + ((long long)g * n_tiles + tl) * n_words;
+        wa_l = tm_word(mrow, wa, c_hi);
+        wb_l = wb == wa ? 0u : tm_word(mrow, wb, c_hi);
+      }
+      uint64_t hit = ballot(((wa_l & ma_chunk) | (wb_l & mb_chunk)) != 0u);
+      if (hit == 0) continue;
+      if ((wa_l & ma_chunk) | (wb_l & mb_chunk)) {
+        const int pair = tl * n_groups + g;
+        pa_l = pre[(long long)pair * n_words + wa];
+        pb_l = wb == wa ? 0u : pre[(long long)pair * n_words + wb];
+        base_l = ebase[pair] - e0;
+      }
+      if (!started) {
+        started = true;
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+          const int key = j0 + 4 * m + wave;
+          a[m] = key < n_tokens ? *reinterpret_cast<const f32x4*>(acc + ((long long)g * n_tokens + key) *
+                                                                      kTmRowFloats + 4 * l)
+                                : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+      }
+      while (hit) {
+        const int x = __builtin_ctzll(hit);
+        hit &= hit - 1;
+        const uint32_t wa_t = __builtin_amdgcn_readlane(wa_l, x), wb_t = __builtin_amdgcn_readlane(wb_l, x);
+        const uint32_t pa_t = __builtin_amdgcn_readlane(pa_l, x), pb_t = __builtin_amdgcn_readlane(pb_l, x);
+        const unsigned long long base_t =
+            ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((uint32_t)(base_l >> 32), x) << 32) |
+            (uint32_t)__builtin_amdgcn_readlane((uint32_t)base_l, x);
+        f32x4 xs[16];
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+          const int key = j0 + 4 * m + wave;
+          const int blk = key >> block_shift;
+          const bool in_b = (blk >> 5) != wa;
+          const uint32_t wd = in_b ? wb_t : wa_t;
+          const int bit = blk & 31;
+          const bool member = key < n_tokens && ((wd >> bit) & 1u);
+          const uint32_t rank = (in_b ? pb_t : pa_t) + __popc(wd & ((1u << bit) - 1u));
+          const unsigned long long row =
+              member ? base_t + ((unsigned long long)rank << block_shift) + (key & ((1 << block_shift) - 1)) : 0ull;
+          xs[m] = *reinterpret_cast<const f32x4*>(part + row * kTmRowFloats + 4 * l);
+          if (!member) xs[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+#pragma unroll
+        for (int m = 0; m < 16; ++m) a[m] += xs[m];
+      }
+    }
+    if (started) {
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        const int key = j0 + 4 * m + wave;
+        if (key < n_tokens)
+          *reinterpret_cast<f32x4*>(acc + ((long long)g * n_tokens + key) * kTmRowFloats + 4 * l) = a[m];
+      }
+    }
+  }
+}
+
+// dk = bf16(sigma * acc dK part), dv = bf16(acc dV part); 8 floats per thread.
+__global__ __launch_bounds__(256) void k_tm_final(const float* __restrict__ acc, uint16_t* __restrict__ dk,
+                                                  uint16_t* __restrict__ dv, long long n_rows, float scale) {
+  const long long x = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long row = x >> 5;
+  const int part = (int)(x & 31);
+  if (row >= n_rows) return;
+  const float* src = acc + row * kTmRowFloats + part * 8;
+  const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
+  const float s = part < 16 ? scale : 1.0f;
+  uint4 pk;
+  pk.x = pack_bf16x2(a[0] * s, a[1] * s);
+  pk.y = pack_bf16x2(a[2] * s, a[3] * s);
+  pk.z = pack_bf16x2(b[0] * s, b[1] * s);
+  pk.w = pack_bf16x2(b[2] * s, b[3] * s);
+  uint16_t* dst = (part < 16 ? dk : dv) + row * kD + (part & 15) * 8;
+  *reinterpret_cast<uint4*>(dst) = pk;
+}
+
+__global__ __launch_bounds__(256) void k_tm_zero(f32x4* __restrict__ p, long long n4) {
+  for (long long x = (long long)blockIdx.x * 256 + threadIdx.x; x < n4; x += (long long)gridDim.x * 256)
+    p[x] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
 // ------------------------------------------------------------------------------------ launch
 
 // Static LDS of the dq kernel (two stages, four token tables, scan words) and its dynamic part (the
@@ -652,17 +1153,81 @@ size_t attend_bwd_lds_dq(int n_tokens, int block) {
   return kDqStaticBytes + attend_bwd_dq_list_bytes(n_tokens, block);
 }
 
+// Workspace plan of the backward: delta first; with the tile-major dk/dv also the fp32 gradient
+// accumulator [G][N][256], the pair tables, the work items and the partial rows of one batch.
+BwdPlan attend_bwd_plan(int n_tokens, int n_q_heads, int n_groups, int block, int tile) {
+  BwdPlan pl;
+  auto rup = [](size_t x) { return (x + 255) / 256 * 256; };
+  pl.bytes = rup((size_t)n_tokens * n_q_heads * 4);
+  const char* path = getenv("SGQA_BWD_PATH");
+  if (path && strcmp(path, "key") == 0) return pl;
+  const int shift = __builtin_ctz(block);
+  const long long n_tiles = ((long long)n_tokens + tile - 1) / tile;
+  const long long nbc = ((long long)n_tokens + block - 1) / block;
+  const long long n_words = (nbc + 31) / 32;
+  const long long nbi = kTmKeys / block;
+  long long rows_bound = 0, items_bound = 0;
+  for (long long t = 0; t < n_tiles; ++t) {
+    const long long end = (t + 1) * tile < n_tokens ? (t + 1) * tile : n_tokens;
+    const long long nb = ((end - 1) >> shift) + 1;
+    rows_bound += (long long)n_groups * (nb << shift);
+    items_bound += (long long)n_groups * ((nb + nbi - 1) / nbi);
+  }
+  const long long unit_max = nbc << shift;  // the last tile's union at most
+  long long cap = kTmCapRows;
+  if (const char* e = getenv("SGQA_BWD_BATCH_ROWS")) {
+    const long long x = atoll(e);
+    if (x > 0 && x < cap) cap = x;
+  }
+  if (cap < 2 * unit_max) cap = 2 * unit_max;
+  long long hstep, n_batches;
+  if (cap >= rows_bound) {
+    cap = rows_bound;
+    hstep = rows_bound;
+    n_batches = 1;
+  } else {
+    hstep = cap - unit_max;
+    n_batches = (rows_bound - 1) / hstep + 1;
+  }
+  const long long n_pairs = n_tiles * n_groups;
+  if (n_batches > kTmMaxBatches || items_bound >= (1LL << 32) || n_pairs >= (1LL << 31)) return pl;
+  pl.tile_major = true;
+  pl.n_pairs = (int)n_pairs;
+  pl.n_batches = (int)n_batches;
+  pl.hstep = hstep;
+  pl.cap_rows = cap;
+  size_t off = pl.bytes;
+  auto take = [&](size_t b) {
+    const size_t o = off;
+    off += rup(b);
+    return o;
+  };
+  pl.o_acc = take((size_t)n_groups * n_tokens * kTmRowFloats * 4);
+  pl.o_nblk = take((size_t)n_pairs * 4);
+  pl.o_ebase = take((size_t)(n_pairs + 1) * 8);
+  pl.o_ipref = take((size_t)(n_pairs + 1) * 4);
+  pl.o_bstart = take((size_t)(n_batches + 1) * 4);
+  pl.o_pre = take((size_t)n_pairs * n_words * 4);
+  pl.o_items = take((size_t)items_bound * sizeof(TmItem));
+  pl.o_part = take((size_t)cap * kTmRowFloats * 4);
+  pl.bytes = off;
+  return pl;
+}
+
 hipError_t launch_attend_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint32_t* umask,
                              const uint16_t* out, const float* lse, const uint16_t* dout, uint16_t* dq, uint16_t* dk,
-                             uint16_t* dv, float* delta, int n_tokens, int n_q_heads, int n_groups, int block,
+                             uint16_t* dv, void* ws, int n_tokens, int n_q_heads, int n_groups, int block,
                              int tile, float scale, hipStream_t stream) {
   const long long n_rows = (long long)n_tokens * n_q_heads;
   if (n_rows == 0) return hipSuccess;
-  {  // the dk/dv kernel divides row indices by r with a multiply-high (see k_bwd_dkdv)
+  {  // the dk/dv kernels divide row indices by r with a multiply-high (see k_bwd_dkdv)
     const long long rr = n_q_heads / n_groups;
     const long long tr = (long long)(tile < n_tokens ? tile : n_tokens) * rr;
     if (tr * (rr - 1) >= (1LL << 32)) return hipErrorInvalidValue;
   }
+  const BwdPlan pl = attend_bwd_plan(n_tokens, n_q_heads, n_groups, block, tile);
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  float* delta = reinterpret_cast<float*>(wsb);
   hipLaunchKernelGGL(k_bwd_delta, dim3((unsigned)((n_rows + 15) / 16)), dim3(256), 0, stream, out, dout, delta,
                      n_rows);
   hipError_t e = hipGetLastError();
@@ -672,6 +1237,7 @@ hipError_t launch_attend_bwd(const uint16_t* q, const uint16_t* k, const uint16_
   const int nbc = (n_tokens + block - 1) / block;
   const int n_words = (nbc + 31) / 32;
   const int r = n_q_heads / n_groups;
+  const int shift = __builtin_ctz(block);
   const float scale_log2 = scale * 1.4426950408889634f;
   {
     const int rows_wg = kDqWaves * 32;
@@ -683,19 +1249,53 @@ hipError_t launch_attend_bwd(const uint16_t* q, const uint16_t* k, const uint16_
     const long long grid = (long long)((n_pairs + 7) / 8) * 8 * parts;
     auto kern = k_bwd_dq<kDqWaves>;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kDqWaves * 64), lds, stream, q, k, v, umask, lse, delta,
-                       dout, dq, n_tokens, n_q_heads, n_groups, block, __builtin_ctz(block), tile, scale,
-                       scale_log2, n_words, parts, n_pairs, dq_list_cap(n_tokens, block));
+                       dout, dq, n_tokens, n_q_heads, n_groups, block, shift, tile, scale, scale_log2, n_words,
+                       parts, n_pairs, dq_list_cap(n_tokens, block));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  {
+  if (!pl.tile_major) {
     const int chunks_per_g = (n_tokens + 32 * kBwdWaves - 1) / (32 * kBwdWaves);
     hipLaunchKernelGGL(k_bwd_dkdv, dim3((unsigned)(chunks_per_g * n_groups)), dim3(kBwdWaves * 64), 0, stream, q,
-                       k, v, umask, lse, delta, dout, dk, dv, n_tokens, n_q_heads, n_groups, block,
-                       __builtin_ctz(block), tile, scale, scale_log2, n_words);
-    e = hipGetLastError();
+                       k, v, umask, lse, delta, dout, dk, dv, n_tokens, n_q_heads, n_groups, block, shift, tile,
+                       scale, scale_log2, n_words);
+    return hipGetLastError();
   }
-  return e;
+  float* acc = reinterpret_cast<float*>(wsb + pl.o_acc);
+  uint32_t* nblk = reinterpret_cast<uint32_t*>(wsb + pl.o_nblk);
+  unsigned long long* ebase = reinterpret_cast<unsigned long long*>(wsb + pl.o_ebase);
+  uint32_t* ipref = reinterpret_cast<uint32_t*>(wsb + pl.o_ipref);
+  int* bstart = reinterpret_cast<int*>(wsb + pl.o_bstart);
+  uint32_t* pre = reinterpret_cast<uint32_t*>(wsb + pl.o_pre);
+  TmItem* items = reinterpret_cast<TmItem*>(wsb + pl.o_items);
+  float* part = reinterpret_cast<float*>(wsb + pl.o_part);
+  const long long acc_rows = (long long)n_groups * n_tokens;
+  hipLaunchKernelGGL(k_tm_zero, dim3(2048), dim3(256), 0, stream, reinterpret_cast<f32x4*>(acc),
+                     acc_rows * kTmRowFloats / 4);
+  hipLaunchKernelGGL(k_tm_prefix, dim3((unsigned)pl.n_pairs), dim3(256), 0, stream, umask, pre, nblk, n_tokens,
+                     n_groups, tile, shift, n_tiles, n_words);
+  hipLaunchKernelGGL(k_tm_plan, dim3(1), dim3(kTmPlanThreads), 0, stream, nblk, ebase, ipref, bstart, pl.n_pairs,
+                     shift, pl.hstep, pl.n_batches);
+  hipLaunchKernelGGL(k_tm_items, dim3((unsigned)pl.n_pairs), dim3(256), 0, stream, umask, pre, ipref, items,
+                     n_tokens, n_groups, tile, shift, n_tiles, n_words);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int cu = device_cu_count();
+  const unsigned main_grid = (unsigned)((cu + 7) / 8 * 8);
+  const long long n_chunks = (long long)n_groups * ((n_tokens + 63) / 64);
+  const unsigned red_grid = (unsigned)(n_chunks < 8LL * cu ? n_chunks : 8LL * cu);
+  for (int b = 0; b < pl.n_batches; ++b) {
+    hipLaunchKernelGGL(k_tm_dkdv, dim3(main_grid), dim3(kTmWaves * 64), 0, stream, q, k, v, umask, lse, delta, dout,
+                       pre, ebase, ipref, bstart, items, part, b, n_tokens, n_q_heads, n_groups, block, shift, tile,
+                       scale_log2, n_tiles, n_words);
+    hipLaunchKernelGGL(k_tm_reduce, dim3(red_grid), dim3(256), 0, stream, umask, pre, ebase, bstart, part, acc, b,
+                       n_tokens, n_groups, shift, tile, n_tiles, n_words);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_tm_final, dim3((unsigned)((acc_rows * 32 + 255) / 256)), dim3(256), 0, stream, acc, dk, dv,
+                     acc_rows, scale);
+  return hipGetLastError();
 }
 
 hipError_t prepare_attend_bwd_kernels(int lds_max) { return allow_full_lds((const void*)k_bwd_dq<kDqWaves>, lds_max); }

@@ -27,6 +27,7 @@ struct DeviceState {
   std::once_flag once;
   int status = SGQA_ERR_DEVICE;
   int lds_max = 65536;
+  int cu_count = 256;
   void* scratch = nullptr;  // this device's address of `scratch` (null if it could not be resolved)
 };
 DeviceState g_device[kMaxDevices];
@@ -48,6 +49,7 @@ DeviceState* device_state() {
     int v = 0;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0) v = 65536;
     d.lds_max = v;
+    if (prop.multiProcessorCount > 0) d.cu_count = prop.multiProcessorCount;
     d.status = prepare_kernels(v) == hipSuccess ? SGQA_OK : SGQA_ERR_HIP;
     void* ptr = nullptr;
     if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess) d.scratch = ptr;
@@ -66,6 +68,11 @@ int device_ready() {
 int max_lds_per_block() {
   const DeviceState* d = device_state();
   return d ? d->lds_max : 65536;
+}
+
+int device_cu_count() {
+  const DeviceState* d = device_state();
+  return d ? d->cu_count : 256;
 }
 
 hipError_t allow_full_lds(const void* fn, int lds_max) {
@@ -268,7 +275,8 @@ int sgqa_workspace_size(const sgqa_params* p, int op, size_t* bytes) {
       return st;
     case SGQA_OP_ATTEND_BWD:
       st = check_params(p, NEED_ATTN | NEED_UNION | NEED_LIST | NEED_BWD, true);
-      if (st == SGQA_OK) *bytes = round_up((size_t)p->n_tokens * p->n_q_heads * 4);
+      if (st == SGQA_OK)
+        *bytes = attend_bwd_plan(p->n_tokens, p->n_q_heads, p->n_kv_heads, p->block, p->union_tile).bytes;
       return st;
     case SGQA_OP_ATTEND_MASKED:
       st = check_params(p, NEED_ATTN | NEED_UNION | NEED_LIST | NEED_MASKED, true);
@@ -370,9 +378,10 @@ int sgqa_attend_bwd(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(umask) || !aligned16(ucount) || !aligned16(out) ||
       !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(ws))
     return SGQA_ERR_ALIGN;
-  if (!ws || ws_bytes < round_up((size_t)p->n_tokens * p->n_q_heads * 4)) return SGQA_ERR_WORKSPACE;
+  if (!ws || ws_bytes < attend_bwd_plan(p->n_tokens, p->n_q_heads, p->n_kv_heads, p->block, p->union_tile).bytes)
+    return SGQA_ERR_WORKSPACE;
   if ((st = device_ready()) != SGQA_OK) return st;
-  return status_of(launch_attend_bwd(q, k, v, umask, out, lse, dout, dq, dk, dv, static_cast<float*>(ws),
+  return status_of(launch_attend_bwd(q, k, v, umask, out, lse, dout, dq, dk, dv, ws,
                                      p->n_tokens, p->n_q_heads, p->n_kv_heads, p->block, p->union_tile, scale_of(p),
                                      (hipStream_t)stream));
 }

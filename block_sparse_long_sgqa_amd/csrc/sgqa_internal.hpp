@@ -62,11 +62,24 @@ hipError_t launch_attend(const uint16_t* q, const uint16_t* k, const uint16_t* v
                          const int32_t* ucount, uint16_t* out, int n_tokens, int n_q_heads, int n_groups, int block,
                          int tile, float scale, hipStream_t stream, float* lse = nullptr);
 
+// Workspace of the backward (attend_bwd_plan(...).bytes) and how dk/dv are computed: key-major
+// (one kernel) or tile-major (per-tile partial rows in batches, then an ordered sum). The
+// environment variable SGQA_BWD_PATH=key forces the key-major kernel; SGQA_BWD_BATCH_ROWS=n lowers
+// the partial rows per batch (at least twice the largest union's rows).
+struct BwdPlan {
+  bool tile_major = false;
+  int n_pairs = 0, n_batches = 0;
+  long long cap_rows = 0, hstep = 0;
+  size_t o_acc = 0, o_nblk = 0, o_ebase = 0, o_ipref = 0, o_bstart = 0, o_pre = 0, o_items = 0, o_part = 0;
+  size_t bytes = 0;  // whole workspace (the deltas first)
+};
+BwdPlan attend_bwd_plan(int n_tokens, int n_q_heads, int n_groups, int block, int tile);
+
 // Backward of launch_attend given its output and lse: dq [N][Hq][D], dk/dv [G][N][D] (bf16), from
-// dout [N][Hq][D]; delta [N][Hq] fp32 is scratch (rowwise <dout, out>).
+// dout [N][Hq][D]; ws holds attend_bwd_plan(...).bytes (the deltas <dout, out> per row first).
 hipError_t launch_attend_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint32_t* umask,
                              const uint16_t* out, const float* lse, const uint16_t* dout, uint16_t* dq, uint16_t* dk,
-                             uint16_t* dv, float* delta, int n_tokens, int n_q_heads, int n_groups, int block,
+                             uint16_t* dv, void* ws, int n_tokens, int n_q_heads, int n_groups, int block,
                              int tile, float scale, hipStream_t stream);
 size_t attend_bwd_lds_dq(int n_tokens, int block);
 
@@ -100,6 +113,8 @@ constexpr size_t kGfx950LdsBytes = 160 * 1024;
 
 // Largest dynamic LDS allocation one workgroup may use on the current device (bytes).
 int max_lds_per_block();
+// Compute units of the current device.
+int device_cu_count();
 
 // Once per device, before any launch: let every kernel that takes dynamic LDS use all that is left
 // beside its static LDS (lds_max = the device's limit per workgroup). One function per kernel file.

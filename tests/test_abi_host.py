@@ -93,6 +93,45 @@ def test_bad_shapes_are_rejected_before_any_launch(sg, kw):
     assert st == sg.SGQA_ERR_SHAPE
 
 
+def bwd_workspace(N, Hq, G, B, Tq, batch_rows=1 << 22, max_batches=1024):
+    """The backward's workspace as its header states it: the deltas (N Hq fp32), and for the
+    tile-major dk/dv (when its batches of partial rows number at most max_batches) the fp32
+    accumulator (G N rows of 1 KiB), nblk / ebase / ipref per pair, the batch starts, the word
+    prefixes (pairs x mask words), the work items (8 B) and one batch of 1-KiB partial rows."""
+    r = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    delta = r(N * Hq * 4)
+    T, nbc = -(-N // Tq), -(-N // B)
+    W, nbi = -(-nbc // 32), 128 // B
+    nb = [-(-min(N, (t + 1) * Tq) // B) for t in range(T)]
+    rows = G * sum(n * B for n in nb)
+    items = G * sum(-(-n // nbi) for n in nb)
+    unit = nbc * B
+    cap = max(min(batch_rows, 1 << 22), 2 * unit)
+    if cap >= rows:
+        cap, n_b = rows, 1
+    else:
+        n_b = (rows - 1) // (cap - unit) + 1
+    P = T * G
+    if n_b > max_batches:
+        return delta
+    return (delta + r(G * N * 1024) + r(P * 4) + r((P + 1) * 8) + r((P + 1) * 4) + r((n_b + 1) * 4)
+            + r(P * W * 4) + r(items * 8) + r(cap * 1024))
+
+
+@pytest.mark.parametrize("shape", [(131072, 64, 8, 8, 128), (32768, 64, 8, 8, 64), (20037, 8, 1, 1, 64),
+                                   (1205, 16, 2, 8, 64), (5, 16, 2, 8, 16)])
+def test_backward_workspace(sg, shape, monkeypatch):
+    N, Hq, G, B, Tq = shape
+    p = _p(n_tokens=N, n_q_heads=Hq, n_kv_heads=G, block=B, topk_tokens=max(B, 64), union_tile=Tq)
+    monkeypatch.delenv("SGQA_BWD_PATH", raising=False)
+    monkeypatch.delenv("SGQA_BWD_BATCH_ROWS", raising=False)
+    assert sg.workspace_size(p, sg.SGQA_OP_ATTEND_BWD) == bwd_workspace(N, Hq, G, B, Tq)
+    monkeypatch.setenv("SGQA_BWD_BATCH_ROWS", "1")
+    assert sg.workspace_size(p, sg.SGQA_OP_ATTEND_BWD) == bwd_workspace(N, Hq, G, B, Tq, batch_rows=1)
+    monkeypatch.setenv("SGQA_BWD_PATH", "key")
+    assert sg.workspace_size(p, sg.SGQA_OP_ATTEND_BWD) == (N * Hq * 4 + 255) // 256 * 256
+
+
 @pytest.mark.parametrize("n_tokens", [262144 + 8, 1 << 20])
 def test_long_context_prefill_is_accepted(sg, n_tokens):
     # The attention kernels walk a tile's block list in fixed-size LDS segments, so no sequence
@@ -103,7 +142,7 @@ def test_long_context_prefill_is_accepted(sg, n_tokens):
     T, W = (N + 127) // 128, ((N + 7) // 8 + 31) // 32
     assert sg.workspace_size(p, sg.SGQA_OP_PREFILL) == r(N // 8 * 64 * 2) + r(G * T * W * 4) + r(G * T * 4)
     assert sg.workspace_size(p, sg.SGQA_OP_ATTEND) == 0
-    assert sg.workspace_size(p, sg.SGQA_OP_ATTEND_BWD) == r(N * 64 * 4)
+    assert sg.workspace_size(p, sg.SGQA_OP_ATTEND_BWD) == bwd_workspace(N, 64, G, 8, 128)
     assert sg.workspace_size(p, sg.SGQA_OP_INDEX_TOPK) == 0
 
 

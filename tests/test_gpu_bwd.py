@@ -7,6 +7,8 @@ A bf16 operand carries a relative rounding error of at most 2^-9 ~ 2e-3; a sum o
 cancellation (the dS of a row sum to 0) keeps its absolute error near 2^-9 * sqrt(n) * term size,
 well inside 2e-2 s for the sizes here. Full-size runs check exact invariants instead.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -78,6 +80,28 @@ def run_fwd_bwd(sg, p, xd, umask, ucount, dout):
     return out, lse, dq, dk, dv
 
 
+# The two dk/dv designs: tile-major (per-tile partial rows summed in tile order; the default where
+# its batches stay few), the same with the smallest batches the plan allows (many batches, so the
+# ordered sum runs across batch boundaries), and key-major (the fallback for the longest contexts).
+MODES = {"tile": {}, "tile_batched": {"SGQA_BWD_BATCH_ROWS": "1"}, "key": {"SGQA_BWD_PATH": "key"}}
+
+
+class bwd_mode:
+    """Sets the library's backward-path environment variables for the duration of a block."""
+
+    def __init__(self, mode):
+        self.env = MODES[mode]
+
+    def __enter__(self):
+        for k in ("SGQA_BWD_PATH", "SGQA_BWD_BATCH_ROWS"):
+            os.environ.pop(k, None)
+        os.environ.update(self.env)
+
+    def __exit__(self, *a):
+        for k in self.env:
+            os.environ.pop(k, None)
+
+
 @pytest.mark.parametrize("name", list(BWD))
 def test_attend_bwd_matches_oracle(sg, name):
     wl = BWD[name]
@@ -93,19 +117,22 @@ def test_attend_bwd_matches_oracle(sg, name):
     xd = to_dev(x)
     um = torch.from_numpy(umask.view(np.int32)).cuda()
     uc = torch.from_numpy(ucount).cuda()
-    out, lse, dq, dk, dv = run_fwd_bwd(sg, p, xd, um, uc, dout.cuda())
-    # The forward with lse is the forward.
-    ref = torch.empty_like(out)
-    sg.sgqa_attend(p, xd["q"], xd["k"], xd["v"], um, uc, ref)
-    torch.cuda.synchronize()
-    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
-    assert_close_grad(dq, want_dq, f"dq {name}")
-    assert_close_grad(dk, want_dk, f"dk {name}")
-    assert_close_grad(dv, want_dv, f"dv {name}")
-    # Deterministic: a second run gives the same bits.
-    _, _, dq2, dk2, dv2 = run_fwd_bwd(sg, p, xd, um, uc, dout.cuda())
-    for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):
-        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    for mode in MODES:
+        say(f"attend_bwd {name}: dk/dv mode {mode}")
+        with bwd_mode(mode):
+            out, lse, dq, dk, dv = run_fwd_bwd(sg, p, xd, um, uc, dout.cuda())
+            # The forward with lse is the forward.
+            ref = torch.empty_like(out)
+            sg.sgqa_attend(p, xd["q"], xd["k"], xd["v"], um, uc, ref)
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+            assert_close_grad(dq, want_dq, f"dq {name} {mode}")
+            assert_close_grad(dk, want_dk, f"dk {name} {mode}")
+            assert_close_grad(dv, want_dv, f"dv {name} {mode}")
+            # Deterministic: a second run gives the same bits.
+            _, _, dq2, dk2, dv2 = run_fwd_bwd(sg, p, xd, um, uc, dout.cuda())
+            for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):
+                assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
 # Full-size checks: key ranges near the end (their rows span many tiles, so the dk/dv kernel walks
@@ -130,6 +157,18 @@ def test_attend_bwd_full_size(sg, name):
     dout = torch.randn((N, Hq, D), generator=gen, device="cuda").to(torch.bfloat16)
     say(f"attend_bwd {name}: forward + backward")
     out, lse, dq, dk, dv = run_fwd_bwd(sg, p, x, umask, ucount, dout)
+    # The key-major design on the same inputs: every key's gradient agrees with the tile-major
+    # one (both sum the same products in fp32, in different orders).
+    with bwd_mode("key"):
+        say(f"attend_bwd {name}: key-major dk/dv")
+        _, _, dq_k, dk_k, dv_k = run_fwd_bwd(sg, p, x, umask, ucount, dout)
+    assert torch.equal(dq.view(torch.int16), dq_k.view(torch.int16))
+    for a, b, what in ((dk, dk_k, "dk"), (dv, dv_k, "dv")):
+        scale = a.float().abs().max().item()
+        err = (a.float() - b.float()).abs()
+        say(f"{what} tile-major vs key-major: max {err.max().item() / scale:.3e} mean {err.mean().item() / scale:.3e}")
+        assert err.max().item() <= 1e-2 * scale and err.mean().item() <= 1e-4 * scale
+    del dq_k, dk_k, dv_k
 
     # Invariants over every key: sum_j dv[g][j] = sum over the group's rows of dout (each row's p
     # sums to 1), and sum_j dk[g][j] = 0 (each row's dS sums to 0), to within the bf16 rounding.
