@@ -149,14 +149,16 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
   // Gathers. Loop step n fetches the K tile of chunk n + 1 and the V tile of chunk n. Each lane
   // takes the tokens of its rows from the chunks' token tables, which the first wave writes two steps
   // ahead; invalid keys read row 0 of the group (finite data, masked out through the token table).
-  //  * Plain variant, register-staged: at the start of the step every wave loads its share of the
-  //    16 + 16 wave-wide 16-byte loads (1 KiB each) into registers, and after the mid-step barrier it
-  //    writes them to the tiles. The loads fly during the first half-period; unlike LDS-direct loads
-  //    they do not hold up the issuing wave, and the compiler has no LDS write in flight to wait for
-  //    before the operand reads (spreading them over the products, or issuing them from the softmax
-  //    group only, measured slower). K load i, lane l fills row (64 i + l) / 16, piece (64 i + l) % 16
-  //    (the padding piece of a K row is never written); V load i, lane l fills V slot 64 i + l of the
-  //    tile gather layout.
+  //  * Plain variant, register-staged: in the first half of the step every wave loads its share of
+  //    the 16 + 16 wave-wide 16-byte loads (1 KiB each) into registers, and after the mid-step barrier
+  //    it writes them to the tiles. Group 1 (softmax first) issues its loads at the start of the
+  //    step; group 0 issues one after every second k-step of its score products, so that the 32 loads
+  //    of a step do not reach the memory unit in one burst (2-4 % faster than all at the start; group
+  //    1 spreading its own loads over its second-half products, or issuing all of them from the
+  //    softmax group, measured slower). Unlike LDS-direct loads they do not hold up the issuing wave,
+  //    and the compiler has no LDS write in flight to wait for before the operand reads. K load i,
+  //    lane l fills row (64 i + l) / 16, piece (64 i + l) % 16 (the padding piece of a K row is never
+  //    written); V load i, lane l fills V slot 64 i + l of the tile gather layout.
   //  * Masked variant: LDS-direct loads (tile gather layout, 17 + 16 instructions) in one burst at the
   //    start of the step; it holds the membership state in registers and has none to stage with.
   constexpr bool kStaged = SEL_LOADS == 0;
@@ -318,27 +320,41 @@ __global__ __launch_bounds__(WAVES * 64) void k_attend(const uint16_t* __restric
     uint8_t* v_cur = P ? v_tile1 : v_tile0;   // V(n)
     uint8_t* v_prev = P ? v_tile0 : v_tile1;  // V(n - 1)
     const bool k_on = n + 1 < n_chunks, v_on = n < n_chunks;
-    // S(n) and P(n - 1) V(n - 1) at raised wave priority.
+    int tq[kPer];                    // tokens of this wave's gathers of step n
+    u32x4 stg[kStaged ? kPer : 1];  // staged gathers of step n
+    // S(n) and P(n - 1) V(n - 1) at raised wave priority. Staged variant: group 0 issues its gathers
+    // of the step here (a wave without rows issues them at once; in group 1 that repeats loads it
+    // has already stored, which is harmless and keeps the compiler's counter waits out of the
+    // products).
     auto products = [&]() __attribute__((always_inline)) {
-      if (!has_rows) return;
+      if (!has_rows) {
+        if (kStaged && n < n_chunks)
+#pragma unroll
+          for (int xi = 0; xi < kPer; ++xi) stage_load(xi, tq, stg[xi]);
+        return;
+      }
       __builtin_amdgcn_s_setprio(1);
-      if (n < n_chunks) score_products<QT, NoHook, kKAhead>(k_cur, lo, qreg, s);
+      if (n < n_chunks) {
+        auto hook = [&](int ks) __attribute__((always_inline)) {
+          if (kStaged && grp == 0 && (ks & 1) == 0 && (ks >> 1) < kPer) stage_load(ks >> 1, tq, stg[ks >> 1]);
+        };
+        score_products<QT, decltype(hook), kKAhead>(k_cur, lo, qreg, s, hook);
+      }
       if (n >= 1) pv_products<QT, kVAhead>(v_prev, lo, pb, st);
       __builtin_amdgcn_s_setprio(0);
     };
     if constexpr (SEL)
       if (n + 1 < n_chunks) sel_load(n + 1);
-    u32x4 stg[kStaged ? kPer : 1];
     if (n < n_chunks) {
-      int tq[kPer];
       gather_tokens(n, tq, k_on);
+      if (!kStaged || grp == 1)
 #pragma unroll
-      for (int xi = 0; xi < kPer; ++xi) {
-        if constexpr (kStaged)
-          stage_load(xi, tq, stg[xi]);
-        else
-          gather_one(xi, tq, k_next, v_cur, k_on, v_on);
-      }
+        for (int xi = 0; xi < kPer; ++xi) {
+          if constexpr (kStaged)
+            stage_load(xi, tq, stg[xi]);
+          else
+            gather_one(xi, tq, k_next, v_cur, k_on, v_on);
+        }
     }
     if (grp == 0) {
       products();
