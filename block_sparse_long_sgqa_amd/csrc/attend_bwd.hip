@@ -310,8 +310,44 @@ __global__ __launch_bounds__(WAVES * 64) void k_bwd_dq(const uint16_t* __restric
 
 namespace {
 constexpr int kTileWin = 256;                  // tiles listed per scan window
-constexpr int kRowTileBytes = 32 * 256;        // 32 rows x 128 bf16, swizzled like the forward's V tile
+constexpr int kRowTileBytes = 32 * 256;        // 32 rows x 128 bf16, pieces swizzled by rt_phys
 constexpr int kRgBytes = 2 * kRowTileBytes;    // Q rows, then dO rows
+
+// Row tiles are read both ways: row-wise, 16 bytes per lane (the A operands of S = Q K^T and
+// dP = dO V^T: 16 lanes read one logical piece of 16 consecutive rows), and transposed (two 4x16
+// transposing reads, as for the forward's V tile: 32 lanes read 4 logical pieces of 4 consecutive
+// rows). Physical piece of logical piece p in row `row`: XOR with 4 (row % 4) + (row / 4) % 4,
+// which gives each read phase of either kind 16 distinct pieces, i.e. all 64 banks once (the
+// forward's V swizzle, XOR with 4 (row % 4) alone, leaves the row-wise reads 4-way conflicted). The
+// swizzle repeats every 16 rows.
+__device__ __forceinline__ int rt_phys(int row, int p) { return p ^ (((row & 3) << 2) | ((row >> 2) & 3)); }
+
+// Per-lane byte offsets of the transposed reads of a row tile: d-tile dt, rows r (v0) and r + 8
+// (v1) of the lane's read (see lane_offsets for the forward's V tile); + 16 ss rows for the
+// second half of the 32 rows (the swizzle repeats every 16 rows).
+struct RowTileOffsets {
+  int v0[4], v1[4];
+};
+__device__ __forceinline__ RowTileOffsets row_tile_offsets() {
+  const int l = lane_id(), grp = l >> 4, s16 = l & 15;
+  const int row = 4 * (grp >> 1) + (s16 >> 2);
+  RowTileOffsets o;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    const int piece = 4 * dt + 2 * (grp & 1) + ((s16 & 3) >> 1);
+    o.v0[dt] = row * 256 + 16 * rt_phys(row, piece) + 8 * (s16 & 1);
+    o.v1[dt] = (row + 8) * 256 + 16 * rt_phys(row + 8, piece) + 8 * (s16 & 1);
+  }
+  return o;
+}
+
+// The two transposing reads of a row tile (at a0 + v0 and a0 + v1): a bf16x8 A operand.
+__device__ __forceinline__ bf16x8 rt_tr_read(const uint8_t* a0, int v0, int v1) {
+  const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0 + v0));
+  const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0 + v1));
+  const i16x8 cat = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, cat);
+}
 }  // namespace
 
 // One 32-row group against a wave's 32 keys (lane l holds key column l % 32): from the group's Q and
@@ -320,7 +356,7 @@ constexpr int kRgBytes = 2 * kRowTileBytes;    // Q rows, then dO rows
 // this lane's key is attended by the group's rows (causality is tested here).
 __device__ __forceinline__ void dkdv_rows(const uint8_t* b, const float* lsde, const int* qrow, bool take, int key,
                                           const bf16x8 (&kb)[8], const bf16x8 (&vb)[8], f32x16 (&adk)[4],
-                                          f32x16 (&adv)[4], const LaneOffsets& lo, float scale_log2) {
+                                          f32x16 (&adv)[4], const RowTileOffsets& lo, float scale_log2) {
   const int l = lane_id(), hi = l >> 5;
   const uint8_t* dob = b + kRowTileBytes;
   // S = Q K^T, dP = dO V^T: A operands row (l % 32), logical piece 2 ks + (l / 32).
@@ -332,7 +368,7 @@ __device__ __forceinline__ void dkdv_rows(const uint8_t* b, const float* lsde, c
   }
   // The operands of step ks + 2 are read while the products of step ks run.
   const int arow = l & 31;
-  auto off_of = [&](int ks) { return arow * 256 + 16 * v_phys(arow, 2 * ks + hi); };
+  auto off_of = [&](int ks) { return arow * 256 + 16 * rt_phys(arow, 2 * ks + hi); };
   bf16x8 qa[3], da[3];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
@@ -376,7 +412,9 @@ __device__ __forceinline__ void dkdv_rows(const uint8_t* b, const float* lsde, c
       pd[ss][e] = (__bf16)dp[8 * ss + e];
     }
   // dV^T += dO^T P, dK^T += Q^T dS; step = 2 dt + ss, operands read two steps ahead.
-  auto tr_op = [&](const uint8_t* base, int step) { return tr_read(base + lo.v[step >> 1] + (16 * (step & 1)) * 256); };
+  auto tr_op = [&](const uint8_t* base, int step) {
+    return rt_tr_read(base + (16 * (step & 1)) * 256, lo.v0[step >> 1], lo.v1[step >> 1]);
+  };
   bf16x8 oa[3], qt[3];
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
@@ -462,7 +500,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void k_bwd_dkdv(const uint16_t* __r
   const int nblk = block >= 32 ? 1 : 32 >> block_shift;
   const uint32_t wmask = nblk >= 32 ? 0xFFFFFFFFu : (((1u << nblk) - 1u) << (b0 & 31));
   const int my_blk = (key >> block_shift) - b0;  // this lane's block within the wave's blocks
-  const LaneOffsets lo = lane_offsets(0);
+  const RowTileOffsets lo = row_tile_offsets();
 
   // Row group `rg` of tile `t`: Q and dO rows into buffer `buf` (swizzled row-major, 8 + 8
   // wave-wide loads), and each row's query, lse and delta.
@@ -520,7 +558,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void k_bwd_dkdv(const uint16_t* __r
         const int qq = div_r(rr);
         src_row = tbase + (long long)qq * n_q_heads + (rr - qq * r);
       }
-      const int piece = v_phys(rw, l & 15);
+      const int piece = rt_phys(rw, l & 15);
       sq[ti] = *reinterpret_cast<const u32x4*>(q + src_row * kD + piece * 8);
       sd[ti] = *reinterpret_cast<const u32x4*>(dout + src_row * kD + piece * 8);
     }
@@ -835,7 +873,7 @@ __global__ __launch_bounds__(kTmWaves * 64) void k_tm_dkdv(
   const uint32_t r_magic = r > 1 ? (uint32_t)((0x100000000ull + (uint32_t)r - 1u) / (uint32_t)r) : 0u;
   auto div_r = [&](int x) -> int { return r > 1 ? (int)__umulhi((uint32_t)x, r_magic) : x; };
   const int nbi = kTmKeys >> block_shift;
-  const LaneOffsets lo = lane_offsets(0);
+  const RowTileOffsets lo = row_tile_offsets();
   const bool r_div32 = (32 % r) == 0;
   // This thread's share of a row group: 1-KiB slices ti = 2 wave, 2 wave + 1 of the Q and dO tiles
   // (slice ti, lane l: row 4 ti + l / 16, physical piece l % 16, as in k_bwd_dkdv).
@@ -899,7 +937,7 @@ __global__ __launch_bounds__(kTmWaves * 64) void k_tm_dkdv(
           const int qq = div_r(rr);
           src_row = tbase + (long long)qq * n_q_heads + (rr - qq * r);
         }
-        const int piece = v_phys(rw, l & 15);
+        const int piece = rt_phys(rw, l & 15);
         sq[x] = *reinterpret_cast<const u32x4*>(q + src_row * kD + piece * 8);
         sd[x] = *reinterpret_cast<const u32x4*>(dout + src_row * kD + piece * 8);
       }
