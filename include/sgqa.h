@@ -310,7 +310,16 @@ int sgqa_attend_fwd(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k
  *   dq[i][h] = sigma * sum_{j in J} p_ij (<dout[i][h], v[g][j]> - delta_i) k[g][j]
  * dq [N][Hq][D], dk, dv [G][N][D] bf16 out (fp32 sums, one bf16 rounding; keys no row attends get 0).
  * Deterministic: every sum has a fixed order (no floating-point atomics). Workspace:
- * sgqa_workspace_size(p, SGQA_OP_ATTEND_BWD) (the deltas). Shapes as sgqa_attend, and
+ * sgqa_workspace_size(p, SGQA_OP_ATTEND_BWD): the deltas and, for dk/dv, an fp32 accumulator
+ * [G][N][2D], the per-(tile, group) plan tables and work items, and the fp32 partial rows of one
+ * batch of tiles (at most 4 GiB; about 5.1 GiB in all at N = 131072, G = 8). dk/dv are summed
+ * tile by tile (every key's partial rows in ascending tile order) unless that needs more than 1024
+ * batches (the longest contexts), where a key-major kernel sums every key in one place; both give
+ * the same sums up to fp32 rounding order. Two environment variables, read by the host code at each
+ * call and meant for tests, select the design: SGQA_BWD_PATH=key forces the key-major kernel,
+ * SGQA_BWD_BATCH_ROWS=<n> caps a batch at n partial rows (never below twice the largest tile's
+ * rows); sgqa_workspace_size and sgqa_attend_bwd size the workspace for the design they select at
+ * that moment (a smaller workspace than the call needs -> SGQA_ERR_WORKSPACE). Shapes as sgqa_attend, and
  * min(Tq, N) * r * (r - 1) < 2^32 with r = Hq / G (otherwise SGQA_ERR_SHAPE). */
 int sgqa_attend_bwd(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k, const sgqa_bf16* v,
                     const uint32_t* umask, const int32_t* ucount, const sgqa_bf16* out, const float* lse,
