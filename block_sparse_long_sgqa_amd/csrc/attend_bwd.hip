@@ -15,12 +15,17 @@
 //    padded K and V tiles, Q and dO in registers), dS^T in the score registers, then
 //    dQ^T += K^T dS^T with K^T read transposed (ds_read_b64_tr_b16) from a second, swizzled copy of
 //    the K tile -- the forward's O^T += V^T P^T with V replaced by K.
-//  * dk, dv: key-major, so that every key's sum runs over its rows in one place. A wave owns 32
-//    consecutive keys of one group (their K and V as persistent B operands) and walks the tiles
-//    whose union holds one of its blocks; per 32-row group of such a tile, Q and dO rows are
-//    gathered into the wave's swizzled LDS tiles (double-buffered, one group ahead), S = Q K^T and
-//    dP = dO V^T give P and dS with the keys in the lane columns, and dV^T += dO^T P,
-//    dK^T += Q^T dS take dO^T and Q^T transposed from LDS.
+//  * dk, dv, tile-major (what runs unless the context is too long for its batches): a work item is
+//    128 keys of one tile union, four waves of 32 keys (K and V as persistent B operands); the
+//    tile's Q and dO rows stream once through shared LDS row tiles in 32-row groups, and every wave
+//    pipelines the groups (S and dP of the next group on the matrix cores while the vector ALU forms
+//    P and dS of the current one, then dV^T += dO^T P and dK^T += Q^T dS with transposed reads). Each
+//    item writes fp32 partial rows per key, summed per key in ascending tile order by a second
+//    kernel (see the tile-major section below).
+//  * dk, dv, key-major (the longest contexts): every key's sum runs over its rows in one place. A
+//    wave owns 32 consecutive keys of one group and walks the tiles whose union holds one of its
+//    blocks; per 32-row group of such a tile, Q and dO rows are gathered into the wave's swizzled
+//    LDS tiles (double-buffered, one group ahead), with the same products.
 #include <stdlib.h>
 #include <string.h>
 
@@ -841,6 +846,115 @@ __global__ __launch_bounds__(256) void k_tm_items(const uint32_t* __restrict__ u
   }
 }
 
+// One step of the tile-major row-group pipeline for a wave's 32 keys (lane l holds key column l % 32):
+// S = Q K^T and dP = dO V^T of the NEXT row group (buffer bn) go to the matrix cores while the vector
+// ALU turns the current group's S and dP (registers s, dp) into P and dS, one score element after
+// each product, so that one wave keeps both busy; then dV^T += dO^T P and dK^T += Q^T dS (unscaled)
+// of the current group (buffer bc, its rows' lse and delta in lsde, queries in qrow, -1 past the
+// tile). On return s, dp hold the next group's S and dP. The arithmetic of every element is that of
+// dkdv_rows.
+__device__ __forceinline__ void tm_pipe(const uint8_t* bn, const uint8_t* bc, const float* lsde, const int* qrow,
+                                        bool take, int key, const bf16x8 (&kb)[8], const bf16x8 (&vb)[8],
+                                        f32x16 (&adk)[4], f32x16 (&adv)[4], const RowTileOffsets& lo,
+                                        float scale_log2, f32x16& s, f32x16& dp) {
+  const int l = lane_id(), hi = l >> 5;
+  // Rows of score j: 8 (j / 4) + 4 hi + (j % 4).
+  int4 qi4[4];
+  float4 ls4[4], de4[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    qi4[a] = *reinterpret_cast<const int4*>(qrow + 8 * a + 4 * hi);
+    ls4[a] = *reinterpret_cast<const float4*>(lsde + 8 * a + 4 * hi);
+    de4[a] = *reinterpret_cast<const float4*>(lsde + 32 + 8 * a + 4 * hi);
+  }
+  auto elem = [&](int j) __attribute__((always_inline)) {
+    const int a = j >> 2, c = j & 3;
+    const int qi = c == 0 ? qi4[a].x : (c == 1 ? qi4[a].y : (c == 2 ? qi4[a].z : qi4[a].w));
+    const float ls = c == 0 ? ls4[a].x : (c == 1 ? ls4[a].y : (c == 2 ? ls4[a].z : ls4[a].w));
+    const float de = c == 0 ? de4[a].x : (c == 1 ? de4[a].y : (c == 2 ? de4[a].z : de4[a].w));
+    const bool ok = take && key <= qi;
+    const float p = ok ? fast_exp2(__builtin_fmaf(s[j], scale_log2, -ls)) : 0.0f;
+    s[j] = p;
+    dp[j] = p * (dp[j] - de);
+  };
+  f32x16 s2, dp2;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    s2[j] = 0.0f;
+    dp2[j] = 0.0f;
+  }
+  const uint8_t* dobn = bn + kRowTileBytes;
+  const int arow = l & 31;
+  auto off_of = [&](int ks) { return arow * 256 + 16 * rt_phys(arow, 2 * ks + hi); };
+  bf16x8 qa[3], da[3];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    qa[ks] = *reinterpret_cast<const bf16x8*>(bn + off_of(ks));
+    da[ks] = *reinterpret_cast<const bf16x8*>(dobn + off_of(ks));
+  }
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    if (ks + 2 < 8) {
+      qa[(ks + 2) % 3] = *reinterpret_cast<const bf16x8*>(bn + off_of(ks + 2));
+      da[(ks + 2) % 3] = *reinterpret_cast<const bf16x8*>(dobn + off_of(ks + 2));
+    }
+    s2 = mfma32(qa[ks % 3], kb[ks], s2);
+    elem(2 * ks);
+    dp2 = mfma32(da[ks % 3], vb[ks], dp2);
+    elem(2 * ks + 1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  bf16x8 pp[2], pd[2];
+#pragma unroll
+  for (int ss = 0; ss < 2; ++ss)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pp[ss][e] = (__bf16)s[8 * ss + e];
+      pd[ss][e] = (__bf16)dp[8 * ss + e];
+    }
+  // dV^T += dO^T P, dK^T += Q^T dS; step = 2 dt + ss, operands read two steps ahead.
+  const uint8_t* dobc = bc + kRowTileBytes;
+  auto tr_op = [&](const uint8_t* base, int step) {
+    return rt_tr_read(base + (16 * (step & 1)) * 256, lo.v0[step >> 1], lo.v1[step >> 1]);
+  };
+  bf16x8 oa[3], qt[3];
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    oa[st] = tr_op(dobc, st);
+    qt[st] = tr_op(bc, st);
+  }
+#pragma unroll
+  for (int st = 0; st < 8; ++st) {
+    if (st + 2 < 8) {
+      oa[(st + 2) % 3] = tr_op(dobc, st + 2);
+      qt[(st + 2) % 3] = tr_op(bc, st + 2);
+    }
+    const int dt = st >> 1, ss = st & 1;
+    adv[dt] = mfma32(oa[st % 3], pp[ss], adv[dt]);
+    adk[dt] = mfma32(qt[st % 3], pd[ss], adk[dt]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  s = s2;
+  dp = dp2;
+}
+
+// S and dP of the first row group (buffer b) for tm_pipe.
+__device__ __forceinline__ void tm_first(const uint8_t* b, const bf16x8 (&kb)[8], const bf16x8 (&vb)[8], f32x16& s,
+                                         f32x16& dp) {
+  const int l = lane_id(), hi = l >> 5, arow = l & 31;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    s[j] = 0.0f;
+    dp[j] = 0.0f;
+  }
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const int off = arow * 256 + 16 * rt_phys(arow, 2 * ks + hi);
+    s = mfma32(*reinterpret_cast<const bf16x8*>(b + off), kb[ks], s);
+    dp = mfma32(*reinterpret_cast<const bf16x8*>(b + kRowTileBytes + off), vb[ks], dp);
+  }
+}
+
 // Work items of batch `batch`: every key's partial row of the item's tile (see above). A
 // persistent grid (a multiple of 8 workgroups): XCD x takes the x-th eighth of the batch's items,
 // so the items of one pair, which read the same rows, share an L2.
@@ -851,12 +965,15 @@ __global__ __launch_bounds__(kTmWaves * 64) void k_tm_dkdv(
     const uint32_t* __restrict__ ipref, const int* __restrict__ bstart, const TmItem* __restrict__ items,
     float* __restrict__ part, int batch, int n_tokens, int n_q_heads, int n_groups, int block, int block_shift,
     int tile, float scale_log2, int n_tiles, int n_words) {
-  __shared__ __align__(16) uint8_t rows0[kRgBytes];
+  __shared__ __align__(16) uint8_t rows0[kRgBytes];  // row groups rg % 3 == 0, 1, 2
   __shared__ __align__(16) uint8_t rows1[kRgBytes];
+  __shared__ __align__(16) uint8_t rows2[kRgBytes];
   __shared__ __align__(16) float lsde0[64];  // lse of the 32 rows, then delta
   __shared__ __align__(16) float lsde1[64];
+  __shared__ __align__(16) float lsde2[64];
   __shared__ __align__(16) int qrow0[32];    // query of each row (-1 past the tile)
   __shared__ __align__(16) int qrow1[32];
+  __shared__ __align__(16) int qrow2[32];
   __shared__ uint32_t blist[kTmKeys];        // the item's blocks
   const int wave = threadIdx.x >> 6, l = lane_id(), hi = l >> 5;
   const int ps = bstart[batch], pe = bstart[batch + 1];
@@ -983,6 +1100,8 @@ __global__ __launch_bounds__(kTmWaves * 64) void k_tm_dkdv(
       }
     }
     store_rg(rows0, lsde0, qrow0, sqa, sda, lsa, dea, qia);
+    store_rg(rows1, lsde1, qrow1, sqb, sdb, lsb, deb, qib);
+    load_rg(2, sqa, sda, lsa, dea, qia);
     __syncthreads();
 
     // This lane's key: entry kr * 128 + 32 wave + l % 32 of the union.
@@ -993,7 +1112,6 @@ __global__ __launch_bounds__(kTmWaves * 64) void k_tm_dkdv(
     if (!key_ok) key = 0;
     // Keys ascend with the entry, so lane 0 holds the wave's first key (none valid if it is not).
     const bool wave_keys = __builtin_amdgcn_readfirstlane((int)key_ok) != 0;
-    const int key_min = __builtin_amdgcn_readfirstlane(key);
 
     bf16x8 kb[8], vb[8];
     {
@@ -1013,27 +1131,28 @@ __global__ __launch_bounds__(kTmWaves * 64) void k_tm_dkdv(
         adv[dt][j] = 0.0f;
       }
 
-    // Step rg (P = rg % 2): group rg is in buffer P, group rg + 1 in register set 1 - P (set a for
-    // P = 1, b for P = 0); load group rg + 2 into the other set, compute rg, store rg + 1.
-    auto step = [&](auto parity, int rg) __attribute__((always_inline)) {
-      constexpr int P = decltype(parity)::value;
-      if (P == 0)
-        load_rg(rg + 2, sqa, sda, lsa, dea, qia);
-      else
-        load_rg(rg + 2, sqb, sdb, lsb, deb, qib);
-      const int last_q = i0 + div_r(min(rg * 32 + 31, nrows - 1));
-      if (wave_keys && last_q >= key_min)
-        dkdv_rows(P ? rows1 : rows0, P ? lsde1 : lsde0, P ? qrow1 : qrow0, key_ok, key, kb, vb, adk, adv, lo,
-                  scale_log2);
-      if (P == 0)
-        store_rg(rows1, lsde1, qrow1, sqb, sdb, lsb, deb, qib);
-      else
-        store_rg(rows0, lsde0, qrow0, sqa, sda, lsa, dea, qia);
+    // Step rg (B = rg % 3): groups rg and rg + 1 are in buffers B and B + 1 (mod 3), group rg + 2 in
+    // register set a, and s, dp hold S and dP of group rg. The step stores group rg + 2 into buffer
+    // B + 2 (read last in step rg - 1), loads group rg + 3, and runs tm_pipe: P and dS of group rg
+    // with S and dP of group rg + 1, then dV and dK of group rg. Every step issues the same loads and
+    // stores (groups past the tile repeat the last one and are never computed).
+    f32x16 s, dp;
+    if (wave_keys) tm_first(rows0, kb, vb, s, dp);
+    auto step = [&](auto phase, int rg) __attribute__((always_inline)) {
+      constexpr int B = decltype(phase)::value;
+      uint8_t* const bufs[3] = {rows0, rows1, rows2};
+      float* const lsdes[3] = {lsde0, lsde1, lsde2};
+      int* const qrows[3] = {qrow0, qrow1, qrow2};
+      store_rg(bufs[(B + 2) % 3], lsdes[(B + 2) % 3], qrows[(B + 2) % 3], sqa, sda, lsa, dea, qia);
+      load_rg(rg + 3, sqa, sda, lsa, dea, qia);
+      if (wave_keys && rg < n_rg)
+        tm_pipe(bufs[(B + 1) % 3], bufs[B], lsdes[B], qrows[B], key_ok, key, kb, vb, adk, adv, lo, scale_log2, s, dp);
       __syncthreads();
     };
-    for (int rg = 0; rg < n_rg; rg += 2) {
+    for (int rg = 0; rg < n_rg; rg += 3) {
       step(std::integral_constant<int, 0>(), rg);
-      if (rg + 1 < n_rg) step(std::integral_constant<int, 1>(), rg + 1);
+      step(std::integral_constant<int, 1>(), rg + 1);
+      step(std::integral_constant<int, 2>(), rg + 2);
     }
 
     // Partial row of this key: unscaled dK^T column (128 floats), then dV^T column.
