@@ -128,7 +128,7 @@ def test_index_topk_bit_exact(sg, name):
 
 
 @pytest.mark.parametrize("case", ["zero_queries", "dense_k", "negative_weights", "all_equal_keys",
-                                  "strided_outliers"])
+                                  "strided_outliers", "sample_sees_only_the_top"])
 def test_index_topk_degenerate_cases(sg, case):
     wl = datagen.PREFILL.replace(name=f"deg_{case}", n_tokens=2500, n_q_heads=16, n_kv_heads=2, topk_tokens=400,
                                  union_tile=32)
@@ -138,6 +138,12 @@ def test_index_topk_degenerate_cases(sg, case):
         # Every 4th block scores far above the rest and the others tie in small groups: a strided
         # sample of the candidates is unrepresentative (the kernel must still be exact).
         wl = wl.replace(n_tokens=4096, topk_tokens=128)
+    if case == "sample_sees_only_the_top":
+        # Odd blocks score above zero, even blocks exactly zero. Rows with 641..1152 candidates
+        # take their threshold from a stride-2 sample of the odd blocks only, which sets it above
+        # the true K_B-th score in most rows: those rows must take every candidate in a second
+        # pass (the kernel must still be exact).
+        wl = wl.replace(n_tokens=8192 + 5, topk_tokens=256)
     x = datagen.prefill_inputs(wl)
     if case == "zero_queries":
         x["qi"] = torch.zeros_like(x["qi"])
@@ -153,6 +159,14 @@ def test_index_topk_degenerate_cases(sg, case):
             ki[sel] = 4.0 if res == 2 else 3.0
         x["ki"] = ki.to(torch.bfloat16)
         x["qi"] = x["qi"].abs()
+    if case == "sample_sees_only_the_top":
+        gen = torch.Generator().manual_seed(12)
+        blocks = torch.arange(wl.n_tokens) // wl.block
+        mag = torch.randint(1, 5, x["ki"].shape, generator=gen).float()
+        sign = torch.where(blocks % 2 == 1, 1.0, -1.0).unsqueeze(1)
+        x["ki"] = (mag * sign).to(torch.bfloat16)
+        x["qi"] = x["qi"].abs()
+        x["w"] = x["w"].abs()
     p = params_of(wl)
     ch = OracleChain(x, p)
     say(f"index_topk degenerate {case}")
