@@ -13,6 +13,10 @@ import datagen
 import oracle
 
 # Attention tolerance on unit-scale outputs (max-abs and mean-abs error against the fp64 oracle).
+# The max-abs bar scales with the output where an output exceeds unit scale (queries attending a
+# handful of keys return nearly single V rows, up to ~4.5 for N(0,1) values): per element
+# |got - want| <= MAX_ABS * max(1, |want|). Rounding the exact output to the bf16 result alone costs
+# up to 2^-9 |want|, 0.0078 at |want| = 4, most of an absolute 1e-2.
 MAX_ABS = 1e-2
 MEAN_ABS = 1e-3
 
@@ -46,8 +50,9 @@ def assert_close_attention(got_bf16: torch.Tensor, want_f64: np.ndarray, what: s
     err = np.abs(got - want_f64)
     assert np.isfinite(got).all(), f"{what}: non-finite outputs"
     mx, mean = float(err.max()), float(err.mean())
-    say(f"{what}: max_abs={mx:.3e} mean_abs={mean:.3e}")
-    assert mx <= MAX_ABS, f"{what}: max abs error {mx}"
+    rel = float((err / np.maximum(1.0, np.abs(want_f64))).max())
+    say(f"{what}: max_abs={mx:.3e} mean_abs={mean:.3e} max_abs/max(1,|want|)={rel:.3e}")
+    assert rel <= MAX_ABS, f"{what}: max error {rel} of max(1, |want|) (max abs {mx})"
     assert mean <= MEAN_ABS, f"{what}: mean abs error {mean}"
 
 

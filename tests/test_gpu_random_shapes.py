@@ -1,0 +1,137 @@
+"""GPU parity on seeded random shapes, end to end through the C ABI against the oracle.
+
+The fixed cases elsewhere list chosen shapes; here sequence length, query and KV head counts, block
+size, k and union tile are drawn together (fixed seeds), so combinations none of them lists meet the
+oracle: ragged last blocks, chunks and tiles at once, K_B that is not a multiple of a chunk's
+blocks, K_B above or below the candidate count, one or several KV groups, head ratios from 1 to 8.
+Selections (top-k and the fused tile union) must be bit-exact; attention outputs within the
+attention tolerance; gradients within the relative gradient bar of the backward tests. Every draw
+is sized so that the fp64 oracle takes seconds.
+"""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+from tests.gpu_common import OracleChain, assert_close_attention, bits, params_of, say, to_dev
+from tests.test_gpu_bwd import assert_close_grad, run_fwd_bwd
+
+pytestmark = pytest.mark.gpu
+
+N_PREFILL = 40
+N_DECODE = 20
+
+
+@pytest.fixture(scope="module")
+def sg():
+    import block_sparse_long_sgqa_amd as sg
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    sg.lib()
+    return sg
+
+
+def draw_prefill(seed: int) -> datagen.Workload:
+    rng = np.random.default_rng(7000 + seed)
+    B = int(rng.choice([1, 2, 4, 8, 16, 32, 64]))
+    G = int(rng.choice([1, 2, 3, 4]))
+    r = int(rng.choice([1, 2, 4, 8]))
+    N = int(rng.integers(2 * B, 2600))  # sequences shorter than a block are covered by the fixed cases
+    kb = int(rng.integers(1, 260 if B > 1 else 700))
+    tile = int(rng.choice([1, 7, 16, 33, 64, 128]))
+    qi_mode = str(rng.choice(["iid", "corr"]))
+    return datagen.PREFILL.replace(name=f"rand_prefill_{seed}", n_tokens=N, n_q_heads=G * r, n_kv_heads=G,
+                                   block=B, topk_tokens=kb * B, union_tile=tile, qi_mode=qi_mode)
+
+
+def describe(wl: datagen.Workload) -> str:
+    return (f"N={wl.n_tokens} Hq={wl.n_q_heads} G={wl.n_kv_heads} B={wl.block} K_B={wl.kb} "
+            f"Tq={wl.union_tile} qi={wl.qi_mode}")
+
+
+@pytest.mark.parametrize("seed", range(N_PREFILL))
+def test_random_prefill(sg, seed):
+    wl = draw_prefill(seed)
+    p = params_of(wl)
+    x = datagen.prefill_inputs(wl)
+    ch = OracleChain(x, p)
+    sel = ch.topk()
+    want_mask, want_cnt = oracle.union(sel, p.n_tokens, p.block, p.union_tile)
+    want = oracle.attend(bits(x["q"]), bits(x["k"]), bits(x["v"]), want_mask, p.block, p.union_tile)
+    say(f"random prefill {seed}: {describe(wl)}")
+    xd = to_dev(x)
+    G, N = p.n_kv_heads, p.n_tokens
+    kbar = torch.from_numpy(ch.kbar.view(np.int16)).view(torch.bfloat16).cuda().reshape(-1, p.idx_dim)
+    blk = torch.empty((N // p.block, p.idx_dim), dtype=torch.bfloat16, device="cuda")
+    if N // p.block > 0:
+        sg.sgqa_compress(p, xd["ki"], blk)
+    topk = torch.empty((G, N, p.kb), dtype=torch.int32, device="cuda")
+    sg.sgqa_index_topk(p, xd["qi"], xd["w"], kbar, topk)
+    umask = torch.empty((G, p.n_tiles, p.n_words), dtype=torch.int32, device="cuda")
+    ucount = torch.empty((G, p.n_tiles), dtype=torch.int32, device="cuda")
+    sg.sgqa_index_union(p, xd["qi"], xd["w"], kbar, umask, ucount)
+    out = torch.empty((N, p.n_q_heads, p.head_dim), dtype=torch.bfloat16, device="cuda")
+    sg.sgqa_prefill(p, xd["q"], xd["k"], xd["v"], xd["qi"], xd["w"], xd["ki"], out,
+                    sg.workspace(p, sg.SGQA_OP_PREFILL))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(blk), ch.kbar)
+    np.testing.assert_array_equal(topk.cpu().numpy(), sel)
+    np.testing.assert_array_equal(umask.cpu().numpy().view(np.uint32), want_mask)
+    np.testing.assert_array_equal(ucount.cpu().numpy(), want_cnt)
+    assert_close_attention(out, want, f"random prefill {seed}")
+
+
+@pytest.mark.parametrize("seed", [s for s in range(N_PREFILL) if draw_prefill(s).n_tokens <= 1600])
+def test_random_backward(sg, seed):
+    wl = draw_prefill(seed)
+    p = params_of(wl)
+    x = datagen.prefill_inputs(wl)
+    ch = OracleChain(x, p)
+    umask, ucount = oracle.union(ch.topk(), p.n_tokens, p.block, p.union_tile)
+    g = torch.Generator().manual_seed(31 + seed)
+    dout = torch.randn((p.n_tokens, p.n_q_heads, p.head_dim), generator=g).to(torch.bfloat16)
+    want_dq, want_dk, want_dv = oracle.attend_bwd(bits(x["q"]), bits(x["k"]), bits(x["v"]), umask, bits(dout),
+                                                  p.block, p.union_tile)
+    say(f"random backward {seed}: {describe(wl)}")
+    xd = to_dev(x)
+    um = torch.from_numpy(umask.view(np.int32)).cuda()
+    uc = torch.from_numpy(ucount).cuda()
+    _, _, dq, dk, dv = run_fwd_bwd(sg, p, xd, um, uc, dout.cuda())
+    assert_close_grad(dq, want_dq, f"dq random {seed}")
+    assert_close_grad(dk, want_dk, f"dk random {seed}")
+    assert_close_grad(dv, want_dv, f"dv random {seed}")
+
+
+def draw_decode(seed: int) -> datagen.Workload:
+    rng = np.random.default_rng(9100 + seed)
+    B = int(rng.choice([1, 2, 4, 8, 16, 32, 64]))
+    G = int(rng.choice([1, 2, 3, 5, 8]))
+    S = int(rng.integers(1, 5))
+    L = int(rng.integers(2 * B, 40000))
+    kb = int(rng.integers(1, 1500))
+    return datagen.DECODE.replace(name=f"rand_decode_{seed}", n_tokens=L, n_seqs=S, n_q_heads=8 * G, n_kv_heads=G,
+                                  topk_tokens=kb * B, block=B)
+
+
+@pytest.mark.parametrize("seed", range(N_DECODE))
+def test_random_decode(sg, seed):
+    wl = draw_decode(seed)
+    p = params_of(wl)
+    S, L, G, B = wl.n_seqs, wl.n_tokens, wl.n_kv_heads, wl.block
+    x = datagen.decode_inputs(wl)
+    kbar = oracle.compress(bits(x["ki_cache"]), B)
+    want_sel, want_out = oracle.decode(x["q"], x["k_cache"], x["v_cache"], kbar, x["qi"], x["w"], B, p.kb)
+    say(f"random decode {seed}: L={L} S={S} G={G} B={B} K_B={p.kb}")
+    xd = to_dev(x)
+    blk = torch.empty((S, L // B, 64), dtype=torch.bfloat16, device="cuda")
+    if L // B > 0:
+        sg.sgqa_compress(p, xd["ki_cache"], blk)
+    out = torch.empty((S, p.n_q_heads, 128), dtype=torch.bfloat16, device="cuda")
+    topk = torch.empty((S, G, p.kb), dtype=torch.int32, device="cuda")
+    sg.sgqa_decode(p, xd["q"], xd["k_cache"], xd["v_cache"], blk, xd["qi"], xd["w"], out, sg.workspace(p, sg.SGQA_OP_DECODE),
+                   topk_out=topk)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(blk), kbar.reshape(bits(blk).shape))
+    np.testing.assert_array_equal(topk.cpu().numpy(), want_sel)
+    assert_close_attention(out, want_out, f"random decode {seed}")
