@@ -135,3 +135,110 @@ def test_random_decode(sg, seed):
     np.testing.assert_array_equal(bits(blk), kbar.reshape(bits(blk).shape))
     np.testing.assert_array_equal(topk.cpu().numpy(), want_sel)
     assert_close_attention(out, want_out, f"random decode {seed}")
+
+
+# ---------------------------------------------------------------- variants
+
+def masked_fits(B: int, r: int) -> bool:
+    """The masked-union kernel's per-chunk membership table (64 / B block entries times one word per
+    32 queries of a 256-row workgroup) must fit its 64 words."""
+    span = -(-256 // r) + 1
+    return (64 // B) * ((span + 31) // 32) <= 64
+
+
+def draw_masked(seed: int) -> datagen.Workload:
+    rng = np.random.default_rng(8300 + seed)
+    while True:
+        B = int(rng.choice([1, 2, 4, 8, 16, 32, 64]))
+        r = int(rng.choice([1, 2, 4, 8, 16]))
+        if masked_fits(B, r):
+            break
+    G = int(rng.choice([1, 2]))
+    N = int(rng.integers(2 * B, 1800))
+    kb = int(rng.integers(1, 200 if B > 1 else 500))
+    tile = int(rng.choice([1, 5, 16, 48, 64, 128]))
+    return datagen.PREFILL.replace(name=f"rand_masked_{seed}", n_tokens=N, n_q_heads=G * r, n_kv_heads=G,
+                                   block=B, topk_tokens=kb * B, union_tile=tile, qi_mode="iid")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_prefill_masked(sg, seed):
+    wl = draw_masked(seed)
+    p = params_of(wl)
+    x = datagen.prefill_inputs(wl)
+    ch = OracleChain(x, p)
+    want = oracle.attend_sel(bits(x["q"]), bits(x["k"]), bits(x["v"]), ch.topk(), p.block)
+    say(f"random masked prefill {seed}: {describe(wl)}")
+    xd = to_dev(x)
+    out = torch.empty((p.n_tokens, p.n_q_heads, p.head_dim), dtype=torch.bfloat16, device="cuda")
+    sg.sgqa_prefill_masked(p, xd["q"], xd["k"], xd["v"], xd["qi"], xd["w"], xd["ki"], out,
+                           sg.workspace(p, sg.SGQA_OP_PREFILL_MASKED))
+    torch.cuda.synchronize()
+    assert_close_attention(out, want, f"random masked prefill {seed}")
+
+
+def draw_varlen(seed: int):
+    rng = np.random.default_rng(9700 + seed)
+    B = int(rng.choice([1, 2, 4, 8, 16, 32, 64]))
+    G = int(rng.choice([1, 2, 3]))
+    S = int(rng.integers(1, 6))
+    C = int(rng.integers(2 * B, 6000))
+    kb = int(rng.integers(1, 600))
+    page = int(rng.choice([p for p in (1, 2, 4, 8, 16, 32, 64, 128, 256) if p >= B]))
+    lens = [int(v) for v in rng.integers(1, C + 1, size=S)]
+    wl = datagen.DECODE.replace(name=f"rand_varlen_{seed}", n_tokens=C, n_seqs=S, n_q_heads=8 * G, n_kv_heads=G,
+                                topk_tokens=kb * B, block=B)
+    return wl, page, lens
+
+
+def oracle_prefix(x, s, L, B, kb, caches=None):
+    """The oracle's decode of sequence s over the first L positions of its caches."""
+    sl = slice(s, s + 1)
+    kbar = oracle.compress(bits(x["ki_cache"][sl, :L]), B)
+    if caches is None:
+        return oracle.decode(x["q"][sl], x["k_cache"][sl, :, :L].contiguous(), x["v_cache"][sl, :, :L].contiguous(),
+                             kbar, x["qi"][sl], x["w"], B, kb)
+    return oracle.decode_fp8(x["q"][sl], caches["k8"][sl, :, :L].contiguous(), caches["v8"][sl, :, :L].contiguous(),
+                             caches["kv_scale"][sl], kbar, x["qi"][sl], x["w"], B, kb)
+
+
+@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("fp8", [False, True])
+def test_random_varlen_paged_decode(sg, seed, fp8):
+    from tests.test_gpu_incremental import to_pages
+
+    wl, page, lens = draw_varlen(seed)
+    p = params_of(wl)
+    S, C, G, B = wl.n_seqs, wl.n_tokens, wl.n_kv_heads, wl.block
+    x = datagen.decode_inputs(wl)
+    f = datagen.fp8_caches(wl) if fp8 else None
+    say(f"random varlen decode {seed} fp8={fp8}: C={C} S={S} G={G} B={B} K_B={p.kb} page={page} lens={lens}")
+    xd = to_dev(x)
+    blk = torch.empty((S, C // B, 64), dtype=torch.bfloat16, device="cuda")
+    sg.sgqa_compress(p, xd["ki_cache"], blk)
+    ws = sg.workspace(p, sg.SGQA_OP_DECODE)
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    kc, vc = (f["k8"].cuda(), f["v8"].cuda()) if fp8 else (xd["k_cache"], xd["v_cache"])
+
+    def run(k_cache, v_cache, pages=None):
+        out = torch.empty((S, p.n_q_heads, 128), dtype=torch.bfloat16, device="cuda")
+        topk = torch.empty((S, G, p.kb), dtype=torch.int32, device="cuda")
+        if fp8:
+            sg.sgqa_decode_fp8(p, xd["q"], k_cache, v_cache, f["kv_scale"].cuda(), blk, xd["qi"], xd["w"], out, ws,
+                               seq_lens=sl, pages=pages, topk_out=topk)
+        else:
+            sg.sgqa_decode_varlen(p, xd["q"], k_cache, v_cache, blk, xd["qi"], xd["w"], sl, out, ws, pages=pages,
+                                  topk_out=topk)
+        torch.cuda.synchronize()
+        return out, topk
+
+    out, topk = run(kc, vc)
+    for s, L in enumerate(lens):
+        sel, want = oracle_prefix(x, s, L, B, p.kb, f)
+        np.testing.assert_array_equal(topk[s:s + 1].cpu().numpy(), sel)
+        assert_close_attention(out[s:s + 1], want, f"random varlen {seed} fp8={fp8} seq {s} L={L}")
+    table, kpool, n_pages = to_pages(sg, kc, page, 100 + seed)
+    _, vpool, _ = to_pages(sg, vc, page, 100 + seed)
+    out_p, topk_p = run(kpool, vpool, sg.Pages(table, page, n_pages))
+    assert torch.equal(topk_p, topk)
+    assert torch.equal(out_p.view(torch.int16), out.view(torch.int16))
