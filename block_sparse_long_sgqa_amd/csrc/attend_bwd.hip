@@ -1140,13 +1140,27 @@ __global__ __launch_bounds__(kTmWaves * 64) void k_tm_dkdv(
     if (wave_keys) tm_first(rows0, kb, vb, s, dp);
     auto step = [&](auto phase, int rg) __attribute__((always_inline)) {
       constexpr int B = decltype(phase)::value;
-      uint8_t* const bufs[3] = {rows0, rows1, rows2};
-      float* const lsdes[3] = {lsde0, lsde1, lsde2};
-      int* const qrows[3] = {qrow0, qrow1, qrow2};
-      store_rg(bufs[(B + 2) % 3], lsdes[(B + 2) % 3], qrows[(B + 2) % 3], sqa, sda, lsa, dea, qia);
+      // Buffers of groups rg (B), rg + 1 and rg + 2, selected at compile time.
+      auto buf = [&](auto which) __attribute__((always_inline)) -> uint8_t* {
+        constexpr int X = decltype(which)::value;
+        return X == 0 ? rows0 : (X == 1 ? rows1 : rows2);
+      };
+      auto lsde_of = [&](auto which) __attribute__((always_inline)) -> float* {
+        constexpr int X = decltype(which)::value;
+        return X == 0 ? lsde0 : (X == 1 ? lsde1 : lsde2);
+      };
+      auto qrow_of = [&](auto which) __attribute__((always_inline)) -> int* {
+        constexpr int X = decltype(which)::value;
+        return X == 0 ? qrow0 : (X == 1 ? qrow1 : qrow2);
+      };
+      using Cur = std::integral_constant<int, B>;
+      using Next = std::integral_constant<int, (B + 1) % 3>;
+      using Free = std::integral_constant<int, (B + 2) % 3>;
+      store_rg(buf(Free()), lsde_of(Free()), qrow_of(Free()), sqa, sda, lsa, dea, qia);
       load_rg(rg + 3, sqa, sda, lsa, dea, qia);
       if (wave_keys && rg < n_rg)
-        tm_pipe(bufs[(B + 1) % 3], bufs[B], lsdes[B], qrows[B], key_ok, key, kb, vb, adk, adv, lo, scale_log2, s, dp);
+        tm_pipe(buf(Next()), buf(Cur()), lsde_of(Cur()), qrow_of(Cur()), key_ok, key, kb, vb, adk, adv, lo,
+                scale_log2, s, dp);
       __syncthreads();
     };
     for (int rg = 0; rg < n_rg; rg += 3) {
