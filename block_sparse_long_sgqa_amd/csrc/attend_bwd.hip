@@ -21,13 +21,16 @@
 //    pipelines the groups (S and dP of the next group on the matrix cores while the vector ALU forms
 //    P and dS of the current one, then dV^T += dO^T P and dK^T += Q^T dS with transposed reads). Each
 //    item writes fp32 partial rows per key, summed per key in ascending tile order by a second
-//    kernel (see the tile-major section below).
+//    kernel that runs on a second stream, beside the products of the next batch of tiles (see the
+//    tile-major section below).
 //  * dk, dv, key-major (the longest contexts): every key's sum runs over its rows in one place. A
 //    wave owns 32 consecutive keys of one group and walks the tiles whose union holds one of its
 //    blocks; per 32-row group of such a tile, Q and dO rows are gathered into the wave's swizzled
 //    LDS tiles (double-buffered, one group ahead), with the same products.
 #include <stdlib.h>
 #include <string.h>
+
+#include <mutex>
 
 #include "attn_common.hpp"
 
@@ -703,14 +706,18 @@ __global__ __launch_bounds__(kBwdWaves * 64) void k_bwd_dkdv(const uint16_t* __r
 // in batches of at most a fixed number of rows: a planning pass on the device numbers the pairs'
 // rows and items, and batch b holds the pairs whose first row lies in [b H, (b + 1) H) with H the
 // batch size minus the largest pair; the host launches the worst-case number of batches, and the
-// kernels of an empty batch return at once.
+// kernels of an empty batch return at once. The partial rows alternate between two buffers: the
+// sums of batch b (bound by HBM) run on a second stream while the products of batch b + 1 (bound
+// by the matrix cores and LDS, one wave per SIMD) fill the other buffer, the two kernels sharing
+// the CUs.
 
 namespace {
 constexpr int kTmWaves = 4;
 constexpr int kTmKeys = kTmWaves * 32;      // union entries per work item
 constexpr int kTmRowFloats = 2 * kD;        // partial row: dK^T column, then dV^T column
-constexpr long long kTmCapRows = 1LL << 22; // partial rows per batch (4 GiB)
-constexpr int kTmMaxBatches = 1024;         // more batches than this: the key-major kernel runs
+constexpr long long kTmCapRows = 1LL << 21; // partial rows per batch buffer (2 GiB; two buffers)
+constexpr int kTmReduceLds = 96 * 1024;     // LDS reserved (unused) by a reduce workgroup
+constexpr int kTmMaxBatches = 2048;         // more batches than this: the key-major kernel runs
 constexpr int kTmPlanThreads = 1024;
 struct TmItem {
   uint32_t pair, word;  // (tile, group) pair t * G + g; mask word holding the item's first block
@@ -978,6 +985,8 @@ __global__ __launch_bounds__(kTmWaves * 64) void k_tm_dkdv(
   const int wave = threadIdx.x >> 6, l = lane_id(), hi = l >> 5;
   const int ps = bstart[batch], pe = bstart[batch + 1];
   if (ps >= pe) return;
+  // The previous batch's reduction shares the SIMDs (one wave each): these waves issue first.
+  __builtin_amdgcn_s_setprio(2);
   const uint32_t it0 = ipref[ps];
   const uint32_t n_items = ipref[pe] - it0;
   const unsigned long long e0 = ebase[ps];
@@ -1186,97 +1195,92 @@ __global__ __launch_bounds__(kTmWaves * 64) void k_tm_dkdv(
   }
 }
 
-// acc[g][j] += the partial rows of key j from the batch's tiles, in ascending tile order (a
-// persistent grid over 64-key chunks). Wave w, step m handles key j0 + 4 m + w; lane l its floats
-// 4 l .. 4 l + 3. A tile's membership words for the chunk come 64 tiles at a time, one per lane.
-__global__ __launch_bounds__(256) void k_tm_reduce(const uint32_t* __restrict__ umask,
-                                                   const uint32_t* __restrict__ pre,
-                                                   const unsigned long long* __restrict__ ebase,
-                                                   const int* __restrict__ bstart, const float* __restrict__ part,
-                                                   float* __restrict__ acc, int batch, int n_tokens, int n_groups,
-                                                   int block_shift, int tile, int n_tiles, int n_words) {
+// acc[g][j] += the partial rows of key j from the batch's tiles, in ascending tile order. This
+// kernel runs on a second stream beside the dk/dv kernel of the next batch, whose workgroup holds
+// one wave per SIMD at 424 registers, so it is built to share a CU with it: at most 88 registers a
+// lane, one workgroup per CU (a grid of one per CU, and a dynamic-LDS reservation of
+// kTmReduceLds that leaves no room for a second one but room for the dk/dv workgroup), persistent
+// over 32-key chunks. Wave w owns keys j0 + 8 w .. j0 + 8 w + 7 (one block for B = 8; for any B
+// their blocks lie in one mask word), lane l their floats 4 l .. 4 l + 3. The tiles' membership
+// words for the wave's keys come 64 tiles at a time, one per lane, and the wave walks only the
+// tiles whose union holds one of its keys. Partial rows are read once: non-temporal loads.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(88))) void k_tm_reduce(
+    const uint32_t* __restrict__ umask, const uint32_t* __restrict__ pre, const unsigned long long* __restrict__ ebase,
+    const int* __restrict__ bstart, const float* __restrict__ part, float* __restrict__ acc, int batch, int n_tokens,
+    int n_groups, int block_shift, int tile, int n_tiles, int n_words) {
   const int ps = bstart[batch], pe = bstart[batch + 1];
   if (ps >= pe) return;
   const unsigned long long e0 = ebase[ps];
-  const int wave = threadIdx.x >> 6, l = lane_id();
-  const int cpg = (n_tokens + 63) >> 6;
+  // The wave index as a uniform value: keys, rows and row addresses stay scalar.
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), l = lane_id();
+  const uint32_t lofs = 4u * (uint32_t)l;
+  const int cpg = (n_tokens + 31) >> 5;
   const int n_chunks = cpg * n_groups;
   for (int c = blockIdx.x; c < n_chunks; c += gridDim.x) {
-    const int g = c / cpg, j0 = (c - g * cpg) << 6;
-    // Tiles of this group in the batch (pairs t * G + g in [ps, pe)) that reach key j0.
-    const int t_lo = max(ps - g <= 0 ? 0 : (ps - g + n_groups - 1) / n_groups, j0 / tile);
+    const int g = c / cpg;
+    const int k0 = ((c - g * cpg) << 5) + 8 * wave;
+    if (k0 >= n_tokens) continue;
+    // Tiles of this group in the batch (pairs t * G + g in [ps, pe)) that reach key k0.
+    const int t_lo = max(ps - g <= 0 ? 0 : (ps - g + n_groups - 1) / n_groups, k0 / tile);
     const int t_hi = pe - g <= 0 ? 0 : (pe - g + n_groups - 1) / n_groups;
     if (t_lo >= t_hi) continue;
-    const int b_first = j0 >> block_shift, b_last = (min(j0 + 63, n_tokens - 1)) >> block_shift;
-    const int wa = b_first >> 5, wb = b_last >> 5;  // wb = wa + 1 only for B = 1
-    const uint32_t ma_chunk = wb == wa ? ((b_last & 31) == 31 ? ~0u : (2u << (b_last & 31)) - 1u) &
-                                             ~((1u << (b_first & 31)) - 1u)
-                                       : ~((1u << (b_first & 31)) - 1u);
-    const uint32_t mb_chunk = wb == wa ? 0u : ((b_last & 31) == 31 ? ~0u : (2u << (b_last & 31)) - 1u);
+    const int k_end = min(k0 + 8, n_tokens), n_keys = k_end - k0;
+    // Rows as a uniform pointer plus this lane's 32-bit float offset (scalar-base addressing).
+    float* const arow = acc + ((long long)g * n_tokens + k0) * kTmRowFloats;
+    const int b_first = k0 >> block_shift, b_last = (k_end - 1) >> block_shift;
+    const int wa = b_first >> 5;
+    const uint32_t wmask =
+        ((b_last & 31) == 31 ? ~0u : (2u << (b_last & 31)) - 1u) & ~((1u << (b_first & 31)) - 1u);
     bool started = false;
-    f32x4 a[16];
+    f32x4 a[8];
     for (int tb = t_lo; tb < t_hi; tb += 64) {
       const int tl = tb + l;
-      uint32_t wa_l = 0u, wb_l = 0u, pa_l = 0u, pb_l = 0u;
-      unsigned long long base_l = 0;
-      if (tl < t_hi) {
-        const int c_hi = tm_chi(tl, n_tokens, tile, block_shift);
-        const uint32_t* mrow = umask + ((long long)g * n_tiles + tl) * n_words;
-        wa_l = tm_word(mrow, wa, c_hi);
-        wb_l = wb == wa ? 0u : tm_word(mrow, wb, c_hi);
-      }
-      uint64_t hit = ballot(((wa_l & ma_chunk) | (wb_l & mb_chunk)) != 0u);
+      uint32_t w_l = 0u;
+      if (tl < t_hi)
+        w_l = tm_word(umask + ((long long)g * n_tiles + tl) * n_words, wa, tm_chi(tl, n_tokens, tile, block_shift));
+      uint64_t hit = ballot((w_l & wmask) != 0u);
       if (hit == 0) continue;
-      if ((wa_l & ma_chunk) | (wb_l & mb_chunk)) {
+      uint32_t p_l = 0u;
+      unsigned long long base_l = 0;
+      if (w_l & wmask) {
         const int pair = tl * n_groups + g;
-        pa_l = pre[(long long)pair * n_words + wa];
-        pb_l = wb == wa ? 0u : pre[(long long)pair * n_words + wb];
+        p_l = pre[(long long)pair * n_words + wa];
         base_l = ebase[pair] - e0;
       }
       if (!started) {
         started = true;
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
-          const int key = j0 + 4 * m + wave;
-          a[m] = key < n_tokens ? *reinterpret_cast<const f32x4*>(acc + ((long long)g * n_tokens + key) *
-                                                                      kTmRowFloats + 4 * l)
-                                : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        }
+        for (int m = 0; m < 8; ++m)
+          a[m] = m < n_keys ? *reinterpret_cast<const f32x4*>(arow + (lofs + 256u * m)) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       }
       while (hit) {
         const int x = __builtin_ctzll(hit);
         hit &= hit - 1;
-        const uint32_t wa_t = __builtin_amdgcn_readlane(wa_l, x), wb_t = __builtin_amdgcn_readlane(wb_l, x);
-        const uint32_t pa_t = __builtin_amdgcn_readlane(pa_l, x), pb_t = __builtin_amdgcn_readlane(pb_l, x);
+        const uint32_t w_t = __builtin_amdgcn_readlane(w_l, x), p_t = __builtin_amdgcn_readlane(p_l, x);
         const unsigned long long base_t =
             ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((uint32_t)(base_l >> 32), x) << 32) |
             (uint32_t)__builtin_amdgcn_readlane((uint32_t)base_l, x);
-        f32x4 xs[16];
+        f32x4 xs[8];
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
-          const int key = j0 + 4 * m + wave;
-          const int blk = key >> block_shift;
-          const bool in_b = (blk >> 5) != wa;
-          const uint32_t wd = in_b ? wb_t : wa_t;
-          const int bit = blk & 31;
-          const bool member = key < n_tokens && ((wd >> bit) & 1u);
-          const uint32_t rank = (in_b ? pb_t : pa_t) + __popc(wd & ((1u << bit) - 1u));
+        for (int m = 0; m < 8; ++m) {
+          const int key = k0 + m;
+          const int bit = (key >> block_shift) & 31;
+          const bool member = key < n_tokens && ((w_t >> bit) & 1u);
+          const uint32_t rank = p_t + __popc(w_t & ((1u << bit) - 1u));
           const unsigned long long row =
               member ? base_t + ((unsigned long long)rank << block_shift) + (key & ((1 << block_shift) - 1)) : 0ull;
-          xs[m] = *reinterpret_cast<const f32x4*>(part + row * kTmRowFloats + 4 * l);
+          const float* prow = part + row * kTmRowFloats;  // uniform
+          xs[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(prow + lofs));
           if (!member) xs[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         }
 #pragma unroll
-        for (int m = 0; m < 16; ++m) a[m] += xs[m];
+        for (int m = 0; m < 8; ++m) a[m] += xs[m];
       }
     }
     if (started) {
 #pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        const int key = j0 + 4 * m + wave;
-        if (key < n_tokens)
-          *reinterpret_cast<f32x4*>(acc + ((long long)g * n_tokens + key) * kTmRowFloats + 4 * l) = a[m];
-      }
+      for (int m = 0; m < 8; ++m)
+        if (m < n_keys) *reinterpret_cast<f32x4*>(arow + (lofs + 256u * m)) = a[m];
     }
   }
 }
@@ -1380,10 +1384,41 @@ BwdPlan attend_bwd_plan(int n_tokens, int n_q_heads, int n_groups, int block, in
   pl.o_bstart = take((size_t)(n_batches + 1) * 4);
   pl.o_pre = take((size_t)n_pairs * n_words * 4);
   pl.o_items = take((size_t)items_bound * sizeof(TmItem));
-  pl.o_part = take((size_t)cap * kTmRowFloats * 4);
+  // Batch b's partial rows go to buffer b % 2: the reduction of batch b runs while the dk/dv kernel
+  // fills the other buffer with batch b + 1.
+  pl.o_part = take((size_t)(n_batches > 1 ? 2 : 1) * cap * kTmRowFloats * 4);
   pl.bytes = off;
   return pl;
 }
+
+namespace {
+// The second stream of the tile-major backward on one device (the reductions run there, beside the
+// dk/dv kernel on the caller's stream) and the events that order the two, created by the first
+// backward on the device and kept until the process ends. The events are shared by the calls on
+// the device, so a call holds `mu` while it enqueues its batches.
+struct BwdStreams {
+  std::once_flag once;
+  hipError_t status = hipErrorNotInitialized;
+  hipStream_t side = nullptr;
+  hipEvent_t dkdv_done[2] = {nullptr, nullptr}, reduce_done[2] = {nullptr, nullptr};
+  std::mutex mu;
+};
+constexpr int kBwdMaxDevices = 64;
+BwdStreams g_bwd_streams[kBwdMaxDevices];
+
+BwdStreams* bwd_streams() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kBwdMaxDevices) return nullptr;
+  BwdStreams& b = g_bwd_streams[dev];
+  std::call_once(b.once, [&b] {
+    hipError_t e = hipStreamCreateWithFlags(&b.side, hipStreamNonBlocking);
+    for (int i = 0; i < 2 && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&b.dkdv_done[i], hipEventDisableTiming);
+    for (int i = 0; i < 2 && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&b.reduce_done[i], hipEventDisableTiming);
+    b.status = e;
+  });
+  return &b;
+}
+}  // namespace
 
 hipError_t launch_attend_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint32_t* umask,
                              const uint16_t* out, const float* lse, const uint16_t* dout, uint16_t* dq, uint16_t* dk,
@@ -1397,6 +1432,13 @@ hipError_t launch_attend_bwd(const uint16_t* q, const uint16_t* k, const uint16_
     if (tr * (rr - 1) >= (1LL << 32)) return hipErrorInvalidValue;
   }
   const BwdPlan pl = attend_bwd_plan(n_tokens, n_q_heads, n_groups, block, tile);
+  BwdStreams* bs = nullptr;
+  if (pl.tile_major) {  // set up before the first launch, so that a failure launches nothing
+    bs = bwd_streams();
+    if (!bs) return hipErrorInvalidDevice;
+    if (bs->status != hipSuccess) return bs->status;
+    if (kTmReduceLds > max_lds_per_block()) return hipErrorInvalidValue;
+  }
   uint8_t* wsb = static_cast<uint8_t*>(ws);
   float* delta = reinterpret_cast<float*>(wsb);
   hipLaunchKernelGGL(k_bwd_delta, dim3((unsigned)((n_rows + 15) / 16)), dim3(256), 0, stream, out, dout, delta,
@@ -1453,22 +1495,40 @@ hipError_t launch_attend_bwd(const uint16_t* q, const uint16_t* k, const uint16_
   if (e != hipSuccess) return e;
   const int cu = device_cu_count();
   const unsigned main_grid = (unsigned)((cu + 7) / 8 * 8);
-  const long long n_chunks = (long long)n_groups * ((n_tokens + 63) / 64);
-  const unsigned red_grid = (unsigned)(n_chunks < 8LL * cu ? n_chunks : 8LL * cu);
-  for (int b = 0; b < pl.n_batches; ++b) {
-    hipLaunchKernelGGL(k_tm_dkdv, dim3(main_grid), dim3(kTmWaves * 64), 0, stream, q, k, v, umask, lse, delta, dout,
-                       pre, ebase, ipref, bstart, items, part, b, n_tokens, n_q_heads, n_groups, block, shift, tile,
-                       scale_log2, n_tiles, n_words);
-    hipLaunchKernelGGL(k_tm_reduce, dim3(red_grid), dim3(256), 0, stream, umask, pre, ebase, bstart, part, acc, b,
-                       n_tokens, n_groups, shift, tile, n_tiles, n_words);
+  const long long n_chunks = (long long)n_groups * ((n_tokens + 31) / 32);
+  const unsigned red_grid = (unsigned)(n_chunks < cu ? n_chunks : cu);
+  // Batch b: dk/dv on the caller's stream into buffer b % 2 (after the reduction of batch b - 2 has
+  // read it), then its reduction on the side stream (after that dk/dv); the side stream keeps the
+  // reductions in batch order, and the caller's stream waits for the last one.
+  {
+    std::lock_guard<std::mutex> lock(bs->mu);
+    for (int b = 0; b < pl.n_batches; ++b) {
+      float* pb = part + (size_t)(b & 1) * (size_t)pl.cap_rows * kTmRowFloats;
+      if (b >= 2 && (e = hipStreamWaitEvent(stream, bs->reduce_done[b & 1], 0)) != hipSuccess) return e;
+      hipLaunchKernelGGL(k_tm_dkdv, dim3(main_grid), dim3(kTmWaves * 64), 0, stream, q, k, v, umask, lse, delta,
+                         dout, pre, ebase, ipref, bstart, items, pb, b, n_tokens, n_q_heads, n_groups, block, shift,
+                         tile, scale_log2, n_tiles, n_words);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if ((e = hipEventRecord(bs->dkdv_done[b & 1], stream)) != hipSuccess) return e;
+      if ((e = hipStreamWaitEvent(bs->side, bs->dkdv_done[b & 1], 0)) != hipSuccess) return e;
+      hipLaunchKernelGGL(k_tm_reduce, dim3(red_grid), dim3(256), kTmReduceLds, bs->side, umask, pre, ebase, bstart,
+                         pb, acc, b, n_tokens, n_groups, shift, tile, n_tiles, n_words);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if ((e = hipEventRecord(bs->reduce_done[b & 1], bs->side)) != hipSuccess) return e;
+    }
+    e = hipStreamWaitEvent(stream, bs->reduce_done[(pl.n_batches - 1) & 1], 0);
+    if (e != hipSuccess) return e;
   }
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_tm_final, dim3((unsigned)((acc_rows * 32 + 255) / 256)), dim3(256), 0, stream, acc, dk, dv,
                      acc_rows, scale);
   return hipGetLastError();
 }
 
-hipError_t prepare_attend_bwd_kernels(int lds_max) { return allow_full_lds((const void*)k_bwd_dq<kDqWaves>, lds_max); }
+hipError_t prepare_attend_bwd_kernels(int lds_max) {
+  hipError_t e = allow_full_lds((const void*)k_bwd_dq<kDqWaves>, lds_max);
+  if (e == hipSuccess && kTmReduceLds <= lds_max)
+    e = hipFuncSetAttribute((const void*)k_tm_reduce, hipFuncAttributeMaxDynamicSharedMemorySize, kTmReduceLds);
+  return e;
+}
 
 }  // namespace sgqa

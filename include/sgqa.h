@@ -32,9 +32,9 @@
  *     leave the earlier kernels of a multi-kernel call (prefill, decode) enqueued. A fault inside
  *     a kernel surfaces at the caller's next synchronization.
  *   - Results are deterministic: the same inputs give the same bits (no floating-point atomics).
- *   - Calls keep no state beyond per-device facts filled once (thread-safe) on first use; calls on
- *     different streams or host threads may run concurrently if their outputs and workspaces do
- *     not overlap.
+ *   - Calls keep no state beyond per-device facts filled once (thread-safe) on first use, and the
+ *     backward's second stream and events (sgqa_attend_bwd); calls on different streams or host
+ *     threads may run concurrently if their outputs and workspaces do not overlap.
  *   - v1 limits: head_dim == 128, idx_heads == 4, idx_dim == 64, block a power of two <= 64,
  *     topk_tokens a positive multiple of block with topk_tokens/block <= 2048, n_q_heads a multiple
  *     of n_kv_heads, n_q_heads/n_kv_heads <= 16, n_tokens >= 1, union_tile >= 1.
@@ -311,11 +311,16 @@ int sgqa_attend_fwd(const sgqa_params* p, const sgqa_bf16* q, const sgqa_bf16* k
  * dq [N][Hq][D], dk, dv [G][N][D] bf16 out (fp32 sums, one bf16 rounding; keys no row attends get 0).
  * Deterministic: every sum has a fixed order (no floating-point atomics). Workspace:
  * sgqa_workspace_size(p, SGQA_OP_ATTEND_BWD): the deltas and, for dk/dv, an fp32 accumulator
- * [G][N][2D], the per-(tile, group) plan tables and work items, and the fp32 partial rows of one
- * batch of tiles (at most 4 GiB; about 5.1 GiB in all at N = 131072, G = 8). dk/dv are summed
- * tile by tile (every key's partial rows in ascending tile order) unless that needs more than 1024
- * batches (the longest contexts), where a key-major kernel sums every key in one place; both give
- * the same sums up to fp32 rounding order. Two environment variables, read by the host code at each
+ * [G][N][2D], the per-(tile, group) plan tables and work items, and the fp32 partial rows of the
+ * batches of tiles (two buffers of at most 2 GiB; about 5.1 GiB in all at N = 131072, G = 8). dk/dv
+ * are summed tile by tile (every key's partial rows in ascending tile order) unless that needs more
+ * than 2048 batches (the longest contexts), where a key-major kernel sums every key in one place;
+ * both give the same sums up to fp32 rounding order. The tile-by-tile sums of a batch run on a
+ * second stream, beside the next batch's products on `stream`: the first such call on a device
+ * creates that stream (default priority, non-blocking) and four events, kept until the process
+ * ends; the call makes `stream` wait for that work before its last kernel, so the results are
+ * ordered on `stream` as for any other call, and the call holds a lock while it enqueues (calls on
+ * one device share the events). Two environment variables, read by the host code at each
  * call and meant for tests, select the design: SGQA_BWD_PATH=key forces the key-major kernel,
  * SGQA_BWD_BATCH_ROWS=<n> caps a batch at n partial rows (never below twice the largest tile's
  * rows); sgqa_workspace_size and sgqa_attend_bwd size the workspace for the design they select at

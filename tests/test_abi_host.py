@@ -93,11 +93,12 @@ def test_bad_shapes_are_rejected_before_any_launch(sg, kw):
     assert st == sg.SGQA_ERR_SHAPE
 
 
-def bwd_workspace(N, Hq, G, B, Tq, batch_rows=1 << 22, max_batches=1024):
+def bwd_workspace(N, Hq, G, B, Tq, batch_rows=1 << 21, max_batches=2048):
     """The backward's workspace as its header states it: the deltas (N Hq fp32), and for the
     tile-major dk/dv (when its batches of partial rows number at most max_batches) the fp32
     accumulator (G N rows of 1 KiB), nblk / ebase / ipref per pair, the batch starts, the word
-    prefixes (pairs x mask words), the work items (8 B) and one batch of 1-KiB partial rows."""
+    prefixes (pairs x mask words), the work items (8 B) and the 1-KiB partial rows: one batch, or two
+    buffers of a batch each when there are several batches (one is reduced while the other fills)."""
     r = lambda x: (x + 255) // 256 * 256  # noqa: E731
     delta = r(N * Hq * 4)
     T, nbc = -(-N // Tq), -(-N // B)
@@ -106,7 +107,7 @@ def bwd_workspace(N, Hq, G, B, Tq, batch_rows=1 << 22, max_batches=1024):
     rows = G * sum(n * B for n in nb)
     items = G * sum(-(-n // nbi) for n in nb)
     unit = nbc * B
-    cap = max(min(batch_rows, 1 << 22), 2 * unit)
+    cap = max(min(batch_rows, 1 << 21), 2 * unit)
     if cap >= rows:
         cap, n_b = rows, 1
     else:
@@ -115,7 +116,7 @@ def bwd_workspace(N, Hq, G, B, Tq, batch_rows=1 << 22, max_batches=1024):
     if n_b > max_batches:
         return delta
     return (delta + r(G * N * 1024) + r(P * 4) + r((P + 1) * 8) + r((P + 1) * 4) + r((n_b + 1) * 4)
-            + r(P * W * 4) + r(items * 8) + r(cap * 1024))
+            + r(P * W * 4) + r(items * 8) + r((2 if n_b > 1 else 1) * cap * 1024))
 
 
 @pytest.mark.parametrize("shape", [(131072, 64, 8, 8, 128), (32768, 64, 8, 8, 64), (20037, 8, 1, 1, 64),
