@@ -206,3 +206,77 @@ def test_attend_bwd_full_size(sg, name):
     assert_close_grad(dq[torch.from_numpy(rows).long().cuda()], pq, f"dq {name} sampled rows")
     assert_close_grad(dk[g0, key_lo:key_hi], pk, f"dk {name} keys")
     assert_close_grad(dv[g0, key_lo:key_hi], pv, f"dv {name} keys")
+
+
+def test_attend_bwd_stream_order(sg):
+    """The tile-order sums of each dk/dv batch run on the library's own second stream; the results
+    must still be ordered on the caller's stream. With many small batches (the event hand-offs
+    between the two streams at every batch): two calls back to back on a caller-made stream, sharing
+    one workspace and read on that stream without a host wait in between, and two host threads
+    calling at once on two streams, all give the bits of a call on the default stream."""
+    import threading
+
+    wl = datagen.PREFILL.replace(name="bwd_streams", n_tokens=8192, n_q_heads=16, n_kv_heads=2,
+                                 topk_tokens=512, union_tile=64)
+    p = params_of(wl)
+    N, Hq, G, D = p.n_tokens, p.n_q_heads, p.n_kv_heads, p.head_dim
+    x = datagen.prefill_inputs(wl, device="cuda")
+    umask = torch.empty((G, p.n_tiles, p.n_words), dtype=torch.int32, device="cuda")
+    ucount = torch.empty((G, p.n_tiles), dtype=torch.int32, device="cuda")
+    blk = torch.empty((N // p.block, p.idx_dim), dtype=torch.bfloat16, device="cuda")
+    sg.sgqa_compress(p, x["ki"], blk)
+    sg.sgqa_index_union(p, x["qi"], x["w"], blk, umask, ucount)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(3)
+    dout = torch.randn((N, Hq, D), generator=gen, device="cuda").to(torch.bfloat16)
+    with bwd_mode("tile_batched"):
+        # The tile-major design runs (its workspace holds more than the deltas).
+        assert sg.workspace_size(p, sg.SGQA_OP_ATTEND_BWD) > N * Hq * 4 + 256
+        out, lse, dq0, dk0, dv0 = run_fwd_bwd(sg, p, x, umask, ucount, dout)
+
+        def grads():
+            return (torch.empty_like(dq0), torch.empty_like(dk0), torch.empty_like(dv0))
+
+        def same(got, what):
+            for a, b, n in zip(got, (dq0, dk0, dv0), ("dq", "dk", "dv")):
+                assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{what}: {n} differs"
+
+        s = torch.cuda.Stream()
+        ws = sg.workspace(p, sg.SGQA_OP_ATTEND_BWD)
+        g1, g2 = grads(), grads()
+        torch.cuda.synchronize()
+        say("attend_bwd streams: two calls back to back on a caller stream")
+        with torch.cuda.stream(s):
+            for g in (g1, g2):
+                sg.sgqa_attend_bwd(p, x["q"], x["k"], x["v"], umask, ucount, out, lse, dout, *g, ws, stream=s)
+            copies = [tuple(t.clone() for t in g) for g in (g1, g2)]
+        s.synchronize()
+        for c, what in zip(copies, ("first call", "second call")):
+            same(c, what)
+
+        say("attend_bwd streams: two host threads on two streams")
+        streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+        wss = [sg.workspace(p, sg.SGQA_OP_ATTEND_BWD) for _ in streams]
+        outs = [grads(), grads()]
+        torch.cuda.synchronize()
+        errors = []
+
+        def work(t):
+            try:
+                st = streams[t]
+                with torch.cuda.stream(st):
+                    for _ in range(2):
+                        sg.sgqa_attend_bwd(p, x["q"], x["k"], x["v"], umask, ucount, out, lse, dout, *outs[t],
+                                           wss[t], stream=st)
+                st.synchronize()
+            except Exception as e:  # reported on the main thread
+                errors.append(e)
+
+        threads = [threading.Thread(target=work, args=(t,)) for t in range(2)]
+        for t in threads:
+            t.start()
+        for t in threads:
+            t.join()
+        assert not errors, errors
+        for t in range(2):
+            same(outs[t], f"thread {t}")
