@@ -120,13 +120,20 @@ def bwd_workspace(N, Hq, G, B, Tq, batch_rows=1 << 21, max_batches=2048):
 
 
 @pytest.mark.parametrize("shape", [(131072, 64, 8, 8, 128), (32768, 64, 8, 8, 64), (20037, 8, 1, 1, 64),
-                                   (1205, 16, 2, 8, 64), (5, 16, 2, 8, 16)])
+                                   (1205, 16, 2, 8, 64), (5, 16, 2, 8, 16),
+                                   # either side of the batch limit: 1898 batches (tile-major), 2837 (key-major)
+                                   (327680, 64, 8, 8, 128), (393216, 64, 8, 8, 128)])
 def test_backward_workspace(sg, shape, monkeypatch):
     N, Hq, G, B, Tq = shape
     p = _p(n_tokens=N, n_q_heads=Hq, n_kv_heads=G, block=B, topk_tokens=max(B, 64), union_tile=Tq)
     monkeypatch.delenv("SGQA_BWD_PATH", raising=False)
     monkeypatch.delenv("SGQA_BWD_BATCH_ROWS", raising=False)
     assert sg.workspace_size(p, sg.SGQA_OP_ATTEND_BWD) == bwd_workspace(N, Hq, G, B, Tq)
+    deltas = (N * Hq * 4 + 255) // 256 * 256
+    if N == 327680:
+        assert bwd_workspace(N, Hq, G, B, Tq) > deltas  # the tile-major design
+    if N == 393216:
+        assert bwd_workspace(N, Hq, G, B, Tq) == deltas  # too many batches: key-major
     monkeypatch.setenv("SGQA_BWD_BATCH_ROWS", "1")
     assert sg.workspace_size(p, sg.SGQA_OP_ATTEND_BWD) == bwd_workspace(N, Hq, G, B, Tq, batch_rows=1)
     monkeypatch.setenv("SGQA_BWD_PATH", "key")
