@@ -8,6 +8,8 @@ Selections (top-k and the fused tile union) must be bit-exact; attention outputs
 attention tolerance; gradients within the relative gradient bar of the backward tests. Every draw
 is sized so that the fp64 oracle takes seconds.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -101,6 +103,25 @@ def test_random_backward(sg, seed):
     assert_close_grad(dq, want_dq, f"dq random {seed}")
     assert_close_grad(dk, want_dk, f"dk random {seed}")
     assert_close_grad(dv, want_dv, f"dv random {seed}")
+    # Again with the smallest batches the plan allows (many batches, the partial-row buffers
+    # alternating and each batch's tile-order sum on the second stream). The batches are runs of
+    # whole tiles summed in tile order, so while the tile-major design runs the gradients are the
+    # same bits; past its batch limit the key-major design runs and is held to the oracle instead.
+    deltas = (p.n_tokens * p.n_q_heads * 4 + 255) // 256 * 256
+    tile_major = sg.workspace_size(p, sg.SGQA_OP_ATTEND_BWD) > deltas
+    os.environ["SGQA_BWD_BATCH_ROWS"] = "1"
+    try:
+        batched_tile_major = sg.workspace_size(p, sg.SGQA_OP_ATTEND_BWD) > deltas
+        _, _, dq2, dk2, dv2 = run_fwd_bwd(sg, p, xd, um, uc, dout.cuda())
+    finally:
+        os.environ.pop("SGQA_BWD_BATCH_ROWS", None)
+    if tile_major and batched_tile_major:
+        for a, b, n in ((dq, dq2, "dq"), (dk, dk2, "dk"), (dv, dv2, "dv")):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{n} random {seed}: batched run differs"
+    else:
+        assert_close_grad(dq2, want_dq, f"dq random {seed} batched")
+        assert_close_grad(dk2, want_dk, f"dk random {seed} batched")
+        assert_close_grad(dv2, want_dv, f"dv random {seed} batched")
 
 
 def draw_decode(seed: int) -> datagen.Workload:
